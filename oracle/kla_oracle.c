@@ -1,0 +1,175 @@
+/*
+ * kla_oracle.c -- fp64 CPU oracle for the Kalman Linear Attention forward pass.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU
+ * baseline leg of the benchmark may load this file's library.  The product
+ * path (the HIP library under scan_amd/) never includes, links or calls it,
+ * and this file includes nothing from there.
+ *
+ * Sources (cited by title and section):
+ *  [KLA]  "Kalman Linear Attention: Parallel Bayesian Filtering For Efficient
+ *         Language Modelling and State Tracking", gist.science explainer,
+ *         technical summary (技術要約) > method (手法) §1-§3.
+ *  [KDN]  "Kalman Delta Networks: Uncertainty-aware Associative Memory",
+ *         abstract (fugumt page): diagonal and isotropic variants.
+ *
+ * What is computed.  [KLA] method §1 models the memory as a linear-Gaussian
+ * state-space model: an exactly discretised OU prior (decay a, process noise
+ * qn), noisy observations through the key k with observation noise r (the
+ * value precision is 1/r), and a readout of the posterior mean through the
+ * query q.  The filter runs in information form (precision l, information
+ * eta = l * mean), [KLA] method §2.  The pages give the Mobius form of the
+ * precision map but not its coefficients, so this library fixes one concrete
+ * recurrence; it is the exact Kalman filter of the independent scalar chains
+ *     x_t[i,j] = a_t[i] x_{t-1}[i,j] + N(0, qn[i]),
+ *     v_t[j]   = k_t[i] x_t[i,j]     + N(0, r_t),
+ * i.e. the diagonal (mean-field) family of [KDN]:
+ *
+ *   predict:  lp          = l / (a^2 + qn*l)           (variance a^2/l + qn)
+ *   gate:     g           = lp * a / l                  (information carried)
+ *   update:   l_t         = lp + k^2 / r
+ *             eta_t[i,:]  = g * eta_{t-1}[i,:] + k * v_t / r
+ *   readout:  o_t         = sum_i q_t[i] * eta_t[i,:] / l_t[i]
+ *
+ * The readout uses the posterior at t (token t included).  Isotropic mode
+ * ([KDN]: one uncertainty scalar per head) keeps a scalar l per head with
+ * per-token a_t and qn_t, and takes the precision increment as the
+ * trace-matched isotropic projection b_t = sum_i k_t[i]^2 / (d_k r_t); the
+ * information rows are updated exactly as above with the scalar gate.
+ *
+ * No blocking, no reordering: a plain sequential loop over t per (b,h),
+ * OpenMP only across independent (b,h) sequences.
+ *
+ * Layouts (dense, row-major):
+ *   q,k [B,H,T,dk]  v,o [B,H,T,dv]  r [B,H,T]
+ *   diag: a [B,H,T,dk]  qn [H,dk]   l0,lT [B,H,dk]
+ *   iso:  a [B,H,T]     qn [B,H,T]  l0,lT [B,H]
+ *   eta0,etaT [B,H,dk,dv]
+ * l0 == NULL means l0 = 1, eta0 == NULL means eta0 = 0.  lT, etaT, l_all
+ * (the precision after every token: [B,H,T,dk] or [B,H,T]) may be NULL.
+ */
+#include <stdlib.h>
+#include <string.h>
+
+#define KLA_ORACLE_DIAG 0
+#define KLA_ORACLE_ISO 1
+
+static void run_sequence(int T, int dk, int dv, int cov,
+                         const double* q, const double* k, const double* v,
+                         const double* a, const double* qn, const double* r,
+                         double* l, double* eta, double* o, double* l_all,
+                         double* lnew)
+{
+    for (int t = 0; t < T; ++t) {
+        const double* qt = q + (size_t)t * dk;
+        const double* kt = k + (size_t)t * dk;
+        const double* vt = v + (size_t)t * dv;
+        const double rt = r[t];
+        if (cov == KLA_ORACLE_DIAG) {
+            const double* at = a + (size_t)t * dk;
+            for (int i = 0; i < dk; ++i) {
+                const double lprev = l[i];
+                const double lp = lprev / (at[i] * at[i] + qn[i] * lprev);
+                const double g = lp * at[i] / lprev;
+                lnew[i] = lp + kt[i] * kt[i] / rt;
+                double* row = eta + (size_t)i * dv;
+                for (int j = 0; j < dv; ++j)
+                    row[j] = g * row[j] + kt[i] * vt[j] / rt;
+            }
+            for (int i = 0; i < dk; ++i) l[i] = lnew[i];
+            if (l_all)
+                for (int i = 0; i < dk; ++i) l_all[(size_t)t * dk + i] = l[i];
+        } else {
+            const double at = a[t];
+            const double qt_noise = qn[t];
+            double ksq = 0.0;
+            for (int i = 0; i < dk; ++i) ksq += kt[i] * kt[i];
+            const double lprev = l[0];
+            const double lp = lprev / (at * at + qt_noise * lprev);
+            const double g = lp * at / lprev;
+            l[0] = lp + ksq / ((double)dk * rt);
+            for (int i = 0; i < dk; ++i) {
+                double* row = eta + (size_t)i * dv;
+                for (int j = 0; j < dv; ++j)
+                    row[j] = g * row[j] + kt[i] * vt[j] / rt;
+            }
+            if (l_all) l_all[t] = l[0];
+        }
+        double* ot = o + (size_t)t * dv;
+        for (int j = 0; j < dv; ++j) ot[j] = 0.0;
+        for (int i = 0; i < dk; ++i) {
+            const double li = (cov == KLA_ORACLE_DIAG) ? l[i] : l[0];
+            const double* row = eta + (size_t)i * dv;
+            for (int j = 0; j < dv; ++j) ot[j] += qt[i] * row[j] / li;
+        }
+    }
+}
+
+/* Returns 0 on success, nonzero on bad arguments or allocation failure. */
+int kla_oracle_fwd(int B, int H, int T, int dk, int dv, int cov,
+                   const double* q, const double* k, const double* v,
+                   const double* a, const double* qn, const double* r,
+                   const double* l0, const double* eta0,
+                   double* o, double* lT, double* etaT, double* l_all,
+                   int nthreads)
+{
+    if (B < 1 || H < 1 || T < 0 || dk < 1 || dv < 1) return 1;
+    if (cov != KLA_ORACLE_DIAG && cov != KLA_ORACLE_ISO) return 1;
+    if (!q || !k || !v || !a || !qn || !r || !o) return 1;
+    const int nl = (cov == KLA_ORACLE_DIAG) ? dk : 1;
+    const long long nseq = (long long)B * H;
+    int failed = 0;
+    if (nthreads < 1) nthreads = 1;
+
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads) reduction(| : failed)
+    for (long long s = 0; s < nseq; ++s) {
+        const int h = (int)(s % H);
+        double* l = (double*)malloc(sizeof(double) * (size_t)nl);
+        double* lnew = (double*)malloc(sizeof(double) * (size_t)nl);
+        double* eta = (double*)malloc(sizeof(double) * (size_t)dk * dv);
+        if (!l || !lnew || !eta) {
+            free(l); free(lnew); free(eta);
+            failed |= 1;
+            continue;
+        }
+        for (int i = 0; i < nl; ++i) l[i] = l0 ? l0[s * nl + i] : 1.0;
+        for (size_t e = 0; e < (size_t)dk * dv; ++e)
+            eta[e] = eta0 ? eta0[(size_t)s * dk * dv + e] : 0.0;
+
+        const size_t tk = (size_t)s * T * dk, tv = (size_t)s * T * dv;
+        const double* as;
+        const double* qns;
+        if (cov == KLA_ORACLE_DIAG) {
+            as = a + tk;
+            qns = qn + (size_t)h * dk;
+        } else {
+            as = a + (size_t)s * T;
+            qns = qn + (size_t)s * T;
+        }
+        run_sequence(T, dk, dv, cov, q + tk, k + tk, v + tv, as, qns,
+                     r + (size_t)s * T, l, eta, o + tv,
+                     l_all ? l_all + (size_t)s * T * nl : NULL, lnew);
+        if (lT)
+            for (int i = 0; i < nl; ++i) lT[s * nl + i] = l[i];
+        if (etaT)
+            memcpy(etaT + (size_t)s * dk * dv, eta, sizeof(double) * (size_t)dk * dv);
+        free(l); free(lnew); free(eta);
+    }
+    return failed;
+}
+
+/*
+ * One decode step for every (b,h): the same recurrence with T = 1, state
+ * updated in place.  q,k [B,H,dk]; v,o [B,H,dv]; r [B,H]; diag: a [B,H,dk],
+ * qn [H,dk], l [B,H,dk]; iso: a, qn, l [B,H]; eta [B,H,dk,dv].
+ */
+int kla_oracle_step(int B, int H, int dk, int dv, int cov,
+                    const double* q, const double* k, const double* v,
+                    const double* a, const double* qn, const double* r,
+                    double* l, double* eta, double* o, int nthreads)
+{
+    if (!l || !eta) return 1;
+    /* With T = 1 the per-sequence layouts of fwd coincide with step's. */
+    return kla_oracle_fwd(B, H, 1, dk, dv, cov, q, k, v, a, qn, r, l, eta,
+                          o, l, eta, NULL, nthreads);
+}
