@@ -1,0 +1,174 @@
+#!/usr/bin/env python3
+"""KLA forward benchmark on one MI355X.
+
+One step = one klaFwd over the whole batch of the workload (all heads, all
+tokens), inputs resident in HBM.  Default workload: the LM layer at
+1.3B-like width, B=8 H=16 T=2048 dk=dv=128, bf16 q/k/v/o, fp32 state.
+
+Prints ONE JSON line with tokens/s, the roofline of the forward kernel
+(algorithmic HBM bytes / measured kernel time against 8 TB/s), and the fp64
+oracle timed on the host cores over a bounded sample of the same workload.
+
+  python bench.py [--steps K] [--warmup W] [--workload lm_diag] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def alg_bytes(w) -> float:
+    """Algorithmic HBM bytes of one forward: each input read once, each output
+    written once (l0 = 1, eta0 = 0 are not read), no intermediate state."""
+    es = 2 if w.dtype == "bf16" else 4
+    ntok = w.B * w.H * w.T
+    if w.cov == "diag":
+        per_tok = (2 * w.dk + w.dv) * es + 4 * w.dk + 4 + w.dv * es
+        per_seq = 4 * w.dk + 4 * w.dk * w.dv
+    else:
+        per_tok = (2 * w.dk + w.dv) * es + 12 + w.dv * es
+        per_seq = 4 + 4 * w.dk * w.dv
+    return float(ntok * per_tok + w.B * w.H * per_seq)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="lm_diag")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
+                    help="target wall time of the oracle sample")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the forward shards over (b,h) with no communication, see the design notes.",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import scan_amd
+    from scan_amd import inputs as gen
+
+    w = gen.WORKLOADS[args.workload]
+    print(f"bench: workload {w}", file=sys.stderr, flush=True)
+    host = gen.make_inputs(w, seed=0)
+    names = ("q", "k", "v", "a", "qn", "r")
+    # two resident copies, alternated, so consecutive steps do not reuse the
+    # 256 MB last-level cache
+    sets = [[host[n].to("cuda") for n in names]]
+    sets.append([t.clone() for t in sets[0]])
+    B, H, T, dk, dv = w.B, w.H, w.T, w.dk, w.dv
+    outs = []
+    for _ in range(2):
+        o = torch.empty(B, H, T, dv, dtype=sets[0][2].dtype, device="cuda")
+        lT = torch.empty((B, H, dk) if w.cov == "diag" else (B, H), device="cuda")
+        etaT = torch.empty(B, H, dk, dv, device="cuda")
+        outs.append((o, lT, etaT))
+
+    def step(i):
+        s = sets[i % 2]
+        o, lT, etaT = outs[i % 2]
+        scan_amd.fwd(*s, cov=w.cov, o=o, lT=lT, etaT=etaT)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    per = []
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        e_a = torch.cuda.Event(enable_timing=True)
+        e_b = torch.cuda.Event(enable_timing=True)
+        e_a.record(stream)
+        step(i)
+        e_b.record(stream)
+        per.append((e_a, e_b))
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    total_ms = ev0.elapsed_time(ev1)
+    ms_per_step = total_ms / args.steps
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in per]))
+
+    tokens = B * T
+    value = tokens / (ms_per_step / 1e3)
+    nbytes = alg_bytes(w)
+    achieved = nbytes / (kern_ms / 1e3) / 1e9
+    print(f"bench: {ms_per_step:.4f} ms/step (kernel {kern_ms:.4f} ms), {achieved:.1f} GB/s "
+          f"algorithmic, wall {wall:.3f}s", file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        threads = oracle.default_threads()
+        # calibrate on one sequence, then size the sample to ~cpu-seconds
+        one = {n: host[n][:1, :1] for n in names}
+        if w.cov == "diag":
+            one["qn"] = host["qn"][:1]
+        t0 = time.perf_counter()
+        oracle.fwd(*(one[n] for n in names), cov=oracle.DIAG if w.cov == "diag" else oracle.ISO,
+                   nthreads=1)
+        t_one = time.perf_counter() - t0
+        nseq_total = B * H
+        nseq = int(max(threads, min(nseq_total, args.cpu_seconds * threads / max(t_one, 1e-6))))
+        nseq = max(1, min(nseq_total, nseq // H * H if nseq >= H else nseq))
+        nb = max(1, nseq // H) if nseq >= H else 1
+        nh = H if nseq >= H else nseq
+        sub = {n: host[n][:nb, :nh] for n in names}
+        if w.cov == "diag":
+            sub["qn"] = host["qn"][:nh]
+        t0 = time.perf_counter()
+        oracle.fwd(*(sub[n] for n in names), cov=oracle.DIAG if w.cov == "diag" else oracle.ISO,
+                   nthreads=threads)
+        t_cpu = time.perf_counter() - t0
+        seqs = nb * nh
+        cpu_tok_s = seqs * T / H / t_cpu   # token-heads/s over H heads = tokens/s
+        cpu = {"value": cpu_tok_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "sample": f"{seqs} of {nseq_total} (b,h) sequences at full T={T} "
+                         f"({nb}x{nh}), fp64 sequential recurrence, {t_cpu:.1f}s"}
+
+    line = {
+        "metric": "KLA layer fwd tokens/s at B·T, H×d; % of HBM/MFMA roofline",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "H": H, "T": T, "dk": dk, "dv": dv,
+                   "cov": w.cov, "global_batch": B, "seq_len": T, "parallelism": "none"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": f"kla_fwd_{w.cov}_kernel", "alg_bytes": nbytes,
+                     "kernel_ms": kern_ms},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,137 @@
+/*
+ * kla.h -- C ABI of the MI355X (gfx950) Kalman Linear Attention forward path.
+ *
+ * Method sources (cited by title and section):
+ *  [KLA]  "Kalman Linear Attention: Parallel Bayesian Filtering For Efficient
+ *         Language Modelling and State Tracking" -- gist.science explainer,
+ *         technical summary (技術要約) > method (手法) §1 probabilistic
+ *         formulation, §2 Mobius parallelisation, §3 uncertainty gating,
+ *         §4 architecture (drop-in replacement for an SSM / attention layer).
+ *  [KDN]  "Kalman Delta Networks: Uncertainty-aware Associative Memory" --
+ *         abstract: diagonal and isotropic scan-compatible variants and
+ *         constant-memory decoding.
+ *
+ * The operation (per batch b, head h).  The memory is the information form of
+ * a Kalman filter over a linear-Gaussian state-space model ([KLA] method §1):
+ * OU decay a_t, process noise qn, observation of the value through the key
+ * k_t with noise r_t, readout of the posterior mean through the query q_t.
+ * The pages fix the Mobius form of the precision map ([KLA] method §2) but not
+ * its coefficients; this library computes, for every key dim i,
+ *
+ *   lp          = l_{t-1}[i] / (a_t[i]^2 + qn[i] * l_{t-1}[i])
+ *   l_t[i]      = lp + k_t[i]^2 / r_t
+ *   eta_t[i,:]  = (lp * a_t[i] / l_{t-1}[i]) * eta_{t-1}[i,:] + k_t[i] v_t / r_t
+ *   o_t         = sum_i q_t[i] * eta_t[i,:] / l_t[i]
+ *
+ * i.e. the precision map l -> ((1 + b qn) l + b a^2) / (qn l + a^2) with
+ * b = k^2 / r, composed associatively as 2x2 projective matrices.  In the
+ * isotropic variant ([KDN]) l is one scalar per head, a_t and qn_t are per
+ * token, and the precision increment is b_t = sum_i k_t[i]^2 / (d_k r_t);
+ * the information rows are updated as above with the scalar gate.
+ *
+ * Layouts: dense, row-major, head-major ("BHTD"):
+ *   q, k        [B,H,T,dk]      dtype (fp32 or bf16)
+ *   v, o        [B,H,T,dv]      dtype
+ *   r           [B,H,T]         fp32
+ *   diag:  a [B,H,T,dk]  qn [H,dk]    l0,lT [B,H,dk]   fp32
+ *   iso:   a [B,H,T]     qn [B,H,T]   l0,lT [B,H]      fp32
+ *   eta0, etaT  [B,H,dk,dv]     fp32
+ *
+ * Ownership and execution: every pointer is a DEVICE pointer owned by the
+ * caller.  The library never allocates, frees or synchronises device
+ * memory; all work is enqueued asynchronously on the given HIP stream
+ * (NULL = the default stream).  Outputs are fully overwritten.  The library
+ * holds no mutable global state and is reentrant.
+ *
+ * Errors: argument errors are detected on the host and returned before any
+ * HIP call, with nothing written.  A failing launch returns KLA_ERR_HIP.
+ * No C++ exception crosses this interface.
+ *
+ * Numerical preconditions (documented, not checked on the device):
+ * r > 0, l0 > 0, 0 < a <= 1, qn >= 0, a^2 + qn * l > 0.  Otherwise the
+ * results are undefined (they propagate as NaN/Inf).
+ */
+#ifndef KLA_H
+#define KLA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KLA_OK = 0,
+    KLA_ERR_NULL = 1,        /* a required pointer is NULL                         */
+    KLA_ERR_SHAPE = 2,       /* a dimension is negative or the dims pointer is bad */
+    KLA_ERR_UNSUPPORTED = 3, /* (dk, dv, dtype, cov) combination not built          */
+    KLA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                    */
+    KLA_ERR_WORKSPACE = 5,   /* workspace smaller than klaFwdWorkspaceBytes()       */
+    KLA_ERR_HIP = 6,         /* the HIP runtime reported an error at launch         */
+    KLA_ERR_INTERNAL = 7,    /* unexpected internal condition                       */
+    KLA_ERR_ALIAS = 8        /* an output overlaps an input it must not overlap     */
+} klaStatus;
+
+typedef enum { KLA_F32 = 0, KLA_BF16 = 1 } klaDtype; /* dtype of q, k, v and o */
+typedef enum { KLA_DIAG = 0, KLA_ISO = 1 } klaCov;   /* precision structure   */
+
+typedef struct {
+    int B, H, T;  /* batch, heads, tokens (T is ignored by klaStep)          */
+    int dk, dv;   /* key and value head dims                                 */
+    int dtype;    /* klaDtype                                                */
+    int cov;      /* klaCov                                                  */
+} klaDims;
+
+/* Whether klaFwd/klaStep accept these dims (dk, dv, dtype, cov). */
+int klaIsSupported(const klaDims* d);
+
+/*
+ * Device workspace (bytes) that klaFwd needs for these dims; 0 means none
+ * (workspace may then be NULL).  Returns 0 for unsupported dims too.
+ * Long sequences are split across workgroups and their carries pass through
+ * the workspace.
+ */
+size_t klaFwdWorkspaceBytes(const klaDims* d);
+
+/*
+ * Forward pass over T tokens for all (b,h) ([KLA] method §1-§3; [KDN]).
+ * In:  q, k, v, a, qnoise, r as laid out above; l0, eta0 the filter state
+ *      before the first token (l0 == NULL means l0 = 1; eta0 == NULL means
+ *      eta0 = 0; they are independent).
+ * Out: o [B,H,T,dv] (o_t uses the posterior after token t); lT, etaT the
+ *      state after the last token (either may be NULL to skip it).
+ * T == 0 (or B*H == 0) is valid: o is empty and lT/etaT receive l0/eta0;
+ * the token inputs (q, k, v, a, qnoise, r, o) may then be NULL.
+ * Every non-NULL pointer must be 16-byte aligned (KLA_ERR_ALIGN).
+ * Aliasing: o must not overlap any input; lT/etaT must not overlap l0/eta0
+ * (KLA_ERR_ALIAS).  workspace must hold klaFwdWorkspaceBytes(d) bytes and
+ * must not be used by another call that runs at the same time.
+ */
+klaStatus klaFwd(const klaDims* d,
+                 const void* q, const void* k, const void* v,
+                 const float* a, const float* qnoise, const float* r,
+                 const float* l0, const float* eta0,
+                 void* o, float* lT, float* etaT,
+                 void* workspace, size_t workspaceBytes, void* hipStream);
+
+/*
+ * One decode step for every (b,h) (the same recurrence with T = 1;
+ * constant-memory decoding, [KDN]).  State is updated in place.
+ * Layouts: q, k [B,H,dk]; v, o [B,H,dv]; r [B,H];
+ *          diag: a [B,H,dk], qnoise [H,dk], l [B,H,dk];
+ *          iso:  a, qnoise, l [B,H];  eta [B,H,dk,dv] (all fp32 except q,k,v,o).
+ * d->T is ignored.  o must not overlap the other arguments.
+ */
+klaStatus klaStep(const klaDims* d,
+                  const void* q, const void* k, const void* v,
+                  const float* a, const float* qnoise, const float* r,
+                  float* l, float* eta, void* o, void* hipStream);
+
+/* Static, human-readable description of a status code (never NULL). */
+const char* klaStatusString(klaStatus s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KLA_H */

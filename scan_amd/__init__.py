@@ -1,0 +1,178 @@
+"""Thin Python binding of the gfx950 KLA forward library (include/kla.h).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+libkla.so.  PyTorch provides device memory and the current HIP stream.  There
+is no CPU fallback: if the library is missing or no GPU is present the calls
+raise.
+
+Low level (same names and arguments as the C ABI, raw device pointers):
+    klaFwd, klaStep, klaFwdWorkspaceBytes, klaIsSupported, klaStatusString
+Convenience (torch tensors in, torch tensors out):
+    fwd(q, k, v, a, qn, r, l0=None, eta0=None, cov="diag") -> (o, lT, etaT)
+    step(q, k, v, a, qn, r, l, eta, cov="diag") -> o      (l, eta updated in place)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["klaFwd", "klaStep", "klaFwdWorkspaceBytes", "klaIsSupported", "klaStatusString",
+           "KlaDims", "KlaError", "fwd", "step", "lib_path", "load"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libkla.so")
+
+KLA_OK = 0
+KLA_F32, KLA_BF16 = 0, 1
+KLA_DIAG, KLA_ISO = 0, 1
+STATUS_NAMES = {0: "KLA_OK", 1: "KLA_ERR_NULL", 2: "KLA_ERR_SHAPE", 3: "KLA_ERR_UNSUPPORTED",
+                4: "KLA_ERR_ALIGN", 5: "KLA_ERR_WORKSPACE", 6: "KLA_ERR_HIP",
+                7: "KLA_ERR_INTERNAL", 8: "KLA_ERR_ALIAS"}
+
+
+class KlaDims(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("H", ctypes.c_int), ("T", ctypes.c_int),
+                ("dk", ctypes.c_int), ("dv", ctypes.c_int),
+                ("dtype", ctypes.c_int), ("cov", ctypes.c_int)]
+
+
+class KlaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what} failed: {klaStatusString(status)}")
+
+
+_lib = None
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libkla.so (built in-tree by scan_amd.build / __graft_entry__.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"HIP library {_LIB_PATH} is not built; run __graft_entry__.build()")
+    try:  # share torch's HIP runtime (same soname) when torch is present
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, fp, sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t
+    dp = ctypes.POINTER(KlaDims)
+    lib.klaIsSupported.argtypes = [dp]
+    lib.klaIsSupported.restype = ctypes.c_int
+    lib.klaFwdWorkspaceBytes.argtypes = [dp]
+    lib.klaFwdWorkspaceBytes.restype = sz
+    lib.klaFwd.argtypes = [dp, vp, vp, vp, fp, fp, fp, fp, fp, vp, fp, fp, vp, sz, vp]
+    lib.klaFwd.restype = ctypes.c_int
+    lib.klaStep.argtypes = [dp, vp, vp, vp, fp, fp, fp, fp, fp, vp, vp]
+    lib.klaStep.restype = ctypes.c_int
+    lib.klaStatusString.argtypes = [ctypes.c_int]
+    lib.klaStatusString.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+# ------------------------------------------------------------------ C ABI
+
+def klaIsSupported(dims: KlaDims) -> bool:
+    return bool(load().klaIsSupported(ctypes.byref(dims)))
+
+
+def klaFwdWorkspaceBytes(dims: KlaDims) -> int:
+    return int(load().klaFwdWorkspaceBytes(ctypes.byref(dims)))
+
+
+def klaFwd(dims, q, k, v, a, qnoise, r, l0, eta0, o, lT, etaT, workspace, workspaceBytes,
+           stream) -> int:
+    """Raw call: pointer arguments are ints (device addresses) or None."""
+    return int(load().klaFwd(ctypes.byref(dims), q, k, v, a, qnoise, r, l0, eta0, o, lT, etaT,
+                             workspace, workspaceBytes, stream))
+
+
+def klaStep(dims, q, k, v, a, qnoise, r, l, eta, o, stream) -> int:
+    return int(load().klaStep(ctypes.byref(dims), q, k, v, a, qnoise, r, l, eta, o, stream))
+
+
+def klaStatusString(status: int) -> str:
+    try:
+        return load().klaStatusString(int(status)).decode()
+    except RuntimeError:
+        return STATUS_NAMES.get(int(status), f"status {status}")
+
+
+# ------------------------------------------------------------------ torch helpers
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return KLA_BF16
+    if t.dtype == torch.float32:
+        return KLA_F32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _check_device(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("all tensors must be contiguous device tensors")
+
+
+def _stream():
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def fwd(q, k, v, a, qn, r, l0=None, eta0=None, cov: str = "diag", o=None, lT=None, etaT=None,
+        want_state: bool = True):
+    """KLA forward on the current stream.  Returns (o, lT, etaT) as device tensors.
+
+    q,k [B,H,T,dk], v [B,H,T,dv] (bf16 or fp32); a, qn, r, l0, eta0 fp32 in the
+    layouts of include/kla.h.  Outputs are allocated unless passed in.
+    """
+    import torch
+    _check_device(q, k, v, a, qn, r, l0, eta0)
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    c = KLA_DIAG if cov == "diag" else KLA_ISO
+    dims = KlaDims(B, H, T, dk, dv, _dtype_code(q), c)
+    dev = q.device
+    if o is None:
+        o = torch.empty(B, H, T, dv, dtype=v.dtype, device=dev)
+    if want_state:
+        if lT is None:
+            lT = torch.empty((B, H, dk) if c == KLA_DIAG else (B, H), dtype=torch.float32, device=dev)
+        if etaT is None:
+            etaT = torch.empty(B, H, dk, dv, dtype=torch.float32, device=dev)
+    ws_bytes = klaFwdWorkspaceBytes(dims)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    st = klaFwd(dims, _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(qn), _ptr(r), _ptr(l0), _ptr(eta0),
+                _ptr(o), _ptr(lT), _ptr(etaT), _ptr(ws), ws_bytes, _stream())
+    if st != KLA_OK:
+        raise KlaError(st, "klaFwd")
+    return o, lT, etaT
+
+
+def step(q, k, v, a, qn, r, l, eta, cov: str = "diag", o=None):
+    """One decode step on the current stream; l and eta are updated in place."""
+    import torch
+    _check_device(q, k, v, a, qn, r, l, eta)
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    c = KLA_DIAG if cov == "diag" else KLA_ISO
+    dims = KlaDims(B, H, 1, dk, dv, _dtype_code(q), c)
+    if o is None:
+        o = torch.empty(B, H, dv, dtype=v.dtype, device=q.device)
+    st = klaStep(dims, _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(qn), _ptr(r), _ptr(l), _ptr(eta),
+                 _ptr(o), _stream())
+    if st != KLA_OK:
+        raise KlaError(st, "klaStep")
+    return o

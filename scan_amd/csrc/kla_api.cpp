@@ -1,0 +1,176 @@
+// kla_api.cpp -- C-ABI front end of the KLA forward library (see include/kla.h).
+//
+// Validates every argument on the host, before any HIP call, then enqueues
+// the gfx950 kernels on the caller's stream.  Nothing here allocates device
+// memory or synchronises.
+#include "kla.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include "kla_internal.h"
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Span {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+Span span(const void* p, size_t bytes) { return Span{(uintptr_t)p, (uintptr_t)p + bytes}; }
+
+bool overlap(Span a, Span b) {
+    if (a.lo == a.hi || b.lo == b.hi || a.lo == 0 || b.lo == 0) return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+bool dims_ok(const klaDims* d) {
+    return d->B >= 0 && d->H >= 0 && d->T >= 0 && d->dk >= 1 && d->dv >= 1;
+}
+
+bool kinds_ok(const klaDims* d) {
+    return (d->dtype == KLA_F32 || d->dtype == KLA_BF16) && (d->cov == KLA_DIAG || d->cov == KLA_ISO);
+}
+
+bool supported(const klaDims* d) {
+    if (!kinds_ok(d)) return false;
+    return d->cov == KLA_DIAG ? kla::fwd_diag_supported(d->dk, d->dv, d->dtype)
+                              : kla::fwd_iso_supported(d->dk, d->dv, d->dtype);
+}
+
+int env_vtiles() {
+    const char* s = getenv("KLA_FWD_VTILES");
+    if (!s || !*s) return 0;
+    return atoi(s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int klaIsSupported(const klaDims* d) {
+    if (!d || !dims_ok(d)) return 0;
+    return supported(d) && kla::step_supported(d->dk, d->dv, d->dtype, d->cov) ? 1 : 0;
+}
+
+size_t klaFwdWorkspaceBytes(const klaDims* d) {
+    (void)d;
+    return 0;  // every supported shape runs without a workspace
+}
+
+klaStatus klaFwd(const klaDims* d, const void* q, const void* k, const void* v, const float* a,
+                 const float* qnoise, const float* r, const float* l0, const float* eta0, void* o,
+                 float* lT, float* etaT, void* workspace, size_t workspaceBytes, void* hipStream) {
+    if (!d) return KLA_ERR_NULL;
+    if (!dims_ok(d)) return KLA_ERR_SHAPE;
+    if (!kinds_ok(d) || !supported(d)) return KLA_ERR_UNSUPPORTED;
+    const long long B = d->B, H = d->H, T = d->T, dk = d->dk, dv = d->dv;
+    const long long BH = B * H;
+    if (BH > (1LL << 30) || T > (1LL << 30)) return KLA_ERR_SHAPE;
+    const bool iso = d->cov == KLA_ISO;
+    const size_t es = d->dtype == KLA_BF16 ? 2 : 4;
+    const size_t nlt = (size_t)(iso ? BH : BH * dk);
+    const size_t neta = (size_t)(BH * dk * dv);
+
+    if (BH == 0) return KLA_OK;
+    const bool has_tokens = T > 0;
+    // With T == 0 no token input is read; only the state is passed through.
+    if (has_tokens && (!q || !k || !v || !a || !qnoise || !r || !o)) return KLA_ERR_NULL;
+
+    const void* big[] = {q, k, v, a, o, eta0, etaT, qnoise, r, l0, lT};
+    for (const void* p : big)
+        if (p && !aligned16(p)) return KLA_ERR_ALIGN;
+
+    const size_t wneed = klaFwdWorkspaceBytes(d);
+    if (wneed > 0 && (!workspace || workspaceBytes < wneed)) return KLA_ERR_WORKSPACE;
+
+    const size_t ntk = (size_t)(BH * T);
+    const Span s_o = span(o, ntk * dv * es);
+    const Span s_lT = span(lT, nlt * 4), s_etaT = span(etaT, neta * 4);
+    const Span ins[] = {span(q, ntk * dk * es), span(k, ntk * dk * es), span(v, ntk * dv * es),
+                        span(a, (iso ? ntk : ntk * dk) * 4),
+                        span(qnoise, (iso ? ntk : (size_t)(H * dk)) * 4), span(r, ntk * 4),
+                        span(l0, nlt * 4), span(eta0, neta * 4)};
+    for (const Span& s : ins) {
+        if (overlap(s_o, s) || overlap(s_lT, s) || overlap(s_etaT, s)) return KLA_ERR_ALIAS;
+    }
+    if (overlap(s_o, s_lT) || overlap(s_o, s_etaT) || overlap(s_lT, s_etaT)) return KLA_ERR_ALIAS;
+
+    kla::FwdArgs fa;
+    fa.q = q; fa.k = k; fa.v = v; fa.a = a; fa.qn = qnoise; fa.r = r;
+    fa.l0 = l0; fa.eta0 = eta0; fa.o = o; fa.lT = lT; fa.etaT = etaT;
+    fa.B = (int)B; fa.H = (int)H; fa.T = (int)T; fa.dk = (int)dk; fa.dv = (int)dv;
+    hipStream_t st = (hipStream_t)hipStream;
+
+    hipError_t e;
+    if (!has_tokens) {
+        fa.n_vtiles = 1;
+        e = kla::launch_fwd_empty(fa, iso ? 1 : 0, st);
+    } else {
+        const int nvt_env = env_vtiles();
+        if (iso) {
+            fa.n_vtiles = nvt_env > 0 ? nvt_env : kla::fwd_iso_vtiles(fa.B, fa.H, fa.dk);
+            if (fa.dv % fa.n_vtiles) return KLA_ERR_UNSUPPORTED;
+            e = kla::launch_fwd_iso(fa, d->dtype, st);
+        } else {
+            fa.n_vtiles = nvt_env > 0 ? nvt_env : kla::fwd_diag_vtiles(fa.B, fa.H, fa.T, fa.dk, fa.dv);
+            e = kla::launch_fwd_diag(fa, d->dtype, st);
+        }
+        if (e == hipErrorInvalidValue) return KLA_ERR_UNSUPPORTED;
+    }
+    return e == hipSuccess ? KLA_OK : KLA_ERR_HIP;
+}
+
+klaStatus klaStep(const klaDims* d, const void* q, const void* k, const void* v, const float* a,
+                  const float* qnoise, const float* r, float* l, float* eta, void* o,
+                  void* hipStream) {
+    if (!d) return KLA_ERR_NULL;
+    if (d->B < 0 || d->H < 0 || d->dk < 1 || d->dv < 1) return KLA_ERR_SHAPE;
+    if (!kinds_ok(d) || !kla::step_supported(d->dk, d->dv, d->dtype, d->cov)) return KLA_ERR_UNSUPPORTED;
+    const long long BH = (long long)d->B * d->H;
+    if (BH > (1LL << 30)) return KLA_ERR_SHAPE;
+    if (BH == 0) return KLA_OK;
+    if (!q || !k || !v || !a || !qnoise || !r || !l || !eta || !o) return KLA_ERR_NULL;
+    const void* ptrs[] = {q, k, v, a, qnoise, r, l, eta, o};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return KLA_ERR_ALIGN;
+    const bool iso = d->cov == KLA_ISO;
+    const size_t es = d->dtype == KLA_BF16 ? 2 : 4;
+    const size_t nl = (size_t)(iso ? BH : BH * d->dk);
+    const Span s_o = span(o, (size_t)BH * d->dv * es);
+    const Span others[] = {span(q, (size_t)BH * d->dk * es), span(k, (size_t)BH * d->dk * es),
+                           span(v, (size_t)BH * d->dv * es), span(a, nl * 4),
+                           span(qnoise, (iso ? (size_t)BH : (size_t)d->H * d->dk) * 4),
+                           span(r, (size_t)BH * 4), span(l, nl * 4),
+                           span(eta, (size_t)BH * d->dk * d->dv * 4)};
+    for (const Span& s : others)
+        if (overlap(s_o, s)) return KLA_ERR_ALIAS;
+    if (overlap(span(l, nl * 4), span(eta, (size_t)BH * d->dk * d->dv * 4))) return KLA_ERR_ALIAS;
+
+    kla::StepArgs sa;
+    sa.q = q; sa.k = k; sa.v = v; sa.a = a; sa.qn = qnoise; sa.r = r;
+    sa.l = l; sa.eta = eta; sa.o = o;
+    sa.B = d->B; sa.H = d->H; sa.dk = d->dk; sa.dv = d->dv;
+    const hipError_t e = kla::launch_step(sa, d->dtype, d->cov, (hipStream_t)hipStream);
+    if (e == hipErrorInvalidValue) return KLA_ERR_UNSUPPORTED;
+    return e == hipSuccess ? KLA_OK : KLA_ERR_HIP;
+}
+
+const char* klaStatusString(klaStatus s) {
+    switch (s) {
+        case KLA_OK: return "KLA_OK: success";
+        case KLA_ERR_NULL: return "KLA_ERR_NULL: a required pointer is NULL";
+        case KLA_ERR_SHAPE: return "KLA_ERR_SHAPE: a dimension is negative or too large";
+        case KLA_ERR_UNSUPPORTED: return "KLA_ERR_UNSUPPORTED: (dk, dv, dtype, cov) not built";
+        case KLA_ERR_ALIGN: return "KLA_ERR_ALIGN: a pointer is not 16-byte aligned";
+        case KLA_ERR_WORKSPACE: return "KLA_ERR_WORKSPACE: workspace missing or too small";
+        case KLA_ERR_HIP: return "KLA_ERR_HIP: the HIP runtime reported a launch error";
+        case KLA_ERR_INTERNAL: return "KLA_ERR_INTERNAL: internal error";
+        case KLA_ERR_ALIAS: return "KLA_ERR_ALIAS: an output overlaps an input";
+    }
+    return "unknown klaStatus";
+}
+
+}  // extern "C"

@@ -1,0 +1,130 @@
+// kla_common.h -- gfx950 vector types and MFMA operand helpers shared by the
+// forward and decode kernels of this library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace kla {
+
+typedef __bf16 bf16;
+typedef bf16 bf16x8 __attribute__((__vector_size__(16)));
+typedef bf16 bf16x4 __attribute__((__vector_size__(8)));
+typedef bf16 bf16x2 __attribute__((__vector_size__(4)));
+typedef short s16x4 __attribute__((__vector_size__(8)));
+typedef float f32x4 __attribute__((__vector_size__(16)));
+typedef float f32x2 __attribute__((__vector_size__(8)));
+
+// A "K32 step" contracts 32 values of the shared dimension with one
+// 16x16 output tile; every lane holds 8 consecutive values of its row (A) or
+// column (B).  A "K16 step" holds 4.  Both operands of one step are loaded
+// with the same lane/slot -> k mapping, so the products pair up regardless of
+// the instruction's internal K order.  The 16x16 accumulator layout (lane l
+// holds rows 4*(l/16)+e, column l%16) equals the K16 A/B operand layout, so
+// an accumulator can feed the next product without passing through LDS.
+template <typename T>
+struct Mma;
+
+template <>
+struct Mma<bf16> {
+    typedef bf16x8 K32;
+    typedef s16x4 K16;
+    static __device__ __forceinline__ K32 ld32(const bf16* p) { return *(const bf16x8*)p; }
+    static __device__ __forceinline__ K16 ld16(const bf16* p) { return *(const s16x4*)p; }
+    static __device__ __forceinline__ f32x4 mma32(K32 a, K32 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ f32x4 mma16(K16 a, K16 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ K16 from_acc(f32x4 x) {
+        bf16x4 h = {(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
+        return __builtin_bit_cast(s16x4, h);
+    }
+};
+
+template <>
+struct Mma<float> {
+    struct K32 { f32x4 lo, hi; };
+    typedef f32x4 K16;
+    static __device__ __forceinline__ K32 ld32(const float* p) {
+        K32 r;
+        r.lo = *(const f32x4*)p;
+        r.hi = *(const f32x4*)(p + 4);
+        return r;
+    }
+    static __device__ __forceinline__ K16 ld16(const float* p) { return *(const f32x4*)p; }
+    static __device__ __forceinline__ f32x4 mma32(K32 a, K32 b, f32x4 c) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[e], b.lo[e], c, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[e], b.hi[e], c, 0, 0, 0);
+        return c;
+    }
+    static __device__ __forceinline__ f32x4 mma16(K16 a, K16 b, f32x4 c) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], c, 0, 0, 0);
+        return c;
+    }
+    static __device__ __forceinline__ K16 from_acc(f32x4 x) { return x; }
+};
+
+// Two consecutive values of the input dtype, as loaded from / stored to HBM.
+template <typename T> struct Pair;
+template <> struct Pair<bf16> {
+    typedef bf16x2 V;
+    static __device__ __forceinline__ float lo(V v) { return (float)v[0]; }
+    static __device__ __forceinline__ float hi(V v) { return (float)v[1]; }
+    static __device__ __forceinline__ V make(float a, float b) { V r = {(bf16)a, (bf16)b}; return r; }
+    static __device__ __forceinline__ V zero() { V r = {(bf16)0.f, (bf16)0.f}; return r; }
+};
+template <> struct Pair<float> {
+    typedef f32x2 V;
+    static __device__ __forceinline__ float lo(V v) { return v[0]; }
+    static __device__ __forceinline__ float hi(V v) { return v[1]; }
+    static __device__ __forceinline__ V make(float a, float b) { V r = {a, b}; return r; }
+    static __device__ __forceinline__ V zero() { V r = {0.f, 0.f}; return r; }
+};
+
+// Four consecutive values (a row fragment, an output store).
+template <typename T> struct Quad;
+template <> struct Quad<bf16> {
+    typedef bf16x4 V;
+    static __device__ __forceinline__ V make(f32x4 x) {
+        V r = {(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
+        return r;
+    }
+    static __device__ __forceinline__ f32x4 to_f32(V v) {
+        return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+    }
+    static __device__ __forceinline__ V zero() { return make(f32x4{0.f, 0.f, 0.f, 0.f}); }
+};
+template <> struct Quad<float> {
+    typedef f32x4 V;
+    static __device__ __forceinline__ V make(f32x4 x) { return x; }
+    static __device__ __forceinline__ f32x4 to_f32(V v) { return v; }
+    static __device__ __forceinline__ V zero() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+};
+
+// Eight consecutive values (16 bytes of bf16, 32 bytes of fp32).
+template <typename T> struct Oct;
+template <> struct Oct<bf16> {
+    typedef bf16x8 V;
+    static __device__ __forceinline__ float get(const V& v, int e) { return (float)v[e]; }
+    static __device__ __forceinline__ V zero() {
+        V r;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r[e] = (bf16)0.f;
+        return r;
+    }
+};
+template <> struct Oct<float> {
+    struct V { f32x4 lo, hi; };
+    static __device__ __forceinline__ float get(const V& v, int e) { return e < 4 ? v.lo[e] : v.hi[e - 4]; }
+    static __device__ __forceinline__ V zero() { V r; r.lo = f32x4{0.f, 0.f, 0.f, 0.f}; r.hi = r.lo; return r; }
+};
+
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+}  // namespace kla

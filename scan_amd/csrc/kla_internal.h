@@ -1,0 +1,58 @@
+// kla_internal.h -- launch descriptors shared by the C-ABI front end
+// (kla_api.cpp) and the gfx950 kernels.  Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kla {
+
+// Arguments of one forward launch.  Every pointer is a device pointer.
+struct FwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* a;
+    const float* qn;
+    const float* r;
+    const float* l0;    // may be null (l0 = 1)
+    const float* eta0;  // may be null (eta0 = 0)
+    void* o;
+    float* lT;          // may be null
+    float* etaT;        // may be null
+    int B, H, T, dk, dv;
+    int n_vtiles;       // workgroups per (b,h) along the value dim
+};
+
+struct StepArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* a;
+    const float* qn;
+    const float* r;
+    float* l;
+    float* eta;
+    void* o;
+    int B, H, dk, dv;
+};
+
+enum Dt { DT_F32 = 0, DT_BF16 = 1 };
+
+// Each returns hipSuccess or the launch error.  Shapes were validated by the
+// caller; the functions return hipErrorInvalidValue for a (dk, dv, dtype)
+// combination they were not instantiated for.
+hipError_t launch_fwd_diag(const FwdArgs& a, int dtype, hipStream_t s);
+hipError_t launch_fwd_iso(const FwdArgs& a, int dtype, hipStream_t s);
+hipError_t launch_step(const StepArgs& a, int dtype, int cov, hipStream_t s);
+hipError_t launch_fwd_empty(const FwdArgs& a, int cov, hipStream_t s);
+
+bool fwd_diag_supported(int dk, int dv, int dtype);
+bool fwd_iso_supported(int dk, int dv, int dtype);
+bool step_supported(int dk, int dv, int dtype, int cov);
+// Value-dim tiles per (b,h) (workgroups per sequence) the forward uses.
+int fwd_diag_vtiles(int B, int H, int T, int dk, int dv);
+int fwd_iso_vtiles(int B, int H, int dk);
+
+}  // namespace kla

@@ -1,0 +1,152 @@
+"""CPU-side contract of the C ABI (no GPU needed, no compute call).
+
+Checks that libkla.so loads, exports every function include/kla.h declares,
+and that every host-detectable argument error is returned before any HIP
+call.  Pointer arguments here are fake (never dereferenced): validation
+rejects the call before anything touches them.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import scan_amd
+from scan_amd import KlaDims
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kla.h")
+
+OK, NULL, SHAPE, UNSUP, ALIGN, WS, HIP, INTERNAL, ALIAS = range(9)
+F32, BF16 = 0, 1
+DIAG, ISO = 0, 1
+
+# fake, well separated, 256-byte aligned "device" addresses
+BASE = 1 << 40
+
+
+def addr(i):
+    return BASE + i * (1 << 32)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\S[^\n(]*?\b(kla[A-Z]\w*)\s*\(", text, re.M)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = scan_amd.load()
+    names = declared_functions()
+    assert {"klaFwd", "klaStep", "klaFwdWorkspaceBytes", "klaStatusString",
+            "klaIsSupported"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", scan_amd.lib_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (kla\w+)$", out, re.M))
+    assert set(names) <= exported
+
+
+def test_status_strings_cover_every_code():
+    seen = set()
+    for s in range(9):
+        txt = scan_amd.klaStatusString(s)
+        assert txt.startswith(scan_amd.STATUS_NAMES[s])
+        seen.add(txt)
+    assert len(seen) == 9
+    assert "unknown" in scan_amd.klaStatusString(99)
+
+
+@pytest.mark.parametrize("dk", [16, 32, 64, 128])
+@pytest.mark.parametrize("dtype", [F32, BF16])
+@pytest.mark.parametrize("cov", [DIAG, ISO])
+def test_supported_shapes(dk, dtype, cov):
+    assert scan_amd.klaIsSupported(KlaDims(2, 3, 100, dk, dk, dtype, cov))
+    assert scan_amd.klaFwdWorkspaceBytes(KlaDims(2, 3, 100, dk, dk, dtype, cov)) == 0
+
+
+@pytest.mark.parametrize("dims", [(1, 1, 8, 48, 48), (1, 1, 8, 256, 256), (1, 1, 8, 64, 32),
+                                  (1, 1, 8, 8, 8)])
+def test_unsupported_shapes(dims):
+    d = KlaDims(*dims, F32, DIAG)
+    assert not scan_amd.klaIsSupported(d)
+    assert fwd_call(d) == UNSUP
+
+
+def fwd_call(d, **over):
+    args = dict(q=addr(1), k=addr(2), v=addr(3), a=addr(4), qnoise=addr(5), r=addr(6),
+                l0=addr(7), eta0=addr(8), o=addr(9), lT=addr(10), etaT=addr(11), workspace=None,
+                workspaceBytes=0, stream=None)
+    args.update(over)
+    return scan_amd.klaFwd(d, **args)
+
+
+def step_call(d, **over):
+    args = dict(q=addr(1), k=addr(2), v=addr(3), a=addr(4), qnoise=addr(5), r=addr(6),
+                l=addr(7), eta=addr(8), o=addr(9), stream=None)
+    args.update(over)
+    return scan_amd.klaStep(d, **args)
+
+
+def test_null_dims():
+    lib = scan_amd.load()
+    assert lib.klaFwd(None, *([None] * 12), 0, None) == NULL
+    assert lib.klaStep(None, *([None] * 10)) == NULL
+    assert lib.klaIsSupported(None) == 0
+
+
+@pytest.mark.parametrize("field", ["B", "H", "T", "dk", "dv"])
+def test_negative_dims(field):
+    d = KlaDims(1, 2, 16, 16, 16, F32, DIAG)
+    setattr(d, field, -1)
+    assert fwd_call(d) == SHAPE
+
+
+def test_bad_enums():
+    assert fwd_call(KlaDims(1, 2, 16, 16, 16, 7, DIAG)) == UNSUP
+    assert fwd_call(KlaDims(1, 2, 16, 16, 16, F32, 5)) == UNSUP
+    assert step_call(KlaDims(1, 2, 1, 16, 16, F32, 5)) == UNSUP
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "a", "qnoise", "r", "o"])
+def test_required_pointers(name):
+    d = KlaDims(1, 2, 16, 16, 16, F32, DIAG)
+    assert fwd_call(d, **{name: None}) == NULL
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "a", "qnoise", "r", "l", "eta", "o"])
+def test_step_required_pointers(name):
+    d = KlaDims(4, 2, 1, 64, 64, BF16, ISO)
+    assert step_call(d, **{name: None}) == NULL
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "a", "o", "eta0", "etaT", "l0", "lT", "r"])
+def test_misaligned(name):
+    d = KlaDims(1, 2, 16, 16, 16, F32, DIAG)
+    assert fwd_call(d, **{name: addr(20) + 4}) == ALIGN
+
+
+def test_empty_batch_is_a_no_op():
+    # B*H == 0: nothing to do, nothing is dereferenced, no HIP call
+    assert fwd_call(KlaDims(0, 4, 16, 16, 16, F32, DIAG)) == OK
+    assert step_call(KlaDims(3, 0, 1, 16, 16, F32, DIAG)) == OK
+
+
+def test_output_aliasing_rejected():
+    d = KlaDims(1, 2, 16, 16, 16, F32, DIAG)
+    assert fwd_call(d, o=addr(1)) == ALIAS            # o over q
+    assert fwd_call(d, lT=addr(7)) == ALIAS           # lT over l0
+    assert fwd_call(d, etaT=addr(8) + 16) == ALIAS    # etaT inside eta0
+    assert fwd_call(d, lT=addr(9)) == ALIAS           # lT over o
+    ds = KlaDims(1, 2, 1, 16, 16, F32, DIAG)
+    assert step_call(ds, o=addr(8)) == ALIAS          # o over eta
+    assert step_call(ds, l=addr(8)) == ALIAS          # l over eta
+
+
+def test_header_documents_every_entry_point():
+    text = open(HEADER).read()
+    for n in declared_functions():
+        # every declaration is preceded by a comment block
+        idx = text.index(n + "(")
+        assert "*/" in text[max(0, idx - 600):idx], n

@@ -1,0 +1,223 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Every input comes from scan_amd.inputs (seeded); the oracle sees the stored
+values upcast to fp64.  Small cases compare every output element; the
+full-size workloads run in the benchmark's launch configuration and compare
+sampled (b,h) sequences that the oracle computes one by one.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import scan_amd
+from scan_amd import inputs as gen
+from tests.gpu_util import assert_parity, compare, run_hip, run_oracle, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _print_case(*args):
+    print("CASE", *args, flush=True)
+
+
+# ------------------------------------------------------------------ small, full compare
+
+@pytest.mark.parametrize("name,over", [
+    ("small_diag", {}),
+    ("lm_diag", dict(B=1, H=2, T=300)),
+    ("long_diag", dict(B=1, H=2, T=1100)),
+    ("symbols_diag", dict(B=16, H=4)),
+    ("iso", dict(B=1, H=3, T=700)),
+])
+def test_parity_small(name, over):
+    _print_case(name, over)
+    inp = gen.make_inputs(name, seed=0, **over)
+    w = inp["workload"]
+    hip = run_hip(inp, w.cov)
+    ref = run_oracle(inp, w.cov)
+    errs = compare(hip, ref)
+    print(name, errs)
+    assert_parity(errs, w.dtype, name)
+
+
+@pytest.mark.parametrize("cov", ["diag", "iso"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
+@pytest.mark.parametrize("T", [1, 15, 17, 33, 100])
+def test_parity_edges_with_state(cov, dtype, d, T):
+    """Ragged lengths, every head dim, both dtypes, non-trivial l0/eta0."""
+    _print_case(cov, dtype, d, T)
+    base = "small_diag" if cov == "diag" else "iso"
+    inp = gen.make_inputs(base, seed=T + d, B=2, H=2, T=T, dk=d, dv=d, dtype=dtype)
+    st = gen.make_state(inp["workload"], seed=7)
+    hip = run_hip(inp, cov, st["l0"], st["eta0"])
+    ref = run_oracle(inp, cov, st["l0"], st["eta0"])
+    assert_parity(compare(hip, ref), dtype, f"{cov} {dtype} d={d} T={T}")
+
+
+@pytest.mark.parametrize("cov", ["diag", "iso"])
+def test_empty_sequence_returns_state(cov):
+    _print_case("empty", cov)
+    inp = gen.make_inputs("small_diag" if cov == "diag" else "iso", seed=1, B=2, H=2, T=0,
+                          dk=32, dv=32)
+    st = gen.make_state(inp["workload"], seed=3)
+    hip = run_hip(inp, cov, st["l0"], st["eta0"])
+    assert hip["o"].shape[2] == 0
+    assert np.array_equal(hip["lT"], st["l0"].double().numpy())
+    assert np.array_equal(hip["etaT"], st["eta0"].double().numpy())
+
+
+# ------------------------------------------------------------------ full size, sampled
+
+SAMPLES = {
+    "lm_diag": [(0, 0), (3, 7), (7, 15)],
+    "long_diag": [(0, 0), (0, 9)],
+    "iso": [(0, 0), (2, 17), (3, 31)],
+}
+
+
+@pytest.mark.parametrize("name", ["lm_diag", "long_diag", "iso"])
+def test_parity_full_size_sampled(name):
+    _print_case("full", name)
+    inp = gen.make_inputs(name, seed=0)
+    w = inp["workload"]
+    hip = run_hip(inp, w.cov)
+    sel = SAMPLES[name]
+    ref = run_oracle(inp, w.cov, sel=sel)
+    sub = {k: np.stack([hip[k][b, h] for b, h in sel]) for k in hip}
+    errs = compare(sub, ref, nlead=1)
+    print(name, errs)
+    assert_parity(errs, w.dtype, name)
+    for k in hip:
+        assert np.all(np.isfinite(hip[k])), k
+
+
+def test_parity_symbols_full():
+    _print_case("full symbols_diag")
+    inp = gen.make_inputs("symbols_diag", seed=0)
+    hip = run_hip(inp, "diag")
+    ref = run_oracle(inp, "diag")
+    errs = compare(hip, ref)
+    print("symbols_diag", errs)
+    assert_parity(errs, "f32", "symbols_diag")
+
+
+# ------------------------------------------------------------------ properties
+
+@pytest.mark.parametrize("cov", ["diag", "iso"])
+def test_split_handoff_on_device(cov):
+    _print_case("handoff", cov)
+    name = "lm_diag" if cov == "diag" else "iso"
+    inp = gen.make_inputs(name, seed=5, B=2, H=2, T=257)
+    dev = {k: to_dev(v) for k, v in inp.items() if isinstance(v, torch.Tensor)}
+    o, lT, etaT = scan_amd.fwd(dev["q"], dev["k"], dev["v"], dev["a"], dev["qn"], dev["r"], cov=cov)
+    T1 = 100
+    tsl = lambda x, a, b: x[:, :, a:b].contiguous()
+    qn1 = tsl(dev["qn"], 0, T1) if cov == "iso" else dev["qn"]
+    qn2 = tsl(dev["qn"], T1, 257) if cov == "iso" else dev["qn"]
+    o1, l1, e1 = scan_amd.fwd(*(tsl(dev[n], 0, T1) for n in ("q", "k", "v", "a")), qn1,
+                              tsl(dev["r"], 0, T1), cov=cov)
+    o2, l2, e2 = scan_amd.fwd(*(tsl(dev[n], T1, 257) for n in ("q", "k", "v", "a")), qn2,
+                              tsl(dev["r"], T1, 257), l1, e1, cov=cov)
+    torch.cuda.synchronize()
+    tol = 2e-2
+    full = o.float()
+    cat = torch.cat([o1, o2], dim=2).float()
+    assert float((cat - full).abs().max() / full.abs().max()) < tol
+    assert float(((l2 - lT).abs() / lT).max()) < 1e-5
+    assert float((e2 - etaT).abs().max() / etaT.abs().max()) < tol
+
+
+@pytest.mark.parametrize("cov", ["diag", "iso"])
+def test_steps_match_forward(cov):
+    _print_case("steps", cov)
+    name = "lm_diag" if cov == "diag" else "iso"
+    inp = gen.make_inputs(name, seed=9, B=2, H=3, T=20, dk=64, dv=64, dtype="f32")
+    dev = {k: to_dev(v) for k, v in inp.items() if isinstance(v, torch.Tensor)}
+    o, lT, etaT = scan_amd.fwd(dev["q"], dev["k"], dev["v"], dev["a"], dev["qn"], dev["r"], cov=cov)
+    B, H = 2, 3
+    l = torch.ones((B, H, 64) if cov == "diag" else (B, H), device="cuda")
+    eta = torch.zeros(B, H, 64, 64, device="cuda")
+    for t in range(20):
+        sl = lambda x: x[:, :, t].contiguous()
+        ot = scan_amd.step(sl(dev["q"]), sl(dev["k"]), sl(dev["v"]), sl(dev["a"]),
+                           dev["qn"] if cov == "diag" else sl(dev["qn"]), sl(dev["r"]), l, eta,
+                           cov=cov)
+        assert float((ot - o[:, :, t]).abs().max() / o[:, :, t].abs().max()) < 1e-4
+    assert float(((l - lT).abs() / lT).max()) < 1e-5
+    assert float((eta - etaT).abs().max() / etaT.abs().max()) < 1e-4
+
+
+def test_decode_full_batch_sampled():
+    """iso decode at B=256, H=32: 128-token prefix via klaFwd, 64 klaStep tokens."""
+    _print_case("decode")
+    w = gen.DECODE
+    pre = gen.make_inputs(w, seed=1)
+    stp = gen.make_inputs(w, seed=2, T=gen.DECODE_STEPS)
+    dp = {k: to_dev(v) for k, v in pre.items() if isinstance(v, torch.Tensor)}
+    ds = {k: to_dev(v) for k, v in stp.items() if isinstance(v, torch.Tensor)}
+    _, l, eta = scan_amd.fwd(dp["q"], dp["k"], dp["v"], dp["a"], dp["qn"], dp["r"], cov="iso")
+    outs = []
+    for t in range(gen.DECODE_STEPS):
+        sl = lambda x: x[:, :, t].contiguous()
+        outs.append(scan_amd.step(sl(ds["q"]), sl(ds["k"]), sl(ds["v"]), sl(ds["a"]), sl(ds["qn"]),
+                                  sl(ds["r"]), l, eta, cov="iso"))
+    torch.cuda.synchronize()
+    o = torch.stack(outs, dim=2).double().cpu().numpy()
+    sel = [(0, 0), (100, 5), (255, 31)]
+    ref_pre = run_oracle(pre, "iso", sel=sel)
+    # continue the oracle from its own prefix state on the selected sequences
+    for n, (b, h) in enumerate(sel):
+        one = {k: (v[b:b + 1, h:h + 1] if isinstance(v, torch.Tensor) else v)
+               for k, v in stp.items()}
+        r = oracle.fwd(one["q"], one["k"], one["v"], one["a"], one["qn"], one["r"],
+                       ref_pre["lT"][n][None, None], ref_pre["etaT"][n][None, None],
+                       cov=oracle.ISO)
+        err = np.abs(o[b, h] - r["o"][0, 0]).max() / np.abs(r["o"][0, 0]).max()
+        assert err < 2e-2, (b, h, err)
+        lerr = abs(float(l[b, h]) - r["lT"][0, 0]) / r["lT"][0, 0]
+        assert lerr < 1e-4, (b, h, lerr)
+
+
+def test_bitwise_deterministic():
+    _print_case("determinism")
+    inp = gen.make_inputs("lm_diag", seed=3, B=2, H=4, T=500)
+    a = run_hip(inp, "diag")
+    for _ in range(5):
+        b = run_hip(inp, "diag")
+        for k in a:
+            assert np.array_equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_adversarial_gates_finite_and_exact(dtype):
+    """a -> 0.01, r = 1e-3, |k| up to 5: gate products underflow inside a chunk,
+    which forces the sub-chunk split; results stay finite and match the oracle."""
+    _print_case("adversarial", dtype)
+    inp = gen.make_inputs("small_diag", seed=4, B=1, H=2, T=200, dk=64, dv=64, dtype=dtype)
+    g = torch.Generator().manual_seed(11)
+    T = 200
+    a = torch.full((1, 2, T, 64), 0.01)
+    a[:, :, ::7] = 0.9
+    inp["a"] = a
+    inp["r"] = torch.full((1, 2, T), 1e-3)
+    inp["k"] = (5 * (2 * torch.rand(1, 2, T, 64, generator=g) - 1)).to(inp["k"].dtype)
+    hip = run_hip(inp, "diag")
+    for k in hip:
+        assert np.all(np.isfinite(hip[k])), k
+    ref = run_oracle(inp, "diag")
+    assert_parity(compare(hip, ref), dtype, "adversarial")
+
+
+def test_vtile_split_invariance(monkeypatch):
+    _print_case("vtiles")
+    inp = gen.make_inputs("lm_diag", seed=6, B=1, H=2, T=150)
+    monkeypatch.setenv("KLA_FWD_VTILES", "1")
+    a = run_hip(inp, "diag")
+    monkeypatch.setenv("KLA_FWD_VTILES", "2")
+    b = run_hip(inp, "diag")
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
