@@ -40,6 +40,13 @@ bool supported(const klaDims* d) {
                               : kla::fwd_iso_supported(d->dk, d->dv, d->dtype);
 }
 
+// KLA_FWD_DIAG_IMPL=chunk selects the single-role chunk kernel for every
+// diagonal shape (the wave-specialised kernel is used where it is built).
+bool use_pipe() {
+    const char* s = getenv("KLA_FWD_DIAG_IMPL");
+    return !(s && s[0] == 'c');
+}
+
 int env_vtiles() {
     const char* s = getenv("KLA_FWD_VTILES");
     if (!s || !*s) return 0;
@@ -116,7 +123,10 @@ klaStatus klaFwd(const klaDims* d, const void* q, const void* k, const void* v, 
             e = kla::launch_fwd_iso(fa, d->dtype, st);
         } else {
             fa.n_vtiles = nvt_env > 0 ? nvt_env : kla::fwd_diag_vtiles(fa.B, fa.H, fa.T, fa.dk, fa.dv);
-            e = kla::launch_fwd_diag(fa, d->dtype, st);
+            if (use_pipe() && kla::fwd_diag_pipe_supported(fa.dk, fa.dv, fa.n_vtiles))
+                e = kla::launch_fwd_diag_pipe(fa, d->dtype, st);
+            else
+                e = kla::launch_fwd_diag(fa, d->dtype, st);
         }
         if (e == hipErrorInvalidValue) return KLA_ERR_UNSUPPORTED;
     }

@@ -44,6 +44,8 @@ enum Dt { DT_F32 = 0, DT_BF16 = 1 };
 // caller; the functions return hipErrorInvalidValue for a (dk, dv, dtype)
 // combination they were not instantiated for.
 hipError_t launch_fwd_diag(const FwdArgs& a, int dtype, hipStream_t s);
+hipError_t launch_fwd_diag_pipe(const FwdArgs& a, int dtype, hipStream_t s);
+bool fwd_diag_pipe_supported(int dk, int dv, int nvt);
 hipError_t launch_fwd_iso(const FwdArgs& a, int dtype, hipStream_t s);
 hipError_t launch_step(const StepArgs& a, int dtype, int cov, hipStream_t s);
 hipError_t launch_fwd_empty(const FwdArgs& a, int cov, hipStream_t s);
