@@ -123,7 +123,7 @@ klaStatus klaFwd(const klaDims* d, const void* q, const void* k, const void* v, 
             e = kla::launch_fwd_iso(fa, d->dtype, st);
         } else {
             fa.n_vtiles = nvt_env > 0 ? nvt_env : kla::fwd_diag_vtiles(fa.B, fa.H, fa.T, fa.dk, fa.dv);
-            if (use_pipe() && kla::fwd_diag_pipe_supported(fa.dk, fa.dv, fa.n_vtiles))
+            if (use_pipe() && kla::fwd_diag_pipe_supported(fa.dk, fa.dv, fa.n_vtiles, d->dtype))
                 e = kla::launch_fwd_diag_pipe(fa, d->dtype, st);
             else
                 e = kla::launch_fwd_diag(fa, d->dtype, st);

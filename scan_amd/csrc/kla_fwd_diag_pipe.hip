@@ -1,28 +1,37 @@
-// kla_fwd_diag_pipe.hip -- gfx950 forward kernel, diagonal precision, for
-// key dims 64 and 128: wave-specialised software pipeline.
+// kla_fwd_diag_pipe.hip -- gfx950 forward kernel, diagonal precision,
+// three-role software pipeline (key dims 64 and 128).
 //
 // Sources: "Kalman Linear Attention: Parallel Bayesian Filtering For Efficient
 // Language Modelling and State Tracking" (gist.science explainer, method §1-§3)
 // and "Kalman Delta Networks: Uncertainty-aware Associative Memory" (abstract,
-// diagonal variant).  The recurrence and the mean-form gated scan are the
-// same as in kla_fwd_diag.hip:
-//   lp = l/(a^2 + qn l),  l' = lp + k^2/r,
-//   m_t = f_t (.) m_{t-1} + w_t v_t^T,  f = a lp / l',  w = k / (r l'),
-//   o_t = q_t^T m_t.
+// diagonal variant).  Per (b,h) and key dim i:
+//   lp = l/(a^2 + qn l),  l' = lp + k^2/r                          (precision)
+//   m_t = f_t (.) m_{t-1} + w_t v_t^T,  f = a lp / l',  w = k/(r l')  (mean)
+//   o_t = q_t^T m_t
+// (the information-form update divided by l'; every gate f lies in (0, 1]).
 //
-// The precision recursion is sequential in t for each key dim, so one
-// workgroup splits its waves by role and overlaps them chunk by chunk:
-//   chain waves (one lane per key dim) run the precision recurrence of chunk
-//     c+1 -- four dependent VALU ops per token -- and leave (a*lp, l) in LDS;
-//   gate waves turn chunk c's precisions into gates and MFMA operands (every
-//     lane owns two key dims and 8 tokens; the cumulative gate products cross
-//     token groups with lane shuffles inside the wave, no barrier), then run
-//     the chunk's MFMA work (causal S^T tiles, readout, state update) with the
-//     fp32 state in accumulator registers.
-// Two workgroup barriers per 32-token chunk.  Gate products that fall below
-// 2^-64 inside a chunk trigger the exact sub-chunk split (rare, slow path).
+// One workgroup owns one (b,h) and DV value columns and walks the sequence in
+// 32-token chunks.  Its waves have three roles that work on three different
+// chunks at once and meet at ONE workgroup barrier per chunk:
+//   chain waves  (one lane per key dim) run the sequential precision recursion
+//                of chunk c+2: four dependent VALU ops per token.  They write
+//                (a*lp, l) to LDS and flag the chunk if some cumulative gate
+//                product inside it drops below 2^-64;
+//   gate waves   turn chunk c+1's precisions into gates f, w and cumulative
+//                products G (lanes own 2 key dims x 8 tokens; the products
+//                cross token groups with DPP row shifts), and write the bf16
+//                MFMA operands q^ = q G, w^ = w / G (or, for a flagged chunk,
+//                the raw fp32 gates);
+//   MMA waves    own the fp32 state m (accumulator registers) and run chunk
+//                c: causal S^T = W^ Q^^T tiles, O^T = m^T Q^^T + V^T P^T,
+//                m += W^^T V.  All products use 16x16x32 MFMAs: the K index of
+//                an operand fragment is permuted so that two stacked 16x16
+//                accumulator tiles form one K=32 operand without LDS.
+//                A flagged chunk is applied token by token (exact, slower).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "kla_common.h"
 #include "kla_internal.h"
@@ -33,122 +42,123 @@ namespace {
 constexpr float kFloor = 5.421010862427522e-20f;  // 2^-64
 
 template <typename TIn, int DK_, int DV_>
-struct PCfg {
+struct P3 {
     static constexpr int DK = DK_;
-    static constexpr int DV = DV_;              // value columns of this workgroup
-    static constexpr int C = 32;                // tokens per chunk
-    static constexpr int NCW = DK / 64;         // chain waves
-    static constexpr int NGW = 4;               // gate waves
-    static constexpr int NW = NCW + NGW;
-    static constexpr int NT = NW * 64;
-    static constexpr int JT = DV / 16 / NGW;    // value tiles per gate wave
-    static constexpr int IT = DK / 16;
-    static constexpr int NB = C / 16;
-    static constexpr int NIP = DK / 2;          // key-dim pairs
-    static constexpr int NGRP = 256 / NIP;      // token groups (over all gate lanes)
-    static constexpr int TPG = C / NGRP;        // tokens per group
-    static constexpr int IPW = 64 / NGRP;       // key-dim pairs per gate wave
+    static constexpr int DV = DV_;
+    static constexpr int C = 32;                 // tokens per chunk
+    static constexpr int NCW = DK / 64;          // chain waves
+    static constexpr int JT = 2;                 // 16-column value tiles per MMA wave
+    static constexpr int NMW = DV / 32;          // MMA waves
+    static constexpr int NGW = 4;                // gate waves
+    static constexpr int NW = NCW + NMW + NGW;
+    static constexpr int NT = 64 * NW;
+    static constexpr int IT = DK / 16;           // 16-row tiles of the state
+    static constexpr int KB = DK / 32;           // K=32 blocks over the key dim
+    static constexpr int NIP = DK / 2;           // key-dim pairs
+    static constexpr int NGRP = 256 / NIP;       // token groups
+    static constexpr int TPG = C / NGRP;         // tokens per group
+    static constexpr int IPW = 64 / NGRP;        // key-dim pairs per gate wave
     static constexpr int PE = 16 / (int)sizeof(TIn);
-    static constexpr int QS = DK + PE;
-    static constexpr int CS = C + PE;
+    static constexpr int QS = DK + PE;           // row stride of Q^, W^
+    static constexpr int CS = C + PE;            // row stride of W^T, V^T
+    static constexpr int LPS = DK + 2;           // row stride of the chain buffer
     static constexpr int VQ = DV / 4;
     static constexpr int VUNITS = (C / 2) * VQ;
-    static constexpr int VPT = (VUNITS + 255) / 256;
-    static_assert(DK == 64 || DK == 128, "pipelined kernel covers dk 64 and 128");
-    static_assert(JT >= 1 && DV % (16 * NGW) == 0, "value tiles");
-    static_assert(TPG >= 1 && C % NGRP == 0, "gate layout");
+    static constexpr int VPT = VUNITS / 256;
+    static_assert(DK == 64 || DK == 128, "key dims 64 and 128");
+    static_assert(DV % 32 == 0 && VUNITS % 256 == 0, "value tiles");
 };
 
 template <typename TIn, class K>
-struct PSmem {
-    f32x2 LP[2][K::C][K::DK];   // (a*lp, l) from the chain, by chunk parity
-    TIn Q[K::C][K::QS];         // q^ = q G
-    TIn W[K::C][K::QS];         // w^ = w / G
-    TIn WT[K::DK][K::CS];       // w^ transposed
-    TIn VT[K::DV][K::CS];       // v transposed
-    float rho[2][K::C];         // 1/r_t by chunk parity
-    float E[2][K::DK];          // pending end-of-subchunk state scale, by parity
-    float sc[K::DK];            // state scale before a sub-chunk's readout
+struct OpFac {
+    TIn Q[K::C][K::QS];
+    TIn W[K::C][K::QS];
+    TIn WT[K::DK][K::CS];
+};
+template <class K>
+struct OpRaw {
+    float f[K::C][K::DK];
+    float w[K::C][K::DK];
+};
+
+template <typename TIn, class K>
+struct S3 {
+    f32x2 LP[2][K::C][K::LPS];   // (a*lp, l) by chunk parity
+    union {
+        OpFac<TIn, K> fac;
+        OpRaw<K> raw;
+    } op[2];                      // MFMA operands (or raw gates) by chunk parity
+    TIn VT[2][K::DV][K::CS];      // v^T by chunk parity
+    float rho[2][K::C];           // 1/r_t by chunk parity
+    float sc[2][K::DK];           // state scale before the chunk's readout
+    float E[2][K::DK];            // end-of-chunk gate product (pending state scale)
     float lT[K::DK];
-    int L1;
-    int bad[2];
+    int bad[4];                   // chunk needs the exact token-by-token path
 };
 
-// Pre-scale, readout and state update for tokens [ts, L1) of the chunk at t0.
-template <typename TIn, class K>
-__device__ __forceinline__ void pipe_mfma(PSmem<TIn, K>& sm, f32x4 (&accM)[K::IT][K::JT],
-                                          const FwdArgs& p, int bh, int vt, int t0, int ts,
-                                          int L1, int gw, int lane) {
-    typedef Mma<TIn> M;
-    const int c16 = lane & 15, g = lane >> 4;
-#pragma unroll
-    for (int it = 0; it < K::IT; ++it) {
-        const f32x4 s = *(const f32x4*)&sm.sc[it * 16 + 4 * g];
-#pragma unroll
-        for (int jj = 0; jj < K::JT; ++jj) accM[it][jj] *= s;
+// Eight bf16/f32 values forming one K=32 operand fragment: slots 0-3 hold
+// k = 4g..4g+3 of the first 16-block, slots 4-7 the same of the second.
+template <typename T> struct Frag;
+template <> struct Frag<bf16> {
+    typedef bf16x8 V;
+    static __device__ __forceinline__ V ld(const bf16* row, int g) {
+        const s16x4 lo = *(const s16x4*)(row + 4 * g);
+        const s16x4 hi = *(const s16x4*)(row + 16 + 4 * g);
+        typedef short s16x8 __attribute__((__vector_size__(16)));
+        s16x8 r = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        return __builtin_bit_cast(V, r);
     }
-    typename M::K16 AM[K::IT][K::JT];
+    static __device__ __forceinline__ V from_acc(f32x4 lo, f32x4 hi) {
+        V r = {(bf16)lo[0], (bf16)lo[1], (bf16)lo[2], (bf16)lo[3],
+               (bf16)hi[0], (bf16)hi[1], (bf16)hi[2], (bf16)hi[3]};
+        return r;
+    }
+    static __device__ __forceinline__ f32x4 mma(V a, V b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+};
+template <> struct Frag<float> {
+    struct V { f32x4 lo, hi; };
+    static __device__ __forceinline__ V ld(const float* row, int g) {
+        V r;
+        r.lo = *(const f32x4*)(row + 4 * g);
+        r.hi = *(const f32x4*)(row + 16 + 4 * g);
+        return r;
+    }
+    static __device__ __forceinline__ V from_acc(f32x4 lo, f32x4 hi) { V r; r.lo = lo; r.hi = hi; return r; }
+    static __device__ __forceinline__ f32x4 mma(V a, V b, f32x4 c) {
 #pragma unroll
-    for (int it = 0; it < K::IT; ++it)
+        for (int e = 0; e < 4; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[e], b.lo[e], c, 0, 0, 0);
 #pragma unroll
-        for (int jj = 0; jj < K::JT; ++jj) AM[it][jj] = M::from_acc(accM[it][jj]);
+        for (int e = 0; e < 4; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[e], b.hi[e], c, 0, 0, 0);
+        return c;
+    }
+};
 
-    const int tb0 = ts / 16, tb1 = (L1 + 15) / 16;
-#pragma unroll
-    for (int tau = 0; tau < K::NB; ++tau) {
-        if (tau < tb0 || tau >= tb1) continue;
-        typename M::K16 P[K::NB];
-#pragma unroll
-        for (int sig = 0; sig <= tau; ++sig) {
-            if (sig < tb0) continue;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < K::DK / 32; ++kk)
-                acc = M::mma32(M::ld32(&sm.W[sig * 16 + c16][kk * 32 + 8 * g]),
-                               M::ld32(&sm.Q[tau * 16 + c16][kk * 32 + 8 * g]), acc);
-            if (sig == tau) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (4 * g + e > c16) acc[e] = 0.f;
-            }
-            P[sig] = M::from_acc(acc);
-        }
-        const int t = tau * 16 + c16;
-        const bool store = (t >= ts) && (t < L1);
-#pragma unroll
-        for (int jj = 0; jj < K::JT; ++jj) {
-            const int jt = gw * K::JT + jj;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int it = 0; it < K::IT; ++it)
-                acc = M::mma16(AM[it][jj], M::ld16(&sm.Q[tau * 16 + c16][it * 16 + 4 * g]), acc);
-#pragma unroll
-            for (int sig = 0; sig <= tau; ++sig) {
-                if (sig < tb0) continue;
-                acc = M::mma16(M::ld16(&sm.VT[jt * 16 + c16][sig * 16 + 4 * g]), P[sig], acc);
-            }
-            if (store) {
-                TIn* o = (TIn*)p.o;
-                const size_t off = ((size_t)bh * p.T + t0 + t) * p.dv + (size_t)vt * K::DV +
-                                   jt * 16 + 4 * g;
-                *(typename Quad<TIn>::V*)(o + off) = Quad<TIn>::make(acc);
-            }
-        }
-    }
-#pragma unroll
-    for (int it = 0; it < K::IT; ++it)
-#pragma unroll
-        for (int jj = 0; jj < K::JT; ++jj) {
-            const int jt = gw * K::JT + jj;
-            accM[it][jj] = M::mma32(M::ld32(&sm.WT[it * 16 + c16][8 * g]),
-                                    M::ld32(&sm.VT[jt * 16 + c16][8 * g]), accM[it][jj]);
-        }
+template <int N>
+__device__ __forceinline__ float dpp_row_shr(float x) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x110 + N, 0xF, 0xF, false));
 }
 
-// Store N consecutive values of T (16-byte aligned destination) as wide LDS writes.
+// Exclusive product over the NGRP consecutive lanes (token groups) of a key-dim pair.
+template <class K>
+__device__ __forceinline__ float group_excl_prod(float x, int grp) {
+    float y = dpp_row_shr<1>(x);
+    if (grp >= 1) x *= y;
+    y = dpp_row_shr<2>(x);
+    if (grp >= 2) x *= y;
+    if constexpr (K::NGRP > 4) {
+        y = dpp_row_shr<4>(x);
+        if (grp >= 4) x *= y;
+    }
+    y = dpp_row_shr<1>(x);
+    return grp == 0 ? 1.f : y;
+}
+
 template <typename T, int N>
 __device__ __forceinline__ void store_row(T* dst, const T (&v)[N]) {
-    constexpr int PER = 16 / (int)sizeof(T);   // values per 16-byte store
+    constexpr int PER = 16 / (int)sizeof(T);
     if constexpr (N % PER == 0) {
 #pragma unroll
         for (int b = 0; b < N / PER; ++b) {
@@ -157,8 +167,9 @@ __device__ __forceinline__ void store_row(T* dst, const T (&v)[N]) {
             for (int e = 0; e < PER; ++e) tmp[e] = v[b * PER + e];
             *(f32x4*)(dst + b * PER) = __builtin_bit_cast(f32x4, tmp);
         }
-    } else if constexpr ((N * (int)sizeof(T)) % 8 == 0) {
+    } else {
         constexpr int P8 = 8 / (int)sizeof(T);
+        static_assert(N % P8 == 0, "row store");
 #pragma unroll
         for (int b = 0; b < N / P8; ++b) {
             T tmp[P8];
@@ -166,155 +177,125 @@ __device__ __forceinline__ void store_row(T* dst, const T (&v)[N]) {
             for (int e = 0; e < P8; ++e) tmp[e] = v[b * P8 + e];
             *(f32x2*)(dst + b * P8) = __builtin_bit_cast(f32x2, tmp);
         }
-    } else {
-#pragma unroll
-        for (int e = 0; e < N; ++e) dst[e] = v[e];
     }
 }
 
-// Exclusive product over the token groups of one key-dim pair (lanes
-// grp*IPW + ipl of the same wave).
-template <class K>
-__device__ __forceinline__ float group_exclusive_prod(float x, int grp) {
-    float incl = x;
-#pragma unroll
-    for (int d = 1; d < K::NGRP; d <<= 1) {
-        const float y = __shfl_up(incl, d * K::IPW, 64);
-        if (grp >= d) incl *= y;
-    }
-    float excl = __shfl_up(incl, K::IPW, 64);
-    return grp == 0 ? 1.f : excl;
+// Wait until every outstanding vector-memory load of this wave has landed
+// (vmcnt(0); expcnt and lgkmcnt left at their maxima).  Called at the top of
+// a pipeline step, before the step issues the next chunk's loads: the
+// previous loads were issued a whole step earlier, so this costs nothing, and
+// the current chunk's registers then need no further waits however many new
+// loads are in flight (the hardware counter only tracks 63).
+__device__ __forceinline__ void wait_prev_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+__device__ __forceinline__ int chunk_len(int T, int c, int C) {
+    const int n = T - c * C;
+    return n < C ? n : C;
 }
 
-// Chain role: one lane per key dim, precision recurrence one chunk ahead.
+// ------------------------------------------------------------------ chain role
 template <typename TIn, class K>
-__device__ __forceinline__ void chain_role(PSmem<TIn, K>& sm, const FwdArgs& p, int bh, int vt,
-                                           int wave, int lane) {
+__device__ void chain_role(S3<TIn, K>& sm, const FwdArgs& p, int bh, int vt, int cw, int lane) {
     constexpr int C = K::C, DK = K::DK;
-    const int ci = wave * 64 + lane;
-    const int h = bh % p.H;
+    const int i = cw * 64 + lane;
     const size_t rowbase = (size_t)bh * p.T;
     const int nchunks = (p.T + C - 1) / C;
+    const int nsteps = (nchunks + 3) & ~1;  // nchunks + 2 pipeline steps, rounded up to even
     const TIn* kp = (const TIn*)p.k;
 
-    float cl = p.l0 ? p.l0[(size_t)bh * DK + ci] : 1.f;
-    const float cqn = p.qn[(size_t)h * DK + ci];
-    float ca[C], na[C];
-    TIn ck[C], nk[C];
-    float crho = 1.f, nrho = 1.f;   // r_t of lane t, turned into 1/r_t before use
+    float l = p.l0 ? p.l0[(size_t)bh * DK + i] : 1.f;
+    const float qn = p.qn[(size_t)(bh % p.H) * DK + i];
+    // One chunk of inputs per buffer; the two buffers alternate, so a chunk's
+    // loads are issued a whole iteration before their first use.
+    struct Buf {
+        float a[C];
+        TIn k[C];
+        float r;  // r of token `lane` of the chunk
+    };
+    Buf b0, b1;
 
-    auto load = [&](int c, float (&a_)[C], TIn (&k_)[C], float& r_) {
-        const int t0 = c * C;
-        const int L = (p.T - t0) < C ? (p.T - t0) : C;
+    auto load = [&](int c, Buf& b) {
+        const int t0 = c * C, L = chunk_len(p.T, c, C);
 #pragma unroll
         for (int t = 0; t < C; ++t) {
-            const int tt = t < L ? t : L - 1;   // clamp: every load stays in bounds
-            const size_t off = (rowbase + t0 + tt) * DK + ci;
-            a_[t] = p.a[off];
-            k_[t] = kp[off];
+            const size_t off = (rowbase + t0 + (t < L ? t : L - 1)) * DK + i;
+            b.a[t] = p.a[off];
+            b.k[t] = kp[off];
         }
-        r_ = p.r[rowbase + t0 + (lane < L ? lane : L - 1)];
+        b.r = p.r[rowbase + t0 + (lane < L ? lane : L - 1)];
     };
-    // lp = l / (a^2 + qn l),  l' = lp + k^2 / r, over tokens [u0, u1) of chunk c
-    auto run = [&](int c, int u0, int u1) {
-        const int t0 = c * C;
-        const int L = (p.T - t0) < C ? (p.T - t0) : C;
-        const int par = c & 1;
+    auto step = [&](int c, Buf& cur, Buf& nxt) {
+        const int cc = c + 2;  // chunk scanned in this iteration
+        wait_prev_loads();
+        if (nchunks > 0) load(cc + 1 < nchunks ? cc + 1 : nchunks - 1, nxt);
+        if (cc < nchunks) {
+            const int L = chunk_len(p.T, cc, C), par = cc & 1;
+            const float rho = 1.f / cur.r;
+            if (cw == 0 && lane < C) sm.rho[par][lane] = rho;
+            // full chunks take a copy of the scan without per-token tests
+            auto scan = [&](auto full) {
+                constexpr bool FULL = decltype(full)::value;
+                float num = 1.f, den = 1.f, G = 1.f;
 #pragma unroll
-        for (int t = 0; t < C; ++t) {
-            if (t >= u0 && t < u1 && t < L) {
-                const float rho =
-                    __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, crho), t));
-                const float a = ca[t], kv = (float)ck[t];
-                const float b = kv * kv * rho;
-                const float lp = cl * fast_rcp(__builtin_fmaf(cqn, cl, a * a));
-                cl = lp + b;
-                sm.LP[par][t][ci] = f32x2{a * lp, cl};
-            }
+                for (int t = 0; t < C; ++t) {
+                    if (FULL || t < L) {
+                        const float rt = __builtin_bit_cast(
+                            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rho), t));
+                        const float a = cur.a[t], kv = (float)cur.k[t];
+                        const float lp = l * fast_rcp(__builtin_fmaf(qn, l, a * a));
+                        l = __builtin_fmaf(kv * kv, rt, lp);
+                        const float alp = a * lp;
+                        sm.LP[par][t][i] = f32x2{alp, l};
+                        if (t >= 1) { num *= alp; den *= l; }
+                    }
+                    if (t % 8 == 7) { G *= num * fast_rcp(den); num = 1.f; den = 1.f; }
+                }
+                return G * num * fast_rcp(den);
+            };
+            const float G = L == C ? scan(std::true_type{}) : scan(std::false_type{});
+            if (__builtin_amdgcn_ballot_w64(G < kFloor)) sm.bad[cc & 3] = 1;
         }
-    };
-    auto advance = [&]() {
-#pragma unroll
-        for (int t = 0; t < C; ++t) { ca[t] = na[t]; ck[t] = nk[t]; }
-        crho = nrho;
+        __syncthreads();
     };
 
-    sm.E[1][ci] = 1.f;
-    if (wave == 0 && lane == 0) { sm.bad[0] = 0; sm.bad[1] = 0; }
-    if (nchunks > 0) {
-        load(0, ca, ck, crho);
-        if (nchunks > 1) load(1, na, nk, nrho);
-        crho = 1.f / crho;
-        if (wave == 0 && lane < C) sm.rho[0][lane] = crho;
-        run(0, 0, C);
-        advance();
+    if (nchunks > 0) load(0, b0);
+    for (int c = -2; c < nsteps - 2; c += 2) {
+        step(c, b0, b1);
+        step(c + 1, b1, b0);
     }
+    sm.lT[i] = l;
+    if (p.lT && vt == 0) p.lT[(size_t)bh * DK + i] = l;
     __syncthreads();
-
-    for (int c = 0; c < nchunks; ++c) {
-        const int t0 = c * C;
-        const int L = (p.T - t0) < C ? (p.T - t0) : C;
-        const int cp = c & 1;
-        const bool has_next = c + 1 < nchunks;
-        if (c + 2 < nchunks) load(c + 2, na, nk, nrho);
-        if (has_next) {
-            crho = 1.f / crho;
-            if (wave == 0 && lane < C) sm.rho[cp ^ 1][lane] = crho;
-            run(c + 1, 0, C / 2);
-        }
-        __syncthreads();                                         // X
-        if (sm.bad[cp]) {                                        // mirror the split's barriers
-            int ts = 0;
-            while (ts < L) {
-                __syncthreads();                                 // F1
-                const int L1 = sm.L1;
-                __syncthreads();                                 // F2
-                ts = L1;
-                __syncthreads();                                 // F3
-                if (wave == 0 && lane == 0) sm.L1 = L;
-                __syncthreads();                                 // F4
-            }
-        }
-        if (has_next) {
-            run(c + 1, C / 2, C);
-            advance();
-        }
-        __syncthreads();                                         // Y
-    }
-    sm.lT[ci] = cl;
-    if (p.lT && vt == 0) p.lT[(size_t)bh * DK + ci] = cl;
-    __syncthreads();                                             // E
 }
 
-// Gate role: gates, MFMA operands, MFMA work for the current chunk.
+// ------------------------------------------------------------------ gate role
 template <typename TIn, class K>
-__device__ __forceinline__ void gate_role(PSmem<TIn, K>& sm, const FwdArgs& p, int bh, int vt,
-                                          int gw, int lane) {
+__device__ void gate_role(S3<TIn, K>& sm, const FwdArgs& p, int bh, int vt, int gw, int lane) {
     typedef Pair<TIn> PR;
     constexpr int C = K::C, DK = K::DK, DV = K::DV, TPG = K::TPG;
     const size_t rowbase = (size_t)bh * p.T;
     const int nchunks = (p.T + C - 1) / C;
-    const int grp = lane / K::IPW, ipl = lane % K::IPW;
-    const int ip = gw * K::IPW + ipl;               // key-dim pair
-    const int c16 = lane & 15, g = lane >> 4;
+    const int nsteps = (nchunks + 3) & ~1;
+    const int grp = lane % K::NGRP, ipl = lane / K::NGRP;
+    const int ip = gw * K::IPW + ipl;
     const int gtid = gw * 64 + lane;
     const TIn* qp = (const TIn*)p.q;
     const TIn* kp = (const TIn*)p.k;
     const TIn* vp = (const TIn*)p.v;
 
-    typename PR::V gq[TPG], gk[TPG], nq[TPG], nk[TPG];
-    typename Quad<TIn>::V gv[K::VPT][2], nv[K::VPT][2];
-    auto load = [&](int c, typename PR::V (&q2)[TPG], typename PR::V (&k2)[TPG],
-                    typename Quad<TIn>::V (&v4)[K::VPT][2]) {
-        const int t0 = c * C;
-        const int L = (p.T - t0) < C ? (p.T - t0) : C;
+    struct Buf {
+        typename PR::V q[TPG], k[TPG];
+        typename Quad<TIn>::V v[K::VPT][2];
+    };
+    Buf b0, b1;
+    auto load = [&](int c, Buf& bf) {
+        const int t0 = c * C, L = chunk_len(p.T, c, C);
 #pragma unroll
         for (int u = 0; u < TPG; ++u) {
             const int t = grp * TPG + u;
-            const int tt = t < L ? t : L - 1;   // clamp: masked later, load stays in bounds
-            const size_t off = (rowbase + t0 + tt) * DK + 2 * ip;
-            q2[u] = *(const typename PR::V*)(qp + off);
-            k2[u] = *(const typename PR::V*)(kp + off);
+            const size_t off = (rowbase + t0 + (t < L ? t : L - 1)) * DK + 2 * ip;
+            bf.q[u] = *(const typename PR::V*)(qp + off);
+            bf.k[u] = *(const typename PR::V*)(kp + off);
         }
 #pragma unroll
         for (int x = 0; x < K::VPT; ++x) {
@@ -323,202 +304,263 @@ __device__ __forceinline__ void gate_role(PSmem<TIn, K>& sm, const FwdArgs& p, i
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) {
                 const int t = 2 * tp + h2;
-                const int tt = t < L ? t : L - 1;   // rows past the end meet zero weights
-                const int jj = unit < K::VUNITS ? 4 * jq : 0;
-                const size_t off = (rowbase + t0 + tt) * p.dv + (size_t)vt * DV + jj;
-                v4[x][h2] = *(const typename Quad<TIn>::V*)(vp + off);
+                const size_t off = (rowbase + t0 + (t < L ? t : L - 1)) * p.dv + (size_t)vt * DV + 4 * jq;
+                bf.v[x][h2] = *(const typename Quad<TIn>::V*)(vp + off);
             }
         }
     };
 
-    f32x4 accM[K::IT][K::JT];
+    auto step = [&](int c, Buf& cur, Buf& nxt) {
+        const int cg = c + 1;  // chunk gated in this iteration
+        wait_prev_loads();
+        if (nchunks > 0) load(cg + 1 < nchunks ? (cg + 1 > 0 ? cg + 1 : 0) : nchunks - 1, nxt);
+        if (cg >= 0 && cg < nchunks) {
+            const int L = chunk_len(p.T, cg, C), par = cg & 1;
+            // V^T of the chunk
 #pragma unroll
-    for (int it = 0; it < K::IT; ++it)
-#pragma unroll
-        for (int jj = 0; jj < K::JT; ++jj) {
-            const int jt = gw * K::JT + jj;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = it * 16 + 4 * g + e;
-                const int j = vt * DV + jt * 16 + c16;
-                accM[it][jj][e] = p.eta0 ? p.eta0[((size_t)bh * DK + i) * p.dv + j] /
-                                               (p.l0 ? p.l0[(size_t)bh * DK + i] : 1.f)
-                                         : 0.f;
-            }
-        }
-    if (nchunks > 0) load(0, gq, gk, gv);
-    __syncthreads();
-
-    int par = 0;  // E parity the next sub-chunk writes
-    for (int c = 0; c < nchunks; ++c) {
-        const int t0 = c * C;
-        const int L = (p.T - t0) < C ? (p.T - t0) : C;
-        const int cp = c & 1;
-        const bool has_next = c + 1 < nchunks;
-
-        // ---------------- phase A: V^T, gates, operands
-#pragma unroll
-        for (int x = 0; x < K::VPT; ++x) {
-            const int unit = gtid + x * 256;
-            if (unit < K::VUNITS) {
+            for (int x = 0; x < K::VPT; ++x) {
+                const int unit = gtid + x * 256;
                 const int tp = unit / K::VQ, jq = unit % K::VQ;
-                const f32x4 v0 = Quad<TIn>::to_f32(gv[x][0]), v1 = Quad<TIn>::to_f32(gv[x][1]);
+                const f32x4 v0 = Quad<TIn>::to_f32(cur.v[x][0]), v1 = Quad<TIn>::to_f32(cur.v[x][1]);
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    *(typename PR::V*)&sm.VT[4 * jq + e][2 * tp] = PR::make(v0[e], v1[e]);
+                    *(typename PR::V*)&sm.VT[par][4 * jq + e][2 * tp] = PR::make(v0[e], v1[e]);
             }
-        }
-        if (has_next) load(c + 1, nq, nk, nv);
-
-        float f[TPG][2], w[TPG][2], G[TPG][2];
-        float p0 = 1.f, p1 = 1.f;
-#pragma unroll
-        for (int u = 0; u < TPG; ++u) {
-            const int t = grp * TPG + u;
-            const f32x4 lp = *(const f32x4*)&sm.LP[cp][t][2 * ip];   // a*lp, l for 2 key dims
-            const float rh = sm.rho[cp][t];
-            const float rl0 = fast_rcp(lp[1]), rl1 = fast_rcp(lp[3]);
-            f[u][0] = lp[0] * rl0;
-            f[u][1] = lp[2] * rl1;
-            w[u][0] = PR::lo(gk[u]) * rh * rl0;
-            w[u][1] = PR::hi(gk[u]) * rh * rl1;
-            if (t > 0 && t < L) { p0 *= f[u][0]; p1 *= f[u][1]; }
-            G[u][0] = p0;
-            G[u][1] = p1;
-        }
-        {
-            const float e0 = group_exclusive_prod<K>(p0, grp);
-            const float e1 = group_exclusive_prod<K>(p1, grp);
-            bool badl = false;
-            TIn wt0[TPG], wt1[TPG];
+            // gates
+            float f[TPG][2], w[TPG][2];
 #pragma unroll
             for (int u = 0; u < TPG; ++u) {
                 const int t = grp * TPG + u;
-                const float g0 = G[u][0] * e0, g1 = G[u][1] * e1;
-                const bool in = t < L;
-                badl |= in && (g0 < kFloor || g1 < kFloor);
-                float q0 = 0.f, q1 = 0.f, w0 = 0.f, w1 = 0.f;
-                if (in) {
-                    q0 = PR::lo(gq[u]) * g0;
-                    q1 = PR::hi(gq[u]) * g1;
-                    w0 = w[u][0] * fast_rcp(g0);
-                    w1 = w[u][1] * fast_rcp(g1);
-                }
-                *(typename PR::V*)&sm.Q[t][2 * ip] = PR::make(q0, q1);
-                *(typename PR::V*)&sm.W[t][2 * ip] = PR::make(w0, w1);
-                wt0[u] = (TIn)w0;
-                wt1[u] = (TIn)w1;
-                if (t == 0) {
-                    sm.sc[2 * ip] = sm.E[par ^ 1][2 * ip] * f[u][0];
-                    sm.sc[2 * ip + 1] = sm.E[par ^ 1][2 * ip + 1] * f[u][1];
-                }
-                if (t == L - 1) {
-                    sm.E[par][2 * ip] = g0;
-                    sm.E[par][2 * ip + 1] = g1;
-                }
+                const f32x4 lq = *(const f32x4*)&sm.LP[par][t][2 * ip];  // a*lp, l (two key dims)
+                const float rh = sm.rho[par][t];
+                const float rl0 = fast_rcp(lq[1]), rl1 = fast_rcp(lq[3]);
+                f[u][0] = lq[0] * rl0;
+                f[u][1] = lq[2] * rl1;
+                w[u][0] = PR::lo(cur.k[u]) * rh * rl0;
+                w[u][1] = PR::hi(cur.k[u]) * rh * rl1;
             }
-            store_row<TIn, TPG>(&sm.WT[2 * ip][grp * TPG], wt0);
-            store_row<TIn, TPG>(&sm.WT[2 * ip + 1][grp * TPG], wt1);
-            if (__builtin_amdgcn_ballot_w64(badl)) sm.bad[cp] = 1;
-            if (gtid == 0) { sm.bad[cp ^ 1] = 0; sm.L1 = L; }
-        }
-        __syncthreads();                                         // X
-
-        // ---------------- phase B: MFMA (or the exact split)
-        if (!sm.bad[cp]) {
-            pipe_mfma<TIn, K>(sm, accM, p, bh, vt, t0, 0, L, gw, lane);
-            par ^= 1;
-        } else {
-            int ts = 0;
-            while (ts < L) {
-                float Gs[TPG][2];
-                float s0 = 1.f, s1 = 1.f;
+            const float* Eprev = sm.E[par ^ 1];
+            if (!sm.bad[cg & 3]) {
+                float G[TPG][2];
+                float p0 = 1.f, p1 = 1.f;
 #pragma unroll
                 for (int u = 0; u < TPG; ++u) {
                     const int t = grp * TPG + u;
-                    if (t > ts && t < L) { s0 *= f[u][0]; s1 *= f[u][1]; }
-                    Gs[u][0] = s0;
-                    Gs[u][1] = s1;
+                    if (t > 0 && t < L) { p0 *= f[u][0]; p1 *= f[u][1]; }
+                    G[u][0] = p0;
+                    G[u][1] = p1;
                 }
-                const float e0 = group_exclusive_prod<K>(s0, grp);
-                const float e1 = group_exclusive_prod<K>(s1, grp);
-                int firstbad = L;
-#pragma unroll
-                for (int u = 0; u < TPG; ++u) {
-                    const int t = grp * TPG + u;
-                    Gs[u][0] *= e0;
-                    Gs[u][1] *= e1;
-                    if (t >= ts && t < L && (Gs[u][0] < kFloor || Gs[u][1] < kFloor))
-                        firstbad = t < firstbad ? t : firstbad;
-                }
-                if (firstbad < L) atomicMin(&sm.L1, firstbad);
-                __syncthreads();                                 // F1
-                const int L1 = sm.L1;
+                const float e0 = group_excl_prod<K>(p0, grp), e1 = group_excl_prod<K>(p1, grp);
                 TIn wt0[TPG], wt1[TPG];
 #pragma unroll
                 for (int u = 0; u < TPG; ++u) {
                     const int t = grp * TPG + u;
-                    const bool keep = (t >= ts) && (t < L1);
+                    const float g0 = G[u][0] * e0, g1 = G[u][1] * e1;
                     float q0 = 0.f, q1 = 0.f, w0 = 0.f, w1 = 0.f;
-                    if (keep) {
-                        q0 = PR::lo(gq[u]) * Gs[u][0];
-                        q1 = PR::hi(gq[u]) * Gs[u][1];
-                        w0 = w[u][0] * fast_rcp(Gs[u][0]);
-                        w1 = w[u][1] * fast_rcp(Gs[u][1]);
+                    if (t < L) {
+                        q0 = PR::lo(cur.q[u]) * g0;
+                        q1 = PR::hi(cur.q[u]) * g1;
+                        w0 = w[u][0] * fast_rcp(g0);
+                        w1 = w[u][1] * fast_rcp(g1);
                     }
-                    *(typename PR::V*)&sm.Q[t][2 * ip] = PR::make(q0, q1);
-                    *(typename PR::V*)&sm.W[t][2 * ip] = PR::make(w0, w1);
+                    *(typename PR::V*)&sm.op[par].fac.Q[t][2 * ip] = PR::make(q0, q1);
+                    *(typename PR::V*)&sm.op[par].fac.W[t][2 * ip] = PR::make(w0, w1);
                     wt0[u] = (TIn)w0;
                     wt1[u] = (TIn)w1;
-                    if (t == ts) {
-                        sm.sc[2 * ip] = sm.E[par ^ 1][2 * ip] * f[u][0];
-                        sm.sc[2 * ip + 1] = sm.E[par ^ 1][2 * ip + 1] * f[u][1];
+                    if (t == 0) {
+                        sm.sc[par][2 * ip] = Eprev[2 * ip] * f[u][0];
+                        sm.sc[par][2 * ip + 1] = Eprev[2 * ip + 1] * f[u][1];
                     }
-                    if (t == L1 - 1) {
-                        sm.E[par][2 * ip] = Gs[u][0];
-                        sm.E[par][2 * ip + 1] = Gs[u][1];
+                    if (t == L - 1) {
+                        sm.E[par][2 * ip] = g0;
+                        sm.E[par][2 * ip + 1] = g1;
                     }
                 }
-                store_row<TIn, TPG>(&sm.WT[2 * ip][grp * TPG], wt0);
-                store_row<TIn, TPG>(&sm.WT[2 * ip + 1][grp * TPG], wt1);
-                __syncthreads();                                 // F2
-                pipe_mfma<TIn, K>(sm, accM, p, bh, vt, t0, ts, L1, gw, lane);
-                par ^= 1;
-                ts = L1;
-                __syncthreads();                                 // F3
-                __syncthreads();                                 // F4 (a chain lane resets L1)
+                store_row<TIn, TPG>(&sm.op[par].fac.WT[2 * ip][grp * TPG], wt0);
+                store_row<TIn, TPG>(&sm.op[par].fac.WT[2 * ip + 1][grp * TPG], wt1);
+            } else {
+                // flagged chunk: raw fp32 gates for the token-by-token path
+#pragma unroll
+                for (int u = 0; u < TPG; ++u) {
+                    const int t = grp * TPG + u;
+                    const bool in = t < L;
+                    *(f32x2*)&sm.op[par].raw.f[t][2 * ip] = f32x2{in ? f[u][0] : 1.f, in ? f[u][1] : 1.f};
+                    *(f32x2*)&sm.op[par].raw.w[t][2 * ip] = f32x2{in ? w[u][0] : 0.f, in ? w[u][1] : 0.f};
+                    if (t == 0) {
+                        sm.sc[par][2 * ip] = Eprev[2 * ip];
+                        sm.sc[par][2 * ip + 1] = Eprev[2 * ip + 1];
+                    }
+                    if (t == L - 1) {
+                        sm.E[par][2 * ip] = 1.f;
+                        sm.E[par][2 * ip + 1] = 1.f;
+                    }
+                }
             }
         }
-        if (has_next) {
-#pragma unroll
-            for (int u = 0; u < TPG; ++u) { gq[u] = nq[u]; gk[u] = nk[u]; }
-#pragma unroll
-            for (int x = 0; x < K::VPT; ++x) { gv[x][0] = nv[x][0]; gv[x][1] = nv[x][1]; }
-        }
-        __syncthreads();                                         // Y
+        __syncthreads();
+    };
+
+    if (gtid < DK) sm.E[1][gtid] = 1.f;
+    // iteration c gates chunk c+1, which sits in b0 when c is odd; the first
+    // iteration only loads chunk 0
+    for (int c = -2; c < nsteps - 2; c += 2) {
+        step(c, b1, b0);
+        step(c + 1, b0, b1);
     }
-    __syncthreads();                                             // E
-    if (p.etaT) {
+    __syncthreads();
+}
+
+// ------------------------------------------------------------------ MMA role
+template <typename TIn, class K>
+__device__ void mma_role(S3<TIn, K>& sm, const FwdArgs& p, int bh, int vt, int mw, int lane) {
+    typedef Frag<TIn> F;
+    typedef typename F::V FV;
+    constexpr int C = K::C, DK = K::DK, DV = K::DV, IT = K::IT, JT = K::JT, KB = K::KB;
+    const size_t rowbase = (size_t)bh * p.T;
+    const int nchunks = (p.T + C - 1) / C;
+    const int nsteps = (nchunks + 3) & ~1;
+    const int c16 = lane & 15, g = lane >> 4;
+    TIn* op = (TIn*)p.o;
+    const TIn* qp = (const TIn*)p.q;
+
+    f32x4 acc[IT][JT];
 #pragma unroll
-        for (int it = 0; it < K::IT; ++it)
+    for (int it = 0; it < IT; ++it)
 #pragma unroll
-            for (int jj = 0; jj < K::JT; ++jj) {
-                const int jt = gw * K::JT + jj;
+        for (int jj = 0; jj < JT; ++jj) {
+            const int j = vt * DV + (mw * JT + jj) * 16 + c16;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = it * 16 + 4 * g + e;
+                acc[it][jj][e] = p.eta0 ? p.eta0[((size_t)bh * DK + i) * p.dv + j] /
+                                              (p.l0 ? p.l0[(size_t)bh * DK + i] : 1.f)
+                                        : 0.f;
+            }
+        }
+
+    auto step = [&](int c) {
+        if (c >= 0 && c < nchunks) {
+            const int L = chunk_len(p.T, c, C), par = c & 1, t0 = c * C;
+            const bool bad = sm.bad[c & 3];
+            if (mw == 0 && lane == 0 && c >= 1) sm.bad[(c - 1) & 3] = 0;
+            // m <- sc (.) m
+#pragma unroll
+            for (int it = 0; it < IT; ++it) {
+                const f32x4 s = *(const f32x4*)&sm.sc[par][it * 16 + 4 * g];
+#pragma unroll
+                for (int jj = 0; jj < JT; ++jj) acc[it][jj] *= s;
+            }
+            if (!bad) {
+                const OpFac<TIn, K>& o = sm.op[par].fac;
+                FV Qf[2][KB], Vf[JT];
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+#pragma unroll
+                    for (int kk = 0; kk < KB; ++kk) Qf[b][kk] = F::ld(&o.Q[b * 16 + c16][kk * 32], g);
+#pragma unroll
+                for (int jj = 0; jj < JT; ++jj) Vf[jj] = F::ld(&sm.VT[par][(mw * JT + jj) * 16 + c16][0], g);
+                // causal S^T tiles (sigma, tau)
+                f32x4 s00 = {0.f, 0.f, 0.f, 0.f}, s01 = s00, s11 = s00;
+#pragma unroll
+                for (int kk = 0; kk < KB; ++kk) {
+                    const FV w0 = F::ld(&o.W[c16][kk * 32], g);
+                    const FV w1 = F::ld(&o.W[16 + c16][kk * 32], g);
+                    s00 = F::mma(w0, Qf[0][kk], s00);
+                    s01 = F::mma(w0, Qf[1][kk], s01);
+                    s11 = F::mma(w1, Qf[1][kk], s11);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (4 * g + e > c16) { s00[e] = 0.f; s11[e] = 0.f; }
+                }
+                const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+                const FV P0 = F::from_acc(s00, zero), P1 = F::from_acc(s01, s11);
+                // readout O^T = m^T Q^^T + V^T P^T, the state as the A operand
+#pragma unroll
+                for (int jj = 0; jj < JT; ++jj) {
+                    f32x4 out0 = {0.f, 0.f, 0.f, 0.f}, out1 = out0;
+#pragma unroll
+                    for (int kk = 0; kk < KB; ++kk) {
+                        const FV am = F::from_acc(acc[2 * kk][jj], acc[2 * kk + 1][jj]);
+                        out0 = F::mma(am, Qf[0][kk], out0);
+                        out1 = F::mma(am, Qf[1][kk], out1);
+                    }
+                    out0 = F::mma(Vf[jj], P0, out0);
+                    out1 = F::mma(Vf[jj], P1, out1);
+                    const size_t col = (size_t)vt * DV + (mw * JT + jj) * 16 + 4 * g;
+                    if (c16 < L)
+                        *(typename Quad<TIn>::V*)(op + (rowbase + t0 + c16) * p.dv + col) = Quad<TIn>::make(out0);
+                    if (16 + c16 < L)
+                        *(typename Quad<TIn>::V*)(op + (rowbase + t0 + 16 + c16) * p.dv + col) = Quad<TIn>::make(out1);
+                }
+                // m += W^^T V
+#pragma unroll
+                for (int it = 0; it < IT; ++it) {
+                    const FV wt = F::ld(&o.WT[it * 16 + c16][0], g);
+#pragma unroll
+                    for (int jj = 0; jj < JT; ++jj) acc[it][jj] = F::mma(wt, Vf[jj], acc[it][jj]);
+                }
+            } else {
+                // exact path: m <- f_t (.) m + w_t v_t^T, o_t = q_t^T m, token by token
+                const OpRaw<K>& o = sm.op[par].raw;
+                for (int t = 0; t < L; ++t) {
+                    float vj[JT];
+#pragma unroll
+                    for (int jj = 0; jj < JT; ++jj) vj[jj] = (float)sm.VT[par][(mw * JT + jj) * 16 + c16][t];
+                    float part[JT];
+#pragma unroll
+                    for (int jj = 0; jj < JT; ++jj) part[jj] = 0.f;
+#pragma unroll
+                    for (int it = 0; it < IT; ++it) {
+                        const f32x4 fi = *(const f32x4*)&o.f[t][it * 16 + 4 * g];
+                        const f32x4 wi = *(const f32x4*)&o.w[t][it * 16 + 4 * g];
+                        const f32x4 qi = Quad<TIn>::to_f32(
+                            *(const typename Quad<TIn>::V*)(qp + (rowbase + t0 + t) * DK + it * 16 + 4 * g));
+#pragma unroll
+                        for (int jj = 0; jj < JT; ++jj) {
+                            acc[it][jj] = fi * acc[it][jj] + wi * vj[jj];
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) part[jj] += qi[e] * acc[it][jj][e];
+                        }
+                        // rarely taken path: keep its loads next to their uses so
+                        // it does not raise the register demand of the kernel
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+#pragma unroll
+                    for (int jj = 0; jj < JT; ++jj) {
+                        part[jj] += __shfl_xor(part[jj], 16, 64);
+                        part[jj] += __shfl_xor(part[jj], 32, 64);
+                        if (g == 0)
+                            op[(rowbase + t0 + t) * p.dv + (size_t)vt * DV + (mw * JT + jj) * 16 + c16] =
+                                (TIn)part[jj];
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    };
+    for (int c = -2; c < nsteps - 2; ++c) step(c);
+    __syncthreads();
+    if (p.etaT && nchunks > 0) {
+        const int lp = (nchunks - 1) & 1;
+#pragma unroll
+        for (int it = 0; it < IT; ++it)
+#pragma unroll
+            for (int jj = 0; jj < JT; ++jj) {
+                const int j = vt * DV + (mw * JT + jj) * 16 + c16;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int i = it * 16 + 4 * g + e;
-                    const int j = vt * DV + jt * 16 + c16;
-                    p.etaT[((size_t)bh * DK + i) * p.dv + j] =
-                        accM[it][jj][e] * sm.E[par ^ 1][i] * sm.lT[i];
+                    p.etaT[((size_t)bh * DK + i) * p.dv + j] = acc[it][jj][e] * sm.E[lp][i] * sm.lT[i];
                 }
             }
     }
 }
 
 template <typename TIn, int DK, int DV>
-__global__ __launch_bounds__((PCfg<TIn, DK, DV>::NT)) void kla_fwd_diag_pipe_kernel(FwdArgs p) {
-    typedef PCfg<TIn, DK, DV> K;
-    __shared__ PSmem<TIn, K> sm;
+__global__ __launch_bounds__((P3<TIn, DK, DV>::NT)) void kla_fwd_diag_pipe_kernel(FwdArgs p) {
+    typedef P3<TIn, DK, DV> K;
+    __shared__ S3<TIn, K> sm;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int BH = p.B * p.H, nvt = p.n_vtiles;
     int bh, vt;
@@ -533,41 +575,44 @@ __global__ __launch_bounds__((PCfg<TIn, DK, DV>::NT)) void kla_fwd_diag_pipe_ker
             vt = id % nvt;
         }
     }
-    // Both roles execute the same sequence of workgroup barriers.
+    if (threadIdx.x < 4) sm.bad[threadIdx.x] = 0;
+    __syncthreads();
+    // All roles run the same even number of pipeline steps (nchunks + 2,
+    // rounded up) with one barrier each, then one more.
     if (wave < K::NCW)
         chain_role<TIn, K>(sm, p, bh, vt, wave, lane);
+    else if (wave < K::NCW + K::NMW)
+        mma_role<TIn, K>(sm, p, bh, vt, wave - K::NCW, lane);
     else
-        gate_role<TIn, K>(sm, p, bh, vt, wave - K::NCW, lane);
+        gate_role<TIn, K>(sm, p, bh, vt, wave - K::NCW - K::NMW, lane);
 }
 
 template <typename TIn, int DK, int DV>
 hipError_t launch(const FwdArgs& a, hipStream_t s) {
-    typedef PCfg<TIn, DK, DV> K;
+    typedef P3<TIn, DK, DV> K;
     const int nblk = a.B * a.H * a.n_vtiles;
     hipLaunchKernelGGL((kla_fwd_diag_pipe_kernel<TIn, DK, DV>), dim3(nblk), dim3(K::NT), 0, s, a);
     return hipGetLastError();
 }
 
-template <typename TIn>
-hipError_t dispatch(const FwdArgs& a, hipStream_t s) {
-    const int dvt = a.dv / a.n_vtiles;
-    if (a.dk != a.dv || a.dv % a.n_vtiles) return hipErrorInvalidValue;
-    if (a.dk == 128 && dvt == 128) return launch<TIn, 128, 128>(a, s);
-    if (a.dk == 128 && dvt == 64) return launch<TIn, 128, 64>(a, s);
-    if (a.dk == 64 && dvt == 64) return launch<TIn, 64, 64>(a, s);
-    return hipErrorInvalidValue;
-}
-
 }  // namespace
 
-bool fwd_diag_pipe_supported(int dk, int dv, int nvt) {
-    if (dk != dv || dv % nvt) return false;
+bool fwd_diag_pipe_supported(int dk, int dv, int nvt, int dtype) {
+    if (dk != dv || nvt < 1 || dv % nvt) return false;
     const int dvt = dv / nvt;
-    return (dk == 128 && (dvt == 128 || dvt == 64)) || (dk == 64 && dvt == 64);
+    if (dtype == DT_BF16) return (dk == 128 && (dvt == 128 || dvt == 64)) || (dk == 64 && dvt == 64);
+    return dk == 64 && dvt == 64;
 }
 
 hipError_t launch_fwd_diag_pipe(const FwdArgs& a, int dtype, hipStream_t s) {
-    return dtype == DT_BF16 ? dispatch<bf16>(a, s) : dispatch<float>(a, s);
+    if (!fwd_diag_pipe_supported(a.dk, a.dv, a.n_vtiles, dtype)) return hipErrorInvalidValue;
+    const int dvt = a.dv / a.n_vtiles;
+    if (dtype == DT_BF16) {
+        if (a.dk == 128 && dvt == 128) return launch<bf16, 128, 128>(a, s);
+        if (a.dk == 128 && dvt == 64) return launch<bf16, 128, 64>(a, s);
+        return launch<bf16, 64, 64>(a, s);
+    }
+    return launch<float, 64, 64>(a, s);
 }
 
 }  // namespace kla

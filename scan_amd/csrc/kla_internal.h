@@ -45,7 +45,7 @@ enum Dt { DT_F32 = 0, DT_BF16 = 1 };
 // combination they were not instantiated for.
 hipError_t launch_fwd_diag(const FwdArgs& a, int dtype, hipStream_t s);
 hipError_t launch_fwd_diag_pipe(const FwdArgs& a, int dtype, hipStream_t s);
-bool fwd_diag_pipe_supported(int dk, int dv, int nvt);
+bool fwd_diag_pipe_supported(int dk, int dv, int nvt, int dtype);
 hipError_t launch_fwd_iso(const FwdArgs& a, int dtype, hipStream_t s);
 hipError_t launch_step(const StepArgs& a, int dtype, int cov, hipStream_t s);
 hipError_t launch_fwd_empty(const FwdArgs& a, int cov, hipStream_t s);
