@@ -130,6 +130,15 @@ klaStatus klaStep(const klaDims* d,
 /* Static, human-readable description of a status code (never NULL). */
 const char* klaStatusString(klaStatus s);
 
+/*
+ * Diagnostic: name of the kernel family that klaFwd launches for these dims
+ * (the name profilers show, e.g. "kla_fwd_diag_pipe_kernel"; " (value tiles)"
+ * is appended when each (b,h) is split over several workgroups by value
+ * columns).  Static string, never NULL; "" for NULL, invalid or unsupported
+ * dims.  Honours the same environment overrides as klaFwd.
+ */
+const char* klaFwdKernelName(const klaDims* d);
+
 #ifdef __cplusplus
 }
 #endif

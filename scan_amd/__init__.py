@@ -73,6 +73,8 @@ def load():
     lib.klaStep.restype = ctypes.c_int
     lib.klaStatusString.argtypes = [ctypes.c_int]
     lib.klaStatusString.restype = ctypes.c_char_p
+    lib.klaFwdKernelName.argtypes = [dp]
+    lib.klaFwdKernelName.restype = ctypes.c_char_p
     _lib = lib
     return lib
 
@@ -103,6 +105,17 @@ def klaStatusString(status: int) -> str:
         return load().klaStatusString(int(status)).decode()
     except RuntimeError:
         return STATUS_NAMES.get(int(status), f"status {status}")
+
+
+def klaFwdKernelName(dims: KlaDims) -> str:
+    return load().klaFwdKernelName(ctypes.byref(dims)).decode()
+
+
+def fwd_kernel_name(B, H, T, dk, dv, cov="diag", dtype="bf16") -> str:
+    """Kernel family klaFwd launches for these sizes (for profiles and reports)."""
+    dims = KlaDims(B, H, T, dk, dv, KLA_BF16 if dtype == "bf16" else KLA_F32,
+                   KLA_DIAG if cov == "diag" else KLA_ISO)
+    return klaFwdKernelName(dims)
 
 
 # ------------------------------------------------------------------ torch helpers

@@ -53,9 +53,41 @@ int env_vtiles() {
     return atoi(s);
 }
 
+// Kernel that klaFwd launches for these (supported) dims; n_vtiles receives
+// the number of value-column tiles each (b,h) is split into.
+enum FwdKernel { FK_EMPTY, FK_ISO, FK_DIAG_PIPE, FK_DIAG_CHUNK };
+
+FwdKernel pick_kernel(const klaDims* d, int* n_vtiles) {
+    const int nvt_env = env_vtiles();
+    if (d->T == 0) {
+        *n_vtiles = 1;
+        return FK_EMPTY;
+    }
+    if (d->cov == KLA_ISO) {
+        *n_vtiles = nvt_env > 0 ? nvt_env : kla::fwd_iso_vtiles(d->B, d->H, d->dk);
+        return FK_ISO;
+    }
+    *n_vtiles = nvt_env > 0 ? nvt_env : kla::fwd_diag_vtiles(d->B, d->H, d->T, d->dk, d->dv);
+    if (use_pipe() && kla::fwd_diag_pipe_supported(d->dk, d->dv, *n_vtiles, d->dtype))
+        return FK_DIAG_PIPE;
+    return FK_DIAG_CHUNK;
+}
+
 }  // namespace
 
 extern "C" {
+
+const char* klaFwdKernelName(const klaDims* d) {
+    if (!d || !dims_ok(d) || !supported(d)) return "";
+    int nvt = 1;
+    switch (pick_kernel(d, &nvt)) {
+        case FK_EMPTY: return "kla_fwd_empty_kernel";
+        case FK_ISO: return nvt > 1 ? "kla_fwd_iso_kernel (value tiles)" : "kla_fwd_iso_kernel";
+        case FK_DIAG_PIPE:
+            return nvt > 1 ? "kla_fwd_diag_pipe_kernel (value tiles)" : "kla_fwd_diag_pipe_kernel";
+        default: return nvt > 1 ? "kla_fwd_diag_kernel (value tiles)" : "kla_fwd_diag_kernel";
+    }
+}
 
 int klaIsSupported(const klaDims* d) {
     if (!d || !dims_ok(d)) return 0;
@@ -112,24 +144,16 @@ klaStatus klaFwd(const klaDims* d, const void* q, const void* k, const void* v, 
     hipStream_t st = (hipStream_t)hipStream;
 
     hipError_t e;
-    if (!has_tokens) {
-        fa.n_vtiles = 1;
-        e = kla::launch_fwd_empty(fa, iso ? 1 : 0, st);
-    } else {
-        const int nvt_env = env_vtiles();
-        if (iso) {
-            fa.n_vtiles = nvt_env > 0 ? nvt_env : kla::fwd_iso_vtiles(fa.B, fa.H, fa.dk);
+    switch (pick_kernel(d, &fa.n_vtiles)) {
+        case FK_EMPTY: e = kla::launch_fwd_empty(fa, iso ? 1 : 0, st); break;
+        case FK_ISO:
             if (fa.dv % fa.n_vtiles) return KLA_ERR_UNSUPPORTED;
             e = kla::launch_fwd_iso(fa, d->dtype, st);
-        } else {
-            fa.n_vtiles = nvt_env > 0 ? nvt_env : kla::fwd_diag_vtiles(fa.B, fa.H, fa.T, fa.dk, fa.dv);
-            if (use_pipe() && kla::fwd_diag_pipe_supported(fa.dk, fa.dv, fa.n_vtiles, d->dtype))
-                e = kla::launch_fwd_diag_pipe(fa, d->dtype, st);
-            else
-                e = kla::launch_fwd_diag(fa, d->dtype, st);
-        }
-        if (e == hipErrorInvalidValue) return KLA_ERR_UNSUPPORTED;
+            break;
+        case FK_DIAG_PIPE: e = kla::launch_fwd_diag_pipe(fa, d->dtype, st); break;
+        default: e = kla::launch_fwd_diag(fa, d->dtype, st); break;
     }
+    if (e == hipErrorInvalidValue) return KLA_ERR_UNSUPPORTED;
     return e == hipSuccess ? KLA_OK : KLA_ERR_HIP;
 }
 

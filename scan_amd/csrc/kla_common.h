@@ -123,6 +123,48 @@ template <> struct Oct<float> {
     static __device__ __forceinline__ V zero() { V r; r.lo = f32x4{0.f, 0.f, 0.f, 0.f}; r.hi = r.lo; return r; }
 };
 
+// Range-checked loads through a buffer resource.  The descriptor holds a
+// 48-bit base, stride 0, a byte range and the gfx9-family format word; a load
+// whose (vector offset + immediate offset) falls at or past the range reads
+// zero, so chunk tails need no clamped addresses.  Per-token row offsets are
+// compile-time constants and fold into the 12-bit immediate field.
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// The base and range must be the same in every lane (they are read from the
+// first active lane, which keeps the descriptor in scalar registers).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+    const unsigned long long a = (unsigned long long)base;
+    const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)a);
+    const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(a >> 32));
+    void* b = (void*)(((unsigned long long)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(b, (short)0, __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
+template <typename V>
+__device__ __forceinline__ V buf_load(__amdgpu_buffer_rsrc_t r, int voff) {
+    if constexpr (sizeof(V) == 2) {
+        return __builtin_bit_cast(V, (unsigned short)__builtin_amdgcn_raw_buffer_load_b16(r, voff, 0, 0));
+    } else if constexpr (sizeof(V) == 4) {
+        return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0));
+    } else if constexpr (sizeof(V) == 8) {
+        return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0));
+    } else {
+        static_assert(sizeof(V) == 16, "2, 4, 8 or 16 bytes");
+        return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+    }
+}
+
+// Workgroup barrier that orders LDS only.  __syncthreads() also releases
+// global memory, which on gfx9 waits for every vector-memory load in flight
+// (vmcnt(0)) and so drains any prefetch at each barrier; waves that exchange
+// data only through LDS need just lgkmcnt(0) before the s_barrier.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }

@@ -65,6 +65,12 @@ struct P3 {
     static constexpr int VQ = DV / 4;
     static constexpr int VUNITS = (C / 2) * VQ;
     static constexpr int VPT = VUNITS / 256;
+    // chain and gate waves keep NBC / NBG chunks of inputs in registers and
+    // load NBC-1 / NBG-1 chunks ahead; every role runs a multiple of UNR
+    // pipeline steps
+    static constexpr int NBC = 2;
+    static constexpr int NBG = 2;
+    static constexpr int UNR = NBC * NBG / (NBC == NBG ? NBC : 1);
     static_assert(DK == 64 || DK == 128, "key dims 64 and 128");
     static_assert(DV % 32 == 0 && VUNITS % 256 == 0, "value tiles");
 };
@@ -180,13 +186,22 @@ __device__ __forceinline__ void store_row(T* dst, const T (&v)[N]) {
     }
 }
 
-// Wait until every outstanding vector-memory load of this wave has landed
-// (vmcnt(0); expcnt and lgkmcnt left at their maxima).  Called at the top of
-// a pipeline step, before the step issues the next chunk's loads: the
-// previous loads were issued a whole step earlier, so this costs nothing, and
-// the current chunk's registers then need no further waits however many new
-// loads are in flight (the hardware counter only tracks 63).
-__device__ __forceinline__ void wait_prev_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// Wait until at most N vector-memory operations of this wave are in flight
+// (expcnt and lgkmcnt left at their maxima; the counter holds at most 63).
+// Called at the top of a pipeline step, before the step issues its loads, with
+// N = the loads of the one chunk issued after the current chunk's: the current
+// chunk's registers then need no further waits, however many loads follow.
+template <int N>
+__device__ __forceinline__ void wait_loads() {
+    constexpr int n = N < 63 ? N : 63;
+    __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Pipeline steps of every role: nchunks + 2, rounded up to a multiple of UNR.
+template <class K>
+__device__ __forceinline__ int pipe_steps(int nchunks) {
+    return (nchunks + 2 + K::UNR - 1) / K::UNR * K::UNR;
+}
 
 __device__ __forceinline__ int chunk_len(int T, int c, int C) {
     const int n = T - c * C;
@@ -200,37 +215,62 @@ __device__ void chain_role(S3<TIn, K>& sm, const FwdArgs& p, int bh, int vt, int
     const int i = cw * 64 + lane;
     const size_t rowbase = (size_t)bh * p.T;
     const int nchunks = (p.T + C - 1) / C;
-    const int nsteps = (nchunks + 3) & ~1;  // nchunks + 2 pipeline steps, rounded up to even
+    const int nsteps = pipe_steps<K>(nchunks);
     const TIn* kp = (const TIn*)p.k;
 
     float l = p.l0 ? p.l0[(size_t)bh * DK + i] : 1.f;
     const float qn = p.qn[(size_t)(bh % p.H) * DK + i];
-    // One chunk of inputs per buffer; the two buffers alternate, so a chunk's
-    // loads are issued a whole iteration before their first use.
+    // One chunk of inputs per buffer; NBC buffers rotate, so a chunk's loads
+    // are issued NBC-1 iterations before their first use.
+    constexpr int NB = K::NBC, D = NB - 1;
     struct Buf {
         float a[C];
-        TIn k[C];
-        float r;  // r of token `lane` of the chunk
+        unsigned k[C];  // bits of k, zero-extended (bf16 values sit in the low half)
+        float r;        // r of token `lane` of the chunk
     };
-    Buf b0, b1;
+    Buf b[NB];
 
+    // Rows of a and k are read through buffer resources that each span a
+    // 4 KiB window of rows, so the row offsets are immediates and rows past T
+    // (the tail of the last chunk, chunks past the end) read as zero.
+    constexpr int ARB = DK * 4, KRB = DK * (int)sizeof(TIn);  // row bytes
+    constexpr int ARW = 4096 / ARB < C ? 4096 / ARB : C;       // rows per window
+    constexpr int KRW = 4096 / KRB < C ? 4096 / KRB : C;
+    const char* abase = (const char*)(p.a + rowbase * DK);
+    const char* kbase = (const char*)(kp + rowbase * DK);
+    const char* rbase = (const char*)(p.r + rowbase);
+    auto rows_left = [&](int t, int cap) {
+        const int n = p.T - t;
+        return n < 0 ? 0 : (n < cap ? n : cap);
+    };
     auto load = [&](int c, Buf& b) {
-        const int t0 = c * C, L = chunk_len(p.T, c, C);
+        const int t0 = c * C;
 #pragma unroll
-        for (int t = 0; t < C; ++t) {
-            const size_t off = (rowbase + t0 + (t < L ? t : L - 1)) * DK + i;
-            b.a[t] = p.a[off];
-            b.k[t] = kp[off];
+        for (int w = 0; w < C / ARW; ++w) {
+            const int tw = t0 + w * ARW;
+            const auto rs = make_rsrc(abase + (size_t)tw * ARB, rows_left(tw, ARW) * ARB);
+#pragma unroll
+            for (int t = 0; t < ARW; ++t) b.a[w * ARW + t] = buf_load<float>(rs, i * 4 + t * ARB);
         }
-        b.r = p.r[rowbase + t0 + (lane < L ? lane : L - 1)];
+#pragma unroll
+        for (int w = 0; w < C / KRW; ++w) {
+            const int tw = t0 + w * KRW;
+            const auto rs = make_rsrc(kbase + (size_t)tw * KRB, rows_left(tw, KRW) * KRB);
+#pragma unroll
+            for (int t = 0; t < KRW; ++t)
+                b.k[w * KRW + t] = sizeof(TIn) == 2
+                                       ? (unsigned)buf_load<unsigned short>(rs, i * 2 + t * KRB)
+                                       : buf_load<unsigned>(rs, i * 4 + t * KRB);
+        }
+        b.r = buf_load<float>(make_rsrc(rbase + (size_t)t0 * 4, rows_left(t0, C) * 4), lane * 4);
     };
     auto step = [&](int c, Buf& cur, Buf& nxt) {
         const int cc = c + 2;  // chunk scanned in this iteration
-        wait_prev_loads();
-        if (nchunks > 0) load(cc + 1 < nchunks ? cc + 1 : nchunks - 1, nxt);
+        wait_loads<(D - 1) * (2 * C + 1)>();
+        if (nchunks > 0) load(cc + D, nxt);
         if (cc < nchunks) {
             const int L = chunk_len(p.T, cc, C), par = cc & 1;
-            const float rho = 1.f / cur.r;
+            const float rho = lane < L ? 1.f / cur.r : 0.f;
             if (cw == 0 && lane < C) sm.rho[par][lane] = rho;
             // full chunks take a copy of the scan without per-token tests
             auto scan = [&](auto full) {
@@ -241,7 +281,9 @@ __device__ void chain_role(S3<TIn, K>& sm, const FwdArgs& p, int bh, int vt, int
                     if (FULL || t < L) {
                         const float rt = __builtin_bit_cast(
                             float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rho), t));
-                        const float a = cur.a[t], kv = (float)cur.k[t];
+                        const float a = cur.a[t];
+                        const float kv = __builtin_bit_cast(
+                            float, sizeof(TIn) == 2 ? cur.k[t] << 16 : cur.k[t]);
                         const float lp = l * fast_rcp(__builtin_fmaf(qn, l, a * a));
                         l = __builtin_fmaf(kv * kv, rt, lp);
                         const float alp = a * lp;
@@ -255,17 +297,21 @@ __device__ void chain_role(S3<TIn, K>& sm, const FwdArgs& p, int bh, int vt, int
             const float G = L == C ? scan(std::true_type{}) : scan(std::false_type{});
             if (__builtin_amdgcn_ballot_w64(G < kFloor)) sm.bad[cc & 3] = 1;
         }
-        __syncthreads();
+        lds_barrier();
     };
 
-    if (nchunks > 0) load(0, b0);
-    for (int c = -2; c < nsteps - 2; c += 2) {
-        step(c, b0, b1);
-        step(c + 1, b1, b0);
+    if (nchunks > 0) {
+#pragma unroll
+        for (int j = 0; j < D; ++j) load(j, b[j]);
+    }
+    // step c scans chunk c+2 from buffer (c+2) mod NB and loads chunk c+2+D
+    for (int c = -2; c < nsteps - 2; c += NB) {
+#pragma unroll
+        for (int s = 0; s < NB; ++s) step(c + s, b[s], b[(s + D) % NB]);
     }
     sm.lT[i] = l;
     if (p.lT && vt == 0) p.lT[(size_t)bh * DK + i] = l;
-    __syncthreads();
+    lds_barrier();
 }
 
 // ------------------------------------------------------------------ gate role
@@ -275,7 +321,7 @@ __device__ void gate_role(S3<TIn, K>& sm, const FwdArgs& p, int bh, int vt, int 
     constexpr int C = K::C, DK = K::DK, DV = K::DV, TPG = K::TPG;
     const size_t rowbase = (size_t)bh * p.T;
     const int nchunks = (p.T + C - 1) / C;
-    const int nsteps = (nchunks + 3) & ~1;
+    const int nsteps = pipe_steps<K>(nchunks);
     const int grp = lane % K::NGRP, ipl = lane / K::NGRP;
     const int ip = gw * K::IPW + ipl;
     const int gtid = gw * 64 + lane;
@@ -287,33 +333,46 @@ __device__ void gate_role(S3<TIn, K>& sm, const FwdArgs& p, int bh, int vt, int 
         typename PR::V q[TPG], k[TPG];
         typename Quad<TIn>::V v[K::VPT][2];
     };
-    Buf b0, b1;
+    constexpr int NB = K::NBG, D = NB - 1;
+    Buf b[NB];
+    constexpr int NLD = 2 * TPG + 2 * K::VPT;  // loads per chunk
+    // Each chunk is read through buffer resources spanning its rows, so rows
+    // past T read as zero; a lane's token rows are immediates from its offset.
+    constexpr int ES = (int)sizeof(TIn), QRB = DK * ES;
+    const int VRB = p.dv * ES;
+    const char* qbase = (const char*)(qp + rowbase * DK);
+    const char* kbase = (const char*)(kp + rowbase * DK);
+    const char* vbase = (const char*)(vp + rowbase * p.dv);
+    const int qoff = grp * TPG * QRB + 2 * ip * ES;
+    int voff[K::VPT][2];
+#pragma unroll
+    for (int x = 0; x < K::VPT; ++x) {
+        const int unit = gtid + x * 256;
+        const int tp = unit / K::VQ, jq = unit % K::VQ;
+        voff[x][0] = 2 * tp * VRB + (vt * DV + 4 * jq) * ES;
+        voff[x][1] = voff[x][0] + VRB;
+    }
     auto load = [&](int c, Buf& bf) {
-        const int t0 = c * C, L = chunk_len(p.T, c, C);
+        const int t0 = c * C, n = p.T - t0;
+        const int rows = n < 0 ? 0 : (n < C ? n : C);
+        const auto rq = make_rsrc(qbase + (size_t)t0 * QRB, rows * QRB);
+        const auto rk = make_rsrc(kbase + (size_t)t0 * QRB, rows * QRB);
+        const auto rv = make_rsrc(vbase + (size_t)t0 * VRB, rows * VRB);
 #pragma unroll
         for (int u = 0; u < TPG; ++u) {
-            const int t = grp * TPG + u;
-            const size_t off = (rowbase + t0 + (t < L ? t : L - 1)) * DK + 2 * ip;
-            bf.q[u] = *(const typename PR::V*)(qp + off);
-            bf.k[u] = *(const typename PR::V*)(kp + off);
+            bf.q[u] = buf_load<typename PR::V>(rq, qoff + u * QRB);
+            bf.k[u] = buf_load<typename PR::V>(rk, qoff + u * QRB);
         }
 #pragma unroll
-        for (int x = 0; x < K::VPT; ++x) {
-            const int unit = gtid + x * 256;
-            const int tp = unit / K::VQ, jq = unit % K::VQ;
+        for (int x = 0; x < K::VPT; ++x)
 #pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-                const int t = 2 * tp + h2;
-                const size_t off = (rowbase + t0 + (t < L ? t : L - 1)) * p.dv + (size_t)vt * DV + 4 * jq;
-                bf.v[x][h2] = *(const typename Quad<TIn>::V*)(vp + off);
-            }
-        }
+            for (int h2 = 0; h2 < 2; ++h2) bf.v[x][h2] = buf_load<typename Quad<TIn>::V>(rv, voff[x][h2]);
     };
 
     auto step = [&](int c, Buf& cur, Buf& nxt) {
         const int cg = c + 1;  // chunk gated in this iteration
-        wait_prev_loads();
-        if (nchunks > 0) load(cg + 1 < nchunks ? (cg + 1 > 0 ? cg + 1 : 0) : nchunks - 1, nxt);
+        wait_loads<(D - 1) * NLD>();
+        if (nchunks > 0) load(cg + D, nxt);
         if (cg >= 0 && cg < nchunks) {
             const int L = chunk_len(p.T, cg, C), par = cg & 1;
             // V^T of the chunk
@@ -397,17 +456,21 @@ __device__ void gate_role(S3<TIn, K>& sm, const FwdArgs& p, int bh, int vt, int 
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
     };
 
     if (gtid < DK) sm.E[1][gtid] = 1.f;
-    // iteration c gates chunk c+1, which sits in b0 when c is odd; the first
-    // iteration only loads chunk 0
-    for (int c = -2; c < nsteps - 2; c += 2) {
-        step(c, b1, b0);
-        step(c + 1, b0, b1);
+    // step c gates chunk c+1 from buffer (c+1) mod NB and loads chunk c+1+D;
+    // the first step only loads
+    if (nchunks > 0) {
+#pragma unroll
+        for (int j = 0; j < D - 1; ++j) load(j, b[j]);
     }
-    __syncthreads();
+    for (int c = -2; c < nsteps - 2; c += NB) {
+#pragma unroll
+        for (int s = 0; s < NB; ++s) step(c + s, b[(s + NB - 1) % NB], b[(s + NB - 2) % NB]);
+    }
+    lds_barrier();
 }
 
 // ------------------------------------------------------------------ MMA role
@@ -418,7 +481,7 @@ __device__ void mma_role(S3<TIn, K>& sm, const FwdArgs& p, int bh, int vt, int m
     constexpr int C = K::C, DK = K::DK, DV = K::DV, IT = K::IT, JT = K::JT, KB = K::KB;
     const size_t rowbase = (size_t)bh * p.T;
     const int nchunks = (p.T + C - 1) / C;
-    const int nsteps = (nchunks + 3) & ~1;
+    const int nsteps = pipe_steps<K>(nchunks);
     const int c16 = lane & 15, g = lane >> 4;
     TIn* op = (TIn*)p.o;
     const TIn* qp = (const TIn*)p.q;
@@ -537,10 +600,10 @@ __device__ void mma_role(S3<TIn, K>& sm, const FwdArgs& p, int bh, int vt, int m
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
     };
     for (int c = -2; c < nsteps - 2; ++c) step(c);
-    __syncthreads();
+    lds_barrier();
     if (p.etaT && nchunks > 0) {
         const int lp = (nchunks - 1) & 1;
 #pragma unroll
@@ -576,9 +639,9 @@ __global__ __launch_bounds__((P3<TIn, DK, DV>::NT)) void kla_fwd_diag_pipe_kerne
         }
     }
     if (threadIdx.x < 4) sm.bad[threadIdx.x] = 0;
-    __syncthreads();
-    // All roles run the same even number of pipeline steps (nchunks + 2,
-    // rounded up) with one barrier each, then one more.
+    lds_barrier();
+    // All roles run the same number of pipeline steps (nchunks + 2, rounded
+    // up to a multiple of UNR) with one barrier each, then one more.
     if (wave < K::NCW)
         chain_role<TIn, K>(sm, p, bh, vt, wave, lane);
     else if (wave < K::NCW + K::NMW)

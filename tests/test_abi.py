@@ -150,3 +150,18 @@ def test_header_documents_every_entry_point():
         # every declaration is preceded by a comment block
         idx = text.index(n + "(")
         assert "*/" in text[max(0, idx - 600):idx], n
+
+
+def test_kernel_name_reports_the_dispatch():
+    lm = KlaDims(8, 16, 2048, 128, 128, BF16, DIAG)
+    assert scan_amd.klaFwdKernelName(lm) == "kla_fwd_diag_pipe_kernel (value tiles)"
+    assert scan_amd.klaFwdKernelName(KlaDims(64, 16, 2048, 128, 128, BF16, DIAG)) == \
+        "kla_fwd_diag_pipe_kernel"
+    assert scan_amd.klaFwdKernelName(KlaDims(2, 3, 100, 32, 32, F32, DIAG)) == "kla_fwd_diag_kernel"
+    assert scan_amd.klaFwdKernelName(KlaDims(2, 3, 100, 64, 64, F32, ISO)).startswith(
+        "kla_fwd_iso_kernel")
+    assert scan_amd.klaFwdKernelName(KlaDims(2, 3, 0, 64, 64, BF16, DIAG)) == "kla_fwd_empty_kernel"
+    assert scan_amd.klaFwdKernelName(KlaDims(1, 1, 8, 48, 48, BF16, DIAG)) == ""
+    assert scan_amd.klaFwdKernelName(KlaDims(-1, 1, 8, 64, 64, BF16, DIAG)) == ""
+    lib = scan_amd.load()
+    assert lib.klaFwdKernelName(None) == b""
