@@ -96,8 +96,8 @@ struct S3 {
     } op[2];                      // MFMA operands (or raw gates) by chunk parity
     TIn VT[2][K::DV][K::CS];      // v^T by chunk parity
     float rho[2][K::C];           // 1/r_t by chunk parity
-    float sc[2][K::DK];           // state scale before the chunk's readout
-    float E[2][K::DK];            // end-of-chunk gate product (pending state scale)
+    alignas(16) float sc[2][K::DK];  // state scale before the chunk's readout
+    alignas(16) float E[2][K::DK];   // end-of-chunk gate product (pending state scale)
     float lT[K::DK];
     int bad[4];                   // chunk needs the exact token-by-token path
 };
@@ -399,44 +399,52 @@ __device__ void gate_role(S3<TIn, K>& sm, const FwdArgs& p, int bh, int vt, int 
                 w[u][1] = PR::hi(cur.k[u]) * rh * rl1;
             }
             const float* Eprev = sm.E[par ^ 1];
-            if (!sm.bad[cg & 3]) {
+            // Factorised operands.  Full chunks take a copy with no per-token
+            // tests, so the whole step is one basic block the compiler can
+            // schedule; only the lanes holding token 0 or the last token
+            // store the state prescale and the chunk-end gate.
+            auto fac = [&](auto full) {
+                constexpr bool FULL = decltype(full)::value;
                 float G[TPG][2];
                 float p0 = 1.f, p1 = 1.f;
 #pragma unroll
                 for (int u = 0; u < TPG; ++u) {
                     const int t = grp * TPG + u;
-                    if (t > 0 && t < L) { p0 *= f[u][0]; p1 *= f[u][1]; }
+                    const bool inc = FULL ? (u > 0 || grp > 0) : (t > 0 && t < L);
+                    p0 *= inc ? f[u][0] : 1.f;
+                    p1 *= inc ? f[u][1] : 1.f;
                     G[u][0] = p0;
                     G[u][1] = p1;
                 }
                 const float e0 = group_excl_prod<K>(p0, grp), e1 = group_excl_prod<K>(p1, grp);
                 TIn wt0[TPG], wt1[TPG];
+                float gl0 = 1.f, gl1 = 1.f;
 #pragma unroll
                 for (int u = 0; u < TPG; ++u) {
                     const int t = grp * TPG + u;
                     const float g0 = G[u][0] * e0, g1 = G[u][1] * e1;
-                    float q0 = 0.f, q1 = 0.f, w0 = 0.f, w1 = 0.f;
-                    if (t < L) {
-                        q0 = PR::lo(cur.q[u]) * g0;
-                        q1 = PR::hi(cur.q[u]) * g1;
-                        w0 = w[u][0] * fast_rcp(g0);
-                        w1 = w[u][1] * fast_rcp(g1);
-                    }
+                    const bool in = FULL || t < L;
+                    const float q0 = in ? PR::lo(cur.q[u]) * g0 : 0.f;
+                    const float q1 = in ? PR::hi(cur.q[u]) * g1 : 0.f;
+                    const float w0 = in ? w[u][0] * fast_rcp(g0) : 0.f;
+                    const float w1 = in ? w[u][1] * fast_rcp(g1) : 0.f;
                     *(typename PR::V*)&sm.op[par].fac.Q[t][2 * ip] = PR::make(q0, q1);
                     *(typename PR::V*)&sm.op[par].fac.W[t][2 * ip] = PR::make(w0, w1);
                     wt0[u] = (TIn)w0;
                     wt1[u] = (TIn)w1;
-                    if (t == 0) {
-                        sm.sc[par][2 * ip] = Eprev[2 * ip] * f[u][0];
-                        sm.sc[par][2 * ip + 1] = Eprev[2 * ip + 1] * f[u][1];
-                    }
-                    if (t == L - 1) {
-                        sm.E[par][2 * ip] = g0;
-                        sm.E[par][2 * ip + 1] = g1;
-                    }
+                    if (!FULL && t == L - 1) { gl0 = g0; gl1 = g1; }
+                    if (FULL && u == TPG - 1) { gl0 = g0; gl1 = g1; }
                 }
                 store_row<TIn, TPG>(&sm.op[par].fac.WT[2 * ip][grp * TPG], wt0);
                 store_row<TIn, TPG>(&sm.op[par].fac.WT[2 * ip + 1][grp * TPG], wt1);
+                if (grp == 0) *(f32x2*)&sm.sc[par][2 * ip] =
+                    f32x2{Eprev[2 * ip] * f[0][0], Eprev[2 * ip + 1] * f[0][1]};
+                const int gend = FULL ? K::NGRP - 1 : (L - 1) / TPG;
+                if (grp == gend) *(f32x2*)&sm.E[par][2 * ip] = f32x2{gl0, gl1};
+            };
+            if (!__builtin_amdgcn_readfirstlane(sm.bad[cg & 3])) {
+                if (L == C) fac(std::true_type{});
+                else fac(std::false_type{});
             } else {
                 // flagged chunk: raw fp32 gates for the token-by-token path
 #pragma unroll
@@ -504,7 +512,7 @@ __device__ void mma_role(S3<TIn, K>& sm, const FwdArgs& p, int bh, int vt, int m
     auto step = [&](int c) {
         if (c >= 0 && c < nchunks) {
             const int L = chunk_len(p.T, c, C), par = c & 1, t0 = c * C;
-            const bool bad = sm.bad[c & 3];
+            const bool bad = __builtin_amdgcn_readfirstlane(sm.bad[c & 3]);
             if (mw == 0 && lane == 0 && c >= 1) sm.bad[(c - 1) & 3] = 0;
             // m <- sc (.) m
 #pragma unroll
@@ -551,10 +559,15 @@ __device__ void mma_role(S3<TIn, K>& sm, const FwdArgs& p, int bh, int vt, int m
                     out0 = F::mma(Vf[jj], P0, out0);
                     out1 = F::mma(Vf[jj], P1, out1);
                     const size_t col = (size_t)vt * DV + (mw * JT + jj) * 16 + 4 * g;
-                    if (c16 < L)
-                        *(typename Quad<TIn>::V*)(op + (rowbase + t0 + c16) * p.dv + col) = Quad<TIn>::make(out0);
-                    if (16 + c16 < L)
-                        *(typename Quad<TIn>::V*)(op + (rowbase + t0 + 16 + c16) * p.dv + col) = Quad<TIn>::make(out1);
+                    typename Quad<TIn>::V* o0 = (typename Quad<TIn>::V*)(op + (rowbase + t0 + c16) * p.dv + col);
+                    typename Quad<TIn>::V* o1 = (typename Quad<TIn>::V*)(op + (rowbase + t0 + 16 + c16) * p.dv + col);
+                    if (L == C) {
+                        *o0 = Quad<TIn>::make(out0);
+                        *o1 = Quad<TIn>::make(out1);
+                    } else {
+                        if (c16 < L) *o0 = Quad<TIn>::make(out0);
+                        if (16 + c16 < L) *o1 = Quad<TIn>::make(out1);
+                    }
                 }
                 // m += W^^T V
 #pragma unroll
