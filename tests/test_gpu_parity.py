@@ -221,3 +221,24 @@ def test_vtile_split_invariance(monkeypatch):
     b = run_hip(inp, "diag")
     for k in a:
         assert np.array_equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("d,dtype", [(128, "bf16"), (64, "f32")])
+def test_parity_rescale_and_exact_mix(d, dtype):
+    """Decay regimes in sequence: strong decay (the deferred state scale is
+    folded back every chunk), near-zero gates (exact token-by-token chunks),
+    then ordinary decay, with a non-trivial initial state."""
+    _print_case("rescale-mix", d, dtype)
+    T = 520
+    inp = gen.make_inputs("small_diag", seed=12, B=1, H=2, T=T, dk=d, dv=d, dtype=dtype)
+    g = torch.Generator().manual_seed(13)
+    a = torch.sigmoid(2.0 + torch.randn(1, 2, T, d, generator=g, dtype=torch.float64))
+    a[:, :, :200] = 0.35 + 0.1 * torch.rand(1, 2, 200, d, generator=g, dtype=torch.float64)
+    a[:, :, 260:330] = 0.01
+    inp["a"] = a.float()
+    st = gen.make_state(inp["workload"], seed=14)
+    hip = run_hip(inp, "diag", st["l0"], st["eta0"])
+    for k in hip:
+        assert np.all(np.isfinite(hip[k])), k
+    ref = run_oracle(inp, "diag", st["l0"], st["eta0"])
+    assert_parity(compare(hip, ref), dtype, "rescale-mix")
