@@ -75,6 +75,95 @@ def alg_bytes(w) -> float:
     return float(ntok * per_tok + w.B * w.H * per_seq)
 
 
+def decode_alg_bytes(w) -> float:
+    """Algorithmic HBM bytes of one decode step (one token for every (b,h)):
+    the fp32 state (l, eta) read and written in place, the token's inputs read
+    and its output written."""
+    es = 2 if w.dtype == "bf16" else 4
+    nl = 1 if w.cov == "iso" else w.dk
+    state = 4 * nl + 4 * w.dk * w.dv
+    tok = (2 * w.dk + w.dv) * es + 4 * (1 if w.cov == "iso" else w.dk) \
+        + 4 * (1 if w.cov == "iso" else 0) + 4 + w.dv * es
+    return float(w.B * w.H * (2 * state + tok))
+
+
+def run_decode(args, torch, np, scan_amd, gen) -> dict:
+    """One step = one klaStep for every (b,h) of the decode batch, from states
+    produced by a prefix forward (readings: 128-token prefix, seed 1; decode
+    tokens seed 2)."""
+    w = gen.DECODE
+    pre = gen.make_inputs(w, seed=1, device="cuda")
+    names = ("q", "k", "v", "a", "qn", "r")
+    _, l, eta = scan_amd.fwd(*(pre[n] for n in names), cov=w.cov)
+    n = gen.DECODE_STEPS
+    host = gen.make_inputs(w, seed=2, T=n)
+    toks = []
+    for t in range(n):
+        toks.append([host[x][:, :, t].contiguous().to("cuda") for x in names])
+    o = torch.empty(w.B, w.H, w.dv, dtype=toks[0][2].dtype, device="cuda")
+    for i in range(args.warmup):
+        scan_amd.step(*toks[i % n], l, eta, cov=w.cov, o=o)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    per = []
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(args.steps):
+        e_a = torch.cuda.Event(enable_timing=True)
+        e_b = torch.cuda.Event(enable_timing=True)
+        e_a.record(stream)
+        scan_amd.step(*toks[i % n], l, eta, cov=w.cov, o=o)
+        e_b.record(stream)
+        per.append((e_a, e_b))
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in per]))
+    nbytes = decode_alg_bytes(w)
+    achieved = nbytes / (kern_ms / 1e3) / 1e9
+    print(f"bench: decode {ms_per_step:.4f} ms/step (kernel {kern_ms:.4f} ms), {achieved:.1f} GB/s",
+          file=sys.stderr, flush=True)
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        threads = oracle.default_threads()
+        lh = l.cpu().numpy()
+        eh = eta.cpu().numpy()
+        hx = [[x.cpu() for x in tk] for tk in toks]
+        reps, t_cpu = 0, 0.0
+        while reps == 0 or (t_cpu < 0.5 * args.cpu_seconds and reps < 1000):
+            tk = hx[reps % n]
+            t0 = time.perf_counter()
+            res = oracle.step(*tk, lh, eh, cov=oracle.ISO if w.cov == "iso" else oracle.DIAG,
+                              nthreads=threads)
+            t_cpu += time.perf_counter() - t0
+            lh, eh = res["l"], res["eta"]
+            reps += 1
+        cpu = {"value": w.B * reps / t_cpu, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "sample": f"{reps} full decode steps (B={w.B}, H={w.H}), fp64, {t_cpu:.1f}s"}
+    return {
+        "metric": "KLA decode tokens/s (klaStep, constant-memory state)",
+        "value": w.B / (ms_per_step / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "dk": w.dk, "dv": w.dv, "cov": w.cov,
+                   "global_batch": w.B, "seq_len": 1, "parallelism": "none"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "kla_step_kernel", "alg_bytes": nbytes, "kernel_ms": kern_ms},
+        "cpu_baseline": cpu,
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -101,6 +190,9 @@ def main() -> int:
     import scan_amd
     from scan_amd import inputs as gen
 
+    if args.workload == gen.DECODE.name:
+        print(json.dumps(run_decode(args, torch, np, scan_amd, gen)), flush=True)
+        return 0
     w = gen.WORKLOADS[args.workload]
     print(f"bench: workload {w}", file=sys.stderr, flush=True)
     host = gen.make_inputs(w, seed=0)
