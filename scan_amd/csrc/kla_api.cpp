@@ -40,10 +40,15 @@ bool supported(const klaDims* d) {
                               : kla::fwd_iso_supported(d->dk, d->dv, d->dtype);
 }
 
-// KLA_FWD_DIAG_IMPL=chunk selects the single-role chunk kernel for every
-// diagonal shape (the wave-specialised kernel is used where it is built).
+// KLA_FWD_DIAG_IMPL=chunk / KLA_FWD_ISO_IMPL=chunk select the single-role
+// chunk kernels for every shape (the wave-specialised kernels are used where
+// they are built).
 bool use_pipe() {
     const char* s = getenv("KLA_FWD_DIAG_IMPL");
+    return !(s && s[0] == 'c');
+}
+bool use_iso_pipe() {
+    const char* s = getenv("KLA_FWD_ISO_IMPL");
     return !(s && s[0] == 'c');
 }
 
@@ -55,7 +60,7 @@ int env_vtiles() {
 
 // Kernel that klaFwd launches for these (supported) dims; n_vtiles receives
 // the number of value-column tiles each (b,h) is split into.
-enum FwdKernel { FK_EMPTY, FK_ISO, FK_DIAG_PIPE, FK_DIAG_CHUNK };
+enum FwdKernel { FK_EMPTY, FK_ISO, FK_ISO_PIPE, FK_DIAG_PIPE, FK_DIAG_CHUNK };
 
 FwdKernel pick_kernel(const klaDims* d, int* n_vtiles) {
     const int nvt_env = env_vtiles();
@@ -64,6 +69,12 @@ FwdKernel pick_kernel(const klaDims* d, int* n_vtiles) {
         return FK_EMPTY;
     }
     if (d->cov == KLA_ISO) {
+        const int nvt_pipe = nvt_env > 0 ? nvt_env : (d->dv % 64 == 0 ? d->dv / 64 : 0);
+        if (use_iso_pipe() && nvt_pipe > 0 &&
+            kla::fwd_iso_pipe_supported(d->dk, d->dv, nvt_pipe, d->dtype)) {
+            *n_vtiles = nvt_pipe;
+            return FK_ISO_PIPE;
+        }
         *n_vtiles = nvt_env > 0 ? nvt_env : kla::fwd_iso_vtiles(d->B, d->H, d->dk);
         return FK_ISO;
     }
@@ -83,6 +94,8 @@ const char* klaFwdKernelName(const klaDims* d) {
     switch (pick_kernel(d, &nvt)) {
         case FK_EMPTY: return "kla_fwd_empty_kernel";
         case FK_ISO: return nvt > 1 ? "kla_fwd_iso_kernel (value tiles)" : "kla_fwd_iso_kernel";
+        case FK_ISO_PIPE:
+            return nvt > 1 ? "kla_fwd_iso_pipe_kernel (value tiles)" : "kla_fwd_iso_pipe_kernel";
         case FK_DIAG_PIPE:
             return nvt > 1 ? "kla_fwd_diag_pipe_kernel (value tiles)" : "kla_fwd_diag_pipe_kernel";
         default: return nvt > 1 ? "kla_fwd_diag_kernel (value tiles)" : "kla_fwd_diag_kernel";
@@ -150,6 +163,7 @@ klaStatus klaFwd(const klaDims* d, const void* q, const void* k, const void* v, 
             if (fa.dv % fa.n_vtiles) return KLA_ERR_UNSUPPORTED;
             e = kla::launch_fwd_iso(fa, d->dtype, st);
             break;
+        case FK_ISO_PIPE: e = kla::launch_fwd_iso_pipe(fa, d->dtype, st); break;
         case FK_DIAG_PIPE: e = kla::launch_fwd_diag_pipe(fa, d->dtype, st); break;
         default: e = kla::launch_fwd_diag(fa, d->dtype, st); break;
     }
