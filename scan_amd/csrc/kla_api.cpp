@@ -69,7 +69,7 @@ FwdKernel pick_kernel(const klaDims* d, int* n_vtiles) {
         return FK_EMPTY;
     }
     if (d->cov == KLA_ISO) {
-        const int nvt_pipe = nvt_env > 0 ? nvt_env : (d->dv % 64 == 0 ? d->dv / 64 : 0);
+        const int nvt_pipe = nvt_env > 0 ? nvt_env : kla::fwd_iso_pipe_vtiles(d->B, d->H, d->dk, d->dv);
         if (use_iso_pipe() && nvt_pipe > 0 &&
             kla::fwd_iso_pipe_supported(d->dk, d->dv, nvt_pipe, d->dtype)) {
             *n_vtiles = nvt_pipe;

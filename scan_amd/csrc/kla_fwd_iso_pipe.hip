@@ -31,19 +31,23 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "kla_common.h"
 #include "kla_internal.h"
 
 namespace kla {
 namespace {
 
-template <typename TIn, int DK_>
+template <typename TIn, int DK_, int DV_>
 struct IP {
     static constexpr int DK = DK_;
-    static constexpr int DV = 64;                  // value columns per workgroup
+    static constexpr int DV = DV_;                 // value columns per workgroup
     static constexpr int C = 64;                   // tokens per chunk
     static constexpr int NSW = 4;                  // staging waves
-    static constexpr int NMW = 4;                  // MMA waves (16 columns each)
+    static constexpr int NMW = DV / 16;            // MMA waves (16 columns each)
+    // staging load buffers (NSB-1 chunks in flight): as many as about 120
+    // VGPRs hold
     static constexpr int NW = NSW + 1 + NMW;
     static constexpr int NT = 64 * NW;
     static constexpr int ES = (int)sizeof(TIn);
@@ -60,6 +64,8 @@ struct IP {
     static constexpr int IT = DK / 16;
     static constexpr int NBS = DK * ES <= 128 ? 3 : 2;  // scan-wave load buffers
     static constexpr int KR = DK * ES / 16;        // 16-byte loads per k row
+    static constexpr int BUFV = 4 * QKPL * (8 * ES / 4) + VPL * 2 * (4 * ES / 4);  // VGPRs per buffer
+    static constexpr int NSB = 120 / BUFV < 2 ? 2 : (120 / BUFV > 5 ? 5 : 120 / BUFV);
     static_assert(QKU % (64 * NSW) == 0 && VU % (64 * NSW) == 0, "unit split");
 };
 
@@ -97,6 +103,15 @@ __device__ __forceinline__ float get8(const f32x4* w, int e) {
     if constexpr (sizeof(TIn) == 2) return (float)__builtin_bit_cast(bf16x8, w[0])[e];
     else return w[e >> 2][e & 3];
 }
+
+// bf16 pair (value e of word a, value e of word b) from two rows held as raw
+// 32-bit words: low halves for even e, high halves for odd e (one v_perm).
+__device__ __forceinline__ unsigned bf16_pair(unsigned a, unsigned b, int odd) {
+    return __builtin_amdgcn_perm(b, a, odd ? 0x07060302u : 0x05040100u);
+}
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- DPP scans
 template <int CTRL, int ROWS>
@@ -145,6 +160,17 @@ __device__ __forceinline__ float lane_bcast(float x, int src) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), src));
 }
 
+// Pipeline steps: every role runs the same number of barrier steps.  A role
+// that rotates NB register buffers runs a multiple of NB steps in its loop
+// (work is guarded per step, the barrier is not), then pads to the common total.
+__device__ __forceinline__ int round_up(int n, int m) { return (n + m - 1) / m * m; }
+
+template <class K>
+__device__ __forceinline__ int total_steps(int nchunks) {
+    const int a = round_up(nchunks + 1, K::NSB), b = round_up(nchunks + 1, K::NBS);
+    return a > b ? a : b;
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vm() {
     constexpr int n = N < 63 ? N : 63;
@@ -157,6 +183,9 @@ __device__ void stage_role(IsoSm<TIn, K>& sm, const FwdArgs& p, int bh, int vt, 
     constexpr int C = K::C, DK = K::DK, ES = K::ES;
     constexpr int WPO = 8 * ES / 16;  // 16-byte words per 8-value group
     typedef typename Quad<TIn>::V QV;
+    // a 4-value group of v as raw words (register arrays of 8-byte bf16
+    // vectors are not kept in registers by the compiler)
+    typedef typename std::conditional<sizeof(TIn) == 2, f32x2, f32x4>::type VW;
     const int nchunks = (p.T + C - 1) / C;
     const int sl = sw * 64 + lane;
     const size_t rowbase = (size_t)bh * p.T;
@@ -167,9 +196,10 @@ __device__ void stage_role(IsoSm<TIn, K>& sm, const FwdArgs& p, int bh, int vt, 
 
     struct Regs {
         f32x4 q[K::QKPL][2][WPO], k[K::QKPL][2][WPO];
-        QV v[K::VPL][2];
+        VW v[K::VPL][2];
     };
-    Regs r[3];
+    constexpr int NB = K::NSB;
+    Regs r[NB];
     int qoff[K::QKPL], voff[K::VPL];
 #pragma unroll
     for (int x = 0; x < K::QKPL; ++x) {
@@ -199,7 +229,7 @@ __device__ void stage_role(IsoSm<TIn, K>& sm, const FwdArgs& p, int bh, int vt, 
 #pragma unroll
         for (int x = 0; x < K::VPL; ++x)
 #pragma unroll
-            for (int h = 0; h < 2; ++h) g.v[x][h] = buf_load<QV>(rv, voff[x] + h * VRB);
+            for (int h = 0; h < 2; ++h) g.v[x][h] = buf_load<VW>(rv, voff[x] + h * VRB);
     };
     auto stage = [&](int c, const Regs& g) {
         ChunkBuf<TIn, K>& B = sm.buf[c & 1];
@@ -214,36 +244,53 @@ __device__ void stage_role(IsoSm<TIn, K>& sm, const FwdArgs& p, int bh, int vt, 
                     *(f32x4*)&B.Q[t + h][8 * oc + w * (16 / ES)] = g.q[x][h][w];
                     *(f32x4*)&B.Kr[t + h][8 * oc + w * (16 / ES)] = g.k[x][h][w];
                 }
+            if constexpr (sizeof(TIn) == 2) {
+                const u32x4 k0 = __builtin_bit_cast(u32x4, g.k[x][0][0]);
+                const u32x4 k1 = __builtin_bit_cast(u32x4, g.k[x][1][0]);
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                *(typename Pair<TIn>::V*)&B.KT[8 * oc + e][t] =
-                    Pair<TIn>::make(get8<TIn>(g.k[x][0], e), get8<TIn>(g.k[x][1], e));
+                for (int e = 0; e < 8; ++e)
+                    *(unsigned*)&B.KT[8 * oc + e][t] = bf16_pair(k0[e >> 1], k1[e >> 1], e & 1);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    *(typename Pair<TIn>::V*)&B.KT[8 * oc + e][t] =
+                        Pair<TIn>::make(get8<TIn>(g.k[x][0], e), get8<TIn>(g.k[x][1], e));
+            }
         }
 #pragma unroll
         for (int x = 0; x < K::VPL; ++x) {
             const int u = sl + x * 64 * K::NSW, tp = u / K::VQ, jq = u % K::VQ;
-            const f32x4 v0 = Quad<TIn>::to_f32(g.v[x][0]), v1 = Quad<TIn>::to_f32(g.v[x][1]);
+            if constexpr (sizeof(TIn) == 2) {
+                const u32x2 v0 = __builtin_bit_cast(u32x2, g.v[x][0]);
+                const u32x2 v1 = __builtin_bit_cast(u32x2, g.v[x][1]);
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                *(typename Pair<TIn>::V*)&B.VT[4 * jq + e][2 * tp] = Pair<TIn>::make(v0[e], v1[e]);
+                for (int e = 0; e < 4; ++e)
+                    *(unsigned*)&B.VT[4 * jq + e][2 * tp] = bf16_pair(v0[e >> 1], v1[e >> 1], e & 1);
+            } else {
+                const f32x4 v0 = Quad<TIn>::to_f32(__builtin_bit_cast(QV, g.v[x][0]));
+                const f32x4 v1 = Quad<TIn>::to_f32(__builtin_bit_cast(QV, g.v[x][1]));
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    *(typename Pair<TIn>::V*)&B.VT[4 * jq + e][2 * tp] = Pair<TIn>::make(v0[e], v1[e]);
+            }
         }
     };
     constexpr int NLD = 4 * WPO * K::QKPL + 2 * K::VPL;
-    load(0, r[0]);
-    load(1, r[1]);
-    // step s stages chunk s from buffer s mod 3 and loads chunk s+2
-    for (int s0 = 0; s0 <= nchunks; s0 += 3) {
 #pragma unroll
-        for (int j = 0; j < 3; ++j) {
+    for (int j = 0; j < NB - 1; ++j) load(j, r[j]);
+    // step s stages chunk s from buffer s mod NB and loads chunk s+NB-1
+    const int nloop = round_up(nchunks + 1, NB);
+    for (int s0 = 0; s0 < nloop; s0 += NB) {
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
             const int s = s0 + j;
-            if (s <= nchunks) {
-                wait_vm<NLD>();
-                if (s < nchunks) stage(s, r[j]);
-                load(s + 2, r[(j + 2) % 3]);
-                lds_barrier();
-            }
+            wait_vm<(NB - 2) * NLD>();
+            if (s < nchunks) stage(s, r[j]);
+            load(s + NB - 1, r[(j + NB - 1) % NB]);
+            lds_barrier();
         }
     }
+    for (int s = nloop; s < total_steps<K>(nchunks); ++s) lds_barrier();
 }
 
 // ---------------------------------------------------------------- scan role
@@ -321,18 +368,18 @@ __device__ void scan_role(IsoSm<TIn, K>& sm, const FwdArgs& p, int bh, int vt, i
     constexpr int NLD = K::KR + 3;
 #pragma unroll
     for (int j = 0; j < NB - 1; ++j) load(j, rg[j]);
-    for (int s0 = 0; s0 <= nchunks; s0 += NB) {
+    const int nloop = round_up(nchunks + 1, NB);
+    for (int s0 = 0; s0 < nloop; s0 += NB) {
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
             const int s = s0 + j;
-            if (s <= nchunks) {
-                wait_vm<(NB - 2) * NLD>();
-                if (s < nchunks) scan(s, rg[j]);
-                load(s + NB - 1, rg[(j + NB - 1) % NB]);
-                lds_barrier();
-            }
+            wait_vm<(NB - 2) * NLD>();
+            if (s < nchunks) scan(s, rg[j]);
+            load(s + NB - 1, rg[(j + NB - 1) % NB]);
+            lds_barrier();
         }
     }
+    for (int s = nloop; s < total_steps<K>(nchunks); ++s) lds_barrier();
     if (lane == 0) sm.lT = lc;
     if (p.lT && vt == 0 && lane == 0) p.lT[bh] = lc;
     lds_barrier();
@@ -439,8 +486,8 @@ __device__ void mma_role(IsoSm<TIn, K>& sm, const FwdArgs& p, int bh, int vt, in
                 accM[it] = M::mma32(M::ld32(&B.KT[it * 16 + c16][kb * 32 + 8 * g]), vf, accM[it]);
         }
     };
-    for (int s = 0; s <= nchunks; ++s) {
-        if (s >= 1) chunk(s - 1);
+    for (int s = 0; s < total_steps<K>(nchunks); ++s) {
+        if (s >= 1 && s <= nchunks) chunk(s - 1);
         lds_barrier();
     }
     lds_barrier();
@@ -457,9 +504,9 @@ __device__ void mma_role(IsoSm<TIn, K>& sm, const FwdArgs& p, int bh, int vt, in
     }
 }
 
-template <typename TIn, int DK>
-__global__ __launch_bounds__((IP<TIn, DK>::NT)) void kla_fwd_iso_pipe_kernel(FwdArgs p) {
-    typedef IP<TIn, DK> K;
+template <typename TIn, int DK, int DV>
+__global__ __launch_bounds__((IP<TIn, DK, DV>::NT)) void kla_fwd_iso_pipe_kernel(FwdArgs p) {
+    typedef IP<TIn, DK, DV> K;
     __shared__ IsoSm<TIn, K> sm;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int BH = p.B * p.H, nvt = p.n_vtiles;
@@ -475,8 +522,8 @@ __global__ __launch_bounds__((IP<TIn, DK>::NT)) void kla_fwd_iso_pipe_kernel(Fwd
             vt = id % nvt;
         }
     }
-    // Every role runs nchunks + 1 pipeline steps with one barrier each; the
-    // scan and MMA roles add one more for the final state.
+    // Every role runs total_steps() pipeline steps with one barrier each,
+    // then one more barrier before the final state is read.
     if (wave < K::NSW) {
         stage_role<TIn, K>(sm, p, bh, vt, wave, lane);
         lds_barrier();
@@ -487,25 +534,37 @@ __global__ __launch_bounds__((IP<TIn, DK>::NT)) void kla_fwd_iso_pipe_kernel(Fwd
     }
 }
 
-template <typename TIn, int DK>
+template <typename TIn, int DK, int DV>
 hipError_t launch(const FwdArgs& a, hipStream_t s) {
-    typedef IP<TIn, DK> K;
+    typedef IP<TIn, DK, DV> K;
     const int nblk = a.B * a.H * a.n_vtiles;
-    hipLaunchKernelGGL((kla_fwd_iso_pipe_kernel<TIn, DK>), dim3(nblk), dim3(K::NT), 0, s, a);
+    hipLaunchKernelGGL((kla_fwd_iso_pipe_kernel<TIn, DK, DV>), dim3(nblk), dim3(K::NT), 0, s, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
 bool fwd_iso_pipe_supported(int dk, int dv, int nvt, int dtype) {
-    if (dk != dv || nvt < 1 || dv != 64 * nvt) return false;
+    if (dk != dv || nvt < 1 || dv % nvt) return false;
+    const int dvt = dv / nvt;
+    if (dvt != 64 && dvt != 32) return false;
     return dtype == DT_BF16 ? (dk == 64 || dk == 128) : dk == 64;
+}
+
+int fwd_iso_pipe_vtiles(int B, int H, int dk, int dv) {
+    // 32-column tiles when 64-column tiles would leave most CUs idle
+    const long long bh = (long long)B * H;
+    return (bh * (dv / 64) < 256 && dk <= 64) ? dv / 32 : dv / 64;
 }
 
 hipError_t launch_fwd_iso_pipe(const FwdArgs& a, int dtype, hipStream_t s) {
     if (!fwd_iso_pipe_supported(a.dk, a.dv, a.n_vtiles, dtype)) return hipErrorInvalidValue;
-    if (dtype == DT_BF16) return a.dk == 64 ? launch<bf16, 64>(a, s) : launch<bf16, 128>(a, s);
-    return launch<float, 64>(a, s);
+    const bool wide = a.dv / a.n_vtiles == 64;
+    if (dtype == DT_BF16) {
+        if (a.dk == 64) return wide ? launch<bf16, 64, 64>(a, s) : launch<bf16, 64, 32>(a, s);
+        return wide ? launch<bf16, 128, 64>(a, s) : launch<bf16, 128, 32>(a, s);
+    }
+    return wide ? launch<float, 64, 64>(a, s) : launch<float, 64, 32>(a, s);
 }
 
 }  // namespace kla

@@ -48,8 +48,9 @@ hipError_t launch_fwd_diag_pipe(const FwdArgs& a, int dtype, hipStream_t s);
 bool fwd_diag_pipe_supported(int dk, int dv, int nvt, int dtype);
 hipError_t launch_fwd_iso(const FwdArgs& a, int dtype, hipStream_t s);
 // Wave-specialised pipelined isotropic forward: bf16 dk = dv in {64, 128},
-// fp32 dk = dv = 64, 64 value columns per workgroup (nvt = dv / 64).
+// fp32 dk = dv = 64, 64 or 32 value columns per workgroup.
 bool fwd_iso_pipe_supported(int dk, int dv, int nvt, int dtype);
+int fwd_iso_pipe_vtiles(int B, int H, int dk, int dv);
 hipError_t launch_fwd_iso_pipe(const FwdArgs& a, int dtype, hipStream_t s);
 hipError_t launch_step(const StepArgs& a, int dtype, int cov, hipStream_t s);
 hipError_t launch_fwd_empty(const FwdArgs& a, int cov, hipStream_t s);

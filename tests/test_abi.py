@@ -158,7 +158,9 @@ def test_kernel_name_reports_the_dispatch():
     assert scan_amd.klaFwdKernelName(KlaDims(64, 16, 2048, 128, 128, BF16, DIAG)) == \
         "kla_fwd_diag_pipe_kernel"
     assert scan_amd.klaFwdKernelName(KlaDims(2, 3, 100, 32, 32, F32, DIAG)) == "kla_fwd_diag_kernel"
-    assert scan_amd.klaFwdKernelName(KlaDims(2, 3, 100, 64, 64, F32, ISO)) == "kla_fwd_iso_pipe_kernel"
+    assert scan_amd.klaFwdKernelName(KlaDims(2, 3, 100, 64, 64, F32, ISO)) == \
+        "kla_fwd_iso_pipe_kernel (value tiles)"
+    assert scan_amd.klaFwdKernelName(KlaDims(64, 8, 100, 64, 64, F32, ISO)) == "kla_fwd_iso_pipe_kernel"
     assert scan_amd.klaFwdKernelName(KlaDims(4, 32, 8192, 128, 128, BF16, ISO)) == \
         "kla_fwd_iso_pipe_kernel (value tiles)"
     assert scan_amd.klaFwdKernelName(KlaDims(2, 3, 100, 32, 32, F32, ISO)).startswith(
