@@ -68,6 +68,45 @@ struct Mma<float> {
     static __device__ __forceinline__ K16 from_acc(f32x4 x) { return x; }
 };
 
+// Eight bf16/f32 values forming one K=32 operand fragment: slots 0-3 hold
+// k = 4g..4g+3 of the first 16-block, slots 4-7 the same of the second.
+template <typename T> struct Frag;
+template <> struct Frag<bf16> {
+    typedef bf16x8 V;
+    static __device__ __forceinline__ V ld(const bf16* row, int g) {
+        const s16x4 lo = *(const s16x4*)(row + 4 * g);
+        const s16x4 hi = *(const s16x4*)(row + 16 + 4 * g);
+        typedef short s16x8 __attribute__((__vector_size__(16)));
+        s16x8 r = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        return __builtin_bit_cast(V, r);
+    }
+    static __device__ __forceinline__ V from_acc(f32x4 lo, f32x4 hi) {
+        V r = {(bf16)lo[0], (bf16)lo[1], (bf16)lo[2], (bf16)lo[3],
+               (bf16)hi[0], (bf16)hi[1], (bf16)hi[2], (bf16)hi[3]};
+        return r;
+    }
+    static __device__ __forceinline__ f32x4 mma(V a, V b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+};
+template <> struct Frag<float> {
+    struct V { f32x4 lo, hi; };
+    static __device__ __forceinline__ V ld(const float* row, int g) {
+        V r;
+        r.lo = *(const f32x4*)(row + 4 * g);
+        r.hi = *(const f32x4*)(row + 16 + 4 * g);
+        return r;
+    }
+    static __device__ __forceinline__ V from_acc(f32x4 lo, f32x4 hi) { V r; r.lo = lo; r.hi = hi; return r; }
+    static __device__ __forceinline__ f32x4 mma(V a, V b, f32x4 c) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[e], b.lo[e], c, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[e], b.hi[e], c, 0, 0, 0);
+        return c;
+    }
+};
+
 // Two consecutive values of the input dtype, as loaded from / stored to HBM.
 template <typename T> struct Pair;
 template <> struct Pair<bf16> {
@@ -152,6 +191,18 @@ __device__ __forceinline__ V buf_load(__amdgpu_buffer_rsrc_t r, int voff) {
     } else {
         static_assert(sizeof(V) == 16, "2, 4, 8 or 16 bytes");
         return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+    }
+}
+
+// Range-checked store through a buffer resource: a store whose offset falls at
+// or past the resource's byte range is dropped, so tails need no branch.
+template <typename V>
+__device__ __forceinline__ void buf_store(V v, __amdgpu_buffer_rsrc_t r, int voff) {
+    if constexpr (sizeof(V) == 8) {
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, v), r, voff, 0, 0);
+    } else {
+        static_assert(sizeof(V) == 16, "8 or 16 bytes");
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, voff, 0, 0);
     }
 }
 

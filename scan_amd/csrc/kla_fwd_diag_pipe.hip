@@ -102,45 +102,6 @@ struct S3 {
     int bad[4];                   // chunk needs the exact token-by-token path
 };
 
-// Eight bf16/f32 values forming one K=32 operand fragment: slots 0-3 hold
-// k = 4g..4g+3 of the first 16-block, slots 4-7 the same of the second.
-template <typename T> struct Frag;
-template <> struct Frag<bf16> {
-    typedef bf16x8 V;
-    static __device__ __forceinline__ V ld(const bf16* row, int g) {
-        const s16x4 lo = *(const s16x4*)(row + 4 * g);
-        const s16x4 hi = *(const s16x4*)(row + 16 + 4 * g);
-        typedef short s16x8 __attribute__((__vector_size__(16)));
-        s16x8 r = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        return __builtin_bit_cast(V, r);
-    }
-    static __device__ __forceinline__ V from_acc(f32x4 lo, f32x4 hi) {
-        V r = {(bf16)lo[0], (bf16)lo[1], (bf16)lo[2], (bf16)lo[3],
-               (bf16)hi[0], (bf16)hi[1], (bf16)hi[2], (bf16)hi[3]};
-        return r;
-    }
-    static __device__ __forceinline__ f32x4 mma(V a, V b, f32x4 c) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-    }
-};
-template <> struct Frag<float> {
-    struct V { f32x4 lo, hi; };
-    static __device__ __forceinline__ V ld(const float* row, int g) {
-        V r;
-        r.lo = *(const f32x4*)(row + 4 * g);
-        r.hi = *(const f32x4*)(row + 16 + 4 * g);
-        return r;
-    }
-    static __device__ __forceinline__ V from_acc(f32x4 lo, f32x4 hi) { V r; r.lo = lo; r.hi = hi; return r; }
-    static __device__ __forceinline__ f32x4 mma(V a, V b, f32x4 c) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[e], b.lo[e], c, 0, 0, 0);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[e], b.hi[e], c, 0, 0, 0);
-        return c;
-    }
-};
-
 template <int N>
 __device__ __forceinline__ float dpp_row_shr(float x) {
     return __builtin_bit_cast(

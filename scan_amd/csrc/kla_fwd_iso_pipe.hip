@@ -409,58 +409,79 @@ __device__ void mma_role(IsoSm<TIn, K>& sm, const FwdArgs& p, int bh, int vt, in
             }
     }
 
-    auto chunk = [&](int c) {
+    auto chunk = [&](int c, auto wide_t) {
+        constexpr bool WIDE = decltype(wide_t)::value;
+        typedef Frag<TIn> F;
+        typedef typename F::V FV;
+        constexpr int KB = DK / 32, NT16 = C / 16;
+        constexpr bool KHOIST = DK <= 64;  // keep every K tile's fragments in registers
         const ChunkBuf<TIn, K>& B = sm.buf[c & 1];
         const ScanOut& so = sm.sc[c & 1];
         const int t0 = c * C;
         const int L = (p.T - t0) < C ? (p.T - t0) : C;
-        const bool wide = __builtin_amdgcn_readfirstlane(so.wide);
-        typename M::K16 AM[IT];
+        // o rows of this chunk, range-checked so rows past T are not written
+        const auto ro = make_rsrc(op + (rowbase + t0) * p.dv, L * p.dv * (int)sizeof(TIn));
+        // the incoming state as K=32 A operands (two accumulator tiles each)
+        FV AM[KB];
 #pragma unroll
-        for (int it = 0; it < IT; ++it) AM[it] = M::from_acc(accM[it]);
+        for (int kk = 0; kk < KB; ++kk) AM[kk] = F::from_acc(accM[2 * kk], accM[2 * kk + 1]);
+        FV Kf[KHOIST ? NT16 : 1][KB];
+        if constexpr (KHOIST) {
 #pragma unroll
-        for (int tau = 0; tau < C / 16; ++tau) {
+            for (int sig = 0; sig < NT16; ++sig)
+#pragma unroll
+                for (int kk = 0; kk < KB; ++kk) Kf[sig][kk] = F::ld(&B.Kr[sig * 16 + c16][kk * 32], g);
+        }
+#pragma unroll
+        for (int tau = 0; tau < NT16; ++tau) {
             const int t = tau * 16 + c16;
+            FV Qf[KB];
+#pragma unroll
+            for (int kk = 0; kk < KB; ++kk) Qf[kk] = F::ld(&B.Q[t][kk * 32], g);
+            // causal S^T tiles (rows s, column t) and the state readout, all
+            // independent products issued back to back
+            f32x4 S[NT16];
+#pragma unroll
+            for (int sig = 0; sig <= tau; ++sig) {
+                S[sig] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < KB; ++kk) {
+                    const FV kf = KHOIST ? Kf[KHOIST ? sig : 0][kk] : F::ld(&B.Kr[sig * 16 + c16][kk * 32], g);
+                    S[sig] = F::mma(kf, Qf[kk], S[sig]);
+                }
+            }
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < KB; ++kk) acc = F::mma(AM[kk], Qf[kk], acc);
             const float et = so.e[t], gt = so.gam[t];
-            typename M::K16 P[C / 16];
+            typename M::K16 P[NT16];
 #pragma unroll
-            for (int sig = 0; sig < C / 16; ++sig) {
-                if (sig > tau) continue;
-                f32x4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kk = 0; kk < DK / 32; ++kk)
-                    s = M::mma32(M::ld32(&B.Kr[sig * 16 + c16][kk * 32 + 8 * g]),
-                                 M::ld32(&B.Q[t][kk * 32 + 8 * g]), s);
-                const f32x4 ei = *(const f32x4*)&so.ei[sig * 16 + 4 * g];
-                if (!wide) {
+            for (int sig = 0; sig <= tau; ++sig) {
+                f32x4 sv = S[sig];
+                if constexpr (!WIDE) {
+                    const f32x4 ei = *(const f32x4*)&so.ei[sig * 16 + 4 * g];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const float v = s[e] * ei[e] * et;
-                        s[e] = (sig < tau || 4 * g + e <= c16) ? v : 0.f;
+                        const float v = sv[e] * ei[e] * et;
+                        sv[e] = (sig < tau || 4 * g + e <= c16) ? v : 0.f;
                     }
                 } else {
                     const f32x4 gs = *(const f32x4*)&so.gam[sig * 16 + 4 * g];
                     const f32x4 cs = *(const f32x4*)&so.cs[sig * 16 + 4 * g];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const float v = s[e] * cs[e] * fast_exp2(gt - gs[e]);
-                        s[e] = (sig < tau || 4 * g + e <= c16) ? v : 0.f;
+                        const float v = sv[e] * cs[e] * fast_exp2(gt - gs[e]);
+                        sv[e] = (sig < tau || 4 * g + e <= c16) ? v : 0.f;
                     }
                 }
-                P[sig] = M::from_acc(s);
+                P[sig] = M::from_acc(sv);
             }
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int it = 0; it < IT; ++it) acc = M::mma16(AM[it], M::ld16(&B.Q[t][it * 16 + 4 * g]), acc);
             acc *= so.fc[t];
 #pragma unroll
-            for (int sig = 0; sig < C / 16; ++sig) {
-                if (sig > tau) continue;
+            for (int sig = 0; sig <= tau; ++sig)
                 acc = M::mma16(M::ld16(&B.VT[jrow][sig * 16 + 4 * g]), P[sig], acc);
-            }
-            typename Quad<TIn>::V* dst =
-                (typename Quad<TIn>::V*)(op + (rowbase + t0 + t) * p.dv + (size_t)vt * K::DV + mw * 16 + 4 * g);
-            if (L == C || t < L) *dst = Quad<TIn>::make(acc);
+            buf_store(Quad<TIn>::make(acc), ro,
+                      (t * p.dv + vt * K::DV + mw * 16 + 4 * g) * (int)sizeof(TIn));
         }
         // state update: M <- fcend M + K^T diag(wsc) V
         const float fe = so.fcend;
@@ -487,7 +508,10 @@ __device__ void mma_role(IsoSm<TIn, K>& sm, const FwdArgs& p, int bh, int vt, in
         }
     };
     for (int s = 0; s < total_steps<K>(nchunks); ++s) {
-        if (s >= 1 && s <= nchunks) chunk(s - 1);
+        if (s >= 1 && s <= nchunks) {
+            if (__builtin_amdgcn_readfirstlane(sm.sc[(s - 1) & 1].wide)) chunk(s - 1, std::true_type{});
+            else chunk(s - 1, std::false_type{});
+        }
         lds_barrier();
     }
     lds_barrier();
