@@ -58,6 +58,14 @@ int env_vtiles() {
     return atoi(s);
 }
 
+// KLA_FWD_NSEG=n forces n sequence segments on the wave-specialised diagonal
+// kernel (1 = no split); by default long sequences with few (b,h) are split.
+int env_nseg() {
+    const char* s = getenv("KLA_FWD_NSEG");
+    if (!s || !*s) return 0;
+    return atoi(s);
+}
+
 // Kernel that klaFwd launches for these (supported) dims; n_vtiles receives
 // the number of value-column tiles each (b,h) is split into.
 enum FwdKernel { FK_EMPTY, FK_ISO, FK_ISO_PIPE, FK_DIAG_PIPE, FK_DIAG_CHUNK };
@@ -84,6 +92,25 @@ FwdKernel pick_kernel(const klaDims* d, int* n_vtiles) {
     return FK_DIAG_CHUNK;
 }
 
+// Sequence segments klaFwd uses for these dims (1 = no split) and their
+// length: segments of seg_len tokens, the last one ragged and non-empty.
+int pick_nseg(const klaDims* d, int* seg_len = nullptr) {
+    int nvt = 1;
+    if (d->T <= 0 || pick_kernel(d, &nvt) != FK_DIAG_PIPE) return 1;
+    const int e = env_nseg();
+    int n = e > 0 ? e : kla::fwd_diag_nseg(d->B, d->H, d->T, d->dk, d->dv, nvt);
+    if (n <= 1) return 1;
+    const int len = kla::fwd_diag_seg_len(d->T, n);
+    n = (d->T + len - 1) / len;
+    if (seg_len) *seg_len = len;
+    return n < 1 ? 1 : n;
+}
+
+size_t seg_bytes(const klaDims* d, int nseg) {
+    if (nseg <= 1) return 0;
+    return kla::seg_workspace(d->B, d->H, d->T, d->dk, d->dv, d->dtype == KLA_BF16 ? 2 : 4, nseg).bytes;
+}
+
 }  // namespace
 
 extern "C" {
@@ -108,8 +135,8 @@ int klaIsSupported(const klaDims* d) {
 }
 
 size_t klaFwdWorkspaceBytes(const klaDims* d) {
-    (void)d;
-    return 0;  // every supported shape runs without a workspace
+    if (!d || !dims_ok(d) || !supported(d) || d->B == 0 || d->H == 0) return 0;
+    return seg_bytes(d, pick_nseg(d));
 }
 
 klaStatus klaFwd(const klaDims* d, const void* q, const void* k, const void* v, const float* a,
@@ -137,6 +164,7 @@ klaStatus klaFwd(const klaDims* d, const void* q, const void* k, const void* v, 
 
     const size_t wneed = klaFwdWorkspaceBytes(d);
     if (wneed > 0 && (!workspace || workspaceBytes < wneed)) return KLA_ERR_WORKSPACE;
+    if (wneed > 0 && !aligned16(workspace)) return KLA_ERR_ALIGN;
 
     const size_t ntk = (size_t)(BH * T);
     const Span s_o = span(o, ntk * dv * es);
@@ -149,6 +177,12 @@ klaStatus klaFwd(const klaDims* d, const void* q, const void* k, const void* v, 
         if (overlap(s_o, s) || overlap(s_lT, s) || overlap(s_etaT, s)) return KLA_ERR_ALIAS;
     }
     if (overlap(s_o, s_lT) || overlap(s_o, s_etaT) || overlap(s_lT, s_etaT)) return KLA_ERR_ALIAS;
+    if (wneed > 0) {
+        const Span s_ws = span(workspace, wneed);
+        for (const Span& s : ins)
+            if (overlap(s_ws, s)) return KLA_ERR_ALIAS;
+        if (overlap(s_ws, s_o) || overlap(s_ws, s_lT) || overlap(s_ws, s_etaT)) return KLA_ERR_ALIAS;
+    }
 
     kla::FwdArgs fa;
     fa.q = q; fa.k = k; fa.v = v; fa.a = a; fa.qn = qnoise; fa.r = r;
@@ -164,7 +198,32 @@ klaStatus klaFwd(const klaDims* d, const void* q, const void* k, const void* v, 
             e = kla::launch_fwd_iso(fa, d->dtype, st);
             break;
         case FK_ISO_PIPE: e = kla::launch_fwd_iso_pipe(fa, d->dtype, st); break;
-        case FK_DIAG_PIPE: e = kla::launch_fwd_diag_pipe(fa, d->dtype, st); break;
+        case FK_DIAG_PIPE: {
+            int seg_len = 0;
+            const int nseg = pick_nseg(d, &seg_len);
+            if (nseg <= 1) {
+                e = kla::launch_fwd_diag_pipe(fa, d->dtype, st);
+                break;
+            }
+            // sequence split: segment products, precision carry, segment
+            // forwards, state carry, output correction
+            const kla::SegWorkspace w = kla::seg_workspace(d->B, d->H, d->T, d->dk, d->dv, (int)es, nseg);
+            char* ws = (char*)workspace;
+            float* P = (float*)(ws + w.off_P);
+            fa.nseg = nseg;
+            fa.seg_len = seg_len;
+            fa.seg_l0 = (const float*)(ws + w.off_l0);
+            fa.seg_d = (float*)(ws + w.off_d);
+            fa.seg_lend = (float*)(ws + w.off_lend);
+            fa.seg_m = (float*)(ws + w.off_m);
+            fa.seg_qhat = ws + w.off_qhat;
+            e = kla::launch_seg_mobius(fa, P, d->dtype, st);
+            if (e == hipSuccess) e = kla::launch_seg_carry_l(fa, P, st);
+            if (e == hipSuccess) e = kla::launch_fwd_diag_pipe(fa, d->dtype, st);
+            if (e == hipSuccess) e = kla::launch_seg_carry_m(fa, st);
+            if (e == hipSuccess) e = kla::launch_seg_correct(fa, d->dtype, st);
+            break;
+        }
         default: e = kla::launch_fwd_diag(fa, d->dtype, st); break;
     }
     if (e == hipErrorInvalidValue) return KLA_ERR_UNSUPPORTED;

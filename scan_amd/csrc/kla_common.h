@@ -198,10 +198,12 @@ __device__ __forceinline__ V buf_load(__amdgpu_buffer_rsrc_t r, int voff) {
 // or past the resource's byte range is dropped, so tails need no branch.
 template <typename V>
 __device__ __forceinline__ void buf_store(V v, __amdgpu_buffer_rsrc_t r, int voff) {
-    if constexpr (sizeof(V) == 8) {
+    if constexpr (sizeof(V) == 4) {
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), r, voff, 0, 0);
+    } else if constexpr (sizeof(V) == 8) {
         __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, v), r, voff, 0, 0);
     } else {
-        static_assert(sizeof(V) == 16, "8 or 16 bytes");
+        static_assert(sizeof(V) == 16, "4, 8 or 16 bytes");
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, voff, 0, 0);
     }
 }

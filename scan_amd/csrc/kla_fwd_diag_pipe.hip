@@ -99,6 +99,8 @@ struct S3 {
     alignas(16) float sc[2][K::DK];  // state scale before the chunk's readout
     alignas(16) float E[2][K::DK];   // end-of-chunk gate product (pending state scale)
     float lT[K::DK];
+    alignas(16) float Wc[2][K::DK];  // sequence split: gate product from the segment
+                                     // start through token 0 of the chunk
     int bad[4];                   // chunk needs the exact token-by-token path
 };
 
@@ -169,18 +171,29 @@ __device__ __forceinline__ int chunk_len(int T, int c, int C) {
     return n < C ? n : C;
 }
 
+// Token span of one workgroup: the whole sequence, or one segment of it.
+struct Span {
+    int seg;   // segment index (0 without a split)
+    int T0;    // first token
+    int TL;    // tokens
+    bool last; // last segment of the (b,h)
+};
+
 // ------------------------------------------------------------------ chain role
-template <typename TIn, class K>
-__device__ void chain_role(S3<TIn, K>& sm, const FwdArgs& p, int bh, int vt, int cw, int lane) {
+template <typename TIn, class K, bool SEG>
+__device__ void chain_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int bh, int vt, int cw,
+                           int lane) {
     constexpr int C = K::C, DK = K::DK;
     const int i = cw * 64 + lane;
-    const size_t rowbase = (size_t)bh * p.T;
-    const int nchunks = (p.T + C - 1) / C;
+    const size_t rowbase = (size_t)bh * p.T + sp.T0;
+    const int nchunks = (sp.TL + C - 1) / C;
     const int nsteps = pipe_steps<K>(nchunks);
     const TIn* kp = (const TIn*)p.k;
 
-    float l = p.l0 ? p.l0[(size_t)bh * DK + i] : 1.f;
+    float l = SEG ? p.seg_l0[((size_t)bh * p.nseg + sp.seg) * DK + i]
+                  : (p.l0 ? p.l0[(size_t)bh * DK + i] : 1.f);
     const float qn = p.qn[(size_t)(bh % p.H) * DK + i];
+    float wrun = 1.f;  // sequence split: gate product from the segment start
     // One chunk of inputs per buffer; NBC buffers rotate, so a chunk's loads
     // are issued NBC-1 iterations before their first use.
     constexpr int NB = K::NBC, D = NB - 1;
@@ -201,7 +214,7 @@ __device__ void chain_role(S3<TIn, K>& sm, const FwdArgs& p, int bh, int vt, int
     const char* kbase = (const char*)(kp + rowbase * DK);
     const char* rbase = (const char*)(p.r + rowbase);
     auto rows_left = [&](int t, int cap) {
-        const int n = p.T - t;
+        const int n = sp.TL - t;
         return n < 0 ? 0 : (n < cap ? n : cap);
     };
     auto load = [&](int c, Buf& b) {
@@ -230,9 +243,10 @@ __device__ void chain_role(S3<TIn, K>& sm, const FwdArgs& p, int bh, int vt, int
         wait_loads<(D - 1) * (2 * C + 1)>();
         if (nchunks > 0) load(cc + D, nxt);
         if (cc < nchunks) {
-            const int L = chunk_len(p.T, cc, C), par = cc & 1;
+            const int L = chunk_len(sp.TL, cc, C), par = cc & 1;
             const float rho = lane < L ? 1.f / cur.r : 0.f;
             if (cw == 0 && lane < C) sm.rho[par][lane] = rho;
+            float alp0 = 1.f, l0t = 1.f;  // token 0 of the chunk (sequence split)
             // full chunks take a copy of the scan without per-token tests
             auto scan = [&](auto full) {
                 constexpr bool FULL = decltype(full)::value;
@@ -250,6 +264,7 @@ __device__ void chain_role(S3<TIn, K>& sm, const FwdArgs& p, int bh, int vt, int
                         const float alp = a * lp;
                         sm.LP[par][t][i] = f32x2{alp, l};
                         if (t >= 1) { num *= alp; den *= l; }
+                        if (SEG && t == 0) { alp0 = alp; l0t = l; }
                     }
                     if (t % 8 == 7) { G *= num * fast_rcp(den); num = 1.f; den = 1.f; }
                 }
@@ -257,6 +272,11 @@ __device__ void chain_role(S3<TIn, K>& sm, const FwdArgs& p, int bh, int vt, int
             };
             const float G = L == C ? scan(std::true_type{}) : scan(std::false_type{});
             if (__builtin_amdgcn_ballot_w64(G < kFloor)) sm.bad[cc & 3] = 1;
+            if constexpr (SEG) {
+                const float wc = wrun * alp0 * fast_rcp(l0t);  // through token 0
+                sm.Wc[par][i] = wc;
+                wrun = wc * G;                                // through the chunk's end
+            }
         }
         lds_barrier();
     };
@@ -271,17 +291,28 @@ __device__ void chain_role(S3<TIn, K>& sm, const FwdArgs& p, int bh, int vt, int
         for (int s = 0; s < NB; ++s) step(c + s, b[s], b[(s + D) % NB]);
     }
     sm.lT[i] = l;
-    if (p.lT && vt == 0) p.lT[(size_t)bh * DK + i] = l;
+    if (sp.last && p.lT && vt == 0) p.lT[(size_t)bh * DK + i] = l;
+    if constexpr (SEG) {
+        if (vt == 0) {
+            p.seg_d[((size_t)bh * p.nseg + sp.seg) * DK + i] = wrun;
+            if (sp.last) p.seg_lend[(size_t)bh * DK + i] = l;
+        }
+    }
     lds_barrier();
 }
 
 // ------------------------------------------------------------------ gate role
-template <typename TIn, class K>
-__device__ void gate_role(S3<TIn, K>& sm, const FwdArgs& p, int bh, int vt, int gw, int lane) {
+template <typename TIn, class K, bool SEG>
+__device__ void gate_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int bh, int vt, int gw,
+                          int lane) {
     typedef Pair<TIn> PR;
     constexpr int C = K::C, DK = K::DK, DV = K::DV, TPG = K::TPG;
-    const size_t rowbase = (size_t)bh * p.T;
-    const int nchunks = (p.T + C - 1) / C;
+    const size_t rowbase = (size_t)bh * p.T + sp.T0;
+    const int nchunks = (sp.TL + C - 1) / C;
+    // sequence split: segments after the first also write q (.) (gate product
+    // since the segment start) for the correction pass (one value-tile
+    // workgroup writes it)
+    const bool wq = SEG && sp.seg > 0 && vt == 0;
     const int nsteps = pipe_steps<K>(nchunks);
     const int grp = lane % K::NGRP, ipl = lane / K::NGRP;
     const int ip = gw * K::IPW + ipl;
@@ -314,7 +345,7 @@ __device__ void gate_role(S3<TIn, K>& sm, const FwdArgs& p, int bh, int vt, int 
         voff[x][1] = voff[x][0] + VRB;
     }
     auto load = [&](int c, Buf& bf) {
-        const int t0 = c * C, n = p.T - t0;
+        const int t0 = c * C, n = sp.TL - t0;
         const int rows = n < 0 ? 0 : (n < C ? n : C);
         const auto rq = make_rsrc(qbase + (size_t)t0 * QRB, rows * QRB);
         const auto rk = make_rsrc(kbase + (size_t)t0 * QRB, rows * QRB);
@@ -335,7 +366,7 @@ __device__ void gate_role(S3<TIn, K>& sm, const FwdArgs& p, int bh, int vt, int 
         wait_loads<(D - 1) * NLD>();
         if (nchunks > 0) load(cg + D, nxt);
         if (cg >= 0 && cg < nchunks) {
-            const int L = chunk_len(p.T, cg, C), par = cg & 1;
+            const int L = chunk_len(sp.TL, cg, C), par = cg & 1;
             // V^T of the chunk
 #pragma unroll
             for (int x = 0; x < K::VPT; ++x) {
@@ -360,6 +391,11 @@ __device__ void gate_role(S3<TIn, K>& sm, const FwdArgs& p, int bh, int vt, int 
                 w[u][1] = PR::hi(cur.k[u]) * rh * rl1;
             }
             const float* Eprev = sm.E[par ^ 1];
+            const float wc0 = SEG ? sm.Wc[par][2 * ip] : 1.f, wc1 = SEG ? sm.Wc[par][2 * ip + 1] : 1.f;
+            // q-hat rows of this chunk (range 0 when not written)
+            const auto rqh = SEG && wq ? make_rsrc((const TIn*)p.seg_qhat + (rowbase + (size_t)cg * C) * DK,
+                                                   L * DK * (int)sizeof(TIn))
+                                       : make_rsrc(p.q, 0);
             // Factorised operands.  Full chunks take a copy with no per-token
             // tests, so the whole step is one basic block the compiler can
             // schedule; only the lanes holding token 0 or the last token
@@ -391,6 +427,10 @@ __device__ void gate_role(S3<TIn, K>& sm, const FwdArgs& p, int bh, int vt, int 
                     const float w1 = in ? w[u][1] * fast_rcp(g1) : 0.f;
                     *(typename PR::V*)&sm.op[par].fac.Q[t][2 * ip] = PR::make(q0, q1);
                     *(typename PR::V*)&sm.op[par].fac.W[t][2 * ip] = PR::make(w0, w1);
+                    if constexpr (SEG) {
+                        if (wq)
+                            buf_store(PR::make(q0 * wc0, q1 * wc1), rqh, (t * DK + 2 * ip) * (int)sizeof(TIn));
+                    }
                     wt0[u] = (TIn)w0;
                     wt1[u] = (TIn)w1;
                     if (!FULL && t == L - 1) { gl0 = g0; gl1 = g1; }
@@ -407,6 +447,31 @@ __device__ void gate_role(S3<TIn, K>& sm, const FwdArgs& p, int bh, int vt, int 
                 if (L == C) fac(std::true_type{});
                 else fac(std::false_type{});
             } else {
+                if constexpr (SEG) {
+                    if (wq) {
+                        // q (.) gate product for the correction pass, from the
+                        // chunk-start products of this path's raw gates
+                        float p0 = 1.f, p1 = 1.f;
+                        float G[TPG][2];
+#pragma unroll
+                        for (int u = 0; u < TPG; ++u) {
+                            const int t = grp * TPG + u;
+                            const bool inc = t > 0 && t < L;
+                            p0 *= inc ? f[u][0] : 1.f;
+                            p1 *= inc ? f[u][1] : 1.f;
+                            G[u][0] = p0;
+                            G[u][1] = p1;
+                        }
+                        const float e0 = group_excl_prod<K>(p0, grp), e1 = group_excl_prod<K>(p1, grp);
+#pragma unroll
+                        for (int u = 0; u < TPG; ++u) {
+                            const int t = grp * TPG + u;
+                            const float q0 = PR::lo(cur.q[u]) * G[u][0] * e0 * wc0;
+                            const float q1 = PR::hi(cur.q[u]) * G[u][1] * e1 * wc1;
+                            buf_store(PR::make(q0, q1), rqh, (t * DK + 2 * ip) * (int)sizeof(TIn));
+                        }
+                    }
+                }
                 // flagged chunk: raw fp32 gates for the token-by-token path
 #pragma unroll
                 for (int u = 0; u < TPG; ++u) {
@@ -443,15 +508,17 @@ __device__ void gate_role(S3<TIn, K>& sm, const FwdArgs& p, int bh, int vt, int 
 }
 
 // ------------------------------------------------------------------ MMA role
-template <typename TIn, class K>
-__device__ void mma_role(S3<TIn, K>& sm, const FwdArgs& p, int bh, int vt, int mw, int lane) {
+template <typename TIn, class K, bool SEG>
+__device__ void mma_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int bh, int vt, int mw,
+                         int lane) {
     typedef Frag<TIn> F;
     typedef typename F::V FV;
     constexpr int C = K::C, DK = K::DK, DV = K::DV, IT = K::IT, JT = K::JT, KB = K::KB;
-    const size_t rowbase = (size_t)bh * p.T;
-    const int nchunks = (p.T + C - 1) / C;
+    const size_t rowbase = (size_t)bh * p.T + sp.T0;
+    const int nchunks = (sp.TL + C - 1) / C;
     const int nsteps = pipe_steps<K>(nchunks);
     const int c16 = lane & 15, g = lane >> 4;
+    const bool has_eta0 = p.eta0 && sp.seg == 0;  // later segments start from a zero state
     TIn* op = (TIn*)p.o;
     const TIn* qp = (const TIn*)p.q;
 
@@ -464,15 +531,15 @@ __device__ void mma_role(S3<TIn, K>& sm, const FwdArgs& p, int bh, int vt, int m
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = it * 16 + 4 * g + e;
-                acc[it][jj][e] = p.eta0 ? p.eta0[((size_t)bh * DK + i) * p.dv + j] /
-                                              (p.l0 ? p.l0[(size_t)bh * DK + i] : 1.f)
-                                        : 0.f;
+                acc[it][jj][e] = has_eta0 ? p.eta0[((size_t)bh * DK + i) * p.dv + j] /
+                                                (p.l0 ? p.l0[(size_t)bh * DK + i] : 1.f)
+                                          : 0.f;
             }
         }
 
     auto step = [&](int c) {
         if (c >= 0 && c < nchunks) {
-            const int L = chunk_len(p.T, c, C), par = c & 1, t0 = c * C;
+            const int L = chunk_len(sp.TL, c, C), par = c & 1, t0 = c * C;
             const bool bad = __builtin_amdgcn_readfirstlane(sm.bad[c & 3]);
             if (mw == 0 && lane == 0 && c >= 1) sm.bad[(c - 1) & 3] = 0;
             // m <- sc (.) m
@@ -484,6 +551,8 @@ __device__ void mma_role(S3<TIn, K>& sm, const FwdArgs& p, int bh, int vt, int m
             }
             if (!bad) {
                 const OpFac<TIn, K>& o = sm.op[par].fac;
+                // o rows of this chunk; rows past T fall outside the range
+                const auto ro = make_rsrc(op + (rowbase + t0) * p.dv, L * p.dv * (int)sizeof(TIn));
                 FV Qf[2][KB], Vf[JT];
 #pragma unroll
                 for (int b = 0; b < 2; ++b)
@@ -519,16 +588,9 @@ __device__ void mma_role(S3<TIn, K>& sm, const FwdArgs& p, int bh, int vt, int m
                     }
                     out0 = F::mma(Vf[jj], P0, out0);
                     out1 = F::mma(Vf[jj], P1, out1);
-                    const size_t col = (size_t)vt * DV + (mw * JT + jj) * 16 + 4 * g;
-                    typename Quad<TIn>::V* o0 = (typename Quad<TIn>::V*)(op + (rowbase + t0 + c16) * p.dv + col);
-                    typename Quad<TIn>::V* o1 = (typename Quad<TIn>::V*)(op + (rowbase + t0 + 16 + c16) * p.dv + col);
-                    if (L == C) {
-                        *o0 = Quad<TIn>::make(out0);
-                        *o1 = Quad<TIn>::make(out1);
-                    } else {
-                        if (c16 < L) *o0 = Quad<TIn>::make(out0);
-                        if (16 + c16 < L) *o1 = Quad<TIn>::make(out1);
-                    }
+                    const int col = vt * DV + (mw * JT + jj) * 16 + 4 * g;
+                    buf_store(Quad<TIn>::make(out0), ro, (c16 * p.dv + col) * (int)sizeof(TIn));
+                    buf_store(Quad<TIn>::make(out1), ro, ((16 + c16) * p.dv + col) * (int)sizeof(TIn));
                 }
                 // m += W^^T V
 #pragma unroll
@@ -578,7 +640,10 @@ __device__ void mma_role(S3<TIn, K>& sm, const FwdArgs& p, int bh, int vt, int m
     };
     for (int c = -2; c < nsteps - 2; ++c) step(c);
     lds_barrier();
-    if (p.etaT && nchunks > 0) {
+    // final state: the stored state times the pending chunk gate is the mean
+    // state; the information form multiplies it by the precision
+    float* dst = SEG ? p.seg_m + ((size_t)bh * p.nseg + sp.seg) * DK * p.dv : p.etaT + (size_t)bh * DK * p.dv;
+    if ((SEG || p.etaT) && nchunks > 0) {
         const int lp = (nchunks - 1) & 1;
 #pragma unroll
         for (int it = 0; it < IT; ++it)
@@ -588,47 +653,59 @@ __device__ void mma_role(S3<TIn, K>& sm, const FwdArgs& p, int bh, int vt, int m
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int i = it * 16 + 4 * g + e;
-                    p.etaT[((size_t)bh * DK + i) * p.dv + j] = acc[it][jj][e] * sm.E[lp][i] * sm.lT[i];
+                    dst[(size_t)i * p.dv + j] = acc[it][jj][e] * sm.E[lp][i] * (SEG ? 1.f : sm.lT[i]);
                 }
             }
     }
 }
 
-template <typename TIn, int DK, int DV>
+template <typename TIn, int DK, int DV, bool SEG>
 __global__ __launch_bounds__((P3<TIn, DK, DV>::NT)) void kla_fwd_diag_pipe_kernel(FwdArgs p) {
     typedef P3<TIn, DK, DV> K;
     __shared__ S3<TIn, K> sm;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int BH = p.B * p.H, nvt = p.n_vtiles;
-    int bh, vt;
+    const int BH = p.B * p.H, nvt = p.n_vtiles, nseg = SEG ? p.nseg : 1;
+    const int nu = nvt * nseg;  // workgroups per (b,h): value tiles x segments
+    int bh, u;
     {
         const int id = blockIdx.x;
-        if (nvt > 1 && BH % 8 == 0) {   // all value tiles of a (b,h) on one XCD
+        if (nu > 1 && BH % 8 == 0) {   // all workgroups of a (b,h) on one XCD
             const int x = id % 8, kx = id / 8;
-            bh = (kx / nvt) * 8 + x;
-            vt = kx % nvt;
+            bh = (kx / nu) * 8 + x;
+            u = kx % nu;
         } else {
-            bh = id / nvt;
-            vt = id % nvt;
+            bh = id / nu;
+            u = id % nu;
         }
     }
+    const int vt = u % nvt;
+    Span sp;
+    sp.seg = u / nvt;
+    sp.T0 = SEG ? sp.seg * p.seg_len : 0;
+    sp.TL = SEG ? (p.T - sp.T0 < p.seg_len ? p.T - sp.T0 : p.seg_len) : p.T;
+    sp.last = sp.seg == nseg - 1;
     if (threadIdx.x < 4) sm.bad[threadIdx.x] = 0;
     lds_barrier();
     // All roles run the same number of pipeline steps (nchunks + 2, rounded
     // up to a multiple of UNR) with one barrier each, then one more.
     if (wave < K::NCW)
-        chain_role<TIn, K>(sm, p, bh, vt, wave, lane);
+        chain_role<TIn, K, SEG>(sm, p, sp, bh, vt, wave, lane);
     else if (wave < K::NCW + K::NMW)
-        mma_role<TIn, K>(sm, p, bh, vt, wave - K::NCW, lane);
+        mma_role<TIn, K, SEG>(sm, p, sp, bh, vt, wave - K::NCW, lane);
     else
-        gate_role<TIn, K>(sm, p, bh, vt, wave - K::NCW - K::NMW, lane);
+        gate_role<TIn, K, SEG>(sm, p, sp, bh, vt, wave - K::NCW - K::NMW, lane);
 }
 
 template <typename TIn, int DK, int DV>
 hipError_t launch(const FwdArgs& a, hipStream_t s) {
     typedef P3<TIn, DK, DV> K;
-    const int nblk = a.B * a.H * a.n_vtiles;
-    hipLaunchKernelGGL((kla_fwd_diag_pipe_kernel<TIn, DK, DV>), dim3(nblk), dim3(K::NT), 0, s, a);
+    if (a.nseg > 1) {
+        const int nblk = a.B * a.H * a.n_vtiles * a.nseg;
+        hipLaunchKernelGGL((kla_fwd_diag_pipe_kernel<TIn, DK, DV, true>), dim3(nblk), dim3(K::NT), 0, s, a);
+    } else {
+        const int nblk = a.B * a.H * a.n_vtiles;
+        hipLaunchKernelGGL((kla_fwd_diag_pipe_kernel<TIn, DK, DV, false>), dim3(nblk), dim3(K::NT), 0, s, a);
+    }
     return hipGetLastError();
 }
 

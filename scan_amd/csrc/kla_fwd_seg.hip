@@ -1,0 +1,274 @@
+// kla_fwd_seg.hip -- the passes around a sequence-split diagonal KLA forward
+// for gfx950.
+//
+// Method: "Kalman Linear Attention: Parallel Bayesian Filtering For Efficient
+// Language Modelling and State Tracking" (technical summary > method §2): the
+// precision update is a Mobius map, so the map of a whole segment of tokens is
+// the product of the segments' 2x2 matrices, and the precision entering every
+// segment follows from a short scan over segment products.  The mean state is
+// affine in the incoming state (m_t = f_t m_{t-1} + w_t v_t^T), so each
+// segment can run from a zero state and be corrected afterwards.
+//
+// With nseg segments per (b,h) the forward runs:
+//   1. kla_seg_mobius:   the product of each segment's precision matrices,
+//                        per key dim (segments 0 .. nseg-2);
+//   2. kla_seg_carry_l:  the precision entering each segment;
+//   3. the wave-specialised forward on every segment (local outputs, local
+//      final mean state, the segment's total gate, and q (.) gate product);
+//   4. kla_seg_carry_m:  the mean state entering each segment, and etaT;
+//   5. kla_seg_correct:  o_t += (q_t (.) G_t)^T M_in for every later segment.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kla_common.h"
+#include "kla_internal.h"
+
+namespace kla {
+namespace {
+
+__device__ __forceinline__ size_t seg_row(const FwdArgs& p, int bh, int s) {
+    return (size_t)bh * p.nseg + s;
+}
+
+// -------------------------------------------------- 1. segment products
+// One workgroup per (b,h, segment); NSUB threads per key dim each compose a
+// contiguous run of the segment's tokens, then the runs are combined in order.
+template <typename TIn, int DK>
+__global__ __launch_bounds__(1024) void kla_seg_mobius(FwdArgs p, float* P) {
+    constexpr int NSUB = 1024 / DK;
+    __shared__ f32x4 sP[NSUB][DK];
+    const int i = threadIdx.x % DK, sub = threadIdx.x / DK;
+    const int nfull = p.nseg - 1;
+    const int bh = blockIdx.x / nfull, s = blockIdx.x % nfull;
+    const int h = bh % p.H;
+    const int T0 = s * p.seg_len;
+    const int sl = (p.seg_len + NSUB - 1) / NSUB;
+    const int tb = T0 + sub * sl;
+    int te = tb + sl;
+    if (te > T0 + p.seg_len) te = T0 + p.seg_len;
+    if (te > p.T) te = p.T;
+    const float qn = p.qn[(size_t)h * DK + i];
+    const float* ap = p.a + (size_t)bh * p.T * DK + i;
+    const TIn* kp = (const TIn*)p.k + (size_t)bh * p.T * DK + i;
+    const float* rp = p.r + (size_t)bh * p.T;
+    // P = M_t ... M_tb, later tokens on the left
+    float p00 = 1.f, p01 = 0.f, p10 = 0.f, p11 = 1.f;
+    int t = tb;
+    auto step = [&](float a, float kv, float r) {
+        const float b = kv * kv / r, a2 = a * a;
+        const float m00 = __builtin_fmaf(b, qn, 1.f), m01 = b * a2, m10 = qn, m11 = a2;
+        const float n00 = m00 * p00 + m01 * p10, n01 = m00 * p01 + m01 * p11;
+        const float n10 = m10 * p00 + m11 * p10, n11 = m10 * p01 + m11 * p11;
+        p00 = n00; p01 = n01; p10 = n10; p11 = n11;
+    };
+    for (; t + 8 <= te; t += 8) {
+        float a[8], kv[8], r[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            a[u] = ap[(size_t)(t + u) * DK];
+            kv[u] = (float)kp[(size_t)(t + u) * DK];
+            r[u] = rp[t + u];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            step(a[u], kv[u], r[u]);
+            if (u % 4 == 3) {
+                const float sc = fast_rcp(p00 + p01 + p10 + p11);  // positive rescale: same map
+                p00 *= sc; p01 *= sc; p10 *= sc; p11 *= sc;
+            }
+        }
+    }
+    for (; t < te; ++t) step(ap[(size_t)t * DK], (float)kp[(size_t)t * DK], rp[t]);
+    sP[sub][i] = f32x4{p00, p01, p10, p11};
+    __syncthreads();
+    if (sub == 0) {
+        f32x4 q = sP[0][i];
+        for (int u = 1; u < NSUB; ++u) {
+            const f32x4 m = sP[u][i];  // later run on the left
+            f32x4 n;
+            n[0] = m[0] * q[0] + m[1] * q[2];
+            n[1] = m[0] * q[1] + m[1] * q[3];
+            n[2] = m[2] * q[0] + m[3] * q[2];
+            n[3] = m[2] * q[1] + m[3] * q[3];
+            const float sc = fast_rcp(n[0] + n[1] + n[2] + n[3]);
+            q = n * sc;
+        }
+        *(f32x4*)&P[(seg_row(p, bh, s) * DK + i) * 4] = q;
+    }
+}
+
+// -------------------------------------------------- 2. precision carry
+__global__ void kla_seg_carry_l(FwdArgs p, const float* P) {
+    const int n = p.B * p.H * p.dk;
+    const int x = blockIdx.x * blockDim.x + threadIdx.x;
+    if (x >= n) return;
+    const int bh = x / p.dk, i = x % p.dk;
+    float l = p.l0 ? p.l0[x] : 1.f;
+    float* out = const_cast<float*>(p.seg_l0);
+    for (int s = 0; s < p.nseg; ++s) {
+        out[seg_row(p, bh, s) * p.dk + i] = l;
+        if (s + 1 < p.nseg) {
+            const f32x4 m = *(const f32x4*)&P[(seg_row(p, bh, s) * p.dk + i) * 4];
+            l = __builtin_fmaf(m[0], l, m[1]) / __builtin_fmaf(m[2], l, m[3]);
+        }
+    }
+}
+
+// -------------------------------------------------- 4. state carry
+// Segment 0 ran from the caller's state, later ones from zero, so the state
+// entering segment s (s >= 1) is M_s = d_{s-1} M_{s-1} + Mloc_{s-1} with
+// M_0 = 0; it overwrites slot s-1 (already consumed).  etaT = lT (.) M_nseg.
+__global__ void kla_seg_carry_m(FwdArgs p) {
+    const size_t n = (size_t)p.B * p.H * p.dk * p.dv;
+    const size_t x = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (x >= n) return;
+    const int j = (int)(x % p.dv);
+    const int i = (int)((x / p.dv) % p.dk);
+    const int bh = (int)(x / ((size_t)p.dv * p.dk));
+    float m = 0.f;
+    for (int s = 0; s < p.nseg; ++s) {
+        const size_t row = seg_row(p, bh, s);
+        float* slot = p.seg_m + (row * p.dk + i) * p.dv + j;
+        const float ml = *slot;
+        const float d = p.seg_d[row * p.dk + i];
+        if (s >= 1) *(slot - (size_t)p.dk * p.dv) = m;  // M entering segment s
+        m = __builtin_fmaf(d, m, ml);
+    }
+    if (p.etaT) p.etaT[x] = m * p.seg_lend[(size_t)bh * p.dk + i];
+}
+
+// -------------------------------------------------- 5. output correction
+// o_t += sum_i qhat_t[i] M_s[i,:] for the tokens of segment s >= 1.  One
+// workgroup per (b,h, segment, 256-token block); M_s^T is staged once in LDS
+// as the A operand, every wave then runs 16-token tiles.
+template <typename TIn, int DK, int DV>
+__global__ __launch_bounds__(256) void kla_seg_correct(FwdArgs p) {
+    typedef Frag<TIn> F;
+    typedef typename F::V FV;
+    constexpr int TB = 256, PE = 16 / (int)sizeof(TIn), MS = DK + PE;
+    __shared__ TIn MT[DV][MS];
+    const int nlater = p.nseg - 1;
+    const int nblk = (p.seg_len + TB - 1) / TB;
+    int id = blockIdx.x;
+    const int blk = id % nblk;
+    id /= nblk;
+    const int s = 1 + id % nlater;
+    const int bh = id / nlater;
+    const int T0 = s * p.seg_len;
+    int TL = p.T - T0;
+    if (TL > p.seg_len) TL = p.seg_len;
+    const int tb = blk * TB;
+    if (tb >= TL) return;  // uniform over the workgroup
+    // stage M_s^T (M_s lives in slot s-1)
+    const float* M = p.seg_m + seg_row(p, bh, s - 1) * DK * DV;
+    for (int x = threadIdx.x; x < DK * DV; x += 256) {
+        const int i = x / DV, j = x % DV;
+        MT[j][i] = (TIn)M[x];
+    }
+    __syncthreads();
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int c16 = lane & 15, g = lane >> 4;
+    const size_t row0 = (size_t)bh * p.T + T0 + tb;
+    const int rows = TL - tb < TB ? TL - tb : TB;
+    const TIn* qh = (const TIn*)p.seg_qhat + row0 * DK;
+    TIn* o = (TIn*)p.o + row0 * p.dv;
+    const auto ro = make_rsrc(o, rows * p.dv * (int)sizeof(TIn));
+    for (int tt = wave * 16; tt < rows; tt += 64) {
+        const int t = tt + c16;
+        FV qf[DK / 32];
+#pragma unroll
+        for (int kk = 0; kk < DK / 32; ++kk) {
+            // rows past the block end read row `rows - 1` (their result is dropped)
+            const int tr = t < rows ? t : rows - 1;
+            qf[kk] = F::ld(qh + (size_t)tr * DK + kk * 32, g);
+        }
+#pragma unroll
+        for (int jt = 0; jt < DV / 16; ++jt) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < DK / 32; ++kk) acc = F::mma(F::ld(&MT[jt * 16 + c16][kk * 32], g), qf[kk], acc);
+            // lane holds o[t][jt*16 + 4g + e]
+            const int off = (t * p.dv + jt * 16 + 4 * g) * (int)sizeof(TIn);
+            const f32x4 prev = Quad<TIn>::to_f32(buf_load<typename Quad<TIn>::V>(ro, off));
+            buf_store(Quad<TIn>::make(prev + acc), ro, off);
+        }
+    }
+}
+
+template <typename TIn>
+hipError_t launch_mobius_t(const FwdArgs& a, float* P, hipStream_t s) {
+    const int nblk = a.B * a.H * (a.nseg - 1);
+    if (a.dk == 128) hipLaunchKernelGGL((kla_seg_mobius<TIn, 128>), dim3(nblk), dim3(1024), 0, s, a, P);
+    else if (a.dk == 64) hipLaunchKernelGGL((kla_seg_mobius<TIn, 64>), dim3(nblk), dim3(1024), 0, s, a, P);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+template <typename TIn>
+hipError_t launch_correct_t(const FwdArgs& a, hipStream_t s) {
+    const int nblk = a.B * a.H * (a.nseg - 1) * ((a.seg_len + 255) / 256);
+    if (a.dk == 128 && a.dv == 128)
+        hipLaunchKernelGGL((kla_seg_correct<TIn, 128, 128>), dim3(nblk), dim3(256), 0, s, a);
+    else if (a.dk == 128 && a.dv == 64)
+        hipLaunchKernelGGL((kla_seg_correct<TIn, 128, 64>), dim3(nblk), dim3(256), 0, s, a);
+    else if (a.dk == 64 && a.dv == 64)
+        hipLaunchKernelGGL((kla_seg_correct<TIn, 64, 64>), dim3(nblk), dim3(256), 0, s, a);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+SegWorkspace seg_workspace(int B, int H, int T, int dk, int dv, int es, int nseg) {
+    const size_t bh = (size_t)B * H;
+    SegWorkspace w;
+    size_t o = 0;
+    w.off_P = o;    o += align256(bh * nseg * dk * 4 * sizeof(float));
+    w.off_l0 = o;   o += align256(bh * nseg * dk * sizeof(float));
+    w.off_d = o;    o += align256(bh * nseg * dk * sizeof(float));
+    w.off_lend = o; o += align256(bh * dk * sizeof(float));
+    w.off_m = o;    o += align256(bh * nseg * dk * dv * sizeof(float));
+    w.off_qhat = o; o += align256(bh * (size_t)T * dk * es);
+    w.bytes = o;
+    return w;
+}
+
+int fwd_diag_nseg(int B, int H, int T, int dk, int dv, int nvt) {
+    (void)dv;
+    if (dk != 64 && dk != 128) return 1;
+    const long long units = (long long)B * H * nvt;
+    if (units >= 192 || T < 2048) return 1;
+    int n = (int)((256 + units - 1) / units);
+    if (n > T / 1024) n = T / 1024;
+    return n < 2 ? 1 : n;
+}
+
+int fwd_diag_seg_len(int T, int nseg) {
+    const int l = (T + nseg - 1) / nseg;
+    return (l + 31) / 32 * 32;
+}
+
+hipError_t launch_seg_mobius(const FwdArgs& a, float* P, int dtype, hipStream_t s) {
+    return dtype == DT_BF16 ? launch_mobius_t<bf16>(a, P, s) : launch_mobius_t<float>(a, P, s);
+}
+
+hipError_t launch_seg_carry_l(const FwdArgs& a, const float* P, hipStream_t s) {
+    const int n = a.B * a.H * a.dk;
+    hipLaunchKernelGGL(kla_seg_carry_l, dim3((n + 255) / 256), dim3(256), 0, s, a, P);
+    return hipGetLastError();
+}
+
+hipError_t launch_seg_carry_m(const FwdArgs& a, hipStream_t s) {
+    const size_t n = (size_t)a.B * a.H * a.dk * a.dv;
+    hipLaunchKernelGGL(kla_seg_carry_m, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_seg_correct(const FwdArgs& a, int dtype, hipStream_t s) {
+    return dtype == DT_BF16 ? launch_correct_t<bf16>(a, s) : launch_correct_t<float>(a, s);
+}
+
+}  // namespace kla

@@ -23,7 +23,35 @@ struct FwdArgs {
     float* etaT;        // may be null
     int B, H, T, dk, dv;
     int n_vtiles;       // workgroups per (b,h) along the value dim
+
+    // Sequence split (diagonal, wave-specialised kernel only).  With nseg > 1
+    // the workgroup of segment s handles tokens [s*seg_len, min(T,(s+1)*seg_len))
+    // of its (b,h), starts from seg_l0 and a zero state, and leaves its local
+    // result for the carry and correction passes.  nseg == 1 is the plain
+    // forward and ignores the seg_* pointers.
+    int nseg = 1;
+    int seg_len = 0;
+    const float* seg_l0 = nullptr;  // [BH, nseg, dk] precision before each segment
+    float* seg_m = nullptr;         // [BH, nseg, dk, dv] local final mean state
+    float* seg_d = nullptr;         // [BH, nseg, dk] total gate (decay) of each segment
+    float* seg_lend = nullptr;      // [BH, dk] precision after the last segment
+    void* seg_qhat = nullptr;       // [BH, T, dk] q (.) gate product since segment start
 };
+
+// Workspace of the sequence split: every array above, 256-byte aligned.
+struct SegWorkspace {
+    size_t off_P, off_l0, off_d, off_lend, off_m, off_qhat, bytes;
+};
+SegWorkspace seg_workspace(int B, int H, int T, int dk, int dv, int es, int nseg);
+// Segments per (b,h) for a diagonal forward on the wave-specialised kernel
+// (1 = no split).
+int fwd_diag_nseg(int B, int H, int T, int dk, int dv, int nvt);
+int fwd_diag_seg_len(int T, int nseg);
+// The passes around the split forward (kla_fwd_seg.hip).
+hipError_t launch_seg_mobius(const FwdArgs& a, float* P, int dtype, hipStream_t s);
+hipError_t launch_seg_carry_l(const FwdArgs& a, const float* P, hipStream_t s);
+hipError_t launch_seg_carry_m(const FwdArgs& a, hipStream_t s);
+hipError_t launch_seg_correct(const FwdArgs& a, int dtype, hipStream_t s);
 
 struct StepArgs {
     const void* q;

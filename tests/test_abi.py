@@ -170,3 +170,20 @@ def test_kernel_name_reports_the_dispatch():
     assert scan_amd.klaFwdKernelName(KlaDims(-1, 1, 8, 64, 64, BF16, DIAG)) == ""
     lib = scan_amd.load()
     assert lib.klaFwdKernelName(None) == b""
+
+
+def test_split_workspace_contract(monkeypatch):
+    long = KlaDims(1, 16, 32768, 128, 128, BF16, DIAG)
+    ws = scan_amd.klaFwdWorkspaceBytes(long)
+    assert ws > 0
+    assert scan_amd.klaFwdWorkspaceBytes(KlaDims(8, 16, 2048, 128, 128, BF16, DIAG)) == 0
+    assert scan_amd.klaFwdWorkspaceBytes(KlaDims(1, 16, 32768, 32, 32, F32, DIAG)) == 0
+    # a split forward without (or with too small) a workspace is rejected
+    assert fwd_call(long) == WS
+    assert fwd_call(long, workspace=addr(12), workspaceBytes=ws - 1) == WS
+    assert fwd_call(long, workspace=addr(12) + 8, workspaceBytes=ws) == ALIGN
+    # the workspace may not overlap an input or output
+    assert fwd_call(long, workspace=addr(3) - 4096, workspaceBytes=ws) == ALIAS
+    assert fwd_call(long, workspace=addr(9) + 4096, workspaceBytes=ws) == ALIAS
+    monkeypatch.setenv("KLA_FWD_NSEG", "1")
+    assert scan_amd.klaFwdWorkspaceBytes(long) == 0

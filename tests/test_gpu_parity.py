@@ -242,3 +242,29 @@ def test_parity_rescale_and_exact_mix(d, dtype):
         assert np.all(np.isfinite(hip[k])), k
     ref = run_oracle(inp, "diag", st["l0"], st["eta0"])
     assert_parity(compare(hip, ref), dtype, "rescale-mix")
+
+
+@pytest.mark.parametrize("name,over,nseg,state", [
+    ("long_diag", dict(B=1, H=2, T=3000), "3", True),       # bf16 d128, ragged last segment
+    ("small_diag", dict(B=1, H=2, T=700, dk=64, dv=64), "4", True),  # fp32 d64
+    ("long_diag", dict(B=1, H=2, T=4096), "", False),       # split chosen by the library
+])
+def test_parity_sequence_split(monkeypatch, name, over, nseg, state):
+    """Sequence split: segment precision products, carries and the output
+    correction reproduce the unsplit recurrence, with and without a state."""
+    _print_case("split", name, over, nseg)
+    if nseg:
+        monkeypatch.setenv("KLA_FWD_NSEG", nseg)
+    if over.get("dk") == 64:
+        monkeypatch.setenv("KLA_FWD_VTILES", "1")  # the 64-column wave-specialised kernel
+    inp = gen.make_inputs(name, seed=21, **over)
+    w = inp["workload"]
+    dims = scan_amd.KlaDims(w.B, w.H, w.T, w.dk, w.dv, 1 if w.dtype == "bf16" else 0, 0)
+    assert scan_amd.klaFwdWorkspaceBytes(dims) > 0
+    l0 = eta0 = None
+    if state:
+        st = gen.make_state(w, seed=22)
+        l0, eta0 = st["l0"], st["eta0"]
+    hip = run_hip(inp, "diag", l0, eta0)
+    ref = run_oracle(inp, "diag", l0, eta0)
+    assert_parity(compare(hip, ref), w.dtype, f"split {name} {over}")
