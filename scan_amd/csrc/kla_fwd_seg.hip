@@ -10,9 +10,11 @@
 // segment can run from a zero state and be corrected afterwards.
 //
 // With nseg segments per (b,h) the forward runs:
-//   1. kla_seg_mobius:   the product of each segment's precision matrices,
-//                        per key dim (segments 0 .. nseg-2);
-//   2. kla_seg_carry_l:  the precision entering each segment;
+//   1. kla_seg_mobius:   the product of the precision matrices of every
+//                        block of kSegBlk tokens before the last segment, per
+//                        key dim;
+//   2. kla_seg_carry_l:  the precision entering each segment (a walk over
+//                        the block products);
 //   3. the wave-specialised forward on every segment (local outputs, local
 //      final mean state, the segment's total gate, and q (.) gate product);
 //   4. kla_seg_carry_m:  the mean state entering each segment, and etaT;
@@ -30,23 +32,26 @@ __device__ __forceinline__ size_t seg_row(const FwdArgs& p, int bh, int s) {
     return (size_t)bh * p.nseg + s;
 }
 
-// -------------------------------------------------- 1. segment products
-// One workgroup per (b,h, segment); NSUB threads per key dim each compose a
-// contiguous run of the segment's tokens, then the runs are combined in order.
+__device__ __forceinline__ int seg_blocks(const FwdArgs& p) {
+    return (p.nseg - 1) * (p.seg_len / kSegBlk);
+}
+
+// -------------------------------------------------- 1. block products
+// One workgroup per (b,h, block of kSegBlk tokens); NSUB threads per key dim
+// each compose a contiguous run of the block, then the runs are combined in
+// order.
 template <typename TIn, int DK>
 __global__ __launch_bounds__(1024) void kla_seg_mobius(FwdArgs p, float* P) {
     constexpr int NSUB = 1024 / DK;
     __shared__ f32x4 sP[NSUB][DK];
     const int i = threadIdx.x % DK, sub = threadIdx.x / DK;
-    const int nfull = p.nseg - 1;
-    const int bh = blockIdx.x / nfull, s = blockIdx.x % nfull;
+    const int nb = seg_blocks(p);
+    const int bh = blockIdx.x / nb, s = blockIdx.x % nb;
     const int h = bh % p.H;
-    const int T0 = s * p.seg_len;
-    const int sl = (p.seg_len + NSUB - 1) / NSUB;
+    const int T0 = s * kSegBlk;
+    constexpr int sl = kSegBlk / NSUB;
     const int tb = T0 + sub * sl;
-    int te = tb + sl;
-    if (te > T0 + p.seg_len) te = T0 + p.seg_len;
-    if (te > p.T) te = p.T;
+    const int te = tb + sl;  // blocks before the last segment are full
     const float qn = p.qn[(size_t)h * DK + i];
     const float* ap = p.a + (size_t)bh * p.T * DK + i;
     const TIn* kp = (const TIn*)p.k + (size_t)bh * p.T * DK + i;
@@ -93,7 +98,7 @@ __global__ __launch_bounds__(1024) void kla_seg_mobius(FwdArgs p, float* P) {
             const float sc = fast_rcp(n[0] + n[1] + n[2] + n[3]);
             q = n * sc;
         }
-        *(f32x4*)&P[(seg_row(p, bh, s) * DK + i) * 4] = q;
+        *(f32x4*)&P[(((size_t)bh * nb + s) * DK + i) * 4] = q;
     }
 }
 
@@ -105,12 +110,30 @@ __global__ void kla_seg_carry_l(FwdArgs p, const float* P) {
     const int bh = x / p.dk, i = x % p.dk;
     float l = p.l0 ? p.l0[x] : 1.f;
     float* out = const_cast<float*>(p.seg_l0);
+    const int nb = seg_blocks(p), per = p.seg_len / kSegBlk;
+    const f32x4* Pb = (const f32x4*)P + (size_t)bh * nb * p.dk + i;
     for (int s = 0; s < p.nseg; ++s) {
         out[seg_row(p, bh, s) * p.dk + i] = l;
-        if (s + 1 < p.nseg) {
-            const f32x4 m = *(const f32x4*)&P[(seg_row(p, bh, s) * p.dk + i) * 4];
-            l = __builtin_fmaf(m[0], l, m[1]) / __builtin_fmaf(m[2], l, m[3]);
+        if (s + 1 == p.nseg) break;
+        // the segment's map: its block matrices composed (later on the left),
+        // eight independent loads at a time
+        f32x4 q = {1.f, 0.f, 0.f, 1.f};
+        for (int b0 = s * per; b0 < (s + 1) * per; b0 += 8) {
+            f32x4 m[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                m[u] = b0 + u < (s + 1) * per ? Pb[(size_t)(b0 + u) * p.dk] : f32x4{1.f, 0.f, 0.f, 1.f};
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                f32x4 n;
+                n[0] = m[u][0] * q[0] + m[u][1] * q[2];
+                n[1] = m[u][0] * q[1] + m[u][1] * q[3];
+                n[2] = m[u][2] * q[0] + m[u][3] * q[2];
+                n[3] = m[u][2] * q[1] + m[u][3] * q[3];
+                q = n * fast_rcp(n[0] + n[1] + n[2] + n[3]);
+            }
         }
+        l = __builtin_fmaf(q[0], l, q[1]) / __builtin_fmaf(q[2], l, q[3]);
     }
 }
 
@@ -145,7 +168,7 @@ template <typename TIn, int DK, int DV>
 __global__ __launch_bounds__(256) void kla_seg_correct(FwdArgs p) {
     typedef Frag<TIn> F;
     typedef typename F::V FV;
-    constexpr int TB = 256, PE = 16 / (int)sizeof(TIn), MS = DK + PE;
+    constexpr int TB = 1024, PE = 16 / (int)sizeof(TIn), MS = DK + PE;
     __shared__ TIn MT[DV][MS];
     const int nlater = p.nseg - 1;
     const int nblk = (p.seg_len + TB - 1) / TB;
@@ -173,31 +196,35 @@ __global__ __launch_bounds__(256) void kla_seg_correct(FwdArgs p) {
     const TIn* qh = (const TIn*)p.seg_qhat + row0 * DK;
     TIn* o = (TIn*)p.o + row0 * p.dv;
     const auto ro = make_rsrc(o, rows * p.dv * (int)sizeof(TIn));
+    typedef typename Quad<TIn>::V QV;
     for (int tt = wave * 16; tt < rows; tt += 64) {
         const int t = tt + c16;
+        // every load of the tile first: q-hat rows (rows past the block end
+        // read row `rows - 1`; their result is dropped) and the current o
         FV qf[DK / 32];
 #pragma unroll
         for (int kk = 0; kk < DK / 32; ++kk) {
-            // rows past the block end read row `rows - 1` (their result is dropped)
             const int tr = t < rows ? t : rows - 1;
             qf[kk] = F::ld(qh + (size_t)tr * DK + kk * 32, g);
         }
+        QV prev[DV / 16];
+#pragma unroll
+        for (int jt = 0; jt < DV / 16; ++jt)
+            prev[jt] = buf_load<QV>(ro, (t * p.dv + jt * 16 + 4 * g) * (int)sizeof(TIn));
 #pragma unroll
         for (int jt = 0; jt < DV / 16; ++jt) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            f32x4 acc = Quad<TIn>::to_f32(prev[jt]);
 #pragma unroll
             for (int kk = 0; kk < DK / 32; ++kk) acc = F::mma(F::ld(&MT[jt * 16 + c16][kk * 32], g), qf[kk], acc);
             // lane holds o[t][jt*16 + 4g + e]
-            const int off = (t * p.dv + jt * 16 + 4 * g) * (int)sizeof(TIn);
-            const f32x4 prev = Quad<TIn>::to_f32(buf_load<typename Quad<TIn>::V>(ro, off));
-            buf_store(Quad<TIn>::make(prev + acc), ro, off);
+            buf_store(Quad<TIn>::make(acc), ro, (t * p.dv + jt * 16 + 4 * g) * (int)sizeof(TIn));
         }
     }
 }
 
 template <typename TIn>
 hipError_t launch_mobius_t(const FwdArgs& a, float* P, hipStream_t s) {
-    const int nblk = a.B * a.H * (a.nseg - 1);
+    const int nblk = a.B * a.H * (a.nseg - 1) * (a.seg_len / kSegBlk);
     if (a.dk == 128) hipLaunchKernelGGL((kla_seg_mobius<TIn, 128>), dim3(nblk), dim3(1024), 0, s, a, P);
     else if (a.dk == 64) hipLaunchKernelGGL((kla_seg_mobius<TIn, 64>), dim3(nblk), dim3(1024), 0, s, a, P);
     else return hipErrorInvalidValue;
@@ -206,7 +233,7 @@ hipError_t launch_mobius_t(const FwdArgs& a, float* P, hipStream_t s) {
 
 template <typename TIn>
 hipError_t launch_correct_t(const FwdArgs& a, hipStream_t s) {
-    const int nblk = a.B * a.H * (a.nseg - 1) * ((a.seg_len + 255) / 256);
+    const int nblk = a.B * a.H * (a.nseg - 1) * ((a.seg_len + 1023) / 1024);
     if (a.dk == 128 && a.dv == 128)
         hipLaunchKernelGGL((kla_seg_correct<TIn, 128, 128>), dim3(nblk), dim3(256), 0, s, a);
     else if (a.dk == 128 && a.dv == 64)
@@ -226,7 +253,7 @@ SegWorkspace seg_workspace(int B, int H, int T, int dk, int dv, int es, int nseg
     const size_t bh = (size_t)B * H;
     SegWorkspace w;
     size_t o = 0;
-    w.off_P = o;    o += align256(bh * nseg * dk * 4 * sizeof(float));
+    w.off_P = o;    o += align256(bh * (size_t)(T / kSegBlk + 1) * dk * 4 * sizeof(float));
     w.off_l0 = o;   o += align256(bh * nseg * dk * sizeof(float));
     w.off_d = o;    o += align256(bh * nseg * dk * sizeof(float));
     w.off_lend = o; o += align256(bh * dk * sizeof(float));
@@ -248,7 +275,7 @@ int fwd_diag_nseg(int B, int H, int T, int dk, int dv, int nvt) {
 
 int fwd_diag_seg_len(int T, int nseg) {
     const int l = (T + nseg - 1) / nseg;
-    return (l + 31) / 32 * 32;
+    return (l + kSegBlk - 1) / kSegBlk * kSegBlk;
 }
 
 hipError_t launch_seg_mobius(const FwdArgs& a, float* P, int dtype, hipStream_t s) {

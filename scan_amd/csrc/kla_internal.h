@@ -38,6 +38,10 @@ struct FwdArgs {
     void* seg_qhat = nullptr;       // [BH, T, dk] q (.) gate product since segment start
 };
 
+// Segment lengths are multiples of kSegBlk tokens, the unit of the segment
+// precision products.
+constexpr int kSegBlk = 256;
+
 // Workspace of the sequence split: every array above, 256-byte aligned.
 struct SegWorkspace {
     size_t off_P, off_l0, off_d, off_lend, off_m, off_qhat, bytes;
