@@ -73,9 +73,11 @@ struct Mma<float> {
 template <typename T> struct Frag;
 template <> struct Frag<bf16> {
     typedef bf16x8 V;
-    static __device__ __forceinline__ V ld(const bf16* row, int g) {
-        const s16x4 lo = *(const s16x4*)(row + 4 * g);
-        const s16x4 hi = *(const s16x4*)(row + 16 + 4 * g);
+    static __device__ __forceinline__ V ld(const bf16* row, int g) { return ld2(row + 4 * g, row + 16 + 4 * g); }
+    // slots 0-3 from `lo`, 4-7 from `hi` (for swizzled rows)
+    static __device__ __forceinline__ V ld2(const bf16* lo_p, const bf16* hi_p) {
+        const s16x4 lo = *(const s16x4*)lo_p;
+        const s16x4 hi = *(const s16x4*)hi_p;
         typedef short s16x8 __attribute__((__vector_size__(16)));
         s16x8 r = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         return __builtin_bit_cast(V, r);
@@ -91,10 +93,11 @@ template <> struct Frag<bf16> {
 };
 template <> struct Frag<float> {
     struct V { f32x4 lo, hi; };
-    static __device__ __forceinline__ V ld(const float* row, int g) {
+    static __device__ __forceinline__ V ld(const float* row, int g) { return ld2(row + 4 * g, row + 16 + 4 * g); }
+    static __device__ __forceinline__ V ld2(const float* lo_p, const float* hi_p) {
         V r;
-        r.lo = *(const f32x4*)(row + 4 * g);
-        r.hi = *(const f32x4*)(row + 16 + 4 * g);
+        r.lo = *(const f32x4*)lo_p;
+        r.hi = *(const f32x4*)hi_p;
         return r;
     }
     static __device__ __forceinline__ V from_acc(f32x4 lo, f32x4 hi) { V r; r.lo = lo; r.hi = hi; return r; }

@@ -104,6 +104,20 @@ struct S3 {
     int bad[4];                   // chunk needs the exact token-by-token path
 };
 
+// LDS layouts are permuted so that the lanes of one gate-wave access spread
+// over the banks, while every 8/16-byte operand group stays contiguous and
+// the MFMA waves' addresses stay loop-invariant:
+//   LP row t:     (a*lp, l) of key dim i at column i ^ lp_swz(t)
+//   Q^, W^:       token t at row qw_row<K>(t) (swaps 4-row or 2-row blocks
+//                 in the second half of the chunk)
+//   V^T row j:    4-token group c of the chunk at group c ^ vt_swz<K>(j),
+//                 uniform over the 16 rows of an MFMA tile
+__device__ __forceinline__ int lp_swz(int t) { return ((t >> 3) & 3) << 3; }
+template <class K>
+__device__ __forceinline__ int qw_row(int t) { return t ^ (((t >> 4) & 1) << (K::DK == 128 ? 2 : 1)); }
+template <class K>
+__device__ __forceinline__ int vt_swz(int j) { return (((j >> 4) * (128 / K::DV)) & 7) << 2; }
+
 template <int N>
 __device__ __forceinline__ float dpp_row_shr(float x) {
     return __builtin_bit_cast(
@@ -204,12 +218,10 @@ __device__ void chain_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int
     };
     Buf b[NB];
 
-    // Rows of a and k are read through buffer resources that each span a
-    // 4 KiB window of rows, so the row offsets are immediates and rows past T
-    // (the tail of the last chunk, chunks past the end) read as zero.
+    // Rows of a and k are read through buffer resources that span the rows
+    // of one chunk, so rows past T (the tail of the last chunk, chunks past
+    // the end) read as zero.
     constexpr int ARB = DK * 4, KRB = DK * (int)sizeof(TIn);  // row bytes
-    constexpr int ARW = 4096 / ARB < C ? 4096 / ARB : C;       // rows per window
-    constexpr int KRW = 4096 / KRB < C ? 4096 / KRB : C;
     const char* abase = (const char*)(p.a + rowbase * DK);
     const char* kbase = (const char*)(kp + rowbase * DK);
     const char* rbase = (const char*)(p.r + rowbase);
@@ -218,25 +230,16 @@ __device__ void chain_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int
         return n < 0 ? 0 : (n < cap ? n : cap);
     };
     auto load = [&](int c, Buf& b) {
-        const int t0 = c * C;
+        const int t0 = c * C, rows = rows_left(t0, C);
+        const auto ra = make_rsrc(abase + (size_t)t0 * ARB, rows * ARB);
+        const auto rk = make_rsrc(kbase + (size_t)t0 * KRB, rows * KRB);
 #pragma unroll
-        for (int w = 0; w < C / ARW; ++w) {
-            const int tw = t0 + w * ARW;
-            const auto rs = make_rsrc(abase + (size_t)tw * ARB, rows_left(tw, ARW) * ARB);
+        for (int t = 0; t < C; ++t) b.a[t] = buf_load<float>(ra, i * 4 + t * ARB);
 #pragma unroll
-            for (int t = 0; t < ARW; ++t) b.a[w * ARW + t] = buf_load<float>(rs, i * 4 + t * ARB);
-        }
-#pragma unroll
-        for (int w = 0; w < C / KRW; ++w) {
-            const int tw = t0 + w * KRW;
-            const auto rs = make_rsrc(kbase + (size_t)tw * KRB, rows_left(tw, KRW) * KRB);
-#pragma unroll
-            for (int t = 0; t < KRW; ++t)
-                b.k[w * KRW + t] = sizeof(TIn) == 2
-                                       ? (unsigned)buf_load<unsigned short>(rs, i * 2 + t * KRB)
-                                       : buf_load<unsigned>(rs, i * 4 + t * KRB);
-        }
-        b.r = buf_load<float>(make_rsrc(rbase + (size_t)t0 * 4, rows_left(t0, C) * 4), lane * 4);
+        for (int t = 0; t < C; ++t)
+            b.k[t] = sizeof(TIn) == 2 ? (unsigned)buf_load<unsigned short>(rk, i * 2 + t * KRB)
+                                      : buf_load<unsigned>(rk, i * 4 + t * KRB);
+        b.r = buf_load<float>(make_rsrc(rbase + (size_t)t0 * 4, rows * 4), lane * 4);
     };
     auto step = [&](int c, Buf& cur, Buf& nxt) {
         const int cc = c + 2;  // chunk scanned in this iteration
@@ -246,7 +249,7 @@ __device__ void chain_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int
             const int L = chunk_len(sp.TL, cc, C), par = cc & 1;
             const float rho = lane < L ? 1.f / cur.r : 0.f;
             if (cw == 0 && lane < C) sm.rho[par][lane] = rho;
-            float alp0 = 1.f, l0t = 1.f;  // token 0 of the chunk (sequence split)
+            float f0 = 1.f;  // gate of token 0 of the chunk (sequence split)
             // full chunks take a copy of the scan without per-token tests
             auto scan = [&](auto full) {
                 constexpr bool FULL = decltype(full)::value;
@@ -262,9 +265,9 @@ __device__ void chain_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int
                         const float lp = l * fast_rcp(__builtin_fmaf(qn, l, a * a));
                         l = __builtin_fmaf(kv * kv, rt, lp);
                         const float alp = a * lp;
-                        sm.LP[par][t][i] = f32x2{alp, l};
+                        sm.LP[par][t][i ^ lp_swz(t)] = f32x2{alp, l};
                         if (t >= 1) { num *= alp; den *= l; }
-                        if (SEG && t == 0) { alp0 = alp; l0t = l; }
+                        if (SEG && t == 0) { f0 = alp * fast_rcp(l); }
                     }
                     if (t % 8 == 7) { G *= num * fast_rcp(den); num = 1.f; den = 1.f; }
                 }
@@ -273,7 +276,7 @@ __device__ void chain_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int
             const float G = L == C ? scan(std::true_type{}) : scan(std::false_type{});
             if (__builtin_amdgcn_ballot_w64(G < kFloor)) sm.bad[cc & 3] = 1;
             if constexpr (SEG) {
-                const float wc = wrun * alp0 * fast_rcp(l0t);  // through token 0
+                const float wc = wrun * f0;  // through token 0
                 sm.Wc[par][i] = wc;
                 wrun = wc * G;                                // through the chunk's end
             }
@@ -375,14 +378,15 @@ __device__ void gate_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int 
                 const f32x4 v0 = Quad<TIn>::to_f32(cur.v[x][0]), v1 = Quad<TIn>::to_f32(cur.v[x][1]);
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    *(typename PR::V*)&sm.VT[par][4 * jq + e][2 * tp] = PR::make(v0[e], v1[e]);
+                    *(typename PR::V*)&sm.VT[par][4 * jq + e][(2 * tp) ^ vt_swz<K>(4 * jq + e)] =
+                        PR::make(v0[e], v1[e]);
             }
             // gates
             float f[TPG][2], w[TPG][2];
 #pragma unroll
             for (int u = 0; u < TPG; ++u) {
                 const int t = grp * TPG + u;
-                const f32x4 lq = *(const f32x4*)&sm.LP[par][t][2 * ip];  // a*lp, l (two key dims)
+                const f32x4 lq = *(const f32x4*)&sm.LP[par][t][(2 * ip) ^ lp_swz(t)];  // a*lp, l (two key dims)
                 const float rh = sm.rho[par][t];
                 const float rl0 = fast_rcp(lq[1]), rl1 = fast_rcp(lq[3]);
                 f[u][0] = lq[0] * rl0;
@@ -425,8 +429,8 @@ __device__ void gate_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int 
                     const float q1 = in ? PR::hi(cur.q[u]) * g1 : 0.f;
                     const float w0 = in ? w[u][0] * fast_rcp(g0) : 0.f;
                     const float w1 = in ? w[u][1] * fast_rcp(g1) : 0.f;
-                    *(typename PR::V*)&sm.op[par].fac.Q[t][2 * ip] = PR::make(q0, q1);
-                    *(typename PR::V*)&sm.op[par].fac.W[t][2 * ip] = PR::make(w0, w1);
+                    *(typename PR::V*)&sm.op[par].fac.Q[qw_row<K>(t)][2 * ip] = PR::make(q0, q1);
+                    *(typename PR::V*)&sm.op[par].fac.W[qw_row<K>(t)][2 * ip] = PR::make(w0, w1);
                     if constexpr (SEG) {
                         if (wq)
                             buf_store(PR::make(q0 * wc0, q1 * wc1), rqh, (t * DK + 2 * ip) * (int)sizeof(TIn));
@@ -557,15 +561,19 @@ __device__ void mma_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int b
 #pragma unroll
                 for (int b = 0; b < 2; ++b)
 #pragma unroll
-                    for (int kk = 0; kk < KB; ++kk) Qf[b][kk] = F::ld(&o.Q[b * 16 + c16][kk * 32], g);
+                    for (int kk = 0; kk < KB; ++kk)
+                        Qf[b][kk] = F::ld(&o.Q[qw_row<K>(b * 16 + c16)][kk * 32], g);
 #pragma unroll
-                for (int jj = 0; jj < JT; ++jj) Vf[jj] = F::ld(&sm.VT[par][(mw * JT + jj) * 16 + c16][0], g);
+                for (int jj = 0; jj < JT; ++jj) {
+                    const int j = (mw * JT + jj) * 16 + c16, sw = vt_swz<K>(j);
+                    Vf[jj] = F::ld2(&sm.VT[par][j][(4 * g) ^ sw], &sm.VT[par][j][(16 + 4 * g) ^ sw]);
+                }
                 // causal S^T tiles (sigma, tau)
                 f32x4 s00 = {0.f, 0.f, 0.f, 0.f}, s01 = s00, s11 = s00;
 #pragma unroll
                 for (int kk = 0; kk < KB; ++kk) {
-                    const FV w0 = F::ld(&o.W[c16][kk * 32], g);
-                    const FV w1 = F::ld(&o.W[16 + c16][kk * 32], g);
+                    const FV w0 = F::ld(&o.W[qw_row<K>(c16)][kk * 32], g);
+                    const FV w1 = F::ld(&o.W[qw_row<K>(16 + c16)][kk * 32], g);
                     s00 = F::mma(w0, Qf[0][kk], s00);
                     s01 = F::mma(w0, Qf[1][kk], s01);
                     s11 = F::mma(w1, Qf[1][kk], s11);
@@ -605,7 +613,10 @@ __device__ void mma_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int b
                 for (int t = 0; t < L; ++t) {
                     float vj[JT];
 #pragma unroll
-                    for (int jj = 0; jj < JT; ++jj) vj[jj] = (float)sm.VT[par][(mw * JT + jj) * 16 + c16][t];
+                    for (int jj = 0; jj < JT; ++jj) {
+                        const int j = (mw * JT + jj) * 16 + c16;
+                        vj[jj] = (float)sm.VT[par][j][t ^ vt_swz<K>(j)];
+                    }
                     float part[JT];
 #pragma unroll
                     for (int jj = 0; jj < JT; ++jj) part[jj] = 0.f;
@@ -688,12 +699,22 @@ __global__ __launch_bounds__((P3<TIn, DK, DV>::NT)) void kla_fwd_diag_pipe_kerne
     lds_barrier();
     // All roles run the same number of pipeline steps (nchunks + 2, rounded
     // up to a multiple of UNR) with one barrier each, then one more.
-    if (wave < K::NCW)
+    // Waves w and w+4 of a workgroup share a SIMD.  The chain waves, whose
+    // scan is one long dependency chain, take waves 0.. and share their SIMDs
+    // with the MMA waves (4..), whose VALU load is the lightest; the gate
+    // waves fill the rest and pair with each other.  The chain waves also
+    // win issue ties on their SIMD.
+    static_assert(K::NCW <= 4 && K::NW >= 4 + K::NMW, "wave placement");
+    if (wave < K::NCW) {
+        __builtin_amdgcn_s_setprio(2);
         chain_role<TIn, K, SEG>(sm, p, sp, bh, vt, wave, lane);
-    else if (wave < K::NCW + K::NMW)
-        mma_role<TIn, K, SEG>(sm, p, sp, bh, vt, wave - K::NCW, lane);
-    else
-        gate_role<TIn, K, SEG>(sm, p, sp, bh, vt, wave - K::NCW - K::NMW, lane);
+    } else if (wave < 4) {
+        gate_role<TIn, K, SEG>(sm, p, sp, bh, vt, wave - K::NCW, lane);
+    } else if (wave < 4 + K::NMW) {
+        mma_role<TIn, K, SEG>(sm, p, sp, bh, vt, wave - 4, lane);
+    } else {
+        gate_role<TIn, K, SEG>(sm, p, sp, bh, vt, 4 - K::NCW + (wave - 4 - K::NMW), lane);
+    }
 }
 
 template <typename TIn, int DK, int DV>
