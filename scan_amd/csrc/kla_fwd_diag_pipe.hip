@@ -397,9 +397,16 @@ __device__ void gate_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int 
             const float* Eprev = sm.E[par ^ 1];
             const float wc0 = SEG ? sm.Wc[par][2 * ip] : 1.f, wc1 = SEG ? sm.Wc[par][2 * ip + 1] : 1.f;
             // q-hat rows of this chunk (range 0 when not written)
-            const auto rqh = SEG && wq ? make_rsrc((const TIn*)p.seg_qhat + (rowbase + (size_t)cg * C) * DK,
-                                                   L * DK * (int)sizeof(TIn))
+            // (16-token tiles: the chunk start is a multiple of 16 tokens)
+            const auto rqh = SEG && wq ? make_rsrc((const TIn*)p.seg_qhat +
+                                                       qhat_tile_offset(bh, p.T, DK, sp.T0 + cg * C, 0),
+                                                   (L + 15) / 16 * 16 * DK * (int)sizeof(TIn))
                                        : make_rsrc(p.q, 0);
+            // element offset of (token t of the chunk, key dims 2ip, 2ip+1) there
+            auto qho = [&](int t) {
+                return ((t / 16) * (DK / 32) + (2 * ip) / 32) * 512 + ((2 * ip) % 32 / 8 * 16 + t % 16) * 8 +
+                       (2 * ip) % 8;
+            };
             // Factorised operands.  Full chunks take a copy with no per-token
             // tests, so the whole step is one basic block the compiler can
             // schedule; only the lanes holding token 0 or the last token
@@ -433,7 +440,7 @@ __device__ void gate_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int 
                     *(typename PR::V*)&sm.op[par].fac.W[qw_row<K>(t)][2 * ip] = PR::make(w0, w1);
                     if constexpr (SEG) {
                         if (wq)
-                            buf_store(PR::make(q0 * wc0, q1 * wc1), rqh, (t * DK + 2 * ip) * (int)sizeof(TIn));
+                            buf_store(PR::make(q0 * wc0, q1 * wc1), rqh, qho(t) * (int)sizeof(TIn));
                     }
                     wt0[u] = (TIn)w0;
                     wt1[u] = (TIn)w1;
@@ -472,7 +479,7 @@ __device__ void gate_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int 
                             const int t = grp * TPG + u;
                             const float q0 = PR::lo(cur.q[u]) * G[u][0] * e0 * wc0;
                             const float q1 = PR::hi(cur.q[u]) * G[u][1] * e1 * wc1;
-                            buf_store(PR::make(q0, q1), rqh, (t * DK + 2 * ip) * (int)sizeof(TIn));
+                            buf_store(PR::make(q0, q1), rqh, qho(t) * (int)sizeof(TIn));
                         }
                     }
                 }

@@ -162,16 +162,29 @@ __global__ void kla_seg_carry_m(FwdArgs p) {
 
 // -------------------------------------------------- 5. output correction
 // o_t += sum_i qhat_t[i] M_s[i,:] for the tokens of segment s >= 1.  One
-// workgroup per (b,h, segment, 256-token block); M_s^T is staged once in LDS
-// as the A operand, every wave then runs 16-token tiles.
+// workgroup per (b,h, segment, kCorrBlk-token block); M_s^T is staged once in
+// LDS as the A operand, every wave then runs 16-token tiles.  The q-hat rows
+// are read as MFMA B fragments (16 bytes per lane, K in natural order, the A
+// fragments likewise); the output rows are read and written with whole-row
+// 16-byte accesses and moved to and from the accumulator layout through a
+// small LDS tile of the wave.  The next tile's loads are in flight while the
+// current one is multiplied.
+constexpr int kCorrBlk = 512;
+
 template <typename TIn, int DK, int DV>
 __global__ __launch_bounds__(256) void kla_seg_correct(FwdArgs p) {
     typedef Frag<TIn> F;
     typedef typename F::V FV;
-    constexpr int TB = 1024, PE = 16 / (int)sizeof(TIn), MS = DK + PE;
+    typedef typename Quad<TIn>::V QV;
+    constexpr int PE = 16 / (int)sizeof(TIn), MS = DK + PE, OS = DV + PE, ES = (int)sizeof(TIn);
+    constexpr int KB = DK / 32, JB = DV / 16;
+    constexpr int OL = 16 * DV * ES / 1024;  // 16-byte loads per lane for one tile of o
+    constexpr int RL = DV * ES / 16;         // lanes per o row
+    static_assert(OL >= 1 && 16 * DV * ES % 1024 == 0, "tile of o");
     __shared__ TIn MT[DV][MS];
+    __shared__ TIn OT[4][16][OS];
     const int nlater = p.nseg - 1;
-    const int nblk = (p.seg_len + TB - 1) / TB;
+    const int nblk = (p.seg_len + kCorrBlk - 1) / kCorrBlk;
     int id = blockIdx.x;
     const int blk = id % nblk;
     id /= nblk;
@@ -180,45 +193,88 @@ __global__ __launch_bounds__(256) void kla_seg_correct(FwdArgs p) {
     const int T0 = s * p.seg_len;
     int TL = p.T - T0;
     if (TL > p.seg_len) TL = p.seg_len;
-    const int tb = blk * TB;
+    const int tb = blk * kCorrBlk;
     if (tb >= TL) return;  // uniform over the workgroup
-    // stage M_s^T (M_s lives in slot s-1)
-    const float* M = p.seg_m + seg_row(p, bh, s - 1) * DK * DV;
-    for (int x = threadIdx.x; x < DK * DV; x += 256) {
-        const int i = x / DV, j = x % DV;
-        MT[j][i] = (TIn)M[x];
+    // stage M_s^T (M_s lives in slot s-1): every thread issues all of its
+    // 16-byte loads before the first LDS write
+    {
+        constexpr int NV = DK * DV / 4 / 256;
+        const f32x4* M = (const f32x4*)(p.seg_m + seg_row(p, bh, s - 1) * DK * DV);
+        f32x4 mv[NV];
+#pragma unroll
+        for (int u = 0; u < NV; ++u) mv[u] = M[threadIdx.x + u * 256];
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+            const int x = 4 * (threadIdx.x + u * 256), i = x / DV, j = x % DV;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) MT[j + e][i] = (TIn)mv[u][e];
+        }
     }
     __syncthreads();
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int c16 = lane & 15, g = lane >> 4;
     const size_t row0 = (size_t)bh * p.T + T0 + tb;
-    const int rows = TL - tb < TB ? TL - tb : TB;
-    const TIn* qh = (const TIn*)p.seg_qhat + row0 * DK;
+    const int rows = TL - tb < kCorrBlk ? TL - tb : kCorrBlk;
+    // q-hat tiles of this block (segment and block starts are multiples of 16)
+    const TIn* qh = (const TIn*)p.seg_qhat + qhat_tile_offset(bh, p.T, DK, T0 + tb, 0);
     TIn* o = (TIn*)p.o + row0 * p.dv;
-    const auto ro = make_rsrc(o, rows * p.dv * (int)sizeof(TIn));
-    typedef typename Quad<TIn>::V QV;
-    for (int tt = wave * 16; tt < rows; tt += 64) {
-        const int t = tt + c16;
-        // every load of the tile first: q-hat rows (rows past the block end
-        // read row `rows - 1`; their result is dropped) and the current o
-        FV qf[DK / 32];
+    const auto ro = make_rsrc(o, rows * p.dv * ES);
+    TIn(*ot)[OS] = OT[wave];
+    // K = 32 fragment with slot e holding k = 8g + e
+    auto ldn = [&](const TIn* row) { return F::ld2(row + 8 * g, row + 8 * g + 4); };
+    struct Tile {
+        FV q[KB];     // q-hat of token tt + c16 (rows past the block end: padding, dropped)
+        f32x4 o[OL];  // o rows of the tile, whole rows (zero past the block end)
+    };
+    auto load = [&](int tt, Tile& x) {
+        const TIn* qt = qh + (size_t)(tt / 16) * KB * 512 + lane * 8;
 #pragma unroll
-        for (int kk = 0; kk < DK / 32; ++kk) {
-            const int tr = t < rows ? t : rows - 1;
-            qf[kk] = F::ld(qh + (size_t)tr * DK + kk * 32, g);
+        for (int kk = 0; kk < KB; ++kk) x.q[kk] = F::ld2(qt + kk * 512, qt + kk * 512 + 4);
+#pragma unroll
+        for (int u = 0; u < OL; ++u) x.o[u] = buf_load<f32x4>(ro, tt * p.dv * ES + (lane + 64 * u) * 16);
+    };
+    auto run = [&](int tt, const Tile& x) {
+        // o rows into the accumulator layout: lane (c16, g) takes o[tt+c16][jt*16+4g .. +3]
+#pragma unroll
+        for (int u = 0; u < OL; ++u) {
+            const int f = lane + 64 * u;
+            *(f32x4*)&ot[f / RL][(f % RL) * PE] = x.o[u];
         }
-        QV prev[DV / 16];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+        // M^T fragments are read from LDS for every tile: keeping all of them
+        // in registers would cap the waves per SIMD, and with them the loads
+        // in flight that bound this pass
+        int mo = c16 * MS;
+        asm volatile("" : "+v"(mo));
+        const TIn* mrow = &MT[0][0] + mo;
 #pragma unroll
-        for (int jt = 0; jt < DV / 16; ++jt)
-            prev[jt] = buf_load<QV>(ro, (t * p.dv + jt * 16 + 4 * g) * (int)sizeof(TIn));
+        for (int jt = 0; jt < JB; ++jt) {
+            TIn* cell = &ot[c16][jt * 16 + 4 * g];
+            f32x4 acc = Quad<TIn>::to_f32(*(const QV*)cell);
 #pragma unroll
-        for (int jt = 0; jt < DV / 16; ++jt) {
-            f32x4 acc = Quad<TIn>::to_f32(prev[jt]);
-#pragma unroll
-            for (int kk = 0; kk < DK / 32; ++kk) acc = F::mma(F::ld(&MT[jt * 16 + c16][kk * 32], g), qf[kk], acc);
-            // lane holds o[t][jt*16 + 4g + e]
-            buf_store(Quad<TIn>::make(acc), ro, (t * p.dv + jt * 16 + 4 * g) * (int)sizeof(TIn));
+            for (int kk = 0; kk < KB; ++kk) acc = F::mma(ldn(mrow + jt * 16 * MS + kk * 32), x.q[kk], acc);
+            *(QV*)cell = Quad<TIn>::make(acc);
         }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+#pragma unroll
+        for (int u = 0; u < OL; ++u) {
+            const int f = lane + 64 * u;
+            buf_store(*(const f32x4*)&ot[f / RL][(f % RL) * PE], ro, tt * p.dv * ES + f * 16);
+        }
+    };
+    Tile b0, b1;
+    int tt = wave * 16;
+    if (tt < rows) load(tt, b0);
+    for (; tt < rows; tt += 128) {
+        if (tt + 64 < rows) load(tt + 64, b1);
+        run(tt, b0);
+        if (tt + 64 >= rows) break;
+        if (tt + 128 < rows) load(tt + 128, b0);
+        run(tt + 64, b1);
     }
 }
 
@@ -233,7 +289,7 @@ hipError_t launch_mobius_t(const FwdArgs& a, float* P, hipStream_t s) {
 
 template <typename TIn>
 hipError_t launch_correct_t(const FwdArgs& a, hipStream_t s) {
-    const int nblk = a.B * a.H * (a.nseg - 1) * ((a.seg_len + 1023) / 1024);
+    const int nblk = a.B * a.H * (a.nseg - 1) * ((a.seg_len + kCorrBlk - 1) / kCorrBlk);
     if (a.dk == 128 && a.dv == 128)
         hipLaunchKernelGGL((kla_seg_correct<TIn, 128, 128>), dim3(nblk), dim3(256), 0, s, a);
     else if (a.dk == 128 && a.dv == 64)
@@ -258,7 +314,7 @@ SegWorkspace seg_workspace(int B, int H, int T, int dk, int dv, int es, int nseg
     w.off_d = o;    o += align256(bh * nseg * dk * sizeof(float));
     w.off_lend = o; o += align256(bh * dk * sizeof(float));
     w.off_m = o;    o += align256(bh * nseg * dk * dv * sizeof(float));
-    w.off_qhat = o; o += align256(bh * (size_t)T * dk * es);
+    w.off_qhat = o; o += align256(bh * (size_t)((T + 15) / 16 * 16) * dk * es);
     w.bytes = o;
     return w;
 }

@@ -35,8 +35,18 @@ struct FwdArgs {
     float* seg_m = nullptr;         // [BH, nseg, dk, dv] local final mean state
     float* seg_d = nullptr;         // [BH, nseg, dk] total gate (decay) of each segment
     float* seg_lend = nullptr;      // [BH, dk] precision after the last segment
-    void* seg_qhat = nullptr;       // [BH, T, dk] q (.) gate product since segment start
+    void* seg_qhat = nullptr;       // q (.) gate product since segment start, in
+                                    // 16-token tiles (qhat_tile_offset)
 };
+
+// Element offset of q-hat (token t of sequence bh, key dim i) in the tiled
+// layout the correction pass reads: per (bh, 16-token tile, 32-dim block kb)
+// 512 elements, lane (c16 = t % 16, g = i % 32 / 8) holding 8 consecutive
+// dims at (g * 16 + c16) * 8, so one 64-lane 16-byte load covers a block.
+__host__ __device__ inline size_t qhat_tile_offset(int bh, int T, int dk, int t, int i) {
+    const size_t ntile = (size_t)(T + 15) / 16;
+    return (((size_t)bh * ntile + t / 16) * (dk / 32) + i / 32) * 512 + ((i % 32) / 8 * 16 + t % 16) * 8 + i % 8;
+}
 
 // Segment lengths are multiples of kSegBlk tokens, the unit of the segment
 // precision products.
