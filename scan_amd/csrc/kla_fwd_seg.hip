@@ -39,10 +39,13 @@ __device__ __forceinline__ int seg_blocks(const FwdArgs& p) {
 // -------------------------------------------------- 1. block products
 // One workgroup per (b,h, block of kSegBlk tokens); NSUB threads per key dim
 // each compose a contiguous run of the block, then the runs are combined in
-// order.
+// order.  Workgroups of 512 threads, so that several share a CU, and 16
+// tokens of loads in flight per thread keep enough reads outstanding.
+constexpr int kMobThreads = 512;
+
 template <typename TIn, int DK>
-__global__ __launch_bounds__(1024) void kla_seg_mobius(FwdArgs p, float* P) {
-    constexpr int NSUB = 1024 / DK;
+__global__ __launch_bounds__(kMobThreads) void kla_seg_mobius(FwdArgs p, float* P) {
+    constexpr int NSUB = kMobThreads / DK;
     __shared__ f32x4 sP[NSUB][DK];
     const int i = threadIdx.x % DK, sub = threadIdx.x / DK;
     const int nb = seg_blocks(p);
@@ -50,40 +53,69 @@ __global__ __launch_bounds__(1024) void kla_seg_mobius(FwdArgs p, float* P) {
     const int h = bh % p.H;
     const int T0 = s * kSegBlk;
     constexpr int sl = kSegBlk / NSUB;
-    const int tb = T0 + sub * sl;
-    const int te = tb + sl;  // blocks before the last segment are full
+    const int tb = T0 + sub * sl;  // blocks before the last segment are full
     const float qn = p.qn[(size_t)h * DK + i];
     const float* ap = p.a + (size_t)bh * p.T * DK + i;
     const TIn* kp = (const TIn*)p.k + (size_t)bh * p.T * DK + i;
     const float* rp = p.r + (size_t)bh * p.T;
     // P = M_t ... M_tb, later tokens on the left
     float p00 = 1.f, p01 = 0.f, p10 = 0.f, p11 = 1.f;
-    int t = tb;
-    auto step = [&](float a, float kv, float r) {
-        const float b = kv * kv / r, a2 = a * a;
+    auto step = [&](float a, float kv, float rho) {
+        const float b = kv * kv * rho, a2 = a * a;
         const float m00 = __builtin_fmaf(b, qn, 1.f), m01 = b * a2, m10 = qn, m11 = a2;
         const float n00 = m00 * p00 + m01 * p10, n01 = m00 * p01 + m01 * p11;
         const float n10 = m10 * p00 + m11 * p10, n11 = m10 * p01 + m11 * p11;
         p00 = n00; p01 = n01; p10 = n10; p11 = n11;
     };
-    for (; t + 8 <= te; t += 8) {
-        float a[8], kv[8], r[8];
+    // All lanes of a wave walk the same tokens (64 consecutive key dims of
+    // one run), so 1/r is computed once per token: lane u divides for token
+    // tb + u and the steps read it back by lane.
+    constexpr int TB = 8;  // tokens per load batch
+    static_assert(sl <= 64 && sl % TB == 0 && DK % 64 == 0, "run layout");
+    const int lane = threadIdx.x & 63;
+    const float rho_l = lane < sl ? 1.f / rp[tb + lane] : 0.f;
+    // batches of TB tokens, the next batch's loads in flight during the
+    // current batch's steps
+    struct Batch {
+        float a[TB], kv[TB];
+    };
+    // the run's rows of a and k through buffer resources (offsets from the
+    // run start, so the per-token offsets are immediates or a few registers)
+    const auto ra = make_rsrc(ap - i + (size_t)tb * DK, sl * DK * 4);
+    const auto rk = make_rsrc(kp - i + (size_t)tb * DK, sl * DK * (int)sizeof(TIn));
+    auto load = [&](int t8, Batch& x) {
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            a[u] = ap[(size_t)(t + u) * DK];
-            kv[u] = (float)kp[(size_t)(t + u) * DK];
-            r[u] = rp[t + u];
+        for (int u = 0; u < TB; ++u) {
+            x.a[u] = buf_load<float>(ra, ((t8 + u) * DK + i) * 4);
+            if constexpr (sizeof(TIn) == 2)
+                x.kv[u] = __builtin_bit_cast(
+                    float, (unsigned)buf_load<unsigned short>(rk, ((t8 + u) * DK + i) * 2) << 16);
+            else
+                x.kv[u] = buf_load<float>(rk, ((t8 + u) * DK + i) * 4);
         }
+    };
+    auto run = [&](int t8, const Batch& x) {
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            step(a[u], kv[u], r[u]);
+        for (int u = 0; u < TB; ++u) {
+            const float rho = __builtin_bit_cast(
+                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rho_l), t8 + u));
+            step(x.a[u], x.kv[u], rho);
             if (u % 4 == 3) {
                 const float sc = fast_rcp(p00 + p01 + p10 + p11);  // positive rescale: same map
                 p00 *= sc; p01 *= sc; p10 *= sc; p11 *= sc;
             }
         }
+    };
+    Batch b0, b1;
+    load(0, b0);
+#pragma unroll 1
+    for (int t8 = 0; t8 < sl; t8 += 2 * TB) {
+        if (t8 + TB < sl) load(t8 + TB, b1);
+        run(t8, b0);
+        if (t8 + TB >= sl) break;
+        if (t8 + 2 * TB < sl) load(t8 + 2 * TB, b0);
+        run(t8 + TB, b1);
     }
-    for (; t < te; ++t) step(ap[(size_t)t * DK], (float)kp[(size_t)t * DK], rp[t]);
     sP[sub][i] = f32x4{p00, p01, p10, p11};
     __syncthreads();
     if (sub == 0) {
@@ -281,8 +313,8 @@ __global__ __launch_bounds__(256) void kla_seg_correct(FwdArgs p) {
 template <typename TIn>
 hipError_t launch_mobius_t(const FwdArgs& a, float* P, hipStream_t s) {
     const int nblk = a.B * a.H * (a.nseg - 1) * (a.seg_len / kSegBlk);
-    if (a.dk == 128) hipLaunchKernelGGL((kla_seg_mobius<TIn, 128>), dim3(nblk), dim3(1024), 0, s, a, P);
-    else if (a.dk == 64) hipLaunchKernelGGL((kla_seg_mobius<TIn, 64>), dim3(nblk), dim3(1024), 0, s, a, P);
+    if (a.dk == 128) hipLaunchKernelGGL((kla_seg_mobius<TIn, 128>), dim3(nblk), dim3(kMobThreads), 0, s, a, P);
+    else if (a.dk == 64) hipLaunchKernelGGL((kla_seg_mobius<TIn, 64>), dim3(nblk), dim3(kMobThreads), 0, s, a, P);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }
