@@ -47,8 +47,8 @@ struct P3 {
     static constexpr int DV = DV_;
     static constexpr int C = 32;                 // tokens per chunk
     static constexpr int NCW = DK / 64;          // chain waves
-    static constexpr int JT = 2;                 // 16-column value tiles per MMA wave
     static constexpr int NMW = DV / 32;          // MMA waves
+    static constexpr int JT = DV / (16 * NMW);   // 16-column value tiles per MMA wave
     static constexpr int NGW = 4;                // gate waves
     static constexpr int NW = NCW + NMW + NGW;
     static constexpr int NT = 64 * NW;
@@ -72,7 +72,7 @@ struct P3 {
     static constexpr int NBG = 2;
     static constexpr int UNR = NBC * NBG / (NBC == NBG ? NBC : 1);
     static_assert(DK == 64 || DK == 128, "key dims 64 and 128");
-    static_assert(DV % 32 == 0 && VUNITS % 256 == 0, "value tiles");
+    static_assert(DV % 32 == 0 && JT >= 1 && VUNITS % 256 == 0, "value tiles");
 };
 
 template <typename TIn, class K>
@@ -564,16 +564,24 @@ __device__ void mma_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int b
                 const OpFac<TIn, K>& o = sm.op[par].fac;
                 // o rows of this chunk; rows past T fall outside the range
                 const auto ro = make_rsrc(op + (rowbase + t0) * p.dv, L * p.dv * (int)sizeof(TIn));
-                FV Qf[2][KB], Vf[JT];
-#pragma unroll
-                for (int b = 0; b < 2; ++b)
-#pragma unroll
-                    for (int kk = 0; kk < KB; ++kk)
-                        Qf[b][kk] = F::ld(&o.Q[qw_row<K>(b * 16 + c16)][kk * 32], g);
-#pragma unroll
-                for (int jj = 0; jj < JT; ++jj) {
+                auto ldq = [&](int b, int kk) { return F::ld(&o.Q[qw_row<K>(b * 16 + c16)][kk * 32], g); };
+                auto ldv = [&](int jj) {
                     const int j = (mw * JT + jj) * 16 + c16, sw = vt_swz<K>(j);
-                    Vf[jj] = F::ld2(&sm.VT[par][j][(4 * g) ^ sw], &sm.VT[par][j][(16 + 4 * g) ^ sw]);
+                    return F::ld2(&sm.VT[par][j][(4 * g) ^ sw], &sm.VT[par][j][(16 + 4 * g) ^ sw]);
+                };
+                // With up to two 16-column tiles per wave the Q^ and V^T
+                // fragments stay in registers for the whole chunk; with more,
+                // the state alone takes half the register file, so the work
+                // runs tile by tile and the fragments are re-read from LDS.
+                constexpr bool LEAN = JT > 2;
+                FV Qf[2][KB], Vf[JT];
+                if constexpr (!LEAN) {
+#pragma unroll
+                    for (int b = 0; b < 2; ++b)
+#pragma unroll
+                        for (int kk = 0; kk < KB; ++kk) Qf[b][kk] = ldq(b, kk);
+#pragma unroll
+                    for (int jj = 0; jj < JT; ++jj) Vf[jj] = ldv(jj);
                 }
                 // causal S^T tiles (sigma, tau)
                 f32x4 s00 = {0.f, 0.f, 0.f, 0.f}, s01 = s00, s11 = s00;
@@ -581,9 +589,10 @@ __device__ void mma_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int b
                 for (int kk = 0; kk < KB; ++kk) {
                     const FV w0 = F::ld(&o.W[qw_row<K>(c16)][kk * 32], g);
                     const FV w1 = F::ld(&o.W[qw_row<K>(16 + c16)][kk * 32], g);
-                    s00 = F::mma(w0, Qf[0][kk], s00);
-                    s01 = F::mma(w0, Qf[1][kk], s01);
-                    s11 = F::mma(w1, Qf[1][kk], s11);
+                    const FV q0 = LEAN ? ldq(0, kk) : Qf[0][kk], q1 = LEAN ? ldq(1, kk) : Qf[1][kk];
+                    s00 = F::mma(w0, q0, s00);
+                    s01 = F::mma(w0, q1, s01);
+                    s11 = F::mma(w1, q1, s11);
                 }
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -591,65 +600,67 @@ __device__ void mma_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int b
                 }
                 const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
                 const FV P0 = F::from_acc(s00, zero), P1 = F::from_acc(s01, s11);
+                if constexpr (LEAN) __builtin_amdgcn_sched_barrier(0);
                 // readout O^T = m^T Q^^T + V^T P^T, the state as the A operand
+                // (each column tile reads its state before its own update)
 #pragma unroll
                 for (int jj = 0; jj < JT; ++jj) {
+                    if constexpr (LEAN) __builtin_amdgcn_sched_barrier(0);
+                    const FV vf = LEAN ? ldv(jj) : Vf[jj];
                     f32x4 out0 = {0.f, 0.f, 0.f, 0.f}, out1 = out0;
 #pragma unroll
                     for (int kk = 0; kk < KB; ++kk) {
                         const FV am = F::from_acc(acc[2 * kk][jj], acc[2 * kk + 1][jj]);
-                        out0 = F::mma(am, Qf[0][kk], out0);
-                        out1 = F::mma(am, Qf[1][kk], out1);
+                        out0 = F::mma(am, LEAN ? ldq(0, kk) : Qf[0][kk], out0);
+                        out1 = F::mma(am, LEAN ? ldq(1, kk) : Qf[1][kk], out1);
                     }
-                    out0 = F::mma(Vf[jj], P0, out0);
-                    out1 = F::mma(Vf[jj], P1, out1);
+                    out0 = F::mma(vf, P0, out0);
+                    out1 = F::mma(vf, P1, out1);
                     const int col = vt * DV + (mw * JT + jj) * 16 + 4 * g;
                     buf_store(Quad<TIn>::make(out0), ro, (c16 * p.dv + col) * (int)sizeof(TIn));
                     buf_store(Quad<TIn>::make(out1), ro, ((16 + c16) * p.dv + col) * (int)sizeof(TIn));
+                    if constexpr (LEAN) {
+                        // m[:, tile] += W^^T V[:, tile]
+#pragma unroll
+                        for (int it = 0; it < IT; ++it)
+                            acc[it][jj] = F::mma(F::ld(&o.WT[it * 16 + c16][0], g), vf, acc[it][jj]);
+                    }
                 }
-                // m += W^^T V
+                if constexpr (!LEAN) {
+                    // m += W^^T V
 #pragma unroll
-                for (int it = 0; it < IT; ++it) {
-                    const FV wt = F::ld(&o.WT[it * 16 + c16][0], g);
+                    for (int it = 0; it < IT; ++it) {
+                        const FV wt = F::ld(&o.WT[it * 16 + c16][0], g);
 #pragma unroll
-                    for (int jj = 0; jj < JT; ++jj) acc[it][jj] = F::mma(wt, Vf[jj], acc[it][jj]);
+                        for (int jj = 0; jj < JT; ++jj) acc[it][jj] = F::mma(wt, Vf[jj], acc[it][jj]);
+                    }
                 }
             } else {
                 // exact path: m <- f_t (.) m + w_t v_t^T, o_t = q_t^T m, token by token
                 const OpRaw<K>& o = sm.op[par].raw;
-                for (int t = 0; t < L; ++t) {
-                    float vj[JT];
+                // one 16-column tile at a time, so the loop touches a quarter
+                // of the state at most
 #pragma unroll
-                    for (int jj = 0; jj < JT; ++jj) {
-                        const int j = (mw * JT + jj) * 16 + c16;
-                        vj[jj] = (float)sm.VT[par][j][t ^ vt_swz<K>(j)];
-                    }
-                    float part[JT];
+                for (int jj = 0; jj < JT; ++jj) {
+                    const int j = (mw * JT + jj) * 16 + c16;
+#pragma unroll 1
+                    for (int t = 0; t < L; ++t) {
+                        const float vj = (float)sm.VT[par][j][t ^ vt_swz<K>(j)];
+                        float part = 0.f;
 #pragma unroll
-                    for (int jj = 0; jj < JT; ++jj) part[jj] = 0.f;
+                        for (int it = 0; it < IT; ++it) {
+                            const f32x4 fi = *(const f32x4*)&o.f[t][it * 16 + 4 * g];
+                            const f32x4 wi = *(const f32x4*)&o.w[t][it * 16 + 4 * g];
+                            const f32x4 qi = Quad<TIn>::to_f32(
+                                *(const typename Quad<TIn>::V*)(qp + (rowbase + t0 + t) * DK + it * 16 + 4 * g));
+                            acc[it][jj] = fi * acc[it][jj] + wi * vj;
 #pragma unroll
-                    for (int it = 0; it < IT; ++it) {
-                        const f32x4 fi = *(const f32x4*)&o.f[t][it * 16 + 4 * g];
-                        const f32x4 wi = *(const f32x4*)&o.w[t][it * 16 + 4 * g];
-                        const f32x4 qi = Quad<TIn>::to_f32(
-                            *(const typename Quad<TIn>::V*)(qp + (rowbase + t0 + t) * DK + it * 16 + 4 * g));
-#pragma unroll
-                        for (int jj = 0; jj < JT; ++jj) {
-                            acc[it][jj] = fi * acc[it][jj] + wi * vj[jj];
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) part[jj] += qi[e] * acc[it][jj][e];
+                            for (int e = 0; e < 4; ++e) part += qi[e] * acc[it][jj][e];
+                            __builtin_amdgcn_sched_barrier(0);
                         }
-                        // rarely taken path: keep its loads next to their uses so
-                        // it does not raise the register demand of the kernel
-                        __builtin_amdgcn_sched_barrier(0);
-                    }
-#pragma unroll
-                    for (int jj = 0; jj < JT; ++jj) {
-                        part[jj] += __shfl_xor(part[jj], 16, 64);
-                        part[jj] += __shfl_xor(part[jj], 32, 64);
-                        if (g == 0)
-                            op[(rowbase + t0 + t) * p.dv + (size_t)vt * DV + (mw * JT + jj) * 16 + c16] =
-                                (TIn)part[jj];
+                        part += __shfl_xor(part, 16, 64);
+                        part += __shfl_xor(part, 32, 64);
+                        if (g == 0) op[(rowbase + t0 + t) * p.dv + (size_t)vt * DV + j] = (TIn)part;
                     }
                 }
             }
