@@ -31,8 +31,10 @@ HBM_PEAK_GBS = 8000.0
 # are reported only while the kernel they were taken on is unchanged.
 KERNEL_SOURCES = {
     "diag": ["scan_amd/csrc/kla_fwd_diag_pipe.hip", "scan_amd/csrc/kla_fwd_diag.hip",
-             "scan_amd/csrc/kla_common.h"],
-    "iso": ["scan_amd/csrc/kla_fwd_iso.hip", "scan_amd/csrc/kla_common.h"],
+             "scan_amd/csrc/kla_fwd_seg.hip", "scan_amd/csrc/kla_common.h",
+             "scan_amd/csrc/kla_internal.h"],
+    "iso": ["scan_amd/csrc/kla_fwd_iso_pipe.hip", "scan_amd/csrc/kla_fwd_iso.hip",
+            "scan_amd/csrc/kla_common.h", "scan_amd/csrc/kla_internal.h"],
 }
 
 
