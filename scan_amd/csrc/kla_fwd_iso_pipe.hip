@@ -46,9 +46,13 @@ struct IP {
     static constexpr int C = 64;                   // tokens per chunk
     static constexpr int NSW = 4;                  // staging waves
     static constexpr int NMW = DV / 16;            // MMA waves (16 columns each)
-    // staging load buffers (NSB-1 chunks in flight): as many as about 120
-    // VGPRs hold
-    static constexpr int NW = NSW + 1 + NMW;
+    // bf16 dk = 64: a P wave forms the scaled causal score tiles of a chunk
+    // once, one step ahead of the MMA waves, which then read them from LDS;
+    // the chunk buffers rotate over three chunks.  Otherwise every MMA wave
+    // forms them itself and two chunk buffers rotate.
+    static constexpr bool PW = DK == 64 && sizeof(TIn) == 2;
+    static constexpr int NCB = PW ? 3 : 2;         // chunk buffers
+    static constexpr int NW = NSW + 1 + (PW ? 1 : 0) + NMW;
     static constexpr int NT = 64 * NW;
     static constexpr int ES = (int)sizeof(TIn);
     static constexpr int PE = 16 / ES;             // row padding (16 bytes)
@@ -65,7 +69,9 @@ struct IP {
     static constexpr int NBS = DK * ES <= 128 ? 3 : 2;  // scan-wave load buffers
     static constexpr int KR = DK * ES / 16;        // 16-byte loads per k row
     static constexpr int BUFV = 4 * QKPL * (8 * ES / 4) + VPL * 2 * (4 * ES / 4);  // VGPRs per buffer
-    static constexpr int NSB = 120 / BUFV < 2 ? 2 : (120 / BUFV > 5 ? 5 : 120 / BUFV);
+    // (at least 3: the staging waves also form the key norms of the chunk
+    // after the one they stage)
+    static constexpr int NSB = 120 / BUFV < 3 ? 3 : (120 / BUFV > 5 ? 5 : 120 / BUFV);
     static_assert(QKU % (64 * NSW) == 0 && VU % (64 * NSW) == 0, "unit split");
 };
 
@@ -91,8 +97,12 @@ struct alignas(16) ScanOut {
 
 template <typename TIn, class K>
 struct IsoSm {
-    ChunkBuf<TIn, K> buf[2];
-    ScanOut sc[2];
+    ChunkBuf<TIn, K> buf[K::NCB];
+    ScanOut sc[K::NCB];
+    // scaled causal score tiles (t-tile tau, s-tile sig <= tau) of a chunk as
+    // MFMA B fragments, one per lane (P wave only)
+    typename Mma<TIn>::K16 P[K::PW ? 2 : 1][10][K::PW ? 64 : 1];
+    float ksq[2][64];  // |k_t|^2 of a chunk, from the staging waves
     float lT;
 };
 
@@ -167,8 +177,20 @@ __device__ __forceinline__ int round_up(int n, int m) { return (n + m - 1) / m *
 
 template <class K>
 __device__ __forceinline__ int total_steps(int nchunks) {
-    const int a = round_up(nchunks + 1, K::NSB), b = round_up(nchunks + 1, K::NBS);
+    const int n = nchunks + 1 + (K::PW ? 1 : 0);  // the MMA waves finish chunk s-1 (s-2 with a P wave)
+    const int a = round_up(n, K::NSB), b = round_up(n, K::NBS);
     return a > b ? a : b;
+}
+
+// Sum of x over each group of G consecutive lanes (G = 8 or 16), in every lane
+// of the group.
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+    x += dpp<0xB1, 0xF>(0.f, x);   // quad_perm [1,0,3,2]
+    x += dpp<0x4E, 0xF>(0.f, x);   // quad_perm [2,3,0,1]
+    x += dpp<0x141, 0xF>(0.f, x);  // row_half_mirror
+    if constexpr (G == 16) x += dpp<0x140, 0xF>(0.f, x);  // row_mirror
+    return x;
 }
 
 template <int N>
@@ -232,7 +254,7 @@ __device__ void stage_role(IsoSm<TIn, K>& sm, const FwdArgs& p, int bh, int vt, 
             for (int h = 0; h < 2; ++h) g.v[x][h] = buf_load<VW>(rv, voff[x] + h * VRB);
     };
     auto stage = [&](int c, const Regs& g) {
-        ChunkBuf<TIn, K>& B = sm.buf[c & 1];
+        ChunkBuf<TIn, K>& B = sm.buf[c % K::NCB];
 #pragma unroll
         for (int x = 0; x < K::QKPL; ++x) {
             const int u = sl + x * 64 * K::NSW, tp = u / K::KOCT, oc = u % K::KOCT;
@@ -275,17 +297,45 @@ __device__ void stage_role(IsoSm<TIn, K>& sm, const FwdArgs& p, int bh, int vt, 
             }
         }
     };
+    // |k_t|^2 of chunk c for the scan wave: each unit sums its 8 dims of two
+    // tokens, the KOCT units of a token pair are consecutive lanes
+    auto norms = [&](int c, const Regs& g) {
+        float* ks = sm.ksq[c & 1];
+#pragma unroll
+        for (int x = 0; x < K::QKPL; ++x) {
+            const int u = sl + x * 64 * K::NSW, tp = u / K::KOCT, oc = u % K::KOCT;
+            float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float k0 = get8<TIn>(g.k[x][0], e), k1 = get8<TIn>(g.k[x][1], e);
+                s0 = __builtin_fmaf(k0, k0, s0);
+                s1 = __builtin_fmaf(k1, k1, s1);
+            }
+            s0 = group_sum<K::KOCT>(s0);
+            s1 = group_sum<K::KOCT>(s1);
+            if (oc == 0) *(f32x2*)&ks[2 * tp] = f32x2{s0, s1};
+        }
+    };
+    static_assert(K::KOCT == 8 || K::KOCT == 16, "key-norm groups");
+    static_assert(NB >= 3, "the next chunk's rows must be loaded a step ahead");
     constexpr int NLD = 4 * WPO * K::QKPL + 2 * K::VPL;
 #pragma unroll
     for (int j = 0; j < NB - 1; ++j) load(j, r[j]);
-    // step s stages chunk s from buffer s mod NB and loads chunk s+NB-1
+    // chunk 0's norms before the pipeline's first step (all roles pass one
+    // extra barrier here)
+    wait_vm<(NB - 2) * NLD>();
+    norms(0, r[0]);
+    lds_barrier();
+    // step s stages chunk s from buffer s mod NB, forms the norms of chunk
+    // s+1 and loads chunk s+NB-1
     const int nloop = round_up(nchunks + 1, NB);
     for (int s0 = 0; s0 < nloop; s0 += NB) {
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
             const int s = s0 + j;
-            wait_vm<(NB - 2) * NLD>();
+            wait_vm<(NB - 3) * NLD>();
             if (s < nchunks) stage(s, r[j]);
+            if (s + 1 < nchunks) norms(s + 1, r[(j + 1) % NB]);
             load(s + NB - 1, r[(j + NB - 1) % NB]);
             lds_barrier();
         }
@@ -296,47 +346,31 @@ __device__ void stage_role(IsoSm<TIn, K>& sm, const FwdArgs& p, int bh, int vt, 
 // ---------------------------------------------------------------- scan role
 template <typename TIn, class K>
 __device__ void scan_role(IsoSm<TIn, K>& sm, const FwdArgs& p, int bh, int vt, int lane) {
-    constexpr int C = K::C, DK = K::DK, ES = K::ES, NB = K::NBS;
+    constexpr int C = K::C, DK = K::DK, NB = K::NBS;
     const int nchunks = (p.T + C - 1) / C;
     const size_t rowbase = (size_t)bh * p.T;
-    const char* kb = (const char*)((const TIn*)p.k + rowbase * DK);
     const char* ab = (const char*)(p.a + rowbase);
     const char* qnb = (const char*)(p.qn + rowbase);
     const char* rb = (const char*)(p.r + rowbase);
 
     struct Regs {
-        f32x4 k[K::KR];  // the lane's k row as raw 16-byte words
         float a, qn, r;
     };
     Regs rg[NB];
     auto load = [&](int c, Regs& g) {
         const int t0 = c * C, n = p.T - t0;
         const int rows = n < 0 ? 0 : (n < C ? n : C);
-        const auto rk = make_rsrc(kb + (size_t)t0 * DK * ES, rows * DK * ES);
-#pragma unroll
-        for (int x = 0; x < K::KR; ++x) g.k[x] = buf_load<f32x4>(rk, lane * DK * ES + 16 * x);
         g.a = buf_load<float>(make_rsrc(ab + (size_t)t0 * 4, rows * 4), lane * 4);
         g.qn = buf_load<float>(make_rsrc(qnb + (size_t)t0 * 4, rows * 4), lane * 4);
         g.r = buf_load<float>(make_rsrc(rb + (size_t)t0 * 4, rows * 4), lane * 4);
     };
     float lc = p.l0 ? p.l0[bh] : 1.f;
     auto scan = [&](int c, const Regs& g) {
-        ScanOut& o = sm.sc[c & 1];
+        ScanOut& o = sm.sc[c % K::NCB];
         const int t = lane;
         const int L = (p.T - c * C) < C ? (p.T - c * C) : C;
         const bool in = t < L;
-        float ksq = 0.f;
-#pragma unroll
-        for (int x = 0; x < K::KR; ++x) {
-            if constexpr (sizeof(TIn) == 2) {
-                const bf16x8 v = __builtin_bit_cast(bf16x8, g.k[x]);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) ksq = __builtin_fmaf((float)v[e], (float)v[e], ksq);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) ksq = __builtin_fmaf(g.k[x][e], g.k[x][e], ksq);
-            }
-        }
+        const float ksq = sm.ksq[c & 1][t];  // from the staging waves
         const float rho = in ? 1.f / g.r : 0.f;
         const float b = ksq * rho * (1.f / (float)DK);
         const float a2 = g.a * g.a;
@@ -365,9 +399,10 @@ __device__ void scan_role(IsoSm<TIn, K>& sm, const FwdArgs& p, int bh, int vt, i
         }
         lc = lane_bcast(lt, L - 1);
     };
-    constexpr int NLD = K::KR + 3;
+    constexpr int NLD = 3;
 #pragma unroll
     for (int j = 0; j < NB - 1; ++j) load(j, rg[j]);
+    lds_barrier();  // chunk 0's key norms
     const int nloop = round_up(nchunks + 1, NB);
     for (int s0 = 0; s0 < nloop; s0 += NB) {
 #pragma unroll
@@ -382,6 +417,90 @@ __device__ void scan_role(IsoSm<TIn, K>& sm, const FwdArgs& p, int bh, int vt, i
     for (int s = nloop; s < total_steps<K>(nchunks); ++s) lds_barrier();
     if (lane == 0) sm.lT = lc;
     if (p.lT && vt == 0 && lane == 0) p.lT[bh] = lc;
+    lds_barrier();
+}
+
+// Scaled causal score tiles of token tile tau of a chunk: for every s-tile
+// sig <= tau, S[s,t] = k_s . q_t times c_s 2^(Gamma_t - Gamma_s), zero for
+// s > t, as K=16 MFMA B fragments.  kfrag(sig, kk) gives the K=32 fragment of
+// k rows sig*16.. at dims kk*32..; Qf the q fragments of the tile's tokens.
+template <typename TIn, class K, bool WIDE, class KF>
+__device__ __forceinline__ void score_tiles(const ScanOut& so, KF kfrag,
+                                            const typename Frag<TIn>::V (&Qf)[K::DK / 32], int tau,
+                                            int c16, int g, typename Mma<TIn>::K16 (&P)[K::C / 16]) {
+    typedef Frag<TIn> F;
+    typedef Mma<TIn> M;
+    constexpr int KB = K::DK / 32, NT16 = K::C / 16;
+    const int t = tau * 16 + c16;
+    f32x4 S[NT16];
+#pragma unroll
+    for (int sig = 0; sig <= tau; ++sig) {
+        S[sig] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KB; ++kk) S[sig] = F::mma(kfrag(sig, kk), Qf[kk], S[sig]);
+    }
+    const float et = so.e[t], gt = so.gam[t];
+#pragma unroll
+    for (int sig = 0; sig <= tau; ++sig) {
+        f32x4 sv = S[sig];
+        if constexpr (!WIDE) {
+            const f32x4 ei = *(const f32x4*)&so.ei[sig * 16 + 4 * g];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float v = sv[e] * ei[e] * et;
+                sv[e] = (sig < tau || 4 * g + e <= c16) ? v : 0.f;
+            }
+        } else {
+            const f32x4 gs = *(const f32x4*)&so.gam[sig * 16 + 4 * g];
+            const f32x4 cs = *(const f32x4*)&so.cs[sig * 16 + 4 * g];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float v = sv[e] * cs[e] * fast_exp2(gt - gs[e]);
+                sv[e] = (sig < tau || 4 * g + e <= c16) ? v : 0.f;
+            }
+        }
+        P[sig] = M::from_acc(sv);
+    }
+}
+
+// ------------------------------------------------------------------- P role
+// With PW: step s forms the score tiles of chunk s-1 into P[(s-1) & 1].
+template <typename TIn, class K>
+__device__ void p_role(IsoSm<TIn, K>& sm, const FwdArgs& p, int lane) {
+    typedef Frag<TIn> F;
+    typedef typename F::V FV;
+    constexpr int C = K::C, DK = K::DK, KB = DK / 32, NT16 = C / 16;
+    const int nchunks = (p.T + C - 1) / C;
+    const int c16 = lane & 15, g = lane >> 4;
+    auto pchunk = [&](int c, auto wide_t) {
+        constexpr bool WIDE = decltype(wide_t)::value;
+        const ChunkBuf<TIn, K>& B = sm.buf[c % K::NCB];
+        const ScanOut& so = sm.sc[c % K::NCB];
+        typename Mma<TIn>::K16(*out)[64] = sm.P[c & 1];
+        FV Kf[NT16][KB];
+#pragma unroll
+        for (int sig = 0; sig < NT16; ++sig)
+#pragma unroll
+            for (int kk = 0; kk < KB; ++kk) Kf[sig][kk] = F::ld(&B.Kr[sig * 16 + c16][kk * 32], g);
+#pragma unroll
+        for (int tau = 0; tau < NT16; ++tau) {
+            FV Qf[KB];
+#pragma unroll
+            for (int kk = 0; kk < KB; ++kk) Qf[kk] = F::ld(&B.Q[tau * 16 + c16][kk * 32], g);
+            typename Mma<TIn>::K16 P[NT16];
+            score_tiles<TIn, K, WIDE>(so, [&](int sig, int kk) { return Kf[sig][kk]; }, Qf, tau, c16, g, P);
+#pragma unroll
+            for (int sig = 0; sig <= tau; ++sig) out[tau * (tau + 1) / 2 + sig][lane] = P[sig];
+        }
+    };
+    lds_barrier();  // chunk 0's key norms
+    for (int s = 0; s < total_steps<K>(nchunks); ++s) {
+        if (s >= 1 && s <= nchunks) {
+            if (__builtin_amdgcn_readfirstlane(sm.sc[(s - 1) % K::NCB].wide)) pchunk(s - 1, std::true_type{});
+            else pchunk(s - 1, std::false_type{});
+        }
+        lds_barrier();
+    }
     lds_barrier();
 }
 
@@ -415,8 +534,8 @@ __device__ void mma_role(IsoSm<TIn, K>& sm, const FwdArgs& p, int bh, int vt, in
         typedef typename F::V FV;
         constexpr int KB = DK / 32, NT16 = C / 16;
         constexpr bool KHOIST = DK <= 64;  // keep every K tile's fragments in registers
-        const ChunkBuf<TIn, K>& B = sm.buf[c & 1];
-        const ScanOut& so = sm.sc[c & 1];
+        const ChunkBuf<TIn, K>& B = sm.buf[c % K::NCB];
+        const ScanOut& so = sm.sc[c % K::NCB];
         const int t0 = c * C;
         const int L = (p.T - t0) < C ? (p.T - t0) : C;
         // o rows of this chunk, range-checked so rows past T are not written
@@ -425,8 +544,8 @@ __device__ void mma_role(IsoSm<TIn, K>& sm, const FwdArgs& p, int bh, int vt, in
         FV AM[KB];
 #pragma unroll
         for (int kk = 0; kk < KB; ++kk) AM[kk] = F::from_acc(accM[2 * kk], accM[2 * kk + 1]);
-        FV Kf[KHOIST ? NT16 : 1][KB];
-        if constexpr (KHOIST) {
+        FV Kf[KHOIST && !K::PW ? NT16 : 1][KB];
+        if constexpr (KHOIST && !K::PW) {
 #pragma unroll
             for (int sig = 0; sig < NT16; ++sig)
 #pragma unroll
@@ -438,43 +557,22 @@ __device__ void mma_role(IsoSm<TIn, K>& sm, const FwdArgs& p, int bh, int vt, in
             FV Qf[KB];
 #pragma unroll
             for (int kk = 0; kk < KB; ++kk) Qf[kk] = F::ld(&B.Q[t][kk * 32], g);
-            // causal S^T tiles (rows s, column t) and the state readout, all
-            // independent products issued back to back
-            f32x4 S[NT16];
-#pragma unroll
-            for (int sig = 0; sig <= tau; ++sig) {
-                S[sig] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kk = 0; kk < KB; ++kk) {
-                    const FV kf = KHOIST ? Kf[KHOIST ? sig : 0][kk] : F::ld(&B.Kr[sig * 16 + c16][kk * 32], g);
-                    S[sig] = F::mma(kf, Qf[kk], S[sig]);
-                }
-            }
+            // the state readout and the scaled causal score tiles
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < KB; ++kk) acc = F::mma(AM[kk], Qf[kk], acc);
-            const float et = so.e[t], gt = so.gam[t];
             typename M::K16 P[NT16];
+            if constexpr (K::PW) {
 #pragma unroll
-            for (int sig = 0; sig <= tau; ++sig) {
-                f32x4 sv = S[sig];
-                if constexpr (!WIDE) {
-                    const f32x4 ei = *(const f32x4*)&so.ei[sig * 16 + 4 * g];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float v = sv[e] * ei[e] * et;
-                        sv[e] = (sig < tau || 4 * g + e <= c16) ? v : 0.f;
-                    }
-                } else {
-                    const f32x4 gs = *(const f32x4*)&so.gam[sig * 16 + 4 * g];
-                    const f32x4 cs = *(const f32x4*)&so.cs[sig * 16 + 4 * g];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float v = sv[e] * cs[e] * fast_exp2(gt - gs[e]);
-                        sv[e] = (sig < tau || 4 * g + e <= c16) ? v : 0.f;
-                    }
-                }
-                P[sig] = M::from_acc(sv);
+                for (int sig = 0; sig <= tau; ++sig) P[sig] = sm.P[c & 1][tau * (tau + 1) / 2 + sig][lane];
+            } else {
+                score_tiles<TIn, K, WIDE>(
+                    so,
+                    [&](int sig, int kk) {
+                        if constexpr (KHOIST) return Kf[KHOIST ? sig : 0][kk];
+                        else return F::ld(&B.Kr[sig * 16 + c16][kk * 32], g);
+                    },
+                    Qf, tau, c16, g, P);
             }
             acc *= so.fc[t];
 #pragma unroll
@@ -507,10 +605,15 @@ __device__ void mma_role(IsoSm<TIn, K>& sm, const FwdArgs& p, int bh, int vt, in
                 accM[it] = M::mma32(M::ld32(&B.KT[it * 16 + c16][kb * 32 + 8 * g]), vf, accM[it]);
         }
     };
+    constexpr int LAG = K::PW ? 2 : 1;  // chunk finished in step s: s - LAG
+    lds_barrier();                      // chunk 0's key norms
     for (int s = 0; s < total_steps<K>(nchunks); ++s) {
-        if (s >= 1 && s <= nchunks) {
-            if (__builtin_amdgcn_readfirstlane(sm.sc[(s - 1) & 1].wide)) chunk(s - 1, std::true_type{});
-            else chunk(s - 1, std::false_type{});
+        if (s >= LAG && s < nchunks + LAG) {
+            if (K::PW) chunk(s - LAG, std::false_type{});  // the P wave handled the range
+            else if (__builtin_amdgcn_readfirstlane(sm.sc[(s - LAG) % K::NCB].wide))
+                chunk(s - LAG, std::true_type{});
+            else
+                chunk(s - LAG, std::false_type{});
         }
         lds_barrier();
     }
@@ -554,7 +657,13 @@ __global__ __launch_bounds__((IP<TIn, DK, DV>::NT)) void kla_fwd_iso_pipe_kernel
     } else if (wave == K::NSW) {
         scan_role<TIn, K>(sm, p, bh, vt, lane);
     } else {
-        mma_role<TIn, K>(sm, p, bh, vt, wave - K::NSW - 1, lane);
+        if constexpr (K::PW) {
+            if (wave == K::NSW + 1) {
+                p_role<TIn, K>(sm, p, lane);
+                return;
+            }
+        }
+        mma_role<TIn, K>(sm, p, bh, vt, wave - K::NSW - 1 - (K::PW ? 1 : 0), lane);
     }
 }
 
