@@ -86,9 +86,14 @@ FwdKernel pick_kernel(const klaDims* d, int* n_vtiles) {
         *n_vtiles = nvt_env > 0 ? nvt_env : kla::fwd_iso_vtiles(d->B, d->H, d->dk);
         return FK_ISO;
     }
+    if (use_pipe()) {
+        const int nvt_pipe = nvt_env > 0 ? nvt_env : kla::fwd_diag_pipe_vtiles(d->dk, d->dv, d->dtype);
+        if (nvt_pipe > 0 && kla::fwd_diag_pipe_supported(d->dk, d->dv, nvt_pipe, d->dtype)) {
+            *n_vtiles = nvt_pipe;
+            return FK_DIAG_PIPE;
+        }
+    }
     *n_vtiles = nvt_env > 0 ? nvt_env : kla::fwd_diag_vtiles(d->B, d->H, d->T, d->dk, d->dv);
-    if (use_pipe() && kla::fwd_diag_pipe_supported(d->dk, d->dv, *n_vtiles, d->dtype))
-        return FK_DIAG_PIPE;
     return FK_DIAG_CHUNK;
 }
 

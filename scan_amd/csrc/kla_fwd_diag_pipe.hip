@@ -48,7 +48,7 @@ struct P3 {
     static constexpr int C = 32;                 // tokens per chunk
     static constexpr int NCW = DK / 64;          // chain waves
     static constexpr int NMW = DV / 32;          // MMA waves
-    static constexpr int JT = DV / (16 * NMW);   // 16-column value tiles per MMA wave
+    static constexpr int JT = 2;                 // 16-column value tiles per MMA wave
     static constexpr int NGW = 4;                // gate waves
     static constexpr int NW = NCW + NMW + NGW;
     static constexpr int NT = 64 * NW;
@@ -72,7 +72,7 @@ struct P3 {
     static constexpr int NBG = 2;
     static constexpr int UNR = NBC * NBG / (NBC == NBG ? NBC : 1);
     static_assert(DK == 64 || DK == 128, "key dims 64 and 128");
-    static_assert(DV % 32 == 0 && JT >= 1 && VUNITS % 256 == 0, "value tiles");
+    static_assert(DV % 32 == 0 && VUNITS % 256 == 0, "value tiles");
 };
 
 template <typename TIn, class K>
@@ -218,10 +218,16 @@ __device__ void chain_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int
     };
     Buf b[NB];
 
-    // Rows of a and k are read through buffer resources that span the rows
-    // of one chunk, so rows past T (the tail of the last chunk, chunks past
-    // the end) read as zero.
+    // Rows of a and k are read through buffer resources over one chunk's
+    // rows, so rows past T (the tail of the last chunk, chunks past the end)
+    // read as zero.  At dk = 64 the resources cover 4 KiB windows, whose row
+    // offsets are immediates: register offsets for the rows past 4 KiB spill
+    // the chain role there.  At dk = 128 one resource per chunk and input is
+    // faster (measured).
     constexpr int ARB = DK * 4, KRB = DK * (int)sizeof(TIn);  // row bytes
+    constexpr bool WIN = DK < 128;
+    constexpr int ARW = WIN && 4096 / ARB < C ? 4096 / ARB : C;  // rows per resource
+    constexpr int KRW = WIN && 4096 / KRB < C ? 4096 / KRB : C;
     const char* abase = (const char*)(p.a + rowbase * DK);
     const char* kbase = (const char*)(kp + rowbase * DK);
     const char* rbase = (const char*)(p.r + rowbase);
@@ -231,14 +237,24 @@ __device__ void chain_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int
     };
     auto load = [&](int c, Buf& b) {
         const int t0 = c * C, rows = rows_left(t0, C);
-        const auto ra = make_rsrc(abase + (size_t)t0 * ARB, rows * ARB);
-        const auto rk = make_rsrc(kbase + (size_t)t0 * KRB, rows * KRB);
+        const char* a0 = abase + (size_t)t0 * ARB;
+        const char* k0 = kbase + (size_t)t0 * KRB;
 #pragma unroll
-        for (int t = 0; t < C; ++t) b.a[t] = buf_load<float>(ra, i * 4 + t * ARB);
+        for (int w = 0; w < C / ARW; ++w) {
+            const int n = rows - w * ARW;
+            const auto rs = make_rsrc(a0 + w * ARW * ARB, (n < 0 ? 0 : (n < ARW ? n : ARW)) * ARB);
 #pragma unroll
-        for (int t = 0; t < C; ++t)
-            b.k[t] = sizeof(TIn) == 2 ? (unsigned)buf_load<unsigned short>(rk, i * 2 + t * KRB)
-                                      : buf_load<unsigned>(rk, i * 4 + t * KRB);
+            for (int t = 0; t < ARW; ++t) b.a[w * ARW + t] = buf_load<float>(rs, i * 4 + t * ARB);
+        }
+#pragma unroll
+        for (int w = 0; w < C / KRW; ++w) {
+            const int n = rows - w * KRW;
+            const auto rs = make_rsrc(k0 + w * KRW * KRB, (n < 0 ? 0 : (n < KRW ? n : KRW)) * KRB);
+#pragma unroll
+            for (int t = 0; t < KRW; ++t)
+                b.k[w * KRW + t] = sizeof(TIn) == 2 ? (unsigned)buf_load<unsigned short>(rs, i * 2 + t * KRB)
+                                                    : buf_load<unsigned>(rs, i * 4 + t * KRB);
+        }
         b.r = buf_load<float>(make_rsrc(rbase + (size_t)t0 * 4, rows * 4), lane * 4);
     };
     auto step = [&](int c, Buf& cur, Buf& nxt) {
@@ -564,24 +580,16 @@ __device__ void mma_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int b
                 const OpFac<TIn, K>& o = sm.op[par].fac;
                 // o rows of this chunk; rows past T fall outside the range
                 const auto ro = make_rsrc(op + (rowbase + t0) * p.dv, L * p.dv * (int)sizeof(TIn));
-                auto ldq = [&](int b, int kk) { return F::ld(&o.Q[qw_row<K>(b * 16 + c16)][kk * 32], g); };
-                auto ldv = [&](int jj) {
-                    const int j = (mw * JT + jj) * 16 + c16, sw = vt_swz<K>(j);
-                    return F::ld2(&sm.VT[par][j][(4 * g) ^ sw], &sm.VT[par][j][(16 + 4 * g) ^ sw]);
-                };
-                // With up to two 16-column tiles per wave the Q^ and V^T
-                // fragments stay in registers for the whole chunk; with more,
-                // the state alone takes half the register file, so the work
-                // runs tile by tile and the fragments are re-read from LDS.
-                constexpr bool LEAN = JT > 2;
                 FV Qf[2][KB], Vf[JT];
-                if constexpr (!LEAN) {
 #pragma unroll
-                    for (int b = 0; b < 2; ++b)
+                for (int b = 0; b < 2; ++b)
 #pragma unroll
-                        for (int kk = 0; kk < KB; ++kk) Qf[b][kk] = ldq(b, kk);
+                    for (int kk = 0; kk < KB; ++kk)
+                        Qf[b][kk] = F::ld(&o.Q[qw_row<K>(b * 16 + c16)][kk * 32], g);
 #pragma unroll
-                    for (int jj = 0; jj < JT; ++jj) Vf[jj] = ldv(jj);
+                for (int jj = 0; jj < JT; ++jj) {
+                    const int j = (mw * JT + jj) * 16 + c16, sw = vt_swz<K>(j);
+                    Vf[jj] = F::ld2(&sm.VT[par][j][(4 * g) ^ sw], &sm.VT[par][j][(16 + 4 * g) ^ sw]);
                 }
                 // causal S^T tiles (sigma, tau)
                 f32x4 s00 = {0.f, 0.f, 0.f, 0.f}, s01 = s00, s11 = s00;
@@ -589,10 +597,9 @@ __device__ void mma_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int b
                 for (int kk = 0; kk < KB; ++kk) {
                     const FV w0 = F::ld(&o.W[qw_row<K>(c16)][kk * 32], g);
                     const FV w1 = F::ld(&o.W[qw_row<K>(16 + c16)][kk * 32], g);
-                    const FV q0 = LEAN ? ldq(0, kk) : Qf[0][kk], q1 = LEAN ? ldq(1, kk) : Qf[1][kk];
-                    s00 = F::mma(w0, q0, s00);
-                    s01 = F::mma(w0, q1, s01);
-                    s11 = F::mma(w1, q1, s11);
+                    s00 = F::mma(w0, Qf[0][kk], s00);
+                    s01 = F::mma(w0, Qf[1][kk], s01);
+                    s11 = F::mma(w1, Qf[1][kk], s11);
                 }
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -600,46 +607,34 @@ __device__ void mma_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int b
                 }
                 const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
                 const FV P0 = F::from_acc(s00, zero), P1 = F::from_acc(s01, s11);
-                if constexpr (LEAN) __builtin_amdgcn_sched_barrier(0);
                 // readout O^T = m^T Q^^T + V^T P^T, the state as the A operand
-                // (each column tile reads its state before its own update)
 #pragma unroll
                 for (int jj = 0; jj < JT; ++jj) {
-                    if constexpr (LEAN) __builtin_amdgcn_sched_barrier(0);
-                    const FV vf = LEAN ? ldv(jj) : Vf[jj];
                     f32x4 out0 = {0.f, 0.f, 0.f, 0.f}, out1 = out0;
 #pragma unroll
                     for (int kk = 0; kk < KB; ++kk) {
                         const FV am = F::from_acc(acc[2 * kk][jj], acc[2 * kk + 1][jj]);
-                        out0 = F::mma(am, LEAN ? ldq(0, kk) : Qf[0][kk], out0);
-                        out1 = F::mma(am, LEAN ? ldq(1, kk) : Qf[1][kk], out1);
+                        out0 = F::mma(am, Qf[0][kk], out0);
+                        out1 = F::mma(am, Qf[1][kk], out1);
                     }
-                    out0 = F::mma(vf, P0, out0);
-                    out1 = F::mma(vf, P1, out1);
+                    out0 = F::mma(Vf[jj], P0, out0);
+                    out1 = F::mma(Vf[jj], P1, out1);
                     const int col = vt * DV + (mw * JT + jj) * 16 + 4 * g;
                     buf_store(Quad<TIn>::make(out0), ro, (c16 * p.dv + col) * (int)sizeof(TIn));
                     buf_store(Quad<TIn>::make(out1), ro, ((16 + c16) * p.dv + col) * (int)sizeof(TIn));
-                    if constexpr (LEAN) {
-                        // m[:, tile] += W^^T V[:, tile]
-#pragma unroll
-                        for (int it = 0; it < IT; ++it)
-                            acc[it][jj] = F::mma(F::ld(&o.WT[it * 16 + c16][0], g), vf, acc[it][jj]);
-                    }
                 }
-                if constexpr (!LEAN) {
-                    // m += W^^T V
+                // m += W^^T V
 #pragma unroll
-                    for (int it = 0; it < IT; ++it) {
-                        const FV wt = F::ld(&o.WT[it * 16 + c16][0], g);
+                for (int it = 0; it < IT; ++it) {
+                    const FV wt = F::ld(&o.WT[it * 16 + c16][0], g);
 #pragma unroll
-                        for (int jj = 0; jj < JT; ++jj) acc[it][jj] = F::mma(wt, Vf[jj], acc[it][jj]);
-                    }
+                    for (int jj = 0; jj < JT; ++jj) acc[it][jj] = F::mma(wt, Vf[jj], acc[it][jj]);
                 }
             } else {
                 // exact path: m <- f_t (.) m + w_t v_t^T, o_t = q_t^T m, token by token
                 const OpRaw<K>& o = sm.op[par].raw;
-                // one 16-column tile at a time, so the loop touches a quarter
-                // of the state at most
+                // one 16-column tile at a time: updating every tile per token
+                // raised the register demand of the whole role
 #pragma unroll
                 for (int jj = 0; jj < JT; ++jj) {
                     const int j = (mw * JT + jj) * 16 + c16;
@@ -753,18 +748,20 @@ hipError_t launch(const FwdArgs& a, hipStream_t s) {
 bool fwd_diag_pipe_supported(int dk, int dv, int nvt, int dtype) {
     if (dk != dv || nvt < 1 || dv % nvt) return false;
     const int dvt = dv / nvt;
-    if (dtype == DT_BF16) return (dk == 128 && (dvt == 128 || dvt == 64)) || (dk == 64 && dvt == 64);
-    return dk == 64 && dvt == 64;
+    return dvt == 64 && (dk == 64 || (dk == 128 && dtype == DT_BF16));
+}
+
+int fwd_diag_pipe_vtiles(int dk, int dv, int dtype) {
+    // 64-column tiles: measured faster than wider ones (register pressure)
+    // and than 32-column tiles of the single-role kernel
+    return dv % 64 == 0 && fwd_diag_pipe_supported(dk, dv, dv / 64, dtype) ? dv / 64 : 0;
 }
 
 hipError_t launch_fwd_diag_pipe(const FwdArgs& a, int dtype, hipStream_t s) {
     if (!fwd_diag_pipe_supported(a.dk, a.dv, a.n_vtiles, dtype)) return hipErrorInvalidValue;
     const int dvt = a.dv / a.n_vtiles;
-    if (dtype == DT_BF16) {
-        if (a.dk == 128 && dvt == 128) return launch<bf16, 128, 128>(a, s);
-        if (a.dk == 128 && dvt == 64) return launch<bf16, 128, 64>(a, s);
-        return launch<bf16, 64, 64>(a, s);
-    }
+    (void)dvt;
+    if (dtype == DT_BF16) return a.dk == 128 ? launch<bf16, 128, 64>(a, s) : launch<bf16, 64, 64>(a, s);
     return launch<float, 64, 64>(a, s);
 }
 

@@ -358,7 +358,10 @@ int fwd_diag_nseg(int B, int H, int T, int dk, int dv, int nvt) {
     if (units >= 192 || T < 2048) return 1;
     int n = (int)((256 + units - 1) / units);
     if (n > T / 1024) n = T / 1024;
-    return n < 2 ? 1 : n;
+    // the extra passes cost about what a workgroup spends on 1,500 tokens:
+    // split only when a workgroup saves more than that
+    if (n < 2 || T - T / n < 1536) return 1;
+    return n;
 }
 
 int fwd_diag_seg_len(int T, int nseg) {

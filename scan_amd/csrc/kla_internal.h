@@ -88,6 +88,8 @@ enum Dt { DT_F32 = 0, DT_BF16 = 1 };
 hipError_t launch_fwd_diag(const FwdArgs& a, int dtype, hipStream_t s);
 hipError_t launch_fwd_diag_pipe(const FwdArgs& a, int dtype, hipStream_t s);
 bool fwd_diag_pipe_supported(int dk, int dv, int nvt, int dtype);
+// Value tiles of the wave-specialised diagonal forward (0 = shape not built).
+int fwd_diag_pipe_vtiles(int dk, int dv, int dtype);
 hipError_t launch_fwd_iso(const FwdArgs& a, int dtype, hipStream_t s);
 // Wave-specialised pipelined isotropic forward: bf16 dk = dv in {64, 128},
 // fp32 dk = dv = 64, 64 or 32 value columns per workgroup.

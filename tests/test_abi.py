@@ -155,8 +155,11 @@ def test_header_documents_every_entry_point():
 def test_kernel_name_reports_the_dispatch():
     lm = KlaDims(8, 16, 2048, 128, 128, BF16, DIAG)
     assert scan_amd.klaFwdKernelName(lm) == "kla_fwd_diag_pipe_kernel (value tiles)"
+    # dv = 128 always runs as two 64-column tiles; dk = dv = 64 as one
     assert scan_amd.klaFwdKernelName(KlaDims(64, 16, 2048, 128, 128, BF16, DIAG)) == \
-        "kla_fwd_diag_pipe_kernel"
+        "kla_fwd_diag_pipe_kernel (value tiles)"
+    assert scan_amd.klaFwdKernelName(KlaDims(8, 16, 2048, 64, 64, BF16, DIAG)) == "kla_fwd_diag_pipe_kernel"
+    assert scan_amd.klaFwdKernelName(KlaDims(8, 16, 2048, 64, 64, F32, DIAG)) == "kla_fwd_diag_pipe_kernel"
     assert scan_amd.klaFwdKernelName(KlaDims(2, 3, 100, 32, 32, F32, DIAG)) == "kla_fwd_diag_kernel"
     assert scan_amd.klaFwdKernelName(KlaDims(2, 3, 100, 64, 64, F32, ISO)) == \
         "kla_fwd_iso_pipe_kernel (value tiles)"
@@ -177,6 +180,9 @@ def test_split_workspace_contract(monkeypatch):
     ws = scan_amd.klaFwdWorkspaceBytes(long)
     assert ws > 0
     assert scan_amd.klaFwdWorkspaceBytes(KlaDims(8, 16, 2048, 128, 128, BF16, DIAG)) == 0
+    # a split pays only when each workgroup saves enough tokens
+    assert scan_amd.klaFwdWorkspaceBytes(KlaDims(2, 16, 2048, 64, 64, BF16, DIAG)) == 0
+    assert scan_amd.klaFwdWorkspaceBytes(KlaDims(2, 16, 8192, 64, 64, BF16, DIAG)) > 0
     assert scan_amd.klaFwdWorkspaceBytes(KlaDims(1, 16, 32768, 32, 32, F32, DIAG)) == 0
     # a split forward without (or with too small) a workspace is rejected
     assert fwd_call(long) == WS
