@@ -4,6 +4,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 namespace kla {
 
 typedef __bf16 bf16;
@@ -42,15 +44,72 @@ struct Mma<bf16> {
     }
 };
 
+// fp32 operands run on the bf16 matrix cores as split pairs: x = hi + lo
+// with hi = bf16(x) and lo = bf16(x - hi), and a product as
+// hi*hi + hi*lo + lo*hi, accumulated in fp32 (the dropped lo*lo and the
+// rounding of lo are about 2^-17 of |x y| each).  gfx950 has no xf32 MFMA,
+// and three bf16 MFMAs take about a fifth of the time of the fp32 MFMAs
+// covering the same K.
+struct SplitK32 { bf16x8 hi, lo; };
+struct SplitK16 { s16x4 hi, lo; };
+
+__device__ __forceinline__ SplitK32 split8(f32x4 a, f32x4 b) {  // slots 0-3 from a, 4-7 from b
+    SplitK32 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const bf16 ha = (bf16)a[e], hb = (bf16)b[e];
+        r.hi[e] = ha;
+        r.hi[e + 4] = hb;
+        r.lo[e] = (bf16)(a[e] - (float)ha);
+        r.lo[e + 4] = (bf16)(b[e] - (float)hb);
+    }
+    return r;
+}
+
+__device__ __forceinline__ SplitK16 split4(f32x4 a) {
+    bf16x4 h, l;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        h[e] = (bf16)a[e];
+        l[e] = (bf16)(a[e] - (float)h[e]);
+    }
+    SplitK16 r;
+    r.hi = __builtin_bit_cast(s16x4, h);
+    r.lo = __builtin_bit_cast(s16x4, l);
+    return r;
+}
+
 template <>
 struct Mma<float> {
+    typedef SplitK32 K32;
+    typedef SplitK16 K16;
+    static __device__ __forceinline__ K32 make32(f32x4 a, f32x4 b) { return split8(a, b); }
+    static __device__ __forceinline__ K32 ld32(const float* p) {
+        return split8(*(const f32x4*)p, *(const f32x4*)(p + 4));
+    }
+    static __device__ __forceinline__ K16 ld16(const float* p) { return split4(*(const f32x4*)p); }
+    static __device__ __forceinline__ f32x4 mma32(K32 a, K32 b, f32x4 c) {
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b.hi, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.lo, c, 0, 0, 0);
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ f32x4 mma16(K16 a, K16 b, f32x4 c) {
+        c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.lo, b.hi, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.hi, b.lo, c, 0, 0, 0);
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.hi, b.hi, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ K16 from_acc(f32x4 x) { return split4(x); }
+};
+
+// The fp32 MFMAs themselves, same interface as Mma<float>: faster than the
+// split pairs where the operands are re-read for every product, as in the
+// single-role kernels at large dk.
+struct MmaF32 {
     struct K32 { f32x4 lo, hi; };
     typedef f32x4 K16;
+    static __device__ __forceinline__ K32 make32(f32x4 a, f32x4 b) { return K32{a, b}; }
     static __device__ __forceinline__ K32 ld32(const float* p) {
-        K32 r;
-        r.lo = *(const f32x4*)p;
-        r.hi = *(const f32x4*)(p + 4);
-        return r;
+        return K32{*(const f32x4*)p, *(const f32x4*)(p + 4)};
     }
     static __device__ __forceinline__ K16 ld16(const float* p) { return *(const f32x4*)p; }
     static __device__ __forceinline__ f32x4 mma32(K32 a, K32 b, f32x4 c) {
@@ -67,6 +126,12 @@ struct Mma<float> {
     }
     static __device__ __forceinline__ K16 from_acc(f32x4 x) { return x; }
 };
+
+// Matrix-core operands for the single-role kernels: split pairs for fp32 at
+// dk 32 and 64, the fp32 MFMAs at dk 16 and 128 (measured).
+template <typename TIn, int DK>
+using MmaFor = typename std::conditional<std::is_same<TIn, float>::value && (DK <= 16 || DK >= 128), MmaF32,
+                                         Mma<TIn>>::type;
 
 // Eight bf16/f32 values forming one K=32 operand fragment: slots 0-3 hold
 // k = 4g..4g+3 of the first 16-block, slots 4-7 the same of the second.
@@ -92,21 +157,25 @@ template <> struct Frag<bf16> {
     }
 };
 template <> struct Frag<float> {
+    typedef SplitK32 V;  // split bf16 pairs, see Mma<float>
+    static __device__ __forceinline__ V ld(const float* row, int g) { return ld2(row + 4 * g, row + 16 + 4 * g); }
+    static __device__ __forceinline__ V ld2(const float* lo_p, const float* hi_p) {
+        return split8(*(const f32x4*)lo_p, *(const f32x4*)hi_p);
+    }
+    static __device__ __forceinline__ V from_acc(f32x4 lo, f32x4 hi) { return split8(lo, hi); }
+    static __device__ __forceinline__ f32x4 mma(V a, V b, f32x4 c) { return Mma<float>::mma32(a, b, c); }
+};
+
+// K=32 fragments for the fp32 MFMAs themselves (slot order as Frag<bf16>).
+struct FragF32 {
     struct V { f32x4 lo, hi; };
     static __device__ __forceinline__ V ld(const float* row, int g) { return ld2(row + 4 * g, row + 16 + 4 * g); }
     static __device__ __forceinline__ V ld2(const float* lo_p, const float* hi_p) {
-        V r;
-        r.lo = *(const f32x4*)lo_p;
-        r.hi = *(const f32x4*)hi_p;
-        return r;
+        return V{*(const f32x4*)lo_p, *(const f32x4*)hi_p};
     }
-    static __device__ __forceinline__ V from_acc(f32x4 lo, f32x4 hi) { V r; r.lo = lo; r.hi = hi; return r; }
+    static __device__ __forceinline__ V from_acc(f32x4 lo, f32x4 hi) { return V{lo, hi}; }
     static __device__ __forceinline__ f32x4 mma(V a, V b, f32x4 c) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[e], b.lo[e], c, 0, 0, 0);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[e], b.hi[e], c, 0, 0, 0);
-        return c;
+        return MmaF32::mma32(MmaF32::K32{a.lo, a.hi}, MmaF32::K32{b.lo, b.hi}, c);
     }
 };
 

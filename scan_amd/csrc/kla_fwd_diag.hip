@@ -26,6 +26,8 @@
 //            after the chunk's first token), q^ = q G, w^ = w / G
 //   mfma     S^T = W^ Q^^T (causal 16x16 tiles), O^T = M^T Q^^T + V^T P^T,
 //            M += W^^T V; M is the fp32 state in accumulator registers
+// The barriers order LDS only: __syncthreads() would also wait for the loads
+// of the next chunk issued before it, which are meant to stay in flight.
 // Every factor of the factorisation is bounded: G in [2^-64, 1].  If a gate
 // product inside a chunk would fall below 2^-64, the chunk is cut there and
 // the rest is processed as a new sub-chunk (exact, only slower).
@@ -143,7 +145,7 @@ template <typename TIn, class K>
 __device__ __forceinline__ void mfma_subchunk(Smem<TIn, K>& sm, f32x4 (&accM)[K::IT][K::JT],
                                               const FwdArgs& p, int bh, int vt, int t0,
                                               int ts, int L1, int wave, int lane) {
-    typedef Mma<TIn> M;
+    typedef MmaFor<TIn, K::DK> M;
     const int c16 = lane & 15, g = lane >> 4;
 
     // 1. m <- (pending end scale * first-token gate) (.) m, row-wise.
@@ -261,7 +263,7 @@ __global__ __launch_bounds__((Cfg<TIn, DK, DV, C>::NT)) void kla_fwd_diag_kernel
         sm.lcar[tid] = p.l0 ? p.l0[(size_t)bh * DK + tid] : 1.f;
         sm.E[1][tid] = 1.f;
     }
-    __syncthreads();
+    lds_barrier();
     f32x4 accM[K::IT][K::JT];
 #pragma unroll
     for (int it = 0; it < K::IT; ++it)
@@ -287,7 +289,7 @@ __global__ __launch_bounds__((Cfg<TIn, DK, DV, C>::NT)) void kla_fwd_diag_kernel
 
         // ---- stage: rho, (a^2, b) for the chain, V^T
         if (tid < C) sm.rho[tid] = 1.f / cur.r;
-        __syncthreads();  // rho visible
+        lds_barrier();  // rho visible
 #pragma unroll
         for (int u = 0; u < K::TPG; ++u) {
             const int t = grp * K::TPG + u;
@@ -314,7 +316,7 @@ __global__ __launch_bounds__((Cfg<TIn, DK, DV, C>::NT)) void kla_fwd_diag_kernel
         ChunkRegs<TIn, K> nxt;
         const int t0n = t0 + C;
         if (t0n < p.T) load_chunk<TIn, K>(nxt, p, bh, vt, t0n, (p.T - t0n) < C ? (p.T - t0n) : C, tid);
-        __syncthreads();
+        lds_barrier();
 
         // ---- chain: one lane per key dim, sequential over the chunk
         if (tid < DK) {
@@ -327,7 +329,7 @@ __global__ __launch_bounds__((Cfg<TIn, DK, DV, C>::NT)) void kla_fwd_diag_kernel
             }
             sm.lcar[tid] = l;
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- gates (a): f = a lp / l, w = k / (r l)
         float f[K::TPG][2], w[K::TPG][2];
@@ -356,10 +358,10 @@ __global__ __launch_bounds__((Cfg<TIn, DK, DV, C>::NT)) void kla_fwd_diag_kernel
                 G[u][0] = p0;
                 G[u][1] = p1;
             }
-            __syncthreads();  // previous readers of gtot / sm.L1 are done
+            lds_barrier();  // previous readers of gtot / sm.L1 are done
             sm.gtot[grp][2 * ip] = p0;
             sm.gtot[grp][2 * ip + 1] = p1;
-            __syncthreads();
+            lds_barrier();
             // (c) cumulative gates, range check
             float pre0 = 1.f, pre1 = 1.f;
             for (int gg = 0; gg < grp; ++gg) {
@@ -376,7 +378,7 @@ __global__ __launch_bounds__((Cfg<TIn, DK, DV, C>::NT)) void kla_fwd_diag_kernel
                     firstbad = t < firstbad ? t : firstbad;
             }
             if (firstbad < L) atomicMin(&sm.L1, firstbad);
-            __syncthreads();
+            lds_barrier();
             const int L1 = sm.L1;
             // (d) operands of this sub-chunk; zero outside [ts, L1)
             TIn wt0[K::TPG], wt1[K::TPG];
@@ -409,18 +411,18 @@ __global__ __launch_bounds__((Cfg<TIn, DK, DV, C>::NT)) void kla_fwd_diag_kernel
                 sm.u.op.WT[2 * ip][grp * K::TPG + u] = wt0[u];
                 sm.u.op.WT[2 * ip + 1][grp * K::TPG + u] = wt1[u];
             }
-            __syncthreads();
+            lds_barrier();
 
             mfma_subchunk<TIn, K>(sm, accM, p, bh, vt, t0, ts, L1, wave, lane);
 
             par ^= 1;
             ts = L1;
             if (ts < L) {
-                __syncthreads();  // all waves done reading this sub-chunk's operands
+                lds_barrier();  // all waves done reading this sub-chunk's operands
                 if (tid == 0) sm.L1 = L;
             }
         }
-        __syncthreads();  // LDS free for the next chunk's stage
+        lds_barrier();  // LDS free for the next chunk's stage
         cur = nxt;
     }
 

@@ -18,6 +18,8 @@
 // with a scalar gate per token, so the chunk's decay matrix
 // D[s,t] = prod_{u=s+1..t} f_u = exp2(Gamma_t - Gamma_s) is formed entry-wise
 // (every entry <= 1, no range problem) and q, k feed the MFMA unscaled.
+// The barriers order LDS only, so the next chunk's loads stay in flight
+// across them.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -121,7 +123,7 @@ __device__ __forceinline__ void iso_load(IsoRegs<TIn, K>& R, const FwdArgs& p, i
 template <typename TIn, int DK, int DV>
 __global__ __launch_bounds__((IsoCfg<TIn, DK, DV>::NT)) void kla_fwd_iso_kernel(FwdArgs p) {
     typedef IsoCfg<TIn, DK, DV> K;
-    typedef Mma<TIn> M;
+    typedef MmaFor<TIn, K::DK> M;
     __shared__ IsoSmem<TIn, K> sm;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -142,7 +144,7 @@ __global__ __launch_bounds__((IsoCfg<TIn, DK, DV>::NT)) void kla_fwd_iso_kernel(
     }
 
     if (tid == 0) sm.lcar = p.l0 ? p.l0[bh] : 1.f;
-    __syncthreads();
+    lds_barrier();
     // state m0 = eta0 / l0, wave owns value tile `wave`: lane holds rows 4g+e, column c16
     f32x4 accM[K::IT];
     {
@@ -198,7 +200,7 @@ __global__ __launch_bounds__((IsoCfg<TIn, DK, DV>::NT)) void kla_fwd_iso_kernel(
         IsoRegs<TIn, K> nxt;
         const int t0n = t0 + K::C;
         if (t0n < p.T) iso_load<TIn, K>(nxt, p, bh, vt, t0n, (p.T - t0n) < K::C ? (p.T - t0n) : K::C, tid);
-        __syncthreads();
+        lds_barrier();
 
         // ---- precision scan and gates: wave 0, lane = token
         if (wave == 0) {
@@ -246,7 +248,7 @@ __global__ __launch_bounds__((IsoCfg<TIn, DK, DV>::NT)) void kla_fwd_iso_kernel(
                 sm.lcar = lend;
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- K~^T[i][s] = k_s[i] * c_s * exp2(Gamma_end - Gamma_s)
 #pragma unroll
@@ -264,7 +266,7 @@ __global__ __launch_bounds__((IsoCfg<TIn, DK, DV>::NT)) void kla_fwd_iso_kernel(
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- MFMA: readout and state update for this wave's value tile
         typename M::K16 AM[K::IT];
@@ -321,7 +323,7 @@ __global__ __launch_bounds__((IsoCfg<TIn, DK, DV>::NT)) void kla_fwd_iso_kernel(
                 accM[it] = M::mma32(M::ld32(&sm.KT[it * 16 + c16][sc * 32 + 8 * g]),
                                     M::ld32(&sm.VT[jrow][sc * 32 + 8 * g]), accM[it]);
         }
-        __syncthreads();
+        lds_barrier();
         cur = nxt;
     }
 

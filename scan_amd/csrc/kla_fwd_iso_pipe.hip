@@ -52,6 +52,11 @@ struct IP {
     // forms them itself and two chunk buffers rotate.
     static constexpr bool PW = DK == 64 && sizeof(TIn) == 2;
     static constexpr int NCB = PW ? 3 : 2;         // chunk buffers
+    // matrix-core operands: fp32 as split bf16 pairs, except with 64-column
+    // tiles, where the pairs' extra registers spill (measured slower)
+    static constexpr bool F32MMA = sizeof(TIn) == 4 && DV == 64;
+    typedef typename std::conditional<F32MMA, MmaF32, Mma<TIn>>::type M;
+    typedef typename std::conditional<F32MMA, FragF32, Frag<TIn>>::type F;
     static constexpr int NW = NSW + 1 + (PW ? 1 : 0) + NMW;
     static constexpr int NT = 64 * NW;
     static constexpr int ES = (int)sizeof(TIn);
@@ -101,7 +106,7 @@ struct IsoSm {
     ScanOut sc[K::NCB];
     // scaled causal score tiles (t-tile tau, s-tile sig <= tau) of a chunk as
     // MFMA B fragments, one per lane (P wave only)
-    typename Mma<TIn>::K16 P[K::PW ? 2 : 1][10][K::PW ? 64 : 1];
+    typename K::M::K16 P[K::PW ? 2 : 1][10][K::PW ? 64 : 1];
     float ksq[2][64];  // |k_t|^2 of a chunk, from the staging waves
     float lT;
 };
@@ -426,10 +431,10 @@ __device__ void scan_role(IsoSm<TIn, K>& sm, const FwdArgs& p, int bh, int vt, i
 // k rows sig*16.. at dims kk*32..; Qf the q fragments of the tile's tokens.
 template <typename TIn, class K, bool WIDE, class KF>
 __device__ __forceinline__ void score_tiles(const ScanOut& so, KF kfrag,
-                                            const typename Frag<TIn>::V (&Qf)[K::DK / 32], int tau,
-                                            int c16, int g, typename Mma<TIn>::K16 (&P)[K::C / 16]) {
-    typedef Frag<TIn> F;
-    typedef Mma<TIn> M;
+                                            const typename K::F::V (&Qf)[K::DK / 32], int tau,
+                                            int c16, int g, typename K::M::K16 (&P)[K::C / 16]) {
+    typedef typename K::F F;
+    typedef typename K::M M;
     constexpr int KB = K::DK / 32, NT16 = K::C / 16;
     const int t = tau * 16 + c16;
     f32x4 S[NT16];
@@ -467,7 +472,7 @@ __device__ __forceinline__ void score_tiles(const ScanOut& so, KF kfrag,
 // With PW: step s forms the score tiles of chunk s-1 into P[(s-1) & 1].
 template <typename TIn, class K>
 __device__ void p_role(IsoSm<TIn, K>& sm, const FwdArgs& p, int lane) {
-    typedef Frag<TIn> F;
+    typedef typename K::F F;
     typedef typename F::V FV;
     constexpr int C = K::C, DK = K::DK, KB = DK / 32, NT16 = C / 16;
     const int nchunks = (p.T + C - 1) / C;
@@ -476,7 +481,7 @@ __device__ void p_role(IsoSm<TIn, K>& sm, const FwdArgs& p, int lane) {
         constexpr bool WIDE = decltype(wide_t)::value;
         const ChunkBuf<TIn, K>& B = sm.buf[c % K::NCB];
         const ScanOut& so = sm.sc[c % K::NCB];
-        typename Mma<TIn>::K16(*out)[64] = sm.P[c & 1];
+        typename K::M::K16(*out)[64] = sm.P[c & 1];
         FV Kf[NT16][KB];
 #pragma unroll
         for (int sig = 0; sig < NT16; ++sig)
@@ -487,7 +492,7 @@ __device__ void p_role(IsoSm<TIn, K>& sm, const FwdArgs& p, int lane) {
             FV Qf[KB];
 #pragma unroll
             for (int kk = 0; kk < KB; ++kk) Qf[kk] = F::ld(&B.Q[tau * 16 + c16][kk * 32], g);
-            typename Mma<TIn>::K16 P[NT16];
+            typename K::M::K16 P[NT16];
             score_tiles<TIn, K, WIDE>(so, [&](int sig, int kk) { return Kf[sig][kk]; }, Qf, tau, c16, g, P);
 #pragma unroll
             for (int sig = 0; sig <= tau; ++sig) out[tau * (tau + 1) / 2 + sig][lane] = P[sig];
@@ -507,7 +512,7 @@ __device__ void p_role(IsoSm<TIn, K>& sm, const FwdArgs& p, int lane) {
 // ----------------------------------------------------------------- MMA role
 template <typename TIn, class K>
 __device__ void mma_role(IsoSm<TIn, K>& sm, const FwdArgs& p, int bh, int vt, int mw, int lane) {
-    typedef Mma<TIn> M;
+    typedef typename K::M M;
     constexpr int C = K::C, DK = K::DK, IT = K::IT;
     const int nchunks = (p.T + C - 1) / C;
     const int c16 = lane & 15, g = lane >> 4;
@@ -530,7 +535,7 @@ __device__ void mma_role(IsoSm<TIn, K>& sm, const FwdArgs& p, int bh, int vt, in
 
     auto chunk = [&](int c, auto wide_t) {
         constexpr bool WIDE = decltype(wide_t)::value;
-        typedef Frag<TIn> F;
+        typedef typename K::F F;
         typedef typename F::V FV;
         constexpr int KB = DK / 32, NT16 = C / 16;
         constexpr bool KHOIST = DK <= 64;  // keep every K tile's fragments in registers
@@ -587,18 +592,19 @@ __device__ void mma_role(IsoSm<TIn, K>& sm, const FwdArgs& p, int bh, int vt, in
         for (int it = 0; it < IT; ++it) accM[it] *= fe;
 #pragma unroll
         for (int kb = 0; kb < C / 32; ++kb) {
-            typename M::K32 vf = M::ld32(&B.VT[jrow][kb * 32 + 8 * g]);
             const f32x4 w0 = *(const f32x4*)&so.wsc[kb * 32 + 8 * g];
             const f32x4 w1 = *(const f32x4*)&so.wsc[kb * 32 + 8 * g + 4];
+            typename M::K32 vf;
             if constexpr (sizeof(TIn) == 2) {
+                vf = M::ld32(&B.VT[jrow][kb * 32 + 8 * g]);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     vf[e] = (bf16)((float)vf[e] * w0[e]);
                     vf[e + 4] = (bf16)((float)vf[e + 4] * w1[e]);
                 }
             } else {
-                vf.lo *= w0;
-                vf.hi *= w1;
+                const float* vr = &B.VT[jrow][kb * 32 + 8 * g];
+                vf = M::make32(*(const f32x4*)vr * w0, *(const f32x4*)(vr + 4) * w1);
             }
 #pragma unroll
             for (int it = 0; it < IT; ++it)
