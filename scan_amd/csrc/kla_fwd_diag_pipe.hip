@@ -383,7 +383,6 @@ __device__ void gate_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int 
     auto step = [&](int c, Buf& cur, Buf& nxt) {
         const int cg = c + 1;  // chunk gated in this iteration
         wait_loads<(D - 1) * NLD>();
-        if (nchunks > 0) load(cg + D, nxt);
         if (cg >= 0 && cg < nchunks) {
             const int L = chunk_len(sp.TL, cg, C), par = cg & 1;
             // V^T of the chunk
@@ -517,6 +516,10 @@ __device__ void gate_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int 
                 }
             }
         }
+        // The next chunk's rows are requested after this step's work: at the
+        // step start they would queue with the chain waves' requests, which
+        // are on the critical path (measured 8% faster).
+        if (nchunks > 0) load(cg + D, nxt);
         lds_barrier();
     };
 
