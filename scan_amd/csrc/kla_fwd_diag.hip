@@ -141,7 +141,9 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<TIn, K>& R, const FwdArgs& 
 }
 
 // Pre-scale of the state, its bf16 (or fp32) A-operand, readout, state update.
-template <typename TIn, class K>
+// FULL: the sub-chunk is the whole chunk (ts = 0, L1 = C), so the token-block
+// loop has compile-time bounds and unrolls into one schedulable block.
+template <typename TIn, class K, bool FULL>
 __device__ __forceinline__ void mfma_subchunk(Smem<TIn, K>& sm, f32x4 (&accM)[K::IT][K::JT],
                                               const FwdArgs& p, int bh, int vt, int t0,
                                               int ts, int L1, int wave, int lane) {
@@ -163,7 +165,8 @@ __device__ __forceinline__ void mfma_subchunk(Smem<TIn, K>& sm, f32x4 (&accM)[K:
         for (int jj = 0; jj < K::JT; ++jj) AM[it][jj] = M::from_acc(accM[it][jj]);
 
     // 3-4. per 16-token block: causal S^T tiles, then O^T tiles.
-    const int tb0 = ts / 16, tb1 = (L1 + 15) / 16;
+    const int tb0 = FULL ? 0 : ts / 16, tb1 = FULL ? K::NB : (L1 + 15) / 16;
+#pragma unroll
     for (int tau = tb0; tau < tb1; ++tau) {
         typename M::K16 P[K::NB];
 #pragma unroll
@@ -190,7 +193,7 @@ __device__ __forceinline__ void mfma_subchunk(Smem<TIn, K>& sm, f32x4 (&accM)[K:
             P[sig] = M::from_acc(acc);
         }
         const int t = tau * 16 + c16;
-        const bool store = (t >= ts) && (t < L1);
+        const bool store = FULL || ((t >= ts) && (t < L1));
 #pragma unroll
         for (int jj = 0; jj < K::JT; ++jj) {
             const int jt = wave * K::JT + jj;
@@ -312,20 +315,23 @@ __global__ __launch_bounds__((Cfg<TIn, DK, DV, C>::NT)) void kla_fwd_diag_kernel
             }
         }
         if (tid == 0) sm.L1 = L;
-        // keep the chunk's q, k, a for the gate phase; prefetch the next chunk
-        ChunkRegs<TIn, K> nxt;
-        const int t0n = t0 + C;
-        if (t0n < p.T) load_chunk<TIn, K>(nxt, p, bh, vt, t0n, (p.T - t0n) < C ? (p.T - t0n) : C, tid);
         lds_barrier();
 
         // ---- chain: one lane per key dim, sequential over the chunk
         if (tid < DK) {
             float l = sm.lcar[tid];
-            for (int t = 0; t < L; ++t) {
+            auto link = [&](int t) {
                 const f32x2 ab = sm.u.AB[t][tid];
                 const float lp = l * fast_rcp(__builtin_fmaf(qn_i, l, ab[0]));
                 l = lp + ab[1];
                 sm.u.AB[t][tid] = f32x2{lp, l};
+            };
+            if (L == C) {
+                // full chunk: unrolled, so the LDS reads run ahead of the chain
+#pragma unroll
+                for (int t = 0; t < C; ++t) link(t);
+            } else {
+                for (int t = 0; t < L; ++t) link(t);
             }
             sm.lcar[tid] = l;
         }
@@ -413,7 +419,10 @@ __global__ __launch_bounds__((Cfg<TIn, DK, DV, C>::NT)) void kla_fwd_diag_kernel
             }
             lds_barrier();
 
-            mfma_subchunk<TIn, K>(sm, accM, p, bh, vt, t0, ts, L1, wave, lane);
+            if (ts == 0 && L1 == C)
+                mfma_subchunk<TIn, K, true>(sm, accM, p, bh, vt, t0, ts, L1, wave, lane);
+            else
+                mfma_subchunk<TIn, K, false>(sm, accM, p, bh, vt, t0, ts, L1, wave, lane);
 
             par ^= 1;
             ts = L1;
@@ -422,8 +431,11 @@ __global__ __launch_bounds__((Cfg<TIn, DK, DV, C>::NT)) void kla_fwd_diag_kernel
                 if (tid == 0) sm.L1 = L;
             }
         }
+        // Prefetch the next chunk at the end of this one: issued at the stage
+        // they queued ahead of the chain's critical path (measured 5% slower).
+        const int t0n = t0 + C;
+        if (t0n < p.T) load_chunk<TIn, K>(cur, p, bh, vt, t0n, (p.T - t0n) < C ? (p.T - t0n) : C, tid);
         lds_barrier();  // LDS free for the next chunk's stage
-        cur = nxt;
     }
 
     // ---- epilogue: m <- pending scale (.) m;  etaT = lT (.) m;  lT
