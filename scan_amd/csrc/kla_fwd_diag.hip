@@ -81,11 +81,10 @@ struct Smem {
         } op;
     } u;
     TIn VT[K::DV][K::CS];
-    float gtot[K::NG][K::DK];
+    alignas(8) float gtot[K::NG][K::DK];
     float E[2][K::DK];   // pending end-of-subchunk state scale, by parity
     float sc[K::DK];     // state scale applied before a sub-chunk's readout
     float lcar[K::DK];   // precision carry between chunks
-    float rho[K::C];     // 1 / r_t
     int L1;
 };
 
@@ -96,7 +95,7 @@ struct ChunkRegs {
     typename Pair<TIn>::V k[K::TPG];
     f32x2 a[K::TPG];
     typename Quad<TIn>::V v[K::VPT][2];
-    float r;
+    float r[K::TPG];  // r of the lane's gate-phase tokens
 };
 
 template <typename TIn, class K>
@@ -137,7 +136,11 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<TIn, K>& R, const FwdArgs& 
             }
         }
     }
-    R.r = (tid < L) ? p.r[row0 + tid] : 1.f;
+#pragma unroll
+    for (int u = 0; u < K::TPG; ++u) {
+        const int t = grp * K::TPG + u;
+        R.r[u] = t < L ? p.r[row0 + t] : 1.f;
+    }
 }
 
 // Pre-scale of the state, its bf16 (or fp32) A-operand, readout, state update.
@@ -290,13 +293,15 @@ __global__ __launch_bounds__((Cfg<TIn, DK, DV, C>::NT)) void kla_fwd_diag_kernel
     for (int t0 = 0; t0 < p.T; t0 += C) {
         const int L = (p.T - t0) < C ? (p.T - t0) : C;
 
-        // ---- stage: rho, (a^2, b) for the chain, V^T
-        if (tid < C) sm.rho[tid] = 1.f / cur.r;
-        lds_barrier();  // rho visible
+        // ---- stage: (a^2, b) for the chain, V^T.  Each lane divides 1/r for
+        // its own tokens, which saves a barrier and an LDS round trip.
+        float rho[K::TPG];
+#pragma unroll
+        for (int u = 0; u < K::TPG; ++u) rho[u] = 1.f / cur.r[u];
 #pragma unroll
         for (int u = 0; u < K::TPG; ++u) {
             const int t = grp * K::TPG + u;
-            const float rh = sm.rho[t];
+            const float rh = rho[u];
             const float k0 = PR::lo(cur.k[u]), k1 = PR::hi(cur.k[u]);
             const f32x2 av = cur.a[u];
             f32x4 ab = {av[0] * av[0], k0 * k0 * rh, av[1] * av[1], k1 * k1 * rh};
@@ -346,7 +351,7 @@ __global__ __launch_bounds__((Cfg<TIn, DK, DV, C>::NT)) void kla_fwd_diag_kernel
             const float rl0 = fast_rcp(pl[1]), rl1 = fast_rcp(pl[3]);
             f[u][0] = cur.a[u][0] * pl[0] * rl0;
             f[u][1] = cur.a[u][1] * pl[2] * rl1;
-            const float rh = sm.rho[t];
+            const float rh = rho[u];
             w[u][0] = PR::lo(cur.k[u]) * rh * rl0;
             w[u][1] = PR::hi(cur.k[u]) * rh * rl1;
         }
@@ -364,15 +369,20 @@ __global__ __launch_bounds__((Cfg<TIn, DK, DV, C>::NT)) void kla_fwd_diag_kernel
                 G[u][0] = p0;
                 G[u][1] = p1;
             }
-            lds_barrier();  // previous readers of gtot / sm.L1 are done
-            sm.gtot[grp][2 * ip] = p0;
-            sm.gtot[grp][2 * ip + 1] = p1;
+            // previous readers of gtot / sm.L1: the last sub-chunk (the first
+            // sub-chunk's were in the previous chunk, several barriers ago)
+            if (ts > 0) lds_barrier();
+            *(f32x2*)&sm.gtot[grp][2 * ip] = f32x2{p0, p1};
             lds_barrier();
-            // (c) cumulative gates, range check
+            // (c) cumulative gates, range check; all group totals are read at once
             float pre0 = 1.f, pre1 = 1.f;
-            for (int gg = 0; gg < grp; ++gg) {
-                pre0 *= sm.gtot[gg][2 * ip];
-                pre1 *= sm.gtot[gg][2 * ip + 1];
+#pragma unroll
+            for (int gg = 0; gg < K::NG - 1; ++gg) {
+                const f32x2 gv = *(const f32x2*)&sm.gtot[gg][2 * ip];
+                if (gg < grp) {
+                    pre0 *= gv[0];
+                    pre1 *= gv[1];
+                }
             }
             int firstbad = L;
 #pragma unroll
@@ -431,8 +441,10 @@ __global__ __launch_bounds__((Cfg<TIn, DK, DV, C>::NT)) void kla_fwd_diag_kernel
                 if (tid == 0) sm.L1 = L;
             }
         }
-        // Prefetch the next chunk at the end of this one: issued at the stage
-        // they queued ahead of the chain's critical path (measured 5% slower).
+        // Prefetch the next chunk at the end of this one.  Requested at the
+        // stage, the loads queued ahead of the chain's critical path; requested
+        // by the waves that idle through the chain, they slowed the workgroups
+        // sharing the CU (both measured).
         const int t0n = t0 + C;
         if (t0n < p.T) load_chunk<TIn, K>(cur, p, bh, vt, t0n, (p.T - t0n) < C ? (p.T - t0n) : C, tid);
         lds_barrier();  // LDS free for the next chunk's stage
