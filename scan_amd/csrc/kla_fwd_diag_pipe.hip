@@ -347,6 +347,12 @@ __device__ void gate_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int 
     constexpr int NB = K::NBG, D = NB - 1;
     Buf b[NB];
     constexpr int NLD = 2 * TPG + 2 * K::VPT;  // loads per chunk
+    // The next chunk's rows are requested after the step's work (LATE): at
+    // the step start they queue with the chain waves' requests, which are on
+    // the critical path (measured 8% faster).  With the sequence split they
+    // are requested at the step start: the later request lost the L2 reuse of
+    // the rows the chain waves had just read (HBM reads 1.6x, measured slower).
+    constexpr bool LATE = !SEG;
     // Each chunk is read through buffer resources spanning its rows, so rows
     // past T read as zero; a lane's token rows are immediates from its offset.
     constexpr int ES = (int)sizeof(TIn), QRB = DK * ES;
@@ -383,6 +389,7 @@ __device__ void gate_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int 
     auto step = [&](int c, Buf& cur, Buf& nxt) {
         const int cg = c + 1;  // chunk gated in this iteration
         wait_loads<(D - 1) * NLD>();
+        if (!LATE && nchunks > 0) load(cg + D, nxt);
         if (cg >= 0 && cg < nchunks) {
             const int L = chunk_len(sp.TL, cg, C), par = cg & 1;
             // V^T of the chunk
@@ -516,10 +523,7 @@ __device__ void gate_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int 
                 }
             }
         }
-        // The next chunk's rows are requested after this step's work: at the
-        // step start they would queue with the chain waves' requests, which
-        // are on the critical path (measured 8% faster).
-        if (nchunks > 0) load(cg + D, nxt);
+        if (LATE && nchunks > 0) load(cg + D, nxt);
         lds_barrier();
     };
 
