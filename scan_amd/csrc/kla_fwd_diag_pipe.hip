@@ -18,10 +18,12 @@
 //                (a*lp, l) to LDS and flag the chunk if some cumulative gate
 //                product inside it drops below 2^-64;
 //   gate waves   turn chunk c+1's precisions into gates f, w and cumulative
-//                products G (lanes own 2 key dims x 8 tokens; the products
-//                cross token groups with DPP row shifts), and write the bf16
-//                MFMA operands q^ = q G, w^ = w / G (or, for a flagged chunk,
-//                the raw fp32 gates);
+//                products G (lanes own 2 key dims x 8 tokens at dk 128, x 4
+//                at dk 64; the products cross token groups with DPP row
+//                shifts), and write the MFMA operands q^ = q G, w^ = w / G
+//                (or, for a flagged chunk, the raw fp32 gates).  They request
+//                the next chunk's rows after their work, the chain waves at
+//                the start of theirs;
 //   MMA waves    own the fp32 state m (accumulator registers) and run chunk
 //                c: causal S^T = W^ Q^^T tiles, O^T = m^T Q^^T + V^T P^T,
 //                m += W^^T V.  All products use 16x16x32 MFMAs: the K index of
