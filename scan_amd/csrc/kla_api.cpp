@@ -10,6 +10,7 @@
 #include <stdlib.h>
 
 #include "kla_internal.h"
+#include "kla_short.h"
 
 namespace {
 
@@ -58,6 +59,13 @@ int env_vtiles() {
     return atoi(s);
 }
 
+// KLA_FWD_SHORT=0 keeps short sequences (T <= kShortTMax) on the chunked
+// kernels instead of the short-sequence kernel.
+bool use_short() {
+    const char* s = getenv("KLA_FWD_SHORT");
+    return !(s && s[0] == '0');
+}
+
 // KLA_FWD_NSEG=n forces n sequence segments on the wave-specialised diagonal
 // kernel (1 = no split); by default long sequences with few (b,h) are split.
 int env_nseg() {
@@ -68,13 +76,17 @@ int env_nseg() {
 
 // Kernel that klaFwd launches for these (supported) dims; n_vtiles receives
 // the number of value-column tiles each (b,h) is split into.
-enum FwdKernel { FK_EMPTY, FK_ISO, FK_ISO_PIPE, FK_DIAG_PIPE, FK_DIAG_CHUNK };
+enum FwdKernel { FK_EMPTY, FK_SHORT, FK_ISO, FK_ISO_PIPE, FK_DIAG_PIPE, FK_DIAG_CHUNK };
 
 FwdKernel pick_kernel(const klaDims* d, int* n_vtiles) {
     const int nvt_env = env_vtiles();
     if (d->T == 0) {
         *n_vtiles = 1;
         return FK_EMPTY;
+    }
+    if (use_short() && kla::fwd_short_supported(d->dk, d->dv, d->T)) {
+        *n_vtiles = 1;
+        return FK_SHORT;
     }
     if (d->cov == KLA_ISO) {
         const int nvt_pipe = nvt_env > 0 ? nvt_env : kla::fwd_iso_pipe_vtiles(d->B, d->H, d->dk, d->dv);
@@ -125,6 +137,7 @@ const char* klaFwdKernelName(const klaDims* d) {
     int nvt = 1;
     switch (pick_kernel(d, &nvt)) {
         case FK_EMPTY: return "kla_fwd_empty_kernel";
+        case FK_SHORT: return "kla_fwd_short_kernel";
         case FK_ISO: return nvt > 1 ? "kla_fwd_iso_kernel (value tiles)" : "kla_fwd_iso_kernel";
         case FK_ISO_PIPE:
             return nvt > 1 ? "kla_fwd_iso_pipe_kernel (value tiles)" : "kla_fwd_iso_pipe_kernel";
@@ -198,6 +211,7 @@ klaStatus klaFwd(const klaDims* d, const void* q, const void* k, const void* v, 
     hipError_t e;
     switch (pick_kernel(d, &fa.n_vtiles)) {
         case FK_EMPTY: e = kla::launch_fwd_empty(fa, iso ? 1 : 0, st); break;
+        case FK_SHORT: e = kla::launch_fwd_short(fa, d->dtype, iso ? 1 : 0, st); break;
         case FK_ISO:
             if (fa.dv % fa.n_vtiles) return KLA_ERR_UNSUPPORTED;
             e = kla::launch_fwd_iso(fa, d->dtype, st);

@@ -169,10 +169,22 @@ def test_kernel_name_reports_the_dispatch():
     assert scan_amd.klaFwdKernelName(KlaDims(2, 3, 100, 32, 32, F32, ISO)).startswith(
         "kla_fwd_iso_kernel")
     assert scan_amd.klaFwdKernelName(KlaDims(2, 3, 0, 64, 64, BF16, DIAG)) == "kla_fwd_empty_kernel"
+    # short sequences (prefill into cached states, multi-token decode)
+    for T, cov in ((1, DIAG), (32, DIAG), (7, ISO), (32, ISO)):
+        assert scan_amd.klaFwdKernelName(KlaDims(256, 32, T, 64, 64, BF16, cov)) == "kla_fwd_short_kernel"
+    assert scan_amd.klaFwdKernelName(KlaDims(256, 32, 33, 64, 64, BF16, DIAG)) != "kla_fwd_short_kernel"
     assert scan_amd.klaFwdKernelName(KlaDims(1, 1, 8, 48, 48, BF16, DIAG)) == ""
     assert scan_amd.klaFwdKernelName(KlaDims(-1, 1, 8, 64, 64, BF16, DIAG)) == ""
     lib = scan_amd.load()
     assert lib.klaFwdKernelName(None) == b""
+
+
+def test_short_path_switch(monkeypatch):
+    short = KlaDims(256, 32, 8, 64, 64, BF16, ISO)
+    assert scan_amd.klaFwdKernelName(short) == "kla_fwd_short_kernel"
+    assert scan_amd.klaFwdWorkspaceBytes(short) == 0
+    monkeypatch.setenv("KLA_FWD_SHORT", "0")
+    assert scan_amd.klaFwdKernelName(short) == "kla_fwd_iso_pipe_kernel"
 
 
 def test_split_workspace_contract(monkeypatch):

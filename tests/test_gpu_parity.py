@@ -132,6 +132,54 @@ def test_split_handoff_on_device(cov):
 
 
 @pytest.mark.parametrize("cov", ["diag", "iso"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
+@pytest.mark.parametrize("T", [2, 4, 5, 31, 32])
+def test_parity_short_sequences(cov, dtype, d, T):
+    """T <= 32 runs on the short-sequence kernel (state in registers, tokens
+    in blocks of four): block boundaries, a ragged last block, cached states."""
+    _print_case("short", cov, dtype, d, T)
+    base = "small_diag" if cov == "diag" else "iso"
+    inp = gen.make_inputs(base, seed=40 + T + d, B=3, H=2, T=T, dk=d, dv=d, dtype=dtype)
+    assert scan_amd.fwd_kernel_name(3, 2, T, d, d, cov=cov, dtype=dtype) == "kla_fwd_short_kernel"
+    st = gen.make_state(inp["workload"], seed=11)
+    hip = run_hip(inp, cov, st["l0"], st["eta0"])
+    ref = run_oracle(inp, cov, st["l0"], st["eta0"])
+    assert_parity(compare(hip, ref), dtype, f"short {cov} {dtype} d={d} T={T}")
+
+
+@pytest.mark.parametrize("cov", ["diag", "iso"])
+@pytest.mark.parametrize("d", [16, 32])
+def test_parity_short_packed_heads(cov, d):
+    """Small heads share a workgroup (16 of d 16, 4 of d 32): 35 (b,h) leave
+    the last workgroup partly filled, and its spare groups store nothing."""
+    _print_case("short packed", cov, d)
+    base = "small_diag" if cov == "diag" else "iso"
+    inp = gen.make_inputs(base, seed=70 + d, B=5, H=7, T=9, dk=d, dv=d, dtype="bf16")
+    assert scan_amd.fwd_kernel_name(5, 7, 9, d, d, cov=cov, dtype="bf16") == "kla_fwd_short_kernel"
+    st = gen.make_state(inp["workload"], seed=13)
+    hip = run_hip(inp, cov, st["l0"], st["eta0"])
+    ref = run_oracle(inp, cov, st["l0"], st["eta0"])
+    assert_parity(compare(hip, ref), "bf16", f"short packed {cov} d={d}")
+
+
+@pytest.mark.parametrize("cov", ["diag", "iso"])
+def test_short_path_matches_chunked_kernels(cov, monkeypatch):
+    """The short-sequence kernel and the chunked kernels (KLA_FWD_SHORT=0)
+    give the same results within the fp32 tolerance."""
+    _print_case("short vs chunked", cov)
+    base = "small_diag" if cov == "diag" else "iso"
+    inp = gen.make_inputs(base, seed=21, B=4, H=3, T=27, dk=64, dv=64, dtype="f32")
+    st = gen.make_state(inp["workload"], seed=12)
+    a = run_hip(inp, cov, st["l0"], st["eta0"])
+    monkeypatch.setenv("KLA_FWD_SHORT", "0")
+    assert scan_amd.fwd_kernel_name(4, 3, 27, 64, 64, cov=cov, dtype="f32") != "kla_fwd_short_kernel"
+    b = run_hip(inp, cov, st["l0"], st["eta0"])
+    for key in ("o", "lT", "etaT"):
+        assert float(np.abs(a[key] - b[key]).max() / np.abs(b[key]).max()) < 1e-4, key
+
+
+@pytest.mark.parametrize("cov", ["diag", "iso"])
 def test_steps_match_forward(cov):
     _print_case("steps", cov)
     name = "lm_diag" if cov == "diag" else "iso"
