@@ -35,6 +35,8 @@ KERNEL_SOURCES = {
              "scan_amd/csrc/kla_internal.h"],
     "iso": ["scan_amd/csrc/kla_fwd_iso_pipe.hip", "scan_amd/csrc/kla_fwd_iso.hip",
             "scan_amd/csrc/kla_common.h", "scan_amd/csrc/kla_internal.h"],
+    "short": ["scan_amd/csrc/kla_fwd_short.hip", "scan_amd/csrc/kla_short.h",
+              "scan_amd/csrc/kla_common.h", "scan_amd/csrc/kla_internal.h"],
 }
 
 
@@ -161,6 +163,107 @@ def run_decode(args, torch, np, scan_amd, gen) -> dict:
     }
 
 
+def calibration_copy(args, torch) -> None:
+    """With --calib-copy-mb, one device copy of known size after the timed
+    steps: the reference that scales the HBM traffic counters."""
+    if args.calib_copy_mb > 0:
+        nb = args.calib_copy_mb << 20
+        src = torch.ones(nb, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"bench: calibration copy of {nb} bytes done", file=sys.stderr, flush=True)
+        del src, dst
+
+
+def prefill_alg_bytes(w) -> float:
+    """Algorithmic HBM bytes of one forward over a chunk that continues cached
+    states: the token inputs and outputs of alg_bytes, plus the fp32 state
+    (l, eta) read once and written once."""
+    nl = 1 if w.cov == "iso" else w.dk
+    per_seq_in = 4 * nl + 4 * w.dk * w.dv
+    return alg_bytes(w) + float(w.B * w.H * per_seq_in)
+
+
+def run_prefill(args, torch, np, scan_amd, gen) -> dict:
+    """One step = one klaFwd over a T-token chunk for every (b,h) of the
+    decode batch, from cached states (a DECODE.T-token prefix forward, seed 1)
+    into a second state buffer; chunk tokens seed 2, two resident copies
+    alternated."""
+    w = gen.PREFILL
+    names = ("q", "k", "v", "a", "qn", "r")
+    pre = gen.make_inputs(gen.DECODE, seed=1, device="cuda")
+    _, l0, eta0 = scan_amd.fwd(*(pre[n] for n in names), cov=w.cov)
+    del pre
+    host = gen.make_inputs(w, seed=2)
+    sets = [[host[n].to("cuda") for n in names]]
+    sets.append([t.clone() for t in sets[0]])
+    o = torch.empty(w.B, w.H, w.T, w.dv, dtype=sets[0][2].dtype, device="cuda")
+    lT = torch.empty_like(l0)
+    etaT = torch.empty_like(eta0)
+    kname = scan_amd.fwd_kernel_name(w.B, w.H, w.T, w.dk, w.dv, cov=w.cov, dtype=w.dtype)
+
+    def step(i):
+        scan_amd.fwd(*sets[i % 2], l0, eta0, cov=w.cov, o=o, lT=lT, etaT=etaT)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    nbytes = prefill_alg_bytes(w)
+    achieved = nbytes / (ms_per_step / 1e3) / 1e9
+    traffic = stored_traffic(w.name, "short")
+    calibration_copy(args, torch)
+    print(f"bench: prefill {ms_per_step:.4f} ms/step ({kname}), {achieved:.1f} GB/s",
+          file=sys.stderr, flush=True)
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        threads = oracle.default_threads()
+        hx = [host[n].double().numpy() for n in names]
+        lh, eh = l0.double().cpu().numpy(), eta0.double().cpu().numpy()
+        reps, t_cpu = 0, 0.0
+        while reps == 0 or (t_cpu < 0.5 * args.cpu_seconds and reps < 1000):
+            t0 = time.perf_counter()
+            oracle.fwd(*hx, lh, eh, cov=oracle.ISO if w.cov == "iso" else oracle.DIAG,
+                       nthreads=threads)
+            t_cpu += time.perf_counter() - t0
+            reps += 1
+        cpu = {"value": w.B * w.T * reps / t_cpu, "unit": "tokens/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"{reps} full chunk forward(s) (B={w.B}, H={w.H}, T={w.T}) from the "
+                         f"cached states, fp64, {t_cpu:.1f}s"}
+    return {
+        "metric": "KLA chunk tokens/s from cached states (klaFwd, T-token prefill / multi-token decode)",
+        "value": w.B * w.T / (ms_per_step / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv,
+                   "cov": w.cov, "global_batch": w.B, "seq_len": w.T, "parallelism": "none"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic["bytes_per_launch"] if traffic else None,
+                     "kernel": kname, "alg_bytes": nbytes, "kernel_ms": ms_per_step},
+        "cpu_baseline": cpu,
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -189,6 +292,9 @@ def main() -> int:
 
     if args.workload == gen.DECODE.name:
         print(json.dumps(run_decode(args, torch, np, scan_amd, gen)), flush=True)
+        return 0
+    if args.workload == gen.PREFILL.name:
+        print(json.dumps(run_prefill(args, torch, np, scan_amd, gen)), flush=True)
         return 0
     w = gen.WORKLOADS[args.workload]
     print(f"bench: workload {w}", file=sys.stderr, flush=True)
@@ -241,15 +347,7 @@ def main() -> int:
     print(f"bench: {ms_per_step:.4f} ms/step (kernel {kern_ms:.4f} ms), {achieved:.1f} GB/s "
           f"algorithmic, wall {wall:.3f}s", file=sys.stderr, flush=True)
 
-    if args.calib_copy_mb > 0:
-        nb = args.calib_copy_mb << 20
-        src = torch.ones(nb, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        print(f"bench: calibration copy of {nb} bytes done", file=sys.stderr, flush=True)
-        del src, dst
+    calibration_copy(args, torch)
 
     cpu = None
     if not args.no_cpu:

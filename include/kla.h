@@ -106,6 +106,10 @@ size_t klaFwdWorkspaceBytes(const klaDims* d);
  * Aliasing: o must not overlap any input; lT/etaT must not overlap l0/eta0
  * (KLA_ERR_ALIAS).  workspace must hold klaFwdWorkspaceBytes(d) bytes and
  * must not be used by another call that runs at the same time.
+ * Serving: a prefill chunk or several decode tokens continue a cached state
+ * by passing it as l0/eta0 and a second state buffer as lT/etaT (constant-
+ * memory decoding, [KDN]); up to 32 tokens run on a kernel that holds the
+ * state on chip for the whole call.
  */
 klaStatus klaFwd(const klaDims* d,
                  const void* q, const void* k, const void* v,

@@ -62,6 +62,10 @@ WORKLOADS = {
 
 DECODE = Workload("iso_decode", 256, 32, 128, 64, 64, "iso", "bf16")
 DECODE_STEPS = 64
+# serving: a 16-token chunk (prefill piece or multi-token decode) continuing
+# the cached states of the decode batch (T is the chunk length; the states
+# come from a DECODE.T-token prefix forward)
+PREFILL = Workload("iso_prefill16", 256, 32, 16, 64, 64, "iso", "bf16")
 
 _TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
 

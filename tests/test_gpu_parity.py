@@ -230,6 +230,31 @@ def test_decode_full_batch_sampled():
         assert lerr < 1e-4, (b, h, lerr)
 
 
+def test_prefill_full_batch_sampled():
+    """Serving chunk at B=256, H=32 (the bench's iso_prefill16 launch): a
+    128-token prefix via klaFwd, then one 16-token klaFwd from the cached
+    states (the short-sequence kernel) into a second state buffer."""
+    _print_case("prefill")
+    w = gen.PREFILL
+    pre = gen.make_inputs(gen.DECODE, seed=1)
+    chk = gen.make_inputs(w, seed=2)
+    dp = {k: to_dev(v) for k, v in pre.items() if isinstance(v, torch.Tensor)}
+    _, l0, eta0 = scan_amd.fwd(dp["q"], dp["k"], dp["v"], dp["a"], dp["qn"], dp["r"], cov="iso")
+    assert scan_amd.fwd_kernel_name(w.B, w.H, w.T, w.dk, w.dv, cov="iso",
+                                    dtype=w.dtype) == "kla_fwd_short_kernel"
+    hip = run_hip(chk, "iso", l0, eta0)
+    sel = [(0, 0), (100, 5), (255, 31)]
+    ref_pre = run_oracle(pre, "iso", sel=sel)
+    for n, (b, h) in enumerate(sel):
+        one = {k: (v[b:b + 1, h:h + 1] if isinstance(v, torch.Tensor) else v)
+               for k, v in chk.items()}
+        r = oracle.fwd(one["q"], one["k"], one["v"], one["a"], one["qn"], one["r"],
+                       ref_pre["lT"][n][None, None], ref_pre["etaT"][n][None, None],
+                       cov=oracle.ISO)
+        errs = compare({k: hip[k][b:b + 1, h:h + 1] for k in hip}, r)
+        assert_parity(errs, w.dtype, f"prefill ({b},{h})")
+
+
 def test_bitwise_deterministic():
     _print_case("determinism")
     inp = gen.make_inputs("lm_diag", seed=3, B=2, H=4, T=500)
