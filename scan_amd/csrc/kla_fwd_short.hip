@@ -13,9 +13,9 @@
 // one; g and l are then scalars per head).
 //
 // With few tokens per (b,h) the forward is bound by the state: reading eta0
-// and writing etaT (2 d_k d_v fp32 per (b,h)) outweighs the tokens.  One
-// workgroup per (b,h) keeps its slice of eta in registers for the whole
-// sequence (row group rg, value quad jq: rows rg*RPT .. rg*RPT+RPT-1 of
+// and writing etaT (2 d_k d_v fp32 per (b,h)) outweighs the tokens.  The
+// threads of a (b,h) keep its eta in registers for the whole sequence, each
+// a slice (row group rg, value quad jq: rows rg*RPT .. rg*RPT+RPT-1 of
 // columns 4jq..4jq+3), so the state crosses HBM once in each direction, in
 // 16-byte accesses, and a thread reads its rows' coefficients as vectors.
 // Tokens go in blocks of four.  The coefficients of a block (gates, k/r,
@@ -40,11 +40,15 @@ constexpr int kShortThreads = 256;
 constexpr int kShortTB = KLA_SHORT_TB;  // tokens per block
 
 // Threads per (b,h): each thread holds at least four state rows of one value
-// quad, so small heads share a workgroup (16 heads of d 16, 4 of d 32) and
-// every workgroup carries about the same work.
+// quad, so small heads share a workgroup (16 heads of d 16, 8 of d 32, 2 of
+// d 64) and every workgroup carries about the same work.
 template <int D>
 struct ShortLayout {
-    static constexpr int NTH = D * D / 16 < kShortThreads ? D * D / 16 : kShortThreads;
+    // state elements per thread, at least: 32 (16 at d16, where the v rows of
+    // a block need 16 threads per head); more threads per head mean more LDS
+    // traffic per element (coefficients, partials, row-group sums)
+    static constexpr int EPT = D == 16 ? 16 : 32;
+    static constexpr int NTH = D * D / EPT < kShortThreads ? D * D / EPT : kShortThreads;
     static constexpr int NH = kShortThreads / NTH;  // (b,h) per workgroup
     static constexpr int VQ = D / 4;                 // value quads per row
     static constexpr int RG = NTH / VQ;              // row groups of a (b,h)
@@ -70,11 +74,8 @@ struct ShortSm {
     float red[kShortTB][kShortThreads / 64];  // iso, (b,h) over 4 waves: |k|^2 per wave
 };
 
-// The diagonal kernel at d 32 fits 6 waves per SIMD in registers without
-// spills when asked to (the LDS allows 6 workgroups of 4 waves per CU).
 template <typename TIn, int D, bool ISO>
-__global__ __launch_bounds__(kShortThreads) __attribute__((amdgpu_waves_per_eu(!ISO && D == 32 ? 6 : 1)))
-void kla_fwd_short_kernel(FwdArgs p) {
+__global__ __launch_bounds__(kShortThreads) void kla_fwd_short_kernel(FwdArgs p) {
     typedef ShortLayout<D> Ly;
     constexpr int NT = kShortThreads, TB = kShortTB, NTH = Ly::NTH, NH = Ly::NH;
     constexpr int VQ = Ly::VQ, RG = Ly::RG, RPT = Ly::RPT;
@@ -179,7 +180,7 @@ void kla_fwd_short_kernel(FwdArgs p) {
                 float ksq = 0.f;
                 if constexpr (RED) {
 #pragma unroll
-                    for (int w = 0; w < NT / 64; ++w) ksq += sm.red[u][w];
+                    for (int w = 0; w < NTH / 64; ++w) ksq += sm.red[u][grp * (NTH / 64) + w];
                 } else {
                     ksq = ksq_sum(x, u);
                 }
