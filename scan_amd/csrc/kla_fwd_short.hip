@@ -19,7 +19,8 @@
 // columns 4jq..4jq+3), so the state crosses HBM once in each direction, in
 // 16-byte accesses, and a thread reads its rows' coefficients as vectors.
 // Tokens go in blocks of four.  The coefficients of a block (gates, k/r,
-// q/l') are formed by one lane per key dim and staged in LDS; every thread
+// q/l') are formed by one lane per key dim, with the hardware reciprocal
+// (about 1 ulp), and staged in LDS; every thread
 // applies the block's tokens to its rows and leaves a partial readout per
 // token, and the partials are summed over row groups.  The next block's
 // inputs are loaded while a block is applied, and its coefficients are staged
@@ -164,12 +165,12 @@ __global__ __launch_bounds__(kShortThreads) void kla_fwd_short_kernel(FwdArgs p)
                 for (int u = 0; u < TB; ++u) {
                     if (u < nb) {
                         const float a = x.a[u], kv = (float)x.k[u];
-                        const float rho = 1.f / x.r[u];
-                        const float lp = l / __builtin_fmaf(qn_i, l, a * a);
-                        const float ln = lp + kv * kv * rho;
-                        sm.g[grp][u][lt] = lp * a / l;
+                        const float rho = fast_rcp(x.r[u]);
+                        const float rd = fast_rcp(__builtin_fmaf(qn_i, l, a * a));
+                        const float ln = __builtin_fmaf(kv * kv, rho, l * rd);
+                        sm.g[grp][u][lt] = a * rd;  // lp a / l with lp = l rd
                         sm.kap[grp][u][lt] = kv * rho;
-                        sm.qs[grp][u][lt] = (float)x.q[u] / ln;
+                        sm.qs[grp][u][lt] = (float)x.q[u] * fast_rcp(ln);
                         l = ln;
                     }
                 }
@@ -185,13 +186,13 @@ __global__ __launch_bounds__(kShortThreads) void kla_fwd_short_kernel(FwdArgs p)
                     ksq = ksq_sum(x, u);
                 }
                 if (u < nb) {
-                    const float a = x.a[u], rho = 1.f / x.r[u];
-                    const float lp = l / __builtin_fmaf(x.qn[u], l, a * a);
-                    const float ln = lp + ksq * rho * (1.f / (float)D);
-                    if (lt == 0) sm.g[grp][u][0] = lp * a / l;
+                    const float a = x.a[u], rho = fast_rcp(x.r[u]);
+                    const float rd = fast_rcp(__builtin_fmaf(x.qn[u], l, a * a));
+                    const float ln = __builtin_fmaf(ksq * (1.f / (float)D), rho, l * rd);
+                    if (lt == 0) sm.g[grp][u][0] = a * rd;  // lp a / l with lp = l rd
                     if (kd) {
                         sm.kap[grp][u][lt] = (float)x.k[u] * rho;
-                        sm.qs[grp][u][lt] = (float)x.q[u] / ln;
+                        sm.qs[grp][u][lt] = (float)x.q[u] * fast_rcp(ln);
                     }
                     l = ln;
                 }
