@@ -62,6 +62,8 @@ def _bind(lib):
     lib.kla_oracle_fwd.argtypes = [i, i, i, i, i, i] + [dp] * 12 + [i]
     lib.kla_oracle_step.restype = ctypes.c_int
     lib.kla_oracle_step.argtypes = [i, i, i, i, i] + [dp] * 9 + [i]
+    lib.kla_oracle_fwd_residual.restype = ctypes.c_int
+    lib.kla_oracle_fwd_residual.argtypes = [i, i, i, i, i, i] + [dp] * 11 + [i]
     return lib
 
 
@@ -134,3 +136,27 @@ def step(q, k, v, a, qn, r, l, eta, cov: int = DIAG, nthreads: int | None = None
     if rc != 0:
         raise RuntimeError(f"kla_oracle_step failed with code {rc}")
     return {"o": o, "l": l, "eta": eta}
+
+
+def fwd_residual(q, k, v, a, qn, r, l0=None, m0=None, cov: int = DIAG,
+                 nthreads: int | None = None, lib_path: str | None = None):
+    """Residual-write forward (Kalman-gain-weighted residual write), fp64.
+
+    Same shapes as ``fwd``; the state is the posterior mean m (m0, mT
+    [B,H,dk,dv]) with the precision l.  Returns dict(o, lT, mT).
+    """
+    lib = _load(lib_path)
+    q, k, v, a, qn, r = (_f64(x) for x in (q, k, v, a, qn, r))
+    l0, m0 = _f64(l0), _f64(m0)
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    nl = dk if cov == DIAG else 1
+    o = np.empty((B, H, T, dv))
+    lT = np.empty((B, H, nl) if cov == DIAG else (B, H))
+    mT = np.empty((B, H, dk, dv))
+    rc = lib.kla_oracle_fwd_residual(B, H, T, dk, dv, cov, _ptr(q), _ptr(k), _ptr(v), _ptr(a),
+                                     _ptr(qn), _ptr(r), _ptr(l0), _ptr(m0), _ptr(o), _ptr(lT),
+                                     _ptr(mT), nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"kla_oracle_fwd_residual failed with code {rc}")
+    return {"o": o, "lT": lT, "mT": mT}

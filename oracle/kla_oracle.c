@@ -173,3 +173,136 @@ int kla_oracle_step(int B, int H, int dk, int dv, int cov,
     return kla_oracle_fwd(B, H, 1, dk, dv, cov, q, k, v, a, qn, r, l, eta,
                           o, l, eta, NULL, nthreads);
 }
+
+/*
+ * Residual-write forward (the Kalman-gain-weighted residual write of [KDN]).
+ *
+ * The memory x_t (dk x dv) is observed through the full key contraction,
+ *     v_t[j] = sum_i k_t[i] x_t[i,j] + N(0, r_t),
+ * with the same OU transition per row as above.  Each one-step posterior is
+ * projected onto the diagonal (or isotropic) Gaussian family by mean-field
+ * variational inference, which keeps the exact posterior mean and takes the
+ * diagonal of the posterior precision (its trace average for the isotropic
+ * family).  The state is (l, m) with m the posterior mean (mean form, not
+ * information form):
+ *
+ *   predict:  lp   = l / (a^2 + qn*l),   m_pred = a (.) m   (row i scaled by a_i)
+ *   gain:     g_i  = (k_i / lp_i) / (sum_j k_j^2 / lp_j + r)
+ *   residual: u    = v - m_pred^T k
+ *   update:   m_t  = m_pred + g u^T,      l_t = lp + k^2 / r
+ *   readout:  o_t  = m_t^T q_t
+ *
+ * Isotropic mode: one lp per head, g = k / (|k|^2 + r lp), and
+ * l_t = lp + |k|^2 / (d_k r).  Same layouts and conventions as
+ * kla_oracle_fwd, with m0/mT (the mean) in place of eta0/etaT.
+ */
+static void run_sequence_residual(int T, int dk, int dv, int cov,
+                                  const double* q, const double* k, const double* v,
+                                  const double* a, const double* qn, const double* r,
+                                  double* l, double* m, double* o, double* lp, double* g,
+                                  double* u)
+{
+    for (int t = 0; t < T; ++t) {
+        const double* qt = q + (size_t)t * dk;
+        const double* kt = k + (size_t)t * dk;
+        const double* vt = v + (size_t)t * dv;
+        const double rt = r[t];
+        /* predict: precision and mean */
+        if (cov == KLA_ORACLE_DIAG) {
+            const double* at = a + (size_t)t * dk;
+            for (int i = 0; i < dk; ++i) {
+                lp[i] = l[i] / (at[i] * at[i] + qn[i] * l[i]);
+                for (int j = 0; j < dv; ++j) m[(size_t)i * dv + j] *= at[i];
+            }
+        } else {
+            lp[0] = l[0] / (a[t] * a[t] + qn[t] * l[0]);
+            for (size_t e = 0; e < (size_t)dk * dv; ++e) m[e] *= a[t];
+        }
+        /* gain */
+        double s = 0.0;
+        for (int i = 0; i < dk; ++i) {
+            const double lpi = (cov == KLA_ORACLE_DIAG) ? lp[i] : lp[0];
+            s += kt[i] * kt[i] / lpi;
+        }
+        for (int i = 0; i < dk; ++i) {
+            const double lpi = (cov == KLA_ORACLE_DIAG) ? lp[i] : lp[0];
+            g[i] = (kt[i] / lpi) / (s + rt);
+        }
+        /* residual against the predicted mean, then the write */
+        for (int j = 0; j < dv; ++j) {
+            double pred = 0.0;
+            for (int i = 0; i < dk; ++i) pred += m[(size_t)i * dv + j] * kt[i];
+            u[j] = vt[j] - pred;
+        }
+        for (int i = 0; i < dk; ++i)
+            for (int j = 0; j < dv; ++j) m[(size_t)i * dv + j] += g[i] * u[j];
+        /* precision update */
+        if (cov == KLA_ORACLE_DIAG) {
+            for (int i = 0; i < dk; ++i) l[i] = lp[i] + kt[i] * kt[i] / rt;
+        } else {
+            double ksq = 0.0;
+            for (int i = 0; i < dk; ++i) ksq += kt[i] * kt[i];
+            l[0] = lp[0] + ksq / ((double)dk * rt);
+        }
+        /* readout of the posterior mean */
+        double* ot = o + (size_t)t * dv;
+        for (int j = 0; j < dv; ++j) {
+            double acc = 0.0;
+            for (int i = 0; i < dk; ++i) acc += qt[i] * m[(size_t)i * dv + j];
+            ot[j] = acc;
+        }
+    }
+}
+
+/* Returns 0 on success, nonzero on bad arguments or allocation failure. */
+int kla_oracle_fwd_residual(int B, int H, int T, int dk, int dv, int cov,
+                            const double* q, const double* k, const double* v,
+                            const double* a, const double* qn, const double* r,
+                            const double* l0, const double* m0,
+                            double* o, double* lT, double* mT, int nthreads)
+{
+    if (B < 1 || H < 1 || T < 0 || dk < 1 || dv < 1) return 1;
+    if (cov != KLA_ORACLE_DIAG && cov != KLA_ORACLE_ISO) return 1;
+    if (!q || !k || !v || !a || !qn || !r || !o) return 1;
+    const int nl = (cov == KLA_ORACLE_DIAG) ? dk : 1;
+    const long long nseq = (long long)B * H;
+    int failed = 0;
+    if (nthreads < 1) nthreads = 1;
+
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads) reduction(| : failed)
+    for (long long s = 0; s < nseq; ++s) {
+        const int h = (int)(s % H);
+        double* l = (double*)malloc(sizeof(double) * (size_t)nl);
+        double* lp = (double*)malloc(sizeof(double) * (size_t)nl);
+        double* g = (double*)malloc(sizeof(double) * (size_t)dk);
+        double* u = (double*)malloc(sizeof(double) * (size_t)dv);
+        double* m = (double*)malloc(sizeof(double) * (size_t)dk * dv);
+        if (!l || !lp || !g || !u || !m) {
+            free(l); free(lp); free(g); free(u); free(m);
+            failed |= 1;
+            continue;
+        }
+        for (int i = 0; i < nl; ++i) l[i] = l0 ? l0[s * nl + i] : 1.0;
+        for (size_t e = 0; e < (size_t)dk * dv; ++e)
+            m[e] = m0 ? m0[(size_t)s * dk * dv + e] : 0.0;
+
+        const size_t tk = (size_t)s * T * dk, tv = (size_t)s * T * dv;
+        const double* as;
+        const double* qns;
+        if (cov == KLA_ORACLE_DIAG) {
+            as = a + tk;
+            qns = qn + (size_t)h * dk;
+        } else {
+            as = a + (size_t)s * T;
+            qns = qn + (size_t)s * T;
+        }
+        run_sequence_residual(T, dk, dv, cov, q + tk, k + tk, v + tv, as, qns,
+                              r + (size_t)s * T, l, m, o + tv, lp, g, u);
+        if (lT)
+            for (int i = 0; i < nl; ++i) lT[s * nl + i] = l[i];
+        if (mT)
+            memcpy(mT + (size_t)s * dk * dv, m, sizeof(double) * (size_t)dk * dv);
+        free(l); free(lp); free(g); free(u); free(m);
+    }
+    return failed;
+}
