@@ -37,6 +37,8 @@ KERNEL_SOURCES = {
             "scan_amd/csrc/kla_common.h", "scan_amd/csrc/kla_internal.h"],
     "short": ["scan_amd/csrc/kla_fwd_short.hip", "scan_amd/csrc/kla_short.h",
               "scan_amd/csrc/kla_common.h", "scan_amd/csrc/kla_internal.h"],
+    "residual": ["scan_amd/csrc/kla_fwd_residual.hip", "scan_amd/csrc/kla_residual.h",
+                 "scan_amd/csrc/kla_common.h", "scan_amd/csrc/kla_internal.h"],
 }
 
 
@@ -296,7 +298,10 @@ def main() -> int:
     if args.workload == gen.PREFILL.name:
         print(json.dumps(run_prefill(args, torch, np, scan_amd, gen)), flush=True)
         return 0
-    w = gen.WORKLOADS[args.workload]
+    # the residual-write forward (klaFwdResidual) at the LM-layer shape, or
+    # the KLA forward (klaFwd) on one of the named workloads
+    residual = args.workload == gen.RESIDUAL.name
+    w = gen.RESIDUAL if residual else gen.WORKLOADS[args.workload]
     print(f"bench: workload {w}", file=sys.stderr, flush=True)
     host = gen.make_inputs(w, seed=0)
     names = ("q", "k", "v", "a", "qn", "r")
@@ -315,7 +320,10 @@ def main() -> int:
     def step(i):
         s = sets[i % 2]
         o, lT, etaT = outs[i % 2]
-        scan_amd.fwd(*s, cov=w.cov, o=o, lT=lT, etaT=etaT)
+        if residual:
+            scan_amd.fwd_residual(*s, cov=w.cov, o=o, lT=lT, mT=etaT)
+        else:
+            scan_amd.fwd(*s, cov=w.cov, o=o, lT=lT, etaT=etaT)
 
     for i in range(args.warmup):
         step(i)
@@ -353,12 +361,13 @@ def main() -> int:
     if not args.no_cpu:
         import oracle
         threads = oracle.default_threads()
+        oracle_fwd = oracle.fwd_residual if residual else oracle.fwd
         # calibrate on one sequence, then size the sample to ~cpu-seconds
         one = {n: host[n][:1, :1] for n in names}
         if w.cov == "diag":
             one["qn"] = host["qn"][:1]
         t0 = time.perf_counter()
-        oracle.fwd(*(one[n] for n in names), cov=oracle.DIAG if w.cov == "diag" else oracle.ISO,
+        oracle_fwd(*(one[n] for n in names), cov=oracle.DIAG if w.cov == "diag" else oracle.ISO,
                    nthreads=1)
         t_one = time.perf_counter() - t0
         nseq_total = B * H
@@ -375,7 +384,7 @@ def main() -> int:
         reps, t_cpu = 0, 0.0
         while reps == 0 or (t_cpu < 0.5 * args.cpu_seconds and reps < 100):
             t0 = time.perf_counter()
-            oracle.fwd(*(sub[n] for n in names), cov=cov_code, nthreads=threads)
+            oracle_fwd(*(sub[n] for n in names), cov=cov_code, nthreads=threads)
             t_cpu += time.perf_counter() - t0
             reps += 1
         seqs = nb * nh
@@ -384,10 +393,12 @@ def main() -> int:
                "sample": f"{seqs} of {nseq_total} (b,h) sequences at full T={T} "
                          f"({nb}x{nh}), fp64 sequential recurrence, {reps} pass(es) in {t_cpu:.1f}s"}
 
-    traffic = stored_traffic(w.name, w.cov)
-    kernel_name = scan_amd.fwd_kernel_name(w.B, w.H, w.T, w.dk, w.dv, w.cov, w.dtype)
+    traffic = stored_traffic(w.name, "residual" if residual else w.cov)
+    kernel_name = ("kla_fwd_residual_kernel" if residual else
+                   scan_amd.fwd_kernel_name(w.B, w.H, w.T, w.dk, w.dv, w.cov, w.dtype))
     line = {
-        "metric": "KLA layer fwd tokens/s at B·T, H×d; % of HBM/MFMA roofline",
+        "metric": ("KLA residual-write layer fwd tokens/s at B·T, H×d; % of HBM roofline" if residual
+                   else "KLA layer fwd tokens/s at B·T, H×d; % of HBM/MFMA roofline"),
         "value": value,
         "unit": "tokens/s",
         "n_gpus": 1,

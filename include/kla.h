@@ -131,6 +131,31 @@ klaStatus klaStep(const klaDims* d,
                   const float* a, const float* qnoise, const float* r,
                   float* l, float* eta, void* o, void* hipStream);
 
+/*
+ * Residual-write forward over T tokens for all (b,h) ([KDN]: the Kalman gain
+ * weights each residual write).  The memory is observed through the full key
+ * contraction, v_t = x_t^T k_t + noise, and each one-step posterior is
+ * projected onto the diagonal (isotropic) Gaussian family by mean-field
+ * variational inference, which keeps its mean.  With the state (l, m), m the
+ * posterior MEAN [B,H,dk,dv] (not the information l*m of klaFwd):
+ *     lp = l / (a^2 + qnoise*l),   m_pred = a (.) m   (row i scaled by a_i)
+ *     g  = (k/lp) / (sum_i k_i^2/lp_i + r)            (iso: k / (|k|^2 + r*lp))
+ *     m  = m_pred + g (v - m_pred^T k)^T
+ *     l  = lp + k^2/r                                  (iso: lp + |k|^2/(dk*r))
+ *     o  = m^T q
+ * Layouts, dtypes, alignment, ownership and execution as klaFwd, with m0 / mT
+ * in place of eta0 / etaT (m0 == NULL means m0 = 0; l0 == NULL means l0 = 1;
+ * lT, mT may be NULL).  Supported: dk == dv in {16, 32, 64, 128}, either
+ * dtype and cov (KLA_ERR_UNSUPPORTED otherwise); no workspace.  T == 0
+ * passes the state through.  Aliasing: o must not overlap any input; lT / mT
+ * must not overlap l0 / m0 (KLA_ERR_ALIAS).
+ */
+klaStatus klaFwdResidual(const klaDims* d,
+                         const void* q, const void* k, const void* v,
+                         const float* a, const float* qnoise, const float* r,
+                         const float* l0, const float* m0,
+                         void* o, float* lT, float* mT, void* hipStream);
+
 /* Static, human-readable description of a status code (never NULL). */
 const char* klaStatusString(klaStatus s);
 

@@ -6,18 +6,20 @@ is no CPU fallback: if the library is missing or no GPU is present the calls
 raise.
 
 Low level (same names and arguments as the C ABI, raw device pointers):
-    klaFwd, klaStep, klaFwdWorkspaceBytes, klaIsSupported, klaStatusString
+    klaFwd, klaStep, klaFwdResidual, klaFwdWorkspaceBytes, klaIsSupported, klaStatusString
 Convenience (torch tensors in, torch tensors out):
     fwd(q, k, v, a, qn, r, l0=None, eta0=None, cov="diag") -> (o, lT, etaT)
     step(q, k, v, a, qn, r, l, eta, cov="diag") -> o      (l, eta updated in place)
+    fwd_residual(q, k, v, a, qn, r, l0=None, m0=None, cov="diag") -> (o, lT, mT)
 """
 from __future__ import annotations
 
 import ctypes
 import os
 
-__all__ = ["klaFwd", "klaStep", "klaFwdWorkspaceBytes", "klaIsSupported", "klaStatusString",
-           "KlaDims", "KlaError", "fwd", "step", "lib_path", "load"]
+__all__ = ["klaFwd", "klaStep", "klaFwdResidual", "klaFwdWorkspaceBytes", "klaIsSupported",
+           "klaStatusString", "KlaDims", "KlaError", "fwd", "step", "fwd_residual", "lib_path",
+           "load"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libkla.so")
@@ -71,6 +73,8 @@ def load():
     lib.klaFwd.restype = ctypes.c_int
     lib.klaStep.argtypes = [dp, vp, vp, vp, fp, fp, fp, fp, fp, vp, vp]
     lib.klaStep.restype = ctypes.c_int
+    lib.klaFwdResidual.argtypes = [dp, vp, vp, vp, fp, fp, fp, fp, fp, vp, fp, fp, vp]
+    lib.klaFwdResidual.restype = ctypes.c_int
     lib.klaStatusString.argtypes = [ctypes.c_int]
     lib.klaStatusString.restype = ctypes.c_char_p
     lib.klaFwdKernelName.argtypes = [dp]
@@ -98,6 +102,12 @@ def klaFwd(dims, q, k, v, a, qnoise, r, l0, eta0, o, lT, etaT, workspace, worksp
 
 def klaStep(dims, q, k, v, a, qnoise, r, l, eta, o, stream) -> int:
     return int(load().klaStep(ctypes.byref(dims), q, k, v, a, qnoise, r, l, eta, o, stream))
+
+
+def klaFwdResidual(dims, q, k, v, a, qnoise, r, l0, m0, o, lT, mT, stream) -> int:
+    """Raw call of the residual-write forward (pointers as ints or None)."""
+    return int(load().klaFwdResidual(ctypes.byref(dims), q, k, v, a, qnoise, r, l0, m0, o, lT, mT,
+                                     stream))
 
 
 def klaStatusString(status: int) -> str:
@@ -189,3 +199,28 @@ def step(q, k, v, a, qn, r, l, eta, cov: str = "diag", o=None):
     if st != KLA_OK:
         raise KlaError(st, "klaStep")
     return o
+
+
+def fwd_residual(q, k, v, a, qn, r, l0=None, m0=None, cov: str = "diag", o=None, lT=None,
+                 mT=None):
+    """Residual-write forward on the current stream.  Returns (o, lT, mT), mT
+    the posterior mean [B,H,dk,dv].  Layouts as ``fwd``; outputs are
+    allocated unless passed in."""
+    import torch
+    _check_device(q, k, v, a, qn, r, l0, m0)
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    c = KLA_DIAG if cov == "diag" else KLA_ISO
+    dims = KlaDims(B, H, T, dk, dv, _dtype_code(q), c)
+    dev = q.device
+    if o is None:
+        o = torch.empty(B, H, T, dv, dtype=v.dtype, device=dev)
+    if lT is None:
+        lT = torch.empty((B, H, dk) if c == KLA_DIAG else (B, H), dtype=torch.float32, device=dev)
+    if mT is None:
+        mT = torch.empty(B, H, dk, dv, dtype=torch.float32, device=dev)
+    st = klaFwdResidual(dims, _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(qn), _ptr(r), _ptr(l0),
+                        _ptr(m0), _ptr(o), _ptr(lT), _ptr(mT), _stream())
+    if st != KLA_OK:
+        raise KlaError(st, "klaFwdResidual")
+    return o, lT, mT

@@ -17,7 +17,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkla.so")
 SOURCES = ["kla_api.cpp", "kla_fwd_diag.hip", "kla_fwd_diag_pipe.hip", "kla_fwd_iso.hip",
-           "kla_fwd_iso_pipe.hip", "kla_fwd_seg.hip", "kla_fwd_short.hip", "kla_step.hip"]
+           "kla_fwd_iso_pipe.hip", "kla_fwd_residual.hip", "kla_fwd_seg.hip", "kla_fwd_short.hip",
+           "kla_step.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

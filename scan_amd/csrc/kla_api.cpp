@@ -10,6 +10,7 @@
 #include <stdlib.h>
 
 #include "kla_internal.h"
+#include "kla_residual.h"
 #include "kla_short.h"
 
 namespace {
@@ -297,6 +298,49 @@ const char* klaStatusString(klaStatus s) {
         case KLA_ERR_ALIAS: return "KLA_ERR_ALIAS: an output overlaps an input";
     }
     return "unknown klaStatus";
+}
+
+klaStatus klaFwdResidual(const klaDims* d, const void* q, const void* k, const void* v, const float* a,
+                         const float* qnoise, const float* r, const float* l0, const float* m0, void* o,
+                         float* lT, float* mT, void* hipStream) {
+    if (!d) return KLA_ERR_NULL;
+    if (!dims_ok(d)) return KLA_ERR_SHAPE;
+    if (!kinds_ok(d) || !kla::fwd_residual_supported(d->dk, d->dv)) return KLA_ERR_UNSUPPORTED;
+    const long long B = d->B, H = d->H, T = d->T, dk = d->dk, dv = d->dv;
+    const long long BH = B * H;
+    if (BH > (1LL << 30) || T > (1LL << 30)) return KLA_ERR_SHAPE;
+    const bool iso = d->cov == KLA_ISO;
+    const size_t es = d->dtype == KLA_BF16 ? 2 : 4;
+    const size_t nlt = (size_t)(iso ? BH : BH * dk);
+    const size_t nm = (size_t)(BH * dk * dv);
+
+    if (BH == 0) return KLA_OK;
+    if (T > 0 && (!q || !k || !v || !a || !qnoise || !r || !o)) return KLA_ERR_NULL;
+    const void* ptrs[] = {q, k, v, a, o, m0, mT, qnoise, r, l0, lT};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return KLA_ERR_ALIGN;
+
+    const size_t ntk = (size_t)(BH * T);
+    const Span s_o = span(o, ntk * dv * es);
+    const Span s_lT = span(lT, nlt * 4), s_mT = span(mT, nm * 4);
+    const Span ins[] = {span(q, ntk * dk * es), span(k, ntk * dk * es), span(v, ntk * dv * es),
+                        span(a, (iso ? ntk : ntk * dk) * 4),
+                        span(qnoise, (iso ? ntk : (size_t)(H * dk)) * 4), span(r, ntk * 4),
+                        span(l0, nlt * 4), span(m0, nm * 4)};
+    for (const Span& s : ins)
+        if (overlap(s_o, s) || overlap(s_lT, s) || overlap(s_mT, s)) return KLA_ERR_ALIAS;
+    if (overlap(s_o, s_lT) || overlap(s_o, s_mT) || overlap(s_lT, s_mT)) return KLA_ERR_ALIAS;
+
+    kla::FwdArgs fa;
+    fa.q = q; fa.k = k; fa.v = v; fa.a = a; fa.qn = qnoise; fa.r = r;
+    fa.l0 = l0; fa.eta0 = m0; fa.o = o; fa.lT = lT; fa.etaT = mT;
+    fa.B = (int)B; fa.H = (int)H; fa.T = (int)T; fa.dk = (int)dk; fa.dv = (int)dv;
+    fa.n_vtiles = kla::fwd_residual_vtiles(fa.B, fa.H, fa.dk);
+    if (const char* env = getenv("KLA_RES_VTILES")) fa.n_vtiles = atoi(env) == 2 && dk >= 64 ? 2 : 1;
+    hipStream_t st = (hipStream_t)hipStream;
+    const hipError_t e = T == 0 ? kla::launch_fwd_empty(fa, iso ? 1 : 0, st)
+                                : kla::launch_fwd_residual(fa, d->dtype, iso ? 1 : 0, st);
+    return e == hipSuccess ? KLA_OK : KLA_ERR_HIP;
 }
 
 }  // extern "C"

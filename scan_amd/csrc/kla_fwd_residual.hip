@@ -1,0 +1,436 @@
+// kla_fwd_residual.hip -- gfx950 forward of the residual-write variant: the
+// Kalman gain weights a write of the residual v - m_pred^T k (the delta-style
+// write of "Kalman Delta Networks: Uncertainty-aware Associative Memory",
+// abstract; diagonal and isotropic approximations).
+//
+// Recurrence per (b,h), state (l, m) with m the posterior mean (dk x dv):
+//   lp = l / (a^2 + qn l),  m_pred = a (.) m               (row i scaled by a_i)
+//   g  = P k / (k^T P k + r),  P = diag(1/lp)               (iso: P = I/lp)
+//   m  = m_pred + g (v - m_pred^T k)^T,  l = lp + k^2/r     (iso: lp + |k|^2/(dk r))
+//   o  = m^T q
+// The precision is the Mobius map of the KLA forward; the mean write couples
+// the key dims through the prediction m_pred^T k.
+//
+// Tokens go in blocks of n <= 4.  With G_t the product of the block's decays
+// through token t and D(s,t) = a_{s+1} ... a_t (products only, no division),
+// the block's residuals u_t and outputs follow from the state M0 at its start:
+//   u_t = v_t - P_t - sum_{s<t} A[t][s] u_s,   P_t = (G_t k_t)^T M0
+//   o_t = O_t + sum_{s<=t} C[t][s] u_s,         O_t = (G_t q_t)^T M0
+//   M_end = G_end (.) M0 + sum_s (D(s,end) g_s) u_s^T
+// with A[t][s] = sum_i D(s,t)_i k_t,i g_s,i and C[t][s] = sum_i D(s,t)_i q_t,i g_s,i.
+// A and C (20 key-dim sums per block) depend on the inputs only, so they are
+// formed for the next block while the current one runs.
+//
+// Layout as in the short-sequence kernel: the threads of a (b,h) keep M in
+// registers (row group rg, value quad jq), small heads share a workgroup.
+// Per block: (1) every thread forms its rows' partial predictions and
+// readouts against M0; barrier; (4) partials are summed over the row groups
+// (and the next block's coefficients are finished); barrier; (6) one thread
+// per value quad solves the 4x4 unit-lower-triangular system for the
+// residuals and writes the outputs; barrier; (8) every thread updates its
+// rows.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kla_common.h"
+#include "kla_residual.h"
+
+namespace kla {
+namespace {
+
+constexpr int kResThreads = 256;
+constexpr int kResTB = 4;                          // tokens per block
+constexpr int kNP = kResTB * (kResTB + 1) / 2;     // token pairs s <= t
+__device__ __forceinline__ constexpr int pidx(int t, int s) { return t * (t + 1) / 2 + s; }
+
+// A (b,h) may be split by value columns into tiles of DVT columns: the
+// residual write couples the key dims, not the value columns, so each tile
+// runs on its own (the key-dim sums are formed in every tile).
+template <int D, int DVT>
+struct ResLayout {
+    static constexpr int EPT = D == 16 ? 16 : 32;  // state elements per thread, at least
+    static constexpr int NTH = D * DVT / EPT < kResThreads ? D * DVT / EPT : kResThreads;
+    static constexpr int NH = kResThreads / NTH;   // (b,h, value tile) per workgroup
+    static constexpr int VQ = DVT / 4;             // value quads per row of the tile
+    static constexpr int RG = NTH / VQ;            // row groups of a (b,h)
+    static constexpr int RPT = D / RG;             // rows per thread
+    static constexpr int KW = D < 64 ? D : 64;     // key-dim lanes per wave
+    static_assert(RPT % 4 == 0 && kResTB * VQ <= NTH && NTH * NH == kResThreads && NTH % D == 0,
+                  "layout");
+};
+
+// Coefficient buffers alternate by block parity: block b+1's are written
+// after the first barrier of block b, when every thread has finished block
+// b-1's state update, the last reader of that buffer.
+template <int D, int DVT>
+struct ResSm {
+    static constexpr int NH = ResLayout<D, DVT>::NH, NTH = ResLayout<D, DVT>::NTH;
+    alignas(16) float kt[2][NH][kResTB][D];   // G_t k_t
+    alignas(16) float qt[2][NH][kResTB][D];   // G_t q_t
+    alignas(16) float e[2][NH][kResTB][D];    // D(s,end) g_s
+    alignas(16) float gn[2][NH][D];           // G_end
+    alignas(16) float v[2][NH][kResTB][DVT];
+    float A[2][NH][kResTB][kResTB];           // [t][s], s < t
+    float C[2][NH][kResTB][kResTB];           // [t][s], s <= t
+    alignas(16) f32x4 part[2][NH][kResTB][NTH];  // prediction / readout partials
+    alignas(16) float pr[2][NH][kResTB][DVT];  // their sums over the row groups
+    alignas(16) float u[NH][kResTB][DVT];      // residuals
+    float red[2 * kNP][kResThreads / 64];     // d 128: per-wave partial sums
+};
+
+template <typename TIn, int D, int DVT, bool ISO>
+__global__ __launch_bounds__(kResThreads) void kla_fwd_residual_kernel(FwdArgs p) {
+    typedef ResLayout<D, DVT> Ly;
+    constexpr int NVT = D / DVT;
+    constexpr int TB = kResTB, NTH = Ly::NTH, NH = Ly::NH, VQ = Ly::VQ, RG = Ly::RG, RPT = Ly::RPT;
+    constexpr int KW = Ly::KW;
+    constexpr bool RED = D > 64;  // key dims of a head span two waves
+    typedef typename Quad<TIn>::V QV;
+    __shared__ ResSm<D, DVT> sm;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int grp = NH == 1 ? 0 : tid / NTH, lt = NH == 1 ? tid : tid % NTH;
+    // Value tiles of one (b,h) run 8 workgroups apart, on the same XCD
+    // (workgroups go round-robin over the 8 XCDs), so the second tile's reads
+    // of k, q, a and r hit that XCD's L2.
+    const int x8 = (int)blockIdx.x;
+    const int vt = NVT == 1 ? 0 : (x8 / 8) % NVT;
+    const int hb = NVT == 1 ? x8 : (x8 / (8 * NVT)) * 8 + x8 % 8;
+    const int nbh = p.B * p.H;
+    if (NVT > 1 && hb >= (nbh + NH - 1) / NH) return;  // padding of the grid to the XCD pattern
+    const int bh_ = NH == 1 ? hb : hb * NH + grp;
+    const bool valid = NH == 1 || bh_ < nbh;
+    const int bh = valid ? bh_ : nbh - 1;  // a spare group loads in bounds and stores nothing
+    const int h = bh % p.H;
+    const int col0 = vt * DVT;  // first value column of the tile
+    const int jq = lt % VQ, rg = lt / VQ, i0 = rg * RPT;
+    const bool kd = lt < D;  // key-dim lane
+    const int kdim = kd ? lt : D - 1;
+    const size_t row0 = (size_t)bh * p.T;
+    const TIn* q = (const TIn*)p.q;
+    const TIn* k = (const TIn*)p.k;
+    const TIn* v = (const TIn*)p.v;
+    TIn* o = (TIn*)p.o;
+
+    // the thread's slice of the mean state
+    f32x4 M[RPT];
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+        const size_t off = ((size_t)bh * D + i0 + m) * D + col0 + 4 * jq;
+        M[m] = p.eta0 ? *(const f32x4*)(p.eta0 + off) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    float l;  // precision of key dim kdim (diag) or of the head (iso)
+    if constexpr (!ISO) l = p.l0 ? p.l0[(size_t)bh * D + kdim] : 1.f;
+    else l = p.l0 ? p.l0[bh] : 1.f;
+    const float qn_i = !ISO ? p.qn[(size_t)h * D + kdim] : 0.f;
+
+    struct Raw {
+        TIn k[TB], q[TB];
+        float a[TB], r[TB], qn[TB];
+        QV vq;
+    };
+    auto load = [&](int t0, Raw& x) {
+        const int nb = p.T - t0 < TB ? p.T - t0 : TB;
+#pragma unroll
+        for (int u = 0; u < TB; ++u) {
+            const size_t t = row0 + t0 + (u < nb ? u : nb - 1), idx = t * D + kdim;
+            x.k[u] = k[idx];
+            x.q[u] = q[idx];
+            x.r[u] = p.r[t];
+            if constexpr (!ISO) {
+                x.a[u] = p.a[idx];
+                x.qn[u] = 0.f;
+            } else {
+                x.a[u] = p.a[t];
+                x.qn[u] = p.qn[t];
+            }
+        }
+        const int uv = lt / VQ < nb ? lt / VQ : nb - 1;
+        x.vq = *(const QV*)(v + (row0 + t0 + uv) * D + col0 + 4 * jq);
+    };
+    auto settle = [&](Raw& x) {
+#pragma unroll
+        for (int u = 0; u < TB; ++u) {
+            asm volatile("" : "+v"(x.k[u]), "+v"(x.q[u]), "+v"(x.a[u]), "+v"(x.r[u]));
+            if constexpr (ISO) asm volatile("" : "+v"(x.qn[u]));
+        }
+        asm volatile("" : "+v"(x.vq));
+    };
+
+    // ---- a block's coefficients, in two steps around a barrier
+    // Pre: per key-dim lane, the block's gains up to their common divisor and
+    // the 20 key-dim sums (diag: k_t.D(s,t).k_s/lp_s and q_t.D(s,t).k_s/lp_s;
+    // iso: k_t.k_s and q_t.k_s), reduced over the wave's key-dim lanes.
+    struct Pre {
+        float kf[TB], qf[TB], c[TB], cum[TB];  // k, q, k/lp (diag), G_t (diag)
+        float lp[TB];                           // diag: predicted precision
+        float sum[2 * kNP];                     // [0,kNP): k-sums, [kNP,2kNP): q-sums
+    };
+    auto pre = [&](const Raw& x, int nb, Pre& P) {
+        float dec[TB];
+#pragma unroll
+        for (int u = 0; u < TB; ++u) {
+            const bool on = u < nb && kd;
+            P.kf[u] = on ? (float)x.k[u] : 0.f;
+            P.qf[u] = on ? (float)x.q[u] : 0.f;
+            dec[u] = u < nb ? x.a[u] : 1.f;
+        }
+        if constexpr (!ISO) {
+            float g = 1.f;
+#pragma unroll
+            for (int u = 0; u < TB; ++u) {
+                const float rd = fast_rcp(__builtin_fmaf(qn_i, l, dec[u] * dec[u]));
+                const float lp = l * rd;
+                P.lp[u] = lp;
+                P.c[u] = P.kf[u] * fast_rcp(lp);
+                g *= dec[u];
+                P.cum[u] = g;
+                if (u < nb) l = __builtin_fmaf(P.kf[u] * P.kf[u], fast_rcp(x.r[u]), lp);
+            }
+#pragma unroll
+            for (int t = 0; t < TB; ++t) {
+                float dst = 1.f;  // D(s,t) for s = t, t-1, ...
+#pragma unroll
+                for (int s = t; s >= 0; --s) {
+                    if (s < t) dst *= dec[s + 1];
+                    P.sum[pidx(t, s)] = dst * P.kf[t] * P.c[s];
+                    P.sum[kNP + pidx(t, s)] = dst * P.qf[t] * P.c[s];
+                }
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < TB; ++t)
+#pragma unroll
+                for (int s = 0; s <= t; ++s) {
+                    P.sum[pidx(t, s)] = P.kf[t] * P.kf[s];
+                    P.sum[kNP + pidx(t, s)] = P.qf[t] * P.kf[s];
+                }
+        }
+#pragma unroll
+        for (int j = 0; j < 2 * kNP; ++j) {
+            float s = P.sum[j];
+#pragma unroll
+            for (int m = 1; m < KW; m <<= 1) s += __shfl_xor(s, m, 64);
+            P.sum[j] = s;
+        }
+        if constexpr (RED) {
+            if (lane == 0) {
+#pragma unroll
+                for (int j = 0; j < 2 * kNP; ++j) sm.red[j][wave] = P.sum[j];
+            }
+        }
+    };
+    // Finish (after a barrier): the whole-head sums, the gains' divisors and
+    // the coefficients of buffer c.
+    auto finish = [&](const Raw& x, int nb, Pre& P, int c) {
+        if constexpr (RED) {
+            // the head's key dims are the group's first two waves
+            const int w0 = grp * (NTH / 64);
+#pragma unroll
+            for (int j = 0; j < 2 * kNP; ++j) P.sum[j] = sm.red[j][w0] + sm.red[j][w0 + 1];
+        }
+        float dec[TB], inv[TB], cum[TB];
+        float scale[TB];  // iso: 1 / lp_s (the gain is k_s / (lp_s (s_s + r_s)))
+#pragma unroll
+        for (int u = 0; u < TB; ++u) dec[u] = u < nb ? x.a[u] : 1.f;
+        if constexpr (!ISO) {
+#pragma unroll
+            for (int u = 0; u < TB; ++u) {
+                inv[u] = fast_rcp(P.sum[pidx(u, u)] + x.r[u]);
+                scale[u] = 1.f;
+                cum[u] = P.cum[u];
+            }
+        } else {
+            float g = 1.f;
+#pragma unroll
+            for (int u = 0; u < TB; ++u) {
+                const float ksq = P.sum[pidx(u, u)];
+                const float rd = fast_rcp(__builtin_fmaf(x.qn[u], l, dec[u] * dec[u]));
+                const float lp = l * rd, rlp = fast_rcp(lp);
+                inv[u] = fast_rcp(__builtin_fmaf(ksq, rlp, x.r[u]));
+                scale[u] = rlp;
+                if (u < nb) l = __builtin_fmaf(ksq * (1.f / (float)D), fast_rcp(x.r[u]), lp);
+                g *= dec[u];
+                cum[u] = g;
+            }
+        }
+        const float gend = cum[nb - 1];
+        if (kd) {
+#pragma unroll
+            for (int u = 0; u < TB; ++u) {
+                // D(u, end) g_u: decays after token u through the block's end
+                float after = 1.f;
+#pragma unroll
+                for (int w = u + 1; w < TB; ++w)
+                    if (w < nb) after *= dec[w];
+                const float gu = (ISO ? P.kf[u] * scale[u] : P.c[u]) * inv[u];
+                sm.e[c][grp][u][lt] = after * gu;
+                sm.kt[c][grp][u][lt] = cum[u] * P.kf[u];
+                sm.qt[c][grp][u][lt] = cum[u] * P.qf[u];
+            }
+            sm.gn[c][grp][lt] = gend;
+        }
+        if (lt == 0) {
+#pragma unroll
+            for (int t = 0; t < TB; ++t) {
+                float dst = 1.f;
+#pragma unroll
+                for (int s = t; s >= 0; --s) {
+                    if (s < t) dst *= dec[s + 1];
+                    const float w = (ISO ? dst * scale[s] : 1.f) * inv[s];
+                    sm.A[c][grp][t][s] = s < t ? w * P.sum[pidx(t, s)] : 0.f;
+                    sm.C[c][grp][t][s] = w * P.sum[kNP + pidx(t, s)];
+                }
+            }
+        }
+        if (lt / VQ < nb) *(f32x4*)&sm.v[c][grp][lt / VQ][4 * jq] = Quad<TIn>::to_f32(x.vq);
+    };
+
+    {
+        Raw x;
+        load(0, x);
+        settle(x);
+        Pre P;
+        const int nb0 = p.T < TB ? p.T : TB;
+        pre(x, nb0, P);
+        lds_barrier();
+        finish(x, nb0, P, 0);
+        lds_barrier();
+    }
+    int c = 0;
+    for (int t0 = 0; t0 < p.T; t0 += TB, c ^= 1) {
+        const int nb = p.T - t0 < TB ? p.T - t0 : TB;
+        const bool more = t0 + TB < p.T;
+        const int nbn = more ? (p.T - t0 - TB < TB ? p.T - t0 - TB : TB) : 0;
+        Raw x;
+        load(more ? t0 + TB : t0, x);
+        // (1) partial predictions and readouts of the block's tokens against M0
+#pragma unroll
+        for (int u = 0; u < TB; ++u) {
+            if (u < nb) {
+                f32x4 ap = {0.f, 0.f, 0.f, 0.f}, ao = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int m4 = 0; m4 < RPT; m4 += 4) {
+                    const f32x4 kv = *(const f32x4*)&sm.kt[c][grp][u][i0 + m4];
+                    const f32x4 qv = *(const f32x4*)&sm.qt[c][grp][u][i0 + m4];
+#pragma unroll
+                    for (int x4 = 0; x4 < 4; ++x4) {
+                        ap += kv[x4] * M[m4 + x4];
+                        ao += qv[x4] * M[m4 + x4];
+                    }
+                }
+                sm.part[0][grp][u][lt] = ap;
+                sm.part[1][grp][u][lt] = ao;
+            }
+        }
+        // (2) the next block's key-dim sums
+        settle(x);
+        Pre P;
+        if (more) pre(x, nbn, P);
+        lds_barrier();
+        // (4) sums over the row groups; the next block's coefficients
+        for (int w = lt; w < 2 * nb * VQ; w += NTH) {
+            const int kind = w / (nb * VQ), rem = w % (nb * VQ), u = rem / VQ, j4 = rem % VQ;
+            f32x4 s = sm.part[kind][grp][u][j4];
+#pragma unroll
+            for (int r2 = 1; r2 < RG; ++r2) s += sm.part[kind][grp][u][r2 * VQ + j4];
+            *(f32x4*)&sm.pr[kind][grp][u][4 * j4] = s;
+        }
+        if (more) finish(x, nbn, P, c ^ 1);
+        lds_barrier();
+        // (6) residuals and outputs, one thread per value quad
+        if (lt < VQ) {
+            f32x4 us[TB];
+#pragma unroll
+            for (int t = 0; t < TB; ++t) {
+                if (t < nb) {
+                    f32x4 ut = *(const f32x4*)&sm.v[c][grp][t][4 * lt] - *(const f32x4*)&sm.pr[0][grp][t][4 * lt];
+#pragma unroll
+                    for (int s = 0; s < t; ++s) ut -= sm.A[c][grp][t][s] * us[s];
+                    us[t] = ut;
+                    f32x4 ot = *(const f32x4*)&sm.pr[1][grp][t][4 * lt];
+#pragma unroll
+                    for (int s = 0; s <= t; ++s) ot += sm.C[c][grp][t][s] * us[s];
+                    *(f32x4*)&sm.u[grp][t][4 * lt] = ut;
+                    if (valid) *(QV*)(o + (row0 + t0 + t) * D + col0 + 4 * lt) = Quad<TIn>::make(ot);
+                }
+            }
+        }
+        lds_barrier();
+        // (8) the state at the block's end
+#pragma unroll
+        for (int m4 = 0; m4 < RPT; m4 += 4) {
+            const f32x4 gv = *(const f32x4*)&sm.gn[c][grp][i0 + m4];
+#pragma unroll
+            for (int x4 = 0; x4 < 4; ++x4) M[m4 + x4] *= gv[x4];
+        }
+#pragma unroll
+        for (int u = 0; u < TB; ++u) {
+            if (u < nb) {
+                const f32x4 uu = *(const f32x4*)&sm.u[grp][u][4 * jq];
+#pragma unroll
+                for (int m4 = 0; m4 < RPT; m4 += 4) {
+                    const f32x4 ev = *(const f32x4*)&sm.e[c][grp][u][i0 + m4];
+#pragma unroll
+                    for (int x4 = 0; x4 < 4; ++x4) M[m4 + x4] += ev[x4] * uu;
+                }
+            }
+        }
+    }
+    if (!valid) return;
+    if (p.etaT) {
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) *(f32x4*)(p.etaT + ((size_t)bh * D + i0 + m) * D + col0 + 4 * jq) = M[m];
+    }
+    if (p.lT && vt == 0) {
+        if constexpr (!ISO) {
+            if (kd) p.lT[(size_t)bh * D + lt] = l;
+        } else if (lt == 0) {
+            p.lT[bh] = l;
+        }
+    }
+}
+
+template <typename TIn, int D, int DVT, bool ISO>
+void launch(const FwdArgs& a, hipStream_t s) {
+    typedef ResLayout<D, DVT> Ly;
+    const int nbh = a.B * a.H, ngroups = (nbh + Ly::NH - 1) / Ly::NH;
+    constexpr int NVT = D / DVT;
+    const dim3 grid((unsigned)(NVT == 1 ? ngroups : (ngroups + 7) / 8 * 8 * NVT));
+    hipLaunchKernelGGL((kla_fwd_residual_kernel<TIn, D, DVT, ISO>), grid, dim3(kResThreads), 0, s, a);
+}
+
+template <typename TIn, bool ISO>
+hipError_t dispatch(const FwdArgs& a, hipStream_t s) {
+    const int nvt = a.n_vtiles;
+    switch (a.dk) {
+        case 16: launch<TIn, 16, 16, ISO>(a, s); break;
+        case 32: launch<TIn, 32, 32, ISO>(a, s); break;
+        case 64: nvt == 2 ? launch<TIn, 64, 32, ISO>(a, s) : launch<TIn, 64, 64, ISO>(a, s); break;
+        case 128: nvt == 2 ? launch<TIn, 128, 64, ISO>(a, s) : launch<TIn, 128, 128, ISO>(a, s); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool fwd_residual_supported(int dk, int dv) {
+    return dk == dv && (dk == 16 || dk == 32 || dk == 64 || dk == 128);
+}
+
+int fwd_residual_vtiles(int B, int H, int dk) {
+    // two value tiles for d 64 / 128 while there are fewer (b,h) than about
+    // two workgroups per CU
+    const long long nbh = (long long)B * H;
+    return dk >= 64 && nbh < 512 ? 2 : 1;
+}
+
+hipError_t launch_fwd_residual(const FwdArgs& a, int dtype, int cov, hipStream_t s) {
+    if (!fwd_residual_supported(a.dk, a.dv) || a.T < 1) return hipErrorInvalidValue;
+    if (a.n_vtiles != 1 && !(a.n_vtiles == 2 && a.dk >= 64)) return hipErrorInvalidValue;
+    if (dtype == DT_BF16) return cov ? dispatch<bf16, true>(a, s) : dispatch<bf16, false>(a, s);
+    return cov ? dispatch<float, true>(a, s) : dispatch<float, false>(a, s);
+}
+
+}  // namespace kla

@@ -66,6 +66,8 @@ DECODE_STEPS = 64
 # the cached states of the decode batch (T is the chunk length; the states
 # come from a DECODE.T-token prefix forward)
 PREFILL = Workload("iso_prefill16", 256, 32, 16, 64, 64, "iso", "bf16")
+# the residual-write forward at the LM-layer shape (same draws as lm_diag)
+RESIDUAL = Workload("residual_lm_diag", 8, 16, 2048, 128, 128, "diag", "bf16")
 
 _TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
 

@@ -205,3 +205,33 @@ def test_split_workspace_contract(monkeypatch):
     assert fwd_call(long, workspace=addr(9) + 4096, workspaceBytes=ws) == ALIAS
     monkeypatch.setenv("KLA_FWD_NSEG", "1")
     assert scan_amd.klaFwdWorkspaceBytes(long) == 0
+
+
+# ------------------------------------------------------------------ klaFwdResidual
+
+def res_call(d, **over):
+    args = dict(q=addr(1), k=addr(2), v=addr(3), a=addr(4), qnoise=addr(5), r=addr(6),
+                l0=addr(7), m0=addr(8), o=addr(9), lT=addr(10), mT=addr(11), stream=None)
+    args.update(over)
+    return scan_amd.klaFwdResidual(d, **args)
+
+
+def test_residual_argument_errors():
+    lib = scan_amd.load()
+    assert lib.klaFwdResidual(None, *([None] * 11), None) == NULL
+    d = KlaDims(1, 2, 16, 16, 16, F32, DIAG)
+    for field in ("B", "H", "T", "dk", "dv"):
+        bad = KlaDims(1, 2, 16, 16, 16, F32, DIAG)
+        setattr(bad, field, -1)
+        assert res_call(bad) == SHAPE, field
+    for dims in [(1, 1, 8, 48, 48), (1, 1, 8, 64, 32), (1, 1, 8, 256, 256)]:
+        assert res_call(KlaDims(*dims, F32, ISO)) == UNSUP, dims
+    assert res_call(KlaDims(1, 2, 16, 16, 16, 7, DIAG)) == UNSUP
+    for name in ("q", "k", "v", "a", "qnoise", "r", "o"):
+        assert res_call(d, **{name: None}) == NULL, name
+    for name in ("q", "k", "v", "a", "o", "m0", "mT", "l0", "lT", "r"):
+        assert res_call(d, **{name: addr(20) + 4}) == ALIGN, name
+    assert res_call(d, o=addr(2)) == ALIAS           # o over k
+    assert res_call(d, lT=addr(7)) == ALIAS          # lT over l0
+    assert res_call(d, mT=addr(8) + 16) == ALIAS     # mT inside m0
+    assert res_call(KlaDims(0, 4, 16, 16, 16, F32, DIAG)) == OK
