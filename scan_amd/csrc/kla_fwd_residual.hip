@@ -41,7 +41,34 @@ namespace {
 constexpr int kResThreads = 256;
 constexpr int kResTB = 4;                          // tokens per block
 constexpr int kNP = kResTB * (kResTB + 1) / 2;     // token pairs s <= t
+constexpr int kNS = 32;                            // 2*kNP sums, padded to a power of two
 __device__ __forceinline__ constexpr int pidx(int t, int s) { return t * (t + 1) / 2 + s; }
+
+// One exchange of the reduce-scatter over lane mask M of the N values a lane
+// still holds: the lane keeps the half chosen by its lane bit, sends the
+// other half to its partner and adds the partner's copy of the kept half
+// (N == 1: a plain exchange-and-add).  base accumulates the index of the
+// first kept value.
+template <int N, int M>
+__device__ __forceinline__ void reduce_scatter(float* w, int lane, int& base) {
+    if constexpr (M >= 1) {
+        if constexpr (N > 1) {
+            constexpr int H = N / 2;
+            const bool hi = (lane & M) != 0;
+#pragma unroll
+            for (int j = 0; j < H; ++j) {
+                const float keep = hi ? w[H + j] : w[j];
+                const float send = hi ? w[j] : w[H + j];
+                w[j] = keep + __shfl_xor(send, M, 64);
+            }
+            base += hi ? H : 0;
+            reduce_scatter<H, M / 2>(w, lane, base);
+        } else {
+            w[0] += __shfl_xor(w[0], M, 64);
+            reduce_scatter<N, M / 2>(w, lane, base);
+        }
+    }
+}
 
 // A (b,h) may be split by value columns into tiles of DVT columns: the
 // residual write couples the key dims, not the value columns, so each tile
@@ -55,7 +82,8 @@ struct ResLayout {
     static constexpr int RG = NTH / VQ;            // row groups of a (b,h)
     static constexpr int RPT = D / RG;             // rows per thread
     static constexpr int KW = D < 64 ? D : 64;     // key-dim lanes per wave
-    static_assert(RPT % 4 == 0 && kResTB * VQ <= NTH && NTH * NH == kResThreads && NTH % D == 0,
+    static_assert(RPT % 4 == 0 && kResTB * VQ <= NTH && NTH * NH == kResThreads && NTH % D == 0 &&
+                      (KW == 16 || KW == 32 || KW == 64),
                   "layout");
 };
 
@@ -75,7 +103,9 @@ struct ResSm {
     alignas(16) f32x4 part[2][NH][kResTB][NTH];  // prediction / readout partials
     alignas(16) float pr[2][NH][kResTB][DVT];  // their sums over the row groups
     alignas(16) float u[NH][kResTB][DVT];      // residuals
-    float red[2 * kNP][kResThreads / 64];     // d 128: per-wave partial sums
+    // the 2*kNP key-dim sums (padded to kNS) of each reduction unit: a
+    // group's key-dim lanes, or at d 128 each of its two waves
+    float sums[kResThreads / 16][kNS];
 };
 
 template <typename TIn, int D, int DVT, bool ISO>
@@ -206,18 +236,24 @@ __global__ __launch_bounds__(kResThreads) void kla_fwd_residual_kernel(FwdArgs p
                     P.sum[kNP + pidx(t, s)] = P.qf[t] * P.kf[s];
                 }
         }
+        // Reduce-scatter over the KW key-dim lanes: at each exchange a lane
+        // keeps one half of its values (chosen by its lane bit), sends the
+        // other half to its partner and adds the partner's copy of the kept
+        // half.  After log2(kNS) halvings each lane holds one value summed
+        // over 32 lanes (two values over 16 at KW = 16); a last full exchange
+        // completes KW = 64.  The owners write the sums to LDS.
+        float w[kNS];
 #pragma unroll
-        for (int j = 0; j < 2 * kNP; ++j) {
-            float s = P.sum[j];
+        for (int j = 0; j < kNS; ++j) w[j] = j < 2 * kNP ? P.sum[j] : 0.f;
+        int base = 0;
+        reduce_scatter<kNS, KW / 2>(w, lane, base);
+        // owners: lane holds values base .. base+NOUT-1 of its unit
+        constexpr int NOUT = kNS / KW > 0 ? kNS / KW : 1;
+        const int unit = RED ? wave : grp;
+        const bool owner = kd && (KW < 64 || (lane & 1) == 0);
+        if (owner) {
 #pragma unroll
-            for (int m = 1; m < KW; m <<= 1) s += __shfl_xor(s, m, 64);
-            P.sum[j] = s;
-        }
-        if constexpr (RED) {
-            if (lane == 0) {
-#pragma unroll
-                for (int j = 0; j < 2 * kNP; ++j) sm.red[j][wave] = P.sum[j];
-            }
+            for (int j = 0; j < NOUT; ++j) sm.sums[unit][base + j] = w[j];
         }
     };
     // Finish (after a barrier): the whole-head sums, the gains' divisors and
@@ -227,7 +263,10 @@ __global__ __launch_bounds__(kResThreads) void kla_fwd_residual_kernel(FwdArgs p
             // the head's key dims are the group's first two waves
             const int w0 = grp * (NTH / 64);
 #pragma unroll
-            for (int j = 0; j < 2 * kNP; ++j) P.sum[j] = sm.red[j][w0] + sm.red[j][w0 + 1];
+            for (int j = 0; j < 2 * kNP; ++j) P.sum[j] = sm.sums[w0][j] + sm.sums[w0 + 1][j];
+        } else {
+#pragma unroll
+            for (int j = 0; j < 2 * kNP; ++j) P.sum[j] = sm.sums[grp][j];
         }
         float dec[TB], inv[TB], cum[TB];
         float scale[TB];  // iso: 1 / lp_s (the gain is k_s / (lp_s (s_s + r_s)))
@@ -254,7 +293,10 @@ __global__ __launch_bounds__(kResThreads) void kla_fwd_residual_kernel(FwdArgs p
                 cum[u] = g;
             }
         }
-        const float gend = cum[nb - 1];
+        float gend = 1.f;  // G at the block's last token
+#pragma unroll
+        for (int u = 0; u < TB; ++u)
+            if (u == nb - 1) gend = cum[u];
         if (kd) {
 #pragma unroll
             for (int u = 0; u < TB; ++u) {
