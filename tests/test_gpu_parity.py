@@ -344,3 +344,27 @@ def test_parity_sequence_split(monkeypatch, name, over, nseg, state):
     hip = run_hip(inp, "diag", l0, eta0)
     ref = run_oracle(inp, "diag", l0, eta0)
     assert_parity(compare(hip, ref), w.dtype, f"split {name} {over}")
+
+
+@pytest.mark.parametrize("cov", ["diag", "iso"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_short_adversarial_gates(cov, dtype):
+    """The short-sequence kernel with a -> 0.01 (every 7th token 0.9),
+    r = 1e-3 and |k| up to 5, from a cached state: finite and at parity."""
+    _print_case("short adversarial", cov, dtype)
+    T = 31
+    base = "small_diag" if cov == "diag" else "iso"
+    inp = gen.make_inputs(base, seed=14, B=2, H=3, T=T, dk=64, dv=64, dtype=dtype)
+    assert scan_amd.fwd_kernel_name(2, 3, T, 64, 64, cov=cov, dtype=dtype) == "kla_fwd_short_kernel"
+    g = torch.Generator().manual_seed(15)
+    a = torch.full(inp["a"].shape, 0.01)
+    a[:, :, ::7] = 0.9
+    inp["a"] = a
+    inp["r"] = torch.full((2, 3, T), 1e-3)
+    inp["k"] = (5 * (2 * torch.rand(2, 3, T, 64, generator=g) - 1)).to(inp["k"].dtype)
+    st = gen.make_state(inp["workload"], seed=16)
+    hip = run_hip(inp, cov, st["l0"], st["eta0"])
+    for k in hip:
+        assert np.all(np.isfinite(hip[k])), k
+    ref = run_oracle(inp, cov, st["l0"], st["eta0"])
+    assert_parity(compare(hip, ref), dtype, f"short adversarial {cov}")

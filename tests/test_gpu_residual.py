@@ -131,3 +131,25 @@ def test_residual_value_tiles(cov, d, nvt, monkeypatch):
     hip = run_hip_res(inp, cov, st["l0"], st["eta0"])
     ref = run_oracle_res(inp, cov, st["l0"], st["eta0"])
     assert_parity(compare(hip, ref), "f32", f"residual tiles {cov} d={d} nvt={nvt}")
+
+
+@pytest.mark.parametrize("cov", ["diag", "iso"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_residual_adversarial_gates(cov, dtype):
+    """a -> 0.01 (every 7th token 0.9), r = 1e-3, |k| up to 5: near-exact
+    interpolating writes and fast decay; finite and at parity."""
+    _print_case("adversarial", cov, dtype)
+    T = 200
+    base = "small_diag" if cov == "diag" else "iso"
+    inp = gen.make_inputs(base, seed=24, B=1, H=3, T=T, dk=64, dv=64, dtype=dtype)
+    g = torch.Generator().manual_seed(25)
+    a = torch.full(inp["a"].shape, 0.01)
+    a[:, :, ::7] = 0.9
+    inp["a"] = a
+    inp["r"] = torch.full((1, 3, T), 1e-3)
+    inp["k"] = (5 * (2 * torch.rand(1, 3, T, 64, generator=g) - 1)).to(inp["k"].dtype)
+    hip = run_hip_res(inp, cov)
+    for k in hip:
+        assert np.all(np.isfinite(hip[k])), k
+    ref = run_oracle_res(inp, cov)
+    assert_parity(compare(hip, ref), dtype, f"residual adversarial {cov}")
