@@ -28,6 +28,10 @@
  * isotropic variant ([KDN]) l is one scalar per head, a_t and qn_t are per
  * token, and the precision increment is b_t = sum_i k_t[i]^2 / (d_k r_t);
  * the information rows are updated as above with the scalar gate.
+ * klaFwdResidual (below) computes the residual-write variant of [KDN], in
+ * which the key dims are coupled through the prediction of v.
+ * (Short sequences and decode steps continue a cached state; see klaFwd and
+ * klaStep.)
  *
  * Layouts: dense, row-major, head-major ("BHTD"):
  *   q, k        [B,H,T,dk]      dtype (fp32 or bf16)
