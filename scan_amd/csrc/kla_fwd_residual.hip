@@ -31,6 +31,7 @@
 // rows.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "kla_common.h"
 #include "kla_residual.h"
@@ -73,50 +74,61 @@ __device__ __forceinline__ void reduce_scatter(float* w, int lane, int& base) {
 // A (b,h) may be split by value columns into tiles of DVT columns: the
 // residual write couples the key dims, not the value columns, so each tile
 // runs on its own (the key-dim sums are formed in every tile).
-template <int D, int DVT>
+//
+// MM (d 64 / 128, 64-column tiles): the matrix-core layout.  Each of the four
+// waves owns 16 value columns of the tile as D/16 accumulator tiles (lane l:
+// key dims 16 rt + 4 (l/16) + e, column l%16), which is also the B operand
+// of a 16-wide contraction over key dims.  The block's predictions and
+// readouts are then one pass of MFMAs per wave, with the block's G_t k_t and
+// G_t q_t stacked as 8 rows of the A operand, and the state update is a
+// second pass with the residuals as the B operand: nothing is summed across
+// waves, and one barrier fewer is needed per block.
+template <int D, int DVT, bool MM>
 struct ResLayout {
     static constexpr int EPT = D == 16 ? 16 : 32;  // state elements per thread, at least
-    static constexpr int NTH = D * DVT / EPT < kResThreads ? D * DVT / EPT : kResThreads;
+    static constexpr int NTH = MM ? kResThreads : D * DVT / EPT < kResThreads ? D * DVT / EPT : kResThreads;
     static constexpr int NH = kResThreads / NTH;   // (b,h, value tile) per workgroup
     static constexpr int VQ = DVT / 4;             // value quads per row of the tile
-    static constexpr int RG = NTH / VQ;            // row groups of a (b,h)
-    static constexpr int RPT = D / RG;             // rows per thread
+    static constexpr int RG = MM ? 1 : NTH / VQ;   // row groups of a (b,h)
+    static constexpr int RPT = MM ? 4 : D / RG;    // rows per thread
     static constexpr int KW = D < 64 ? D : 64;     // key-dim lanes per wave
     static_assert(RPT % 4 == 0 && kResTB * VQ <= NTH && NTH * NH == kResThreads && NTH % D == 0 &&
-                      (KW == 16 || KW == 32 || KW == 64),
+                      (KW == 16 || KW == 32 || KW == 64) && (!MM || (DVT == 64 && D >= 64)),
                   "layout");
 };
 
 // Coefficient buffers alternate by block parity: block b+1's are written
 // after the first barrier of block b, when every thread has finished block
 // b-1's state update, the last reader of that buffer.
-template <int D, int DVT>
+template <int D, int DVT, bool MM>
 struct ResSm {
-    static constexpr int NH = ResLayout<D, DVT>::NH, NTH = ResLayout<D, DVT>::NTH;
+    static constexpr int NH = ResLayout<D, DVT, MM>::NH, NTH = ResLayout<D, DVT, MM>::NTH;
+    static constexpr int X = MM ? 1 : 0;  // arrays only the thread-row layout uses shrink to one entry
     alignas(16) float kt[2][NH][kResTB][D];   // G_t k_t
     alignas(16) float qt[2][NH][kResTB][D];   // G_t q_t
-    alignas(16) float e[2][NH][kResTB][D];    // D(s,end) g_s
+    alignas(16) float e[2][NH][MM ? D : kResTB][MM ? kResTB : D];  // D(s,end) g_s ([i][s] for MM)
     alignas(16) float gn[2][NH][D];           // G_end
     alignas(16) float v[2][NH][kResTB][DVT];
     float A[2][NH][kResTB][kResTB];           // [t][s], s < t
     float C[2][NH][kResTB][kResTB];           // [t][s], s <= t
-    alignas(16) f32x4 part[2][NH][kResTB][NTH];  // prediction / readout partials
-    alignas(16) float pr[2][NH][kResTB][DVT];  // their sums over the row groups
-    alignas(16) float u[NH][kResTB][DVT];      // residuals
+    alignas(16) f32x4 part[2][NH][X ? 1 : kResTB][X ? 1 : NTH];  // prediction / readout partials
+    alignas(16) float pr[2][NH][X ? 1 : kResTB][X ? 4 : DVT];  // their sums over the row groups
+    alignas(16) float u[NH][X ? 1 : kResTB][X ? 4 : DVT];      // residuals
     // the 2*kNP key-dim sums (padded to kNS) of each reduction unit: a
     // group's key-dim lanes, or at d 128 each of its two waves
     float sums[kResThreads / 16][kNS];
 };
 
-template <typename TIn, int D, int DVT, bool ISO>
+template <typename TIn, int D, int DVT, bool ISO, bool MM>
 __global__ __launch_bounds__(kResThreads) void kla_fwd_residual_kernel(FwdArgs p) {
-    typedef ResLayout<D, DVT> Ly;
+    typedef ResLayout<D, DVT, MM> Ly;
     constexpr int NVT = D / DVT;
     constexpr int TB = kResTB, NTH = Ly::NTH, NH = Ly::NH, VQ = Ly::VQ, RG = Ly::RG, RPT = Ly::RPT;
     constexpr int KW = Ly::KW;
     constexpr bool RED = D > 64;  // key dims of a head span two waves
     typedef typename Quad<TIn>::V QV;
-    __shared__ ResSm<D, DVT> sm;
+    __shared__ ResSm<D, DVT, MM> sm;
+    typedef Mma<TIn> MA;  // bf16 operands, or split bf16 pairs for fp32 inputs
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int grp = NH == 1 ? 0 : tid / NTH, lt = NH == 1 ? tid : tid % NTH;
@@ -142,12 +154,21 @@ __global__ __launch_bounds__(kResThreads) void kla_fwd_residual_kernel(FwdArgs p
     const TIn* v = (const TIn*)p.v;
     TIn* o = (TIn*)p.o;
 
-    // the thread's slice of the mean state
-    f32x4 M[RPT];
+    // the thread's slice of the mean state: RPT rows of one value quad, or
+    // (MM) D/16 accumulator tiles of the wave's 16 columns
+    constexpr int NM = MM ? D / 16 : RPT;
+    const int wcol = col0 + 16 * wave + (lane & 15);  // MM: the lane's value column
+    f32x4 M[NM];
 #pragma unroll
-    for (int m = 0; m < RPT; ++m) {
-        const size_t off = ((size_t)bh * D + i0 + m) * D + col0 + 4 * jq;
-        M[m] = p.eta0 ? *(const f32x4*)(p.eta0 + off) : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int m = 0; m < NM; ++m) {
+        if constexpr (MM) {
+#pragma unroll
+            for (int x4 = 0; x4 < 4; ++x4)
+                M[m][x4] = p.eta0 ? p.eta0[((size_t)bh * D + 16 * m + 4 * (lane >> 4) + x4) * D + wcol] : 0.f;
+        } else {
+            const size_t off = ((size_t)bh * D + i0 + m) * D + col0 + 4 * jq;
+            M[m] = p.eta0 ? *(const f32x4*)(p.eta0 + off) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
     }
     float l;  // precision of key dim kdim (diag) or of the head (iso)
     if constexpr (!ISO) l = p.l0 ? p.l0[(size_t)bh * D + kdim] : 1.f;
@@ -306,7 +327,8 @@ __global__ __launch_bounds__(kResThreads) void kla_fwd_residual_kernel(FwdArgs p
                 for (int w = u + 1; w < TB; ++w)
                     if (w < nb) after *= dec[w];
                 const float gu = (ISO ? P.kf[u] * scale[u] : P.c[u]) * inv[u];
-                sm.e[c][grp][u][lt] = after * gu;
+                if constexpr (MM) sm.e[c][grp][lt][u] = after * gu;
+                else sm.e[c][grp][u][lt] = after * gu;
                 sm.kt[c][grp][u][lt] = cum[u] * P.kf[u];
                 sm.qt[c][grp][u][lt] = cum[u] * P.qf[u];
             }
@@ -346,75 +368,126 @@ __global__ __launch_bounds__(kResThreads) void kla_fwd_residual_kernel(FwdArgs p
         const int nbn = more ? (p.T - t0 - TB < TB ? p.T - t0 - TB : TB) : 0;
         Raw x;
         load(more ? t0 + TB : t0, x);
-        // (1) partial predictions and readouts of the block's tokens against M0
+        if constexpr (MM) {
+            // (1) predictions (slots 0-3: G_t k_t) and readouts (slots 4-7:
+            // G_t q_t) of the block's tokens against M0, over the key-dim tiles
+            const int slot = lane & 15, kq = lane >> 4;
+            const float* arow = slot < 4 ? &sm.kt[c][0][slot][0] : &sm.qt[c][0][slot & 3][0];
+            f32x4 po = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int u = 0; u < TB; ++u) {
-            if (u < nb) {
-                f32x4 ap = {0.f, 0.f, 0.f, 0.f}, ao = {0.f, 0.f, 0.f, 0.f};
+            for (int rt = 0; rt < D / 16; ++rt) {
+                const f32x4 av = slot < 8 ? *(const f32x4*)(arow + 16 * rt + 4 * kq) : f32x4{0.f, 0.f, 0.f, 0.f};
+                po = MA::mma16(MA::from_acc(av), MA::from_acc(M[rt]), po);
+            }
+            // (2) residuals and outputs: lane j < 16 of the wave solves column
+            // 16 wave + j (predictions in its rows 0-3, readouts in lane j+16)
+            float o0[TB];
 #pragma unroll
-                for (int m4 = 0; m4 < RPT; m4 += 4) {
-                    const f32x4 kv = *(const f32x4*)&sm.kt[c][grp][u][i0 + m4];
-                    const f32x4 qv = *(const f32x4*)&sm.qt[c][grp][u][i0 + m4];
+            for (int e = 0; e < TB; ++e) o0[e] = __shfl(po[e], lane + 16, 64);
+            f32x4 uv = {0.f, 0.f, 0.f, 0.f};
+            if (lane < 16) {
 #pragma unroll
-                    for (int x4 = 0; x4 < 4; ++x4) {
-                        ap += kv[x4] * M[m4 + x4];
-                        ao += qv[x4] * M[m4 + x4];
+                for (int t = 0; t < TB; ++t) {
+                    if (t < nb) {
+                        float ut = sm.v[c][0][t][16 * wave + lane] - po[t];
+#pragma unroll
+                        for (int s2 = 0; s2 < t; ++s2) ut -= sm.A[c][0][t][s2] * uv[s2];
+                        uv[t] = ut;
+                        float ot = o0[t];
+#pragma unroll
+                        for (int s2 = 0; s2 <= t; ++s2) ot += sm.C[c][0][t][s2] * uv[s2];
+                        if (valid) o[(row0 + t0 + t) * D + wcol] = (TIn)ot;
                     }
                 }
-                sm.part[0][grp][u][lt] = ap;
-                sm.part[1][grp][u][lt] = ao;
             }
-        }
-        // (2) the next block's key-dim sums
-        settle(x);
-        Pre P;
-        if (more) pre(x, nbn, P);
-        lds_barrier();
-        // (4) sums over the row groups; the next block's coefficients
-        for (int w = lt; w < 2 * nb * VQ; w += NTH) {
-            const int kind = w / (nb * VQ), rem = w % (nb * VQ), u = rem / VQ, j4 = rem % VQ;
-            f32x4 s = sm.part[kind][grp][u][j4];
+            // (3) the state at the block's end: M = G_end (.) M + E U, with E
+            // (key dims x tokens) the A operand and the residuals the B operand
+            const auto ub = MA::from_acc(uv);
 #pragma unroll
-            for (int r2 = 1; r2 < RG; ++r2) s += sm.part[kind][grp][u][r2 * VQ + j4];
-            *(f32x4*)&sm.pr[kind][grp][u][4 * j4] = s;
-        }
-        if (more) finish(x, nbn, P, c ^ 1);
-        lds_barrier();
-        // (6) residuals and outputs, one thread per value quad
-        if (lt < VQ) {
-            f32x4 us[TB];
-#pragma unroll
-            for (int t = 0; t < TB; ++t) {
-                if (t < nb) {
-                    f32x4 ut = *(const f32x4*)&sm.v[c][grp][t][4 * lt] - *(const f32x4*)&sm.pr[0][grp][t][4 * lt];
-#pragma unroll
-                    for (int s = 0; s < t; ++s) ut -= sm.A[c][grp][t][s] * us[s];
-                    us[t] = ut;
-                    f32x4 ot = *(const f32x4*)&sm.pr[1][grp][t][4 * lt];
-#pragma unroll
-                    for (int s = 0; s <= t; ++s) ot += sm.C[c][grp][t][s] * us[s];
-                    *(f32x4*)&sm.u[grp][t][4 * lt] = ut;
-                    if (valid) *(QV*)(o + (row0 + t0 + t) * D + col0 + 4 * lt) = Quad<TIn>::make(ot);
+            for (int rt = 0; rt < D / 16; ++rt) {
+                const f32x4 gv = *(const f32x4*)&sm.gn[c][0][16 * rt + 4 * kq];
+                M[rt] *= gv;
+                const f32x4 ev = lane < 16 ? *(const f32x4*)&sm.e[c][0][16 * rt + slot][0] : f32x4{0.f, 0.f, 0.f, 0.f};
+                M[rt] = MA::mma16(MA::from_acc(ev), ub, M[rt]);
+            }
+            // (4) the next block's coefficients
+            settle(x);
+            Pre P;
+            if (more) pre(x, nbn, P);
+            lds_barrier();
+            if (more) finish(x, nbn, P, c ^ 1);
+            lds_barrier();
+        } else {
+            // (1) partial predictions and readouts of the block's tokens against M0
+    #pragma unroll
+            for (int u = 0; u < TB; ++u) {
+                if (u < nb) {
+                    f32x4 ap = {0.f, 0.f, 0.f, 0.f}, ao = {0.f, 0.f, 0.f, 0.f};
+    #pragma unroll
+                    for (int m4 = 0; m4 < RPT; m4 += 4) {
+                        const f32x4 kv = *(const f32x4*)&sm.kt[c][grp][u][i0 + m4];
+                        const f32x4 qv = *(const f32x4*)&sm.qt[c][grp][u][i0 + m4];
+    #pragma unroll
+                        for (int x4 = 0; x4 < 4; ++x4) {
+                            ap += kv[x4] * M[m4 + x4];
+                            ao += qv[x4] * M[m4 + x4];
+                        }
+                    }
+                    sm.part[0][grp][u][lt] = ap;
+                    sm.part[1][grp][u][lt] = ao;
                 }
             }
-        }
-        lds_barrier();
-        // (8) the state at the block's end
-#pragma unroll
-        for (int m4 = 0; m4 < RPT; m4 += 4) {
-            const f32x4 gv = *(const f32x4*)&sm.gn[c][grp][i0 + m4];
-#pragma unroll
-            for (int x4 = 0; x4 < 4; ++x4) M[m4 + x4] *= gv[x4];
-        }
-#pragma unroll
-        for (int u = 0; u < TB; ++u) {
-            if (u < nb) {
-                const f32x4 uu = *(const f32x4*)&sm.u[grp][u][4 * jq];
-#pragma unroll
-                for (int m4 = 0; m4 < RPT; m4 += 4) {
-                    const f32x4 ev = *(const f32x4*)&sm.e[c][grp][u][i0 + m4];
-#pragma unroll
-                    for (int x4 = 0; x4 < 4; ++x4) M[m4 + x4] += ev[x4] * uu;
+            // (2) the next block's key-dim sums
+            settle(x);
+            Pre P;
+            if (more) pre(x, nbn, P);
+            lds_barrier();
+            // (4) sums over the row groups; the next block's coefficients
+            for (int w = lt; w < 2 * nb * VQ; w += NTH) {
+                const int kind = w / (nb * VQ), rem = w % (nb * VQ), u = rem / VQ, j4 = rem % VQ;
+                f32x4 s = sm.part[kind][grp][u][j4];
+    #pragma unroll
+                for (int r2 = 1; r2 < RG; ++r2) s += sm.part[kind][grp][u][r2 * VQ + j4];
+                *(f32x4*)&sm.pr[kind][grp][u][4 * j4] = s;
+            }
+            if (more) finish(x, nbn, P, c ^ 1);
+            lds_barrier();
+            // (6) residuals and outputs, one thread per value quad
+            if (lt < VQ) {
+                f32x4 us[TB];
+    #pragma unroll
+                for (int t = 0; t < TB; ++t) {
+                    if (t < nb) {
+                        f32x4 ut = *(const f32x4*)&sm.v[c][grp][t][4 * lt] - *(const f32x4*)&sm.pr[0][grp][t][4 * lt];
+    #pragma unroll
+                        for (int s = 0; s < t; ++s) ut -= sm.A[c][grp][t][s] * us[s];
+                        us[t] = ut;
+                        f32x4 ot = *(const f32x4*)&sm.pr[1][grp][t][4 * lt];
+    #pragma unroll
+                        for (int s = 0; s <= t; ++s) ot += sm.C[c][grp][t][s] * us[s];
+                        *(f32x4*)&sm.u[grp][t][4 * lt] = ut;
+                        if (valid) *(QV*)(o + (row0 + t0 + t) * D + col0 + 4 * lt) = Quad<TIn>::make(ot);
+                    }
+                }
+            }
+            lds_barrier();
+            // (8) the state at the block's end
+    #pragma unroll
+            for (int m4 = 0; m4 < RPT; m4 += 4) {
+                const f32x4 gv = *(const f32x4*)&sm.gn[c][grp][i0 + m4];
+    #pragma unroll
+                for (int x4 = 0; x4 < 4; ++x4) M[m4 + x4] *= gv[x4];
+            }
+    #pragma unroll
+            for (int u = 0; u < TB; ++u) {
+                if (u < nb) {
+                    const f32x4 uu = *(const f32x4*)&sm.u[grp][u][4 * jq];
+    #pragma unroll
+                    for (int m4 = 0; m4 < RPT; m4 += 4) {
+                        const f32x4 ev = *(const f32x4*)&sm.e[c][grp][u][i0 + m4];
+    #pragma unroll
+                        for (int x4 = 0; x4 < 4; ++x4) M[m4 + x4] += ev[x4] * uu;
+                    }
                 }
             }
         }
@@ -422,7 +495,15 @@ __global__ __launch_bounds__(kResThreads) void kla_fwd_residual_kernel(FwdArgs p
     if (!valid) return;
     if (p.etaT) {
 #pragma unroll
-        for (int m = 0; m < RPT; ++m) *(f32x4*)(p.etaT + ((size_t)bh * D + i0 + m) * D + col0 + 4 * jq) = M[m];
+        for (int m = 0; m < NM; ++m) {
+            if constexpr (MM) {
+#pragma unroll
+                for (int x4 = 0; x4 < 4; ++x4)
+                    p.etaT[((size_t)bh * D + 16 * m + 4 * (lane >> 4) + x4) * D + wcol] = M[m][x4];
+            } else {
+                *(f32x4*)(p.etaT + ((size_t)bh * D + i0 + m) * D + col0 + 4 * jq) = M[m];
+            }
+        }
     }
     if (p.lT && vt == 0) {
         if constexpr (!ISO) {
@@ -433,23 +514,38 @@ __global__ __launch_bounds__(kResThreads) void kla_fwd_residual_kernel(FwdArgs p
     }
 }
 
-template <typename TIn, int D, int DVT, bool ISO>
+template <typename TIn, int D, int DVT, bool ISO, bool MM = false>
 void launch(const FwdArgs& a, hipStream_t s) {
-    typedef ResLayout<D, DVT> Ly;
+    typedef ResLayout<D, DVT, MM> Ly;
     const int nbh = a.B * a.H, ngroups = (nbh + Ly::NH - 1) / Ly::NH;
     constexpr int NVT = D / DVT;
     const dim3 grid((unsigned)(NVT == 1 ? ngroups : (ngroups + 7) / 8 * 8 * NVT));
-    hipLaunchKernelGGL((kla_fwd_residual_kernel<TIn, D, DVT, ISO>), grid, dim3(kResThreads), 0, s, a);
+    hipLaunchKernelGGL((kla_fwd_residual_kernel<TIn, D, DVT, ISO, MM>), grid, dim3(kResThreads), 0, s, a);
+}
+
+// KLA_RES_MM=0 keeps 64-column tiles on the thread-row layout.
+bool res_mm() {
+    const char* env = getenv("KLA_RES_MM");
+    return !(env && env[0] == '0');
 }
 
 template <typename TIn, bool ISO>
 hipError_t dispatch(const FwdArgs& a, hipStream_t s) {
     const int nvt = a.n_vtiles;
+    const bool mm = res_mm();  // matrix-core layout for 64-column tiles
     switch (a.dk) {
         case 16: launch<TIn, 16, 16, ISO>(a, s); break;
         case 32: launch<TIn, 32, 32, ISO>(a, s); break;
-        case 64: nvt == 2 ? launch<TIn, 64, 32, ISO>(a, s) : launch<TIn, 64, 64, ISO>(a, s); break;
-        case 128: nvt == 2 ? launch<TIn, 128, 64, ISO>(a, s) : launch<TIn, 128, 128, ISO>(a, s); break;
+        case 64:
+            if (nvt == 2) launch<TIn, 64, 32, ISO>(a, s);
+            else if (mm) launch<TIn, 64, 64, ISO, true>(a, s);
+            else launch<TIn, 64, 64, ISO>(a, s);
+            break;
+        case 128:
+            if (nvt == 2 && mm) launch<TIn, 128, 64, ISO, true>(a, s);
+            else if (nvt == 2) launch<TIn, 128, 64, ISO>(a, s);
+            else launch<TIn, 128, 128, ISO>(a, s);
+            break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -465,6 +561,11 @@ int fwd_residual_vtiles(int B, int H, int dk) {
     // two value tiles for d 64 / 128 while there are fewer (b,h) than about
     // two workgroups per CU
     const long long nbh = (long long)B * H;
+    // 64-column tiles on the matrix cores: the whole head at d 64; two tiles
+    // at d 128 while there are fewer (b,h) than about two workgroups per CU
+    // (beyond that the second tile's repeated key-dim sums cost more than
+    // the matrix cores save)
+    if (res_mm()) return dk == 128 ? (nbh < 512 ? 2 : 1) : 1;
     return dk >= 64 && nbh < 512 ? 2 : 1;
 }
 

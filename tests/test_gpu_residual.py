@@ -74,7 +74,9 @@ def test_residual_empty_sequence_passes_state(cov):
 
 
 def test_residual_split_handoff():
-    """Two calls, the second continuing from the first's state, equal one call."""
+    """Two calls, the second continuing from the first's state, equal one call
+    within the fp32 parity bar (the matrix-core layout rounds its split bf16
+    products differently when the block boundaries move)."""
     _print_case("handoff")
     inp = gen.make_inputs("small_diag", seed=8, B=2, H=2, T=50, dk=64, dv=64, dtype="f32")
     full = run_hip_res(inp, "diag")
@@ -84,8 +86,10 @@ def test_residual_split_handoff():
     second = run_hip_res(b, "diag", torch.from_numpy(first["lT"]).float(),
                          torch.from_numpy(first["etaT"]).float())
     cat = np.concatenate([first["o"], second["o"]], axis=2)
-    assert float(np.abs(cat - full["o"]).max() / np.abs(full["o"]).max()) < 1e-5
-    assert float(np.abs(second["etaT"] - full["etaT"]).max() / np.abs(full["etaT"]).max()) < 1e-5
+    eo = float(np.abs(cat - full["o"]).max() / np.abs(full["o"]).max())
+    em = float(np.abs(second["etaT"] - full["etaT"]).max() / np.abs(full["etaT"]).max())
+    print("handoff differences", eo, em)
+    assert eo < 1e-4 and em < 1e-4, (eo, em)
 
 
 RES_SAMPLES = [(0, 0), (3, 7), (7, 15)]
@@ -153,3 +157,43 @@ def test_residual_adversarial_gates(cov, dtype):
         assert np.all(np.isfinite(hip[k])), k
     ref = run_oracle_res(inp, cov)
     assert_parity(compare(hip, ref), dtype, f"residual adversarial {cov}")
+
+
+@pytest.mark.parametrize("cov", ["diag", "iso"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_residual_thread_row_layout(cov, d, monkeypatch):
+    """KLA_RES_MM=0: 64-column tiles on the thread-row layout instead of the
+    matrix cores (the layout d 16 / 32 always use)."""
+    _print_case("thread rows", cov, d)
+    monkeypatch.setenv("KLA_RES_MM", "0")
+    base = "small_diag" if cov == "diag" else "iso"
+    inp = gen.make_inputs(base, seed=130 + d, B=2, H=3, T=22, dk=d, dv=d, dtype="f32")
+    st = gen.make_state(inp["workload"], seed=21)
+    hip = run_hip_res(inp, cov, st["l0"], st["eta0"])
+    ref = run_oracle_res(inp, cov, st["l0"], st["eta0"])
+    assert_parity(compare(hip, ref), "f32", f"residual thread rows {cov} d={d}")
+
+
+@pytest.mark.parametrize("cov", ["diag", "iso"])
+def test_residual_many_heads_d128(cov):
+    """512 (b,h) at d 128: one whole-head tile per workgroup (thread rows)."""
+    _print_case("many heads", cov)
+    base = "small_diag" if cov == "diag" else "iso"
+    inp = gen.make_inputs(base, seed=140, B=32, H=16, T=9, dk=128, dv=128, dtype="bf16")
+    hip = run_hip_res(inp, cov)
+    sel = [(0, 0), (13, 7), (31, 15)]
+    per_head = "qn" if cov == "diag" else None  # diag qn is [H, dk]; iso qn is per (b,h,t)
+    sub = {k: (v[[b for b, _ in sel], [h for _, h in sel]][None]
+               if isinstance(v, torch.Tensor) and k != per_head else v) for k, v in inp.items()}
+    outs = {"o": [], "lT": [], "etaT": []}
+    for n, (b, h) in enumerate(sel):
+        one = {k: (v[:, n:n + 1] if isinstance(v, torch.Tensor) and k != per_head else v)
+               for k, v in sub.items()}
+        if cov == "diag":
+            one["qn"] = inp["qn"][h:h + 1]
+        r = run_oracle_res(one, cov)
+        for k in outs:
+            outs[k].append(r[k][0, 0])
+    ref = {k: np.stack(v) for k, v in outs.items()}
+    got = {k: np.stack([hip[k][b, h] for b, h in sel]) for k in hip}
+    assert_parity(compare(got, ref, nlead=1), "bf16", f"residual many heads {cov}")
