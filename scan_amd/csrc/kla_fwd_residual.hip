@@ -109,8 +109,10 @@ struct ResSm {
     alignas(16) float e[2][NH][MM ? D : kResTB][MM ? kResTB : D];  // D(s,end) g_s ([i][s] for MM)
     alignas(16) float gn[2][NH][D];           // G_end
     alignas(16) float v[2][NH][kResTB][DVT];
-    float A[2][NH][kResTB][kResTB];           // [t][s], s < t
-    float C[2][NH][kResTB][kResTB];           // [t][s], s <= t
+    // rows written as f32x4 on the thread-row layout (scalar writes measured
+    // faster on the matrix-core layout)
+    alignas(MM ? 4 : 16) float A[2][NH][kResTB][kResTB];  // [t][s], s < t
+    alignas(MM ? 4 : 16) float C[2][NH][kResTB][kResTB];  // [t][s], s <= t
     alignas(16) f32x4 part[2][NH][X ? 1 : kResTB][X ? 1 : NTH];  // prediction / readout partials
     alignas(16) float pr[2][NH][X ? 1 : kResTB][X ? 4 : DVT];  // their sums over the row groups
     alignas(16) float u[NH][X ? 1 : kResTB][X ? 4 : DVT];      // residuals
@@ -335,15 +337,25 @@ __global__ __launch_bounds__(kResThreads) void kla_fwd_residual_kernel(FwdArgs p
             sm.gn[c][grp][lt] = gend;
         }
         if (lt == 0) {
+            static_assert(TB == 4, "rows of A and C are f32x4");
 #pragma unroll
             for (int t = 0; t < TB; ++t) {
+                f32x4 ar = {0.f, 0.f, 0.f, 0.f}, cr = {0.f, 0.f, 0.f, 0.f};
                 float dst = 1.f;
 #pragma unroll
                 for (int s = t; s >= 0; --s) {
                     if (s < t) dst *= dec[s + 1];
                     const float w = (ISO ? dst * scale[s] : 1.f) * inv[s];
-                    sm.A[c][grp][t][s] = s < t ? w * P.sum[pidx(t, s)] : 0.f;
-                    sm.C[c][grp][t][s] = w * P.sum[kNP + pidx(t, s)];
+                    ar[s] = s < t ? w * P.sum[pidx(t, s)] : 0.f;
+                    cr[s] = w * P.sum[kNP + pidx(t, s)];
+                    if constexpr (MM) {
+                        sm.A[c][grp][t][s] = ar[s];
+                        sm.C[c][grp][t][s] = cr[s];
+                    }
+                }
+                if constexpr (!MM) {
+                    *(f32x4*)&sm.A[c][grp][t][0] = ar;
+                    *(f32x4*)&sm.C[c][grp][t][0] = cr;
                 }
             }
         }
