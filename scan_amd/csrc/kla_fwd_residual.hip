@@ -45,6 +45,17 @@ constexpr int kNP = kResTB * (kResTB + 1) / 2;     // token pairs s <= t
 constexpr int kNS = 32;                            // 2*kNP sums, padded to a power of two
 __device__ __forceinline__ constexpr int pidx(int t, int s) { return t * (t + 1) / 2 + s; }
 
+// An f32x4 as the K16 operand of Mma<T>: bf16 by a vector conversion (two
+// values per instruction), split pairs for fp32.
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::K16 k16(f32x4 x) {
+    if constexpr (std::is_same<T, bf16>::value) {
+        return __builtin_bit_cast(s16x4, __builtin_convertvector(x, bf16x4));
+    } else {
+        return Mma<T>::from_acc(x);
+    }
+}
+
 // One exchange of the reduce-scatter over lane mask M of the N values a lane
 // still holds: the lane keeps the half chosen by its lane bit, sends the
 // other half to its partner and adds the partner's copy of the kept half
@@ -388,8 +399,10 @@ __global__ __launch_bounds__(kResThreads) void kla_fwd_residual_kernel(FwdArgs p
             f32x4 po = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int rt = 0; rt < D / 16; ++rt) {
-                const f32x4 av = slot < 8 ? *(const f32x4*)(arow + 16 * rt + 4 * kq) : f32x4{0.f, 0.f, 0.f, 0.f};
-                po = MA::mma16(MA::from_acc(av), MA::from_acc(M[rt]), po);
+                // read by every lane (no branch, so the reads run ahead), zero in slots 8-15
+                f32x4 av = *(const f32x4*)(arow + 16 * rt + 4 * kq);
+                if (slot >= 8) av = f32x4{0.f, 0.f, 0.f, 0.f};
+                po = MA::mma16(k16<TIn>(av), k16<TIn>(M[rt]), po);
             }
             // (2) residuals and outputs: lane j < 16 of the wave solves column
             // 16 wave + j (predictions in its rows 0-3, readouts in lane j+16)
@@ -414,13 +427,14 @@ __global__ __launch_bounds__(kResThreads) void kla_fwd_residual_kernel(FwdArgs p
             }
             // (3) the state at the block's end: M = G_end (.) M + E U, with E
             // (key dims x tokens) the A operand and the residuals the B operand
-            const auto ub = MA::from_acc(uv);
+            const auto ub = k16<TIn>(uv);
 #pragma unroll
             for (int rt = 0; rt < D / 16; ++rt) {
                 const f32x4 gv = *(const f32x4*)&sm.gn[c][0][16 * rt + 4 * kq];
                 M[rt] *= gv;
-                const f32x4 ev = lane < 16 ? *(const f32x4*)&sm.e[c][0][16 * rt + slot][0] : f32x4{0.f, 0.f, 0.f, 0.f};
-                M[rt] = MA::mma16(MA::from_acc(ev), ub, M[rt]);
+                f32x4 ev = *(const f32x4*)&sm.e[c][0][16 * rt + slot][0];
+                if (lane >= 16) ev = f32x4{0.f, 0.f, 0.f, 0.f};
+                M[rt] = MA::mma16(k16<TIn>(ev), ub, M[rt]);
             }
             // (4) the next block's coefficients
             settle(x);
