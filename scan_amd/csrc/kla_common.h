@@ -16,6 +16,19 @@ typedef short s16x4 __attribute__((__vector_size__(8)));
 typedef float f32x4 __attribute__((__vector_size__(16)));
 typedef float f32x2 __attribute__((__vector_size__(8)));
 
+// Four fp32 values rounded (RNE) to bf16 and packed, two per conversion
+// instruction (a two-element vector conversion maps to v_cvt_pk_bf16_f32;
+// element-wise casts of a four-element vector were emitted one value per
+// instruction plus a permute).
+__device__ __forceinline__ s16x4 pack_bf16x4(float x0, float x1, float x2, float x3) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    typedef unsigned u2 __attribute__((ext_vector_type(2)));
+    const b2 lo = __builtin_convertvector((f2){x0, x1}, b2);
+    const b2 hi = __builtin_convertvector((f2){x2, x3}, b2);
+    return __builtin_bit_cast(s16x4, (u2){__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)});
+}
+
 // A "K32 step" contracts 32 values of the shared dimension with one
 // 16x16 output tile; every lane holds 8 consecutive values of its row (A) or
 // column (B).  A "K16 step" holds 4.  Both operands of one step are loaded
@@ -38,10 +51,7 @@ struct Mma<bf16> {
     static __device__ __forceinline__ f32x4 mma16(K16 a, K16 b, f32x4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
     }
-    static __device__ __forceinline__ K16 from_acc(f32x4 x) {
-        bf16x4 h = {(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
-        return __builtin_bit_cast(s16x4, h);
-    }
+    static __device__ __forceinline__ K16 from_acc(f32x4 x) { return pack_bf16x4(x[0], x[1], x[2], x[3]); }
 };
 
 // fp32 operands run on the bf16 matrix cores as split pairs: x = hi + lo
@@ -185,7 +195,11 @@ template <> struct Pair<bf16> {
     typedef bf16x2 V;
     static __device__ __forceinline__ float lo(V v) { return (float)v[0]; }
     static __device__ __forceinline__ float hi(V v) { return (float)v[1]; }
-    static __device__ __forceinline__ V make(float a, float b) { V r = {(bf16)a, (bf16)b}; return r; }
+    static __device__ __forceinline__ V make(float a, float b) {
+        typedef float f2 __attribute__((ext_vector_type(2)));
+        typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+        return __builtin_bit_cast(V, __builtin_convertvector((f2){a, b}, b2));  // one v_cvt_pk_bf16_f32
+    }
     static __device__ __forceinline__ V zero() { V r = {(bf16)0.f, (bf16)0.f}; return r; }
 };
 template <> struct Pair<float> {
@@ -201,8 +215,7 @@ template <typename T> struct Quad;
 template <> struct Quad<bf16> {
     typedef bf16x4 V;
     static __device__ __forceinline__ V make(f32x4 x) {
-        V r = {(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
-        return r;
+        return __builtin_bit_cast(V, pack_bf16x4(x[0], x[1], x[2], x[3]));
     }
     static __device__ __forceinline__ f32x4 to_f32(V v) {
         return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
