@@ -21,14 +21,19 @@
 // A and C (20 key-dim sums per block) depend on the inputs only, so they are
 // formed for the next block while the current one runs.
 //
-// Layout as in the short-sequence kernel: the threads of a (b,h) keep M in
-// registers (row group rg, value quad jq), small heads share a workgroup.
-// Per block: (1) every thread forms its rows' partial predictions and
-// readouts against M0; barrier; (4) partials are summed over the row groups
-// (and the next block's coefficients are finished); barrier; (6) one thread
-// per value quad solves the 4x4 unit-lower-triangular system for the
-// residuals and writes the outputs; barrier; (8) every thread updates its
-// rows.
+// Two layouts of the state M, both in registers for the whole sequence:
+// - thread rows (d 16 / 32, and d 128 with many (b,h)), as in the
+//   short-sequence kernel: row group rg, value quad jq per thread, small
+//   heads sharing a workgroup.  Per block: (1) every thread forms its rows'
+//   partial predictions and readouts against M0; barrier; (4) partials are
+//   summed over the row groups (and the next block's coefficients are
+//   finished); barrier; (6) one thread per value quad solves the 4x4
+//   unit-lower-triangular system for the residuals and writes the outputs;
+//   barrier; (8) every thread updates its rows.
+// - matrix cores (MM: d 64, and d 128 with few (b,h), 64-column tiles): each
+//   wave keeps 16 columns as MFMA accumulator tiles; predictions, readouts
+//   and the update are MFMA passes within the wave (see ResLayout), with two
+//   barriers per block for the coefficient pipeline only.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>
