@@ -165,7 +165,15 @@ __global__ __launch_bounds__(kResThreads) void kla_fwd_residual_kernel(FwdArgs p
     const int col0 = vt * DVT;  // first value column of the tile
     const int jq = lt % VQ, rg = lt / VQ, i0 = rg * RPT;
     const bool kd = lt < D;  // key-dim lane
-    const int kdim = kd ? lt : D - 1;
+    // MM: every lane holds a key dim (lane lt: dim lt % D); waves 0 .. D/64-1
+    // form the key sums of the coefficient step and the next D/64 waves the
+    // query sums, so each set reduces half of the values
+    const int kdim = MM ? lt % D : kd ? lt : D - 1;
+    constexpr int NKW = D / 64 > 0 ? D / 64 : 1;  // MM: waves per key-dim set
+    const int role = MM ? wave / NKW : 0;          // MM: 0 key sums, 1 query sums, 2+ none
+    // MM: wave 3 stages the v rows and writes A and C (waves 0-1 write the
+    // per-key-dim coefficients); vlt is the lane's index for the v rows
+    const int vlt = MM ? (lt + 64) % NTH : lt;
     const size_t row0 = (size_t)bh * p.T;
     const TIn* q = (const TIn*)p.q;
     const TIn* k = (const TIn*)p.k;
@@ -214,8 +222,8 @@ __global__ __launch_bounds__(kResThreads) void kla_fwd_residual_kernel(FwdArgs p
                 x.qn[u] = p.qn[t];
             }
         }
-        const int uv = lt / VQ < nb ? lt / VQ : nb - 1;
-        x.vq = *(const QV*)(v + (row0 + t0 + uv) * D + col0 + 4 * jq);
+        const int uv = vlt / VQ < nb ? vlt / VQ : nb - 1;
+        x.vq = *(const QV*)(v + (row0 + t0 + uv) * D + col0 + 4 * (vlt % VQ));
     };
     auto settle = [&](Raw& x) {
 #pragma unroll
@@ -239,7 +247,7 @@ __global__ __launch_bounds__(kResThreads) void kla_fwd_residual_kernel(FwdArgs p
         float dec[TB];
 #pragma unroll
         for (int u = 0; u < TB; ++u) {
-            const bool on = u < nb && kd;
+            const bool on = u < nb && (MM || kd);
             P.kf[u] = on ? (float)x.k[u] : 0.f;
             P.qf[u] = on ? (float)x.q[u] : 0.f;
             dec[u] = u < nb ? x.a[u] : 1.f;
@@ -281,24 +289,47 @@ __global__ __launch_bounds__(kResThreads) void kla_fwd_residual_kernel(FwdArgs p
         // half.  After log2(kNS) halvings each lane holds one value summed
         // over 32 lanes (two values over 16 at KW = 16); a last full exchange
         // completes KW = 64.  The owners write the sums to LDS.
-        float w[kNS];
+        if constexpr (MM) {
+            // the wave's set of kNP sums, padded to 16; one value per 4 lanes
+            constexpr int NV = 16;
+            float w[NV];
 #pragma unroll
-        for (int j = 0; j < kNS; ++j) w[j] = j < 2 * kNP ? P.sum[j] : 0.f;
-        int base = 0;
-        reduce_scatter<kNS, KW / 2>(w, lane, base);
-        // owners: lane holds values base .. base+NOUT-1 of its unit
-        constexpr int NOUT = kNS / KW > 0 ? kNS / KW : 1;
-        const int unit = RED ? wave : grp;
-        const bool owner = kd && (KW < 64 || (lane & 1) == 0);
-        if (owner) {
+            for (int j = 0; j < NV; ++j) w[j] = j < kNP ? (role == 0 ? P.sum[j] : P.sum[kNP + j]) : 0.f;
+            int base = 0;
+            reduce_scatter<NV, 32>(w, lane, base);
+            if (role <= 1 && (lane & 3) == 0) sm.sums[wave][base] = w[0];
+        } else {
+            float w[kNS];
 #pragma unroll
-            for (int j = 0; j < NOUT; ++j) sm.sums[unit][base + j] = w[j];
+            for (int j = 0; j < kNS; ++j) w[j] = j < 2 * kNP ? P.sum[j] : 0.f;
+            int base = 0;
+            reduce_scatter<kNS, KW / 2>(w, lane, base);
+            // owners: lane holds values base .. base+NOUT-1 of its unit
+            constexpr int NOUT = kNS / KW > 0 ? kNS / KW : 1;
+            const int unit = RED ? wave : grp;
+            const bool owner = kd && (KW < 64 || (lane & 1) == 0);
+            if (owner) {
+#pragma unroll
+                for (int j = 0; j < NOUT; ++j) sm.sums[unit][base + j] = w[j];
+            }
         }
     };
     // Finish (after a barrier): the whole-head sums, the gains' divisors and
     // the coefficients of buffer c.
     auto finish = [&](const Raw& x, int nb, Pre& P, int c) {
-        if constexpr (RED) {
+        if constexpr (MM) {
+#pragma unroll
+            for (int j = 0; j < kNP; ++j) {
+                float sk = 0.f, sq = 0.f;
+#pragma unroll
+                for (int w = 0; w < NKW; ++w) {
+                    sk += sm.sums[w][j];
+                    sq += sm.sums[NKW + w][j];
+                }
+                P.sum[j] = sk;
+                P.sum[kNP + j] = sq;
+            }
+        } else if constexpr (RED) {
             // the head's key dims are the group's first two waves
             const int w0 = grp * (NTH / 64);
 #pragma unroll
@@ -352,7 +383,7 @@ __global__ __launch_bounds__(kResThreads) void kla_fwd_residual_kernel(FwdArgs p
             }
             sm.gn[c][grp][lt] = gend;
         }
-        if (lt == 0) {
+        if (lt == (MM ? NTH - 1 : 0)) {
             static_assert(TB == 4, "rows of A and C are f32x4");
 #pragma unroll
             for (int t = 0; t < TB; ++t) {
@@ -375,7 +406,7 @@ __global__ __launch_bounds__(kResThreads) void kla_fwd_residual_kernel(FwdArgs p
                 }
             }
         }
-        if (lt / VQ < nb) *(f32x4*)&sm.v[c][grp][lt / VQ][4 * jq] = Quad<TIn>::to_f32(x.vq);
+        if (vlt / VQ < nb) *(f32x4*)&sm.v[c][grp][vlt / VQ][4 * (vlt % VQ)] = Quad<TIn>::to_f32(x.vq);
     };
 
     {
