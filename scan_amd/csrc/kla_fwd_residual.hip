@@ -18,7 +18,7 @@
 //   o_t = O_t + sum_{s<=t} C[t][s] u_s,         O_t = (G_t q_t)^T M0
 //   M_end = G_end (.) M0 + sum_s (D(s,end) g_s) u_s^T
 // with A[t][s] = sum_i D(s,t)_i k_t,i g_s,i and C[t][s] = sum_i D(s,t)_i q_t,i g_s,i.
-// A and C (20 key-dim sums per block) depend on the inputs only, so they are
+// A and C (20 key-dim sums per four-token block, 72 per eight) depend on the inputs only, so they are
 // formed for the next block while the current one runs.
 //
 // Two layouts of the state M, both in registers for the whole sequence:
@@ -33,7 +33,8 @@
 // - matrix cores (MM: d 64, and d 128 with few (b,h), 64-column tiles): each
 //   wave keeps 16 columns as MFMA accumulator tiles; predictions, readouts
 //   and the update are MFMA passes within the wave (see ResLayout), with two
-//   barriers per block for the coefficient pipeline only.
+//   barriers per block for the coefficient pipeline only.  Blocks hold eight
+//   tokens at d 128 and four at d 64.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -45,9 +46,12 @@ namespace kla {
 namespace {
 
 constexpr int kResThreads = 256;
-constexpr int kResTB = 4;                          // tokens per block
-constexpr int kNP = kResTB * (kResTB + 1) / 2;     // token pairs s <= t
+constexpr int kResTB = 4;                          // tokens per block (thread rows)
+constexpr int kResTBM = 8;                         // tokens per block (matrix cores, d 128)
+constexpr int kNP = kResTB * (kResTB + 1) / 2;     // token pairs s <= t (thread rows)
 constexpr int kNS = 32;                            // 2*kNP sums, padded to a power of two
+template <bool MM, int D> constexpr int res_tb() { return MM && D >= 128 ? kResTBM : kResTB; }
+template <bool MM, int D> constexpr int res_np() { return res_tb<MM, D>() * (res_tb<MM, D>() + 1) / 2; }
 __device__ __forceinline__ constexpr int pidx(int t, int s) { return t * (t + 1) / 2 + s; }
 
 // An f32x4 as the K16 operand of Mma<T>: bf16 by a vector conversion (two
@@ -95,8 +99,8 @@ __device__ __forceinline__ void reduce_scatter(float* w, int lane, int& base) {
 // waves owns 16 value columns of the tile as D/16 accumulator tiles (lane l:
 // key dims 16 rt + 4 (l/16) + e, column l%16), which is also the B operand
 // of a 16-wide contraction over key dims.  The block's predictions and
-// readouts are then one pass of MFMAs per wave, with the block's G_t k_t and
-// G_t q_t stacked as 8 rows of the A operand, and the state update is a
+// readouts are then one pass of MFMAs per wave, with the block's eight G_t k_t
+// and eight G_t q_t stacked as the 16 rows of the A operand, and the state update is a
 // second pass with the residuals as the B operand: nothing is summed across
 // waves, and one barrier fewer is needed per block.
 template <int D, int DVT, bool MM>
@@ -108,7 +112,7 @@ struct ResLayout {
     static constexpr int RG = MM ? 1 : NTH / VQ;   // row groups of a (b,h)
     static constexpr int RPT = MM ? 4 : D / RG;    // rows per thread
     static constexpr int KW = D < 64 ? D : 64;     // key-dim lanes per wave
-    static_assert(RPT % 4 == 0 && kResTB * VQ <= NTH && NTH * NH == kResThreads && NTH % D == 0 &&
+    static_assert(RPT % 4 == 0 && res_tb<MM, D>() * VQ <= NTH && NTH * NH == kResThreads && NTH % D == 0 &&
                       (KW == 16 || KW == 32 || KW == 64) && (!MM || (DVT == 64 && D >= 64)),
                   "layout");
 };
@@ -120,28 +124,29 @@ template <int D, int DVT, bool MM>
 struct ResSm {
     static constexpr int NH = ResLayout<D, DVT, MM>::NH, NTH = ResLayout<D, DVT, MM>::NTH;
     static constexpr int X = MM ? 1 : 0;  // arrays only the thread-row layout uses shrink to one entry
-    alignas(16) float kt[2][NH][kResTB][D];   // G_t k_t
-    alignas(16) float qt[2][NH][kResTB][D];   // G_t q_t
-    alignas(16) float e[2][NH][MM ? D : kResTB][MM ? kResTB : D];  // D(s,end) g_s ([i][s] for MM)
+    static constexpr int TB = res_tb<MM, D>();
+    alignas(16) float kt[2][NH][TB][D];   // G_t k_t
+    alignas(16) float qt[2][NH][TB][D];   // G_t q_t
+    alignas(16) float e[2][NH][MM ? D : TB][MM ? TB : D];  // D(s,end) g_s ([i][s] for MM)
     alignas(16) float gn[2][NH][D];           // G_end
-    alignas(16) float v[2][NH][kResTB][DVT];
-    // rows written as f32x4 on the thread-row layout (scalar writes measured
-    // faster on the matrix-core layout)
-    alignas(MM ? 4 : 16) float A[2][NH][kResTB][kResTB];  // [t][s], s < t
-    alignas(MM ? 4 : 16) float C[2][NH][kResTB][kResTB];  // [t][s], s <= t
+    alignas(16) float v[2][NH][TB][DVT];
+    alignas(16) float A[2][NH][TB][TB];  // [t][s], s < t
+    alignas(16) float C[2][NH][TB][TB];  // [t][s], s <= t
     alignas(16) f32x4 part[2][NH][X ? 1 : kResTB][X ? 1 : NTH];  // prediction / readout partials
     alignas(16) float pr[2][NH][X ? 1 : kResTB][X ? 4 : DVT];  // their sums over the row groups
     alignas(16) float u[NH][X ? 1 : kResTB][X ? 4 : DVT];      // residuals
-    // the 2*kNP key-dim sums (padded to kNS) of each reduction unit: a
-    // group's key-dim lanes, or at d 128 each of its two waves
-    float sums[kResThreads / 16][kNS];
+    // the key-dim sums of each reduction unit: thread rows, 2*kNP (padded to
+    // kNS) per group's key-dim lanes or, at d 128, per wave; matrix cores,
+    // one set of NP sums per wave
+    float sums[kResThreads / 16][MM ? 40 : kNS];
 };
 
 template <typename TIn, int D, int DVT, bool ISO, bool MM>
 __global__ __launch_bounds__(kResThreads) void kla_fwd_residual_kernel(FwdArgs p) {
     typedef ResLayout<D, DVT, MM> Ly;
     constexpr int NVT = D / DVT;
-    constexpr int TB = kResTB, NTH = Ly::NTH, NH = Ly::NH, VQ = Ly::VQ, RG = Ly::RG, RPT = Ly::RPT;
+    constexpr int TB = res_tb<MM, D>(), NTH = Ly::NTH, NH = Ly::NH, VQ = Ly::VQ, RG = Ly::RG, RPT = Ly::RPT;
+    constexpr int NP = res_np<MM, D>();  // token pairs s <= t of a block
     constexpr int KW = Ly::KW;
     constexpr bool RED = D > 64;  // key dims of a head span two waves
     typedef typename Quad<TIn>::V QV;
@@ -171,8 +176,8 @@ __global__ __launch_bounds__(kResThreads) void kla_fwd_residual_kernel(FwdArgs p
     const int kdim = MM ? lt % D : kd ? lt : D - 1;
     constexpr int NKW = D / 64 > 0 ? D / 64 : 1;  // MM: waves per key-dim set
     const int role = MM ? wave / NKW : 0;          // MM: 0 key sums, 1 query sums, 2+ none
-    // MM: wave 3 stages the v rows and writes A and C (waves 0-1 write the
-    // per-key-dim coefficients); vlt is the lane's index for the v rows
+    // MM: waves 3 and 0 stage the v rows, wave 3 writes A and C (waves 0-1
+    // write the per-key-dim coefficients); vlt is the lane's index for the v rows
     const int vlt = MM ? (lt + 64) % NTH : lt;
     const size_t row0 = (size_t)bh * p.T;
     const TIn* q = (const TIn*)p.q;
@@ -236,12 +241,12 @@ __global__ __launch_bounds__(kResThreads) void kla_fwd_residual_kernel(FwdArgs p
 
     // ---- a block's coefficients, in two steps around a barrier
     // Pre: per key-dim lane, the block's gains up to their common divisor and
-    // the 20 key-dim sums (diag: k_t.D(s,t).k_s/lp_s and q_t.D(s,t).k_s/lp_s;
+    // the NP key and NP query sums (diag: k_t.D(s,t).k_s/lp_s and q_t.D(s,t).k_s/lp_s;
     // iso: k_t.k_s and q_t.k_s), reduced over the wave's key-dim lanes.
     struct Pre {
         float kf[TB], qf[TB], c[TB], cum[TB];  // k, q, k/lp (diag), G_t (diag)
         float lp[TB];                           // diag: predicted precision
-        float sum[2 * kNP];                     // [0,kNP): k-sums, [kNP,2kNP): q-sums
+        float sum[2 * NP];                      // [0,NP): k-sums, [NP,2NP): q-sums
     };
     auto pre = [&](const Raw& x, int nb, Pre& P) {
         float dec[TB];
@@ -271,7 +276,7 @@ __global__ __launch_bounds__(kResThreads) void kla_fwd_residual_kernel(FwdArgs p
                 for (int s = t; s >= 0; --s) {
                     if (s < t) dst *= dec[s + 1];
                     P.sum[pidx(t, s)] = dst * P.kf[t] * P.c[s];
-                    P.sum[kNP + pidx(t, s)] = dst * P.qf[t] * P.c[s];
+                    P.sum[NP + pidx(t, s)] = dst * P.qf[t] * P.c[s];
                 }
             }
         } else {
@@ -280,7 +285,7 @@ __global__ __launch_bounds__(kResThreads) void kla_fwd_residual_kernel(FwdArgs p
 #pragma unroll
                 for (int s = 0; s <= t; ++s) {
                     P.sum[pidx(t, s)] = P.kf[t] * P.kf[s];
-                    P.sum[kNP + pidx(t, s)] = P.qf[t] * P.kf[s];
+                    P.sum[NP + pidx(t, s)] = P.qf[t] * P.kf[s];
                 }
         }
         // Reduce-scatter over the KW key-dim lanes: at each exchange a lane
@@ -290,14 +295,26 @@ __global__ __launch_bounds__(kResThreads) void kla_fwd_residual_kernel(FwdArgs p
         // over 32 lanes (two values over 16 at KW = 16); a last full exchange
         // completes KW = 64.  The owners write the sums to LDS.
         if constexpr (MM) {
-            // the wave's set of kNP sums, padded to 16; one value per 4 lanes
-            constexpr int NV = 16;
+            // the wave's set of NP sums: up to 16 padded to 16 (one value per
+            // 4 lanes); 36 as 32 (one per 2 lanes) and 4 (one per 16 lanes)
+            constexpr int NV = NP <= 16 ? 16 : 32;
+            constexpr int NR = NP <= 16 ? 0 : 4;
+            static_assert(NP <= NV + NR, "sums per set");
             float w[NV];
 #pragma unroll
-            for (int j = 0; j < NV; ++j) w[j] = j < kNP ? (role == 0 ? P.sum[j] : P.sum[kNP + j]) : 0.f;
+            for (int j = 0; j < NV; ++j) w[j] = j < NP ? (role == 0 ? P.sum[j] : P.sum[NP + j]) : 0.f;
             int base = 0;
             reduce_scatter<NV, 32>(w, lane, base);
-            if (role <= 1 && (lane & 3) == 0) sm.sums[wave][base] = w[0];
+            if (role <= 1 && (lane & (64 / NV - 1)) == 0) sm.sums[wave][base] = w[0];
+            if constexpr (NR > 0) {
+                float w2[NR];
+#pragma unroll
+                for (int j = 0; j < NR; ++j)
+                    w2[j] = NV + j < NP ? (role == 0 ? P.sum[NV + j] : P.sum[NP + NV + j]) : 0.f;
+                int b2 = 0;
+                reduce_scatter<NR, 32>(w2, lane, b2);
+                if (role <= 1 && (lane & (64 / NR - 1)) == 0) sm.sums[wave][NV + b2] = w2[0];
+            }
         } else {
             float w[kNS];
 #pragma unroll
@@ -319,7 +336,7 @@ __global__ __launch_bounds__(kResThreads) void kla_fwd_residual_kernel(FwdArgs p
     auto finish = [&](const Raw& x, int nb, Pre& P, int c) {
         if constexpr (MM) {
 #pragma unroll
-            for (int j = 0; j < kNP; ++j) {
+            for (int j = 0; j < NP; ++j) {
                 float sk = 0.f, sq = 0.f;
 #pragma unroll
                 for (int w = 0; w < NKW; ++w) {
@@ -327,7 +344,7 @@ __global__ __launch_bounds__(kResThreads) void kla_fwd_residual_kernel(FwdArgs p
                     sq += sm.sums[NKW + w][j];
                 }
                 P.sum[j] = sk;
-                P.sum[kNP + j] = sq;
+                P.sum[NP + j] = sq;
             }
         } else if constexpr (RED) {
             // the head's key dims are the group's first two waves
@@ -384,25 +401,27 @@ __global__ __launch_bounds__(kResThreads) void kla_fwd_residual_kernel(FwdArgs p
             sm.gn[c][grp][lt] = gend;
         }
         if (lt == (MM ? NTH - 1 : 0)) {
-            static_assert(TB == 4, "rows of A and C are f32x4");
+            static_assert(TB % 4 == 0, "rows of A and C are written as f32x4 pieces");
 #pragma unroll
             for (int t = 0; t < TB; ++t) {
-                f32x4 ar = {0.f, 0.f, 0.f, 0.f}, cr = {0.f, 0.f, 0.f, 0.f};
+                float ar[TB], cr[TB];
                 float dst = 1.f;
 #pragma unroll
-                for (int s = t; s >= 0; --s) {
+                for (int s = TB - 1; s >= 0; --s) {
+                    if (s > t) {
+                        ar[s] = 0.f;
+                        cr[s] = 0.f;
+                        continue;
+                    }
                     if (s < t) dst *= dec[s + 1];
                     const float w = (ISO ? dst * scale[s] : 1.f) * inv[s];
                     ar[s] = s < t ? w * P.sum[pidx(t, s)] : 0.f;
-                    cr[s] = w * P.sum[kNP + pidx(t, s)];
-                    if constexpr (MM) {
-                        sm.A[c][grp][t][s] = ar[s];
-                        sm.C[c][grp][t][s] = cr[s];
-                    }
+                    cr[s] = w * P.sum[NP + pidx(t, s)];
                 }
-                if constexpr (!MM) {
-                    *(f32x4*)&sm.A[c][grp][t][0] = ar;
-                    *(f32x4*)&sm.C[c][grp][t][0] = cr;
+#pragma unroll
+                for (int s4 = 0; s4 < TB; s4 += 4) {
+                    *(f32x4*)&sm.A[c][grp][t][s4] = f32x4{ar[s4], ar[s4 + 1], ar[s4 + 2], ar[s4 + 3]};
+                    *(f32x4*)&sm.C[c][grp][t][s4] = f32x4{cr[s4], cr[s4 + 1], cr[s4 + 2], cr[s4 + 3]};
                 }
             }
         }
@@ -428,29 +447,36 @@ __global__ __launch_bounds__(kResThreads) void kla_fwd_residual_kernel(FwdArgs p
         Raw x;
         load(more ? t0 + TB : t0, x);
         if constexpr (MM) {
-            // (1) predictions (slots 0-3: G_t k_t) and readouts (slots 4-7:
-            // G_t q_t) of the block's tokens against M0, over the key-dim tiles
+            // (1) predictions (slots 0 .. TB-1: G_t k_t) and readouts (slots
+            // TB .. 2TB-1: G_t q_t) of the block's tokens against M0, over the
+            // key-dim tiles
             const int slot = lane & 15, kq = lane >> 4;
-            const float* arow = slot < 4 ? &sm.kt[c][0][slot][0] : &sm.qt[c][0][slot & 3][0];
+            const float* arow = slot < TB ? &sm.kt[c][0][slot][0] : &sm.qt[c][0][(slot - TB) & (TB - 1)][0];
             f32x4 po = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int rt = 0; rt < D / 16; ++rt) {
-                // read by every lane (no branch, so the reads run ahead), zero in slots 8-15
+                // read by every lane (no branch, so the reads run ahead), zero in unused slots
                 f32x4 av = *(const f32x4*)(arow + 16 * rt + 4 * kq);
-                if (slot >= 8) av = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (slot >= 2 * TB) av = f32x4{0.f, 0.f, 0.f, 0.f};
                 po = MA::mma16(k16<TIn>(av), k16<TIn>(M[rt]), po);
             }
             // (2) residuals and outputs: lane j < 16 of the wave solves column
-            // 16 wave + j (predictions in its rows 0-3, readouts in lane j+16)
-            float o0[TB];
+            // 16 wave + j; row r of the product sits in lane j + 16 (r/4),
+            // element r%4
+            float pt[TB], o0[TB];
 #pragma unroll
-            for (int e = 0; e < TB; ++e) o0[e] = __shfl(po[e], lane + 16, 64);
-            f32x4 uv = {0.f, 0.f, 0.f, 0.f};
+            for (int t = 0; t < TB; ++t) {
+                pt[t] = t < 4 ? po[t] : __shfl(po[t % 4], lane + 16 * (t / 4), 64);
+                o0[t] = __shfl(po[(TB + t) % 4], lane + 16 * ((TB + t) / 4), 64);
+            }
+            float uv[TB];
+#pragma unroll
+            for (int t = 0; t < TB; ++t) uv[t] = 0.f;
             if (lane < 16) {
 #pragma unroll
                 for (int t = 0; t < TB; ++t) {
                     if (t < nb) {
-                        float ut = sm.v[c][0][t][16 * wave + lane] - po[t];
+                        float ut = sm.v[c][0][t][16 * wave + lane] - pt[t];
 #pragma unroll
                         for (int s2 = 0; s2 < t; ++s2) ut -= sm.A[c][0][t][s2] * uv[s2];
                         uv[t] = ut;
@@ -462,14 +488,23 @@ __global__ __launch_bounds__(kResThreads) void kla_fwd_residual_kernel(FwdArgs p
                 }
             }
             // (3) the state at the block's end: M = G_end (.) M + E U, with E
-            // (key dims x tokens) the A operand and the residuals the B operand
-            const auto ub = k16<TIn>(uv);
+            // (key dims x tokens) the A operand and the residuals the B
+            // operand (tokens 4 kq .. 4 kq + 3 in lanes 16 kq .. 16 kq + 15)
+            f32x4 uq = {uv[0], uv[1], uv[2], uv[3]};
+            if constexpr (TB == 8) {
+                f32x4 hi;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) hi[e] = __shfl(uv[4 + e], (lane + 48) & 63, 64);
+                if (lane >= 16) uq = hi;
+                if (lane >= 32) uq = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+            const auto ub = k16<TIn>(uq);
 #pragma unroll
             for (int rt = 0; rt < D / 16; ++rt) {
                 const f32x4 gv = *(const f32x4*)&sm.gn[c][0][16 * rt + 4 * kq];
                 M[rt] *= gv;
-                f32x4 ev = *(const f32x4*)&sm.e[c][0][16 * rt + slot][0];
-                if (lane >= 16) ev = f32x4{0.f, 0.f, 0.f, 0.f};
+                f32x4 ev = *(const f32x4*)&sm.e[c][0][16 * rt + slot][4 * (kq & (TB / 4 - 1))];
+                if (kq >= TB / 4) ev = f32x4{0.f, 0.f, 0.f, 0.f};
                 M[rt] = MA::mma16(k16<TIn>(ev), ub, M[rt]);
             }
             // (4) the next block's coefficients
