@@ -37,9 +37,10 @@ def run_oracle_res(inp, cov, l0=None, m0=None):
 @pytest.mark.parametrize("cov", ["diag", "iso"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("d", [16, 32, 64, 128])
-@pytest.mark.parametrize("T", [1, 3, 4, 9, 70])
+@pytest.mark.parametrize("T", [1, 3, 4, 8, 9, 16, 17, 70])
 def test_residual_parity(cov, dtype, d, T):
-    """Blocks of four with a ragged last block, from a cached state."""
+    """Blocks of four tokens (eight on the matrix-core layout at d 128), whole
+    or with a ragged last block, from a cached state."""
     _print_case(cov, dtype, d, T)
     base = "small_diag" if cov == "diag" else "iso"
     inp = gen.make_inputs(base, seed=90 + T + d, B=3, H=2, T=T, dk=d, dv=d, dtype=dtype)
