@@ -2,14 +2,17 @@
 """KLA forward benchmark on one MI355X.
 
 One step = one klaFwd over the whole batch of the workload (all heads, all
-tokens), inputs resident in HBM.  Default workload: the LM layer at
-1.3B-like width, B=8 H=16 T=2048 dk=dv=128, bf16 q/k/v/o, fp32 state.
+tokens), inputs resident in HBM.  Default workload: the largest single-GPU
+configuration, long context B=1 H=16 T=32768 dk=dv=128, bf16 q/k/v/o, fp32
+state, slow decay.
 
-Prints ONE JSON line with tokens/s, the roofline of the forward kernel
-(algorithmic HBM bytes / measured kernel time against 8 TB/s), and the fp64
-oracle timed on the host cores over a bounded sample of the same workload.
+Prints ONE JSON line with tokens/s, the roofline of the forward (algorithmic
+HBM bytes / measured GPU time against 8 TB/s, and against a device copy of
+the same byte count measured in the same process), the algorithmic matrix
+flops against the MFMA peak of the input dtype, and the fp64 oracle timed on
+the host cores over a bounded sample of the same workload.
 
-  python bench.py [--steps K] [--warmup W] [--workload lm_diag] [--no-cpu]
+  python bench.py [--steps K] [--warmup W] [--workload long_diag] [--no-cpu]
 """
 from __future__ import annotations
 
@@ -26,19 +29,25 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# dense matrix-core peaks of MI355X (TFLOP/s), by the dtype of q, k, v
+MFMA_PEAK_TFS = {"bf16": 2500.0, "f32": 157.3}
+# the last-level cache (MALL) the timed steps must not reuse between steps
+MALL_BYTES = 256 << 20
 
 # Kernel sources whose hash keys the stored HBM-traffic counters: the counters
 # are reported only while the kernel they were taken on is unchanged.
+# Every family also hashes the dispatch (kla_api.cpp: kernel choice, tiles,
+# segments), the shared headers and the build flags.
+_COMMON_SOURCES = ["scan_amd/csrc/kla_api.cpp", "scan_amd/csrc/kla_common.h",
+                   "scan_amd/csrc/kla_internal.h", "scan_amd/build.py"]
 KERNEL_SOURCES = {
     "diag": ["scan_amd/csrc/kla_fwd_diag_pipe.hip", "scan_amd/csrc/kla_fwd_diag.hip",
-             "scan_amd/csrc/kla_fwd_seg.hip", "scan_amd/csrc/kla_common.h",
-             "scan_amd/csrc/kla_internal.h"],
-    "iso": ["scan_amd/csrc/kla_fwd_iso_pipe.hip", "scan_amd/csrc/kla_fwd_iso.hip",
-            "scan_amd/csrc/kla_common.h", "scan_amd/csrc/kla_internal.h"],
-    "short": ["scan_amd/csrc/kla_fwd_short.hip", "scan_amd/csrc/kla_short.h",
-              "scan_amd/csrc/kla_common.h", "scan_amd/csrc/kla_internal.h"],
-    "residual": ["scan_amd/csrc/kla_fwd_residual.hip", "scan_amd/csrc/kla_residual.h",
-                 "scan_amd/csrc/kla_common.h", "scan_amd/csrc/kla_internal.h"],
+             "scan_amd/csrc/kla_fwd_seg.hip"] + _COMMON_SOURCES,
+    "iso": ["scan_amd/csrc/kla_fwd_iso_pipe.hip", "scan_amd/csrc/kla_fwd_iso.hip"] + _COMMON_SOURCES,
+    "short": ["scan_amd/csrc/kla_fwd_short.hip", "scan_amd/csrc/kla_short.h"] + _COMMON_SOURCES,
+    "residual": ["scan_amd/csrc/kla_fwd_residual.hip",
+                 "scan_amd/csrc/kla_residual.h"] + _COMMON_SOURCES,
+    "step": ["scan_amd/csrc/kla_step.hip"] + _COMMON_SOURCES,
 }
 
 
@@ -50,21 +59,60 @@ def kernel_hash(cov: str) -> str:
     return h.hexdigest()[:16]
 
 
-def stored_traffic(workload: str, cov: str):
-    """HBM bytes per launch from the committed rocprofv3 --pmc summary of this
-    workload (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy of known size),
-    or None when there is none or the kernel sources changed since."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.md")
+def _stored_record(kind: str, workload: str, cov: str):
+    path = os.path.join(ROOT, "profiles", f"{kind}_{workload}.md")
     if not os.path.exists(path):
         return None
     with open(path) as f:
-        m = re.search(r"^traffic_json: (\{.*\})$", f.read(), re.M)
+        m = re.search(r"^%s_json: (\{.*\})$" % kind, f.read(), re.M)
     if not m:
         return None
     rec = json.loads(m.group(1))
     if rec.get("kernel_hash") != kernel_hash(cov):
         return None
     return rec
+
+
+def stored_traffic(workload: str, cov: str):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary of this
+    workload (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy of known size),
+    or None when there is none or the kernel sources changed since."""
+    return _stored_record("traffic", workload, cov)
+
+
+def stored_counters(workload: str, cov: str):
+    """Matrix-core and VALU counters of the forward from the committed
+    rocprofv3 --pmc summary of this workload (MFMA busy cycles over the
+    shader busy cycles of the CUs), or None when there is none or the kernel
+    sources changed since."""
+    return _stored_record("counters", workload, cov)
+
+
+def alg_flops(w) -> float:
+    """Algorithmic matrix flops of one forward: 5 dk dv per token-head (decay
+    and rank-1 write 3 dk dv, readout 2 dk dv), independent of chunking."""
+    return float(w.B * w.H * w.T * 5 * w.dk * w.dv)
+
+
+def measure_copy(torch, nbytes: float, reps: int = 10) -> float:
+    """GB/s of a plain device-to-device copy that moves nbytes in total (half
+    read, half written), timed with HIP events on the current stream."""
+    half = int(nbytes // 2) // 16 * 16
+    src = torch.empty(half, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    return 2 * half / (ms / 1e3) / 1e9
 
 
 def alg_bytes(w) -> float:
@@ -271,7 +319,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="lm_diag")
+    ap.add_argument("--workload", default="long_diag")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="target wall time of the oracle sample")
@@ -305,21 +353,25 @@ def main() -> int:
     print(f"bench: workload {w}", file=sys.stderr, flush=True)
     host = gen.make_inputs(w, seed=0)
     names = ("q", "k", "v", "a", "qn", "r")
-    # two resident copies, alternated, so consecutive steps do not reuse the
-    # 256 MB last-level cache
+    # resident copies of the inputs and outputs, rotated so that the data one
+    # step touches was last touched at least three MALL sizes of traffic ago
+    # (consecutive steps never hit the 256 MB last-level cache)
+    nbytes = alg_bytes(w)
+    ncopies = max(2, -(-3 * MALL_BYTES // int(nbytes)))
     sets = [[host[n].to("cuda") for n in names]]
-    sets.append([t.clone() for t in sets[0]])
+    for _ in range(ncopies - 1):
+        sets.append([t.clone() for t in sets[0]])
     B, H, T, dk, dv = w.B, w.H, w.T, w.dk, w.dv
     outs = []
-    for _ in range(2):
+    for _ in range(ncopies):
         o = torch.empty(B, H, T, dv, dtype=sets[0][2].dtype, device="cuda")
         lT = torch.empty((B, H, dk) if w.cov == "diag" else (B, H), device="cuda")
         etaT = torch.empty(B, H, dk, dv, device="cuda")
         outs.append((o, lT, etaT))
 
     def step(i):
-        s = sets[i % 2]
-        o, lT, etaT = outs[i % 2]
+        s = sets[i % ncopies]
+        o, lT, etaT = outs[i % ncopies]
         if residual:
             scan_amd.fwd_residual(*s, cov=w.cov, o=o, lT=lT, mT=etaT)
         else:
@@ -350,10 +402,14 @@ def main() -> int:
 
     tokens = B * T
     value = tokens / (ms_per_step / 1e3)
-    nbytes = alg_bytes(w)
     achieved = nbytes / (kern_ms / 1e3) / 1e9
     print(f"bench: {ms_per_step:.4f} ms/step (kernel {kern_ms:.4f} ms), {achieved:.1f} GB/s "
-          f"algorithmic, wall {wall:.3f}s", file=sys.stderr, flush=True)
+          f"algorithmic, {ncopies} rotating input copies, wall {wall:.3f}s",
+          file=sys.stderr, flush=True)
+    # a plain device copy of the same byte count, measured now on this machine
+    copy_gbs = measure_copy(torch, nbytes)
+    print(f"bench: device copy of {nbytes / 1e6:.1f} MB: {copy_gbs:.1f} GB/s",
+          file=sys.stderr, flush=True)
 
     calibration_copy(args, torch)
 
@@ -393,9 +449,13 @@ def main() -> int:
                "sample": f"{seqs} of {nseq_total} (b,h) sequences at full T={T} "
                          f"({nb}x{nh}), fp64 sequential recurrence, {reps} pass(es) in {t_cpu:.1f}s"}
 
-    traffic = stored_traffic(w.name, "residual" if residual else w.cov)
+    fam = "residual" if residual else w.cov
+    traffic = stored_traffic(w.name, fam)
+    counters = stored_counters(w.name, fam)
     kernel_name = ("kla_fwd_residual_kernel" if residual else
                    scan_amd.fwd_kernel_name(w.B, w.H, w.T, w.dk, w.dv, w.cov, w.dtype))
+    flops = alg_flops(w)
+    mfma_tfs = flops / (kern_ms / 1e3) / 1e12
     line = {
         "metric": ("KLA residual-write layer fwd tokens/s at B·T, H×d; % of HBM roofline" if residual
                    else "KLA layer fwd tokens/s at B·T, H×d; % of HBM/MFMA roofline"),
@@ -416,7 +476,16 @@ def main() -> int:
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic["bytes_per_launch"] if traffic else None,
                      "kernel": kernel_name, "alg_bytes": nbytes,
-                     "kernel_ms": kern_ms},
+                     "kernel_ms": kern_ms,
+                     "copy_gbs": copy_gbs, "frac_of_copy": achieved / copy_gbs},
+        # algorithmic matrix flops per forward over the same GPU time, against
+        # the dense matrix-core peak of the input dtype; mfma_busy is the
+        # counter-measured share of CU busy cycles with the matrix cores busy
+        # (stored rocprofv3 record of the same kernels, null once they change)
+        "mfma": {"achieved": mfma_tfs, "peak": MFMA_PEAK_TFS[w.dtype], "unit": "TFLOP/s",
+                 "frac": mfma_tfs / MFMA_PEAK_TFS[w.dtype], "alg_flops": flops,
+                 "mfma_busy": counters["mfma_busy"] if counters else None,
+                 "valu_busy": counters["valu_busy"] if counters else None},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
