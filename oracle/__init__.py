@@ -1,11 +1,13 @@
-"""fp64 CPU oracle for the Kalman Linear Attention forward pass.
+"""fp64 CPU oracle for the Kalman Linear Attention forward and backward passes.
 
 TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's CPU
 baseline leg may import this package; the product path (``scan_amd``) never
 does, and nothing here imports ``scan_amd``.
 
 The arithmetic lives in ``kla_oracle.c`` (plain sequential recurrence in fp64,
-see its header for the recurrence and its sources).  This module only builds
+see its header for the recurrence and its sources; ``bwd`` is the
+reverse-mode adjoint of that recurrence, one reverse sweep over a stored
+forward trajectory).  This module only builds
 that file with gcc, marshals arrays to contiguous fp64 and calls it.
 
 Sources: "Kalman Linear Attention: Parallel Bayesian Filtering For Efficient
@@ -64,6 +66,9 @@ def _bind(lib):
     lib.kla_oracle_step.argtypes = [i, i, i, i, i] + [dp] * 9 + [i]
     lib.kla_oracle_fwd_residual.restype = ctypes.c_int
     lib.kla_oracle_fwd_residual.argtypes = [i, i, i, i, i, i] + [dp] * 11 + [i]
+    if hasattr(lib, "kla_oracle_bwd"):
+        lib.kla_oracle_bwd.restype = ctypes.c_int
+        lib.kla_oracle_bwd.argtypes = [i, i, i, i, i, i] + [dp] * 19 + [i]
     return lib
 
 
@@ -160,3 +165,33 @@ def fwd_residual(q, k, v, a, qn, r, l0=None, m0=None, cov: int = DIAG,
     if rc != 0:
         raise RuntimeError(f"kla_oracle_fwd_residual failed with code {rc}")
     return {"o": o, "lT": lT, "mT": mT}
+
+
+def bwd(q, k, v, a, qn, r, l0=None, eta0=None, do=None, dlT=None, detaT=None, cov: int = DIAG,
+        nthreads: int | None = None, lib_path: str | None = None):
+    """Backward pass of ``fwd`` in fp64 (reverse-mode adjoint of the
+    sequential recurrence).
+
+    do [B,H,T,dv] is dL/do; dlT, detaT (shapes of lT, etaT) are the gradients
+    of the final state and may be None (zero).  Returns dict(dq, dk, dv, da,
+    dqn, dr, dl0, deta0) in the shapes of the inputs q, k, v, a, qn, r, l0
+    (diag [B,H,dk], iso [B,H]) and eta0; the diagonal dqn [H,dk] is summed
+    over the batch.
+    """
+    lib = _load(lib_path)
+    q, k, v, a, qn, r = (_f64(x) for x in (q, k, v, a, qn, r))
+    l0, eta0, do, dlT, detaT = (_f64(x) for x in (l0, eta0, do, dlT, detaT))
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    nl = dk if cov == DIAG else 1
+    out = {"dq": np.empty((B, H, T, dk)), "dk": np.empty((B, H, T, dk)), "dv": np.empty((B, H, T, dv)),
+           "da": np.empty(a.shape), "dqn": np.empty(qn.shape), "dr": np.empty((B, H, T)),
+           "dl0": np.empty((B, H, nl) if cov == DIAG else (B, H)), "deta0": np.empty((B, H, dk, dv))}
+    rc = lib.kla_oracle_bwd(B, H, T, dk, dv, cov, _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(qn),
+                            _ptr(r), _ptr(l0), _ptr(eta0), _ptr(do), _ptr(dlT), _ptr(detaT),
+                            *(_ptr(out[n]) for n in ("dq", "dk", "dv", "da", "dqn", "dr", "dl0",
+                                                     "deta0")),
+                            nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"kla_oracle_bwd failed with code {rc}")
+    return out

@@ -1,5 +1,6 @@
 /*
- * kla_oracle.c -- fp64 CPU oracle for the Kalman Linear Attention forward pass.
+ * kla_oracle.c -- fp64 CPU oracle for the Kalman Linear Attention forward pass
+ * (and its backward pass, kla_oracle_bwd, at the end of this file).
  *
  * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU
  * baseline leg of the benchmark may load this file's library.  The product
@@ -303,6 +304,220 @@ int kla_oracle_fwd_residual(int B, int H, int T, int dk, int dv, int cov,
         if (mT)
             memcpy(mT + (size_t)s * dk * dv, m, sizeof(double) * (size_t)dk * dv);
         free(l); free(lp); free(g); free(u); free(m);
+    }
+    return failed;
+}
+
+/*
+ * Backward pass of kla_oracle_fwd: reverse-mode adjoint of the sequential
+ * recurrence above ("Kalman Linear Attention ...", fugumt abstract page: the
+ * information-form filter is a primitive for parallel training, so its
+ * gradients are part of the method).
+ *
+ * Given the upstream gradients dO = dL/do [B,H,T,dv], dlT = dL/dlT and
+ * detaT = dL/detaT (either may be NULL = 0), it returns dL/dq, dL/dk, dL/dv,
+ * dL/da, dL/dqn, dL/dr, dL/dl0, dL/deta0 of the scalar L.  Per (b,h) the
+ * forward trajectory (l_t and eta_t for every t) is recomputed and kept, then
+ * one reverse sweep applies the chain rule to each step of the forward, last
+ * token first:
+ *
+ *   readout  o_t = sum_i q_t[i] eta_t[i,:] / l_t[i]
+ *     dq_t[i]     = sum_j dO_t[j] eta_t[i,j] / l_t[i]
+ *     ebar_t[i,:] += q_t[i] dO_t / l_t[i]
+ *     lbar_t[i]   -= q_t[i] dq_t[i] / l_t[i]
+ *   update   eta_t = g_t eta_{t-1} + k_t v_t^T / r_t,   g_t = a_t / D_t
+ *     gbar_t[i]   = sum_j ebar_t[i,j] eta_{t-1}[i,j]
+ *     dk_t[i]    += sum_j ebar_t[i,j] v_t[j] / r_t
+ *     dv_t[j]     = sum_i ebar_t[i,j] k_t[i] / r_t
+ *     dr_t       -= sum_ij ebar_t[i,j] k_t[i] v_t[j] / r_t^2
+ *     ebar_{t-1}  = g_t ebar_t
+ *   precision l_t = lp_t + k_t^2 / r_t,  lp_t = l_{t-1} / D_t,
+ *             D_t = a_t^2 + qn l_{t-1}
+ *     dk_t += lbar_t 2 k_t / r_t,  dr_t -= lbar_t k_t^2 / r_t^2
+ *     lbar_{t-1} = lbar_t a_t^2 / D_t^2 - gbar_t a_t qn / D_t^2
+ *     da_t       = -lbar_t 2 a_t l_{t-1} / D_t^2 + gbar_t (qn l_{t-1} - a_t^2) / D_t^2
+ *     dqn       += -lbar_t l_{t-1}^2 / D_t^2 - gbar_t a_t l_{t-1} / D_t^2
+ *
+ * dl0 = lbar_{-1}, deta0 = ebar_{-1}.  Isotropic mode: the same with the
+ * scalar l, g, D per head; the precision increment sum_i k_i^2 / (d_k r) gives
+ * dk_t[i] += lbar_t 2 k_t[i] / (d_k r_t) and dr_t -= lbar_t sum_i k_t[i]^2 /
+ * (d_k r_t^2), and gbar_t sums over every (i,j).  The diagonal qn [H,dk] is
+ * shared by the batch, so its gradient is summed over b (in order of b);
+ * the isotropic qn is per token.  Shapes as kla_oracle_fwd; da [B,H,T,dk]
+ * (iso [B,H,T]); dqn [H,dk] (iso [B,H,T]); dl0 [B,H,dk] (iso [B,H]).
+ * dl0 and deta0 may be NULL.  Returns 0 on success.
+ */
+static void adjoint_sequence(int T, int dk, int dv, int cov,
+                             const double* q, const double* k, const double* v,
+                             const double* a, const double* qn, const double* r,
+                             const double* lstart, const double* etastart,
+                             const double* dO, const double* dlT, const double* detaT,
+                             double* dq, double* dkk, double* dvv, double* da, double* dqn_acc,
+                             double* dr, double* dl0, double* deta0,
+                             double* ltraj, double* etraj, double* lbar, double* ebar)
+{
+    const int nl = (cov == KLA_ORACLE_DIAG) ? dk : 1;
+    const size_t ne = (size_t)dk * dv;
+    /* forward trajectory: slot 0 holds the state before token 0, slot t+1
+       the state after token t */
+    for (int i = 0; i < nl; ++i) ltraj[i] = lstart ? lstart[i] : 1.0;
+    for (size_t e = 0; e < ne; ++e) etraj[e] = etastart ? etastart[e] : 0.0;
+    for (int t = 0; t < T; ++t) {
+        const double* lo = ltraj + (size_t)t * nl;
+        double* ln = ltraj + (size_t)(t + 1) * nl;
+        const double* eo = etraj + (size_t)t * ne;
+        double* en = etraj + (size_t)(t + 1) * ne;
+        const double* kt = k + (size_t)t * dk;
+        const double* vt = v + (size_t)t * dv;
+        const double rt = r[t];
+        if (cov == KLA_ORACLE_DIAG) {
+            for (int i = 0; i < dk; ++i) {
+                const double ai = a[(size_t)t * dk + i];
+                const double den = ai * ai + qn[i] * lo[i];
+                ln[i] = lo[i] / den + kt[i] * kt[i] / rt;
+                for (int j = 0; j < dv; ++j)
+                    en[(size_t)i * dv + j] = (ai / den) * eo[(size_t)i * dv + j] + kt[i] * vt[j] / rt;
+            }
+        } else {
+            const double at = a[t];
+            const double den = at * at + qn[t] * lo[0];
+            double ksq = 0.0;
+            for (int i = 0; i < dk; ++i) ksq += kt[i] * kt[i];
+            ln[0] = lo[0] / den + ksq / ((double)dk * rt);
+            for (int i = 0; i < dk; ++i)
+                for (int j = 0; j < dv; ++j)
+                    en[(size_t)i * dv + j] = (at / den) * eo[(size_t)i * dv + j] + kt[i] * vt[j] / rt;
+        }
+    }
+    /* adjoints of the final state */
+    for (int i = 0; i < nl; ++i) lbar[i] = dlT ? dlT[i] : 0.0;
+    for (size_t e = 0; e < ne; ++e) ebar[e] = detaT ? detaT[e] : 0.0;
+    for (int t = T - 1; t >= 0; --t) {
+        const double* lt_ = ltraj + (size_t)(t + 1) * nl;   /* l_t     */
+        const double* lp_ = ltraj + (size_t)t * nl;         /* l_{t-1} */
+        const double* et_ = etraj + (size_t)(t + 1) * ne;   /* eta_t   */
+        const double* ep_ = etraj + (size_t)t * ne;         /* eta_{t-1} */
+        const double* qt = q + (size_t)t * dk;
+        const double* kt = k + (size_t)t * dk;
+        const double* vt = v + (size_t)t * dv;
+        const double* dOt = dO + (size_t)t * dv;
+        const double rt = r[t];
+        /* readout */
+        for (int i = 0; i < dk; ++i) {
+            const double li = (cov == KLA_ORACLE_DIAG) ? lt_[i] : lt_[0];
+            double s = 0.0;
+            for (int j = 0; j < dv; ++j) s += dOt[j] * et_[(size_t)i * dv + j];
+            dq[(size_t)t * dk + i] = s / li;
+            for (int j = 0; j < dv; ++j) ebar[(size_t)i * dv + j] += qt[i] * dOt[j] / li;
+            lbar[(cov == KLA_ORACLE_DIAG) ? i : 0] -= qt[i] * (s / li) / li;
+        }
+        /* information update */
+        double gb_iso = 0.0, drt = 0.0;
+        for (int j = 0; j < dv; ++j) dvv[(size_t)t * dv + j] = 0.0;
+        for (int i = 0; i < dk; ++i) {
+            double gb = 0.0, u = 0.0;
+            for (int j = 0; j < dv; ++j) {
+                gb += ebar[(size_t)i * dv + j] * ep_[(size_t)i * dv + j];
+                u += ebar[(size_t)i * dv + j] * vt[j];
+                dvv[(size_t)t * dv + j] += ebar[(size_t)i * dv + j] * kt[i] / rt;
+            }
+            dkk[(size_t)t * dk + i] = u / rt;
+            drt -= kt[i] * u / (rt * rt);
+            if (cov == KLA_ORACLE_DIAG) {
+                /* precision of key dim i, then carry the adjoints back */
+                const double ai = a[(size_t)t * dk + i], lprev = lp_[i], qni = qn[i];
+                const double den = ai * ai + qni * lprev, den2 = den * den;
+                const double lb = lbar[i];
+                dkk[(size_t)t * dk + i] += lb * 2.0 * kt[i] / rt;
+                drt -= lb * kt[i] * kt[i] / (rt * rt);
+                da[(size_t)t * dk + i] = -lb * 2.0 * ai * lprev / den2 + gb * (qni * lprev - ai * ai) / den2;
+                dqn_acc[i] += -lb * lprev * lprev / den2 - gb * ai * lprev / den2;
+                lbar[i] = lb * ai * ai / den2 - gb * ai * qni / den2;
+                for (int j = 0; j < dv; ++j) ebar[(size_t)i * dv + j] *= ai / den;
+            } else {
+                gb_iso += gb;
+            }
+        }
+        if (cov == KLA_ORACLE_ISO) {
+            const double at = a[t], lprev = lp_[0], qnt = qn[t];
+            const double den = at * at + qnt * lprev, den2 = den * den;
+            const double lb = lbar[0];
+            double ksq = 0.0;
+            for (int i = 0; i < dk; ++i) {
+                dkk[(size_t)t * dk + i] += lb * 2.0 * kt[i] / ((double)dk * rt);
+                ksq += kt[i] * kt[i];
+            }
+            drt -= lb * ksq / ((double)dk * rt * rt);
+            da[t] = -lb * 2.0 * at * lprev / den2 + gb_iso * (qnt * lprev - at * at) / den2;
+            dqn_acc[t] = -lb * lprev * lprev / den2 - gb_iso * at * lprev / den2;
+            lbar[0] = lb * at * at / den2 - gb_iso * at * qnt / den2;
+            for (size_t e = 0; e < ne; ++e) ebar[e] *= at / den;
+        }
+        dr[t] = drt;
+    }
+    if (dl0)
+        for (int i = 0; i < nl; ++i) dl0[i] = lbar[i];
+    if (deta0) memcpy(deta0, ebar, sizeof(double) * ne);
+}
+
+int kla_oracle_bwd(int B, int H, int T, int dk, int dv, int cov,
+                   const double* q, const double* k, const double* v,
+                   const double* a, const double* qn, const double* r,
+                   const double* l0, const double* eta0,
+                   const double* dO, const double* dlT, const double* detaT,
+                   double* dq, double* dk_out, double* dv_out, double* da, double* dqn,
+                   double* dr, double* dl0, double* deta0, int nthreads)
+{
+    if (B < 1 || H < 1 || T < 0 || dk < 1 || dv < 1) return 1;
+    if (cov != KLA_ORACLE_DIAG && cov != KLA_ORACLE_ISO) return 1;
+    if (T > 0 && (!q || !k || !v || !a || !qn || !r || !dO || !dq || !dk_out || !dv_out || !da || !dr))
+        return 1;
+    if (!dqn) return 1;
+    const int nl = (cov == KLA_ORACLE_DIAG) ? dk : 1;
+    const long long nseq = (long long)B * H;
+    const size_t ne = (size_t)dk * dv;
+    /* per-sequence partial of the diagonal qn gradient, summed over b below */
+    double* dqn_part = NULL;
+    if (cov == KLA_ORACLE_DIAG) {
+        dqn_part = (double*)calloc((size_t)nseq * dk, sizeof(double));
+        if (!dqn_part) return 1;
+    }
+    int failed = 0;
+    if (nthreads < 1) nthreads = 1;
+
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads) reduction(| : failed)
+    for (long long s = 0; s < nseq; ++s) {
+        const int h = (int)(s % H);
+        double* ltraj = (double*)malloc(sizeof(double) * (size_t)(T + 1) * nl);
+        double* etraj = (double*)malloc(sizeof(double) * (size_t)(T + 1) * ne);
+        double* lbar = (double*)malloc(sizeof(double) * (size_t)nl);
+        double* ebar = (double*)malloc(sizeof(double) * ne);
+        if (!ltraj || !etraj || !lbar || !ebar) {
+            free(ltraj); free(etraj); free(lbar); free(ebar);
+            failed |= 1;
+            continue;
+        }
+        const size_t tk = (size_t)s * T * dk, tv = (size_t)s * T * dv;
+        const double* as = (cov == KLA_ORACLE_DIAG) ? a + tk : a + (size_t)s * T;
+        const double* qns = (cov == KLA_ORACLE_DIAG) ? qn + (size_t)h * dk : qn + (size_t)s * T;
+        double* dqn_s = (cov == KLA_ORACLE_DIAG) ? dqn_part + (size_t)s * dk : dqn + (size_t)s * T;
+        double* da_s = (cov == KLA_ORACLE_DIAG) ? da + tk : da + (size_t)s * T;
+        adjoint_sequence(T, dk, dv, cov, q + tk, k + tk, v + tv, as, qns, r + (size_t)s * T,
+                         l0 ? l0 + (size_t)s * nl : NULL, eta0 ? eta0 + (size_t)s * ne : NULL,
+                         dO + tv, dlT ? dlT + (size_t)s * nl : NULL, detaT ? detaT + (size_t)s * ne : NULL,
+                         dq + tk, dk_out + tk, dv_out + tv, da_s, dqn_s, dr + (size_t)s * T,
+                         dl0 ? dl0 + (size_t)s * nl : NULL, deta0 ? deta0 + (size_t)s * ne : NULL,
+                         ltraj, etraj, lbar, ebar);
+        free(ltraj); free(etraj); free(lbar); free(ebar);
+    }
+    if (cov == KLA_ORACLE_DIAG) {
+        for (int hh = 0; hh < H; ++hh)
+            for (int i = 0; i < dk; ++i) {
+                double acc = 0.0;
+                for (int b = 0; b < B; ++b) acc += dqn_part[((size_t)b * H + hh) * dk + i];
+                dqn[(size_t)hh * dk + i] = acc;
+            }
+        free(dqn_part);
     }
     return failed;
 }
