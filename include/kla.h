@@ -160,6 +160,44 @@ klaStatus klaFwdResidual(const klaDims* d,
                          const float* l0, const float* m0,
                          void* o, float* lT, float* mT, void* hipStream);
 
+/*
+ * Device workspace (bytes) that klaBwd needs for these dims: per (b,h) the
+ * precision after every token and one scalar per token and key dim (per
+ * token when isotropic), both fp64, plus dk fp32 for the diagonal, rounded up
+ * to 256 bytes per (b,h).  0 for unsupported dims.
+ */
+size_t klaBwdWorkspaceBytes(const klaDims* d);
+
+/*
+ * Backward pass of klaFwd ([KLA] abstract: the information-form filter is
+ * trained in parallel as a sequence-model layer, so its gradients are part of
+ * the layer).  For the scalar L = <dO, o> + <dlT, lT> + <detaT, etaT> of one
+ * klaFwd call with the same inputs, it returns dL/dq, dL/dk, dL/dv, dL/da,
+ * dL/dqnoise, dL/dr, dL/dl0 and dL/deta0.
+ * In:  q, k, v, a, qnoise, r, l0, eta0 exactly as passed to klaFwd (l0, eta0
+ *      may be NULL: 1 and 0); dO [B,H,T,dv] in the input dtype; dlT (shape of
+ *      lT) and detaT [B,H,dk,dv] fp32, either may be NULL (zero).
+ * Out: dq, dk [B,H,T,dk] and dv [B,H,T,dv] in the input dtype (rounded RNE
+ *      from fp32); da (diag [B,H,T,dk], iso [B,H,T]), dr [B,H,T] fp32;
+ *      dqnoise fp32: diag [H,dk], summed over the batch; iso [B,H,T];
+ *      dl0 (shape of l0) and deta0 [B,H,dk,dv] fp32, either may be NULL
+ *      (not computed).  All outputs are fully overwritten.
+ * Supported: dk == dv in {16, 32, 64, 128}, either dtype and cov.
+ * workspace must hold klaBwdWorkspaceBytes(d) bytes (16-byte aligned).
+ * Every non-NULL pointer must be 16-byte aligned.  Aliasing: no output may
+ * overlap an input, the workspace or another output (KLA_ERR_ALIAS).
+ * Errors, ownership and execution as klaFwd; preconditions as klaFwd, with
+ * a > 0 (the gradient of the gate divides by a).
+ */
+klaStatus klaBwd(const klaDims* d,
+                 const void* q, const void* k, const void* v,
+                 const float* a, const float* qnoise, const float* r,
+                 const float* l0, const float* eta0,
+                 const void* dO, const float* dlT, const float* detaT,
+                 void* dq, void* dk, void* dv, float* da, float* dqnoise, float* dr,
+                 float* dl0, float* deta0,
+                 void* workspace, size_t workspaceBytes, void* hipStream);
+
 /* Static, human-readable description of a status code (never NULL). */
 const char* klaStatusString(klaStatus s);
 

@@ -6,20 +6,22 @@ is no CPU fallback: if the library is missing or no GPU is present the calls
 raise.
 
 Low level (same names and arguments as the C ABI, raw device pointers):
-    klaFwd, klaStep, klaFwdResidual, klaFwdWorkspaceBytes, klaIsSupported, klaStatusString
+    klaFwd, klaStep, klaFwdResidual, klaBwd, klaFwdWorkspaceBytes, klaBwdWorkspaceBytes,
+    klaIsSupported, klaStatusString
 Convenience (torch tensors in, torch tensors out):
     fwd(q, k, v, a, qn, r, l0=None, eta0=None, cov="diag") -> (o, lT, etaT)
     step(q, k, v, a, qn, r, l, eta, cov="diag") -> o      (l, eta updated in place)
     fwd_residual(q, k, v, a, qn, r, l0=None, m0=None, cov="diag") -> (o, lT, mT)
+    bwd(q, k, v, a, qn, r, l0, eta0, do, dlT=None, detaT=None, cov="diag") -> dict of gradients
 """
 from __future__ import annotations
 
 import ctypes
 import os
 
-__all__ = ["klaFwd", "klaStep", "klaFwdResidual", "klaFwdWorkspaceBytes", "klaIsSupported",
-           "klaStatusString", "KlaDims", "KlaError", "fwd", "step", "fwd_residual", "lib_path",
-           "load"]
+__all__ = ["klaFwd", "klaStep", "klaFwdResidual", "klaBwd", "klaFwdWorkspaceBytes",
+           "klaBwdWorkspaceBytes", "klaIsSupported", "klaStatusString", "KlaDims", "KlaError", "fwd",
+           "step", "fwd_residual", "bwd", "lib_path", "load"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libkla.so")
@@ -79,6 +81,10 @@ def load():
     lib.klaStatusString.restype = ctypes.c_char_p
     lib.klaFwdKernelName.argtypes = [dp]
     lib.klaFwdKernelName.restype = ctypes.c_char_p
+    lib.klaBwdWorkspaceBytes.argtypes = [dp]
+    lib.klaBwdWorkspaceBytes.restype = sz
+    lib.klaBwd.argtypes = [dp] + [vp] * 19 + [vp, sz, vp]
+    lib.klaBwd.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -108,6 +114,18 @@ def klaFwdResidual(dims, q, k, v, a, qnoise, r, l0, m0, o, lT, mT, stream) -> in
     """Raw call of the residual-write forward (pointers as ints or None)."""
     return int(load().klaFwdResidual(ctypes.byref(dims), q, k, v, a, qnoise, r, l0, m0, o, lT, mT,
                                      stream))
+
+
+def klaBwdWorkspaceBytes(dims: KlaDims) -> int:
+    return int(load().klaBwdWorkspaceBytes(ctypes.byref(dims)))
+
+
+def klaBwd(dims, q, k, v, a, qnoise, r, l0, eta0, dO, dlT, detaT, dq, dk, dv, da, dqnoise, dr, dl0,
+           deta0, workspace, workspaceBytes, stream) -> int:
+    """Raw call of the backward pass (pointers as ints or None)."""
+    return int(load().klaBwd(ctypes.byref(dims), q, k, v, a, qnoise, r, l0, eta0, dO, dlT, detaT,
+                             dq, dk, dv, da, dqnoise, dr, dl0, deta0, workspace, workspaceBytes,
+                             stream))
 
 
 def klaStatusString(status: int) -> str:
@@ -224,3 +242,32 @@ def fwd_residual(q, k, v, a, qn, r, l0=None, m0=None, cov: str = "diag", o=None,
     if st != KLA_OK:
         raise KlaError(st, "klaFwdResidual")
     return o, lT, mT
+
+
+def bwd(q, k, v, a, qn, r, l0=None, eta0=None, do=None, dlT=None, detaT=None, cov: str = "diag",
+        want_state: bool = True):
+    """Backward pass of ``fwd`` on the current stream: the gradients of
+    L = <do, o> + <dlT, lT> + <detaT, etaT>.  Returns a dict of device tensors
+    dq, dk, dv (input dtype), da, dqn, dr, dl0, deta0 (fp32) in the shapes of
+    the corresponding inputs (the diagonal dqn [H,dk] sums over the batch)."""
+    import torch
+    _check_device(q, k, v, a, qn, r, l0, eta0, do, dlT, detaT)
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    c = KLA_DIAG if cov == "diag" else KLA_ISO
+    dims = KlaDims(B, H, T, dk, dv, _dtype_code(q), c)
+    dev = q.device
+    out = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
+           "da": torch.empty_like(a), "dqn": torch.empty_like(qn), "dr": torch.empty_like(r)}
+    out["dl0"] = (torch.empty((B, H, dk) if c == KLA_DIAG else (B, H), dtype=torch.float32, device=dev)
+                  if want_state else None)
+    out["deta0"] = torch.empty(B, H, dk, dv, dtype=torch.float32, device=dev) if want_state else None
+    ws_bytes = klaBwdWorkspaceBytes(dims)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    st = klaBwd(dims, _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(qn), _ptr(r), _ptr(l0), _ptr(eta0),
+                _ptr(do), _ptr(dlT), _ptr(detaT), *(_ptr(out[n]) for n in
+                                                     ("dq", "dk", "dv", "da", "dqn", "dr", "dl0", "deta0")),
+                _ptr(ws), ws_bytes, _stream())
+    if st != KLA_OK:
+        raise KlaError(st, "klaBwd")
+    return out

@@ -9,6 +9,7 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include "kla_bwd.h"
 #include "kla_internal.h"
 #include "kla_residual.h"
 #include "kla_short.h"
@@ -340,6 +341,67 @@ klaStatus klaFwdResidual(const klaDims* d, const void* q, const void* k, const v
     hipStream_t st = (hipStream_t)hipStream;
     const hipError_t e = T == 0 ? kla::launch_fwd_empty(fa, iso ? 1 : 0, st)
                                 : kla::launch_fwd_residual(fa, d->dtype, iso ? 1 : 0, st);
+    return e == hipSuccess ? KLA_OK : KLA_ERR_HIP;
+}
+
+size_t klaBwdWorkspaceBytes(const klaDims* d) {
+    if (!d || !dims_ok(d) || !kinds_ok(d) || !kla::bwd_supported(d->dk, d->dv)) return 0;
+    return (size_t)d->B * d->H * kla::bwd_ws_stride(d->T, d->dk, d->cov == KLA_ISO ? 1 : 0) * sizeof(float);
+}
+
+klaStatus klaBwd(const klaDims* d, const void* q, const void* k, const void* v, const float* a,
+                 const float* qnoise, const float* r, const float* l0, const float* eta0, const void* dO,
+                 const float* dlT, const float* detaT, void* dq, void* dk, void* dv, float* da,
+                 float* dqnoise, float* dr, float* dl0, float* deta0, void* workspace,
+                 size_t workspaceBytes, void* hipStream) {
+    if (!d) return KLA_ERR_NULL;
+    if (!dims_ok(d)) return KLA_ERR_SHAPE;
+    if (!kinds_ok(d) || !kla::bwd_supported(d->dk, d->dv)) return KLA_ERR_UNSUPPORTED;
+    const long long B = d->B, H = d->H, T = d->T, dkd = d->dk, dvd = d->dv;
+    const long long BH = B * H;
+    if (BH > (1LL << 30) || T > (1LL << 30)) return KLA_ERR_SHAPE;
+    const bool iso = d->cov == KLA_ISO;
+    const size_t es = d->dtype == KLA_BF16 ? 2 : 4;
+    const size_t ntk = (size_t)(BH * T);
+    const size_t nl = (size_t)(iso ? BH : BH * dkd);
+    const size_t neta = (size_t)(BH * dkd * dvd);
+    const size_t nqn = iso ? ntk : (size_t)(H * dkd);
+    if (H * dkd == 0 || (iso && BH == 0)) return KLA_OK;
+    if (!iso && !dqnoise) return KLA_ERR_NULL;
+    if (ntk > 0 && (!q || !k || !v || !a || !qnoise || !r || !dO || !dq || !dk || !dv || !da ||
+                    !dqnoise || !dr))
+        return KLA_ERR_NULL;
+    const void* ptrs[] = {q, k, v, a, qnoise, r, l0, eta0, dO, dlT, detaT,
+                          dq, dk, dv, da, dqnoise, dr, dl0, deta0};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return KLA_ERR_ALIGN;
+    const size_t wneed = klaBwdWorkspaceBytes(d);
+    if (wneed > 0 && (!workspace || workspaceBytes < wneed)) return KLA_ERR_WORKSPACE;
+    if (wneed > 0 && !aligned16(workspace)) return KLA_ERR_ALIGN;
+    const Span ins[] = {span(q, ntk * dkd * es), span(k, ntk * dkd * es), span(v, ntk * dvd * es),
+                        span(a, (iso ? ntk : ntk * dkd) * 4), span(qnoise, (iso ? ntk : (size_t)(H * dkd)) * 4),
+                        span(r, ntk * 4), span(l0, nl * 4), span(eta0, neta * 4),
+                        span(dO, ntk * dvd * es), span(dlT, nl * 4), span(detaT, neta * 4)};
+    const Span outs[] = {span(dq, ntk * dkd * es), span(dk, ntk * dkd * es), span(dv, ntk * dvd * es),
+                         span(da, (iso ? ntk : ntk * dkd) * 4), span(dqnoise, nqn * 4), span(dr, ntk * 4),
+                         span(dl0, nl * 4), span(deta0, neta * 4), span(workspace, wneed)};
+    const int nout = sizeof(outs) / sizeof(outs[0]);
+    for (int x = 0; x < nout; ++x) {
+        for (const Span& s : ins)
+            if (overlap(outs[x], s)) return KLA_ERR_ALIAS;
+        for (int y = x + 1; y < nout; ++y)
+            if (overlap(outs[x], outs[y])) return KLA_ERR_ALIAS;
+    }
+    kla::BwdArgs ba;
+    ba.q = q; ba.k = k; ba.v = v; ba.a = a; ba.qn = qnoise; ba.r = r; ba.l0 = l0; ba.eta0 = eta0;
+    ba.dO = dO; ba.dlT = dlT; ba.detaT = detaT;
+    ba.gq = dq; ba.gk = dk; ba.gv = dv; ba.ga = da; ba.gqn = dqnoise; ba.gr = dr; ba.gl0 = dl0;
+    ba.geta0 = deta0;
+    ba.ws = (float*)workspace;
+    ba.ws_stride = kla::bwd_ws_stride(d->T, d->dk, iso ? 1 : 0);
+    ba.B = d->B; ba.H = d->H; ba.T = d->T; ba.dk = d->dk; ba.dv = d->dv;
+    const hipError_t e = kla::launch_bwd(ba, d->dtype, iso ? 1 : 0, (hipStream_t)hipStream);
+    if (e == hipErrorInvalidValue) return KLA_ERR_UNSUPPORTED;
     return e == hipSuccess ? KLA_OK : KLA_ERR_HIP;
 }
 

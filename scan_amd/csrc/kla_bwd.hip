@@ -1,0 +1,486 @@
+// kla_bwd.hip -- gfx950 backward pass of the KLA forward (diagonal and
+// isotropic precision).
+//
+// Sources: "Kalman Linear Attention: Parallel Bayesian Filtering For Efficient
+// Language Modelling and State Tracking" (fugumt abstract page: the filter is
+// a primitive for parallel training; gist.science explainer, method §1-§3 for
+// the recurrence) and "Kalman Delta Networks: Uncertainty-aware Associative
+// Memory" (abstract: diagonal and isotropic variants).
+//
+// Forward, per (b,h), information form (key dim i, value column j):
+//   D_t = a_t^2 + qn l_{t-1},  g_t = a_t / D_t,  l_t = l_{t-1} / D_t + k_t^2 / r_t
+//   eta_t = g_t eta_{t-1} + (k_t / r_t) v_t^T,   o_t = sum_i (q_t[i] / l_t[i]) eta_t[i,:]
+// Backward of L with the upstream dO = dL/do, dlT, detaT:
+//   dq_t[i]   = S_t[i] / l_t[i],             S_t[i] = sum_j dO_t[j] eta_t[i,j]
+//   ebar_t    = g_{t+1} ebar_{t+1} + (q_t / l_t) dO_t^T     (ebar_T = detaT, g_T = 1)
+//   U_t[i]    = sum_j ebar_t[i,j] v_t[j],   dv_t[j] = sum_i ebar_t[i,j] k_t[i] / r_t
+// The adjoint of log g_t needs sum_j ebar_t[i,j] eta_{t-1}[i,j], a per-token
+// product of two dk x dv states.  It telescopes instead: with
+// P_t = sum_j ebar_t[i,j] eta_t[i,j] one has P_{t-1} = P_t - kap_t U_t + q_{t-1} dq_{t-1},
+// so  dlog g_t[i] = B[i] + sum_{s>=t} (q_s[i] dq_s[i] - kap_s[i] U_s[i]),
+// B[i] = sum_j detaT[i,j] eta_T[i,j]  (kap = k / r), a reverse cumulative sum
+// of per-token scalars.  Its terms nearly cancel when a token's write
+// dominates the carried state (a small gate next to a large k v / r), so
+// the states eta and ebar, their row sums, the cumulative sum and the
+// precision recursion are carried in fp64 (the staged coefficients are fp32,
+// the same values in both sweeps, so the state products are exact in fp64).  The precision adjoint is then one
+// scalar reverse recursion per key dim (per head when isotropic):
+//   lbar_t   += -q_t dq_t / l_t
+//   dk_t      = U_t / r_t + lbar_t 2 k_t / r_t            (iso: 2 k_t[i] / (dk r_t))
+//   dr_t      = -sum_i (kap_t[i] U_t[i] + lbar_t k_t[i]^2 / r_t) / r_t
+//   da_t      = -lbar_t 2 a_t l_{t-1} / D_t^2 + dlog g_t (qn l_{t-1} - a_t^2) / (a_t D_t)
+//   dqn      += -lbar_t l_{t-1}^2 / D_t^2 - dlog g_t l_{t-1} / D_t
+//   lbar_{t-1} = lbar_t a_t^2 / D_t^2 - dlog g_t qn / D_t
+// dl0 = lbar_{-1}, deta0 = g_0 ebar_0.
+//
+// One workgroup runs all of this for its (b,h) (small heads share a
+// workgroup) in two sweeps over the tokens, the state slice of every thread
+// in registers (rows rg*RPT.. of value quad jq):
+//   sweep 1, forward: eta, dq, and per token l_t and q dq into the workspace;
+//   sweep 2, backward: ebar, U, dv, the precision adjoint, dk, da, dr, dqn.
+// Tokens go in blocks of TB; one lane per key dim forms the block's
+// coefficients, every thread applies the block to its rows and leaves
+// per-row and per-column partial sums in LDS, and the key-dim lanes and
+// value-quad lanes sum them.  The diagonal qn is shared by the batch: each
+// (b,h) leaves its partial in the workspace and a second kernel sums over b.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kla_bwd.h"
+#include "kla_common.h"
+
+namespace kla {
+namespace {
+
+constexpr int kBwdThreads = 256;
+
+typedef double f64x2 __attribute__((ext_vector_type(2)));
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+template <int D>
+struct BwdLayout {
+    static constexpr int EPT = D == 16 ? 16 : 32;   // state elements per thread, at least
+    static constexpr int NTH = D * D / EPT < kBwdThreads ? D * D / EPT : kBwdThreads;
+    static constexpr int NH = kBwdThreads / NTH;    // (b,h) per workgroup
+    static constexpr int VQ = D / 4;                // value quads per row
+    static constexpr int RG = NTH / VQ;             // row groups
+    static constexpr int RPT = D / RG;              // rows per thread
+    static constexpr int TB = D == 128 ? 2 : 4;     // tokens per block (LDS of the row sums)
+    static_assert(RPT % 4 == 0 && TB * VQ <= NTH && NTH * NH == kBwdThreads && D <= NTH, "layout");
+};
+
+template <int D>
+struct BwdSm {
+    typedef BwdLayout<D> Ly;
+    static constexpr int NH = Ly::NH, NTH = Ly::NTH, VQ = Ly::VQ, TB = Ly::TB;
+    // block coefficients per key dim: gate (of the next token in sweep 2),
+    // k / r, q / l; the block's v and dO rows
+    alignas(16) float g[NH][TB][D];
+    alignas(16) float kap[NH][TB][D];
+    alignas(16) float cq[NH][TB][D];
+    alignas(16) float v[NH][TB][D];
+    alignas(16) float dO[NH][TB][D];
+    // per-row partial sums (over a thread's value quad): [token][quad][row]
+    alignas(16) double rpart[NH][TB][VQ][D];
+    // per-column partial sums (over a thread's rows): one quad per thread
+    alignas(16) f32x4 cpart[NH][TB][NTH];
+    double red[NH][TB][2][2];  // cross-wave sums of the key-dim lanes
+};
+
+// Sum over the D key-dim lanes of a group, returned to every lane of the
+// group.  Every thread of the workgroup calls it at the same point (lanes
+// past the key dims pass 0): at D = 128 the two key-dim waves combine
+// through LDS between workgroup barriers.
+template <int D, int NH, int TB>
+__device__ __forceinline__ double kdim_sum(double x, double (&red)[NH][TB][2][2], int grp, int u, int slot,
+                                           int lt) {
+    constexpr int W = D < 64 ? D : 64;
+#pragma unroll
+    for (int m = 1; m < W; m <<= 1) x += __shfl_xor(x, m, 64);
+    if constexpr (D > 64) {
+        if ((lt & 63) == 0 && lt < D) red[grp][u][lt >> 6][slot] = x;
+        __syncthreads();
+        x = red[grp][u][0][slot] + red[grp][u][1][slot];
+        __syncthreads();
+    }
+    return x;
+}
+
+__device__ __forceinline__ f64x4 to_f64(f32x4 x) { return f64x4{x[0], x[1], x[2], x[3]}; }
+
+// gate of one token from the precision before it, in fp64 (the same
+// arithmetic in both sweeps, so the fp32 gates they stage match bit for bit);
+// rd_out receives 1 / (a^2 + qn l)
+__device__ __forceinline__ double gate_of(double a, double qn, double l, double* rd_out) {
+    const double rd = 1. / __builtin_fma(qn, l, a * a);
+    *rd_out = rd;
+    return a * rd;
+}
+
+template <typename TIn, int D, bool ISO>
+__global__ __launch_bounds__(kBwdThreads) void kla_bwd_kernel(BwdArgs p) {
+    typedef BwdLayout<D> Ly;
+    constexpr int TB = Ly::TB, NTH = Ly::NTH, NH = Ly::NH, VQ = Ly::VQ, RG = Ly::RG, RPT = Ly::RPT;
+    constexpr int NL = ISO ? 1 : D;
+    __shared__ BwdSm<D> sm;
+
+    const int tid = threadIdx.x;
+    const int grp = NH == 1 ? 0 : tid / NTH, lt = NH == 1 ? tid : tid % NTH;
+    const int nbh = p.B * p.H, bh_ = NH == 1 ? (int)blockIdx.x : (int)blockIdx.x * NH + grp;
+    const bool valid = NH == 1 || bh_ < nbh;
+    const int bh = valid ? bh_ : nbh - 1;  // a spare group stays in bounds and stores nothing
+    const int h = bh % p.H;
+    const int jq = lt % VQ, rg = lt / VQ;
+    const int T = p.T;
+    const size_t row0 = (size_t)bh * T;
+    const TIn* q = (const TIn*)p.q;
+    const TIn* k = (const TIn*)p.k;
+    const TIn* v = (const TIn*)p.v;
+    const TIn* dOg = (const TIn*)p.dO;
+    const bool kd = lt < D;  // key-dim lane
+    const int i = kd ? lt : D - 1;
+    // workspace of this (b,h): l_t [T][NL] and q dq [T][NL] in fp64 (iso:
+    // summed over key dims), then the diagonal qn partial [D] fp32
+    double* wl = (double*)(p.ws + (size_t)bh * p.ws_stride);
+    double* wqdq = wl + (size_t)T * NL;
+    float* wdqn = (float*)(wqdq + (size_t)T * NL);
+
+    const float qn_i = ISO ? 0.f : p.qn[(size_t)h * D + i];
+    const double l_start = ISO ? (p.l0 ? p.l0[bh] : 1.f) : (p.l0 ? p.l0[(size_t)bh * D + i] : 1.f);
+
+    // ---------------------------------------------------------------- sweep 1
+    f64x4 e[RPT];
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+        const size_t off = ((size_t)bh * D + rg * RPT + m) * D + 4 * jq;
+        e[m] = p.eta0 ? to_f64(*(const f32x4*)(p.eta0 + off)) : f64x4{0., 0., 0., 0.};
+    }
+    double l = l_start;  // the precision recursion runs in fp64
+    // stages v and dO rows (one value quad per thread) of tokens t0.. into LDS
+    auto stage_rows = [&](int t0, int nb) {
+        if (lt < TB * VQ && lt / VQ < nb) {
+            const size_t t = row0 + t0 + lt / VQ;
+            *(f32x4*)&sm.v[grp][lt / VQ][4 * jq] = Quad<TIn>::to_f32(*(const typename Quad<TIn>::V*)(v + t * D + 4 * jq));
+            *(f32x4*)&sm.dO[grp][lt / VQ][4 * jq] = Quad<TIn>::to_f32(*(const typename Quad<TIn>::V*)(dOg + t * D + 4 * jq));
+        }
+    };
+    // forward coefficients of a block (advances l): g, k/r into LDS, l_t into
+    // the workspace
+    auto fwd_coefs = [&](int t0, int nb) {
+#pragma unroll
+        for (int u = 0; u < TB; ++u) {
+            if (u < nb) {
+                const size_t t = row0 + t0 + u;
+                const double kv = (float)k[t * D + i];
+                const double rt = p.r[t];
+                double a, qn, b;
+                if constexpr (ISO) {
+                    a = p.a[t];
+                    qn = p.qn[t];
+                    b = kdim_sum<D, NH, TB>(kd ? kv * kv : 0., sm.red, grp, u, 0, lt) / ((double)D * rt);
+                } else {
+                    a = p.a[t * D + i];
+                    qn = qn_i;
+                    b = kv * kv / rt;
+                }
+                double rd;
+                const double g = gate_of(a, qn, l, &rd);
+                l = __builtin_fma(l, rd, b);
+                if (kd) {
+                    sm.g[grp][u][i] = (float)g;
+                    sm.kap[grp][u][i] = (float)(kv / rt);
+                    if ((!ISO || lt == 0) && valid) wl[(size_t)(t0 + u) * NL + (ISO ? 0 : i)] = l;
+                }
+            }
+        }
+    };
+    if (T > 0) {
+        stage_rows(0, T < TB ? T : TB);
+        fwd_coefs(0, T < TB ? T : TB);
+    }
+    __syncthreads();
+    for (int t0 = 0; t0 < T; t0 += TB) {
+        const int nb = T - t0 < TB ? T - t0 : TB;
+        // ---- the block on the thread's rows; per-row S partials
+#pragma unroll
+        for (int u = 0; u < TB; ++u) {
+            if (u < nb) {
+                const f64x4 vv = to_f64(*(const f32x4*)&sm.v[grp][u][4 * jq]);
+                const f64x4 dd = to_f64(*(const f32x4*)&sm.dO[grp][u][4 * jq]);
+#pragma unroll
+                for (int m4 = 0; m4 < RPT; m4 += 4) {
+                    const f32x4 gv = *(const f32x4*)&sm.g[grp][u][rg * RPT + m4];
+                    const f32x4 kv = *(const f32x4*)&sm.kap[grp][u][rg * RPT + m4];
+                    double sp[4];
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        e[m4 + x] = (double)gv[x] * e[m4 + x] + (double)kv[x] * vv;
+                        const f64x4 pr = e[m4 + x] * dd;
+                        sp[x] = (pr[0] + pr[1]) + (pr[2] + pr[3]);
+                    }
+                    *(f64x2*)&sm.rpart[grp][u][jq][rg * RPT + m4] = f64x2{sp[0], sp[1]};
+                    *(f64x2*)&sm.rpart[grp][u][jq][rg * RPT + m4 + 2] = f64x2{sp[2], sp[3]};
+                }
+            }
+        }
+        __syncthreads();
+        // ---- dq of the block (key-dim lanes; the others compute along and
+        // store nothing), then the next block's coefficients
+#pragma unroll
+        for (int u = 0; u < TB; ++u) {
+            if (u < nb) {
+                double s = 0.;
+#pragma unroll 8
+                for (int x = 0; x < VQ; ++x) s += sm.rpart[grp][u][x][i];
+                const size_t t = row0 + t0 + u;
+                const double lt_ = wl[(size_t)(t0 + u) * NL + (ISO ? 0 : i)];
+                const double qv = (float)q[t * D + i];
+                const double dq = s / lt_;
+                if (kd && valid) ((TIn*)p.gq)[t * D + i] = (TIn)(float)dq;
+                // q dq with q / l rounded to fp32 exactly as sweep 2 stages it
+                // for the readout adjoint, so the telescoping sum stays exact
+                const double qdq = (double)(float)(qv / lt_) * s;
+                if constexpr (ISO) {
+                    const double tot = kdim_sum<D, NH, TB>(kd ? qdq : 0., sm.red, grp, u, 1, lt);
+                    if (lt == 0 && valid) wqdq[t0 + u] = tot;
+                } else {
+                    if (kd && valid) wqdq[(size_t)(t0 + u) * D + i] = qdq;
+                }
+            }
+        }
+        const bool more = t0 + TB < T;
+        if (more) {
+            const int nb2 = T - t0 - TB < TB ? T - t0 - TB : TB;
+            stage_rows(t0 + TB, nb2);
+            fwd_coefs(t0 + TB, nb2);
+        }
+        __syncthreads();
+    }
+    // boundary term of the gate adjoint: B[i] = sum_j detaT[i,j] eta_T[i,j];
+    // the state registers then take ebar_T = detaT
+    double Bsum = 0.;
+    {
+#pragma unroll
+        for (int m4 = 0; m4 < RPT; m4 += 4) {
+            double sp[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const size_t off = ((size_t)bh * D + rg * RPT + m4 + x) * D + 4 * jq;
+                const f64x4 dt = p.detaT ? to_f64(*(const f32x4*)(p.detaT + off)) : f64x4{0., 0., 0., 0.};
+                const f64x4 pr = e[m4 + x] * dt;
+                sp[x] = (pr[0] + pr[1]) + (pr[2] + pr[3]);
+                e[m4 + x] = dt;
+            }
+            *(f64x2*)&sm.rpart[grp][0][jq][rg * RPT + m4] = f64x2{sp[0], sp[1]};
+            *(f64x2*)&sm.rpart[grp][0][jq][rg * RPT + m4 + 2] = f64x2{sp[2], sp[3]};
+        }
+        __syncthreads();
+        if (kd) {
+#pragma unroll 8
+            for (int x = 0; x < VQ; ++x) Bsum += sm.rpart[grp][0][x][i];
+        }
+        if constexpr (ISO) Bsum = kdim_sum<D, NH, TB>(Bsum, sm.red, grp, 0, 0, lt);
+        __syncthreads();
+    }
+
+    // ---------------------------------------------------------------- sweep 2
+    double lbar = ISO ? (p.dlT ? p.dlT[bh] : 0.f) : (p.dlT ? p.dlT[(size_t)bh * D + i] : 0.f);
+    double cum = Bsum;
+    double dqn_acc = 0.;
+    // backward coefficients of block [t0, t0+nb): gate of the token after
+    // each (1 past the end), k/r, q/l; and the v, dO rows
+    auto bwd_coefs = [&](int t0, int nb) {
+        stage_rows(t0, nb);
+        if (kd) {
+#pragma unroll
+            for (int u = 0; u < TB; ++u) {
+                if (u < nb) {
+                    const int t = t0 + u;
+                    const size_t tt = row0 + t;
+                    const double lt_ = wl[(size_t)t * NL + (ISO ? 0 : i)];
+                    double gn = 1., rd;
+                    if (t + 1 < T) {
+                        const double an = ISO ? p.a[tt + 1] : p.a[(tt + 1) * D + i];
+                        const double qnn = ISO ? p.qn[tt + 1] : qn_i;
+                        gn = gate_of(an, qnn, lt_, &rd);
+                    }
+                    sm.g[grp][u][i] = (float)gn;
+                    sm.kap[grp][u][i] = (float)((double)(float)k[tt * D + i] / (double)p.r[tt]);
+                    sm.cq[grp][u][i] = (float)((double)(float)q[tt * D + i] / lt_);
+                }
+            }
+        }
+    };
+    const int nblk = (T + TB - 1) / TB;
+    if (T > 0) bwd_coefs((nblk - 1) * TB, T - (nblk - 1) * TB);
+    __syncthreads();
+    for (int blk = nblk - 1; blk >= 0; --blk) {
+        const int t0 = blk * TB;
+        const int nb = T - t0 < TB ? T - t0 : TB;
+        // ---- ebar over the block's tokens, last first; U and dv partials
+#pragma unroll
+        for (int u = TB - 1; u >= 0; --u) {
+            if (u < nb) {
+                const f64x4 vv = to_f64(*(const f32x4*)&sm.v[grp][u][4 * jq]);
+                const f64x4 dd = to_f64(*(const f32x4*)&sm.dO[grp][u][4 * jq]);
+                f64x4 cs = {0., 0., 0., 0.};
+#pragma unroll
+                for (int m4 = 0; m4 < RPT; m4 += 4) {
+                    const f32x4 gv = *(const f32x4*)&sm.g[grp][u][rg * RPT + m4];
+                    const f32x4 cv = *(const f32x4*)&sm.cq[grp][u][rg * RPT + m4];
+                    const f32x4 kv = *(const f32x4*)&sm.kap[grp][u][rg * RPT + m4];
+                    double sp[4];
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        e[m4 + x] = (double)gv[x] * e[m4 + x] + (double)cv[x] * dd;
+                        const f64x4 pr = e[m4 + x] * vv;
+                        sp[x] = (pr[0] + pr[1]) + (pr[2] + pr[3]);
+                        cs += (double)kv[x] * e[m4 + x];
+                    }
+                    *(f64x2*)&sm.rpart[grp][u][jq][rg * RPT + m4] = f64x2{sp[0], sp[1]};
+                    *(f64x2*)&sm.rpart[grp][u][jq][rg * RPT + m4 + 2] = f64x2{sp[2], sp[3]};
+                }
+                sm.cpart[grp][u][lt] = f32x4{(float)cs[0], (float)cs[1], (float)cs[2], (float)cs[3]};
+            }
+        }
+        __syncthreads();
+        // ---- dv of the block (value-quad lanes)
+        if (lt < TB * VQ && lt / VQ < nb) {
+            const int u = lt / VQ;
+            f32x4 s = sm.cpart[grp][u][jq];
+#pragma unroll
+            for (int r2 = 1; r2 < RG; ++r2) s += sm.cpart[grp][u][r2 * VQ + jq];
+            if (valid) *(typename Quad<TIn>::V*)((TIn*)p.gv + (row0 + t0 + u) * D + 4 * jq) = Quad<TIn>::make(s);
+        }
+        // ---- the precision adjoint over the block (key-dim lanes; the others
+        // compute along and store nothing), last first
+#pragma unroll
+        for (int u = TB - 1; u >= 0; --u) {
+            if (u < nb) {
+                const int t = t0 + u;
+                const size_t tt = row0 + t;
+                double Uv = 0.;
+#pragma unroll 8
+                for (int x = 0; x < VQ; ++x) Uv += sm.rpart[grp][u][x][i];
+                const double kv = (float)k[tt * D + i];
+                const double rt = p.r[tt];
+                const double kap = (float)(kv / rt);  // the staged k/r of the state update
+                const double lt_ = wl[(size_t)t * NL + (ISO ? 0 : i)];
+                const double lprev = t == 0 ? l_start : wl[(size_t)(t - 1) * NL + (ISO ? 0 : i)];
+                double a, qn, qdq, kU;
+                if constexpr (ISO) {
+                    a = p.a[tt];
+                    qn = p.qn[tt];
+                    qdq = wqdq[t];
+                    kU = kdim_sum<D, NH, TB>(kd ? kap * Uv : 0., sm.red, grp, u, 0, lt);
+                } else {
+                    a = p.a[tt * D + i];
+                    qn = qn_i;
+                    qdq = wqdq[(size_t)t * D + i];
+                    kU = kap * Uv;
+                }
+                lbar -= qdq / lt_;
+                cum += qdq - kU;
+                const double dlg = cum;
+                const double den = a * a + qn * lprev;
+                const double rd = 1. / den, rd2 = rd * rd;
+                const double bscale = ISO ? 1. / (double)D : 1.;
+                const double dk = Uv / rt + lbar * 2. * kv * bscale / rt;
+                if (kd && valid) ((TIn*)p.gk)[tt * D + i] = (TIn)(float)dk;
+                // dr: -(kap U + lbar b_i) / r, summed over key dims
+                const double drp = -(kap * Uv + lbar * kv * kv * bscale / rt) / rt;
+                const double dr = kdim_sum<D, NH, TB>(kd ? drp : 0., sm.red, grp, u, 1, lt);
+                if (lt == 0 && valid) p.gr[tt] = (float)dr;
+                const double da = -lbar * 2. * a * lprev * rd2 + dlg * (qn * lprev - a * a) * rd / a;
+                const double dqn = -lbar * lprev * lprev * rd2 - dlg * lprev * rd;
+                if constexpr (ISO) {
+                    if (lt == 0 && valid) {
+                        p.ga[tt] = (float)da;
+                        p.gqn[tt] = (float)dqn;
+                    }
+                } else {
+                    if (kd && valid) p.ga[tt * D + i] = (float)da;
+                    dqn_acc += dqn;
+                }
+                lbar = lbar * a * a * rd2 - dlg * qn * rd;
+            }
+        }
+        if (blk > 0) bwd_coefs(t0 - TB, TB);
+        __syncthreads();
+    }
+    // ---- initial-state gradients: deta0 = g_0 ebar_0, dl0 = lbar_{-1}
+    if (T > 0 && kd) {
+        const double a0 = ISO ? p.a[row0] : p.a[row0 * D + i];
+        const double qn0 = ISO ? p.qn[row0] : qn_i;
+        double rd;
+        sm.g[grp][0][i] = (float)gate_of(a0, qn0, l_start, &rd);
+    }
+    __syncthreads();
+    if (!valid) return;
+    if (p.geta0) {
+#pragma unroll
+        for (int m4 = 0; m4 < RPT; m4 += 4) {
+            const f32x4 gv = T > 0 ? *(const f32x4*)&sm.g[grp][0][rg * RPT + m4] : f32x4{1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const f64x4 r4 = (double)gv[x] * e[m4 + x];
+                *(f32x4*)(p.geta0 + ((size_t)bh * D + rg * RPT + m4 + x) * D + 4 * jq) =
+                    f32x4{(float)r4[0], (float)r4[1], (float)r4[2], (float)r4[3]};
+            }
+        }
+    }
+    if (kd) {
+        if (p.gl0 && (!ISO || lt == 0)) p.gl0[(size_t)bh * NL + (ISO ? 0 : i)] = (float)lbar;
+        if (!ISO) wdqn[i] = (float)dqn_acc;
+    }
+}
+
+// dqn[h, i] = sum over b of the per-(b,h) partials (in order of b).
+__global__ void kla_bwd_dqn_sum(BwdArgs p) {
+    const int n = p.H * p.dk;
+    const int x = blockIdx.x * blockDim.x + threadIdx.x;
+    if (x >= n) return;
+    const int h = x / p.dk, i = x % p.dk;
+    const size_t off = (size_t)p.T * p.dk * 4;  // floats to the partial (after l_t and q dq, fp64)
+    float s = 0.f;
+    for (int b = 0; b < p.B; ++b) s += p.ws[(size_t)(b * p.H + h) * p.ws_stride + off + i];
+    p.gqn[x] = s;
+}
+
+template <typename TIn, bool ISO>
+hipError_t dispatch(const BwdArgs& a, hipStream_t s) {
+    const dim3 block(kBwdThreads);
+    const int nbh = a.B * a.H;
+    auto grid = [&](int nh) { return dim3((nbh + nh - 1) / nh); };
+    if (nbh > 0) switch (a.dk) {
+        case 16: hipLaunchKernelGGL((kla_bwd_kernel<TIn, 16, ISO>), grid(BwdLayout<16>::NH), block, 0, s, a); break;
+        case 32: hipLaunchKernelGGL((kla_bwd_kernel<TIn, 32, ISO>), grid(BwdLayout<32>::NH), block, 0, s, a); break;
+        case 64: hipLaunchKernelGGL((kla_bwd_kernel<TIn, 64, ISO>), grid(BwdLayout<64>::NH), block, 0, s, a); break;
+        case 128: hipLaunchKernelGGL((kla_bwd_kernel<TIn, 128, ISO>), grid(BwdLayout<128>::NH), block, 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || ISO) return e;
+    const int n = a.H * a.dk;
+    hipLaunchKernelGGL(kla_bwd_dqn_sum, dim3((n + 255) / 256), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool bwd_supported(int dk, int dv) { return dk == dv && (dk == 16 || dk == 32 || dk == 64 || dk == 128); }
+
+size_t bwd_ws_stride(int T, int dk, int cov) {
+    const size_t nl = cov ? 1 : (size_t)dk;
+    // l_t and q dq (fp64), the diagonal qn partial (fp32)
+    const size_t n = (size_t)T * nl * 4 + (cov ? 0 : (size_t)dk);
+    return (n + 63) / 64 * 64;  // floats; 256-byte aligned per (b,h)
+}
+
+hipError_t launch_bwd(const BwdArgs& a, int dtype, int cov, hipStream_t s) {
+    if (!bwd_supported(a.dk, a.dv)) return hipErrorInvalidValue;
+    if (dtype == DT_BF16) return cov ? dispatch<bf16, true>(a, s) : dispatch<bf16, false>(a, s);
+    return cov ? dispatch<float, true>(a, s) : dispatch<float, false>(a, s);
+}
+
+}  // namespace kla

@@ -134,3 +134,16 @@ def make_state(w: Workload, seed: int, device="cpu") -> dict:
     l0 = _softplus(torch.randn(*nl, generator=g, dtype=torch.float64)) + 0.2
     eta0 = torch.randn(w.B, w.H, w.dk, w.dv, generator=g, dtype=torch.float64)
     return {"l0": l0.to(torch.float32).to(device), "eta0": eta0.to(torch.float32).to(device)}
+
+
+def make_upstream(w: Workload, seed: int, device="cpu") -> dict:
+    """Upstream gradients for a backward pass of workload w: do ~ N(0,1) in the
+    storage dtype [B,H,T,dv]; dlT ~ N(0,1) (shape of lT) and detaT ~ N(0,1)
+    [B,H,dk,dv] in fp32."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    nl = (w.B, w.H, w.dk) if w.cov == "diag" else (w.B, w.H)
+    do = torch.randn(w.B, w.H, w.T, w.dv, generator=g, dtype=torch.float64)
+    dlT = torch.randn(*nl, generator=g, dtype=torch.float64)
+    detaT = torch.randn(w.B, w.H, w.dk, w.dv, generator=g, dtype=torch.float64)
+    return {"do": do.to(_TORCH_DTYPE[w.dtype]).to(device), "dlT": dlT.to(torch.float32).to(device),
+            "detaT": detaT.to(torch.float32).to(device)}

@@ -235,3 +235,41 @@ def test_residual_argument_errors():
     assert res_call(d, lT=addr(7)) == ALIAS          # lT over l0
     assert res_call(d, mT=addr(8) + 16) == ALIAS     # mT inside m0
     assert res_call(KlaDims(0, 4, 16, 16, 16, F32, DIAG)) == OK
+
+
+# ------------------------------------------------------------------ klaBwd
+
+def bwd_call(d, **over):
+    names = ("q", "k", "v", "a", "qnoise", "r", "l0", "eta0", "dO", "dlT", "detaT",
+             "dq", "dk", "dv", "da", "dqnoise", "dr", "dl0", "deta0")
+    args = {n: addr(i + 1) for i, n in enumerate(names)}
+    args.update(workspace=addr(40), workspaceBytes=scan_amd.klaBwdWorkspaceBytes(d), stream=None)
+    args.update(over)
+    return scan_amd.klaBwd(d, **args)
+
+
+def test_backward_argument_errors():
+    lib = scan_amd.load()
+    assert lib.klaBwd(None, *([None] * 19), None, 0, None) == NULL
+    d = KlaDims(2, 3, 16, 32, 32, BF16, DIAG)
+    # per (b,h): l_t and q dq fp64 [T][dk], qn partial fp32 [dk]
+    per = 16 * 32 * 4 + 32
+    assert scan_amd.klaBwdWorkspaceBytes(d) == 2 * 3 * 4 * ((per + 63) // 64 * 64)
+    for field in ("B", "H", "T", "dk", "dv"):
+        bad = KlaDims(2, 3, 16, 32, 32, BF16, DIAG)
+        setattr(bad, field, -1)
+        assert bwd_call(bad) == SHAPE, field
+    for dims in [(1, 1, 8, 48, 48), (1, 1, 8, 64, 32), (1, 1, 8, 256, 256)]:
+        assert bwd_call(KlaDims(*dims, F32, DIAG)) == UNSUP, dims
+        assert scan_amd.klaBwdWorkspaceBytes(KlaDims(*dims, F32, DIAG)) == 0
+    assert bwd_call(KlaDims(1, 2, 16, 16, 16, 7, DIAG)) == UNSUP
+    for name in ("q", "k", "v", "a", "qnoise", "r", "dO", "dq", "dk", "dv", "da", "dqnoise", "dr"):
+        assert bwd_call(d, **{name: None}) == NULL, name
+    for name in ("q", "dO", "dq", "dqnoise", "dl0", "deta0", "detaT", "workspace"):
+        assert bwd_call(d, **{name: addr(50) + 4}) == ALIGN, name
+    assert bwd_call(d, workspace=None) == WS
+    assert bwd_call(d, workspaceBytes=16) == WS
+    assert bwd_call(d, dq=addr(2)) == ALIAS             # dq over k
+    assert bwd_call(d, dk=addr(12) + 16) == ALIAS       # dk inside dq
+    assert bwd_call(d, workspace=addr(14)) == ALIAS     # workspace over da
+    assert bwd_call(KlaDims(0, 4, 16, 16, 16, F32, ISO)) == OK
