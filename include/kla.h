@@ -123,6 +123,24 @@ klaStatus klaFwd(const klaDims* d,
                  void* workspace, size_t workspaceBytes, void* hipStream);
 
 /*
+ * klaFwd for callers that cannot allocate: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  Same arguments, results
+ * and errors as klaFwd, without the workspace: when the call needs one
+ * (klaFwdWorkspaceBytes(d) > 0, the sequence split of few, long diagonal
+ * sequences) it uses a device array of the library, 64 MiB per GPU, held from
+ * the library's load until the process ends.  A call that needs more returns
+ * KLA_ERR_WORKSPACE before any HIP call.  No memory is allocated or freed.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (several streams or host threads) race and must be serialised by the
+ * caller.
+ */
+klaStatus klaFwdNoAlloc(const klaDims* d,
+                        const void* q, const void* k, const void* v,
+                        const float* a, const float* qnoise, const float* r,
+                        const float* l0, const float* eta0,
+                        void* o, float* lT, float* etaT, void* hipStream);
+
+/*
  * One decode step for every (b,h) (the same recurrence with T = 1;
  * constant-memory decoding, [KDN]).  State is updated in place.
  * Layouts: q, k [B,H,dk]; v, o [B,H,dv]; r [B,H];

@@ -19,7 +19,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["klaFwd", "klaStep", "klaFwdResidual", "klaBwd", "klaFwdWorkspaceBytes",
+__all__ = ["klaFwd", "klaFwdNoAlloc", "klaStep", "klaFwdResidual", "klaBwd", "klaFwdWorkspaceBytes",
            "klaBwdWorkspaceBytes", "klaIsSupported", "klaStatusString", "KlaDims", "KlaError", "fwd",
            "step", "fwd_residual", "bwd", "lib_path", "load"]
 
@@ -81,6 +81,8 @@ def load():
     lib.klaStatusString.restype = ctypes.c_char_p
     lib.klaFwdKernelName.argtypes = [dp]
     lib.klaFwdKernelName.restype = ctypes.c_char_p
+    lib.klaFwdNoAlloc.argtypes = [dp, vp, vp, vp, fp, fp, fp, fp, fp, vp, fp, fp, vp]
+    lib.klaFwdNoAlloc.restype = ctypes.c_int
     lib.klaBwdWorkspaceBytes.argtypes = [dp]
     lib.klaBwdWorkspaceBytes.restype = sz
     lib.klaBwd.argtypes = [dp] + [vp] * 19 + [vp, sz, vp]
@@ -104,6 +106,12 @@ def klaFwd(dims, q, k, v, a, qnoise, r, l0, eta0, o, lT, etaT, workspace, worksp
     """Raw call: pointer arguments are ints (device addresses) or None."""
     return int(load().klaFwd(ctypes.byref(dims), q, k, v, a, qnoise, r, l0, eta0, o, lT, etaT,
                              workspace, workspaceBytes, stream))
+
+
+def klaFwdNoAlloc(dims, q, k, v, a, qnoise, r, l0, eta0, o, lT, etaT, stream) -> int:
+    """Raw call of the forward that takes no workspace (pointers as ints or None)."""
+    return int(load().klaFwdNoAlloc(ctypes.byref(dims), q, k, v, a, qnoise, r, l0, eta0, o, lT, etaT,
+                                    stream))
 
 
 def klaStep(dims, q, k, v, a, qnoise, r, l, eta, o, stream) -> int:

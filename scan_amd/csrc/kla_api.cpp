@@ -159,9 +159,16 @@ size_t klaFwdWorkspaceBytes(const klaDims* d) {
     return seg_bytes(d, pick_nseg(d));
 }
 
-klaStatus klaFwd(const klaDims* d, const void* q, const void* k, const void* v, const float* a,
-                 const float* qnoise, const float* r, const float* l0, const float* eta0, void* o,
-                 float* lT, float* etaT, void* workspace, size_t workspaceBytes, void* hipStream) {
+}  // extern "C"
+
+namespace {
+
+// klaFwd, or (scratch) klaFwdNoAlloc: the split workspace is then the
+// library's device scratch, looked up after every host check has passed.
+klaStatus fwd_entry(const klaDims* d, const void* q, const void* k, const void* v, const float* a,
+                    const float* qnoise, const float* r, const float* l0, const float* eta0, void* o,
+                    float* lT, float* etaT, void* workspace, size_t workspaceBytes, void* hipStream,
+                    bool scratch) {
     if (!d) return KLA_ERR_NULL;
     if (!dims_ok(d)) return KLA_ERR_SHAPE;
     if (!kinds_ok(d) || !supported(d)) return KLA_ERR_UNSUPPORTED;
@@ -183,8 +190,12 @@ klaStatus klaFwd(const klaDims* d, const void* q, const void* k, const void* v, 
         if (p && !aligned16(p)) return KLA_ERR_ALIGN;
 
     const size_t wneed = klaFwdWorkspaceBytes(d);
-    if (wneed > 0 && (!workspace || workspaceBytes < wneed)) return KLA_ERR_WORKSPACE;
-    if (wneed > 0 && !aligned16(workspace)) return KLA_ERR_ALIGN;
+    if (scratch) {
+        if (wneed > kla::kNoAllocScratchBytes) return KLA_ERR_WORKSPACE;
+    } else {
+        if (wneed > 0 && (!workspace || workspaceBytes < wneed)) return KLA_ERR_WORKSPACE;
+        if (wneed > 0 && !aligned16(workspace)) return KLA_ERR_ALIGN;
+    }
 
     const size_t ntk = (size_t)(BH * T);
     const Span s_o = span(o, ntk * dv * es);
@@ -197,11 +208,16 @@ klaStatus klaFwd(const klaDims* d, const void* q, const void* k, const void* v, 
         if (overlap(s_o, s) || overlap(s_lT, s) || overlap(s_etaT, s)) return KLA_ERR_ALIAS;
     }
     if (overlap(s_o, s_lT) || overlap(s_o, s_etaT) || overlap(s_lT, s_etaT)) return KLA_ERR_ALIAS;
-    if (wneed > 0) {
+    if (wneed > 0 && !scratch) {
         const Span s_ws = span(workspace, wneed);
         for (const Span& s : ins)
             if (overlap(s_ws, s)) return KLA_ERR_ALIAS;
         if (overlap(s_ws, s_o) || overlap(s_ws, s_lT) || overlap(s_ws, s_etaT)) return KLA_ERR_ALIAS;
+    }
+
+    if (scratch && wneed > 0) {
+        // the static device array stands in for the caller's workspace
+        if (kla::noalloc_scratch(&workspace) != hipSuccess) return KLA_ERR_HIP;
     }
 
     kla::FwdArgs fa;
@@ -249,6 +265,23 @@ klaStatus klaFwd(const klaDims* d, const void* q, const void* k, const void* v, 
     }
     if (e == hipErrorInvalidValue) return KLA_ERR_UNSUPPORTED;
     return e == hipSuccess ? KLA_OK : KLA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+klaStatus klaFwd(const klaDims* d, const void* q, const void* k, const void* v, const float* a,
+                 const float* qnoise, const float* r, const float* l0, const float* eta0, void* o,
+                 float* lT, float* etaT, void* workspace, size_t workspaceBytes, void* hipStream) {
+    return fwd_entry(d, q, k, v, a, qnoise, r, l0, eta0, o, lT, etaT, workspace, workspaceBytes,
+                     hipStream, false);
+}
+
+klaStatus klaFwdNoAlloc(const klaDims* d, const void* q, const void* k, const void* v, const float* a,
+                        const float* qnoise, const float* r, const float* l0, const float* eta0,
+                        void* o, float* lT, float* etaT, void* hipStream) {
+    return fwd_entry(d, q, k, v, a, qnoise, r, l0, eta0, o, lT, etaT, nullptr, 0, hipStream, true);
 }
 
 klaStatus klaStep(const klaDims* d, const void* q, const void* k, const void* v, const float* a,

@@ -67,6 +67,12 @@ hipError_t launch_seg_carry_l(const FwdArgs& a, const float* P, hipStream_t s);
 hipError_t launch_seg_carry_m(const FwdArgs& a, hipStream_t s);
 hipError_t launch_seg_correct(const FwdArgs& a, int dtype, hipStream_t s);
 
+// Device scratch of klaFwdNoAlloc (kla_noalloc.hip): the largest sequence-
+// split workspace that entry point serves, and the address of the current
+// device's copy (looked up once per device).
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 struct StepArgs {
     const void* q;
     const void* k;
