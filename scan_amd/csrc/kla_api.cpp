@@ -61,6 +61,14 @@ int env_vtiles() {
     return atoi(s);
 }
 
+// KLA_DIAG_CHAIN=scan runs the diagonal precision of the wave-specialised
+// kernel as a wavefront-level Mobius scan (bf16 inputs); default: the
+// per-lane serial recursion, which measured faster.
+bool use_chain_scan() {
+    const char* s = getenv("KLA_DIAG_CHAIN");
+    return s && s[0] == 's';
+}
+
 // KLA_FWD_SHORT=0 keeps short sequences (T <= kShortTMax) on the chunked
 // kernels instead of the short-sequence kernel.
 bool use_short() {
@@ -224,6 +232,7 @@ klaStatus fwd_entry(const klaDims* d, const void* q, const void* k, const void* 
     fa.q = q; fa.k = k; fa.v = v; fa.a = a; fa.qn = qnoise; fa.r = r;
     fa.l0 = l0; fa.eta0 = eta0; fa.o = o; fa.lT = lT; fa.etaT = etaT;
     fa.B = (int)B; fa.H = (int)H; fa.T = (int)T; fa.dk = (int)dk; fa.dv = (int)dv;
+    fa.chain_scan = use_chain_scan();
     hipStream_t st = (hipStream_t)hipStream;
 
     hipError_t e;

@@ -16,7 +16,10 @@
 //   chain waves  (one lane per key dim) run the sequential precision recursion
 //                of chunk c+2: four dependent VALU ops per token.  They write
 //                (a*lp, l) to LDS and flag the chunk if some cumulative gate
-//                product inside it drops below 2^-64;
+//                product inside it drops below 2^-64.  A second chain role
+//                (chain_role_scan, selected at launch) computes the same
+//                chunk as a wavefront-level Mobius scan over lanes that own
+//                4 key dims x 8 tokens;
 //   gate waves   turn chunk c+1's precisions into gates f, w and cumulative
 //                products G (lanes own 2 key dims x 8 tokens at dk 128, x 4
 //                at dk 64; the products cross token groups with DPP row
@@ -97,7 +100,7 @@ struct S3 {
         OpRaw<K> raw;
     } op[2];                      // MFMA operands (or raw gates) by chunk parity
     TIn VT[2][K::DV][K::CS];      // v^T by chunk parity
-    float rho[2][K::C];           // 1/r_t by chunk parity
+    alignas(16) float rho[2][K::C];  // 1/r_t by chunk parity
     alignas(16) float sc[2][K::DK];  // state scale before the chunk's readout
     alignas(16) float E[2][K::DK];   // end-of-chunk gate product (pending state scale)
     float lT[K::DK];
@@ -317,6 +320,252 @@ __device__ void chain_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int
         if (vt == 0) {
             p.seg_d[((size_t)bh * p.nseg + sp.seg) * DK + i] = wrun;
             if (sp.last) p.seg_lend[(size_t)bh * DK + i] = l;
+        }
+    }
+    lds_barrier();
+}
+
+// ------------------------------------------------------------------ chain role, wavefront-level Mobius scan
+// The precision map of one token, l -> ((1 + b qn) l + b a^2) / (qn l + a^2)
+// with b = k^2 / r, is the 2x2 projective matrix [[1 + b qn, b a^2], [qn, a^2]]
+// = [[1, b], [0, 1]] [[1, 0], [qn, a^2]]; maps compose as matrix products and
+// any positive multiple of a matrix is the same map.
+struct Mob {
+    float p11, p12, p21, p22;
+};
+
+__device__ __forceinline__ Mob mob_identity() { return Mob{1.f, 0.f, 0.f, 1.f}; }
+
+// P <- M(b, a^2, qn) P (the token after the ones P already holds)
+__device__ __forceinline__ void mob_push(Mob& P, float b, float a2, float qn) {
+    const float r1 = __builtin_fmaf(qn, P.p11, a2 * P.p21);
+    const float r2 = __builtin_fmaf(qn, P.p12, a2 * P.p22);
+    P.p11 = __builtin_fmaf(b, r1, P.p11);
+    P.p12 = __builtin_fmaf(b, r2, P.p12);
+    P.p21 = r1;
+    P.p22 = r2;
+}
+
+// the map of Y followed by X, i.e. X Y
+__device__ __forceinline__ Mob mob_mul(const Mob& X, const Mob& Y) {
+    return Mob{__builtin_fmaf(X.p11, Y.p11, X.p12 * Y.p21), __builtin_fmaf(X.p11, Y.p12, X.p12 * Y.p22),
+               __builtin_fmaf(X.p21, Y.p11, X.p22 * Y.p21), __builtin_fmaf(X.p21, Y.p12, X.p22 * Y.p22)};
+}
+
+// divides by the entry sum (the entries are non-negative)
+__device__ __forceinline__ void mob_norm(Mob& P) {
+    const float s = fast_rcp((P.p11 + P.p12) + (P.p21 + P.p22));
+    P.p11 *= s;
+    P.p12 *= s;
+    P.p21 *= s;
+    P.p22 *= s;
+}
+
+__device__ __forceinline__ Mob mob_shfl_up(const Mob& P, int delta) {
+    return Mob{__shfl_up(P.p11, delta, 64), __shfl_up(P.p12, delta, 64), __shfl_up(P.p21, delta, 64),
+               __shfl_up(P.p22, delta, 64)};
+}
+
+// Chain waves: the precision of chunk c+2, as a wavefront-level Mobius scan.
+// Lane (dq = lane % 16, tg = lane / 16) owns key dims i0..i0+3 (i0 = 64 cw +
+// 4 dq) and tokens 8 tg .. 8 tg + 7 of the chunk.  Each lane composes its
+// eight tokens' maps for its four key dims; a scan over the four token groups
+// (lane shifts of 16 and 32) gives every group the map of the tokens before
+// it, which applied to the chunk's carried precision gives the group's
+// starting precision; then each lane runs the recursion over its eight
+// tokens, writes (a lp, l) to LDS and forms its share of the chunk's gate
+// product.  Rows arrive as 16-byte (a) and 8/16-byte (k) loads, 18 per lane
+// and chunk, one chunk ahead.
+template <typename TIn, class K, bool SEG>
+__device__ void chain_role_scan(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int bh, int vt, int cw,
+                           int lane) {
+    constexpr int C = K::C, DK = K::DK, TPL = 8;  // tokens per lane
+    static_assert(C == 4 * TPL, "four token groups of eight");
+    typedef typename Quad<TIn>::V QV;
+    const int dq = lane & 15, tg = lane >> 4;
+    const int i0 = cw * 64 + 4 * dq;
+    const size_t rowbase = (size_t)bh * p.T + sp.T0;
+    const int nchunks = (sp.TL + C - 1) / C;
+    const int nsteps = pipe_steps<K>(nchunks);
+    const TIn* kp = (const TIn*)p.k;
+
+    float lin[4], qn[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int i = i0 + e;
+        lin[e] = SEG ? p.seg_l0[((size_t)bh * p.nseg + sp.seg) * DK + i] : (p.l0 ? p.l0[(size_t)bh * DK + i] : 1.f);
+        qn[e] = p.qn[(size_t)(bh % p.H) * DK + i];
+    }
+    float wrun[4] = {1.f, 1.f, 1.f, 1.f};  // sequence split: gate product from the segment start
+    constexpr int NB = K::NBC, D = NB - 1;
+    struct Buf {
+        f32x4 a[TPL];  // a of the lane's four key dims, per token
+        QV k[TPL];     // k likewise
+        f32x4 r[2];    // r of the lane's eight tokens
+    };
+    constexpr int NLD = 2 * TPL + 2;  // loads per chunk
+    Buf b[NB];
+    constexpr int ES = (int)sizeof(TIn), ARB = DK * 4, KRB = DK * ES;  // row bytes
+    const char* abase = (const char*)(p.a + rowbase * DK);
+    const char* kbase = (const char*)(kp + rowbase * DK);
+    const char* rbase = (const char*)(p.r + rowbase);
+    const int aoff = TPL * tg * ARB + i0 * 4, koff = TPL * tg * KRB + i0 * ES, roff = TPL * tg * 4;
+    auto load = [&](int c, Buf& bf) {
+        const int t0 = c * C, n = sp.TL - t0;
+        const int rows = n < 0 ? 0 : (n < C ? n : C);
+        // rows past the segment's end read as zero
+        const auto ra = make_rsrc(abase + (size_t)t0 * ARB, rows * ARB);
+        const auto rk = make_rsrc(kbase + (size_t)t0 * KRB, rows * KRB);
+        const auto rr = make_rsrc(rbase + (size_t)t0 * 4, rows * 4);
+#pragma unroll
+        for (int u = 0; u < TPL; ++u) {
+            bf.a[u] = buf_load<f32x4>(ra, aoff + u * ARB);
+            bf.k[u] = buf_load<QV>(rk, koff + u * KRB);
+        }
+        bf.r[0] = buf_load<f32x4>(rr, roff);
+        bf.r[1] = buf_load<f32x4>(rr, roff + 16);
+    };
+    auto step = [&](int c, Buf& cur, Buf& nxt) {
+        const int cc = c + 2;  // chunk scanned in this iteration
+        wait_loads<(D - 1) * NLD>();
+        if (nchunks > 0) load(cc + D, nxt);
+        if (cc < nchunks) {
+            const int L = chunk_len(sp.TL, cc, C), par = cc & 1;
+            const int tb = TPL * tg;  // the lane's first token
+            float rho[TPL];
+#pragma unroll
+            for (int u = 0; u < TPL; ++u) rho[u] = tb + u < L ? fast_rcp(cur.r[u / 4][u % 4]) : 0.f;
+            if (cw == 0 && dq == 0) {
+                *(f32x4*)&sm.rho[par][tb] = f32x4{rho[0], rho[1], rho[2], rho[3]};
+                *(f32x4*)&sm.rho[par][tb + 4] = f32x4{rho[4], rho[5], rho[6], rho[7]};
+            }
+            float f0[4] = {1.f, 1.f, 1.f, 1.f}, Gp[4] = {1.f, 1.f, 1.f, 1.f}, lfin[4];
+            // full chunks take a copy without per-token tests
+            auto scan = [&](auto full) {
+                constexpr bool FULL = decltype(full)::value;
+                // ---- this lane's eight maps, composed per key dim
+                Mob P[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) P[e] = mob_identity();
+#pragma unroll
+                for (int u = 0; u < TPL; ++u) {
+                    if (FULL || tb + u < L) {
+                        const f32x4 kv = Quad<TIn>::to_f32(cur.k[u]);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float a = cur.a[u][e];
+                            mob_push(P[e], kv[e] * kv[e] * rho[u], a * a, qn[e]);
+                        }
+                    }
+                    if (u == TPL / 2 - 1) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) mob_norm(P[e]);
+                    }
+                }
+                // ---- scan over the four token groups: the map of every token
+                // before the group, applied to the chunk's carried precision
+                float ls[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    mob_norm(P[e]);
+                    Mob Y = mob_shfl_up(P[e], 16);
+                    if (tg >= 1) P[e] = mob_mul(P[e], Y);
+                    mob_norm(P[e]);
+                    Y = mob_shfl_up(P[e], 32);
+                    if (tg >= 2) P[e] = mob_mul(P[e], Y);
+                    Mob E = mob_shfl_up(P[e], 16);
+                    if (tg == 0) E = mob_identity();
+                    ls[e] = __builtin_fmaf(E.p11, lin[e], E.p12) * fast_rcp(__builtin_fmaf(E.p21, lin[e], E.p22));
+                }
+                // ---- the recursion over the lane's tokens
+                float num[4] = {1.f, 1.f, 1.f, 1.f}, den[4] = {1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+                for (int u = 0; u < TPL; ++u) {
+                    const int t = tb + u;
+                    if (FULL || t < L) {
+                        const f32x4 kv = Quad<TIn>::to_f32(cur.k[u]);
+                        float alp[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float a = cur.a[u][e];
+                            const float lp = ls[e] * fast_rcp(__builtin_fmaf(qn[e], ls[e], a * a));
+                            ls[e] = __builtin_fmaf(kv[e] * kv[e], rho[u], lp);
+                            alp[e] = a * lp;
+                            if (t >= 1) {
+                                num[e] *= alp[e];
+                                den[e] *= ls[e];
+                            } else {
+                                f0[e] = alp[e] * fast_rcp(ls[e]);
+                            }
+                        }
+                        const int j = i0 ^ lp_swz(t);
+                        *(f32x4*)&sm.LP[par][t][j] = f32x4{alp[0], ls[0], alp[1], ls[1]};
+                        *(f32x4*)&sm.LP[par][t][j + 2] = f32x4{alp[2], ls[2], alp[3], ls[3]};
+                    }
+                    if (u == TPL / 2 - 1) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            Gp[e] *= num[e] * fast_rcp(den[e]);
+                            num[e] = 1.f;
+                            den[e] = 1.f;
+                        }
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    Gp[e] *= num[e] * fast_rcp(den[e]);
+                    lfin[e] = ls[e];
+                }
+            };
+            if (L == C) scan(std::true_type{});
+            else scan(std::false_type{});
+            // the chunk's gate product (tokens 1..), the precision it leaves
+            // (after the last group), and token 0's gate, in every lane of the
+            // key-dim quad
+            float G[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                G[e] = Gp[e] * __shfl_xor(Gp[e], 16, 64);
+                G[e] *= __shfl_xor(G[e], 32, 64);
+                lin[e] = __shfl(lfin[e], 48 + dq, 64);
+                f0[e] = __shfl(f0[e], dq, 64);
+            }
+            const bool low = G[0] < kFloor || G[1] < kFloor || G[2] < kFloor || G[3] < kFloor;
+            if (__builtin_amdgcn_ballot_w64(low)) sm.bad[cc & 3] = 1;
+            if constexpr (SEG) {
+                f32x4 wc;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    wc[e] = wrun[e] * f0[e];  // through token 0
+                    wrun[e] = wc[e] * G[e];   // through the chunk's end
+                }
+                if (tg == 0) *(f32x4*)&sm.Wc[par][i0] = wc;
+            }
+        }
+        lds_barrier();
+    };
+
+    if (nchunks > 0) {
+#pragma unroll
+        for (int j = 0; j < D; ++j) load(j, b[j]);
+    }
+    // step c scans chunk c+2 from buffer (c+2) mod NB and loads chunk c+2+D
+    for (int c = -2; c < nsteps - 2; c += NB) {
+#pragma unroll
+        for (int s = 0; s < NB; ++s) step(c + s, b[s], b[(s + D) % NB]);
+    }
+    if (tg == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = i0 + e;
+            sm.lT[i] = lin[e];
+            if (sp.last && p.lT && vt == 0) p.lT[(size_t)bh * DK + i] = lin[e];
+            if constexpr (SEG) {
+                if (vt == 0) {
+                    p.seg_d[((size_t)bh * p.nseg + sp.seg) * DK + i] = wrun[e];
+                    if (sp.last) p.seg_lend[(size_t)bh * DK + i] = lin[e];
+                }
+            }
         }
     }
     lds_barrier();
@@ -692,7 +941,7 @@ __device__ void mma_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int b
     }
 }
 
-template <typename TIn, int DK, int DV, bool SEG>
+template <typename TIn, int DK, int DV, bool SEG, bool SCAN>
 __global__ __launch_bounds__((P3<TIn, DK, DV>::NT)) void kla_fwd_diag_pipe_kernel(FwdArgs p) {
     typedef P3<TIn, DK, DV> K;
     __shared__ S3<TIn, K> sm;
@@ -729,7 +978,8 @@ __global__ __launch_bounds__((P3<TIn, DK, DV>::NT)) void kla_fwd_diag_pipe_kerne
     static_assert(K::NCW <= 4 && K::NW >= 4 + K::NMW, "wave placement");
     if (wave < K::NCW) {
         __builtin_amdgcn_s_setprio(2);
-        chain_role<TIn, K, SEG>(sm, p, sp, bh, vt, wave, lane);
+        if constexpr (SCAN) chain_role_scan<TIn, K, SEG>(sm, p, sp, bh, vt, wave, lane);
+        else chain_role<TIn, K, SEG>(sm, p, sp, bh, vt, wave, lane);
     } else if (wave < 4) {
         gate_role<TIn, K, SEG>(sm, p, sp, bh, vt, wave - K::NCW, lane);
     } else if (wave < 4 + K::NMW) {
@@ -739,17 +989,27 @@ __global__ __launch_bounds__((P3<TIn, DK, DV>::NT)) void kla_fwd_diag_pipe_kerne
     }
 }
 
-template <typename TIn, int DK, int DV>
-hipError_t launch(const FwdArgs& a, hipStream_t s) {
+template <typename TIn, int DK, int DV, bool SCAN>
+hipError_t launch_chain(const FwdArgs& a, hipStream_t s) {
     typedef P3<TIn, DK, DV> K;
     if (a.nseg > 1) {
         const int nblk = a.B * a.H * a.n_vtiles * a.nseg;
-        hipLaunchKernelGGL((kla_fwd_diag_pipe_kernel<TIn, DK, DV, true>), dim3(nblk), dim3(K::NT), 0, s, a);
+        hipLaunchKernelGGL((kla_fwd_diag_pipe_kernel<TIn, DK, DV, true, SCAN>), dim3(nblk), dim3(K::NT), 0, s, a);
     } else {
         const int nblk = a.B * a.H * a.n_vtiles;
-        hipLaunchKernelGGL((kla_fwd_diag_pipe_kernel<TIn, DK, DV, false>), dim3(nblk), dim3(K::NT), 0, s, a);
+        hipLaunchKernelGGL((kla_fwd_diag_pipe_kernel<TIn, DK, DV, false, SCAN>), dim3(nblk), dim3(K::NT), 0, s, a);
     }
     return hipGetLastError();
+}
+
+// the serial chain by default; the wavefront-level scan chain on request
+// (bf16 inputs: the fp32 build of the scan chain spills)
+template <typename TIn, int DK, int DV>
+hipError_t launch(const FwdArgs& a, hipStream_t s) {
+    if constexpr (std::is_same<TIn, bf16>::value) {
+        if (a.chain_scan) return launch_chain<TIn, DK, DV, true>(a, s);
+    }
+    return launch_chain<TIn, DK, DV, false>(a, s);
 }
 
 }  // namespace

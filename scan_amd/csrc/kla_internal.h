@@ -23,6 +23,9 @@ struct FwdArgs {
     float* etaT;        // may be null
     int B, H, T, dk, dv;
     int n_vtiles;       // workgroups per (b,h) along the value dim
+    // diagonal wave-specialised kernel, bf16: run the precision as a
+    // wavefront-level Mobius scan instead of the per-lane serial recursion
+    bool chain_scan = false;
 
     // Sequence split (diagonal, wave-specialised kernel only).  With nseg > 1
     // the workgroup of segment s handles tokens [s*seg_len, min(T,(s+1)*seg_len))

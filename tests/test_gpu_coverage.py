@@ -183,3 +183,53 @@ def test_bitwise_deterministic_every_family(case):
         b = run_hip(inp, w.cov, st["l0"], st["eta0"])
         for k in a:
             assert np.array_equal(a[k], b[k]), (k, name, over)
+
+
+# ------------------------------------------------------------------ wavefront-level scan chain
+
+@pytest.mark.parametrize("name,over,nseg,state", [
+    ("lm_diag", dict(B=2, H=2, T=333), "", True),             # bf16 d128, ragged last chunk
+    ("lm_diag", dict(B=1, H=3, T=150, dk=64, dv=64), "", True),  # bf16 d64 (one chain wave)
+    ("long_diag", dict(B=1, H=2, T=3000), "3", True),         # sequence split
+    ("lm_diag", dict(B=8, H=16, T=2048), "", False),          # the LM-layer launch
+])
+def test_scan_chain_parity(monkeypatch, name, over, nseg, state):
+    """KLA_DIAG_CHAIN=scan: the diagonal precision of the wave-specialised
+    kernel as a wavefront-level Mobius scan (lanes own 4 key dims x 8 tokens,
+    group maps composed and scanned across lanes), at parity with the
+    oracle."""
+    _print_case("scan chain", name, over, nseg)
+    monkeypatch.setenv("KLA_DIAG_CHAIN", "scan")
+    if nseg:
+        monkeypatch.setenv("KLA_FWD_NSEG", nseg)
+    inp = gen.make_inputs(name, seed=71, **over)
+    w = inp["workload"]
+    assert scan_amd.fwd_kernel_name(w.B, w.H, w.T, w.dk, w.dv, cov="diag",
+                                    dtype=w.dtype).startswith("kla_fwd_diag_pipe_kernel")
+    l0 = eta0 = None
+    if state:
+        st = gen.make_state(w, seed=72)
+        l0, eta0 = st["l0"], st["eta0"]
+    hip = run_hip(inp, "diag", l0, eta0)
+    ref = run_oracle(inp, "diag", l0, eta0)
+    assert_parity(compare(hip, ref), w.dtype, f"scan chain {name} {over}")
+
+
+def test_scan_chain_adversarial(monkeypatch):
+    """The scan chain with a -> 0.01 (every 7th token 0.9), r = 1e-3, |k| up
+    to 5: group maps spanning many orders of magnitude (renormalised), gate
+    products below the floor (exact chunks)."""
+    _print_case("scan chain adversarial")
+    monkeypatch.setenv("KLA_DIAG_CHAIN", "scan")
+    inp = gen.make_inputs("small_diag", seed=73, B=1, H=2, T=200, dk=128, dv=128, dtype="bf16")
+    g = torch.Generator().manual_seed(74)
+    a = torch.full((1, 2, 200, 128), 0.01)
+    a[:, :, ::7] = 0.9
+    inp["a"] = a
+    inp["r"] = torch.full((1, 2, 200), 1e-3)
+    inp["k"] = (5 * (2 * torch.rand(1, 2, 200, 128, generator=g) - 1)).to(torch.bfloat16)
+    hip = run_hip(inp, "diag")
+    for k in hip:
+        assert np.all(np.isfinite(hip[k])), k
+    ref = run_oracle(inp, "diag")
+    assert_parity(compare(hip, ref), "bf16", "scan chain adversarial")
