@@ -53,7 +53,9 @@
  *
  * Numerical preconditions (documented, not checked on the device):
  * r > 0, l0 > 0, 0 < a <= 1, qn >= 0, a^2 + qn * l > 0.  Otherwise the
- * results are undefined (they propagate as NaN/Inf).
+ * results are undefined (they propagate as NaN/Inf).  With qn = 0 and a < 1
+ * the precision grows by 1/a^2 per token and leaves the fp32 range after
+ * about 64 / |log2 a| tokens; the results are then Inf/NaN as well.
  */
 #ifndef KLA_H
 #define KLA_H

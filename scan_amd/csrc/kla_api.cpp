@@ -251,8 +251,9 @@ klaStatus fwd_entry(const klaDims* d, const void* q, const void* k, const void* 
                 e = kla::launch_fwd_diag_pipe(fa, d->dtype, st);
                 break;
             }
-            // sequence split: segment products, precision carry, segment
-            // forwards, state carry, output correction
+            // sequence split: precision warm-up (exact segment products and
+            // precision carry where it did not settle), segment forwards,
+            // state carry, output correction
             const kla::SegWorkspace w = kla::seg_workspace(d->B, d->H, d->T, d->dk, d->dv, (int)es, nseg);
             char* ws = (char*)workspace;
             float* P = (float*)(ws + w.off_P);
@@ -263,8 +264,10 @@ klaStatus fwd_entry(const klaDims* d, const void* q, const void* k, const void* 
             fa.seg_lend = (float*)(ws + w.off_lend);
             fa.seg_m = (float*)(ws + w.off_m);
             fa.seg_qhat = ws + w.off_qhat;
-            e = kla::launch_seg_mobius(fa, P, d->dtype, st);
-            if (e == hipSuccess) e = kla::launch_seg_carry_l(fa, P, st);
+            int* ok = (int*)(ws + w.off_ok);
+            e = kla::launch_seg_warm(fa, ok, d->dtype, st);
+            if (e == hipSuccess) e = kla::launch_seg_mobius(fa, P, ok, d->dtype, st);
+            if (e == hipSuccess) e = kla::launch_seg_carry_l(fa, P, ok, st);
             if (e == hipSuccess) e = kla::launch_fwd_diag_pipe(fa, d->dtype, st);
             if (e == hipSuccess) e = kla::launch_seg_carry_m(fa, st);
             if (e == hipSuccess) e = kla::launch_seg_correct(fa, d->dtype, st);

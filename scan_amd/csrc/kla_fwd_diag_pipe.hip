@@ -598,12 +598,10 @@ __device__ void gate_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int 
     constexpr int NB = K::NBG, D = NB - 1;
     Buf b[NB];
     constexpr int NLD = 2 * TPG + 2 * K::VPT;  // loads per chunk
-    // The next chunk's rows are requested after the step's work (LATE): at
-    // the step start they queue with the chain waves' requests, which are on
-    // the critical path (measured 8% faster).  With the sequence split they
-    // are requested at the step start: the later request lost the L2 reuse of
-    // the rows the chain waves had just read (HBM reads 1.6x, measured slower).
-    constexpr bool LATE = !SEG;
+    // The next chunk's rows are requested after the step's work: at the step
+    // start they queue with the chain waves' requests, which are on the
+    // critical path (measured 8% faster on the LM-layer shape, 4% on the
+    // split long-context forward).
     // Each chunk is read through buffer resources spanning its rows, so rows
     // past T read as zero; a lane's token rows are immediates from its offset.
     constexpr int ES = (int)sizeof(TIn), QRB = DK * ES;
@@ -640,7 +638,6 @@ __device__ void gate_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int 
     auto step = [&](int c, Buf& cur, Buf& nxt) {
         const int cg = c + 1;  // chunk gated in this iteration
         wait_loads<(D - 1) * NLD>();
-        if (!LATE && nchunks > 0) load(cg + D, nxt);
         if (cg >= 0 && cg < nchunks) {
             const int L = chunk_len(sp.TL, cg, C), par = cg & 1;
             // V^T of the chunk
@@ -676,9 +673,22 @@ __device__ void gate_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int 
                                                    (L + 15) / 16 * 16 * DK * (int)sizeof(TIn))
                                        : make_rsrc(p.q, 0);
             // element offset of (token t of the chunk, key dims 2ip, 2ip+1) there
-            auto qho = [&](int t) {
-                return ((t / 16) * (DK / 32) + (2 * ip) / 32) * 512 + ((2 * ip) % 32 / 8 * 16 + t % 16) * 8 +
-                       (2 * ip) % 8;
+            auto qho = [&](int t, int i) {
+                return ((t / 16) * (DK / 32) + i / 32) * 512 + (i % 32 / 8 * 16 + t % 16) * 8 + i % 8;
+            };
+            // eight key dims of q-hat from a row of Q^ (LDS) and Wc, as one
+            // 16-byte store (two for fp32)
+            auto store_qhat8 = [&](const TIn* qr, f32x4 c0, f32x4 c1, int off) {
+                typedef typename Quad<TIn>::V QV;
+                const QV b0 = Quad<TIn>::make(Quad<TIn>::to_f32(*(const QV*)qr) * c0);
+                const QV b1 = Quad<TIn>::make(Quad<TIn>::to_f32(*(const QV*)(qr + 4)) * c1);
+                if constexpr (sizeof(TIn) == 2) {
+                    struct alignas(16) Two { QV x, y; };
+                    buf_store(__builtin_bit_cast(f32x4, Two{b0, b1}), rqh, off);
+                } else {
+                    buf_store(b0, rqh, off);
+                    buf_store(b1, rqh, off + 16);
+                }
             };
             // Factorised operands.  Full chunks take a copy with no per-token
             // tests, so the whole step is one basic block the compiler can
@@ -711,10 +721,6 @@ __device__ void gate_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int 
                     const float w1 = in ? w[u][1] * fast_rcp(g1) : 0.f;
                     *(typename PR::V*)&sm.op[par].fac.Q[qw_row<K>(t)][2 * ip] = PR::make(q0, q1);
                     *(typename PR::V*)&sm.op[par].fac.W[qw_row<K>(t)][2 * ip] = PR::make(w0, w1);
-                    if constexpr (SEG) {
-                        if (wq)
-                            buf_store(PR::make(q0 * wc0, q1 * wc1), rqh, qho(t) * (int)sizeof(TIn));
-                    }
                     wt0[u] = (TIn)w0;
                     wt1[u] = (TIn)w1;
                     if (!FULL && t == L - 1) { gl0 = g0; gl1 = g1; }
@@ -730,6 +736,27 @@ __device__ void gate_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int 
             if (!__builtin_amdgcn_readfirstlane(sm.bad[cg & 3])) {
                 if (L == C) fac(std::true_type{});
                 else fac(std::false_type{});
+                if constexpr (SEG) {
+                    if (wq) {
+                        // q-hat = Q^ (.) Wc, read back from this wave's own
+                        // block of Q^ (all tokens, its 2 IPW key dims) as 8
+                        // consecutive key dims of one token per lane, so
+                        // that each lane writes whole 16-byte pieces of the
+                        // tiled layout (rows past L hold zeros)
+                        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+                        __builtin_amdgcn_wave_barrier();
+                        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+#pragma unroll
+                        for (int x = 0; x < K::IPW / 8; ++x) {
+                            const int pid = x * 64 + lane, t = pid % C;
+                            const int i0 = gw * 2 * K::IPW + 8 * (pid / C);
+                            const f32x4 c0 = *(const f32x4*)&sm.Wc[par][i0];
+                            const f32x4 c1 = *(const f32x4*)&sm.Wc[par][i0 + 4];
+                            store_qhat8(&sm.op[par].fac.Q[qw_row<K>(t)][i0], c0, c1,
+                                        qho(t, i0) * (int)sizeof(TIn));
+                        }
+                    }
+                }
             } else {
                 if constexpr (SEG) {
                     if (wq) {
@@ -752,7 +779,7 @@ __device__ void gate_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int 
                             const int t = grp * TPG + u;
                             const float q0 = PR::lo(cur.q[u]) * G[u][0] * e0 * wc0;
                             const float q1 = PR::hi(cur.q[u]) * G[u][1] * e1 * wc1;
-                            buf_store(PR::make(q0, q1), rqh, qho(t) * (int)sizeof(TIn));
+                            buf_store(PR::make(q0, q1), rqh, qho(t, 2 * ip) * (int)sizeof(TIn));
                         }
                     }
                 }
@@ -774,7 +801,7 @@ __device__ void gate_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int 
                 }
             }
         }
-        if (LATE && nchunks > 0) load(cg + D, nxt);
+        if (nchunks > 0) load(cg + D, nxt);
         lds_barrier();
     };
 

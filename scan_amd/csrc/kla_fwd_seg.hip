@@ -10,11 +10,16 @@
 // segment can run from a zero state and be corrected afterwards.
 //
 // With nseg segments per (b,h) the forward runs:
+//   0. kla_seg_warm:     the precision entering each segment from the map
+//                        of the kWarm tokens before it, applied to both
+//                        extreme precisions (0 and +inf); a (b,h) where the
+//                        two agree at every key dim and segment start skips
+//                        passes 1 and 2;
 //   1. kla_seg_mobius:   the product of the precision matrices of every
 //                        block of kSegBlk tokens before the last segment, per
 //                        key dim;
 //   2. kla_seg_carry_l:  the precision entering each segment (a walk over
-//                        the block products);
+//                        the block products), exact from the caller's l0;
 //   3. the wave-specialised forward on every segment (local outputs, local
 //      final mean state, the segment's total gate, and q (.) gate product);
 //   4. kla_seg_carry_m:  the mean state entering each segment, and etaT;
@@ -36,20 +41,140 @@ __device__ __forceinline__ int seg_blocks(const FwdArgs& p) {
     return (p.nseg - 1) * (p.seg_len / kSegBlk);
 }
 
-// -------------------------------------------------- 1. block products
-// One workgroup per (b,h, block of kSegBlk tokens); NSUB threads per key dim
-// each compose a contiguous run of the block, then the runs are combined in
-// order.  Workgroups of 512 threads, so that several share a CU, and 16
-// tokens of loads in flight per thread keep enough reads outstanding.
-constexpr int kMobThreads = 512;
+// True when the warm-up settled the precision entering every segment of
+// (b,h) bh; the exact passes then leave it alone.
+// (The flags are read without an early exit, so that the loads overlap.)
+__device__ __forceinline__ bool seg_warm_ok(const FwdArgs& p, const int* ok, int bh) {
+    const int* f = ok + seg_row(p, bh, 0) * 2;
+    int all = 1;
+    for (int x = 2; x < 2 * p.nseg; ++x)
+        all &= (x % 2 == 0 || p.dk == 128) ? f[x] : 1;
+    return all != 0;
+}
+
+// Scale a positive 2x2 map by a power of two (exact; the map is unchanged)
+// so that its entries sum to [1, 2).
+__device__ __forceinline__ void mob_renorm(double& p00, double& p01, double& p10, double& p11) {
+    const int e = __builtin_amdgcn_frexp_exp((p00 + p01) + (p10 + p11));
+    p00 = __builtin_amdgcn_ldexp(p00, 1 - e);
+    p01 = __builtin_amdgcn_ldexp(p01, 1 - e);
+    p10 = __builtin_amdgcn_ldexp(p10, 1 - e);
+    p11 = __builtin_amdgcn_ldexp(p11, 1 - e);
+}
+
+// -------------------------------------------------- 0. precision warm-up
+// Every token's precision map x -> x / (qn x + a^2) + k^2 / r is increasing
+// and contracting, so the precision after a run of tokens hardly depends on
+// where the run started: the run's composed map P sends the extreme starts 0
+// and +inf to P(0) = p01/p11 and P(inf) = p00/p10, which enclose the true
+// precision, and once they agree to 2^-20 (relative) their midpoint is the
+// precision to within 2^-21.  The kWarm tokens before each segment start are
+// composed in fp64 (rounding far below that bound; each token's b and a^2
+// are rounded to fp32 as in the forward's chain), kWarmRun tokens per thread
+// and the runs in order; when the window reaches the sequence start
+// the map is applied to the caller's l0 instead (exact).  One workgroup per
+// (b,h, segment s >= 1, 64 key dims), one wave per run.  The (b,h, s, group)
+// flag is set only when every key dim of the group converged; a (b,h) with
+// any flag clear takes the exact passes 1 and 2 instead.
+constexpr int kWarm = 512;
+constexpr int kWarmRun = 32;
+constexpr int kWarmRuns = kWarm / kWarmRun;
 
 template <typename TIn, int DK>
-__global__ __launch_bounds__(kMobThreads) void kla_seg_mobius(FwdArgs p, float* P) {
+__global__ __launch_bounds__(64 * kWarmRuns) void kla_seg_warm(FwdArgs p, int* ok) {
+    __shared__ double sP[kWarmRuns][4][64];
+    constexpr int G = DK / 64;
+    int x = blockIdx.x;
+    const int g = x % G;
+    x /= G;
+    const int s = 1 + x % (p.nseg - 1), bh = x / (p.nseg - 1);
+    const int lane = threadIdx.x & 63, j = threadIdx.x >> 6;
+    const int i = g * 64 + lane;
+    const int h = bh % p.H;
+    const int bnd = s * p.seg_len;
+    const int n = bnd < kWarm ? bnd : kWarm;  // a multiple of kSegBlk
+    const int t0 = bnd - n;
+    const double qn = p.qn[(size_t)h * DK + i];
+    // P = M_last ... M_first with M_t = [[1 + b qn, b a^2], [qn, a^2]]
+    double p00 = 1.0, p01 = 0.0, p10 = 0.0, p11 = 1.0;
+    if (j * kWarmRun < n) {  // uniform over the wave
+        const size_t row = (size_t)bh * p.T + t0 + j * kWarmRun;
+        const auto ra = make_rsrc(p.a + row * DK, kWarmRun * DK * 4);
+        const auto rk = make_rsrc((const TIn*)p.k + row * DK, kWarmRun * DK * (int)sizeof(TIn));
+        // the token's row offset goes in the scalar offset, the lane's column
+        // in the vector offset
+        float av[kWarmRun], kv[kWarmRun];
+#pragma unroll
+        for (int u = 0; u < kWarmRun; ++u) {
+            av[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ra, i * 4, u * DK * 4, 0));
+            if constexpr (sizeof(TIn) == 2)
+                kv[u] = __builtin_bit_cast(
+                    float, (unsigned)(unsigned short)__builtin_amdgcn_raw_buffer_load_b16(rk, i * 2, u * DK * 2, 0)
+                               << 16);
+            else
+                kv[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rk, i * 4, u * DK * 4, 0));
+        }
+        // 1/r once per token (lane u holds token u of the run).  b and a^2 are
+        // rounded to fp32 like the forward's own chain; the composition that
+        // follows is fp64.
+        const float rho_l = 1.f / p.r[row + (lane % kWarmRun)];
+#pragma unroll
+        for (int u = 0; u < kWarmRun; ++u) {
+            const float rt = __builtin_bit_cast(
+                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rho_l), u));
+            const double a2 = (double)(av[u] * av[u]);
+            const double b = (double)(kv[u] * kv[u] * rt);
+            const double m00 = __builtin_fma(b, qn, 1.0), m01 = b * a2;
+            const double n00 = m00 * p00 + m01 * p10, n01 = m00 * p01 + m01 * p11;
+            const double n10 = qn * p00 + a2 * p10, n11 = qn * p01 + a2 * p11;
+            p00 = n00; p01 = n01; p10 = n10; p11 = n11;
+            if (u % 8 == 7) mob_renorm(p00, p01, p10, p11);
+        }
+    }
+    sP[j][0][lane] = p00;
+    sP[j][1][lane] = p01;
+    sP[j][2][lane] = p10;
+    sP[j][3][lane] = p11;
+    __syncthreads();
+    if (j != 0) return;
+    for (int u = 1; u < kWarmRuns; ++u) {  // later runs on the left
+        const double m00 = sP[u][0][lane], m01 = sP[u][1][lane];
+        const double m10 = sP[u][2][lane], m11 = sP[u][3][lane];
+        const double n00 = m00 * p00 + m01 * p10, n01 = m00 * p01 + m01 * p11;
+        const double n10 = m10 * p00 + m11 * p10, n11 = m10 * p01 + m11 * p11;
+        p00 = n00; p01 = n01; p10 = n10; p11 = n11;
+        mob_renorm(p00, p01, p10, p11);
+    }
+    const float l_in = p.l0 ? p.l0[(size_t)bh * DK + i] : 1.f;
+    float* l0out = const_cast<float*>(p.seg_l0);
+    if (s == 1) l0out[seg_row(p, bh, 0) * DK + i] = l_in;
+    double l;
+    bool good;
+    if (t0 == 0) {
+        l = (p00 * l_in + p01) / (p10 * l_in + p11);
+        good = true;
+    } else {
+        const double lo = p01 / p11, hi = p00 / p10;
+        l = 0.5 * (lo + hi);
+        good = __builtin_fabs(hi - lo) <= 0x1p-20 * lo;  // false for NaN (qn = 0)
+    }
+    l0out[seg_row(p, bh, s) * DK + i] = (float)l;
+    const unsigned long long bad = __builtin_amdgcn_ballot_w64(!good);
+    if (lane == 0) ok[seg_row(p, bh, s) * 2 + g] = bad == 0;
+}
+
+// -------------------------------------------------- 1. block products
+// One workgroup per (b,h, block of kSegBlk tokens) at a time; NSUB threads per
+// key dim each compose a contiguous run of the block, then the runs are
+// combined in order.  Workgroups of 512 threads, so that several share a CU,
+// and 16 tokens of loads in flight per thread keep enough reads outstanding.
+constexpr int kMobThreads = 512;
+constexpr int kMobGrid = 1024;
+
+template <typename TIn, int DK>
+__device__ __forceinline__ void mobius_block(const FwdArgs& p, float* P, f32x4 (*sP)[DK], int i, int sub,
+                                             int nb, int bh, int s) {
     constexpr int NSUB = kMobThreads / DK;
-    __shared__ f32x4 sP[NSUB][DK];
-    const int i = threadIdx.x % DK, sub = threadIdx.x / DK;
-    const int nb = seg_blocks(p);
-    const int bh = blockIdx.x / nb, s = blockIdx.x % nb;
     const int h = bh % p.H;
     const int T0 = s * kSegBlk;
     constexpr int sl = kSegBlk / NSUB;
@@ -134,12 +259,29 @@ __global__ __launch_bounds__(kMobThreads) void kla_seg_mobius(FwdArgs p, float* 
     }
 }
 
+template <typename TIn, int DK>
+__global__ __launch_bounds__(kMobThreads) void kla_seg_mobius(FwdArgs p, float* P, const int* ok) {
+    constexpr int NSUB = kMobThreads / DK;
+    __shared__ f32x4 sP[NSUB][DK];
+    const int i = threadIdx.x % DK, sub = threadIdx.x / DK;
+    const int nb = seg_blocks(p);
+    // at most kMobGrid workgroups stride over the blocks, so that the launch
+    // ends at once when the warm-up settled every (b,h)
+    for (int blk = blockIdx.x; blk < p.B * p.H * nb; blk += gridDim.x) {
+        const int bh = blk / nb, s = blk % nb;
+        if (seg_warm_ok(p, ok, bh)) continue;  // uniform over the workgroup
+        mobius_block<TIn, DK>(p, P, sP, i, sub, nb, bh, s);
+        __syncthreads();  // sP is reused by the next block
+    }
+}
+
 // -------------------------------------------------- 2. precision carry
-__global__ void kla_seg_carry_l(FwdArgs p, const float* P) {
+__global__ void kla_seg_carry_l(FwdArgs p, const float* P, const int* ok) {
     const int n = p.B * p.H * p.dk;
     const int x = blockIdx.x * blockDim.x + threadIdx.x;
     if (x >= n) return;
     const int bh = x / p.dk, i = x % p.dk;
+    if (seg_warm_ok(p, ok, bh)) return;
     float l = p.l0 ? p.l0[x] : 1.f;
     float* out = const_cast<float*>(p.seg_l0);
     const int nb = seg_blocks(p), per = p.seg_len / kSegBlk;
@@ -311,11 +453,26 @@ __global__ __launch_bounds__(256) void kla_seg_correct(FwdArgs p) {
 }
 
 template <typename TIn>
-hipError_t launch_mobius_t(const FwdArgs& a, float* P, hipStream_t s) {
-    const int nblk = a.B * a.H * (a.nseg - 1) * (a.seg_len / kSegBlk);
-    if (a.dk == 128) hipLaunchKernelGGL((kla_seg_mobius<TIn, 128>), dim3(nblk), dim3(kMobThreads), 0, s, a, P);
-    else if (a.dk == 64) hipLaunchKernelGGL((kla_seg_mobius<TIn, 64>), dim3(nblk), dim3(kMobThreads), 0, s, a, P);
+hipError_t launch_warm_t(const FwdArgs& a, int* ok, hipStream_t s) {
+    const int nblk = a.B * a.H * (a.nseg - 1) * (a.dk / 64);
+    if (a.dk == 128)
+        hipLaunchKernelGGL((kla_seg_warm<TIn, 128>), dim3(nblk), dim3(64 * kWarmRuns), 0, s, a, ok);
+    else if (a.dk == 64)
+        hipLaunchKernelGGL((kla_seg_warm<TIn, 64>), dim3(nblk), dim3(64 * kWarmRuns), 0, s, a, ok);
     else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+template <typename TIn>
+hipError_t launch_mobius_t(const FwdArgs& a, float* P, const int* ok, hipStream_t s) {
+    int nblk = a.B * a.H * (a.nseg - 1) * (a.seg_len / kSegBlk);
+    if (nblk > kMobGrid) nblk = kMobGrid;
+    if (a.dk == 128)
+        hipLaunchKernelGGL((kla_seg_mobius<TIn, 128>), dim3(nblk), dim3(kMobThreads), 0, s, a, P, ok);
+    else if (a.dk == 64)
+        hipLaunchKernelGGL((kla_seg_mobius<TIn, 64>), dim3(nblk), dim3(kMobThreads), 0, s, a, P, ok);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
@@ -347,6 +504,7 @@ SegWorkspace seg_workspace(int B, int H, int T, int dk, int dv, int es, int nseg
     w.off_lend = o; o += align256(bh * dk * sizeof(float));
     w.off_m = o;    o += align256(bh * nseg * dk * dv * sizeof(float));
     w.off_qhat = o; o += align256(bh * (size_t)((T + 15) / 16 * 16) * dk * es);
+    w.off_ok = o;   o += align256(bh * nseg * 2 * sizeof(int));
     w.bytes = o;
     return w;
 }
@@ -369,13 +527,17 @@ int fwd_diag_seg_len(int T, int nseg) {
     return (l + kSegBlk - 1) / kSegBlk * kSegBlk;
 }
 
-hipError_t launch_seg_mobius(const FwdArgs& a, float* P, int dtype, hipStream_t s) {
-    return dtype == DT_BF16 ? launch_mobius_t<bf16>(a, P, s) : launch_mobius_t<float>(a, P, s);
+hipError_t launch_seg_warm(const FwdArgs& a, int* ok, int dtype, hipStream_t s) {
+    return dtype == DT_BF16 ? launch_warm_t<bf16>(a, ok, s) : launch_warm_t<float>(a, ok, s);
 }
 
-hipError_t launch_seg_carry_l(const FwdArgs& a, const float* P, hipStream_t s) {
+hipError_t launch_seg_mobius(const FwdArgs& a, float* P, const int* ok, int dtype, hipStream_t s) {
+    return dtype == DT_BF16 ? launch_mobius_t<bf16>(a, P, ok, s) : launch_mobius_t<float>(a, P, ok, s);
+}
+
+hipError_t launch_seg_carry_l(const FwdArgs& a, const float* P, const int* ok, hipStream_t s) {
     const int n = a.B * a.H * a.dk;
-    hipLaunchKernelGGL(kla_seg_carry_l, dim3((n + 255) / 256), dim3(256), 0, s, a, P);
+    hipLaunchKernelGGL(kla_seg_carry_l, dim3((n + 255) / 256), dim3(256), 0, s, a, P, ok);
     return hipGetLastError();
 }
 

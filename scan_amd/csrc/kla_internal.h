@@ -57,7 +57,7 @@ constexpr int kSegBlk = 256;
 
 // Workspace of the sequence split: every array above, 256-byte aligned.
 struct SegWorkspace {
-    size_t off_P, off_l0, off_d, off_lend, off_m, off_qhat, bytes;
+    size_t off_P, off_l0, off_d, off_lend, off_m, off_qhat, off_ok, bytes;
 };
 SegWorkspace seg_workspace(int B, int H, int T, int dk, int dv, int es, int nseg);
 // Segments per (b,h) for a diagonal forward on the wave-specialised kernel
@@ -65,8 +65,11 @@ SegWorkspace seg_workspace(int B, int H, int T, int dk, int dv, int es, int nseg
 int fwd_diag_nseg(int B, int H, int T, int dk, int dv, int nvt);
 int fwd_diag_seg_len(int T, int nseg);
 // The passes around the split forward (kla_fwd_seg.hip).
-hipError_t launch_seg_mobius(const FwdArgs& a, float* P, int dtype, hipStream_t s);
-hipError_t launch_seg_carry_l(const FwdArgs& a, const float* P, hipStream_t s);
+// ok: [BH, nseg, 2] flags (per 64 key dims), written by the warm-up and
+// read by the exact passes.
+hipError_t launch_seg_warm(const FwdArgs& a, int* ok, int dtype, hipStream_t s);
+hipError_t launch_seg_mobius(const FwdArgs& a, float* P, const int* ok, int dtype, hipStream_t s);
+hipError_t launch_seg_carry_l(const FwdArgs& a, const float* P, const int* ok, hipStream_t s);
 hipError_t launch_seg_carry_m(const FwdArgs& a, hipStream_t s);
 hipError_t launch_seg_correct(const FwdArgs& a, int dtype, hipStream_t s);
 

@@ -313,6 +313,54 @@ def test_parity_sequence_split(monkeypatch, name, over, nseg, state):
     assert_parity(compare(hip, ref), w.dtype, f"split {name} {over}")
 
 
+def _warm_gap(a, k, r, qn, t0, t1):
+    """Relative gap after walking tokens [t0, t1) of one head from the
+    precisions 0 and +inf (fp64, on the CPU): the quantity the split's
+    precision warm-up tests before it trusts its walk."""
+    lo = np.zeros(a.shape[-1])
+    hi = None
+    for t in range(t0, t1):
+        b = k[t] ** 2 / r[t]
+        hi = 1.0 / qn + b if hi is None else hi / (a[t] ** 2 + qn * hi) + b
+        lo = lo / (a[t] ** 2 + qn * lo) + b
+    with np.errstate(invalid="ignore", divide="ignore"):
+        return (hi - lo) / lo
+
+
+@pytest.mark.parametrize("case", ["slow_decay", "zero_noise"])
+def test_split_warmup_fallback(monkeypatch, case):
+    """Sequence split where the precision warm-up cannot settle one head (a
+    near 1 with a tiny process noise, or a = 1 and qn = 0 on some key dims,
+    where the precision grows without bound): that head takes the exact
+    block-product carry, the other head the warm-up, and both match the
+    oracle."""
+    _print_case("split warm-up fallback", case)
+    monkeypatch.setenv("KLA_FWD_NSEG", "3")
+    inp = gen.make_inputs("long_diag", seed=21, B=1, H=2, T=3000)
+    a, qn = inp["a"].clone(), inp["qn"].clone()
+    if case == "slow_decay":
+        a[:, 0] = 0.9999
+        qn[0] = 1e-6
+    else:
+        a[:, 0, :, ::5] = 1.0
+        qn[0, ::5] = 0.0
+    inp["a"], inp["qn"] = a, qn
+    w = inp["workload"]
+    # the premise: head 0 has not settled 512 tokens before the first
+    # segment start (1024), head 1 has
+    k = inp["k"][0].float().double().numpy()
+    r = inp["r"][0].double().numpy()
+    an, qnn = a[0].double().numpy(), qn.double().numpy()
+    gap0 = _warm_gap(an[0], k[0], r[0], qnn[0], 512, 1024)
+    gap1 = _warm_gap(an[1], k[1], r[1], qnn[1], 512, 1024)
+    assert not np.all(gap0 <= 2.0 ** -20)
+    assert np.all(gap1 <= 2.0 ** -22)
+    st = gen.make_state(w, seed=22)
+    hip = run_hip(inp, "diag", st["l0"], st["eta0"])
+    ref = run_oracle(inp, "diag", st["l0"], st["eta0"])
+    assert_parity(compare(hip, ref), w.dtype, f"split warm-up fallback {case}")
+
+
 @pytest.mark.parametrize("cov", ["diag", "iso"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_short_adversarial_gates(cov, dtype):
