@@ -126,6 +126,65 @@ def make_inputs(w: Workload | str, seed: int = 0, device: str | torch.device = "
     return out
 
 
+# the fused block prologue at the LM-layer shape: pre-activations drawn so
+# that the prologue's a, qn and r have the lm_diag distributions
+BLOCK = Workload("block_lm_diag", 8, 16, 2048, 128, 128, "diag", "bf16")
+BLOCK_WIDTH = 4
+
+
+def make_block_inputs(w: Workload | str, seed: int = 0, device="cpu", width: int = BLOCK_WIDTH,
+                      bias: bool = True, state: bool = False, **override) -> dict:
+    """Inputs of the fused block prologue (diagonal covariance).
+
+    xq, xk, xv ~ N(0,1) (storage dtype): the projections before the causal
+    convolution; za ~ N(a_mu, 1) (storage dtype), so that sigmoid(za) has the
+    workload's distribution of a; zqn ~ N(-2, 0.5) [H,dk] and
+    zr ~ N(0, r_var) [B,H,T] (fp32), so that softplus(zqn) and
+    softplus(zr) + 1e-3 have the workload's qn and r; convolution taps
+    wq, wk, wv [H,d,width] ~ U(-1/sqrt(width), 1/sqrt(width)) and, with bias,
+    biases [H,d] from the same law (fp32); with state, convolution states
+    [B,H,width-1,d] ~ N(0,1) (storage dtype), else None.  r_eps = 1e-3.
+    """
+    if isinstance(w, str):
+        w = BLOCK if w == BLOCK.name else WORKLOADS[w]
+    if override:
+        w = w.with_(**override)
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    B, H, T, dk, dv = w.B, w.H, w.T, w.dk, w.dv
+    f64 = torch.float64
+
+    def randn(*shape):
+        return torch.randn(*shape, generator=g, dtype=f64)
+
+    def unif(*shape):
+        return (2.0 * torch.rand(*shape, generator=g, dtype=f64) - 1.0) / math.sqrt(width)
+
+    st = _TORCH_DTYPE[w.dtype]
+    out = {
+        "xq": randn(B, H, T, dk).to(st), "xk": randn(B, H, T, dk).to(st),
+        "xv": randn(B, H, T, dv).to(st),
+        "za": (w.a_mu + randn(B, H, T, dk)).to(st),
+        "zqn": (-2.0 + math.sqrt(0.5) * randn(H, dk)).to(torch.float32),
+        "zr": (math.sqrt(w.r_var) * randn(B, H, T)).to(torch.float32),
+        "wq": unif(H, dk, width).to(torch.float32), "wk": unif(H, dk, width).to(torch.float32),
+        "wv": unif(H, dv, width).to(torch.float32),
+        "bq": None, "bk": None, "bv": None, "sq": None, "sk": None, "sv": None,
+        "r_eps": 1e-3, "width": width, "workload": w,
+    }
+    if bias:
+        out["bq"] = unif(H, dk).to(torch.float32)
+        out["bk"] = unif(H, dk).to(torch.float32)
+        out["bv"] = unif(H, dv).to(torch.float32)
+    if state:
+        out["sq"] = randn(B, H, width - 1, dk).to(st)
+        out["sk"] = randn(B, H, width - 1, dk).to(st)
+        out["sv"] = randn(B, H, width - 1, dv).to(st)
+    for key, val in out.items():
+        if isinstance(val, torch.Tensor):
+            out[key] = val.to(device)
+    return out
+
+
 def make_state(w: Workload, seed: int, device="cpu") -> dict:
     """A non-trivial starting state for handoff tests: l0 = softplus(N(0,1)) + 0.2
     (positive), eta0 ~ N(0,1) (any real information vector is valid)."""
