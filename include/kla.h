@@ -143,6 +143,55 @@ klaStatus klaFwdNoAlloc(const klaDims* d,
                         void* o, float* lT, float* etaT, void* hipStream);
 
 /*
+ * Fused block prologue.  "Kalman Linear Attention: Parallel Bayesian
+ * Filtering For Efficient Language Modelling and State Tracking" (gist.science
+ * explainer, technical summary > method §4, architecture): the layer is a
+ * Mamba-like fused block with a one-dimensional causal convolution and SiLU.
+ * klaFwdBlock runs the diagonal forward with that prologue inside its loads:
+ *   q = silu(conv_q(xq)), k = silu(conv_k(xk)), v = silu(conv_v(xv)),
+ *   a = sigmoid(za), qn = softplus(zqn), r = softplus(zr) + r_eps,
+ * where conv_x is a depthwise causal convolution of `width` taps along the
+ * sequence: conv(x)_t[c] = bias[c] + sum_{j<W} w[c][W-1-j] x_{t-j}[c] (tap
+ * W-1 on the current token).  Rows before token 0 come from the convolution
+ * state (the W-1 preceding rows, oldest first) or are zero.  A chunked
+ * prefill continues a sequence by passing the previous chunk's last W-1 rows
+ * of xq, xk, xv as the state and its lT, etaT as l0, eta0.
+ */
+typedef struct klaBlock {
+    int width;                         /* W, 1..4                              */
+    const float* wq;                   /* taps [H, dk, W] fp32                 */
+    const float* wk;                   /* taps [H, dk, W] fp32                 */
+    const float* wv;                   /* taps [H, dv, W] fp32                 */
+    const float* bq;                   /* biases [H, dk] fp32, or NULL (zero)  */
+    const float* bk;                   /* biases [H, dk] fp32, or NULL (zero)  */
+    const float* bv;                   /* biases [H, dv] fp32, or NULL (zero)  */
+    const void* sq;                    /* states [B, H, W-1, dk] (dtype), or NULL (zero) */
+    const void* sk;                    /* states [B, H, W-1, dk] (dtype), or NULL (zero) */
+    const void* sv;                    /* states [B, H, W-1, dv] (dtype), or NULL (zero) */
+    float r_eps;                       /* r = softplus(zr) + r_eps, r_eps >= 0 */
+} klaBlock;
+
+/*
+ * In:  xq, xk [B,H,T,dk], xv [B,H,T,dv] and za [B,H,T,dk] in d->dtype;
+ *      zqn [H,dk] and zr [B,H,T] fp32; l0, eta0 as for klaFwd (NULL: l0 = 1,
+ *      eta0 = 0); blk as above (NULL: KLA_ERR_NULL).
+ * Out: o [B,H,T,dv] (dtype), lT, etaT (may be NULL) as for klaFwd.
+ * Diagonal covariance only, dk = dv in {64, 128} (128: bf16), the dims of
+ * the wave-specialised kernel (KLA_ERR_UNSUPPORTED otherwise); width outside
+ * 1..4 or r_eps < 0 is KLA_ERR_SHAPE.  Long sequences are not split across
+ * workgroups: one workgroup per (b,h) and 64 value columns.  No workspace; no
+ * memory is allocated.  Every non-NULL pointer must be 16-byte aligned except
+ * the taps and biases (4-byte).  o must not overlap an input; lT and
+ * etaT must not overlap l0, eta0 (KLA_ERR_ALIAS).  T == 0 passes l0/eta0
+ * through.
+ */
+klaStatus klaFwdBlock(const klaDims* d, const klaBlock* blk,
+                      const void* xq, const void* xk, const void* xv,
+                      const void* za, const float* zqn, const float* zr,
+                      const float* l0, const float* eta0,
+                      void* o, float* lT, float* etaT, void* hipStream);
+
+/*
  * One decode step for every (b,h) (the same recurrence with T = 1;
  * constant-memory decoding, [KDN]).  State is updated in place.
  * Layouts: q, k [B,H,dk]; v, o [B,H,dv]; r [B,H];

@@ -13,15 +13,17 @@ Convenience (torch tensors in, torch tensors out):
     step(q, k, v, a, qn, r, l, eta, cov="diag") -> o      (l, eta updated in place)
     fwd_residual(q, k, v, a, qn, r, l0=None, m0=None, cov="diag") -> (o, lT, mT)
     bwd(q, k, v, a, qn, r, l0, eta0, do, dlT=None, detaT=None, cov="diag") -> dict of gradients
+    fwd_block(xq, xk, xv, za, zqn, zr, wq, wk, wv, ...) -> (o, lT, etaT)  (fused block prologue)
 """
 from __future__ import annotations
 
 import ctypes
 import os
 
-__all__ = ["klaFwd", "klaFwdNoAlloc", "klaStep", "klaFwdResidual", "klaBwd", "klaFwdWorkspaceBytes",
-           "klaBwdWorkspaceBytes", "klaIsSupported", "klaStatusString", "KlaDims", "KlaError", "fwd",
-           "step", "fwd_residual", "bwd", "lib_path", "load"]
+__all__ = ["klaFwd", "klaFwdNoAlloc", "klaFwdBlock", "klaStep", "klaFwdResidual", "klaBwd",
+           "klaFwdWorkspaceBytes", "klaBwdWorkspaceBytes", "klaIsSupported", "klaStatusString",
+           "KlaDims", "KlaBlock", "KlaError", "fwd", "fwd_block", "step", "fwd_residual", "bwd",
+           "lib_path", "load"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libkla.so")
@@ -38,6 +40,15 @@ class KlaDims(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int), ("H", ctypes.c_int), ("T", ctypes.c_int),
                 ("dk", ctypes.c_int), ("dv", ctypes.c_int),
                 ("dtype", ctypes.c_int), ("cov", ctypes.c_int)]
+
+
+class KlaBlock(ctypes.Structure):
+    """klaBlock of include/kla.h: convolution width, taps, biases, states, r_eps."""
+    _fields_ = [("width", ctypes.c_int),
+                ("wq", ctypes.c_void_p), ("wk", ctypes.c_void_p), ("wv", ctypes.c_void_p),
+                ("bq", ctypes.c_void_p), ("bk", ctypes.c_void_p), ("bv", ctypes.c_void_p),
+                ("sq", ctypes.c_void_p), ("sk", ctypes.c_void_p), ("sv", ctypes.c_void_p),
+                ("r_eps", ctypes.c_float)]
 
 
 class KlaError(RuntimeError):
@@ -87,6 +98,8 @@ def load():
     lib.klaBwdWorkspaceBytes.restype = sz
     lib.klaBwd.argtypes = [dp] + [vp] * 19 + [vp, sz, vp]
     lib.klaBwd.restype = ctypes.c_int
+    lib.klaFwdBlock.argtypes = [dp, ctypes.POINTER(KlaBlock)] + [vp] * 11 + [vp]
+    lib.klaFwdBlock.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -112,6 +125,13 @@ def klaFwdNoAlloc(dims, q, k, v, a, qnoise, r, l0, eta0, o, lT, etaT, stream) ->
     """Raw call of the forward that takes no workspace (pointers as ints or None)."""
     return int(load().klaFwdNoAlloc(ctypes.byref(dims), q, k, v, a, qnoise, r, l0, eta0, o, lT, etaT,
                                     stream))
+
+
+def klaFwdBlock(dims, blk, xq, xk, xv, za, zqn, zr, l0, eta0, o, lT, etaT, stream) -> int:
+    """Raw call of the forward with the fused block prologue (blk: KlaBlock or
+    None; pointers as ints or None)."""
+    return int(load().klaFwdBlock(ctypes.byref(dims), ctypes.byref(blk) if blk is not None else None,
+                                  xq, xk, xv, za, zqn, zr, l0, eta0, o, lT, etaT, stream))
 
 
 def klaStep(dims, q, k, v, a, qnoise, r, l, eta, o, stream) -> int:
@@ -207,6 +227,36 @@ def fwd(q, k, v, a, qn, r, l0=None, eta0=None, cov: str = "diag", o=None, lT=Non
                 _ptr(o), _ptr(lT), _ptr(etaT), _ptr(ws), ws_bytes, _stream())
     if st != KLA_OK:
         raise KlaError(st, "klaFwd")
+    return o, lT, etaT
+
+
+def fwd_block(xq, xk, xv, za, zqn, zr, wq, wk, wv, bq=None, bk=None, bv=None, sq=None, sk=None,
+              sv=None, r_eps: float = 1e-3, l0=None, eta0=None, o=None, lT=None, etaT=None,
+              want_state: bool = True):
+    """KLA forward with the fused block prologue (diagonal covariance) on the
+    current stream.  xq, xk, xv, za in the storage dtype, zqn [H,dk] and zr
+    [B,H,T] fp32, taps [H,d,W] and biases [H,d] fp32, states [B,H,W-1,d] in the
+    storage dtype.  Returns (o, lT, etaT); outputs are allocated unless passed
+    in."""
+    import torch
+    _check_device(xq, xk, xv, za, zqn, zr, wq, wk, wv, bq, bk, bv, sq, sk, sv, l0, eta0)
+    B, H, T, dk = xq.shape
+    dv = xv.shape[-1]
+    dims = KlaDims(B, H, T, dk, dv, _dtype_code(xq), KLA_DIAG)
+    blk = KlaBlock(int(wq.shape[-1]), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(bq), _ptr(bk), _ptr(bv),
+                   _ptr(sq), _ptr(sk), _ptr(sv), float(r_eps))
+    dev = xq.device
+    if o is None:
+        o = torch.empty(B, H, T, dv, dtype=xv.dtype, device=dev)
+    if want_state:
+        if lT is None:
+            lT = torch.empty(B, H, dk, dtype=torch.float32, device=dev)
+        if etaT is None:
+            etaT = torch.empty(B, H, dk, dv, dtype=torch.float32, device=dev)
+    st = klaFwdBlock(dims, blk, _ptr(xq), _ptr(xk), _ptr(xv), _ptr(za), _ptr(zqn), _ptr(zr),
+                     _ptr(l0), _ptr(eta0), _ptr(o), _ptr(lT), _ptr(etaT), _stream())
+    if st != KLA_OK:
+        raise KlaError(st, "klaFwdBlock")
     return o, lT, etaT
 
 

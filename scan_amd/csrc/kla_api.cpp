@@ -296,6 +296,62 @@ klaStatus klaFwdNoAlloc(const klaDims* d, const void* q, const void* k, const vo
     return fwd_entry(d, q, k, v, a, qnoise, r, l0, eta0, o, lT, etaT, nullptr, 0, hipStream, true);
 }
 
+klaStatus klaFwdBlock(const klaDims* d, const klaBlock* blk, const void* xq, const void* xk, const void* xv,
+                      const void* za, const float* zqn, const float* zr, const float* l0, const float* eta0,
+                      void* o, float* lT, float* etaT, void* hipStream) {
+    if (!d || !blk) return KLA_ERR_NULL;
+    if (!dims_ok(d)) return KLA_ERR_SHAPE;
+    if (!kinds_ok(d) || d->cov != KLA_DIAG) return KLA_ERR_UNSUPPORTED;
+    const int nvt = kla::fwd_diag_pipe_vtiles(d->dk, d->dv, d->dtype);
+    if (nvt <= 0) return KLA_ERR_UNSUPPORTED;
+    const int W = blk->width;
+    if (W < 1 || W > 4 || !(blk->r_eps >= 0.f)) return KLA_ERR_SHAPE;
+    const long long B = d->B, H = d->H, T = d->T, dk = d->dk, dv = d->dv;
+    const long long BH = B * H;
+    if (BH > (1LL << 30) || T > (1LL << 30)) return KLA_ERR_SHAPE;
+    if (BH == 0) return KLA_OK;
+    const size_t es = d->dtype == KLA_BF16 ? 2 : 4;
+    if (T > 0 && (!xq || !xk || !xv || !za || !zqn || !zr || !o || !blk->wq || !blk->wk || !blk->wv))
+        return KLA_ERR_NULL;
+    const void* big[] = {xq, xk, xv, za, o, eta0, etaT, zqn, zr, l0, lT, blk->sq, blk->sk, blk->sv};
+    for (const void* p : big)
+        if (p && !aligned16(p)) return KLA_ERR_ALIGN;
+    const void* small[] = {blk->wq, blk->wk, blk->wv, blk->bq, blk->bk, blk->bv};
+    for (const void* p : small)
+        if (((uintptr_t)p & 3u) != 0) return KLA_ERR_ALIGN;
+
+    const size_t ntk = (size_t)(BH * T), nlt = (size_t)(BH * dk), neta = (size_t)(BH * dk * dv);
+    const Span s_o = span(o, ntk * dv * es);
+    const Span s_lT = span(lT, nlt * 4), s_etaT = span(etaT, neta * 4);
+    const size_t ws = (size_t)(W - 1);
+    const Span ins[] = {span(xq, ntk * dk * es), span(xk, ntk * dk * es), span(xv, ntk * dv * es),
+                        span(za, ntk * dk * es), span(zqn, (size_t)(H * dk) * 4), span(zr, ntk * 4),
+                        span(l0, nlt * 4), span(eta0, neta * 4),
+                        span(blk->wq, (size_t)(H * dk) * W * 4), span(blk->wk, (size_t)(H * dk) * W * 4),
+                        span(blk->wv, (size_t)(H * dv) * W * 4), span(blk->bq, (size_t)(H * dk) * 4),
+                        span(blk->bk, (size_t)(H * dk) * 4), span(blk->bv, (size_t)(H * dv) * 4),
+                        span(blk->sq, (size_t)BH * ws * dk * es), span(blk->sk, (size_t)BH * ws * dk * es),
+                        span(blk->sv, (size_t)BH * ws * dv * es)};
+    for (const Span& s : ins)
+        if (overlap(s_o, s) || overlap(s_lT, s) || overlap(s_etaT, s)) return KLA_ERR_ALIAS;
+    if (overlap(s_o, s_lT) || overlap(s_o, s_etaT) || overlap(s_lT, s_etaT)) return KLA_ERR_ALIAS;
+
+    kla::FwdArgs fa;
+    fa.q = xq; fa.k = xk; fa.v = xv; fa.a = (const float*)za; fa.qn = zqn; fa.r = zr;
+    fa.l0 = l0; fa.eta0 = eta0; fa.o = o; fa.lT = lT; fa.etaT = etaT;
+    fa.B = (int)B; fa.H = (int)H; fa.T = (int)T; fa.dk = (int)dk; fa.dv = (int)dv;
+    fa.n_vtiles = nvt;
+    fa.conv_w = W;
+    fa.conv_wt[0] = blk->wq; fa.conv_wt[1] = blk->wk; fa.conv_wt[2] = blk->wv;
+    fa.conv_b[0] = blk->bq; fa.conv_b[1] = blk->bk; fa.conv_b[2] = blk->bv;
+    fa.conv_s[0] = blk->sq; fa.conv_s[1] = blk->sk; fa.conv_s[2] = blk->sv;
+    fa.r_eps = blk->r_eps;
+    hipStream_t st = (hipStream_t)hipStream;
+    const hipError_t e = T == 0 ? kla::launch_fwd_empty(fa, 0, st) : kla::launch_fwd_diag_pipe(fa, d->dtype, st);
+    if (e == hipErrorInvalidValue) return KLA_ERR_UNSUPPORTED;
+    return e == hipSuccess ? KLA_OK : KLA_ERR_HIP;
+}
+
 klaStatus klaStep(const klaDims* d, const void* q, const void* k, const void* v, const float* a,
                   const float* qnoise, const float* r, float* l, float* eta, void* o,
                   void* hipStream) {

@@ -307,4 +307,31 @@ __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcp
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// Activations of the fused block prologue, in fp32 from the hardware exp2,
+// log2 and reciprocal (a few ulp).
+constexpr float kLog2e = 1.4426950408889634f, kLn2 = 0.6931471805599453f;
+__device__ __forceinline__ float act_sigmoid(float x) { return fast_rcp(1.f + fast_exp2(-x * kLog2e)); }
+__device__ __forceinline__ float act_silu(float x) { return x * act_sigmoid(x); }
+// softplus(x) = max(x, 0) + log1p(e), e = exp(-|x|).  log1p(e) = log(u) e /
+// (u - 1) with u = 1 + e rounded, which keeps the relative accuracy of the
+// logarithm for small e (Goldberg's log1p identity); e itself once u rounds
+// to 1.
+__device__ __forceinline__ float act_softplus(float x) {
+    const float e = fast_exp2(-__builtin_fabsf(x) * kLog2e);
+    const float u = 1.f + e;
+    const float l1p = u == 1.f ? e : fast_log2(u) * kLn2 * e / (u - 1.f);
+    return __builtin_fmaxf(x, 0.f) + l1p;
+}
+// One channel of a causal depthwise convolution of up to four taps: w[3] on
+// the current token's x0, w[2] on x1 (one token back) ... w[0] on x3.
+template <typename W4>
+__device__ __forceinline__ float conv4(const W4& w, float b, float x0, float x1, float x2, float x3) {
+    return __builtin_fmaf(w[3], x0, __builtin_fmaf(w[2], x1, __builtin_fmaf(w[1], x2, __builtin_fmaf(w[0], x3, b))));
+}
+// The taps of one channel, right-aligned into four (zero for absent taps).
+__device__ __forceinline__ void load_taps4(float (&w)[4], const float* src, int width) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = j >= 4 - width ? src[j - (4 - width)] : 0.f;
+}
+
 }  // namespace kla

@@ -109,6 +109,15 @@ struct S3 {
     int bad[4];                   // chunk needs the exact token-by-token path
 };
 
+// Block prologue: convolution taps (right-aligned into four) and biases of
+// q (all key dims) and v (the workgroup's value columns), for the gate waves.
+template <class K>
+struct PTaps {
+    f32x4 qw[K::DK], vw[K::DV];
+    float qb[K::DK], vb[K::DV];
+};
+struct NoTaps {};
+
 // LDS layouts are permuted so that the lanes of one gate-wave access spread
 // over the banks, while every 8/16-byte operand group stays contiguous and
 // the MFMA waves' addresses stay loop-invariant:
@@ -199,7 +208,7 @@ struct Span {
 };
 
 // ------------------------------------------------------------------ chain role
-template <typename TIn, class K, bool SEG>
+template <typename TIn, class K, bool SEG, bool PRO>
 __device__ void chain_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int bh, int vt, int cw,
                            int lane) {
     constexpr int C = K::C, DK = K::DK;
@@ -211,17 +220,37 @@ __device__ void chain_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int
 
     float l = SEG ? p.seg_l0[((size_t)bh * p.nseg + sp.seg) * DK + i]
                   : (p.l0 ? p.l0[(size_t)bh * DK + i] : 1.f);
-    const float qn = p.qn[(size_t)(bh % p.H) * DK + i];
+    float qn = p.qn[(size_t)(bh % p.H) * DK + i];
+    // Block prologue: qn = softplus(zqn); k = silu(conv(x)) from the taps of
+    // key dim i and a window of the three x values before the token (from
+    // the convolution state before token 0)
+    float kw[4] = {0.f, 0.f, 0.f, 0.f}, kb = 0.f, kx1 = 0.f, kx2 = 0.f, kx3 = 0.f;
+    if constexpr (PRO) {
+        static_assert(!SEG, "the block prologue runs unsplit");
+        qn = act_softplus(qn);
+        const int W = p.conv_w;
+        const size_t ch = (size_t)(bh % p.H) * DK + i;
+        load_taps4(kw, p.conv_wt[1] + ch * W, W);
+        if (p.conv_b[1]) kb = p.conv_b[1][ch];
+        if (p.conv_s[1]) {
+            const TIn* st = (const TIn*)p.conv_s[1] + (size_t)bh * (W - 1) * DK + i;
+            if (W >= 2) kx1 = (float)st[(W - 2) * DK];
+            if (W >= 3) kx2 = (float)st[(W - 3) * DK];
+            if (W >= 4) kx3 = (float)st[(W - 4) * DK];
+        }
+    }
     float wrun = 1.f;  // sequence split: gate product from the segment start
     // One chunk of inputs per buffer; NBC buffers rotate, so a chunk's loads
     // are issued NBC-1 iterations before their first use.
     constexpr int NB = K::NBC, D = NB - 1;
     struct Buf {
-        float a[C];
-        unsigned k[C];  // bits of k, zero-extended (bf16 values sit in the low half)
-        float r;        // r of token `lane` of the chunk
+        // a, or with the prologue the bits of za like those of k
+        typename std::conditional<PRO, unsigned, float>::type a[C];
+        unsigned k[C];  // bits of k (or of its x), zero-extended (bf16 values sit in the low half)
+        float r;        // r (or zr) of token `lane` of the chunk
     };
     Buf b[NB];
+    auto bits_f = [](unsigned u) { return __builtin_bit_cast(float, sizeof(TIn) == 2 ? u << 16 : u); };
 
     // Rows of a and k are read through buffer resources over one chunk's
     // rows, so rows past T (the tail of the last chunk, chunks past the end)
@@ -229,11 +258,11 @@ __device__ void chain_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int
     // offsets are immediates: register offsets for the rows past 4 KiB spill
     // the chain role there.  At dk = 128 one resource per chunk and input is
     // faster (measured).
-    constexpr int ARB = DK * 4, KRB = DK * (int)sizeof(TIn);  // row bytes
+    constexpr int ARB = DK * (PRO ? (int)sizeof(TIn) : 4), KRB = DK * (int)sizeof(TIn);  // row bytes
     constexpr bool WIN = DK < 128;
     constexpr int ARW = WIN && 4096 / ARB < C ? 4096 / ARB : C;  // rows per resource
     constexpr int KRW = WIN && 4096 / KRB < C ? 4096 / KRB : C;
-    const char* abase = (const char*)(p.a + rowbase * DK);
+    const char* abase = (const char*)p.a + rowbase * ARB;
     const char* kbase = (const char*)(kp + rowbase * DK);
     const char* rbase = (const char*)(p.r + rowbase);
     auto rows_left = [&](int t, int cap) {
@@ -249,7 +278,14 @@ __device__ void chain_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int
             const int n = rows - w * ARW;
             const auto rs = make_rsrc(a0 + w * ARW * ARB, (n < 0 ? 0 : (n < ARW ? n : ARW)) * ARB);
 #pragma unroll
-            for (int t = 0; t < ARW; ++t) b.a[w * ARW + t] = buf_load<float>(rs, i * 4 + t * ARB);
+            for (int t = 0; t < ARW; ++t) {
+                if constexpr (!PRO)
+                    b.a[w * ARW + t] = buf_load<float>(rs, i * 4 + t * ARB);
+                else if constexpr (sizeof(TIn) == 2)
+                    b.a[w * ARW + t] = (unsigned)buf_load<unsigned short>(rs, i * 2 + t * ARB);
+                else
+                    b.a[w * ARW + t] = buf_load<unsigned>(rs, i * 4 + t * ARB);
+            }
         }
 #pragma unroll
         for (int w = 0; w < C / KRW; ++w) {
@@ -268,7 +304,7 @@ __device__ void chain_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int
         if (nchunks > 0) load(cc + D, nxt);
         if (cc < nchunks) {
             const int L = chunk_len(sp.TL, cc, C), par = cc & 1;
-            const float rho = lane < L ? 1.f / cur.r : 0.f;
+            const float rho = lane < L ? 1.f / (PRO ? act_softplus(cur.r) + p.r_eps : cur.r) : 0.f;
             if (cw == 0 && lane < C) sm.rho[par][lane] = rho;
             float f0 = 1.f;  // gate of token 0 of the chunk (sequence split)
             // full chunks take a copy of the scan without per-token tests
@@ -280,13 +316,28 @@ __device__ void chain_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int
                     if (FULL || t < L) {
                         const float rt = __builtin_bit_cast(
                             float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rho), t));
-                        const float a = cur.a[t];
-                        const float kv = __builtin_bit_cast(
-                            float, sizeof(TIn) == 2 ? cur.k[t] << 16 : cur.k[t]);
+                        float a, kv;
+                        if constexpr (PRO) {
+                            a = act_sigmoid(bits_f(cur.a[t]));
+                            const float x0 = bits_f(cur.k[t]);
+                            kv = act_silu(conv4(kw, kb, x0, kx1, kx2, kx3));
+                            kx3 = kx2;
+                            kx2 = kx1;
+                            kx1 = x0;
+                        } else {
+                            a = cur.a[t];
+                            kv = bits_f(cur.k[t]);
+                        }
                         const float lp = l * fast_rcp(__builtin_fmaf(qn, l, a * a));
                         l = __builtin_fmaf(kv * kv, rt, lp);
                         const float alp = a * lp;
-                        sm.LP[par][t][i ^ lp_swz(t)] = f32x2{alp, l};
+                        if constexpr (PRO) {
+                            // the gates themselves: the gate waves have no k
+                            const float rl = fast_rcp(l);
+                            sm.LP[par][t][i ^ lp_swz(t)] = f32x2{alp * rl, kv * rt * rl};
+                        } else {
+                            sm.LP[par][t][i ^ lp_swz(t)] = f32x2{alp, l};
+                        }
                         if (t >= 1) { num *= alp; den *= l; }
                         if (SEG && t == 0) { f0 = alp * fast_rcp(l); }
                     }
@@ -571,11 +622,26 @@ __device__ void chain_role_scan(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp
     lds_barrier();
 }
 
+// a lane's 4- or 8-byte value from lane src of the wave
+template <typename V>
+__device__ __forceinline__ V shfl_val(V v, int src) {
+    if constexpr (sizeof(V) == 4) {
+        return __builtin_bit_cast(V, __shfl(__builtin_bit_cast(int, v), src, 64));
+    } else {
+        static_assert(sizeof(V) == 8, "4 or 8 bytes");
+        i32x2 x = __builtin_bit_cast(i32x2, v);
+        x[0] = __shfl(x[0], src, 64);
+        x[1] = __shfl(x[1], src, 64);
+        return __builtin_bit_cast(V, x);
+    }
+}
+
 // ------------------------------------------------------------------ gate role
-template <typename TIn, class K, bool SEG>
-__device__ void gate_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int bh, int vt, int gw,
+template <typename TIn, class K, bool SEG, bool PRO, class TAPS>
+__device__ void gate_role(S3<TIn, K>& sm, TAPS& taps, const FwdArgs& p, const Span& sp, int bh, int vt, int gw,
                           int lane) {
     typedef Pair<TIn> PR;
+    typedef typename Quad<TIn>::V QV;
     constexpr int C = K::C, DK = K::DK, DV = K::DV, TPG = K::TPG;
     const size_t rowbase = (size_t)bh * p.T + sp.T0;
     const int nchunks = (sp.TL + C - 1) / C;
@@ -593,11 +659,12 @@ __device__ void gate_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int 
 
     struct Buf {
         typename PR::V q[TPG], k[TPG];
-        typename Quad<TIn>::V v[K::VPT][2];
+        QV v[K::VPT][2];
+        QV vh[K::VPT][3];  // block prologue: the three v rows before the unit's tokens
     };
     constexpr int NB = K::NBG, D = NB - 1;
     Buf b[NB];
-    constexpr int NLD = 2 * TPG + 2 * K::VPT;  // loads per chunk
+    constexpr int NLD = (PRO ? TPG + 5 * K::VPT : 2 * TPG + 2 * K::VPT);  // loads per chunk
     // The next chunk's rows are requested after the step's work: at the step
     // start they queue with the chain waves' requests, which are on the
     // critical path (measured 8% faster on the LM-layer shape, 4% on the
@@ -618,6 +685,38 @@ __device__ void gate_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int 
         voff[x][0] = 2 * tp * VRB + (vt * DV + 4 * jq) * ES;
         voff[x][1] = voff[x][0] + VRB;
     }
+    // Block prologue: the chain waves form k and the gates f, w; the gate
+    // waves form q and v.  They stage the taps and biases in LDS (read from
+    // the first gated chunk on, after the pipeline's first barrier).  The
+    // three x rows of q before a lane's first token come from the lane of the
+    // previous token group, and for the first group from the last group's
+    // rows of the previous chunk, kept in pq (before token 0: the convolution
+    // state).  The three v rows before a unit's tokens are loaded with it.
+    typename PR::V pq[3];
+    if constexpr (PRO) {
+        const int W = p.conv_w, h = bh % p.H;
+        for (int x = gtid; x < DK; x += 256) {
+            const size_t ch = (size_t)h * DK + x;
+            float w4[4];
+            load_taps4(w4, p.conv_wt[0] + ch * W, W);
+            taps.qw[x] = f32x4{w4[0], w4[1], w4[2], w4[3]};
+            taps.qb[x] = p.conv_b[0] ? p.conv_b[0][ch] : 0.f;
+        }
+        for (int x = gtid; x < DV; x += 256) {
+            const size_t ch = (size_t)h * p.dv + vt * DV + x;
+            float w4[4];
+            load_taps4(w4, p.conv_wt[2] + ch * W, W);
+            taps.vw[x] = f32x4{w4[0], w4[1], w4[2], w4[3]};
+            taps.vb[x] = p.conv_b[2] ? p.conv_b[2][ch] : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {  // token j - 3: state row W - 4 + j
+            const int sr = W - 4 + j;
+            pq[j] = PR::zero();
+            const size_t so = ((size_t)bh * (W - 1) + sr) * DK + 2 * ip;
+            if (sr >= 0 && p.conv_s[0]) pq[j] = *(const typename PR::V*)((const TIn*)p.conv_s[0] + so);
+        }
+    }
     auto load = [&](int c, Buf& bf) {
         const int t0 = c * C, n = sp.TL - t0;
         const int rows = n < 0 ? 0 : (n < C ? n : C);
@@ -627,12 +726,23 @@ __device__ void gate_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int 
 #pragma unroll
         for (int u = 0; u < TPG; ++u) {
             bf.q[u] = buf_load<typename PR::V>(rq, qoff + u * QRB);
-            bf.k[u] = buf_load<typename PR::V>(rk, qoff + u * QRB);
+            if constexpr (!PRO) bf.k[u] = buf_load<typename PR::V>(rk, qoff + u * QRB);
         }
 #pragma unroll
         for (int x = 0; x < K::VPT; ++x)
 #pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) bf.v[x][h2] = buf_load<typename Quad<TIn>::V>(rv, voff[x][h2]);
+            for (int h2 = 0; h2 < 2; ++h2) bf.v[x][h2] = buf_load<QV>(rv, voff[x][h2]);
+        if constexpr (PRO) {
+            // rows t0-3 .. of the sequence, clipped to [0, TL): rows before
+            // token 0 read as zero (the state is added at the first chunk)
+            const int h0 = t0 >= 3 ? t0 - 3 : 0;
+            const int hend = t0 + rows < sp.TL ? t0 + rows : sp.TL;
+            const auto rh = make_rsrc(vbase + (size_t)h0 * VRB, (hend > h0 ? hend - h0 : 0) * VRB);
+#pragma unroll
+            for (int x = 0; x < K::VPT; ++x)
+#pragma unroll
+                for (int j = 0; j < 3; ++j) bf.vh[x][j] = buf_load<QV>(rh, voff[x][0] + (j - 3 + t0 - h0) * VRB);
+        }
     };
 
     auto step = [&](int c, Buf& cur, Buf& nxt) {
@@ -645,24 +755,86 @@ __device__ void gate_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int 
             for (int x = 0; x < K::VPT; ++x) {
                 const int unit = gtid + x * 256;
                 const int tp = unit / K::VQ, jq = unit % K::VQ;
-                const f32x4 v0 = Quad<TIn>::to_f32(cur.v[x][0]), v1 = Quad<TIn>::to_f32(cur.v[x][1]);
+                f32x4 v0 = Quad<TIn>::to_f32(cur.v[x][0]), v1 = Quad<TIn>::to_f32(cur.v[x][1]);
+                if constexpr (PRO) {
+                    f32x4 h[3];
+#pragma unroll
+                    for (int j = 0; j < 3; ++j) h[j] = Quad<TIn>::to_f32(cur.vh[x][j]);
+                    if (cg == 0 && p.conv_s[2]) {
+                        // the first chunk: rows before token 0 from the state
+                        const int W = p.conv_w;
+#pragma unroll
+                        for (int j = 0; j < 3; ++j) {
+                            const int sr = W - 1 + 2 * tp - 3 + j;
+                            if (2 * tp - 3 + j < 0 && sr >= 0)
+                                h[j] += Quad<TIn>::to_f32(*(const QV*)((const TIn*)p.conv_s[2] +
+                                                                      ((size_t)bh * (W - 1) + sr) * p.dv +
+                                                                      vt * DV + 4 * jq));
+                        }
+                    }
+                    const bool in0 = 2 * tp < L, in1 = 2 * tp + 1 < L;
+                    f32x4 y0, y1;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const f32x4 w4 = taps.vw[4 * jq + e];
+                        const float b = taps.vb[4 * jq + e];
+                        y0[e] = in0 ? act_silu(conv4(w4, b, v0[e], h[2][e], h[1][e], h[0][e])) : 0.f;
+                        y1[e] = in1 ? act_silu(conv4(w4, b, v1[e], v0[e], h[2][e], h[1][e])) : 0.f;
+                    }
+                    v0 = y0;
+                    v1 = y1;
+                }
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     *(typename PR::V*)&sm.VT[par][4 * jq + e][(2 * tp) ^ vt_swz<K>(4 * jq + e)] =
                         PR::make(v0[e], v1[e]);
             }
+            // q of the lane's tokens: the loaded rows, or with the block
+            // prologue their convolution and SiLU (the three earlier rows from
+            // the lane of the previous token group)
+            typename PR::V hq[3];
+            if constexpr (PRO) {
+                const int src = grp > 0 ? lane - 1 : lane + K::NGRP - 1;
+#pragma unroll
+                for (int j = 0; j < 3; ++j) hq[j] = shfl_val(grp == K::NGRP - 1 ? pq[j] : cur.q[TPG - 3 + j], src);
+#pragma unroll
+                for (int j = 0; j < 3; ++j) pq[j] = cur.q[TPG - 3 + j];
+            }
+            // value e (0: key dim 2ip, 1: 2ip+1) of row j of a window whose
+            // rows 0..2 are the halo h and 3.. the lane's tokens
+            auto xw = [&](const typename PR::V* rows, const typename PR::V (&h)[3], int j, int e) {
+                const typename PR::V v = j < 3 ? h[j] : rows[j - 3];
+                return e ? PR::hi(v) : PR::lo(v);
+            };
+            auto qval = [&](int u, int e) -> float {
+                if constexpr (PRO) {
+                    const int c = 2 * ip + e;
+                    return act_silu(conv4(taps.qw[c], taps.qb[c], xw(cur.q, hq, 3 + u, e), xw(cur.q, hq, 2 + u, e),
+                                          xw(cur.q, hq, 1 + u, e), xw(cur.q, hq, u, e)));
+                } else {
+                    return e ? PR::hi(cur.q[u]) : PR::lo(cur.q[u]);
+                }
+            };
             // gates
             float f[TPG][2], w[TPG][2];
 #pragma unroll
             for (int u = 0; u < TPG; ++u) {
                 const int t = grp * TPG + u;
-                const f32x4 lq = *(const f32x4*)&sm.LP[par][t][(2 * ip) ^ lp_swz(t)];  // a*lp, l (two key dims)
-                const float rh = sm.rho[par][t];
-                const float rl0 = fast_rcp(lq[1]), rl1 = fast_rcp(lq[3]);
-                f[u][0] = lq[0] * rl0;
-                f[u][1] = lq[2] * rl1;
-                w[u][0] = PR::lo(cur.k[u]) * rh * rl0;
-                w[u][1] = PR::hi(cur.k[u]) * rh * rl1;
+                // a*lp, l (two key dims); with the block prologue f, w
+                const f32x4 lq = *(const f32x4*)&sm.LP[par][t][(2 * ip) ^ lp_swz(t)];
+                if constexpr (PRO) {
+                    f[u][0] = lq[0];
+                    w[u][0] = lq[1];
+                    f[u][1] = lq[2];
+                    w[u][1] = lq[3];
+                } else {
+                    const float rh = sm.rho[par][t];
+                    const float rl0 = fast_rcp(lq[1]), rl1 = fast_rcp(lq[3]);
+                    f[u][0] = lq[0] * rl0;
+                    f[u][1] = lq[2] * rl1;
+                    w[u][0] = PR::lo(cur.k[u]) * rh * rl0;
+                    w[u][1] = PR::hi(cur.k[u]) * rh * rl1;
+                }
             }
             const float* Eprev = sm.E[par ^ 1];
             const float wc0 = SEG ? sm.Wc[par][2 * ip] : 1.f, wc1 = SEG ? sm.Wc[par][2 * ip + 1] : 1.f;
@@ -715,8 +887,8 @@ __device__ void gate_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int 
                     const int t = grp * TPG + u;
                     const float g0 = G[u][0] * e0, g1 = G[u][1] * e1;
                     const bool in = FULL || t < L;
-                    const float q0 = in ? PR::lo(cur.q[u]) * g0 : 0.f;
-                    const float q1 = in ? PR::hi(cur.q[u]) * g1 : 0.f;
+                    const float q0 = in ? qval(u, 0) * g0 : 0.f;
+                    const float q1 = in ? qval(u, 1) * g1 : 0.f;
                     const float w0 = in ? w[u][0] * fast_rcp(g0) : 0.f;
                     const float w1 = in ? w[u][1] * fast_rcp(g1) : 0.f;
                     *(typename PR::V*)&sm.op[par].fac.Q[qw_row<K>(t)][2 * ip] = PR::make(q0, q1);
@@ -777,8 +949,8 @@ __device__ void gate_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int 
 #pragma unroll
                         for (int u = 0; u < TPG; ++u) {
                             const int t = grp * TPG + u;
-                            const float q0 = PR::lo(cur.q[u]) * G[u][0] * e0 * wc0;
-                            const float q1 = PR::hi(cur.q[u]) * G[u][1] * e1 * wc1;
+                            const float q0 = qval(u, 0) * G[u][0] * e0 * wc0;
+                            const float q1 = qval(u, 1) * G[u][1] * e1 * wc1;
                             buf_store(PR::make(q0, q1), rqh, qho(t, 2 * ip) * (int)sizeof(TIn));
                         }
                     }
@@ -968,10 +1140,12 @@ __device__ void mma_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int b
     }
 }
 
-template <typename TIn, int DK, int DV, bool SEG, bool SCAN>
+template <typename TIn, int DK, int DV, bool SEG, bool SCAN, bool PRO>
 __global__ __launch_bounds__((P3<TIn, DK, DV>::NT)) void kla_fwd_diag_pipe_kernel(FwdArgs p) {
+    static_assert(!(SCAN && PRO), "the block prologue runs with the serial chain");
     typedef P3<TIn, DK, DV> K;
     __shared__ S3<TIn, K> sm;
+    __shared__ typename std::conditional<PRO, PTaps<K>, NoTaps>::type taps;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int BH = p.B * p.H, nvt = p.n_vtiles, nseg = SEG ? p.nseg : 1;
     const int nu = nvt * nseg;  // workgroups per (b,h): value tiles x segments
@@ -1006,13 +1180,13 @@ __global__ __launch_bounds__((P3<TIn, DK, DV>::NT)) void kla_fwd_diag_pipe_kerne
     if (wave < K::NCW) {
         __builtin_amdgcn_s_setprio(2);
         if constexpr (SCAN) chain_role_scan<TIn, K, SEG>(sm, p, sp, bh, vt, wave, lane);
-        else chain_role<TIn, K, SEG>(sm, p, sp, bh, vt, wave, lane);
+        else chain_role<TIn, K, SEG, PRO>(sm, p, sp, bh, vt, wave, lane);
     } else if (wave < 4) {
-        gate_role<TIn, K, SEG>(sm, p, sp, bh, vt, wave - K::NCW, lane);
+        gate_role<TIn, K, SEG, PRO>(sm, taps, p, sp, bh, vt, wave - K::NCW, lane);
     } else if (wave < 4 + K::NMW) {
         mma_role<TIn, K, SEG>(sm, p, sp, bh, vt, wave - 4, lane);
     } else {
-        gate_role<TIn, K, SEG>(sm, p, sp, bh, vt, 4 - K::NCW + (wave - 4 - K::NMW), lane);
+        gate_role<TIn, K, SEG, PRO>(sm, taps, p, sp, bh, vt, 4 - K::NCW + (wave - 4 - K::NMW), lane);
     }
 }
 
@@ -1021,18 +1195,29 @@ hipError_t launch_chain(const FwdArgs& a, hipStream_t s) {
     typedef P3<TIn, DK, DV> K;
     if (a.nseg > 1) {
         const int nblk = a.B * a.H * a.n_vtiles * a.nseg;
-        hipLaunchKernelGGL((kla_fwd_diag_pipe_kernel<TIn, DK, DV, true, SCAN>), dim3(nblk), dim3(K::NT), 0, s, a);
+        hipLaunchKernelGGL((kla_fwd_diag_pipe_kernel<TIn, DK, DV, true, SCAN, false>), dim3(nblk), dim3(K::NT), 0,
+                           s, a);
     } else {
         const int nblk = a.B * a.H * a.n_vtiles;
-        hipLaunchKernelGGL((kla_fwd_diag_pipe_kernel<TIn, DK, DV, false, SCAN>), dim3(nblk), dim3(K::NT), 0, s, a);
+        hipLaunchKernelGGL((kla_fwd_diag_pipe_kernel<TIn, DK, DV, false, SCAN, false>), dim3(nblk), dim3(K::NT),
+                           0, s, a);
     }
     return hipGetLastError();
 }
 
 // the serial chain by default; the wavefront-level scan chain on request
-// (bf16 inputs: the fp32 build of the scan chain spills)
+// (bf16 inputs: the fp32 build of the scan chain spills); the block prologue
+// (unsplit, serial chain) when conv_w is set
 template <typename TIn, int DK, int DV>
 hipError_t launch(const FwdArgs& a, hipStream_t s) {
+    if (a.conv_w > 0) {
+        if (a.nseg > 1) return hipErrorInvalidValue;
+        typedef P3<TIn, DK, DV> K;
+        const int nblk = a.B * a.H * a.n_vtiles;
+        hipLaunchKernelGGL((kla_fwd_diag_pipe_kernel<TIn, DK, DV, false, false, true>), dim3(nblk), dim3(K::NT), 0,
+                           s, a);
+        return hipGetLastError();
+    }
     if constexpr (std::is_same<TIn, bf16>::value) {
         if (a.chain_scan) return launch_chain<TIn, DK, DV, true>(a, s);
     }

@@ -27,6 +27,18 @@ struct FwdArgs {
     // wavefront-level Mobius scan instead of the per-lane serial recursion
     bool chain_scan = false;
 
+    // Fused block prologue (conv_w > 0, diagonal wave-specialised kernel):
+    // q, k, v then hold the projections before the causal convolution, a the
+    // decay's pre-activation za in the storage dtype, qn its pre-activation
+    // zqn and r the pre-activation zr; the kernel forms
+    // q = silu(conv(q)), ..., a = sigmoid(za), qn = softplus(zqn),
+    // r = softplus(zr) + r_eps.
+    int conv_w = 0;                       // taps W, 1..4 (0: no prologue)
+    const float* conv_wt[3] = {};         // taps of q, k, v: [H, d, W]
+    const float* conv_b[3] = {};          // biases [H, d] or null (zero)
+    const void* conv_s[3] = {};           // states [B, H, W-1, d] or null (zero)
+    float r_eps = 0.f;
+
     // Sequence split (diagonal, wave-specialised kernel only).  With nseg > 1
     // the workgroup of segment s handles tokens [s*seg_len, min(T,(s+1)*seg_len))
     // of its (b,h), starts from seg_l0 and a zero state, and leaves its local

@@ -273,3 +273,46 @@ def test_backward_argument_errors():
     assert bwd_call(d, dk=addr(12) + 16) == ALIAS       # dk inside dq
     assert bwd_call(d, workspace=addr(14)) == ALIAS     # workspace over da
     assert bwd_call(KlaDims(0, 4, 16, 16, 16, F32, ISO)) == OK
+
+
+def block_call(dims, blk=None, **over):
+    args = dict(xq=addr(1), xk=addr(2), xv=addr(3), za=addr(4), zqn=addr(5), zr=addr(6), l0=None,
+                eta0=None, o=addr(7), lT=addr(8), etaT=addr(9), stream=None)
+    args.update(over)
+    if blk is None:
+        blk = scan_amd.KlaBlock(4, addr(10), addr(11), addr(12), None, None, None, None, None, None,
+                                1e-3)
+    return scan_amd.klaFwdBlock(dims, blk, **args)
+
+
+def test_block_argument_errors():
+    d = KlaDims(2, 3, 40, 128, 128, BF16, DIAG)
+    assert scan_amd.klaFwdBlock(d, None, *([None] * 11), None) == NULL
+    for w in (0, 5, -1):
+        blk = scan_amd.KlaBlock(w, addr(10), addr(11), addr(12), None, None, None, None, None, None, 1e-3)
+        assert block_call(d, blk) == SHAPE, w
+    blk = scan_amd.KlaBlock(4, addr(10), addr(11), addr(12), None, None, None, None, None, None, -1.0)
+    assert block_call(d, blk) == SHAPE
+    blk = scan_amd.KlaBlock(4, addr(10), addr(11), addr(12), None, None, None, None, None, None,
+                            float("nan"))
+    assert block_call(d, blk) == SHAPE
+    # only the diagonal wave-specialised shapes
+    assert block_call(KlaDims(2, 3, 40, 128, 128, BF16, ISO)) == UNSUP
+    assert block_call(KlaDims(2, 3, 40, 32, 32, F32, DIAG)) == UNSUP
+    assert block_call(KlaDims(2, 3, 40, 128, 128, F32, DIAG)) == UNSUP
+    assert block_call(KlaDims(2, 3, 40, 128, 64, BF16, DIAG)) == UNSUP
+    for name in ("xq", "xk", "xv", "za", "zqn", "zr", "o"):
+        assert block_call(d, **{name: None}) == NULL, name
+    blk = scan_amd.KlaBlock(4, None, addr(11), addr(12), None, None, None, None, None, None, 1e-3)
+    assert block_call(d, blk) == NULL
+    assert block_call(d, xq=addr(1) + 8) == ALIGN
+    blk = scan_amd.KlaBlock(4, addr(10) + 2, addr(11), addr(12), None, None, None, None, None, None, 1e-3)
+    assert block_call(d, blk) == ALIGN
+    blk = scan_amd.KlaBlock(4, addr(10) + 4, addr(11), addr(12), None, None, None, addr(13) + 4, None,
+                            None, 1e-3)
+    assert block_call(d, blk) == ALIGN                   # states must be 16-byte aligned
+    assert block_call(d, o=addr(1)) == ALIAS             # o over xq
+    assert block_call(d, lT=addr(5)) == ALIAS            # lT over zqn
+    blk = scan_amd.KlaBlock(4, addr(7), addr(11), addr(12), None, None, None, None, None, None, 1e-3)
+    assert block_call(d, blk) == ALIAS                   # taps under o
+    assert block_call(KlaDims(0, 3, 40, 128, 128, BF16, DIAG)) == OK
