@@ -13,6 +13,8 @@ flops against the MFMA peak of the input dtype, and the fp64 oracle timed on
 the host cores over a bounded sample of the same workload.
 
   python bench.py [--steps K] [--warmup W] [--workload long_diag] [--no-cpu]
+  (workloads: the names in scan_amd.inputs, iso_decode, iso_prefill16,
+   residual_lm_diag, block_lm_diag)
 """
 from __future__ import annotations
 
@@ -127,6 +129,18 @@ def alg_bytes(w) -> float:
         per_tok = (2 * w.dk + w.dv) * es + 12 + w.dv * es
         per_seq = 4 + 4 * w.dk * w.dv
     return float(ntok * per_tok + w.B * w.H * per_seq)
+
+
+def block_alg_bytes(w, width: int) -> float:
+    """Algorithmic HBM bytes of one forward with the fused block prologue: the
+    projections xq, xk, xv and za read once (storage dtype), zr read once, o
+    written once, lT and etaT written once per (b,h), and per head the
+    convolution taps and biases of q, k, v and zqn read once."""
+    es = 2 if w.dtype == "bf16" else 4
+    per_tok = (3 * w.dk + w.dv) * es + 4 + w.dv * es
+    per_seq = 4 * w.dk + 4 * w.dk * w.dv
+    per_head = (2 * w.dk + w.dv) * (width + 1) * 4 + 4 * w.dk
+    return float(w.B * w.H * w.T * per_tok + w.B * w.H * per_seq + w.H * per_head)
 
 
 def decode_alg_bytes(w) -> float:
@@ -314,6 +328,45 @@ def run_prefill(args, torch, np, scan_amd, gen) -> dict:
     }
 
 
+def block_cpu_baseline(args, host, w) -> dict:
+    """The block oracle (fp64 prologue, then the sequential recurrence) timed
+    on a sample of whole sequences of the workload, about --cpu-seconds."""
+    import oracle
+    from oracle import block as oblock
+    threads = oracle.default_threads()
+    names = ("xq", "xk", "xv", "za", "zqn", "zr", "wq", "wk", "wv", "bq", "bk", "bv")
+    B, H, T = w.B, w.H, w.T
+
+    def sub(nb, nh):
+        out = {}
+        for n in names:
+            x = host[n]
+            if n in ("zqn", "wq", "wk", "wv", "bq", "bk", "bv"):
+                out[n] = x[:nh]
+            else:
+                out[n] = x[:nb, :nh]
+        return out
+
+    one = sub(1, 1)
+    t0 = time.perf_counter()
+    oblock.block_fwd(*(one[n] for n in names), r_eps=host["r_eps"], nthreads=1)
+    t_one = time.perf_counter() - t0
+    nseq = int(max(threads, min(B * H, args.cpu_seconds * threads / max(t_one, 1e-6))))
+    nh = H if nseq >= H else max(1, nseq)
+    nb = max(1, min(B, nseq // H)) if nseq >= H else 1
+    s = sub(nb, nh)
+    reps, t_cpu = 0, 0.0
+    while reps == 0 or (t_cpu < 0.5 * args.cpu_seconds and reps < 100):
+        t0 = time.perf_counter()
+        oblock.block_fwd(*(s[n] for n in names), r_eps=host["r_eps"], nthreads=threads)
+        t_cpu += time.perf_counter() - t0
+        reps += 1
+    seqs = nb * nh
+    return {"value": seqs * T * reps / H / t_cpu, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{seqs} of {B * H} (b,h) sequences at full T={T} ({nb}x{nh}), fp64 prologue "
+                      f"(numpy) + sequential recurrence, {reps} pass(es) in {t_cpu:.1f}s"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -346,17 +399,24 @@ def main() -> int:
     if args.workload == gen.PREFILL.name:
         print(json.dumps(run_prefill(args, torch, np, scan_amd, gen)), flush=True)
         return 0
-    # the residual-write forward (klaFwdResidual) at the LM-layer shape, or
-    # the KLA forward (klaFwd) on one of the named workloads
+    # the residual-write forward (klaFwdResidual) at the LM-layer shape, the
+    # forward with the fused block prologue (klaFwdBlock) at the LM-layer
+    # shape, or the KLA forward (klaFwd) on one of the named workloads
     residual = args.workload == gen.RESIDUAL.name
-    w = gen.RESIDUAL if residual else gen.WORKLOADS[args.workload]
+    blockw = args.workload == gen.BLOCK.name
+    w = gen.RESIDUAL if residual else gen.BLOCK if blockw else gen.WORKLOADS[args.workload]
     print(f"bench: workload {w}", file=sys.stderr, flush=True)
-    host = gen.make_inputs(w, seed=0)
-    names = ("q", "k", "v", "a", "qn", "r")
+    if blockw:
+        host = gen.make_block_inputs(w, seed=0)
+        names = ("xq", "xk", "xv", "za", "zqn", "zr", "wq", "wk", "wv", "bq", "bk", "bv")
+        nbytes = block_alg_bytes(w, host["width"])
+    else:
+        host = gen.make_inputs(w, seed=0)
+        names = ("q", "k", "v", "a", "qn", "r")
+        nbytes = alg_bytes(w)
     # resident copies of the inputs and outputs, rotated so that the data one
     # step touches was last touched at least three MALL sizes of traffic ago
     # (consecutive steps never hit the 256 MB last-level cache)
-    nbytes = alg_bytes(w)
     ncopies = max(2, -(-3 * MALL_BYTES // int(nbytes)))
     sets = [[host[n].to("cuda") for n in names]]
     for _ in range(ncopies - 1):
@@ -374,6 +434,8 @@ def main() -> int:
         o, lT, etaT = outs[i % ncopies]
         if residual:
             scan_amd.fwd_residual(*s, cov=w.cov, o=o, lT=lT, mT=etaT)
+        elif blockw:
+            scan_amd.fwd_block(*s, r_eps=host["r_eps"], o=o, lT=lT, etaT=etaT)
         else:
             scan_amd.fwd(*s, cov=w.cov, o=o, lT=lT, etaT=etaT)
 
@@ -414,7 +476,9 @@ def main() -> int:
     calibration_copy(args, torch)
 
     cpu = None
-    if not args.no_cpu:
+    if not args.no_cpu and blockw:
+        cpu = block_cpu_baseline(args, host, w)
+    elif not args.no_cpu:
         import oracle
         threads = oracle.default_threads()
         oracle_fwd = oracle.fwd_residual if residual else oracle.fwd
@@ -453,12 +517,14 @@ def main() -> int:
     traffic = stored_traffic(w.name, fam)
     counters = stored_counters(w.name, fam)
     kernel_name = ("kla_fwd_residual_kernel" if residual else
+                   "kla_fwd_diag_pipe_kernel (block prologue, value tiles)" if blockw else
                    scan_amd.fwd_kernel_name(w.B, w.H, w.T, w.dk, w.dv, w.cov, w.dtype))
     flops = alg_flops(w)
     mfma_tfs = flops / (kern_ms / 1e3) / 1e12
     line = {
         "metric": ("KLA residual-write layer fwd tokens/s at B·T, H×d; % of HBM roofline" if residual
-                   else "KLA layer fwd tokens/s at B·T, H×d; % of HBM/MFMA roofline"),
+                   else "KLA block fwd (fused conv1d+SiLU prologue) tokens/s at B·T, H×d; % of HBM roofline"
+                   if blockw else "KLA layer fwd tokens/s at B·T, H×d; % of HBM/MFMA roofline"),
         "value": value,
         "unit": "tokens/s",
         "n_gpus": 1,
