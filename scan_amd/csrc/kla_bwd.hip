@@ -45,6 +45,7 @@
 // (b,h) leaves its partial in the workspace and a second kernel sums over b.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "kla_bwd.h"
 #include "kla_common.h"
@@ -80,8 +81,10 @@ struct BwdSm {
     alignas(16) float cq[NH][TB][D];
     alignas(16) float v[NH][TB][D];
     alignas(16) float dO[NH][TB][D];
-    // per-row partial sums (over a thread's value quad): [token][quad][row]
-    alignas(16) double rpart[NH][TB][VQ][D];
+    // per-row partial sums (over a thread's value quad): [token][quad][row];
+    // rows padded by two doubles, so that the 32 value quads of a wave store
+    // to different banks
+    alignas(16) double rpart[NH][TB][VQ][D + 2];
     // per-column partial sums (over a thread's rows): one quad per thread
     alignas(16) f32x4 cpart[NH][TB][NTH];
     double red[NH][TB][2][2];  // cross-wave sums of the key-dim lanes
@@ -435,6 +438,370 @@ __global__ __launch_bounds__(kBwdThreads) void kla_bwd_kernel(BwdArgs p) {
     }
 }
 
+// Diagonal precision: the same two sweeps with the global reads of a token
+// block issued one block ahead.  The key-dim lanes load the next block's
+// k, r, a, q (and, in sweep 2, the stored precisions and q dq) into
+// registers before the current block's state update and turn them into the
+// LDS coefficients after it; the staging lanes do the same for the v and dO
+// rows.  The precisions of the current block stay in registers, and the
+// per-token sum of dr over key dims is a wave reduction (the two waves of
+// dk = 128 combine after the block's closing barrier).  The arithmetic and
+// its order are those of kla_bwd_kernel.
+template <typename TIn, int D>
+__global__ __launch_bounds__(kBwdThreads) void kla_bwd_diag_kernel(BwdArgs p) {
+    typedef BwdLayout<D> Ly;
+    typedef typename Quad<TIn>::V QV;
+    constexpr int TB = Ly::TB, NTH = Ly::NTH, NH = Ly::NH, VQ = Ly::VQ, RG = Ly::RG, RPT = Ly::RPT;
+    constexpr int W = D < 64 ? D : 64;  // key-dim lanes per wave
+    __shared__ BwdSm<D> sm;
+    __shared__ double drw[NH][TB][2];   // per-wave sums of dr (dk = 128)
+    (void)RG;
+
+    const int tid = threadIdx.x;
+    const int grp = NH == 1 ? 0 : tid / NTH, lt = NH == 1 ? tid : tid % NTH;
+    const int nbh = p.B * p.H, bh_ = NH == 1 ? (int)blockIdx.x : (int)blockIdx.x * NH + grp;
+    const bool valid = NH == 1 || bh_ < nbh;
+    const int bh = valid ? bh_ : nbh - 1;  // a spare group stays in bounds and stores nothing
+    const int h = bh % p.H;
+    const int jq = lt % VQ, rg = lt / VQ;
+    const int T = p.T;
+    const size_t row0 = (size_t)bh * T;
+    const TIn* q = (const TIn*)p.q;
+    const TIn* k = (const TIn*)p.k;
+    const TIn* v = (const TIn*)p.v;
+    const TIn* dOg = (const TIn*)p.dO;
+    const bool kd = lt < D;            // key-dim lane
+    const bool sl = lt < TB * VQ;      // staging lane: token lt / VQ, value quad jq
+    const int i = kd ? lt : D - 1;
+    double* wl = (double*)(p.ws + (size_t)bh * p.ws_stride);
+    double* wqdq = wl + (size_t)T * D;
+    float* wdqn = (float*)(wqdq + (size_t)T * D);
+
+    const float qn_i = p.qn[(size_t)h * D + i];
+    const double l_start = p.l0 ? p.l0[(size_t)bh * D + i] : 1.f;
+
+    // raw inputs of one token block
+    struct Raw {
+        float k[TB], r[TB], a[TB], q[TB];   // key-dim lanes
+        QV v, dO;                            // staging lanes
+    };
+    auto load_raw = [&](int t0, int nb, Raw& x) {
+        if (kd) {
+#pragma unroll
+            for (int u = 0; u < TB; ++u) {
+                const size_t t = row0 + t0 + (u < nb ? u : 0);
+                x.k[u] = (float)k[t * D + i];
+                x.r[u] = p.r[t];
+                x.a[u] = p.a[t * D + i];
+                x.q[u] = (float)q[t * D + i];
+            }
+        }
+        if (sl && lt / VQ < nb) {
+            const size_t t = row0 + t0 + lt / VQ;
+            x.v = *(const QV*)(v + t * D + 4 * jq);
+            x.dO = *(const QV*)(dOg + t * D + 4 * jq);
+        }
+    };
+    auto stage = [&](const Raw& x, int nb) {
+        if (sl && lt / VQ < nb) {
+            *(f32x4*)&sm.v[grp][lt / VQ][4 * jq] = Quad<TIn>::to_f32(x.v);
+            *(f32x4*)&sm.dO[grp][lt / VQ][4 * jq] = Quad<TIn>::to_f32(x.dO);
+        }
+    };
+
+    // ---------------------------------------------------------------- sweep 1
+    f64x4 e[RPT];
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+        const size_t off = ((size_t)bh * D + rg * RPT + m) * D + 4 * jq;
+        e[m] = p.eta0 ? to_f64(*(const f32x4*)(p.eta0 + off)) : f64x4{0., 0., 0., 0.};
+    }
+    double l = l_start;  // the precision recursion runs in fp64
+    double lb[TB];       // precisions after the current block's tokens
+    float qb[TB];        // q of the current block's tokens
+    // forward coefficients of a block from its raw inputs (advances l)
+    auto fwd_coefs = [&](const Raw& x, int t0, int nb) {
+#pragma unroll
+        for (int u = 0; u < TB; ++u) {
+            if (u < nb) {
+                const double kv = x.k[u], rt = x.r[u];
+                double rd;
+                const double g = gate_of(x.a[u], qn_i, l, &rd);
+                l = __builtin_fma(l, rd, kv * kv / rt);
+                lb[u] = l;
+                qb[u] = x.q[u];
+                if (kd) {
+                    sm.g[grp][u][i] = (float)g;
+                    sm.kap[grp][u][i] = (float)(kv / rt);
+                    if (valid) wl[(size_t)(t0 + u) * D + i] = l;
+                }
+            }
+        }
+        stage(x, nb);
+    };
+    Raw nx{};
+    if (T > 0) {
+        const int nb = T < TB ? T : TB;
+        load_raw(0, nb, nx);
+        fwd_coefs(nx, 0, nb);
+    }
+    lds_barrier();
+    for (int t0 = 0; t0 < T; t0 += TB) {
+        const int nb = T - t0 < TB ? T - t0 : TB;
+        const bool more = t0 + TB < T;
+        const int nb2 = more ? (T - t0 - TB < TB ? T - t0 - TB : TB) : 0;
+        if (more) load_raw(t0 + TB, nb2, nx);
+        // ---- the block on the thread's rows; per-row S partials
+#pragma unroll
+        for (int u = 0; u < TB; ++u) {
+            if (u < nb) {
+                const f64x4 vv = to_f64(*(const f32x4*)&sm.v[grp][u][4 * jq]);
+                const f64x4 dd = to_f64(*(const f32x4*)&sm.dO[grp][u][4 * jq]);
+#pragma unroll
+                for (int m4 = 0; m4 < RPT; m4 += 4) {
+                    const f32x4 gv = *(const f32x4*)&sm.g[grp][u][rg * RPT + m4];
+                    const f32x4 kv = *(const f32x4*)&sm.kap[grp][u][rg * RPT + m4];
+                    double sp[4];
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        e[m4 + x] = (double)gv[x] * e[m4 + x] + (double)kv[x] * vv;
+                        const f64x4 pr = e[m4 + x] * dd;
+                        sp[x] = (pr[0] + pr[1]) + (pr[2] + pr[3]);
+                    }
+                    *(f64x2*)&sm.rpart[grp][u][jq][rg * RPT + m4] = f64x2{sp[0], sp[1]};
+                    *(f64x2*)&sm.rpart[grp][u][jq][rg * RPT + m4 + 2] = f64x2{sp[2], sp[3]};
+                }
+            }
+        }
+        lds_barrier();
+        // ---- dq of the block (key-dim lanes)
+        if (kd) {
+#pragma unroll
+            for (int u = 0; u < TB; ++u) {
+                if (u < nb) {
+                    double s = 0.;
+#pragma unroll 8
+                    for (int x = 0; x < VQ; ++x) s += sm.rpart[grp][u][x][i];
+                    const size_t t = row0 + t0 + u;
+                    const double dq = s / lb[u];
+                    if (valid) {
+                        ((TIn*)p.gq)[t * D + i] = (TIn)(float)dq;
+                        // q dq with q / l rounded to fp32 exactly as sweep 2
+                        // stages it for the readout adjoint
+                        wqdq[(size_t)(t0 + u) * D + i] = (double)(float)((double)qb[u] / lb[u]) * s;
+                    }
+                }
+            }
+        }
+        if (more) fwd_coefs(nx, t0 + TB, nb2);
+        lds_barrier();
+    }
+    // boundary term of the gate adjoint: B[i] = sum_j detaT[i,j] eta_T[i,j];
+    // the state registers then take ebar_T = detaT
+    double Bsum = 0.;
+    {
+#pragma unroll
+        for (int m4 = 0; m4 < RPT; m4 += 4) {
+            double sp[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const size_t off = ((size_t)bh * D + rg * RPT + m4 + x) * D + 4 * jq;
+                const f64x4 dt = p.detaT ? to_f64(*(const f32x4*)(p.detaT + off)) : f64x4{0., 0., 0., 0.};
+                const f64x4 pr = e[m4 + x] * dt;
+                sp[x] = (pr[0] + pr[1]) + (pr[2] + pr[3]);
+                e[m4 + x] = dt;
+            }
+            *(f64x2*)&sm.rpart[grp][0][jq][rg * RPT + m4] = f64x2{sp[0], sp[1]};
+            *(f64x2*)&sm.rpart[grp][0][jq][rg * RPT + m4 + 2] = f64x2{sp[2], sp[3]};
+        }
+        __syncthreads();
+        if (kd) {
+#pragma unroll 8
+            for (int x = 0; x < VQ; ++x) Bsum += sm.rpart[grp][0][x][i];
+        }
+        __syncthreads();
+    }
+
+    // ---------------------------------------------------------------- sweep 2
+    double lbar = p.dlT ? p.dlT[(size_t)bh * D + i] : 0.f;
+    double cum = Bsum;
+    double dqn_acc = 0.;
+    // raw inputs of a block for sweep 2: those of sweep 1, the stored
+    // precisions (after each token, and before the block), the next token's
+    // a and q dq
+    struct Raw2 {
+        Raw x;
+        double lt[TB], lprev0, qdq[TB];
+        float an[TB];
+    };
+    auto load_raw2 = [&](int t0, int nb, Raw2& y) {
+        load_raw(t0, nb, y.x);
+        if (kd) {
+#pragma unroll
+            for (int u = 0; u < TB; ++u) {
+                const int t = t0 + (u < nb ? u : 0);
+                y.lt[u] = wl[(size_t)t * D + i];
+                y.qdq[u] = wqdq[(size_t)t * D + i];
+                y.an[u] = t + 1 < T ? p.a[(row0 + t + 1) * D + i] : 0.f;
+            }
+            y.lprev0 = t0 == 0 ? l_start : wl[(size_t)(t0 - 1) * D + i];
+        }
+    };
+    // the adjoint's inputs of the current block (registers)
+    double c_lt[TB], c_lprev[TB], c_qdq[TB];
+    float c_a[TB], c_k[TB], c_r[TB];
+    // backward coefficients of a block: gate of the token after each (1 past
+    // the end), k/r, q/l into LDS; its adjoint inputs into the registers
+    auto bwd_coefs = [&](const Raw2& y, int t0, int nb) {
+        stage(y.x, nb);
+#pragma unroll
+        for (int u = 0; u < TB; ++u) {
+            if (u < nb) {
+                const int t = t0 + u;
+                const double lt_ = y.lt[u];
+                double gn = 1., rd;
+                if (t + 1 < T) gn = gate_of(y.an[u], qn_i, lt_, &rd);
+                if (kd) {
+                    sm.g[grp][u][i] = (float)gn;
+                    sm.kap[grp][u][i] = (float)((double)y.x.k[u] / (double)y.x.r[u]);
+                    sm.cq[grp][u][i] = (float)((double)y.x.q[u] / lt_);
+                }
+                c_lt[u] = lt_;
+                c_lprev[u] = u == 0 ? y.lprev0 : y.lt[u - 1];
+                c_qdq[u] = y.qdq[u];
+                c_a[u] = y.x.a[u];
+                c_k[u] = y.x.k[u];
+                c_r[u] = y.x.r[u];
+            }
+        }
+    };
+    const int nblk = (T + TB - 1) / TB;
+    Raw2 ny{};
+    if (T > 0) {
+        const int t0 = (nblk - 1) * TB;
+        load_raw2(t0, T - t0, ny);
+        bwd_coefs(ny, t0, T - t0);
+    }
+    lds_barrier();
+    // dr of the previous block's tokens (dk = 128: the two waves' sums)
+    auto store_dr = [&](int t0, int nb) {
+        if constexpr (D > 64) {
+            if (tid < nb && valid) p.gr[row0 + t0 + tid] = (float)(drw[0][tid][0] + drw[0][tid][1]);
+        }
+    };
+    int prev_t0 = -1, prev_nb = 0;
+    for (int blk = nblk - 1; blk >= 0; --blk) {
+        const int t0 = blk * TB;
+        const int nb = T - t0 < TB ? T - t0 : TB;
+        if (blk > 0) load_raw2(t0 - TB, TB, ny);
+        if (prev_t0 >= 0) store_dr(prev_t0, prev_nb);
+        // ---- ebar over the block's tokens, last first; U and dv partials
+#pragma unroll
+        for (int u = TB - 1; u >= 0; --u) {
+            if (u < nb) {
+                const f64x4 vv = to_f64(*(const f32x4*)&sm.v[grp][u][4 * jq]);
+                const f64x4 dd = to_f64(*(const f32x4*)&sm.dO[grp][u][4 * jq]);
+                f64x4 cs = {0., 0., 0., 0.};
+#pragma unroll
+                for (int m4 = 0; m4 < RPT; m4 += 4) {
+                    const f32x4 gv = *(const f32x4*)&sm.g[grp][u][rg * RPT + m4];
+                    const f32x4 cv = *(const f32x4*)&sm.cq[grp][u][rg * RPT + m4];
+                    const f32x4 kv = *(const f32x4*)&sm.kap[grp][u][rg * RPT + m4];
+                    double sp[4];
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        e[m4 + x] = (double)gv[x] * e[m4 + x] + (double)cv[x] * dd;
+                        const f64x4 pr = e[m4 + x] * vv;
+                        sp[x] = (pr[0] + pr[1]) + (pr[2] + pr[3]);
+                        cs += (double)kv[x] * e[m4 + x];
+                    }
+                    *(f64x2*)&sm.rpart[grp][u][jq][rg * RPT + m4] = f64x2{sp[0], sp[1]};
+                    *(f64x2*)&sm.rpart[grp][u][jq][rg * RPT + m4 + 2] = f64x2{sp[2], sp[3]};
+                }
+                sm.cpart[grp][u][lt] = f32x4{(float)cs[0], (float)cs[1], (float)cs[2], (float)cs[3]};
+            }
+        }
+        lds_barrier();
+        // ---- dv of the block (staging lanes)
+        if (sl && lt / VQ < nb) {
+            const int u = lt / VQ;
+            f32x4 s = sm.cpart[grp][u][jq];
+#pragma unroll
+            for (int r2 = 1; r2 < Ly::RG; ++r2) s += sm.cpart[grp][u][r2 * VQ + jq];
+            if (valid) *(QV*)((TIn*)p.gv + (row0 + t0 + u) * D + 4 * jq) = Quad<TIn>::make(s);
+        }
+        // ---- the precision adjoint over the block (key-dim lanes compute,
+        // the dr sums run over every lane of a key-dim wave), last first
+        if (lt < ((D + 63) / 64) * 64) {
+#pragma unroll
+            for (int u = TB - 1; u >= 0; --u) {
+                if (u < nb) {
+                    const int t = t0 + u;
+                    const size_t tt = row0 + t;
+                    double Uv = 0.;
+#pragma unroll 8
+                    for (int x = 0; x < VQ; ++x) Uv += sm.rpart[grp][u][x][i];
+                    const double kv = c_k[u];
+                    const double rt = c_r[u];
+                    const double kap = (float)(kv / rt);  // the staged k/r of the state update
+                    const double lt_ = c_lt[u], lprev = c_lprev[u];
+                    const double a = c_a[u], qn = qn_i, qdq = c_qdq[u];
+                    const double kU = kap * Uv;
+                    lbar -= qdq / lt_;
+                    cum += qdq - kU;
+                    const double dlg = cum;
+                    const double den = a * a + qn * lprev;
+                    const double rd = 1. / den, rd2 = rd * rd;
+                    const double dk = Uv / rt + lbar * 2. * kv / rt;
+                    if (kd && valid) ((TIn*)p.gk)[tt * D + i] = (TIn)(float)dk;
+                    // dr: -(kap U + lbar b_i) / r, summed over key dims
+                    double dr = kd ? -(kap * Uv + lbar * kv * kv / rt) / rt : 0.;
+#pragma unroll
+                    for (int m = 1; m < W; m <<= 1) dr += __shfl_xor(dr, m, 64);
+                    if constexpr (D > 64) {
+                        if ((lt & 63) == 0) drw[0][u][lt >> 6] = dr;
+                    } else {
+                        if (lt == 0 && valid) p.gr[tt] = (float)dr;
+                    }
+                    const double da = -lbar * 2. * a * lprev * rd2 + dlg * (qn * lprev - a * a) * rd / a;
+                    const double dqn = -lbar * lprev * lprev * rd2 - dlg * lprev * rd;
+                    if (kd && valid) p.ga[tt * D + i] = (float)da;
+                    dqn_acc += dqn;
+                    lbar = lbar * a * a * rd2 - dlg * qn * rd;
+                }
+            }
+        }
+        if (blk > 0) bwd_coefs(ny, t0 - TB, TB);
+        prev_t0 = t0;
+        prev_nb = nb;
+        lds_barrier();
+    }
+    if (prev_t0 >= 0) store_dr(prev_t0, prev_nb);
+    // ---- initial-state gradients: deta0 = g_0 ebar_0, dl0 = lbar_{-1}
+    if (T > 0 && kd) {
+        double rd;
+        sm.g[grp][0][i] = (float)gate_of(p.a[row0 * D + i], qn_i, l_start, &rd);
+    }
+    __syncthreads();
+    if (!valid) return;
+    if (p.geta0) {
+#pragma unroll
+        for (int m4 = 0; m4 < RPT; m4 += 4) {
+            const f32x4 gv = T > 0 ? *(const f32x4*)&sm.g[grp][0][rg * RPT + m4] : f32x4{1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const f64x4 r4 = (double)gv[x] * e[m4 + x];
+                *(f32x4*)(p.geta0 + ((size_t)bh * D + rg * RPT + m4 + x) * D + 4 * jq) =
+                    f32x4{(float)r4[0], (float)r4[1], (float)r4[2], (float)r4[3]};
+            }
+        }
+    }
+    if (kd) {
+        if (p.gl0) p.gl0[(size_t)bh * D + i] = (float)lbar;
+        wdqn[i] = (float)dqn_acc;
+    }
+}
+
 // dqn[h, i] = sum over b of the per-(b,h) partials (in order of b).
 __global__ void kla_bwd_dqn_sum(BwdArgs p) {
     const int n = p.H * p.dk;
@@ -447,16 +814,31 @@ __global__ void kla_bwd_dqn_sum(BwdArgs p) {
     p.gqn[x] = s;
 }
 
+// The diagonal backward runs the prefetching kernel, the isotropic one the
+// plain two-sweep kernel (KLA_BWD_IMPL=plain selects it for diagonal too).
+bool bwd_plain() {
+    const char* e = getenv("KLA_BWD_IMPL");
+    return e && e[0] == 'p';
+}
+
+template <typename TIn, int D, bool ISO>
+void launch_d(const BwdArgs& a, dim3 grid, dim3 block, hipStream_t s) {
+    if (!ISO && !bwd_plain())
+        hipLaunchKernelGGL((kla_bwd_diag_kernel<TIn, D>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((kla_bwd_kernel<TIn, D, ISO>), grid, block, 0, s, a);
+}
+
 template <typename TIn, bool ISO>
 hipError_t dispatch(const BwdArgs& a, hipStream_t s) {
     const dim3 block(kBwdThreads);
     const int nbh = a.B * a.H;
     auto grid = [&](int nh) { return dim3((nbh + nh - 1) / nh); };
     if (nbh > 0) switch (a.dk) {
-        case 16: hipLaunchKernelGGL((kla_bwd_kernel<TIn, 16, ISO>), grid(BwdLayout<16>::NH), block, 0, s, a); break;
-        case 32: hipLaunchKernelGGL((kla_bwd_kernel<TIn, 32, ISO>), grid(BwdLayout<32>::NH), block, 0, s, a); break;
-        case 64: hipLaunchKernelGGL((kla_bwd_kernel<TIn, 64, ISO>), grid(BwdLayout<64>::NH), block, 0, s, a); break;
-        case 128: hipLaunchKernelGGL((kla_bwd_kernel<TIn, 128, ISO>), grid(BwdLayout<128>::NH), block, 0, s, a); break;
+        case 16: launch_d<TIn, 16, ISO>(a, grid(BwdLayout<16>::NH), block, s); break;
+        case 32: launch_d<TIn, 32, ISO>(a, grid(BwdLayout<32>::NH), block, s); break;
+        case 64: launch_d<TIn, 64, ISO>(a, grid(BwdLayout<64>::NH), block, s); break;
+        case 128: launch_d<TIn, 128, ISO>(a, grid(BwdLayout<128>::NH), block, s); break;
         default: return hipErrorInvalidValue;
     }
     hipError_t e = hipGetLastError();
