@@ -502,6 +502,14 @@ __global__ __launch_bounds__(kBwdThreads) void kla_bwd_diag_kernel(BwdArgs p) {
             x.dO = *(const QV*)(dOg + t * D + 4 * jq);
         }
     };
+    // sum over the VQ value quads of one row's partials, in four independent
+    // chains (the serial sum is a long dependent chain of fp64 adds)
+    auto quad_sum = [&](const double* col) {
+        double s4[4] = {0., 0., 0., 0.};
+#pragma unroll
+        for (int x = 0; x < VQ; ++x) s4[x % 4] += col[(size_t)x * (D + 2)];
+        return (s4[0] + s4[1]) + (s4[2] + s4[3]);
+    };
     auto stage = [&](const Raw& x, int nb) {
         if (sl && lt / VQ < nb) {
             *(f32x4*)&sm.v[grp][lt / VQ][4 * jq] = Quad<TIn>::to_f32(x.v);
@@ -579,9 +587,7 @@ __global__ __launch_bounds__(kBwdThreads) void kla_bwd_diag_kernel(BwdArgs p) {
 #pragma unroll
             for (int u = 0; u < TB; ++u) {
                 if (u < nb) {
-                    double s = 0.;
-#pragma unroll 8
-                    for (int x = 0; x < VQ; ++x) s += sm.rpart[grp][u][x][i];
+                    const double s = quad_sum(&sm.rpart[grp][u][0][i]);
                     const size_t t = row0 + t0 + u;
                     const double dq = s / lb[u];
                     if (valid) {
@@ -738,9 +744,7 @@ __global__ __launch_bounds__(kBwdThreads) void kla_bwd_diag_kernel(BwdArgs p) {
                 if (u < nb) {
                     const int t = t0 + u;
                     const size_t tt = row0 + t;
-                    double Uv = 0.;
-#pragma unroll 8
-                    for (int x = 0; x < VQ; ++x) Uv += sm.rpart[grp][u][x][i];
+                    const double Uv = quad_sum(&sm.rpart[grp][u][0][i]);
                     const double kv = c_k[u];
                     const double rt = c_r[u];
                     const double kap = (float)(kv / rt);  // the staged k/r of the state update
