@@ -42,7 +42,7 @@ bool bwd_supported(int dk, int dv);
 // Workspace floats per (b,h): the precision after every token, q dq per
 // token (per key dim; summed over key dims when isotropic) and the diagonal
 // qn partial, rounded up to 256 bytes.
-size_t bwd_ws_stride(int T, int dk, int cov);
+size_t bwd_ws_stride(int B, int H, int T, int dk, int cov);
 hipError_t launch_bwd(const BwdArgs& a, int dtype, int cov, hipStream_t s);
 
 }  // namespace kla

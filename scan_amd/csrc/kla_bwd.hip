@@ -447,19 +447,71 @@ __global__ __launch_bounds__(kBwdThreads) void kla_bwd_kernel(BwdArgs p) {
 // per-token sum of dr over key dims is a wave reduction (the two waves of
 // dk = 128 combine after the block's closing barrier).  The arithmetic and
 // its order are those of kla_bwd_kernel.
-template <typename TIn, int D>
+// The key dims of a (b,h) may be split over NRG workgroups (RD rows each, all
+// D value columns): the rows of the state, their precision chains and their
+// gradients are independent, and only dv and dr sum over key dims; those
+// workgroups leave partial sums in the workspace for kla_bwd_combine.  With
+// few (b,h) this fills the GPU and divides the per-token state work.
+template <int D, int NRG>
+struct BwdRL {
+    static constexpr int RD = D / NRG;                                    // rows per workgroup
+    static constexpr int NTH = NRG == 1 ? BwdLayout<D>::NTH : kBwdThreads;
+    static constexpr int NH = NRG == 1 ? BwdLayout<D>::NH : 1;            // (b,h) per workgroup
+    static constexpr int VQ = D / 4;                                      // value quads per row
+    static constexpr int RG = NTH / VQ;                                   // row groups
+    static constexpr int RPT = RD / RG;                                   // rows per thread
+    static constexpr int TB = NRG == 1 ? BwdLayout<D>::TB : 2 * NRG;      // tokens per block
+    static_assert(RPT % 4 == 0 && TB * VQ <= NTH && NTH * NH == kBwdThreads && RD <= NTH, "layout");
+};
+
+template <class Ly, int D>
+struct BwdSmR {
+    static constexpr int NH = Ly::NH, NTH = Ly::NTH, VQ = Ly::VQ, TB = Ly::TB, RD = Ly::RD;
+    alignas(16) float g[NH][TB][RD];
+    alignas(16) float kap[NH][TB][RD];
+    alignas(16) float cq[NH][TB][RD];
+    alignas(16) float v[NH][TB][D];
+    alignas(16) float dO[NH][TB][D];
+    alignas(16) double rpart[NH][TB][VQ][RD + 2];
+    alignas(16) f32x4 cpart[NH][TB][NTH];
+};
+
+// Rows of key dims per backward workgroup: all (1), or 1/2, 1/4 of dk = 128
+// when there are fewer than 256 (b,h).  KLA_BWD_NRG=n overrides it.
+int bwd_nrg_of(long long nbh, int dk, int cov) {
+    const char* e = getenv("KLA_BWD_NRG");
+    const int n = e && *e ? atoi(e) : 0;
+    if (cov || dk != 128) return 1;
+    if (n == 1 || n == 2 || n == 4) return n;
+    return nbh >= 256 ? 1 : nbh >= 128 ? 2 : 4;
+}
+
+template <typename TIn, int D, int NRG>
 __global__ __launch_bounds__(kBwdThreads) void kla_bwd_diag_kernel(BwdArgs p) {
-    typedef BwdLayout<D> Ly;
+    typedef BwdRL<D, NRG> Ly;
     typedef typename Quad<TIn>::V QV;
     constexpr int TB = Ly::TB, NTH = Ly::NTH, NH = Ly::NH, VQ = Ly::VQ, RG = Ly::RG, RPT = Ly::RPT;
-    constexpr int W = D < 64 ? D : 64;  // key-dim lanes per wave
-    __shared__ BwdSm<D> sm;
-    __shared__ double drw[NH][TB][2];   // per-wave sums of dr (dk = 128)
+    constexpr int RD = Ly::RD;
+    constexpr int W = RD < 64 ? RD : 64;  // key-dim lanes per wave
+    __shared__ BwdSmR<Ly, D> sm;
+    __shared__ double drw[NH][TB][2];     // per-wave sums of dr (RD = 128)
     (void)RG;
 
     const int tid = threadIdx.x;
     const int grp = NH == 1 ? 0 : tid / NTH, lt = NH == 1 ? tid : tid % NTH;
-    const int nbh = p.B * p.H, bh_ = NH == 1 ? (int)blockIdx.x : (int)blockIdx.x * NH + grp;
+    const int nbh = p.B * p.H;
+    int bh_, rgp = 0;
+    if constexpr (NRG == 1) {
+        bh_ = NH == 1 ? (int)blockIdx.x : (int)blockIdx.x * NH + grp;
+    } else if (nbh % 8 == 0) {
+        // the row groups of a (b,h) on one XCD, where they share its v, dO rows
+        const int x = blockIdx.x % 8, kx = blockIdx.x / 8;
+        bh_ = (kx / NRG) * 8 + x;
+        rgp = kx % NRG;
+    } else {
+        bh_ = blockIdx.x / NRG;
+        rgp = blockIdx.x % NRG;
+    }
     const bool valid = NH == 1 || bh_ < nbh;
     const int bh = valid ? bh_ : nbh - 1;  // a spare group stays in bounds and stores nothing
     const int h = bh % p.H;
@@ -470,12 +522,17 @@ __global__ __launch_bounds__(kBwdThreads) void kla_bwd_diag_kernel(BwdArgs p) {
     const TIn* k = (const TIn*)p.k;
     const TIn* v = (const TIn*)p.v;
     const TIn* dOg = (const TIn*)p.dO;
-    const bool kd = lt < D;            // key-dim lane
+    const bool kd = lt < RD;           // key-dim lane
     const bool sl = lt < TB * VQ;      // staging lane: token lt / VQ, value quad jq
-    const int i = kd ? lt : D - 1;
+    const int il = kd ? lt : RD - 1;   // key dim in the workgroup's rows
+    const int r0 = rgp * RD;
+    const int i = r0 + il;             // key dim of the (b,h)
     double* wl = (double*)(p.ws + (size_t)bh * p.ws_stride);
     double* wqdq = wl + (size_t)T * D;
     float* wdqn = (float*)(wqdq + (size_t)T * D);
+    // row-group partials of dv [NRG][T][D] and dr [NRG][T]
+    float* wdv = wdqn + D;
+    float* wdr = wdv + (size_t)NRG * T * D;
 
     const float qn_i = p.qn[(size_t)h * D + i];
     const double l_start = p.l0 ? p.l0[(size_t)bh * D + i] : 1.f;
@@ -507,7 +564,7 @@ __global__ __launch_bounds__(kBwdThreads) void kla_bwd_diag_kernel(BwdArgs p) {
     auto quad_sum = [&](const double* col) {
         double s4[4] = {0., 0., 0., 0.};
 #pragma unroll
-        for (int x = 0; x < VQ; ++x) s4[x % 4] += col[(size_t)x * (D + 2)];
+        for (int x = 0; x < VQ; ++x) s4[x % 4] += col[(size_t)x * (RD + 2)];
         return (s4[0] + s4[1]) + (s4[2] + s4[3]);
     };
     auto stage = [&](const Raw& x, int nb) {
@@ -521,7 +578,7 @@ __global__ __launch_bounds__(kBwdThreads) void kla_bwd_diag_kernel(BwdArgs p) {
     f64x4 e[RPT];
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {
-        const size_t off = ((size_t)bh * D + rg * RPT + m) * D + 4 * jq;
+        const size_t off = ((size_t)bh * D + r0 + rg * RPT + m) * D + 4 * jq;
         e[m] = p.eta0 ? to_f64(*(const f32x4*)(p.eta0 + off)) : f64x4{0., 0., 0., 0.};
     }
     double l = l_start;  // the precision recursion runs in fp64
@@ -539,8 +596,8 @@ __global__ __launch_bounds__(kBwdThreads) void kla_bwd_diag_kernel(BwdArgs p) {
                 lb[u] = l;
                 qb[u] = x.q[u];
                 if (kd) {
-                    sm.g[grp][u][i] = (float)g;
-                    sm.kap[grp][u][i] = (float)(kv / rt);
+                    sm.g[grp][u][il] = (float)g;
+                    sm.kap[grp][u][il] = (float)(kv / rt);
                     if (valid) wl[(size_t)(t0 + u) * D + i] = l;
                 }
             }
@@ -587,7 +644,7 @@ __global__ __launch_bounds__(kBwdThreads) void kla_bwd_diag_kernel(BwdArgs p) {
 #pragma unroll
             for (int u = 0; u < TB; ++u) {
                 if (u < nb) {
-                    const double s = quad_sum(&sm.rpart[grp][u][0][i]);
+                    const double s = quad_sum(&sm.rpart[grp][u][0][il]);
                     const size_t t = row0 + t0 + u;
                     const double dq = s / lb[u];
                     if (valid) {
@@ -611,7 +668,7 @@ __global__ __launch_bounds__(kBwdThreads) void kla_bwd_diag_kernel(BwdArgs p) {
             double sp[4];
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
-                const size_t off = ((size_t)bh * D + rg * RPT + m4 + x) * D + 4 * jq;
+                const size_t off = ((size_t)bh * D + r0 + rg * RPT + m4 + x) * D + 4 * jq;
                 const f64x4 dt = p.detaT ? to_f64(*(const f32x4*)(p.detaT + off)) : f64x4{0., 0., 0., 0.};
                 const f64x4 pr = e[m4 + x] * dt;
                 sp[x] = (pr[0] + pr[1]) + (pr[2] + pr[3]);
@@ -621,10 +678,7 @@ __global__ __launch_bounds__(kBwdThreads) void kla_bwd_diag_kernel(BwdArgs p) {
             *(f64x2*)&sm.rpart[grp][0][jq][rg * RPT + m4 + 2] = f64x2{sp[2], sp[3]};
         }
         __syncthreads();
-        if (kd) {
-#pragma unroll 8
-            for (int x = 0; x < VQ; ++x) Bsum += sm.rpart[grp][0][x][i];
-        }
+        if (kd) Bsum = quad_sum(&sm.rpart[grp][0][0][il]);
         __syncthreads();
     }
 
@@ -668,9 +722,9 @@ __global__ __launch_bounds__(kBwdThreads) void kla_bwd_diag_kernel(BwdArgs p) {
                 double gn = 1., rd;
                 if (t + 1 < T) gn = gate_of(y.an[u], qn_i, lt_, &rd);
                 if (kd) {
-                    sm.g[grp][u][i] = (float)gn;
-                    sm.kap[grp][u][i] = (float)((double)y.x.k[u] / (double)y.x.r[u]);
-                    sm.cq[grp][u][i] = (float)((double)y.x.q[u] / lt_);
+                    sm.g[grp][u][il] = (float)gn;
+                    sm.kap[grp][u][il] = (float)((double)y.x.k[u] / (double)y.x.r[u]);
+                    sm.cq[grp][u][il] = (float)((double)y.x.q[u] / lt_);
                 }
                 c_lt[u] = lt_;
                 c_lprev[u] = u == 0 ? y.lprev0 : y.lt[u - 1];
@@ -691,7 +745,7 @@ __global__ __launch_bounds__(kBwdThreads) void kla_bwd_diag_kernel(BwdArgs p) {
     lds_barrier();
     // dr of the previous block's tokens (dk = 128: the two waves' sums)
     auto store_dr = [&](int t0, int nb) {
-        if constexpr (D > 64) {
+        if constexpr (RD > 64) {
             if (tid < nb && valid) p.gr[row0 + t0 + tid] = (float)(drw[0][tid][0] + drw[0][tid][1]);
         }
     };
@@ -734,17 +788,22 @@ __global__ __launch_bounds__(kBwdThreads) void kla_bwd_diag_kernel(BwdArgs p) {
             f32x4 s = sm.cpart[grp][u][jq];
 #pragma unroll
             for (int r2 = 1; r2 < Ly::RG; ++r2) s += sm.cpart[grp][u][r2 * VQ + jq];
-            if (valid) *(QV*)((TIn*)p.gv + (row0 + t0 + u) * D + 4 * jq) = Quad<TIn>::make(s);
+            if (valid) {
+                if constexpr (NRG == 1)
+                    *(QV*)((TIn*)p.gv + (row0 + t0 + u) * D + 4 * jq) = Quad<TIn>::make(s);
+                else
+                    *(f32x4*)(wdv + ((size_t)rgp * T + t0 + u) * D + 4 * jq) = s;
+            }
         }
         // ---- the precision adjoint over the block (key-dim lanes compute,
         // the dr sums run over every lane of a key-dim wave), last first
-        if (lt < ((D + 63) / 64) * 64) {
+        if (lt < ((RD + 63) / 64) * 64) {
 #pragma unroll
             for (int u = TB - 1; u >= 0; --u) {
                 if (u < nb) {
                     const int t = t0 + u;
                     const size_t tt = row0 + t;
-                    const double Uv = quad_sum(&sm.rpart[grp][u][0][i]);
+                    const double Uv = quad_sum(&sm.rpart[grp][u][0][il]);
                     const double kv = c_k[u];
                     const double rt = c_r[u];
                     const double kap = (float)(kv / rt);  // the staged k/r of the state update
@@ -762,10 +821,12 @@ __global__ __launch_bounds__(kBwdThreads) void kla_bwd_diag_kernel(BwdArgs p) {
                     double dr = kd ? -(kap * Uv + lbar * kv * kv / rt) / rt : 0.;
 #pragma unroll
                     for (int m = 1; m < W; m <<= 1) dr += __shfl_xor(dr, m, 64);
-                    if constexpr (D > 64) {
+                    if constexpr (RD > 64) {
                         if ((lt & 63) == 0) drw[0][u][lt >> 6] = dr;
-                    } else {
+                    } else if constexpr (NRG == 1) {
                         if (lt == 0 && valid) p.gr[tt] = (float)dr;
+                    } else {
+                        if (lt == 0 && valid) wdr[(size_t)rgp * T + t] = (float)dr;
                     }
                     const double da = -lbar * 2. * a * lprev * rd2 + dlg * (qn * lprev - a * a) * rd / a;
                     const double dqn = -lbar * lprev * lprev * rd2 - dlg * lprev * rd;
@@ -784,7 +845,7 @@ __global__ __launch_bounds__(kBwdThreads) void kla_bwd_diag_kernel(BwdArgs p) {
     // ---- initial-state gradients: deta0 = g_0 ebar_0, dl0 = lbar_{-1}
     if (T > 0 && kd) {
         double rd;
-        sm.g[grp][0][i] = (float)gate_of(p.a[row0 * D + i], qn_i, l_start, &rd);
+        sm.g[grp][0][il] = (float)gate_of(p.a[row0 * D + i], qn_i, l_start, &rd);
     }
     __syncthreads();
     if (!valid) return;
@@ -795,7 +856,7 @@ __global__ __launch_bounds__(kBwdThreads) void kla_bwd_diag_kernel(BwdArgs p) {
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
                 const f64x4 r4 = (double)gv[x] * e[m4 + x];
-                *(f32x4*)(p.geta0 + ((size_t)bh * D + rg * RPT + m4 + x) * D + 4 * jq) =
+                *(f32x4*)(p.geta0 + ((size_t)bh * D + r0 + rg * RPT + m4 + x) * D + 4 * jq) =
                     f32x4{(float)r4[0], (float)r4[1], (float)r4[2], (float)r4[3]};
             }
         }
@@ -803,6 +864,32 @@ __global__ __launch_bounds__(kBwdThreads) void kla_bwd_diag_kernel(BwdArgs p) {
     if (kd) {
         if (p.gl0) p.gl0[(size_t)bh * D + i] = (float)lbar;
         wdqn[i] = (float)dqn_acc;
+    }
+}
+
+// dv and dr of a row-split backward: the sums of the row groups' partials
+// (in order of the group).  One thread per (b,h, token, value quad).
+template <typename TIn, int NRG>
+__global__ void kla_bwd_combine(BwdArgs p) {
+    const int D = p.dv, VQ = D / 4;
+    const size_t n = (size_t)p.B * p.H * p.T * VQ;
+    const size_t x = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (x >= n) return;
+    const int jq = (int)(x % VQ);
+    const size_t bt = x / VQ;
+    const int t = (int)(bt % p.T);
+    const int bh = (int)(bt / p.T);
+    const float* wdv = p.ws + (size_t)bh * p.ws_stride + (size_t)p.T * p.dk * 4 + p.dk;
+    const float* wdr = wdv + (size_t)NRG * p.T * D;
+    f32x4 s = *(const f32x4*)(wdv + (size_t)t * D + 4 * jq);
+#pragma unroll
+    for (int g = 1; g < NRG; ++g) s += *(const f32x4*)(wdv + ((size_t)g * p.T + t) * D + 4 * jq);
+    *(typename Quad<TIn>::V*)((TIn*)p.gv + bt * D + 4 * jq) = Quad<TIn>::make(s);
+    if (jq == 0) {
+        float r = wdr[t];
+#pragma unroll
+        for (int g = 1; g < NRG; ++g) r += wdr[(size_t)g * p.T + t];
+        p.gr[bt] = r;
     }
 }
 
@@ -827,10 +914,29 @@ bool bwd_plain() {
 
 template <typename TIn, int D, bool ISO>
 void launch_d(const BwdArgs& a, dim3 grid, dim3 block, hipStream_t s) {
-    if (!ISO && !bwd_plain())
-        hipLaunchKernelGGL((kla_bwd_diag_kernel<TIn, D>), grid, block, 0, s, a);
-    else
+    if (ISO || bwd_plain()) {
         hipLaunchKernelGGL((kla_bwd_kernel<TIn, D, ISO>), grid, block, 0, s, a);
+        return;
+    }
+    const int nbh = a.B * a.H;
+    if constexpr (D == 128) {
+        const int nrg = bwd_nrg_of(nbh, D, 0);
+        if (nrg > 1) {
+            const size_t n = (size_t)nbh * a.T * (D / 4);
+            if (nrg == 2)
+                hipLaunchKernelGGL((kla_bwd_diag_kernel<TIn, D, 2>), dim3(nbh * 2), block, 0, s, a);
+            else
+                hipLaunchKernelGGL((kla_bwd_diag_kernel<TIn, D, 4>), dim3(nbh * 4), block, 0, s, a);
+            if (n > 0) {
+                if (nrg == 2)
+                    hipLaunchKernelGGL((kla_bwd_combine<TIn, 2>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+                else
+                    hipLaunchKernelGGL((kla_bwd_combine<TIn, 4>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+            }
+            return;
+        }
+    }
+    hipLaunchKernelGGL((kla_bwd_diag_kernel<TIn, D, 1>), grid, block, 0, s, a);
 }
 
 template <typename TIn, bool ISO>
@@ -856,10 +962,13 @@ hipError_t dispatch(const BwdArgs& a, hipStream_t s) {
 
 bool bwd_supported(int dk, int dv) { return dk == dv && (dk == 16 || dk == 32 || dk == 64 || dk == 128); }
 
-size_t bwd_ws_stride(int T, int dk, int cov) {
+size_t bwd_ws_stride(int B, int H, int T, int dk, int cov) {
     const size_t nl = cov ? 1 : (size_t)dk;
-    // l_t and q dq (fp64), the diagonal qn partial (fp32)
-    const size_t n = (size_t)T * nl * 4 + (cov ? 0 : (size_t)dk);
+    // l_t and q dq (fp64), the diagonal qn partial (fp32), and with a row
+    // split the row groups' partials of dv [NRG][T][dv] and dr [NRG][T]
+    size_t n = (size_t)T * nl * 4 + (cov ? 0 : (size_t)dk);
+    const int nrg = bwd_plain() ? 1 : bwd_nrg_of((long long)B * H, dk, cov);
+    if (nrg > 1) n += (size_t)nrg * T * dk + (size_t)nrg * T;
     return (n + 63) / 64 * 64;  // floats; 256-byte aligned per (b,h)
 }
 

@@ -136,3 +136,34 @@ def test_bwd_deterministic():
     b = run_bwd(inp, up, "diag")
     for n in GRADS:
         assert np.array_equal(a[n], b[n]), n
+
+
+@pytest.mark.parametrize("nrg", ["1", "2", "4"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_bwd_row_groups(monkeypatch, nrg, dtype):
+    """dk = 128 with its key dims on 1, 2 or 4 workgroups per (b,h) (the
+    row-group partials of dv and dr summed by the combine pass), ragged token
+    blocks, a state and final-state gradients; and the row split equals the
+    whole-row kernel to the fp32 bar."""
+    _print_case("bwd row groups", nrg, dtype)
+    monkeypatch.setenv("KLA_BWD_NRG", nrg)
+    inp = gen.make_inputs("small_diag", seed=350, B=2, H=3, T=77, dk=128, dv=128, dtype=dtype)
+    w = inp["workload"]
+    up = gen.make_upstream(w, seed=351)
+    st = gen.make_state(w, seed=352)
+    hip = run_bwd(inp, up, "diag", st)
+    check(hip, run_ref(inp, up, "diag", st), "diag", dtype, f"bwd row groups {nrg} {dtype}")
+    monkeypatch.setenv("KLA_BWD_NRG", "1")
+    whole = run_bwd(inp, up, "diag", st)
+    errs = bwd_errors(hip, whole, "diag")
+    assert all(v <= 1e-5 for v in errs.values()), errs
+
+
+def test_bwd_full_lm_shape_every_sequence():
+    """The LM-layer shape (B8 H16 T2048 d128 bf16, row-split by default),
+    every gradient of every (b,h) against the oracle."""
+    _print_case("bwd full lm shape")
+    inp = gen.make_inputs("lm_diag", seed=0)
+    w = inp["workload"]
+    up = gen.make_upstream(w, seed=1)
+    check(run_bwd(inp, up, "diag"), run_ref(inp, up, "diag"), "diag", "bf16", "bwd full lm shape")
