@@ -447,6 +447,30 @@ __global__ __launch_bounds__(kBwdThreads) void kla_bwd_kernel(BwdArgs p) {
 // per-token sum of dr over key dims is a wave reduction (the two waves of
 // dk = 128 combine after the block's closing barrier).  The arithmetic and
 // its order are those of kla_bwd_kernel.
+// Reciprocal and quotient in fp64 for positive finite operands: the hardware
+// reciprocal estimate refined by two Newton-Raphson steps, r <- r + r (1 - x r),
+// and the quotient a r corrected once by its residual a - b q.  (The compiler's
+// IEEE division sequence is several times longer; the backward's serial
+// adjoint divides about a dozen times per token.)
+__device__ __forceinline__ double rcp64(double x) {
+    double r = __builtin_amdgcn_rcp(x);
+    double e = __builtin_fma(-x, r, 1.0);
+    r = __builtin_fma(r, e, r);
+    e = __builtin_fma(-x, r, 1.0);
+    return __builtin_fma(r, e, r);
+}
+__device__ __forceinline__ double div64(double a, double b) {
+    const double r = rcp64(b);
+    const double q = a * r;
+    return __builtin_fma(__builtin_fma(-b, q, a), r, q);
+}
+// gate of one token from the precision before it (as gate_of)
+__device__ __forceinline__ double gate_r(double a, double qn, double l, double* rd_out) {
+    const double rd = rcp64(__builtin_fma(qn, l, a * a));
+    *rd_out = rd;
+    return a * rd;
+}
+
 // The key dims of a (b,h) may be split over NRG workgroups (RD rows each, all
 // D value columns): the rows of the state, their precision chains and their
 // gradients are independent, and only dv and dr sum over key dims; those
@@ -591,13 +615,13 @@ __global__ __launch_bounds__(kBwdThreads) void kla_bwd_diag_kernel(BwdArgs p) {
             if (u < nb) {
                 const double kv = x.k[u], rt = x.r[u];
                 double rd;
-                const double g = gate_of(x.a[u], qn_i, l, &rd);
-                l = __builtin_fma(l, rd, kv * kv / rt);
+                const double g = gate_r(x.a[u], qn_i, l, &rd);
+                l = __builtin_fma(l, rd, kv * kv * rcp64(rt));
                 lb[u] = l;
                 qb[u] = x.q[u];
                 if (kd) {
                     sm.g[grp][u][il] = (float)g;
-                    sm.kap[grp][u][il] = (float)(kv / rt);
+                    sm.kap[grp][u][il] = (float)div64(kv, rt);
                     if (valid) wl[(size_t)(t0 + u) * D + i] = l;
                 }
             }
@@ -646,12 +670,12 @@ __global__ __launch_bounds__(kBwdThreads) void kla_bwd_diag_kernel(BwdArgs p) {
                 if (u < nb) {
                     const double s = quad_sum(&sm.rpart[grp][u][0][il]);
                     const size_t t = row0 + t0 + u;
-                    const double dq = s / lb[u];
+                    const double dq = div64(s, lb[u]);
                     if (valid) {
                         ((TIn*)p.gq)[t * D + i] = (TIn)(float)dq;
                         // q dq with q / l rounded to fp32 exactly as sweep 2
                         // stages it for the readout adjoint
-                        wqdq[(size_t)(t0 + u) * D + i] = (double)(float)((double)qb[u] / lb[u]) * s;
+                        wqdq[(size_t)(t0 + u) * D + i] = (double)(float)div64(qb[u], lb[u]) * s;
                     }
                 }
             }
@@ -720,11 +744,11 @@ __global__ __launch_bounds__(kBwdThreads) void kla_bwd_diag_kernel(BwdArgs p) {
                 const int t = t0 + u;
                 const double lt_ = y.lt[u];
                 double gn = 1., rd;
-                if (t + 1 < T) gn = gate_of(y.an[u], qn_i, lt_, &rd);
+                if (t + 1 < T) gn = gate_r(y.an[u], qn_i, lt_, &rd);
                 if (kd) {
                     sm.g[grp][u][il] = (float)gn;
-                    sm.kap[grp][u][il] = (float)((double)y.x.k[u] / (double)y.x.r[u]);
-                    sm.cq[grp][u][il] = (float)((double)y.x.q[u] / lt_);
+                    sm.kap[grp][u][il] = (float)div64(y.x.k[u], y.x.r[u]);
+                    sm.cq[grp][u][il] = (float)div64(y.x.q[u], lt_);
                 }
                 c_lt[u] = lt_;
                 c_lprev[u] = u == 0 ? y.lprev0 : y.lt[u - 1];
@@ -806,19 +830,20 @@ __global__ __launch_bounds__(kBwdThreads) void kla_bwd_diag_kernel(BwdArgs p) {
                     const double Uv = quad_sum(&sm.rpart[grp][u][0][il]);
                     const double kv = c_k[u];
                     const double rt = c_r[u];
-                    const double kap = (float)(kv / rt);  // the staged k/r of the state update
+                    const double kap = (float)div64(kv, rt);  // the staged k/r of the state update
+                    const double rr = rcp64(rt);
                     const double lt_ = c_lt[u], lprev = c_lprev[u];
                     const double a = c_a[u], qn = qn_i, qdq = c_qdq[u];
                     const double kU = kap * Uv;
-                    lbar -= qdq / lt_;
+                    lbar -= qdq * rcp64(lt_);
                     cum += qdq - kU;
                     const double dlg = cum;
                     const double den = a * a + qn * lprev;
-                    const double rd = 1. / den, rd2 = rd * rd;
-                    const double dk = Uv / rt + lbar * 2. * kv / rt;
+                    const double rd = rcp64(den), rd2 = rd * rd;
+                    const double dk = (Uv + lbar * 2. * kv) * rr;
                     if (kd && valid) ((TIn*)p.gk)[tt * D + i] = (TIn)(float)dk;
                     // dr: -(kap U + lbar b_i) / r, summed over key dims
-                    double dr = kd ? -(kap * Uv + lbar * kv * kv / rt) / rt : 0.;
+                    double dr = kd ? -(kap * Uv + lbar * kv * kv * rr) * rr : 0.;
 #pragma unroll
                     for (int m = 1; m < W; m <<= 1) dr += __shfl_xor(dr, m, 64);
                     if constexpr (RD > 64) {
@@ -828,7 +853,7 @@ __global__ __launch_bounds__(kBwdThreads) void kla_bwd_diag_kernel(BwdArgs p) {
                     } else {
                         if (lt == 0 && valid) wdr[(size_t)rgp * T + t] = (float)dr;
                     }
-                    const double da = -lbar * 2. * a * lprev * rd2 + dlg * (qn * lprev - a * a) * rd / a;
+                    const double da = -lbar * 2. * a * lprev * rd2 + dlg * (qn * lprev - a * a) * rd * rcp64(a);
                     const double dqn = -lbar * lprev * lprev * rd2 - dlg * lprev * rd;
                     if (kd && valid) p.ga[tt * D + i] = (float)da;
                     dqn_acc += dqn;
@@ -845,7 +870,7 @@ __global__ __launch_bounds__(kBwdThreads) void kla_bwd_diag_kernel(BwdArgs p) {
     // ---- initial-state gradients: deta0 = g_0 ebar_0, dl0 = lbar_{-1}
     if (T > 0 && kd) {
         double rd;
-        sm.g[grp][0][il] = (float)gate_of(p.a[row0 * D + i], qn_i, l_start, &rd);
+        sm.g[grp][0][il] = (float)gate_r(p.a[row0 * D + i], qn_i, l_start, &rd);
     }
     __syncthreads();
     if (!valid) return;
