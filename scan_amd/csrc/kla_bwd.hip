@@ -892,6 +892,412 @@ __global__ __launch_bounds__(kBwdThreads) void kla_bwd_diag_kernel(BwdArgs p) {
     }
 }
 
+// Row-split diagonal backward at dk = dv = 128 with the per-token work of a
+// token block spread over the four waves: wave w takes tokens w, w+4, ... of
+// the block for every key dim of the workgroup (one lane per key dim).  Only
+// the recursions stay serial: the precision l (sweep 1, wave 0) and the
+// adjoints lbar, cum (sweep 2, wave 0), whose per-token coefficients the
+// four waves form in parallel:
+//   lbar_t = lbar_t' - qdq_t / l_t,   cum_t = cum_{t+1} + qdq_t - kap_t U_t,
+//   lbar_{t-1}' = lbar_t a_t^2 rd_t^2 - cum_t qn rd_t        (rd_t = 1 / D_t)
+// so each token's dk, da, dr, dqn follow from (lbar_t, cum_t) in parallel
+// again.  Same arithmetic as kla_bwd_diag_kernel, in another order.
+template <typename TIn, int NRG>
+__global__ __launch_bounds__(kBwdThreads) void kla_bwd_rows_kernel(BwdArgs p) {
+    constexpr int D = 128;
+    typedef BwdRL<D, NRG> Ly;
+    typedef typename Quad<TIn>::V QV;
+    constexpr int TB = Ly::TB, NTH = Ly::NTH, VQ = Ly::VQ, RPT = Ly::RPT, RD = Ly::RD;
+    constexpr int NWV = kBwdThreads / 64, TPW = TB / NWV;  // tokens per wave and block
+    static_assert(Ly::NH == 1 && NTH == kBwdThreads && RD <= 64 && TB % NWV == 0, "row-split layout");
+    __shared__ BwdSmR<Ly, D> sm;
+    __shared__ double s_lt[2][TB][RD];      // sweep 1: l_t of the block, by block parity
+    __shared__ double s_co[TB][4][RD];      // sweep 2: qdq/l, qdq - kap U, a^2 rd^2, qn rd
+    __shared__ double s_lc[TB][2][RD];      // sweep 2: lbar_t, cum_t
+    __shared__ float s_dqn[NWV][RD];
+
+    const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+    const int nbh = p.B * p.H;
+    int bh, rgp;
+    if (nbh % 8 == 0) {
+        const int x = blockIdx.x % 8, kx = blockIdx.x / 8;
+        bh = (kx / NRG) * 8 + x;
+        rgp = kx % NRG;
+    } else {
+        bh = blockIdx.x / NRG;
+        rgp = blockIdx.x % NRG;
+    }
+    const int h = bh % p.H;
+    const int jq = tid % VQ, rg = tid / VQ;
+    const int T = p.T;
+    const size_t row0 = (size_t)bh * T;
+    const TIn* q = (const TIn*)p.q;
+    const TIn* k = (const TIn*)p.k;
+    const TIn* v = (const TIn*)p.v;
+    const TIn* dOg = (const TIn*)p.dO;
+    const bool kd = lane < RD;             // key-dim lane (in every wave)
+    const bool sl = tid < TB * VQ;         // staging lane: token tid / VQ, value quad jq
+    const int il = kd ? lane : RD - 1;
+    const int r0 = rgp * RD;
+    const int i = r0 + il;
+    double* wl = (double*)(p.ws + (size_t)bh * p.ws_stride);
+    double* wqdq = wl + (size_t)T * D;
+    float* wdqn = (float*)(wqdq + (size_t)T * D);
+    float* wdv = wdqn + D;
+    float* wdr = wdv + (size_t)NRG * T * D;
+
+    const float qn_i = p.qn[(size_t)h * D + i];
+    const double l_start = p.l0 ? p.l0[(size_t)bh * D + i] : 1.f;
+
+    auto quad_sum = [&](const double* col) {
+        double s4[4] = {0., 0., 0., 0.};
+#pragma unroll
+        for (int x = 0; x < VQ; ++x) s4[x % 4] += col[(size_t)x * (RD + 2)];
+        return (s4[0] + s4[1]) + (s4[2] + s4[3]);
+    };
+    // the v and dO rows of a block (staging lanes)
+    struct Rows {
+        QV v, dO;
+    };
+    auto load_rows = [&](int t0, int nb, Rows& x) {
+        if (sl && tid / VQ < nb) {
+            const size_t t = row0 + t0 + tid / VQ;
+            x.v = *(const QV*)(v + t * D + 4 * jq);
+            x.dO = *(const QV*)(dOg + t * D + 4 * jq);
+        }
+    };
+    auto stage_rows = [&](const Rows& x, int nb) {
+        if (sl && tid / VQ < nb) {
+            *(f32x4*)&sm.v[0][tid / VQ][4 * jq] = Quad<TIn>::to_f32(x.v);
+            *(f32x4*)&sm.dO[0][tid / VQ][4 * jq] = Quad<TIn>::to_f32(x.dO);
+        }
+    };
+
+    // ---------------------------------------------------------------- sweep 1
+    f64x4 e[RPT];
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+        const size_t off = ((size_t)bh * D + r0 + rg * RPT + m) * D + 4 * jq;
+        e[m] = p.eta0 ? to_f64(*(const f32x4*)(p.eta0 + off)) : f64x4{0., 0., 0., 0.};
+    }
+    double l = l_start;  // wave 0: the precision recursion, fp64
+    // raw inputs of a block: k, r, a of every token (wave 0, for the
+    // recursion) and q of the wave's own tokens
+    struct Raw1 {
+        float k[TB], r[TB], a[TB], q[TPW];
+        Rows rows;
+    };
+    auto load1 = [&](int t0, int nb, Raw1& x) {
+        if (kd) {
+            if (wv == 0) {
+#pragma unroll
+                for (int u = 0; u < TB; ++u) {
+                    const size_t t = row0 + t0 + (u < nb ? u : 0);
+                    x.k[u] = (float)k[t * D + i];
+                    x.r[u] = p.r[t];
+                    x.a[u] = p.a[t * D + i];
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < TPW; ++m) {
+                const int u = wv + NWV * m;
+                x.q[m] = (float)q[(row0 + t0 + (u < nb ? u : 0)) * D + i];
+            }
+        }
+        load_rows(t0, nb, x.rows);
+    };
+    // wave 0: the block's precisions (advances l), gates and k/r into LDS,
+    // l_t into LDS (by parity) and the workspace
+    auto fwd_coefs = [&](const Raw1& x, int t0, int nb, int par) {
+        if (wv == 0) {
+#pragma unroll
+            for (int u = 0; u < TB; ++u) {
+                if (u < nb) {
+                    const double kv = x.k[u], rt = x.r[u];
+                    double rd;
+                    const double g = gate_r(x.a[u], qn_i, l, &rd);
+                    l = __builtin_fma(l, rd, kv * kv * rcp64(rt));
+                    if (kd) {
+                        sm.g[0][u][il] = (float)g;
+                        sm.kap[0][u][il] = (float)div64(kv, rt);
+                        s_lt[par][u][il] = l;
+                        wl[(size_t)(t0 + u) * D + i] = l;
+                    }
+                }
+            }
+        }
+        stage_rows(x.rows, nb);
+    };
+    Raw1 n1{};
+    float qb[TPW] = {};  // q of the wave's tokens of the current block
+    if (T > 0) {
+        const int nb = T < TB ? T : TB;
+        load1(0, nb, n1);
+        fwd_coefs(n1, 0, nb, 0);
+#pragma unroll
+        for (int m = 0; m < TPW; ++m) qb[m] = n1.q[m];
+    }
+    lds_barrier();
+    for (int t0 = 0, bi = 0; t0 < T; t0 += TB, ++bi) {
+        const int nb = T - t0 < TB ? T - t0 : TB;
+        const bool more = t0 + TB < T;
+        const int nb2 = more ? (T - t0 - TB < TB ? T - t0 - TB : TB) : 0;
+        if (more) load1(t0 + TB, nb2, n1);
+        // ---- the block on the thread's rows; per-row S partials
+#pragma unroll
+        for (int u = 0; u < TB; ++u) {
+            if (u < nb) {
+                const f64x4 vv = to_f64(*(const f32x4*)&sm.v[0][u][4 * jq]);
+                const f64x4 dd = to_f64(*(const f32x4*)&sm.dO[0][u][4 * jq]);
+#pragma unroll
+                for (int m4 = 0; m4 < RPT; m4 += 4) {
+                    const f32x4 gv = *(const f32x4*)&sm.g[0][u][rg * RPT + m4];
+                    const f32x4 kv = *(const f32x4*)&sm.kap[0][u][rg * RPT + m4];
+                    double sp[4];
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        e[m4 + x] = (double)gv[x] * e[m4 + x] + (double)kv[x] * vv;
+                        const f64x4 pr = e[m4 + x] * dd;
+                        sp[x] = (pr[0] + pr[1]) + (pr[2] + pr[3]);
+                    }
+                    *(f64x2*)&sm.rpart[0][u][jq][rg * RPT + m4] = f64x2{sp[0], sp[1]};
+                    *(f64x2*)&sm.rpart[0][u][jq][rg * RPT + m4 + 2] = f64x2{sp[2], sp[3]};
+                }
+            }
+        }
+        lds_barrier();
+        // ---- dq of the wave's tokens
+        if (kd) {
+#pragma unroll
+            for (int m = 0; m < TPW; ++m) {
+                const int u = wv + NWV * m;
+                if (u < nb) {
+                    const double s = quad_sum(&sm.rpart[0][u][0][il]);
+                    const double lb = s_lt[bi & 1][u][il];
+                    const size_t t = row0 + t0 + u;
+                    ((TIn*)p.gq)[t * D + i] = (TIn)(float)div64(s, lb);
+                    // q dq with q / l rounded to fp32 exactly as sweep 2 stages it
+                    wqdq[(size_t)(t0 + u) * D + i] = (double)(float)div64(qb[m], lb) * s;
+                }
+            }
+        }
+        if (more) {
+            fwd_coefs(n1, t0 + TB, nb2, (bi + 1) & 1);
+#pragma unroll
+            for (int m = 0; m < TPW; ++m) qb[m] = n1.q[m];
+        }
+        lds_barrier();
+    }
+    // boundary term of the gate adjoint: B[i] = sum_j detaT[i,j] eta_T[i,j]
+    double Bsum = 0.;
+    {
+#pragma unroll
+        for (int m4 = 0; m4 < RPT; m4 += 4) {
+            double sp[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const size_t off = ((size_t)bh * D + r0 + rg * RPT + m4 + x) * D + 4 * jq;
+                const f64x4 dt = p.detaT ? to_f64(*(const f32x4*)(p.detaT + off)) : f64x4{0., 0., 0., 0.};
+                const f64x4 pr = e[m4 + x] * dt;
+                sp[x] = (pr[0] + pr[1]) + (pr[2] + pr[3]);
+                e[m4 + x] = dt;
+            }
+            *(f64x2*)&sm.rpart[0][0][jq][rg * RPT + m4] = f64x2{sp[0], sp[1]};
+            *(f64x2*)&sm.rpart[0][0][jq][rg * RPT + m4 + 2] = f64x2{sp[2], sp[3]};
+        }
+        __syncthreads();  // also orders sweep 1's workspace stores before sweep 2's reads
+        if (kd && wv == 0) Bsum = quad_sum(&sm.rpart[0][0][0][il]);
+        __syncthreads();
+    }
+
+    // ---------------------------------------------------------------- sweep 2
+    double lbar = p.dlT ? p.dlT[(size_t)bh * D + i] : 0.f;  // wave 0
+    double cum = Bsum;                                        // wave 0
+    double dqn_acc = 0.;                                      // per wave
+    // inputs of the wave's tokens of a block
+    struct Raw2 {
+        float k[TPW], r[TPW], a[TPW], q[TPW], an[TPW];
+        double lt[TPW], lp[TPW], qdq[TPW];
+        Rows rows;
+    };
+    auto load2 = [&](int t0, int nb, Raw2& y) {
+        if (kd) {
+#pragma unroll
+            for (int m = 0; m < TPW; ++m) {
+                const int u = wv + NWV * m;
+                const int t = t0 + (u < nb ? u : 0);
+                const size_t tt = row0 + t;
+                y.k[m] = (float)k[tt * D + i];
+                y.r[m] = p.r[tt];
+                y.a[m] = p.a[tt * D + i];
+                y.q[m] = (float)q[tt * D + i];
+                y.an[m] = t + 1 < T ? p.a[(tt + 1) * D + i] : 0.f;
+                y.lt[m] = wl[(size_t)t * D + i];
+                y.lp[m] = t == 0 ? l_start : wl[(size_t)(t - 1) * D + i];
+                y.qdq[m] = wqdq[(size_t)t * D + i];
+            }
+        }
+        load_rows(t0, nb, y.rows);
+    };
+    // the adjoint's inputs of the wave's tokens of the current block
+    float c_k[TPW], c_r[TPW], c_a[TPW];
+    double c_lt[TPW], c_lp[TPW], c_qdq[TPW];
+    // backward coefficients of the wave's tokens: gate of the token after
+    // (1 past the end), k/r, q/l into LDS; the adjoint inputs into registers
+    auto bwd_coefs = [&](const Raw2& y, int t0, int nb) {
+#pragma unroll
+        for (int m = 0; m < TPW; ++m) {
+            const int u = wv + NWV * m;
+            if (u < nb) {
+                double gn = 1., rd;
+                if (t0 + u + 1 < T) gn = gate_r(y.an[m], qn_i, y.lt[m], &rd);
+                if (kd) {
+                    sm.g[0][u][il] = (float)gn;
+                    sm.kap[0][u][il] = (float)div64(y.k[m], y.r[m]);
+                    sm.cq[0][u][il] = (float)div64(y.q[m], y.lt[m]);
+                }
+                c_k[m] = y.k[m];
+                c_r[m] = y.r[m];
+                c_a[m] = y.a[m];
+                c_lt[m] = y.lt[m];
+                c_lp[m] = y.lp[m];
+                c_qdq[m] = y.qdq[m];
+            }
+        }
+        stage_rows(y.rows, nb);
+    };
+    const int nblk = (T + TB - 1) / TB;
+    Raw2 n2{};
+    if (T > 0) {
+        const int t0 = (nblk - 1) * TB;
+        load2(t0, T - t0, n2);
+        bwd_coefs(n2, t0, T - t0);
+    }
+    lds_barrier();
+    for (int blk = nblk - 1; blk >= 0; --blk) {
+        const int t0 = blk * TB;
+        const int nb = T - t0 < TB ? T - t0 : TB;
+        if (blk > 0) load2(t0 - TB, TB, n2);
+        // ---- ebar over the block's tokens, last first; U and dv partials
+#pragma unroll
+        for (int u = TB - 1; u >= 0; --u) {
+            if (u < nb) {
+                const f64x4 vv = to_f64(*(const f32x4*)&sm.v[0][u][4 * jq]);
+                const f64x4 dd = to_f64(*(const f32x4*)&sm.dO[0][u][4 * jq]);
+                f64x4 cs = {0., 0., 0., 0.};
+#pragma unroll
+                for (int m4 = 0; m4 < RPT; m4 += 4) {
+                    const f32x4 gv = *(const f32x4*)&sm.g[0][u][rg * RPT + m4];
+                    const f32x4 cv = *(const f32x4*)&sm.cq[0][u][rg * RPT + m4];
+                    const f32x4 kv = *(const f32x4*)&sm.kap[0][u][rg * RPT + m4];
+                    double sp[4];
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        e[m4 + x] = (double)gv[x] * e[m4 + x] + (double)cv[x] * dd;
+                        const f64x4 pr = e[m4 + x] * vv;
+                        sp[x] = (pr[0] + pr[1]) + (pr[2] + pr[3]);
+                        cs += (double)kv[x] * e[m4 + x];
+                    }
+                    *(f64x2*)&sm.rpart[0][u][jq][rg * RPT + m4] = f64x2{sp[0], sp[1]};
+                    *(f64x2*)&sm.rpart[0][u][jq][rg * RPT + m4 + 2] = f64x2{sp[2], sp[3]};
+                }
+                sm.cpart[0][u][tid] = f32x4{(float)cs[0], (float)cs[1], (float)cs[2], (float)cs[3]};
+            }
+        }
+        lds_barrier();
+        // ---- dv of the block (staging lanes); the per-token coefficients
+        // of the adjoint recursions (each wave its tokens)
+        if (sl && tid / VQ < nb) {
+            const int u = tid / VQ;
+            f32x4 s = sm.cpart[0][u][jq];
+#pragma unroll
+            for (int r2 = 1; r2 < Ly::RG; ++r2) s += sm.cpart[0][u][r2 * VQ + jq];
+            *(f32x4*)(wdv + ((size_t)rgp * T + t0 + u) * D + 4 * jq) = s;
+        }
+        double Uv[TPW], kap[TPW], rr[TPW], rd[TPW];
+#pragma unroll
+        for (int m = 0; m < TPW; ++m) {
+            const int u = wv + NWV * m;
+            if (u < nb && kd) {
+                Uv[m] = quad_sum(&sm.rpart[0][u][0][il]);
+                kap[m] = (float)div64(c_k[m], c_r[m]);
+                rr[m] = rcp64(c_r[m]);
+                const double a = c_a[m];
+                rd[m] = rcp64(a * a + (double)qn_i * c_lp[m]);
+                s_co[u][0][il] = c_qdq[m] * rcp64(c_lt[m]);
+                s_co[u][1][il] = c_qdq[m] - kap[m] * Uv[m];
+                s_co[u][2][il] = a * a * rd[m] * rd[m];
+                s_co[u][3][il] = (double)qn_i * rd[m];
+            }
+        }
+        lds_barrier();
+        // ---- the serial recursions (wave 0), last token first
+        if (wv == 0 && kd) {
+#pragma unroll
+            for (int u = TB - 1; u >= 0; --u) {
+                if (u < nb) {
+                    lbar -= s_co[u][0][il];
+                    cum += s_co[u][1][il];
+                    s_lc[u][0][il] = lbar;
+                    s_lc[u][1][il] = cum;
+                    lbar = lbar * s_co[u][2][il] - cum * s_co[u][3][il];
+                }
+            }
+        }
+        lds_barrier();
+        // ---- the gradients of the wave's tokens
+#pragma unroll
+        for (int m = 0; m < TPW; ++m) {
+            const int u = wv + NWV * m;
+            if (u < nb) {
+                const size_t tt = row0 + t0 + u;
+                const double lb = kd ? s_lc[u][0][il] : 0., dlg = kd ? s_lc[u][1][il] : 0.;
+                const double kv = c_k[m], a = c_a[m], lprev = c_lp[m], qn = qn_i;
+                const double rd2 = rd[m] * rd[m];
+                if (kd) {
+                    ((TIn*)p.gk)[tt * D + i] = (TIn)(float)((Uv[m] + lb * 2. * kv) * rr[m]);
+                    p.ga[tt * D + i] = (float)(-lb * 2. * a * lprev * rd2 +
+                                               dlg * (qn * lprev - a * a) * rd[m] * rcp64(a));
+                    dqn_acc += -lb * lprev * lprev * rd2 - dlg * lprev * rd[m];
+                }
+                double dr = kd ? -(kap[m] * Uv[m] + lb * kv * kv * rr[m]) * rr[m] : 0.;
+#pragma unroll
+                for (int x = 1; x < (RD < 64 ? RD : 64); x <<= 1) dr += __shfl_xor(dr, x, 64);
+                if (lane == 0) wdr[(size_t)rgp * T + t0 + u] = (float)dr;
+            }
+        }
+        if (blk > 0) bwd_coefs(n2, t0 - TB, TB);
+        lds_barrier();
+    }
+    // ---- initial-state gradients: deta0 = g_0 ebar_0, dl0 = lbar_{-1}; the
+    // waves' dqn partials
+    if (kd) s_dqn[wv][il] = (float)dqn_acc;
+    if (T > 0 && kd && wv == 0) {
+        double rdd;
+        sm.g[0][0][il] = (float)gate_r(p.a[row0 * D + i], qn_i, l_start, &rdd);
+    }
+    __syncthreads();
+    if (p.geta0) {
+#pragma unroll
+        for (int m4 = 0; m4 < RPT; m4 += 4) {
+            const f32x4 gv = T > 0 ? *(const f32x4*)&sm.g[0][0][rg * RPT + m4] : f32x4{1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const f64x4 r4 = (double)gv[x] * e[m4 + x];
+                *(f32x4*)(p.geta0 + ((size_t)bh * D + r0 + rg * RPT + m4 + x) * D + 4 * jq) =
+                    f32x4{(float)r4[0], (float)r4[1], (float)r4[2], (float)r4[3]};
+            }
+        }
+    }
+    if (kd && wv == 0) {
+        if (p.gl0) p.gl0[(size_t)bh * D + i] = (float)lbar;
+        float sq = 0.f;
+#pragma unroll
+        for (int w2 = 0; w2 < NWV; ++w2) sq += s_dqn[w2][il];
+        wdqn[i] = sq;
+    }
+}
+
 // dv and dr of a row-split backward: the sums of the row groups' partials
 // (in order of the group).  One thread per (b,h, token, value quad).
 template <typename TIn, int NRG>
@@ -949,9 +1355,9 @@ void launch_d(const BwdArgs& a, dim3 grid, dim3 block, hipStream_t s) {
         if (nrg > 1) {
             const size_t n = (size_t)nbh * a.T * (D / 4);
             if (nrg == 2)
-                hipLaunchKernelGGL((kla_bwd_diag_kernel<TIn, D, 2>), dim3(nbh * 2), block, 0, s, a);
+                hipLaunchKernelGGL((kla_bwd_rows_kernel<TIn, 2>), dim3(nbh * 2), block, 0, s, a);
             else
-                hipLaunchKernelGGL((kla_bwd_diag_kernel<TIn, D, 4>), dim3(nbh * 4), block, 0, s, a);
+                hipLaunchKernelGGL((kla_bwd_rows_kernel<TIn, 4>), dim3(nbh * 4), block, 0, s, a);
             if (n > 0) {
                 if (nrg == 2)
                     hipLaunchKernelGGL((kla_bwd_combine<TIn, 2>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
