@@ -14,7 +14,7 @@ the host cores over a bounded sample of the same workload.
 
   python bench.py [--steps K] [--warmup W] [--workload long_diag] [--no-cpu]
   (workloads: the names in scan_amd.inputs, iso_decode, iso_prefill16,
-   residual_lm_diag, block_lm_diag, bwd_lm_diag)
+   residual_lm_diag, block_lm_diag, block_long_diag, bwd_lm_diag)
 """
 from __future__ import annotations
 
@@ -523,8 +523,10 @@ def main() -> int:
     # forward with the fused block prologue (klaFwdBlock) at the LM-layer
     # shape, or the KLA forward (klaFwd) on one of the named workloads
     residual = args.workload == gen.RESIDUAL.name
-    blockw = args.workload == gen.BLOCK.name
-    w = gen.RESIDUAL if residual else gen.BLOCK if blockw else gen.WORKLOADS[args.workload]
+    blockw = args.workload in (gen.BLOCK.name, gen.BLOCK_LONG.name)
+    w = (gen.RESIDUAL if residual else
+         {gen.BLOCK.name: gen.BLOCK, gen.BLOCK_LONG.name: gen.BLOCK_LONG}[args.workload] if blockw else
+         gen.WORKLOADS[args.workload])
     print(f"bench: workload {w}", file=sys.stderr, flush=True)
     if blockw:
         host = gen.make_block_inputs(w, seed=0)
@@ -637,7 +639,8 @@ def main() -> int:
     traffic = stored_traffic(w.name, fam)
     counters = stored_counters(w.name, fam)
     kernel_name = ("kla_fwd_residual_kernel" if residual else
-                   "kla_fwd_diag_pipe_kernel (block prologue, value tiles)" if blockw else
+                   ("kla_fwd_diag_pipe_kernel (block prologue, value tiles)" +
+                    (", sequence split" if w.B * w.H < 192 // 2 else "")) if blockw else
                    scan_amd.fwd_kernel_name(w.B, w.H, w.T, w.dk, w.dv, w.cov, w.dtype))
     flops = alg_flops(w)
     mfma_tfs = flops / (kern_ms / 1e3) / 1e12

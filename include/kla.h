@@ -178,18 +178,21 @@ typedef struct klaBlock {
  * Out: o [B,H,T,dv] (dtype), lT, etaT (may be NULL) as for klaFwd.
  * Diagonal covariance only, dk = dv in {64, 128} (128: bf16), the dims of
  * the wave-specialised kernel (KLA_ERR_UNSUPPORTED otherwise); width outside
- * 1..4 or r_eps < 0 is KLA_ERR_SHAPE.  Long sequences are not split across
- * workgroups: one workgroup per (b,h) and 64 value columns.  No workspace; no
- * memory is allocated.  Every non-NULL pointer must be 16-byte aligned except
- * the taps and biases (4-byte).  o must not overlap an input; lT and
- * etaT must not overlap l0, eta0 (KLA_ERR_ALIAS).  T == 0 passes l0/eta0
- * through.
+ * 1..4 or r_eps < 0 is KLA_ERR_SHAPE.  Few, long sequences are split into
+ * segments as for klaFwd: workspace must then hold klaFwdWorkspaceBytes(d)
+ * bytes (KLA_ERR_WORKSPACE otherwise; NULL when that is 0) and must not be
+ * used by another call at the same time.  No memory is allocated.  Every
+ * non-NULL pointer must be 16-byte aligned except the taps and biases
+ * (4-byte).  o must not overlap an input; lT and etaT must not overlap l0,
+ * eta0; the workspace must not overlap any argument (KLA_ERR_ALIAS).
+ * T == 0 passes l0/eta0 through.
  */
 klaStatus klaFwdBlock(const klaDims* d, const klaBlock* blk,
                       const void* xq, const void* xk, const void* xv,
                       const void* za, const float* zqn, const float* zr,
                       const float* l0, const float* eta0,
-                      void* o, float* lT, float* etaT, void* hipStream);
+                      void* o, float* lT, float* etaT,
+                      void* workspace, size_t workspaceBytes, void* hipStream);
 
 /*
  * One decode step for every (b,h) (the same recurrence with T = 1;

@@ -98,7 +98,7 @@ def load():
     lib.klaBwdWorkspaceBytes.restype = sz
     lib.klaBwd.argtypes = [dp] + [vp] * 19 + [vp, sz, vp]
     lib.klaBwd.restype = ctypes.c_int
-    lib.klaFwdBlock.argtypes = [dp, ctypes.POINTER(KlaBlock)] + [vp] * 11 + [vp]
+    lib.klaFwdBlock.argtypes = [dp, ctypes.POINTER(KlaBlock)] + [vp] * 11 + [vp, sz, vp]
     lib.klaFwdBlock.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -127,11 +127,13 @@ def klaFwdNoAlloc(dims, q, k, v, a, qnoise, r, l0, eta0, o, lT, etaT, stream) ->
                                     stream))
 
 
-def klaFwdBlock(dims, blk, xq, xk, xv, za, zqn, zr, l0, eta0, o, lT, etaT, stream) -> int:
+def klaFwdBlock(dims, blk, xq, xk, xv, za, zqn, zr, l0, eta0, o, lT, etaT, workspace, workspaceBytes,
+                stream) -> int:
     """Raw call of the forward with the fused block prologue (blk: KlaBlock or
-    None; pointers as ints or None)."""
+    None; pointers as ints or None; the workspace as for klaFwd)."""
     return int(load().klaFwdBlock(ctypes.byref(dims), ctypes.byref(blk) if blk is not None else None,
-                                  xq, xk, xv, za, zqn, zr, l0, eta0, o, lT, etaT, stream))
+                                  xq, xk, xv, za, zqn, zr, l0, eta0, o, lT, etaT, workspace,
+                                  workspaceBytes, stream))
 
 
 def klaStep(dims, q, k, v, a, qnoise, r, l, eta, o, stream) -> int:
@@ -253,8 +255,10 @@ def fwd_block(xq, xk, xv, za, zqn, zr, wq, wk, wv, bq=None, bk=None, bv=None, sq
             lT = torch.empty(B, H, dk, dtype=torch.float32, device=dev)
         if etaT is None:
             etaT = torch.empty(B, H, dk, dv, dtype=torch.float32, device=dev)
+    ws_bytes = klaFwdWorkspaceBytes(dims)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
     st = klaFwdBlock(dims, blk, _ptr(xq), _ptr(xk), _ptr(xv), _ptr(za), _ptr(zqn), _ptr(zr),
-                     _ptr(l0), _ptr(eta0), _ptr(o), _ptr(lT), _ptr(etaT), _stream())
+                     _ptr(l0), _ptr(eta0), _ptr(o), _ptr(lT), _ptr(etaT), _ptr(ws), ws_bytes, _stream())
     if st != KLA_OK:
         raise KlaError(st, "klaFwdBlock")
     return o, lT, etaT

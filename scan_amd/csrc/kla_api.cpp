@@ -171,6 +171,35 @@ size_t klaFwdWorkspaceBytes(const klaDims* d) {
 
 namespace {
 
+// The wave-specialised diagonal forward, split into sequence segments when
+// pick_nseg says so: precision warm-up (exact segment products and precision
+// carry where it did not settle), segment forwards, state carry, output
+// correction.  workspace holds klaFwdWorkspaceBytes(d) bytes when split.
+hipError_t launch_diag_pipe(kla::FwdArgs& fa, const klaDims* d, void* workspace, hipStream_t st) {
+    int seg_len = 0;
+    const int nseg = pick_nseg(d, &seg_len);
+    if (nseg <= 1) return kla::launch_fwd_diag_pipe(fa, d->dtype, st);
+    const size_t es = d->dtype == KLA_BF16 ? 2 : 4;
+    const kla::SegWorkspace w = kla::seg_workspace(d->B, d->H, d->T, d->dk, d->dv, (int)es, nseg);
+    char* ws = (char*)workspace;
+    float* P = (float*)(ws + w.off_P);
+    fa.nseg = nseg;
+    fa.seg_len = seg_len;
+    fa.seg_l0 = (const float*)(ws + w.off_l0);
+    fa.seg_d = (float*)(ws + w.off_d);
+    fa.seg_lend = (float*)(ws + w.off_lend);
+    fa.seg_m = (float*)(ws + w.off_m);
+    fa.seg_qhat = ws + w.off_qhat;
+    int* ok = (int*)(ws + w.off_ok);
+    hipError_t e = kla::launch_seg_warm(fa, ok, d->dtype, st);
+    if (e == hipSuccess) e = kla::launch_seg_mobius(fa, P, ok, d->dtype, st);
+    if (e == hipSuccess) e = kla::launch_seg_carry_l(fa, P, ok, st);
+    if (e == hipSuccess) e = kla::launch_fwd_diag_pipe(fa, d->dtype, st);
+    if (e == hipSuccess) e = kla::launch_seg_carry_m(fa, st);
+    if (e == hipSuccess) e = kla::launch_seg_correct(fa, d->dtype, st);
+    return e;
+}
+
 // klaFwd, or (scratch) klaFwdNoAlloc: the split workspace is then the
 // library's device scratch, looked up after every host check has passed.
 klaStatus fwd_entry(const klaDims* d, const void* q, const void* k, const void* v, const float* a,
@@ -244,35 +273,7 @@ klaStatus fwd_entry(const klaDims* d, const void* q, const void* k, const void* 
             e = kla::launch_fwd_iso(fa, d->dtype, st);
             break;
         case FK_ISO_PIPE: e = kla::launch_fwd_iso_pipe(fa, d->dtype, st); break;
-        case FK_DIAG_PIPE: {
-            int seg_len = 0;
-            const int nseg = pick_nseg(d, &seg_len);
-            if (nseg <= 1) {
-                e = kla::launch_fwd_diag_pipe(fa, d->dtype, st);
-                break;
-            }
-            // sequence split: precision warm-up (exact segment products and
-            // precision carry where it did not settle), segment forwards,
-            // state carry, output correction
-            const kla::SegWorkspace w = kla::seg_workspace(d->B, d->H, d->T, d->dk, d->dv, (int)es, nseg);
-            char* ws = (char*)workspace;
-            float* P = (float*)(ws + w.off_P);
-            fa.nseg = nseg;
-            fa.seg_len = seg_len;
-            fa.seg_l0 = (const float*)(ws + w.off_l0);
-            fa.seg_d = (float*)(ws + w.off_d);
-            fa.seg_lend = (float*)(ws + w.off_lend);
-            fa.seg_m = (float*)(ws + w.off_m);
-            fa.seg_qhat = ws + w.off_qhat;
-            int* ok = (int*)(ws + w.off_ok);
-            e = kla::launch_seg_warm(fa, ok, d->dtype, st);
-            if (e == hipSuccess) e = kla::launch_seg_mobius(fa, P, ok, d->dtype, st);
-            if (e == hipSuccess) e = kla::launch_seg_carry_l(fa, P, ok, st);
-            if (e == hipSuccess) e = kla::launch_fwd_diag_pipe(fa, d->dtype, st);
-            if (e == hipSuccess) e = kla::launch_seg_carry_m(fa, st);
-            if (e == hipSuccess) e = kla::launch_seg_correct(fa, d->dtype, st);
-            break;
-        }
+        case FK_DIAG_PIPE: e = launch_diag_pipe(fa, d, workspace, st); break;
         default: e = kla::launch_fwd_diag(fa, d->dtype, st); break;
     }
     if (e == hipErrorInvalidValue) return KLA_ERR_UNSUPPORTED;
@@ -298,7 +299,8 @@ klaStatus klaFwdNoAlloc(const klaDims* d, const void* q, const void* k, const vo
 
 klaStatus klaFwdBlock(const klaDims* d, const klaBlock* blk, const void* xq, const void* xk, const void* xv,
                       const void* za, const float* zqn, const float* zr, const float* l0, const float* eta0,
-                      void* o, float* lT, float* etaT, void* hipStream) {
+                      void* o, float* lT, float* etaT, void* workspace, size_t workspaceBytes,
+                      void* hipStream) {
     if (!d || !blk) return KLA_ERR_NULL;
     if (!dims_ok(d)) return KLA_ERR_SHAPE;
     if (!kinds_ok(d) || d->cov != KLA_DIAG) return KLA_ERR_UNSUPPORTED;
@@ -319,6 +321,10 @@ klaStatus klaFwdBlock(const klaDims* d, const klaBlock* blk, const void* xq, con
     const void* small[] = {blk->wq, blk->wk, blk->wv, blk->bq, blk->bk, blk->bv};
     for (const void* p : small)
         if (((uintptr_t)p & 3u) != 0) return KLA_ERR_ALIGN;
+    // the sequence split of few, long sequences, as for klaFwd
+    const size_t wneed = klaFwdWorkspaceBytes(d);
+    if (wneed > 0 && (!workspace || workspaceBytes < wneed)) return KLA_ERR_WORKSPACE;
+    if (wneed > 0 && !aligned16(workspace)) return KLA_ERR_ALIGN;
 
     const size_t ntk = (size_t)(BH * T), nlt = (size_t)(BH * dk), neta = (size_t)(BH * dk * dv);
     const Span s_o = span(o, ntk * dv * es);
@@ -335,6 +341,12 @@ klaStatus klaFwdBlock(const klaDims* d, const klaBlock* blk, const void* xq, con
     for (const Span& s : ins)
         if (overlap(s_o, s) || overlap(s_lT, s) || overlap(s_etaT, s)) return KLA_ERR_ALIAS;
     if (overlap(s_o, s_lT) || overlap(s_o, s_etaT) || overlap(s_lT, s_etaT)) return KLA_ERR_ALIAS;
+    if (wneed > 0) {
+        const Span s_ws = span(workspace, wneed);
+        for (const Span& s : ins)
+            if (overlap(s_ws, s)) return KLA_ERR_ALIAS;
+        if (overlap(s_ws, s_o) || overlap(s_ws, s_lT) || overlap(s_ws, s_etaT)) return KLA_ERR_ALIAS;
+    }
 
     kla::FwdArgs fa;
     fa.q = xq; fa.k = xk; fa.v = xv; fa.a = (const float*)za; fa.qn = zqn; fa.r = zr;
@@ -347,7 +359,7 @@ klaStatus klaFwdBlock(const klaDims* d, const klaBlock* blk, const void* xq, con
     fa.conv_s[0] = blk->sq; fa.conv_s[1] = blk->sk; fa.conv_s[2] = blk->sv;
     fa.r_eps = blk->r_eps;
     hipStream_t st = (hipStream_t)hipStream;
-    const hipError_t e = T == 0 ? kla::launch_fwd_empty(fa, 0, st) : kla::launch_fwd_diag_pipe(fa, d->dtype, st);
+    const hipError_t e = T == 0 ? kla::launch_fwd_empty(fa, 0, st) : launch_diag_pipe(fa, d, workspace, st);
     if (e == hipErrorInvalidValue) return KLA_ERR_UNSUPPORTED;
     return e == hipSuccess ? KLA_OK : KLA_ERR_HIP;
 }

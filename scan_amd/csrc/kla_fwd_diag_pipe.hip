@@ -226,18 +226,16 @@ __device__ void chain_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int
     // the convolution state before token 0)
     float kw[4] = {0.f, 0.f, 0.f, 0.f}, kb = 0.f, kx1 = 0.f, kx2 = 0.f, kx3 = 0.f;
     if constexpr (PRO) {
-        static_assert(!SEG, "the block prologue runs unsplit");
         qn = act_softplus(qn);
         const int W = p.conv_w;
         const size_t ch = (size_t)(bh % p.H) * DK + i;
         load_taps4(kw, p.conv_wt[1] + ch * W, W);
         if (p.conv_b[1]) kb = p.conv_b[1][ch];
-        if (p.conv_s[1]) {
-            const TIn* st = (const TIn*)p.conv_s[1] + (size_t)bh * (W - 1) * DK + i;
-            if (W >= 2) kx1 = (float)st[(W - 2) * DK];
-            if (W >= 3) kx2 = (float)st[(W - 3) * DK];
-            if (W >= 4) kx3 = (float)st[(W - 4) * DK];
-        }
+        // the x rows before the span's first token (segments after the first:
+        // the sequence's own rows)
+        kx1 = pro_x(kp, p.conv_s[1], bh, p.T, W, DK, sp.T0 - 1, i);
+        kx2 = pro_x(kp, p.conv_s[1], bh, p.T, W, DK, sp.T0 - 2, i);
+        kx3 = pro_x(kp, p.conv_s[1], bh, p.T, W, DK, sp.T0 - 3, i);
     }
     float wrun = 1.f;  // sequence split: gate product from the segment start
     // One chunk of inputs per buffer; NBC buffers rotate, so a chunk's loads
@@ -710,12 +708,9 @@ __device__ void gate_role(S3<TIn, K>& sm, TAPS& taps, const FwdArgs& p, const Sp
             taps.vb[x] = p.conv_b[2] ? p.conv_b[2][ch] : 0.f;
         }
 #pragma unroll
-        for (int j = 0; j < 3; ++j) {  // token j - 3: state row W - 4 + j
-            const int sr = W - 4 + j;
-            pq[j] = PR::zero();
-            const size_t so = ((size_t)bh * (W - 1) + sr) * DK + 2 * ip;
-            if (sr >= 0 && p.conv_s[0]) pq[j] = *(const typename PR::V*)((const TIn*)p.conv_s[0] + so);
-        }
+        for (int j = 0; j < 3; ++j)  // token T0 + j - 3
+            pq[j] = PR::make(pro_x(qp, p.conv_s[0], bh, p.T, W, DK, sp.T0 + j - 3, 2 * ip),
+                             pro_x(qp, p.conv_s[0], bh, p.T, W, DK, sp.T0 + j - 3, 2 * ip + 1));
     }
     auto load = [&](int c, Buf& bf) {
         const int t0 = c * C, n = sp.TL - t0;
@@ -733,11 +728,12 @@ __device__ void gate_role(S3<TIn, K>& sm, TAPS& taps, const FwdArgs& p, const Sp
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) bf.v[x][h2] = buf_load<QV>(rv, voff[x][h2]);
         if constexpr (PRO) {
-            // rows t0-3 .. of the sequence, clipped to [0, TL): rows before
-            // token 0 read as zero (the state is added at the first chunk)
-            const int h0 = t0 >= 3 ? t0 - 3 : 0;
+            // rows t0-3 .. of the span, clipped to the sequence start and the
+            // span end: rows before token 0 of the sequence read as zero (the
+            // state is added at the first chunk)
+            const int h0 = sp.T0 + t0 >= 3 ? t0 - 3 : -sp.T0;
             const int hend = t0 + rows < sp.TL ? t0 + rows : sp.TL;
-            const auto rh = make_rsrc(vbase + (size_t)h0 * VRB, (hend > h0 ? hend - h0 : 0) * VRB);
+            const auto rh = make_rsrc(vbase + (ptrdiff_t)h0 * VRB, (hend > h0 ? hend - h0 : 0) * VRB);
 #pragma unroll
             for (int x = 0; x < K::VPT; ++x)
 #pragma unroll
@@ -760,7 +756,7 @@ __device__ void gate_role(S3<TIn, K>& sm, TAPS& taps, const FwdArgs& p, const Sp
                     f32x4 h[3];
 #pragma unroll
                     for (int j = 0; j < 3; ++j) h[j] = Quad<TIn>::to_f32(cur.vh[x][j]);
-                    if (cg == 0 && p.conv_s[2]) {
+                    if (cg == 0 && sp.T0 == 0 && p.conv_s[2]) {
                         // the first chunk: rows before token 0 from the state
                         const int W = p.conv_w;
 #pragma unroll
@@ -1211,11 +1207,16 @@ hipError_t launch_chain(const FwdArgs& a, hipStream_t s) {
 template <typename TIn, int DK, int DV>
 hipError_t launch(const FwdArgs& a, hipStream_t s) {
     if (a.conv_w > 0) {
-        if (a.nseg > 1) return hipErrorInvalidValue;
         typedef P3<TIn, DK, DV> K;
-        const int nblk = a.B * a.H * a.n_vtiles;
-        hipLaunchKernelGGL((kla_fwd_diag_pipe_kernel<TIn, DK, DV, false, false, true>), dim3(nblk), dim3(K::NT), 0,
-                           s, a);
+        if (a.nseg > 1) {
+            const int nblk = a.B * a.H * a.n_vtiles * a.nseg;
+            hipLaunchKernelGGL((kla_fwd_diag_pipe_kernel<TIn, DK, DV, true, false, true>), dim3(nblk), dim3(K::NT),
+                               0, s, a);
+        } else {
+            const int nblk = a.B * a.H * a.n_vtiles;
+            hipLaunchKernelGGL((kla_fwd_diag_pipe_kernel<TIn, DK, DV, false, false, true>), dim3(nblk),
+                               dim3(K::NT), 0, s, a);
+        }
         return hipGetLastError();
     }
     if constexpr (std::is_same<TIn, bf16>::value) {

@@ -80,7 +80,7 @@ constexpr int kWarm = 512;
 constexpr int kWarmRun = 32;
 constexpr int kWarmRuns = kWarm / kWarmRun;
 
-template <typename TIn, int DK>
+template <typename TIn, int DK, bool PRO>
 __global__ __launch_bounds__(64 * kWarmRuns) void kla_seg_warm(FwdArgs p, int* ok) {
     __shared__ double sP[kWarmRuns][4][64];
     constexpr int G = DK / 64;
@@ -94,19 +94,27 @@ __global__ __launch_bounds__(64 * kWarmRuns) void kla_seg_warm(FwdArgs p, int* o
     const int bnd = s * p.seg_len;
     const int n = bnd < kWarm ? bnd : kWarm;  // a multiple of kSegBlk
     const int t0 = bnd - n;
-    const double qn = p.qn[(size_t)h * DK + i];
+    const double qn = PRO ? act_softplus(p.qn[(size_t)h * DK + i]) : p.qn[(size_t)h * DK + i];
     // P = M_last ... M_first with M_t = [[1 + b qn, b a^2], [qn, a^2]]
     double p00 = 1.0, p01 = 0.0, p10 = 0.0, p11 = 1.0;
     if (j * kWarmRun < n) {  // uniform over the wave
-        const size_t row = (size_t)bh * p.T + t0 + j * kWarmRun;
-        const auto ra = make_rsrc(p.a + row * DK, kWarmRun * DK * 4);
+        const int tr = t0 + j * kWarmRun;  // the run's first token
+        const size_t row = (size_t)bh * p.T + tr;
+        // a (with the block prologue: its pre-activation, in the input dtype)
+        constexpr int AES = PRO ? (int)sizeof(TIn) : 4;
+        const auto ra = make_rsrc((const char*)p.a + row * DK * AES, kWarmRun * DK * AES);
         const auto rk = make_rsrc((const TIn*)p.k + row * DK, kWarmRun * DK * (int)sizeof(TIn));
         // the token's row offset goes in the scalar offset, the lane's column
         // in the vector offset
         float av[kWarmRun], kv[kWarmRun];
 #pragma unroll
         for (int u = 0; u < kWarmRun; ++u) {
-            av[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ra, i * 4, u * DK * 4, 0));
+            if constexpr (AES == 2)
+                av[u] = __builtin_bit_cast(
+                    float, (unsigned)(unsigned short)__builtin_amdgcn_raw_buffer_load_b16(ra, i * 2, u * DK * 2, 0)
+                               << 16);
+            else
+                av[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ra, i * 4, u * DK * 4, 0));
             if constexpr (sizeof(TIn) == 2)
                 kv[u] = __builtin_bit_cast(
                     float, (unsigned)(unsigned short)__builtin_amdgcn_raw_buffer_load_b16(rk, i * 2, u * DK * 2, 0)
@@ -114,16 +122,37 @@ __global__ __launch_bounds__(64 * kWarmRuns) void kla_seg_warm(FwdArgs p, int* o
             else
                 kv[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rk, i * 4, u * DK * 4, 0));
         }
+        // block prologue: k = silu(conv(x)) from the taps of key dim i and the
+        // three x values before each token
+        float kw[4] = {0.f, 0.f, 0.f, 0.f}, kb = 0.f, x1 = 0.f, x2 = 0.f, x3 = 0.f;
+        if constexpr (PRO) {
+            const int W = p.conv_w;
+            const size_t ch = (size_t)h * DK + i;
+            load_taps4(kw, p.conv_wt[1] + ch * W, W);
+            if (p.conv_b[1]) kb = p.conv_b[1][ch];
+            x1 = pro_x((const TIn*)p.k, p.conv_s[1], bh, p.T, W, DK, tr - 1, i);
+            x2 = pro_x((const TIn*)p.k, p.conv_s[1], bh, p.T, W, DK, tr - 2, i);
+            x3 = pro_x((const TIn*)p.k, p.conv_s[1], bh, p.T, W, DK, tr - 3, i);
+        }
         // 1/r once per token (lane u holds token u of the run).  b and a^2 are
         // rounded to fp32 like the forward's own chain; the composition that
         // follows is fp64.
-        const float rho_l = 1.f / p.r[row + (lane % kWarmRun)];
+        const float rraw = p.r[row + (lane % kWarmRun)];
+        const float rho_l = 1.f / (PRO ? act_softplus(rraw) + p.r_eps : rraw);
 #pragma unroll
         for (int u = 0; u < kWarmRun; ++u) {
             const float rt = __builtin_bit_cast(
                 float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rho_l), u));
-            const double a2 = (double)(av[u] * av[u]);
-            const double b = (double)(kv[u] * kv[u] * rt);
+            float af = av[u], kf = kv[u];
+            if constexpr (PRO) {
+                af = act_sigmoid(av[u]);
+                kf = act_silu(conv4(kw, kb, kv[u], x1, x2, x3));
+                x3 = x2;
+                x2 = x1;
+                x1 = kv[u];
+            }
+            const double a2 = (double)(af * af);
+            const double b = (double)(kf * kf * rt);
             const double m00 = __builtin_fma(b, qn, 1.0), m01 = b * a2;
             const double n00 = m00 * p00 + m01 * p10, n01 = m00 * p01 + m01 * p11;
             const double n10 = qn * p00 + a2 * p10, n11 = qn * p01 + a2 * p11;
@@ -171,7 +200,7 @@ __global__ __launch_bounds__(64 * kWarmRuns) void kla_seg_warm(FwdArgs p, int* o
 constexpr int kMobThreads = 512;
 constexpr int kMobGrid = 1024;
 
-template <typename TIn, int DK>
+template <typename TIn, int DK, bool PRO>
 __device__ __forceinline__ void mobius_block(const FwdArgs& p, float* P, f32x4 (*sP)[DK], int i, int sub,
                                              int nb, int bh, int s) {
     constexpr int NSUB = kMobThreads / DK;
@@ -179,8 +208,10 @@ __device__ __forceinline__ void mobius_block(const FwdArgs& p, float* P, f32x4 (
     const int T0 = s * kSegBlk;
     constexpr int sl = kSegBlk / NSUB;
     const int tb = T0 + sub * sl;  // blocks before the last segment are full
-    const float qn = p.qn[(size_t)h * DK + i];
-    const float* ap = p.a + (size_t)bh * p.T * DK + i;
+    const float qn = PRO ? act_softplus(p.qn[(size_t)h * DK + i]) : p.qn[(size_t)h * DK + i];
+    // a (with the block prologue: its pre-activation, in the input dtype)
+    constexpr int AES = PRO ? (int)sizeof(TIn) : 4;
+    const char* ap = (const char*)p.a + ((size_t)bh * p.T * DK + i) * AES;
     const TIn* kp = (const TIn*)p.k + (size_t)bh * p.T * DK + i;
     const float* rp = p.r + (size_t)bh * p.T;
     // P = M_t ... M_tb, later tokens on the left
@@ -198,7 +229,19 @@ __device__ __forceinline__ void mobius_block(const FwdArgs& p, float* P, f32x4 (
     constexpr int TB = 8;  // tokens per load batch
     static_assert(sl <= 64 && sl % TB == 0 && DK % 64 == 0, "run layout");
     const int lane = threadIdx.x & 63;
-    const float rho_l = lane < sl ? 1.f / rp[tb + lane] : 0.f;
+    const float rho_l = lane < sl ? 1.f / (PRO ? act_softplus(rp[tb + lane]) + p.r_eps : rp[tb + lane]) : 0.f;
+    // block prologue: k = silu(conv(x)) from the taps of key dim i and the
+    // three x values before each token
+    float kw[4] = {0.f, 0.f, 0.f, 0.f}, kb = 0.f, x1 = 0.f, x2 = 0.f, x3 = 0.f;
+    if constexpr (PRO) {
+        const int W = p.conv_w;
+        const size_t ch = (size_t)h * DK + i;
+        load_taps4(kw, p.conv_wt[1] + ch * W, W);
+        if (p.conv_b[1]) kb = p.conv_b[1][ch];
+        x1 = pro_x((const TIn*)p.k, p.conv_s[1], bh, p.T, W, DK, tb - 1, i);
+        x2 = pro_x((const TIn*)p.k, p.conv_s[1], bh, p.T, W, DK, tb - 2, i);
+        x3 = pro_x((const TIn*)p.k, p.conv_s[1], bh, p.T, W, DK, tb - 3, i);
+    }
     // batches of TB tokens, the next batch's loads in flight during the
     // current batch's steps
     struct Batch {
@@ -206,12 +249,16 @@ __device__ __forceinline__ void mobius_block(const FwdArgs& p, float* P, f32x4 (
     };
     // the run's rows of a and k through buffer resources (offsets from the
     // run start, so the per-token offsets are immediates or a few registers)
-    const auto ra = make_rsrc(ap - i + (size_t)tb * DK, sl * DK * 4);
+    const auto ra = make_rsrc(ap - (size_t)i * AES + (size_t)tb * DK * AES, sl * DK * AES);
     const auto rk = make_rsrc(kp - i + (size_t)tb * DK, sl * DK * (int)sizeof(TIn));
     auto load = [&](int t8, Batch& x) {
 #pragma unroll
         for (int u = 0; u < TB; ++u) {
-            x.a[u] = buf_load<float>(ra, ((t8 + u) * DK + i) * 4);
+            if constexpr (AES == 2)
+                x.a[u] = __builtin_bit_cast(
+                    float, (unsigned)buf_load<unsigned short>(ra, ((t8 + u) * DK + i) * 2) << 16);
+            else
+                x.a[u] = buf_load<float>(ra, ((t8 + u) * DK + i) * 4);
             if constexpr (sizeof(TIn) == 2)
                 x.kv[u] = __builtin_bit_cast(
                     float, (unsigned)buf_load<unsigned short>(rk, ((t8 + u) * DK + i) * 2) << 16);
@@ -224,7 +271,15 @@ __device__ __forceinline__ void mobius_block(const FwdArgs& p, float* P, f32x4 (
         for (int u = 0; u < TB; ++u) {
             const float rho = __builtin_bit_cast(
                 float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rho_l), t8 + u));
-            step(x.a[u], x.kv[u], rho);
+            if constexpr (PRO) {
+                const float kf = act_silu(conv4(kw, kb, x.kv[u], x1, x2, x3));
+                x3 = x2;
+                x2 = x1;
+                x1 = x.kv[u];
+                step(act_sigmoid(x.a[u]), kf, rho);
+            } else {
+                step(x.a[u], x.kv[u], rho);
+            }
             if (u % 4 == 3) {
                 const float sc = fast_rcp(p00 + p01 + p10 + p11);  // positive rescale: same map
                 p00 *= sc; p01 *= sc; p10 *= sc; p11 *= sc;
@@ -259,7 +314,7 @@ __device__ __forceinline__ void mobius_block(const FwdArgs& p, float* P, f32x4 (
     }
 }
 
-template <typename TIn, int DK>
+template <typename TIn, int DK, bool PRO>
 __global__ __launch_bounds__(kMobThreads) void kla_seg_mobius(FwdArgs p, float* P, const int* ok) {
     constexpr int NSUB = kMobThreads / DK;
     __shared__ f32x4 sP[NSUB][DK];
@@ -270,7 +325,7 @@ __global__ __launch_bounds__(kMobThreads) void kla_seg_mobius(FwdArgs p, float* 
     for (int blk = blockIdx.x; blk < p.B * p.H * nb; blk += gridDim.x) {
         const int bh = blk / nb, s = blk % nb;
         if (seg_warm_ok(p, ok, bh)) continue;  // uniform over the workgroup
-        mobius_block<TIn, DK>(p, P, sP, i, sub, nb, bh, s);
+        mobius_block<TIn, DK, PRO>(p, P, sP, i, sub, nb, bh, s);
         __syncthreads();  // sP is reused by the next block
     }
 }
@@ -455,10 +510,15 @@ __global__ __launch_bounds__(256) void kla_seg_correct(FwdArgs p) {
 template <typename TIn>
 hipError_t launch_warm_t(const FwdArgs& a, int* ok, hipStream_t s) {
     const int nblk = a.B * a.H * (a.nseg - 1) * (a.dk / 64);
-    if (a.dk == 128)
-        hipLaunchKernelGGL((kla_seg_warm<TIn, 128>), dim3(nblk), dim3(64 * kWarmRuns), 0, s, a, ok);
+    const bool pro = a.conv_w > 0;
+    if (a.dk == 128 && pro)
+        hipLaunchKernelGGL((kla_seg_warm<TIn, 128, true>), dim3(nblk), dim3(64 * kWarmRuns), 0, s, a, ok);
+    else if (a.dk == 128)
+        hipLaunchKernelGGL((kla_seg_warm<TIn, 128, false>), dim3(nblk), dim3(64 * kWarmRuns), 0, s, a, ok);
+    else if (a.dk == 64 && pro)
+        hipLaunchKernelGGL((kla_seg_warm<TIn, 64, true>), dim3(nblk), dim3(64 * kWarmRuns), 0, s, a, ok);
     else if (a.dk == 64)
-        hipLaunchKernelGGL((kla_seg_warm<TIn, 64>), dim3(nblk), dim3(64 * kWarmRuns), 0, s, a, ok);
+        hipLaunchKernelGGL((kla_seg_warm<TIn, 64, false>), dim3(nblk), dim3(64 * kWarmRuns), 0, s, a, ok);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }
@@ -467,10 +527,15 @@ template <typename TIn>
 hipError_t launch_mobius_t(const FwdArgs& a, float* P, const int* ok, hipStream_t s) {
     int nblk = a.B * a.H * (a.nseg - 1) * (a.seg_len / kSegBlk);
     if (nblk > kMobGrid) nblk = kMobGrid;
-    if (a.dk == 128)
-        hipLaunchKernelGGL((kla_seg_mobius<TIn, 128>), dim3(nblk), dim3(kMobThreads), 0, s, a, P, ok);
+    const bool pro = a.conv_w > 0;
+    if (a.dk == 128 && pro)
+        hipLaunchKernelGGL((kla_seg_mobius<TIn, 128, true>), dim3(nblk), dim3(kMobThreads), 0, s, a, P, ok);
+    else if (a.dk == 128)
+        hipLaunchKernelGGL((kla_seg_mobius<TIn, 128, false>), dim3(nblk), dim3(kMobThreads), 0, s, a, P, ok);
+    else if (a.dk == 64 && pro)
+        hipLaunchKernelGGL((kla_seg_mobius<TIn, 64, true>), dim3(nblk), dim3(kMobThreads), 0, s, a, P, ok);
     else if (a.dk == 64)
-        hipLaunchKernelGGL((kla_seg_mobius<TIn, 64>), dim3(nblk), dim3(kMobThreads), 0, s, a, P, ok);
+        hipLaunchKernelGGL((kla_seg_mobius<TIn, 64, false>), dim3(nblk), dim3(kMobThreads), 0, s, a, P, ok);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

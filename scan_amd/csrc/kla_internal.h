@@ -54,6 +54,16 @@ struct FwdArgs {
                                     // 16-token tiles (qhat_tile_offset)
 };
 
+// Block prologue input x (q, k or v projections, [B,H,T,d] in TIn) at token
+// t of sequence bh, channel c, as fp32: the row itself for t >= 0, before the
+// sequence the convolution state row W-1+t ([B,H,W-1,d]) or zero.
+template <typename TIn>
+__device__ __forceinline__ float pro_x(const TIn* x, const void* st, int bh, int T, int W, int d, int t, int c) {
+    if (t >= 0) return (float)x[((size_t)bh * T + t) * d + c];
+    const int sr = W - 1 + t;
+    return st && sr >= 0 ? (float)((const TIn*)st)[((size_t)bh * (W - 1) + sr) * d + c] : 0.f;
+}
+
 // Element offset of q-hat (token t of sequence bh, key dim i) in the tiled
 // layout the correction pass reads: per (bh, 16-token tile, 32-dim block kb)
 // 512 elements, lane (c16 = t % 16, g = i % 32 / 8) holding 8 consecutive

@@ -129,6 +129,8 @@ def make_inputs(w: Workload | str, seed: int = 0, device: str | torch.device = "
 # the fused block prologue at the LM-layer shape: pre-activations drawn so
 # that the prologue's a, qn and r have the lm_diag distributions
 BLOCK = Workload("block_lm_diag", 8, 16, 2048, 128, 128, "diag", "bf16")
+# and at the long-context shape (same draws as long_diag's laws)
+BLOCK_LONG = Workload("block_long_diag", 1, 16, 32768, 128, 128, "diag", "bf16", a_mu=4.0)
 BLOCK_WIDTH = 4
 
 
@@ -146,7 +148,7 @@ def make_block_inputs(w: Workload | str, seed: int = 0, device="cpu", width: int
     [B,H,width-1,d] ~ N(0,1) (storage dtype), else None.  r_eps = 1e-3.
     """
     if isinstance(w, str):
-        w = BLOCK if w == BLOCK.name else WORKLOADS[w]
+        w = {BLOCK.name: BLOCK, BLOCK_LONG.name: BLOCK_LONG}.get(w) or WORKLOADS[w]
     if override:
         w = w.with_(**override)
     g = torch.Generator(device="cpu").manual_seed(seed)

@@ -277,7 +277,8 @@ def test_backward_argument_errors():
 
 def block_call(dims, blk=None, **over):
     args = dict(xq=addr(1), xk=addr(2), xv=addr(3), za=addr(4), zqn=addr(5), zr=addr(6), l0=None,
-                eta0=None, o=addr(7), lT=addr(8), etaT=addr(9), stream=None)
+                eta0=None, o=addr(7), lT=addr(8), etaT=addr(9), workspace=None, workspaceBytes=0,
+                stream=None)
     args.update(over)
     if blk is None:
         blk = scan_amd.KlaBlock(4, addr(10), addr(11), addr(12), None, None, None, None, None, None,
@@ -287,7 +288,7 @@ def block_call(dims, blk=None, **over):
 
 def test_block_argument_errors():
     d = KlaDims(2, 3, 40, 128, 128, BF16, DIAG)
-    assert scan_amd.klaFwdBlock(d, None, *([None] * 11), None) == NULL
+    assert scan_amd.klaFwdBlock(d, None, *([None] * 11), None, 0, None) == NULL
     for w in (0, 5, -1):
         blk = scan_amd.KlaBlock(w, addr(10), addr(11), addr(12), None, None, None, None, None, None, 1e-3)
         assert block_call(d, blk) == SHAPE, w
@@ -316,3 +317,11 @@ def test_block_argument_errors():
     blk = scan_amd.KlaBlock(4, addr(7), addr(11), addr(12), None, None, None, None, None, None, 1e-3)
     assert block_call(d, blk) == ALIAS                   # taps under o
     assert block_call(KlaDims(0, 3, 40, 128, 128, BF16, DIAG)) == OK
+    # a split shape needs the forward's workspace
+    long = KlaDims(1, 16, 32768, 128, 128, BF16, DIAG)
+    need = scan_amd.klaFwdWorkspaceBytes(long)
+    assert need > 0
+    assert block_call(long) == WS
+    assert block_call(long, workspace=addr(20), workspaceBytes=need - 1) == WS
+    assert block_call(long, workspace=addr(20) + 8, workspaceBytes=need) == ALIGN
+    assert block_call(long, workspace=addr(1), workspaceBytes=need) == ALIAS

@@ -116,3 +116,52 @@ def test_block_deterministic():
     r1, r2 = run_hip(b), run_hip(b)
     for key in r1:
         np.testing.assert_array_equal(r1[key], r2[key])
+
+
+@pytest.mark.parametrize("dtype,d,over,nseg,state", [
+    ("bf16", 128, dict(B=1, H=2, T=3000), "3", True),     # ragged last segment, states
+    ("bf16", 128, dict(B=1, H=2, T=4096), "", False),     # split chosen by the library
+    ("f32", 64, dict(B=1, H=2, T=2300), "2", True),
+])
+def test_block_sequence_split(monkeypatch, dtype, d, over, nseg, state):
+    """klaFwdBlock on few, long sequences: the precision warm-up and the
+    segment forwards run the prologue too (k and x rows from before a
+    segment's start, the convolution state before the sequence's)."""
+    _print_case("block split", dtype, d, over, nseg)
+    if nseg:
+        monkeypatch.setenv("KLA_FWD_NSEG", nseg)
+    b = gen.make_block_inputs("long_diag", seed=60, dk=d, dv=d, dtype=dtype, state=state, **over)
+    w = b["workload"]
+    dims = scan_amd.KlaDims(w.B, w.H, w.T, d, d, 1 if dtype == "bf16" else 0, 0)
+    assert scan_amd.klaFwdWorkspaceBytes(dims) > 0
+    st = gen.make_state(w, seed=61) if state else {"l0": None, "eta0": None}
+    hip = run_hip(b, st["l0"], st["eta0"])
+    ref = run_ref(b, st["l0"], st["eta0"])
+    assert_parity(compare(hip, ref), dtype, f"block split {dtype} d{d} {over}")
+
+
+def test_block_split_warmup_fallback(monkeypatch):
+    """One head whose precision cannot settle within the warm-up window (a
+    near 1, a tiny process noise): it takes the exact block-product carry,
+    computed through the prologue as well."""
+    _print_case("block split fallback")
+    monkeypatch.setenv("KLA_FWD_NSEG", "3")
+    b = gen.make_block_inputs("long_diag", seed=62, B=1, H=2, T=3000, state=True)
+    za, zqn = b["za"].clone(), b["zqn"].clone()
+    za[:, 0] = 10.0            # a = sigmoid(10) ~ 0.99995
+    zqn[0] = -14.0             # qn = softplus(-14) ~ 8e-7
+    b["za"], b["zqn"] = za, zqn
+    st = gen.make_state(b["workload"], seed=63)
+    hip = run_hip(b, st["l0"], st["eta0"])
+    ref = run_ref(b, st["l0"], st["eta0"])
+    assert_parity(compare(hip, ref), "bf16", "block split fallback")
+
+
+def test_block_full_long_shape_every_sequence():
+    """B1 H16 T32768 d128 bf16 (split by the library), every head against the
+    oracle."""
+    _print_case("block full long shape")
+    b = gen.make_block_inputs("block_long_diag", seed=0)
+    hip = run_hip(b)
+    ref = run_ref(b)
+    assert_parity(compare(hip, ref), "bf16", "block full long shape")
