@@ -303,6 +303,32 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// One exchange of the reduce-scatter over lane mask M of the N values a lane
+// still holds: the lane keeps the half chosen by its lane bit, sends the
+// other half to its partner and adds the partner's copy of the kept half
+// (N == 1: a plain exchange-and-add).  base accumulates the index of the
+// first kept value.
+template <int N, int M>
+__device__ __forceinline__ void reduce_scatter(float* w, int lane, int& base) {
+    if constexpr (M >= 1) {
+        if constexpr (N > 1) {
+            constexpr int H = N / 2;
+            const bool hi = (lane & M) != 0;
+#pragma unroll
+            for (int j = 0; j < H; ++j) {
+                const float keep = hi ? w[H + j] : w[j];
+                const float send = hi ? w[j] : w[H + j];
+                w[j] = keep + __shfl_xor(send, M, 64);
+            }
+            base += hi ? H : 0;
+            reduce_scatter<H, M / 2>(w, lane, base);
+        } else {
+            w[0] += __shfl_xor(w[0], M, 64);
+            reduce_scatter<N, M / 2>(w, lane, base);
+        }
+    }
+}
+
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }

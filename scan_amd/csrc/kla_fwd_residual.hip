@@ -65,32 +65,6 @@ __device__ __forceinline__ typename Mma<T>::K16 k16(f32x4 x) {
     }
 }
 
-// One exchange of the reduce-scatter over lane mask M of the N values a lane
-// still holds: the lane keeps the half chosen by its lane bit, sends the
-// other half to its partner and adds the partner's copy of the kept half
-// (N == 1: a plain exchange-and-add).  base accumulates the index of the
-// first kept value.
-template <int N, int M>
-__device__ __forceinline__ void reduce_scatter(float* w, int lane, int& base) {
-    if constexpr (M >= 1) {
-        if constexpr (N > 1) {
-            constexpr int H = N / 2;
-            const bool hi = (lane & M) != 0;
-#pragma unroll
-            for (int j = 0; j < H; ++j) {
-                const float keep = hi ? w[H + j] : w[j];
-                const float send = hi ? w[j] : w[H + j];
-                w[j] = keep + __shfl_xor(send, M, 64);
-            }
-            base += hi ? H : 0;
-            reduce_scatter<H, M / 2>(w, lane, base);
-        } else {
-            w[0] += __shfl_xor(w[0], M, 64);
-            reduce_scatter<N, M / 2>(w, lane, base);
-        }
-    }
-}
-
 // A (b,h) may be split by value columns into tiles of DVT columns: the
 // residual write couples the key dims, not the value columns, so each tile
 // runs on its own (the key-dim sums are formed in every tile).
@@ -668,6 +642,7 @@ int fwd_residual_vtiles(int B, int H, int dk) {
 
 hipError_t launch_fwd_residual(const FwdArgs& a, int dtype, int cov, hipStream_t s) {
     if (!fwd_residual_supported(a.dk, a.dv) || a.T < 1) return hipErrorInvalidValue;
+    if (fwd_residual_chunk_supported(a.dk, a.dv, cov)) return launch_fwd_residual_chunk(a, dtype, s);
     if (a.n_vtiles != 1 && !(a.n_vtiles == 2 && a.dk >= 64)) return hipErrorInvalidValue;
     if (dtype == DT_BF16) return cov ? dispatch<bf16, true>(a, s) : dispatch<bf16, false>(a, s);
     return cov ? dispatch<float, true>(a, s) : dispatch<float, false>(a, s);

@@ -1,0 +1,410 @@
+// kla_fwd_residual_chunk.hip -- gfx950 chunked forward of the residual-write
+// variant with diagonal precision ("Kalman Delta Networks: Uncertainty-aware
+// Associative Memory", abstract: the Kalman gain weights a write of the
+// residual; diagonal approximation), on the matrix cores.
+//
+// Recurrence per (b,h) (the same as the block kernel of kla_fwd_residual.hip):
+//   lp = l / (a^2 + qn l),  c = k / lp,  den = k.c + r,  g = c / den
+//   u  = v - (a (.) m)^T k,  m = a (.) m + g u^T,  l = lp + k^2 / r,  o = m^T q
+// Over a chunk of C = 16 tokens from the state M0 at its start, with
+// Gam_t = a_1 ... a_t per key dim, K~ = Gam (.) K, Q~ = Gam (.) Q (rows per
+// token), C^ = C / Gam and u'_s = u_s / den_s:
+//   (a (.) m_{t-1})^T k_t = K~_t^T M0 + sum_{s<t} (K~_t . C^_s) u'_s
+//   (diag(den) + strictlower(K~ C^T)) U' = V - K~ M0
+//   O = Q~ M0 + lower(Q~ C^T) U'
+//   M_C = Gam_C (.) M0 + E^T U',   E_s = (a_{s+1} ... a_C) (.) c_s
+// Only the products with M0 and U' depend on the state.  The rest -- the
+// precision chain, the Gram matrices K~ C^T and Q~ C^T, and the inverse
+// T' = (diag(den) + strictlower(K~ C^T))^{-1} -- depends on the inputs only
+// and runs one and two chunks ahead in other waves.
+//
+// Roles (one workgroup per (b,h) and 64 value columns; tiles of one (b,h)
+// run 8 workgroups apart, on one XCD):
+// - chain waves (dk/64, one lane per key dim): the precision recursion, the
+//   rows of K~, Q~, C^, E and Gam_C in LDS, and per-token partial sums of
+//   den;
+// - prep waves (2): the Gram matrices on the matrix cores (wave 0 K~ C^T,
+//   wave 1 Q~ C^T), and in wave 0 the inverse of the unit lower triangular
+//   I + N, N = diag(den)^-1 strictlower(K~ C^T), by forward substitution
+//   (a column per lane quad), scaled to T';
+// - state waves (2, 32 value columns each as two 16-column groups): per
+//   chunk [K~; Q~] M0, U' = T' (V - K~ M0), O = Q~ M0 + C' U' and the update,
+//   the state in accumulator tiles for the whole sequence.
+// Iteration j of the loop: chain on chunk j, prep on chunk j-1, state on
+// chunk j-2, one workgroup barrier (LDS only) per iteration.
+//
+// C^ = c / Gam divides by the decay products.  A chain wave whose Gam leaves
+// [2^-64, 2^64] within a chunk writes zero C^ rows for its key dims and
+// instead forms their contribution to K~ C^T and Q~ C^T exactly, as sums of
+// D(s,t) k_t c_s and D(s,t) q_t c_s with D(s,t) = a_{s+1} ... a_t (products
+// only), which the prep waves add to the matrix-core Gram.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include "kla_common.h"
+#include "kla_residual.h"
+
+namespace kla {
+namespace {
+
+constexpr int kRC = 16;                 // tokens per chunk
+constexpr int kRCP = kRC + 4;           // padded row of the [.][kRC] arrays
+constexpr float kGamLo = 0x1p-64f, kGamHi = 0x1p64f;  // range of Gam for C^ = c / Gam
+constexpr int kRcDVT = 64;              // value columns per workgroup
+
+template <int D>
+struct RcRoles {
+    static constexpr int NCW = D / 64;  // chain waves
+    static constexpr int NPW = 2;       // prep waves
+    static constexpr int NSW = 2;       // state waves
+    static constexpr int NW = NCW + NPW + NSW;
+};
+
+// S: operand storage (bf16, or fp32 split into bf16 pairs at the read).
+// Token-major rows are padded by 16 bytes and the [.][kRC] rows by 4 values,
+// so that the 16 rows a fragment read touches fall in distinct banks.
+template <typename S, int D>
+struct RcSm {
+    static constexpr int NCW = D / 64;
+    static constexpr int KP = D + 16 / (int)sizeof(S);
+    alignas(16) S kt[3][kRC][KP];                 // K~ rows
+    alignas(16) S qt[3][kRC][KP];                 // Q~ rows
+    alignas(16) S ch[2][kRC][KP];                 // C^ rows (zero off the factorisation)
+    alignas(16) S e[3][D][kRCP];                  // E, key-dim-major
+    alignas(16) S tp[2][kRC][kRCP];               // T'
+    alignas(16) S cp[2][kRC][kRCP];               // C' = lower(Q~ C^T)
+    alignas(16) float gc[3][D];                   // Gam_C
+    alignas(16) float den[2][NCW][kRC];           // partial sums of k.c (+ r in wave 0)
+    alignas(16) float gx[2][NCW][kRC][2 * kRC];   // exact sums [t][s] (K~ C^T), [t][kRC + s] (Q~ C^T)
+    alignas(16) float nt[kRC][4][4];              // N as [t][s % 4][s / 4]
+    int off[2][NCW];                              // chain wave off the factorisation
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_q(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Two accumulator tiles as one K32 operand (slots 0-3 from lo, 4-7 from hi).
+template <typename S>
+__device__ __forceinline__ typename Frag<S>::V frag_acc(f32x4 lo, f32x4 hi) {
+    if constexpr (std::is_same<S, bf16>::value) {
+        typedef short s16x8 __attribute__((__vector_size__(16)));
+        const s16x4 a = pack_bf16x4(lo[0], lo[1], lo[2], lo[3]);
+        const s16x4 b = pack_bf16x4(hi[0], hi[1], hi[2], hi[3]);
+        const s16x8 r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+        return __builtin_bit_cast(bf16x8, r);
+    } else {
+        return Frag<S>::from_acc(lo, hi);
+    }
+}
+
+template <typename TIn, int D>
+__global__ __launch_bounds__(RcRoles<D>::NW * 64) void kla_fwd_residual_chunk_kernel(FwdArgs p) {
+    typedef RcRoles<D> R;
+    typedef TIn S;
+    typedef RcSm<S, D> Sm;
+    typedef Frag<S> F;     // K32 operands
+    typedef Mma<TIn> MA;   // K16 operands
+    constexpr int NVT = D / kRcDVT;
+    __shared__ Sm sm;
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int x8 = (int)blockIdx.x;
+    const int vt = NVT == 1 ? 0 : (x8 / 8) % NVT;
+    const int bh = NVT == 1 ? x8 : (x8 / (8 * NVT)) * 8 + x8 % 8;
+    const int nbh = p.B * p.H;
+    if (bh >= nbh) return;  // padding of the grid to the XCD pattern: the whole workgroup
+    const int h = bh % p.H;
+    const int T = p.T, nch = (T + kRC - 1) / kRC;
+    const size_t row0 = (size_t)bh * T;
+    const TIn* q = (const TIn*)p.q;
+    const TIn* k = (const TIn*)p.k;
+    const TIn* v = (const TIn*)p.v;
+    TIn* o = (TIn*)p.o;
+
+    if (wave < R::NCW) {
+        // ---------------- chain: one lane per key dim
+        const int cw = wave, i = 64 * cw + lane;
+        float l = p.l0 ? p.l0[(size_t)bh * D + i] : 1.f;
+        const float qn = p.qn[(size_t)h * D + i];
+        struct In {
+            TIn k[kRC], q[kRC];
+            float a[kRC], r[kRC];
+        };
+        auto load = [&](int c, In& x) {
+#pragma unroll
+            for (int u = 0; u < kRC; ++u) {
+                const int t = c * kRC + u < T ? c * kRC + u : T - 1;
+                const size_t idx = (row0 + t) * D + i;
+                x.k[u] = k[idx];
+                x.q[u] = q[idx];
+                x.a[u] = p.a[idx];
+                x.r[u] = p.r[row0 + t];
+            }
+        };
+        auto chain = [&](int c, const In& x) {
+            const int b3 = c % 3, b2 = c & 1;
+            float kf[kRC], qf[kRC], af[kRC], cv[kRC], gm[kRC], dk[kRC];
+            float gam = 1.f;
+            bool ok = true;
+#pragma unroll
+            for (int u = 0; u < kRC; ++u) {
+                const bool in = c * kRC + u < T;
+                kf[u] = in ? (float)x.k[u] : 0.f;
+                qf[u] = in ? (float)x.q[u] : 0.f;
+                af[u] = in ? x.a[u] : 1.f;
+                const float ru = in ? x.r[u] : 1.f;
+                const float lp = l * fast_rcp(__builtin_fmaf(qn, l, af[u] * af[u]));
+                cv[u] = kf[u] * fast_rcp(lp);
+                if (in) l = __builtin_fmaf(kf[u] * kf[u], fast_rcp(ru), lp);
+                gam *= af[u];
+                gm[u] = gam;
+                ok = ok && gam >= kGamLo && gam <= kGamHi;
+                dk[u] = __builtin_fmaf(kf[u], cv[u], i == 0 ? ru : 0.f);
+                sm.kt[b3][u][i] = (S)(gam * kf[u]);
+                sm.qt[b3][u][i] = (S)(gam * qf[u]);
+            }
+            sm.gc[b3][i] = gam;
+            {
+                float ev[kRC];
+                float sfx = 1.f;
+#pragma unroll
+                for (int u = kRC - 1; u >= 0; --u) {
+                    ev[u] = sfx * cv[u];
+                    sfx *= af[u];
+                }
+#pragma unroll
+                for (int u4 = 0; u4 < kRC; u4 += 4)
+                    *(typename Quad<S>::V*)&sm.e[b3][i][u4] =
+                        Quad<S>::make(f32x4{ev[u4], ev[u4 + 1], ev[u4 + 2], ev[u4 + 3]});
+            }
+            const bool fac = __all(ok);
+#pragma unroll
+            for (int u = 0; u < kRC; ++u) sm.ch[b2][u][i] = fac ? (S)(cv[u] * fast_rcp(gm[u])) : (S)0.f;
+            {
+                int base = 0;
+                reduce_scatter<kRC, 32>(dk, lane, base);
+                if ((lane & 3) == 0) sm.den[b2][cw][base] = dk[0];
+            }
+            if (!fac) {
+                // this wave's key dims, exactly: D(s,t) k_t c_s (s < t) and D(s,t) q_t c_s (s <= t)
+#pragma unroll
+                for (int t = 0; t < kRC; ++t) {
+                    float w[2 * kRC];
+                    float dst = 1.f;
+#pragma unroll
+                    for (int s = kRC - 1; s >= 0; --s) {
+                        if (s > t) {
+                            w[s] = 0.f;
+                            w[kRC + s] = 0.f;
+                            continue;
+                        }
+                        if (s < t) dst *= af[s + 1];
+                        w[s] = s < t ? dst * kf[t] * cv[s] : 0.f;
+                        w[kRC + s] = dst * qf[t] * cv[s];
+                    }
+                    int base = 0;
+                    reduce_scatter<2 * kRC, 32>(w, lane, base);
+                    if ((lane & 1) == 0) sm.gx[b2][cw][t][base] = w[0];
+                }
+            }
+            if (lane == 0) sm.off[b2][cw] = fac ? 0 : 1;
+        };
+
+        In cur, nxt;
+        load(0, cur);
+        for (int j = 0; j < nch + 2; ++j) {
+            if (j < nch) {
+                if (j + 1 < nch) load(j + 1, nxt);
+                chain(j, cur);
+                cur = nxt;
+            }
+            lds_barrier();
+        }
+        if (p.lT && vt == 0) p.lT[(size_t)bh * D + i] = l;
+    } else if (wave < R::NCW + R::NPW) {
+        // ---------------- prep: Gram matrices, the inverse
+        const int pw = wave - R::NCW;
+        const int cl = lane & 15, g4 = lane >> 4;
+        auto prep = [&](int c) {
+            const int b3 = c % 3, b2 = c & 1;
+            const S* arow = pw == 0 ? &sm.kt[b3][cl][0] : &sm.qt[b3][cl][0];
+            const S* brow = &sm.ch[b2][cl][0];
+            f32x4 G = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < D / 32; ++kb) G = F::mma(F::ld(arow + 32 * kb, g4), F::ld(brow + 32 * kb, g4), G);
+            // G: rows t = 4 g4 + e, column s = cl
+            const int t0 = 4 * g4, s = cl;
+#pragma unroll
+            for (int cw = 0; cw < R::NCW; ++cw)
+                if (sm.off[b2][cw]) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) G[e] += sm.gx[b2][cw][t0 + e][(pw == 0 ? 0 : kRC) + s];
+                }
+            if (pw == 1) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sm.cp[b2][t0 + e][s] = (S)(s <= t0 + e ? G[e] : 0.f);
+                return;
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float dn = 0.f;
+#pragma unroll
+                for (int cw = 0; cw < R::NCW; ++cw) dn += sm.den[b2][cw][t0 + e];
+                sm.nt[t0 + e][s & 3][s >> 2] = s < t0 + e ? G[e] * fast_rcp(dn) : 0.f;
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+            // S = (I + N)^-1 column j = lane / 4; lane phase ph holds rows ph + 4m
+            const int j = lane >> 2, ph = lane & 3;
+            float sv[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) sv[m] = ph + 4 * m == j ? 1.f : 0.f;
+#pragma unroll
+            for (int t = 1; t < kRC; ++t) {
+                const f32x4 nr = *(const f32x4*)&sm.nt[t][ph][0];
+                float part = nr[0] * sv[0];
+#pragma unroll
+                for (int m = 1; m < 4; ++m) part = __builtin_fmaf(nr[m], sv[m], part);
+                part += dpp_q<0xB1>(part);  // quad_perm [1,0,3,2]
+                part += dpp_q<0x4E>(part);  // quad_perm [2,3,0,1]
+                if (ph == (t & 3) && t > j) sv[t >> 2] = -part;
+            }
+            float dj = 0.f;
+#pragma unroll
+            for (int cw = 0; cw < R::NCW; ++cw) dj += sm.den[b2][cw][j];
+            const float rdj = fast_rcp(dj);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) sm.tp[b2][ph + 4 * m][j] = (S)(sv[m] * rdj);
+        };
+        for (int j = 0; j < nch + 2; ++j) {
+            if (j >= 1 && j - 1 < nch) prep(j - 1);
+            lds_barrier();
+        }
+    } else {
+        // ---------------- state: two 16-column groups per wave
+        const int sw = wave - R::NCW - R::NPW;
+        const int cl = lane & 15, g4 = lane >> 4;
+        const int col = vt * kRcDVT + 32 * sw + cl;  // + 16 g
+        constexpr int NRT = D / 16;
+        f32x4 M[2][NRT];
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+            for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    M[g][rt][e] = p.eta0 ? p.eta0[((size_t)bh * D + 16 * rt + 4 * g4 + e) * D + col + 16 * g] : 0.f;
+        TIn vc[2][4], vn[2][4];
+        auto loadv = [&](int c, TIn (&x)[2][4]) {
+#pragma unroll
+            for (int g = 0; g < 2; ++g)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = c * kRC + 4 * g4 + e < T ? c * kRC + 4 * g4 + e : T - 1;
+                    x[g][e] = v[(row0 + t) * D + col + 16 * g];
+                }
+        };
+        auto state = [&](int c, const TIn (&x)[2][4]) {
+            const int b3 = c % 3, b2 = c & 1;
+            f32x4 PK[2], PQ[2];
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                PK[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+                PQ[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+            const S* krow = &sm.kt[b3][cl][0];
+            const S* qrow = &sm.qt[b3][cl][0];
+#pragma unroll
+            for (int kb = 0; kb < D / 32; ++kb) {
+                const auto ak = F::ld(krow + 32 * kb, g4);
+                const auto aq = F::ld(qrow + 32 * kb, g4);
+#pragma unroll
+                for (int g = 0; g < 2; ++g) {
+                    const auto bm = frag_acc<S>(M[g][2 * kb], M[g][2 * kb + 1]);
+                    PK[g] = F::mma(ak, bm, PK[g]);
+                    PQ[g] = F::mma(aq, bm, PQ[g]);
+                }
+            }
+            const auto at = MA::ld16(&sm.tp[b2][cl][4 * g4]);
+            const auto ac = MA::ld16(&sm.cp[b2][cl][4 * g4]);
+            typename MA::K16 ub[2];
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                f32x4 X;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) X[e] = (c * kRC + 4 * g4 + e < T ? (float)x[g][e] : 0.f) - PK[g][e];
+                const f32x4 U = MA::mma16(at, MA::from_acc(X), f32x4{0.f, 0.f, 0.f, 0.f});
+                ub[g] = MA::from_acc(U);
+                const f32x4 O = MA::mma16(ac, ub[g], PQ[g]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = c * kRC + 4 * g4 + e;
+                    if (t < T) o[(row0 + t) * D + col + 16 * g] = (TIn)O[e];
+                }
+            }
+#pragma unroll
+            for (int rt = 0; rt < NRT; ++rt) {
+                const f32x4 gv = *(const f32x4*)&sm.gc[b3][16 * rt + 4 * g4];
+                const auto ae = MA::ld16(&sm.e[b3][16 * rt + cl][4 * g4]);
+#pragma unroll
+                for (int g = 0; g < 2; ++g) M[g][rt] = MA::mma16(ae, ub[g], M[g][rt] * gv);
+            }
+        };
+        loadv(0, vc);
+        for (int j = 0; j < nch + 2; ++j) {
+            if (j >= 2) {
+                const int c = j - 2;
+                if (c + 1 < nch) loadv(c + 1, vn);
+                state(c, vc);
+#pragma unroll
+                for (int g = 0; g < 2; ++g)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) vc[g][e] = vn[g][e];
+            }
+            lds_barrier();
+        }
+        if (p.etaT) {
+#pragma unroll
+            for (int g = 0; g < 2; ++g)
+#pragma unroll
+                for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        p.etaT[((size_t)bh * D + 16 * rt + 4 * g4 + e) * D + col + 16 * g] = M[g][rt][e];
+        }
+    }
+}
+
+template <typename TIn, int D>
+void launch(const FwdArgs& a, hipStream_t s) {
+    constexpr int NVT = D / kRcDVT;
+    const int nbh = a.B * a.H;
+    const dim3 grid((unsigned)(NVT == 1 ? nbh : (nbh + 7) / 8 * 8 * NVT));
+    hipLaunchKernelGGL((kla_fwd_residual_chunk_kernel<TIn, D>), grid, dim3(RcRoles<D>::NW * 64), 0, s, a);
+}
+
+}  // namespace
+
+bool fwd_residual_chunk_supported(int dk, int dv, int cov) {
+    const char* env = getenv("KLA_RES_IMPL");
+    if (env && env[0] == 'b') return false;  // KLA_RES_IMPL=block
+    return cov == 0 && dk == dv && (dk == 64 || dk == 128);
+}
+
+hipError_t launch_fwd_residual_chunk(const FwdArgs& a, int dtype, hipStream_t s) {
+    if (!(a.dk == a.dv && (a.dk == 64 || a.dk == 128)) || a.T < 1) return hipErrorInvalidValue;
+    if (dtype == DT_BF16) {
+        if (a.dk == 64) launch<bf16, 64>(a, s);
+        else launch<bf16, 128>(a, s);
+    } else {
+        if (a.dk == 64) launch<float, 64>(a, s);
+        else launch<float, 128>(a, s);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace kla
