@@ -56,9 +56,12 @@ constexpr int kRcDVT = 64;              // value columns per workgroup
 template <int D>
 struct RcRoles {
     static constexpr int NCW = D / 64;  // chain waves
-    static constexpr int NPW = 2;       // prep waves
     static constexpr int NSW = 2;       // state waves
-    static constexpr int NW = NCW + NPW + NSW;
+    static constexpr int NPW = 2;       // prep waves
+    static constexpr int NW = NCW + NSW + NPW;
+    // waves go round-robin over the four SIMDs: chain waves first, then the
+    // state waves, so that the two never share a SIMD at dk 128
+    static constexpr int W_STATE = NCW, W_PREP = NCW + NSW;
 };
 
 // S: operand storage (bf16, or fp32 split into bf16 pairs at the read).
@@ -67,7 +70,8 @@ struct RcRoles {
 template <typename S, int D>
 struct RcSm {
     static constexpr int NCW = D / 64;
-    static constexpr int KP = D + 16 / (int)sizeof(S);
+    static constexpr int PAD = 16 / (int)sizeof(S);
+    static constexpr int KP = D + PAD;
     alignas(16) S kt[3][kRC][KP];                 // K~ rows
     alignas(16) S qt[3][kRC][KP];                 // Q~ rows
     alignas(16) S ch[2][kRC][KP];                 // C^ rows (zero off the factorisation)
@@ -75,9 +79,18 @@ struct RcSm {
     alignas(16) S tp[2][kRC][kRCP];               // T'
     alignas(16) S cp[2][kRC][kRCP];               // C' = lower(Q~ C^T)
     alignas(16) float gc[3][D];                   // Gam_C
-    alignas(16) float den[2][NCW][kRC];           // partial sums of k.c (+ r in wave 0)
-    alignas(16) float gx[2][NCW][kRC][2 * kRC];   // exact sums [t][s] (K~ C^T), [t][kRC + s] (Q~ C^T)
+    alignas(16) float rr[2][kRC];                 // r of the chunk's tokens
+    alignas(16) float gx[2][NCW][kRC][2 * kRC];   // exact sums [t][s] (K~ C^T, s <= t), [t][kRC + s] (Q~ C^T)
     alignas(16) float nt[kRC][4][4];              // N as [t][s % 4][s / 4]
+    alignas(16) float dn[kRC];                    // den of the chunk's tokens
+    // staging of a chunk's input rows (loaded one chunk ahead into
+    // registers): per chain wave its 64 key dims of k, q, a; per state wave
+    // its 32 columns of v, then of o
+    alignas(16) S rk[NCW][kRC][64 + PAD];
+    alignas(16) S rq[NCW][kRC][64 + PAD];
+    alignas(16) float ra[NCW][kRC][64 + 4];
+    alignas(16) S sv[2][kRC][32 + PAD];
+    alignas(16) S ost[2][kRC][32 + PAD];
     int off[2][NCW];                              // chain wave off the factorisation
 };
 
@@ -100,6 +113,22 @@ __device__ __forceinline__ typename Frag<S>::V frag_acc(f32x4 lo, f32x4 hi) {
     }
 }
 
+// LDS written by some lanes of a wave and then read by others of the same
+// wave: order the accesses (the LDS executes a wave's instructions in order).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
+// Rows [t0, t0 + n) x columns [c0, c0 + ncol) of a row-major [., D] array as
+// a buffer resource of exactly those rows (loads past them read zero, stores
+// past them are dropped).
+template <typename T>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const T* base, size_t row, int n, int D) {
+    return make_rsrc(base + row * D, n * D * (int)sizeof(T));
+}
+
 template <typename TIn, int D>
 __global__ __launch_bounds__(RcRoles<D>::NW * 64) void kla_fwd_residual_chunk_kernel(FwdArgs p) {
     typedef RcRoles<D> R;
@@ -108,6 +137,7 @@ __global__ __launch_bounds__(RcRoles<D>::NW * 64) void kla_fwd_residual_chunk_ke
     typedef Frag<S> F;     // K32 operands
     typedef Mma<TIn> MA;   // K16 operands
     constexpr int NVT = D / kRcDVT;
+    constexpr int ES = (int)sizeof(TIn);
     __shared__ Sm sm;
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -119,50 +149,76 @@ __global__ __launch_bounds__(RcRoles<D>::NW * 64) void kla_fwd_residual_chunk_ke
     const int h = bh % p.H;
     const int T = p.T, nch = (T + kRC - 1) / kRC;
     const size_t row0 = (size_t)bh * T;
-    const TIn* q = (const TIn*)p.q;
-    const TIn* k = (const TIn*)p.k;
-    const TIn* v = (const TIn*)p.v;
-    TIn* o = (TIn*)p.o;
+    auto nvalid = [&](int c) { return T - c * kRC < kRC ? T - c * kRC : kRC; };
 
     if (wave < R::NCW) {
         // ---------------- chain: one lane per key dim
         const int cw = wave, i = 64 * cw + lane;
         float l = p.l0 ? p.l0[(size_t)bh * D + i] : 1.f;
         const float qn = p.qn[(size_t)h * D + i];
-        struct In {
-            TIn k[kRC], q[kRC];
-            float a[kRC], r[kRC];
+        // a chunk's rows of the wave's 64 key dims, 16-byte pieces: lane l
+        // loads token l/4, dims 16 (l%4) .. +15 of k, q and a, and r of token l%16
+        const int lt = lane >> 2, ld = 16 * (lane & 3);
+        constexpr int NKL = ES;  // 16-byte pieces of 16 values of k (or q)
+        struct Raw {
+            i32x4 k[NKL], q[NKL], a[4];
+            float r;
         };
-        auto load = [&](int c, In& x) {
+        auto load = [&](int c, Raw& x) {
+            const int nv = nvalid(c);
+            const size_t r0 = row0 + (size_t)c * kRC;
+            const auto rk = rows_rsrc((const TIn*)p.k, r0, nv, D);
+            const auto rq = rows_rsrc((const TIn*)p.q, r0, nv, D);
+            const auto ra = rows_rsrc(p.a, r0, nv, D);
+            const auto rr = make_rsrc(p.r + r0, nv * 4);
+            const int ko = (lt * D + 64 * cw + ld) * ES;
+#pragma unroll
+            for (int h = 0; h < NKL; ++h) {
+                x.k[h] = buf_load<i32x4>(rk, ko + 16 * h);
+                x.q[h] = buf_load<i32x4>(rq, ko + 16 * h);
+            }
+#pragma unroll
+            for (int h4 = 0; h4 < 4; ++h4) x.a[h4] = buf_load<i32x4>(ra, (lt * D + 64 * cw + ld + 4 * h4) * 4);
+            x.r = buf_load<float>(rr, (lane & 15) * 4);
+        };
+        // (fp32) rows past the sequence's end load as zero
+        auto stage = [&](const Raw& x) {
+#pragma unroll
+            for (int h = 0; h < NKL; ++h) {
+                *(i32x4*)&sm.rk[cw][lt][ld + (16 / ES) * h] = x.k[h];
+                *(i32x4*)&sm.rq[cw][lt][ld + (16 / ES) * h] = x.q[h];
+            }
+#pragma unroll
+            for (int h4 = 0; h4 < 4; ++h4) *(i32x4*)&sm.ra[cw][lt][ld + 4 * h4] = x.a[h4];
+        };
+        auto chain = [&](int c, float rlane) {
+            const int b3 = c % 3, b2 = c & 1;
+            float kf[kRC], qf[kRC], af[kRC], cv[kRC], gm[kRC];
+            // every staged value first (one batch of LDS reads), then the
+            // recursion; rows past the sequence's end hold zeros, their decay is 1
 #pragma unroll
             for (int u = 0; u < kRC; ++u) {
-                const int t = c * kRC + u < T ? c * kRC + u : T - 1;
-                const size_t idx = (row0 + t) * D + i;
-                x.k[u] = k[idx];
-                x.q[u] = q[idx];
-                x.a[u] = p.a[idx];
-                x.r[u] = p.r[row0 + t];
+                kf[u] = (float)sm.rk[cw][u][lane];
+                qf[u] = (float)sm.rq[cw][u][lane];
+                af[u] = sm.ra[cw][u][lane];
             }
-        };
-        auto chain = [&](int c, const In& x) {
-            const int b3 = c % 3, b2 = c & 1;
-            float kf[kRC], qf[kRC], af[kRC], cv[kRC], gm[kRC], dk[kRC];
+            const int nv = nvalid(c);
+#pragma unroll
+            for (int u = 0; u < kRC; ++u) af[u] = u < nv ? af[u] : 1.f;
+            const float rv = lane < nv ? rlane : 1.f;
+            if (cw == 0 && lane < kRC) sm.rr[b2][lane] = rv;
+            const float irl = fast_rcp(rv);
             float gam = 1.f;
             bool ok = true;
 #pragma unroll
             for (int u = 0; u < kRC; ++u) {
-                const bool in = c * kRC + u < T;
-                kf[u] = in ? (float)x.k[u] : 0.f;
-                qf[u] = in ? (float)x.q[u] : 0.f;
-                af[u] = in ? x.a[u] : 1.f;
-                const float ru = in ? x.r[u] : 1.f;
+                const float ir = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, irl), u));
                 const float lp = l * fast_rcp(__builtin_fmaf(qn, l, af[u] * af[u]));
                 cv[u] = kf[u] * fast_rcp(lp);
-                if (in) l = __builtin_fmaf(kf[u] * kf[u], fast_rcp(ru), lp);
+                l = u < nv ? __builtin_fmaf(kf[u] * kf[u], ir, lp) : l;
                 gam *= af[u];
                 gm[u] = gam;
                 ok = ok && gam >= kGamLo && gam <= kGamHi;
-                dk[u] = __builtin_fmaf(kf[u], cv[u], i == 0 ? ru : 0.f);
                 sm.kt[b3][u][i] = (S)(gam * kf[u]);
                 sm.qt[b3][u][i] = (S)(gam * qf[u]);
             }
@@ -183,13 +239,8 @@ __global__ __launch_bounds__(RcRoles<D>::NW * 64) void kla_fwd_residual_chunk_ke
             const bool fac = __all(ok);
 #pragma unroll
             for (int u = 0; u < kRC; ++u) sm.ch[b2][u][i] = fac ? (S)(cv[u] * fast_rcp(gm[u])) : (S)0.f;
-            {
-                int base = 0;
-                reduce_scatter<kRC, 32>(dk, lane, base);
-                if ((lane & 3) == 0) sm.den[b2][cw][base] = dk[0];
-            }
             if (!fac) {
-                // this wave's key dims, exactly: D(s,t) k_t c_s (s < t) and D(s,t) q_t c_s (s <= t)
+                // this wave's key dims, exactly: D(s,t) k_t c_s and D(s,t) q_t c_s (s <= t)
 #pragma unroll
                 for (int t = 0; t < kRC; ++t) {
                     float w[2 * kRC];
@@ -202,7 +253,7 @@ __global__ __launch_bounds__(RcRoles<D>::NW * 64) void kla_fwd_residual_chunk_ke
                             continue;
                         }
                         if (s < t) dst *= af[s + 1];
-                        w[s] = s < t ? dst * kf[t] * cv[s] : 0.f;
+                        w[s] = dst * kf[t] * cv[s];
                         w[kRC + s] = dst * qf[t] * cv[s];
                     }
                     int base = 0;
@@ -213,20 +264,25 @@ __global__ __launch_bounds__(RcRoles<D>::NW * 64) void kla_fwd_residual_chunk_ke
             if (lane == 0) sm.off[b2][cw] = fac ? 0 : 1;
         };
 
-        In cur, nxt;
-        load(0, cur);
+        // iteration j: stage chunk j (its loads were issued at iteration
+        // j - 1), issue the loads of chunk j + 1 into the same registers,
+        // run the chain on chunk j
+        Raw x;
+        load(0, x);
         for (int j = 0; j < nch + 2; ++j) {
             if (j < nch) {
-                if (j + 1 < nch) load(j + 1, nxt);
-                chain(j, cur);
-                cur = nxt;
+                stage(x);
+                const float rl = x.r;
+                if (j + 1 < nch) load(j + 1, x);
+                wave_lds_sync();
+                chain(j, rl);
             }
             lds_barrier();
         }
         if (p.lT && vt == 0) p.lT[(size_t)bh * D + i] = l;
-    } else if (wave < R::NCW + R::NPW) {
-        // ---------------- prep: Gram matrices, the inverse
-        const int pw = wave - R::NCW;
+    } else if (wave >= R::W_PREP) {
+        // ---------------- prep: Gram matrices, den, the inverse
+        const int pw = wave - R::W_PREP;
         const int cl = lane & 15, g4 = lane >> 4;
         auto prep = [&](int c) {
             const int b3 = c % 3, b2 = c & 1;
@@ -248,16 +304,15 @@ __global__ __launch_bounds__(RcRoles<D>::NW * 64) void kla_fwd_residual_chunk_ke
                 for (int e = 0; e < 4; ++e) sm.cp[b2][t0 + e][s] = (S)(s <= t0 + e ? G[e] : 0.f);
                 return;
             }
+            // den_s = (K~ C^T)[s][s] + r_s, from the lanes holding the diagonal
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                float dn = 0.f;
+            for (int e = 0; e < 4; ++e)
+                if (s == t0 + e) sm.dn[s] = G[e] + sm.rr[b2][s];
+            wave_lds_sync();
 #pragma unroll
-                for (int cw = 0; cw < R::NCW; ++cw) dn += sm.den[b2][cw][t0 + e];
-                sm.nt[t0 + e][s & 3][s >> 2] = s < t0 + e ? G[e] * fast_rcp(dn) : 0.f;
-            }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+            for (int e = 0; e < 4; ++e)
+                sm.nt[t0 + e][s & 3][s >> 2] = s < t0 + e ? G[e] * fast_rcp(sm.dn[t0 + e]) : 0.f;
+            wave_lds_sync();
             // S = (I + N)^-1 column j = lane / 4; lane phase ph holds rows ph + 4m
             const int j = lane >> 2, ph = lane & 3;
             float sv[4];
@@ -273,10 +328,7 @@ __global__ __launch_bounds__(RcRoles<D>::NW * 64) void kla_fwd_residual_chunk_ke
                 part += dpp_q<0x4E>(part);  // quad_perm [2,3,0,1]
                 if (ph == (t & 3) && t > j) sv[t >> 2] = -part;
             }
-            float dj = 0.f;
-#pragma unroll
-            for (int cw = 0; cw < R::NCW; ++cw) dj += sm.den[b2][cw][j];
-            const float rdj = fast_rcp(dj);
+            const float rdj = fast_rcp(sm.dn[j]);
 #pragma unroll
             for (int m = 0; m < 4; ++m) sm.tp[b2][ph + 4 * m][j] = (S)(sv[m] * rdj);
         };
@@ -286,30 +338,48 @@ __global__ __launch_bounds__(RcRoles<D>::NW * 64) void kla_fwd_residual_chunk_ke
         }
     } else {
         // ---------------- state: two 16-column groups per wave
-        const int sw = wave - R::NCW - R::NPW;
+        const int sw = wave - R::W_STATE;
         const int cl = lane & 15, g4 = lane >> 4;
-        const int col = vt * kRcDVT + 32 * sw + cl;  // + 16 g
+        const int col0 = vt * kRcDVT + 32 * sw;  // the wave's first value column
+        const int col = col0 + cl;               // + 16 g
         constexpr int NRT = D / 16;
         f32x4 M[2][NRT];
 #pragma unroll
         for (int g = 0; g < 2; ++g)
 #pragma unroll
-            for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    M[g][rt][e] = p.eta0 ? p.eta0[((size_t)bh * D + 16 * rt + 4 * g4 + e) * D + col + 16 * g] : 0.f;
-        TIn vc[2][4], vn[2][4];
-        auto loadv = [&](int c, TIn (&x)[2][4]) {
+            for (int rt = 0; rt < NRT; ++rt) M[g][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (p.eta0) {
 #pragma unroll
             for (int g = 0; g < 2; ++g)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int t = c * kRC + 4 * g4 + e < T ? c * kRC + 4 * g4 + e : T - 1;
-                    x[g][e] = v[(row0 + t) * D + col + 16 * g];
-                }
+                for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        M[g][rt][e] = p.eta0[((size_t)bh * D + 16 * rt + 4 * g4 + e) * D + col + 16 * g];
+        }
+        // the state's loads land here, so that inside the loop the only
+        // vector-memory operations in flight are the output stores
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        // 16-byte pieces of a chunk's 16 x 32 block of v (and of o): PR per
+        // token row, PL per lane
+        constexpr int PR = 32 * ES / 16, PL = kRC * PR / 64;
+        i32x4 vr[PL];
+        auto loadv = [&](int c) {
+            const auto rs = rows_rsrc((const TIn*)p.v, row0 + (size_t)c * kRC, nvalid(c), D);
+#pragma unroll
+            for (int pl = 0; pl < PL; ++pl) {
+                const int pc = lane + 64 * pl, tt = pc / PR, cq = pc % PR;
+                vr[pl] = buf_load<i32x4>(rs, (tt * D + col0) * ES + 16 * cq);
+            }
         };
-        auto state = [&](int c, const TIn (&x)[2][4]) {
+        auto state = [&](int c) {
             const int b3 = c % 3, b2 = c & 1;
+#pragma unroll
+            for (int pl = 0; pl < PL; ++pl) {
+                const int pc = lane + 64 * pl, tt = pc / PR, cq = pc % PR;
+                *(i32x4*)&sm.sv[sw][tt][cq * (16 / ES)] = vr[pl];
+            }
+            if (c + 1 < nch) loadv(c + 1);
             f32x4 PK[2], PQ[2];
 #pragma unroll
             for (int g = 0; g < 2; ++g) {
@@ -329,6 +399,7 @@ __global__ __launch_bounds__(RcRoles<D>::NW * 64) void kla_fwd_residual_chunk_ke
                     PQ[g] = F::mma(aq, bm, PQ[g]);
                 }
             }
+            wave_lds_sync();
             const auto at = MA::ld16(&sm.tp[b2][cl][4 * g4]);
             const auto ac = MA::ld16(&sm.cp[b2][cl][4 * g4]);
             typename MA::K16 ub[2];
@@ -336,14 +407,21 @@ __global__ __launch_bounds__(RcRoles<D>::NW * 64) void kla_fwd_residual_chunk_ke
             for (int g = 0; g < 2; ++g) {
                 f32x4 X;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) X[e] = (c * kRC + 4 * g4 + e < T ? (float)x[g][e] : 0.f) - PK[g][e];
+                for (int e = 0; e < 4; ++e) X[e] = (float)sm.sv[sw][4 * g4 + e][16 * g + cl] - PK[g][e];
                 const f32x4 U = MA::mma16(at, MA::from_acc(X), f32x4{0.f, 0.f, 0.f, 0.f});
                 ub[g] = MA::from_acc(U);
                 const f32x4 O = MA::mma16(ac, ub[g], PQ[g]);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int t = c * kRC + 4 * g4 + e;
-                    if (t < T) o[(row0 + t) * D + col + 16 * g] = (TIn)O[e];
+                for (int e = 0; e < 4; ++e) sm.ost[sw][4 * g4 + e][16 * g + cl] = (S)O[e];
+            }
+            wave_lds_sync();
+            {
+                // the chunk's rows of o: stores past token T - 1 fall outside the resource
+                const auto rs = rows_rsrc((TIn*)p.o, row0 + (size_t)c * kRC, nvalid(c), D);
+#pragma unroll
+                for (int pl = 0; pl < PL; ++pl) {
+                    const int pc = lane + 64 * pl, tt = pc / PR, cq = pc % PR;
+                    buf_store(*(const i32x4*)&sm.ost[sw][tt][cq * (16 / ES)], rs, (tt * D + col0) * ES + 16 * cq);
                 }
             }
 #pragma unroll
@@ -354,17 +432,9 @@ __global__ __launch_bounds__(RcRoles<D>::NW * 64) void kla_fwd_residual_chunk_ke
                 for (int g = 0; g < 2; ++g) M[g][rt] = MA::mma16(ae, ub[g], M[g][rt] * gv);
             }
         };
-        loadv(0, vc);
+        loadv(0);
         for (int j = 0; j < nch + 2; ++j) {
-            if (j >= 2) {
-                const int c = j - 2;
-                if (c + 1 < nch) loadv(c + 1, vn);
-                state(c, vc);
-#pragma unroll
-                for (int g = 0; g < 2; ++g)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) vc[g][e] = vn[g][e];
-            }
+            if (j >= 2) state(j - 2);
             lds_barrier();
         }
         if (p.etaT) {
