@@ -47,7 +47,7 @@ KERNEL_SOURCES = {
              "scan_amd/csrc/kla_fwd_seg.hip"] + _COMMON_SOURCES,
     "iso": ["scan_amd/csrc/kla_fwd_iso_pipe.hip", "scan_amd/csrc/kla_fwd_iso.hip"] + _COMMON_SOURCES,
     "short": ["scan_amd/csrc/kla_fwd_short.hip", "scan_amd/csrc/kla_short.h"] + _COMMON_SOURCES,
-    "residual": ["scan_amd/csrc/kla_fwd_residual.hip",
+    "residual": ["scan_amd/csrc/kla_fwd_residual.hip", "scan_amd/csrc/kla_fwd_residual_chunk.hip",
                  "scan_amd/csrc/kla_residual.h"] + _COMMON_SOURCES,
     "step": ["scan_amd/csrc/kla_step.hip"] + _COMMON_SOURCES,
     "bwd": ["scan_amd/csrc/kla_bwd.hip", "scan_amd/csrc/kla_bwd.h"] + _COMMON_SOURCES,
@@ -638,7 +638,9 @@ def main() -> int:
     fam = "residual" if residual else w.cov
     traffic = stored_traffic(w.name, fam)
     counters = stored_counters(w.name, fam)
-    kernel_name = ("kla_fwd_residual_kernel" if residual else
+    kernel_name = (("kla_fwd_residual_chunk_kernel (16-token chunks on the matrix cores)"
+                    if w.cov == "diag" and w.dk == w.dv and w.dk in (64, 128) else "kla_fwd_residual_kernel")
+                   if residual else
                    ("kla_fwd_diag_pipe_kernel (block prologue, value tiles)" +
                     (", sequence split" if w.B * w.H < 192 // 2 else "")) if blockw else
                    scan_amd.fwd_kernel_name(w.B, w.H, w.T, w.dk, w.dv, w.cov, w.dtype))
