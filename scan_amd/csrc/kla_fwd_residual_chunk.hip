@@ -181,7 +181,7 @@ __global__ __launch_bounds__(RcRoles<D>::NW * 64) void kla_fwd_residual_chunk_ke
             for (int h4 = 0; h4 < 4; ++h4) x.a[h4] = buf_load<i32x4>(ra, (lt * D + 64 * cw + ld + 4 * h4) * 4);
             x.r = buf_load<float>(rr, (lane & 15) * 4);
         };
-        // (fp32) rows past the sequence's end load as zero
+        // rows past the sequence's end load as zero
         auto stage = [&](const Raw& x) {
 #pragma unroll
             for (int h = 0; h < NKL; ++h) {
@@ -210,6 +210,7 @@ __global__ __launch_bounds__(RcRoles<D>::NW * 64) void kla_fwd_residual_chunk_ke
             const float irl = fast_rcp(rv);
             float gam = 1.f;
             bool ok = true;
+            float chv[kRC];  // C^ = c / Gam
 #pragma unroll
             for (int u = 0; u < kRC; ++u) {
                 const float ir = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, irl), u));
@@ -219,11 +220,27 @@ __global__ __launch_bounds__(RcRoles<D>::NW * 64) void kla_fwd_residual_chunk_ke
                 gam *= af[u];
                 gm[u] = gam;
                 ok = ok && gam >= kGamLo && gam <= kGamHi;
+                chv[u] = cv[u] * fast_rcp(gam);
                 sm.kt[b3][u][i] = (S)(gam * kf[u]);
                 sm.qt[b3][u][i] = (S)(gam * qf[u]);
+                sm.ch[b2][u][i] = (S)chv[u];
             }
             sm.gc[b3][i] = gam;
-            {
+            const bool fac = __all(ok);
+            auto put_e = [&](const float (&ev)[kRC]) {
+#pragma unroll
+                for (int u4 = 0; u4 < kRC; u4 += 4)
+                    *(typename Quad<S>::V*)&sm.e[b3][i][u4] =
+                        Quad<S>::make(f32x4{ev[u4], ev[u4 + 1], ev[u4 + 2], ev[u4 + 3]});
+            };
+            if (fac) {
+                // E_s = Gam_C c_s / Gam_s
+                float ev[kRC];
+#pragma unroll
+                for (int u = 0; u < kRC; ++u) ev[u] = gam * chv[u];
+                put_e(ev);
+            } else {
+                // E by products of decays, C^ rows zero
                 float ev[kRC];
                 float sfx = 1.f;
 #pragma unroll
@@ -231,15 +248,9 @@ __global__ __launch_bounds__(RcRoles<D>::NW * 64) void kla_fwd_residual_chunk_ke
                     ev[u] = sfx * cv[u];
                     sfx *= af[u];
                 }
+                put_e(ev);
 #pragma unroll
-                for (int u4 = 0; u4 < kRC; u4 += 4)
-                    *(typename Quad<S>::V*)&sm.e[b3][i][u4] =
-                        Quad<S>::make(f32x4{ev[u4], ev[u4 + 1], ev[u4 + 2], ev[u4 + 3]});
-            }
-            const bool fac = __all(ok);
-#pragma unroll
-            for (int u = 0; u < kRC; ++u) sm.ch[b2][u][i] = fac ? (S)(cv[u] * fast_rcp(gm[u])) : (S)0.f;
-            if (!fac) {
+                for (int u = 0; u < kRC; ++u) sm.ch[b2][u][i] = (S)0.f;
                 // this wave's key dims, exactly: D(s,t) k_t c_s and D(s,t) q_t c_s (s <= t)
 #pragma unroll
                 for (int t = 0; t < kRC; ++t) {
@@ -265,19 +276,24 @@ __global__ __launch_bounds__(RcRoles<D>::NW * 64) void kla_fwd_residual_chunk_ke
         };
 
         // iteration j: stage chunk j (its loads were issued at iteration
-        // j - 1), issue the loads of chunk j + 1 into the same registers,
-        // run the chain on chunk j
-        Raw x;
-        load(0, x);
-        for (int j = 0; j < nch + 2; ++j) {
+        // j - 2), issue chunk j + 2's loads into the registers just staged,
+        // run the chain on chunk j; two register sets in turn
+        Raw xa, xb;
+        load(0, xa);
+        if (nch > 1) load(1, xb);
+        auto step = [&](int j, Raw& x) {
             if (j < nch) {
                 stage(x);
                 const float rl = x.r;
-                if (j + 1 < nch) load(j + 1, x);
+                if (j + 2 < nch) load(j + 2, x);
                 wave_lds_sync();
                 chain(j, rl);
             }
             lds_barrier();
+        };
+        for (int j = 0; j < nch + 2; j += 2) {
+            step(j, xa);
+            if (j + 1 < nch + 2) step(j + 1, xb);
         }
         if (p.lT && vt == 0) p.lT[(size_t)bh * D + i] = l;
     } else if (wave >= R::W_PREP) {
