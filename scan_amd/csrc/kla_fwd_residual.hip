@@ -642,7 +642,7 @@ int fwd_residual_vtiles(int B, int H, int dk) {
 
 hipError_t launch_fwd_residual(const FwdArgs& a, int dtype, int cov, hipStream_t s) {
     if (!fwd_residual_supported(a.dk, a.dv) || a.T < 1) return hipErrorInvalidValue;
-    if (fwd_residual_chunk_supported(a.dk, a.dv, cov)) return launch_fwd_residual_chunk(a, dtype, s);
+    if (fwd_residual_chunk_supported(a.dk, a.dv, cov, dtype)) return launch_fwd_residual_chunk(a, dtype, cov, s);
     if (a.n_vtiles != 1 && !(a.n_vtiles == 2 && a.dk >= 64)) return hipErrorInvalidValue;
     if (dtype == DT_BF16) return cov ? dispatch<bf16, true>(a, s) : dispatch<bf16, false>(a, s);
     return cov ? dispatch<float, true>(a, s) : dispatch<float, false>(a, s);

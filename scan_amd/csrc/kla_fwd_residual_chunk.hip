@@ -1,7 +1,7 @@
 // kla_fwd_residual_chunk.hip -- gfx950 chunked forward of the residual-write
-// variant with diagonal precision ("Kalman Delta Networks: Uncertainty-aware
-// Associative Memory", abstract: the Kalman gain weights a write of the
-// residual; diagonal approximation), on the matrix cores.
+// variant ("Kalman Delta Networks: Uncertainty-aware Associative Memory",
+// abstract: the Kalman gain weights a write of the residual; diagonal and
+// isotropic approximations), on the matrix cores.
 //
 // Recurrence per (b,h) (the same as the block kernel of kla_fwd_residual.hip):
 //   lp = l / (a^2 + qn l),  c = k / lp,  den = k.c + r,  g = c / den
@@ -18,13 +18,19 @@
 // T' = (diag(den) + strictlower(K~ C^T))^{-1} -- depends on the inputs only
 // and runs one and two chunks ahead in other waves.
 //
+// Isotropic: the precision, decay and process noise are scalars per token,
+// c = k / lp and den = |k|^2 / lp + r; the same chunk algebra with a scalar
+// Gam_t.
+//
 // Roles (one workgroup per (b,h) and 64 value columns; tiles of one (b,h)
 // run 8 workgroups apart, on one XCD):
-// - chain waves (dk/64, one lane per key dim): the precision recursion, the
-//   rows of K~, Q~, C^, E and Gam_C in LDS, and per-token partial sums of
-//   den;
+// - chain waves (diagonal: dk/64, one lane per key dim; isotropic: one wave,
+//   key dims lane + 64 m, |k_t|^2 by a wave reduction and the scalar
+//   recursion in every lane): the precision recursion and the rows of K~, Q~,
+//   C^, E and Gam_C in LDS;
 // - prep waves (2): the Gram matrices on the matrix cores (wave 0 K~ C^T,
-//   wave 1 Q~ C^T), and in wave 0 the inverse of the unit lower triangular
+//   wave 1 Q~ C^T), den = diag(K~ C^T) + r, and in wave 0 the inverse of the
+//   unit lower triangular
 //   I + N, N = diag(den)^-1 strictlower(K~ C^T), by forward substitution
 //   (a column per lane quad), scaled to T';
 // - state waves (2, 32 value columns each as two 16-column groups): per
@@ -53,9 +59,9 @@ constexpr int kRCP = kRC + 4;           // padded row of the [.][kRC] arrays
 constexpr float kGamLo = 0x1p-64f, kGamHi = 0x1p64f;  // range of Gam for C^ = c / Gam
 constexpr int kRcDVT = 64;              // value columns per workgroup
 
-template <int D>
+template <int D, bool ISO>
 struct RcRoles {
-    static constexpr int NCW = D / 64;  // chain waves
+    static constexpr int NCW = ISO ? 1 : D / 64;  // chain waves (isotropic: one, a scalar precision)
     static constexpr int NSW = 2;       // state waves
     static constexpr int NPW = 2;       // prep waves
     static constexpr int NW = NCW + NSW + NPW;
@@ -67,9 +73,10 @@ struct RcRoles {
 // S: operand storage (bf16, or fp32 split into bf16 pairs at the read).
 // Token-major rows are padded by 16 bytes and the [.][kRC] rows by 4 values,
 // so that the 16 rows a fragment read touches fall in distinct banks.
-template <typename S, int D>
+template <typename S, int D, bool ISO>
 struct RcSm {
-    static constexpr int NCW = D / 64;
+    static constexpr int NCW = RcRoles<D, ISO>::NCW;
+    static constexpr int DW = ISO ? D : 64;       // key dims per chain wave
     static constexpr int PAD = 16 / (int)sizeof(S);
     static constexpr int KP = D + PAD;
     alignas(16) S kt[3][kRC][KP];                 // K~ rows
@@ -86,9 +93,9 @@ struct RcSm {
     // staging of a chunk's input rows (loaded one chunk ahead into
     // registers): per chain wave its 64 key dims of k, q, a; per state wave
     // its 32 columns of v, then of o
-    alignas(16) S rk[NCW][kRC][64 + PAD];
-    alignas(16) S rq[NCW][kRC][64 + PAD];
-    alignas(16) float ra[NCW][kRC][64 + 4];
+    alignas(16) S rk[NCW][kRC][DW + PAD];
+    alignas(16) S rq[NCW][kRC][DW + PAD];
+    alignas(16) float ra[NCW][kRC][ISO ? 4 : 64 + 4];   // diagonal decays
     alignas(16) S sv[2][kRC][32 + PAD];
     alignas(16) S ost[2][kRC][32 + PAD];
     int off[2][NCW];                              // chain wave off the factorisation
@@ -129,11 +136,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const T* base, size_
     return make_rsrc(base + row * D, n * D * (int)sizeof(T));
 }
 
-template <typename TIn, int D>
-__global__ __launch_bounds__(RcRoles<D>::NW * 64) void kla_fwd_residual_chunk_kernel(FwdArgs p) {
-    typedef RcRoles<D> R;
+template <typename TIn, int D, bool ISO>
+__global__ __launch_bounds__((RcRoles<D, ISO>::NW * 64)) void kla_fwd_residual_chunk_kernel(FwdArgs p) {
+    typedef RcRoles<D, ISO> R;
     typedef TIn S;
-    typedef RcSm<S, D> Sm;
+    typedef RcSm<S, D, ISO> Sm;
     typedef Frag<S> F;     // K32 operands
     typedef Mma<TIn> MA;   // K16 operands
     constexpr int NVT = D / kRcDVT;
@@ -152,6 +159,170 @@ __global__ __launch_bounds__(RcRoles<D>::NW * 64) void kla_fwd_residual_chunk_ke
     auto nvalid = [&](int c) { return T - c * kRC < kRC ? T - c * kRC : kRC; };
 
     if (wave < R::NCW) {
+      if constexpr (ISO) {
+        // ---------------- chain (isotropic): one wave, lane holds key dims lane + 64 m;
+        // the precision, decay and process noise are scalars per token, the
+        // same in every lane
+        constexpr int NDL = D / 64;
+        float l = p.l0 ? p.l0[bh] : 1.f;
+        // a chunk's k, q rows as 16-byte pieces: PRW per row, NP per lane
+        constexpr int PRW = D * ES / 16, NP = kRC * PRW / 64;
+        struct RawI {
+            i32x4 k[NP], q[NP];
+            float a, qn, r;  // of token lane % 16
+        };
+        auto load = [&](int c, RawI& x) {
+            const int nv = nvalid(c);
+            const size_t r0 = row0 + (size_t)c * kRC;
+            const auto rk = rows_rsrc((const TIn*)p.k, r0, nv, D);
+            const auto rq = rows_rsrc((const TIn*)p.q, r0, nv, D);
+#pragma unroll
+            for (int m = 0; m < NP; ++m) {
+                const int pc = lane + 64 * m, t = pc / PRW, pe = pc % PRW;
+                x.k[m] = buf_load<i32x4>(rk, t * D * ES + 16 * pe);
+                x.q[m] = buf_load<i32x4>(rq, t * D * ES + 16 * pe);
+            }
+            x.a = buf_load<float>(make_rsrc(p.a + r0, nv * 4), (lane & 15) * 4);
+            x.qn = buf_load<float>(make_rsrc(p.qn + r0, nv * 4), (lane & 15) * 4);
+            x.r = buf_load<float>(make_rsrc(p.r + r0, nv * 4), (lane & 15) * 4);
+        };
+        auto stage = [&](const RawI& x) {
+#pragma unroll
+            for (int m = 0; m < NP; ++m) {
+                const int pc = lane + 64 * m, t = pc / PRW, pe = pc % PRW;
+                *(i32x4*)&sm.rk[0][t][pe * (16 / ES)] = x.k[m];
+                *(i32x4*)&sm.rq[0][t][pe * (16 / ES)] = x.q[m];
+            }
+        };
+        auto uni = [&](float v, int u) {
+            return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), u));
+        };
+        auto chain = [&](int c, float a_l, float qn_l, float r_l) {
+            const int b3 = c % 3, b2 = c & 1;
+            const int nv = nvalid(c);
+            float kf[NDL][kRC], qf[NDL][kRC];
+#pragma unroll
+            for (int u = 0; u < kRC; ++u)
+#pragma unroll
+                for (int m = 0; m < NDL; ++m) {
+                    kf[m][u] = (float)sm.rk[0][u][lane + 64 * m];
+                    qf[m][u] = (float)sm.rq[0][u][lane + 64 * m];
+                }
+            // token scalars (rows past the sequence's end: a = 1, r = 1, qn = 0)
+            const bool lv = (lane & 15) < nv;
+            const float av = lv ? a_l : 1.f, qv = lv ? qn_l : 0.f, rv = lv ? r_l : 1.f;
+            if (lane < kRC) sm.rr[b2][lane] = rv;
+            const float irv = fast_rcp(rv) * (1.f / (float)D);
+            // |k_t|^2 over the key dims: a reduce-scatter leaves token
+            // 8 b5 + 4 b4 + 2 b3 + b2 in lanes with those lane bits
+            float ks[kRC];
+#pragma unroll
+            for (int u = 0; u < kRC; ++u) {
+                ks[u] = kf[0][u] * kf[0][u];
+#pragma unroll
+                for (int m = 1; m < NDL; ++m) ks[u] = __builtin_fmaf(kf[m][u], kf[m][u], ks[u]);
+            }
+            int base = 0;
+            reduce_scatter<kRC, 32>(ks, lane, base);
+            float cv[NDL][kRC], chv[NDL][kRC];
+            float gam = 1.f;
+            bool ok = true;
+#pragma unroll
+            for (int u = 0; u < kRC; ++u) {
+                const int ol = ((u >> 3) & 1) << 5 | ((u >> 2) & 1) << 4 | ((u >> 1) & 1) << 3 | (u & 1) << 2;
+                const float ksq = uni(ks[0], ol), au = uni(av, u);
+                const float lp = l * fast_rcp(__builtin_fmaf(uni(qv, u), l, au * au));
+                const float rlp = fast_rcp(lp);
+                l = u < nv ? __builtin_fmaf(ksq, uni(irv, u), lp) : l;
+                gam *= au;
+                ok = ok && gam >= kGamLo && gam <= kGamHi;
+                const float igam = fast_rcp(gam);
+#pragma unroll
+                for (int m = 0; m < NDL; ++m) {
+                    const int i = lane + 64 * m;
+                    cv[m][u] = kf[m][u] * rlp;
+                    chv[m][u] = cv[m][u] * igam;
+                    sm.kt[b3][u][i] = (S)(gam * kf[m][u]);
+                    sm.qt[b3][u][i] = (S)(gam * qf[m][u]);
+                    sm.ch[b2][u][i] = (S)chv[m][u];
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < NDL; ++m) sm.gc[b3][lane + 64 * m] = gam;
+            const bool fac = __all(ok);
+#pragma unroll
+            for (int m = 0; m < NDL; ++m) {
+                float ev[kRC];
+                if (fac) {
+#pragma unroll
+                    for (int u = 0; u < kRC; ++u) ev[u] = gam * chv[m][u];
+                } else {
+                    float sfx = 1.f;
+#pragma unroll
+                    for (int u = kRC - 1; u >= 0; --u) {
+                        ev[u] = sfx * cv[m][u];
+                        sfx *= uni(av, u);
+                    }
+                }
+#pragma unroll
+                for (int u4 = 0; u4 < kRC; u4 += 4)
+                    *(typename Quad<S>::V*)&sm.e[b3][lane + 64 * m][u4] =
+                        Quad<S>::make(f32x4{ev[u4], ev[u4 + 1], ev[u4 + 2], ev[u4 + 3]});
+            }
+            if (!fac) {
+                // exactly: D(s,t) k_t.c_s and D(s,t) q_t.c_s (s <= t), D a scalar product
+#pragma unroll
+                for (int u = 0; u < kRC; ++u)
+#pragma unroll
+                    for (int m = 0; m < NDL; ++m) sm.ch[b2][u][lane + 64 * m] = (S)0.f;
+#pragma unroll
+                for (int t = 0; t < kRC; ++t) {
+                    float w[2 * kRC];
+                    float dst = 1.f;
+#pragma unroll
+                    for (int s2 = kRC - 1; s2 >= 0; --s2) {
+                        if (s2 > t) {
+                            w[s2] = 0.f;
+                            w[kRC + s2] = 0.f;
+                            continue;
+                        }
+                        if (s2 < t) dst *= uni(av, s2 + 1);
+                        float sk = 0.f, sq = 0.f;
+#pragma unroll
+                        for (int m = 0; m < NDL; ++m) {
+                            sk = __builtin_fmaf(kf[m][t], cv[m][s2], sk);
+                            sq = __builtin_fmaf(qf[m][t], cv[m][s2], sq);
+                        }
+                        w[s2] = dst * sk;
+                        w[kRC + s2] = dst * sq;
+                    }
+                    int b = 0;
+                    reduce_scatter<2 * kRC, 32>(w, lane, b);
+                    if ((lane & 1) == 0) sm.gx[b2][0][t][b] = w[0];
+                }
+            }
+            if (lane == 0) sm.off[b2][0] = fac ? 0 : 1;
+        };
+
+        RawI xa, xb;
+        load(0, xa);
+        if (nch > 1) load(1, xb);
+        auto step = [&](int j, RawI& x) {
+            if (j < nch) {
+                stage(x);
+                const float a_l = x.a, qn_l = x.qn, r_l = x.r;
+                if (j + 2 < nch) load(j + 2, x);
+                wave_lds_sync();
+                chain(j, a_l, qn_l, r_l);
+            }
+            lds_barrier();
+        };
+        for (int j = 0; j < nch + 2; j += 2) {
+            step(j, xa);
+            if (j + 1 < nch + 2) step(j + 1, xb);
+        }
+        if (p.lT && vt == 0 && lane == 0) p.lT[bh] = l;
+      } else {
         // ---------------- chain: one lane per key dim
         const int cw = wave, i = 64 * cw + lane;
         float l = p.l0 ? p.l0[(size_t)bh * D + i] : 1.f;
@@ -296,6 +467,7 @@ __global__ __launch_bounds__(RcRoles<D>::NW * 64) void kla_fwd_residual_chunk_ke
             if (j + 1 < nch + 2) step(j + 1, xb);
         }
         if (p.lT && vt == 0) p.lT[(size_t)bh * D + i] = l;
+      }
     } else if (wave >= R::W_PREP) {
         // ---------------- prep: Gram matrices, den, the inverse
         const int pw = wave - R::W_PREP;
@@ -465,31 +637,37 @@ __global__ __launch_bounds__(RcRoles<D>::NW * 64) void kla_fwd_residual_chunk_ke
     }
 }
 
-template <typename TIn, int D>
+template <typename TIn, int D, bool ISO>
 void launch(const FwdArgs& a, hipStream_t s) {
     constexpr int NVT = D / kRcDVT;
     const int nbh = a.B * a.H;
     const dim3 grid((unsigned)(NVT == 1 ? nbh : (nbh + 7) / 8 * 8 * NVT));
-    hipLaunchKernelGGL((kla_fwd_residual_chunk_kernel<TIn, D>), grid, dim3(RcRoles<D>::NW * 64), 0, s, a);
+    hipLaunchKernelGGL((kla_fwd_residual_chunk_kernel<TIn, D, ISO>), grid, dim3(RcRoles<D, ISO>::NW * 64), 0, s, a);
+}
+
+template <typename TIn, bool ISO>
+void launch_d(const FwdArgs& a, hipStream_t s) {
+    if constexpr (ISO && sizeof(TIn) == 4) {
+        launch<TIn, 64, ISO>(a, s);  // fp32 isotropic dk 128 stays on the block kernel
+    } else {
+        if (a.dk == 64) launch<TIn, 64, ISO>(a, s);
+        else launch<TIn, 128, ISO>(a, s);
+    }
 }
 
 }  // namespace
 
-bool fwd_residual_chunk_supported(int dk, int dv, int cov) {
+bool fwd_residual_chunk_supported(int dk, int dv, int cov, int dtype) {
     const char* env = getenv("KLA_RES_IMPL");
     if (env && env[0] == 'b') return false;  // KLA_RES_IMPL=block
-    return cov == 0 && dk == dv && (dk == 64 || dk == 128);
+    // fp32 isotropic dk 128: the chain wave's two input register sets would spill
+    return dk == dv && (dk == 64 || (dk == 128 && !(cov && dtype != DT_BF16)));
 }
 
-hipError_t launch_fwd_residual_chunk(const FwdArgs& a, int dtype, hipStream_t s) {
-    if (!(a.dk == a.dv && (a.dk == 64 || a.dk == 128)) || a.T < 1) return hipErrorInvalidValue;
-    if (dtype == DT_BF16) {
-        if (a.dk == 64) launch<bf16, 64>(a, s);
-        else launch<bf16, 128>(a, s);
-    } else {
-        if (a.dk == 64) launch<float, 64>(a, s);
-        else launch<float, 128>(a, s);
-    }
+hipError_t launch_fwd_residual_chunk(const FwdArgs& a, int dtype, int cov, hipStream_t s) {
+    if (!fwd_residual_chunk_supported(a.dk, a.dv, cov, dtype) || a.T < 1) return hipErrorInvalidValue;
+    if (dtype == DT_BF16) cov ? launch_d<bf16, true>(a, s) : launch_d<bf16, false>(a, s);
+    else cov ? launch_d<float, true>(a, s) : launch_d<float, false>(a, s);
     return hipGetLastError();
 }
 

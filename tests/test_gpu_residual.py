@@ -3,8 +3,9 @@ ABI) against the fp64 oracle (oracle.fwd_residual), on seeded inputs from
 scan_amd.inputs.  Small cases compare every element; the LM-layer shape
 compares sampled (b,h) sequences.  Parity metric and bars as the KLA
 forward (tests.gpu_util).  Diagonal dk 64 / 128 run the chunked matrix-core
-kernel (exact sums where the decay products leave its range); the rest, and
-those shapes under KLA_RES_IMPL=block, the block kernel."""
+kernel (exact sums where the decay products leave its range), and so do
+isotropic dk 64 / 128 (fp32 at 64 only); the rest, and those shapes under
+KLA_RES_IMPL=block, the block kernel."""
 import numpy as np
 import pytest
 import torch
@@ -202,17 +203,20 @@ def test_residual_many_heads_d128(cov):
     assert_parity(compare(got, ref, nlead=1), "bf16", f"residual many heads {cov}")
 
 
+@pytest.mark.parametrize("cov", ["diag", "iso"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("d", [64, 128])
-def test_residual_chunk_ragged_grid_every_sequence(dtype, d):
+def test_residual_chunk_ragged_grid_every_sequence(cov, dtype, d):
     """19 (b,h), so the 8-apart value tiles leave padding workgroups; chunks of
-    16 with a ragged last one; every sequence against the oracle."""
-    _print_case("chunk grid", dtype, d)
-    inp = gen.make_inputs("small_diag", seed=150 + d, B=1, H=19, T=41, dk=d, dv=d, dtype=dtype)
+    16 with a ragged last one; every sequence against the oracle (fp32
+    isotropic d 128 runs the block kernel)."""
+    _print_case("chunk grid", cov, dtype, d)
+    base = "small_diag" if cov == "diag" else "iso"
+    inp = gen.make_inputs(base, seed=150 + d, B=1, H=19, T=41, dk=d, dv=d, dtype=dtype)
     st = gen.make_state(inp["workload"], seed=23)
-    hip = run_hip_res(inp, "diag", st["l0"], st["eta0"])
-    ref = run_oracle_res(inp, "diag", st["l0"], st["eta0"])
-    assert_parity(compare(hip, ref), dtype, f"residual chunk grid {dtype} d={d}")
+    hip = run_hip_res(inp, cov, st["l0"], st["eta0"])
+    ref = run_oracle_res(inp, cov, st["l0"], st["eta0"])
+    assert_parity(compare(hip, ref), dtype, f"residual chunk grid {cov} {dtype} d={d}")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -234,15 +238,17 @@ def test_residual_chunk_partial_fallback(dtype):
     assert_parity(compare(hip, ref), dtype, f"residual chunk partial fallback {dtype}")
 
 
-def test_residual_chunk_matches_block_kernel(monkeypatch):
+@pytest.mark.parametrize("cov", ["diag", "iso"])
+def test_residual_chunk_matches_block_kernel(cov, monkeypatch):
     """The chunked kernel and the block kernel (KLA_RES_IMPL=block) agree on
     the LM-layer draws within the bf16 bar (both also meet the oracle)."""
-    _print_case("chunk vs block")
-    inp = gen.make_inputs(gen.RESIDUAL, seed=3, B=2, H=4, T=300)
-    chunk = run_hip_res(inp, "diag")
+    _print_case("chunk vs block", cov)
+    inp = gen.make_inputs(gen.RESIDUAL if cov == "diag" else "iso", seed=3, B=2, H=4, T=300,
+                          dk=128, dv=128, dtype="bf16")
+    chunk = run_hip_res(inp, cov)
     monkeypatch.setenv("KLA_RES_IMPL", "block")
-    block = run_hip_res(inp, "diag")
-    ref = run_oracle_res(inp, "diag")
+    block = run_hip_res(inp, cov)
+    ref = run_oracle_res(inp, cov)
     assert_parity(compare(chunk, ref), "bf16", "residual chunk vs oracle")
     assert_parity(compare(block, ref), "bf16", "residual block vs oracle")
     assert_parity(compare(chunk, block), "bf16", "residual chunk vs block")
