@@ -30,9 +30,8 @@
 //   C^, E and Gam_C in LDS;
 // - prep waves (2): the Gram matrices on the matrix cores (wave 0 K~ C^T,
 //   wave 1 Q~ C^T), den = diag(K~ C^T) + r, and in wave 0 the inverse of the
-//   unit lower triangular
-//   I + N, N = diag(den)^-1 strictlower(K~ C^T), by forward substitution
-//   (a column per lane quad), scaled to T';
+//   unit lower triangular I + N, N = diag(den)^-1 strictlower(K~ C^T), by
+//   forward substitution (a column per lane quad), scaled to T';
 // - state waves (2, 32 value columns each as two 16-column groups): per
 //   chunk [K~; Q~] M0, U' = T' (V - K~ M0), O = Q~ M0 + C' U' and the update,
 //   the state in accumulator tiles for the whole sequence.
@@ -43,7 +42,9 @@
 // [2^-64, 2^64] within a chunk writes zero C^ rows for its key dims and
 // instead forms their contribution to K~ C^T and Q~ C^T exactly, as sums of
 // D(s,t) k_t c_s and D(s,t) q_t c_s with D(s,t) = a_{s+1} ... a_t (products
-// only), which the prep waves add to the matrix-core Gram.
+// only), which the prep waves add to the matrix-core Gram; its E rows then
+// come from suffix products of the decays too (on the factorised path E is
+// Gam_C C^).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -66,7 +67,7 @@ struct RcRoles {
     static constexpr int NPW = 2;       // prep waves
     static constexpr int NW = NCW + NSW + NPW;
     // waves go round-robin over the four SIMDs: chain waves first, then the
-    // state waves, so that the two never share a SIMD at dk 128
+    // state waves, so that the two never share a SIMD
     static constexpr int W_STATE = NCW, W_PREP = NCW + NSW;
 };
 
@@ -90,9 +91,10 @@ struct RcSm {
     alignas(16) float gx[2][NCW][kRC][2 * kRC];   // exact sums [t][s] (K~ C^T, s <= t), [t][kRC + s] (Q~ C^T)
     alignas(16) float nt[kRC][4][4];              // N as [t][s % 4][s / 4]
     alignas(16) float dn[kRC];                    // den of the chunk's tokens
-    // staging of a chunk's input rows (loaded one chunk ahead into
-    // registers): per chain wave its 64 key dims of k, q, a; per state wave
-    // its 32 columns of v, then of o
+    // staging of a chunk's input rows (loaded into registers two chunks
+    // ahead by the chain waves, one by the state waves): per chain wave its
+    // key dims of k, q (and diagonal a); per state wave its 32 columns of v,
+    // then of o
     alignas(16) S rk[NCW][kRC][DW + PAD];
     alignas(16) S rq[NCW][kRC][DW + PAD];
     alignas(16) float ra[NCW][kRC][ISO ? 4 : 64 + 4];   // diagonal decays
@@ -128,9 +130,9 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
 }
 
-// Rows [t0, t0 + n) x columns [c0, c0 + ncol) of a row-major [., D] array as
-// a buffer resource of exactly those rows (loads past them read zero, stores
-// past them are dropped).
+// Rows [row, row + n) of a row-major [., D] array as a buffer resource of
+// exactly those rows (loads past them read zero, stores past them are
+// dropped).
 template <typename T>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const T* base, size_t row, int n, int D) {
     return make_rsrc(base + row * D, n * D * (int)sizeof(T));
