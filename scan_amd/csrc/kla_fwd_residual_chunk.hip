@@ -24,10 +24,10 @@
 //
 // Roles (one workgroup per (b,h) and 64 value columns; tiles of one (b,h)
 // run 8 workgroups apart, on one XCD):
-// - chain waves (diagonal: dk/64, one lane per key dim; isotropic: one wave,
-//   key dims lane + 64 m, |k_t|^2 by a wave reduction and the scalar
-//   recursion in every lane): the precision recursion and the rows of K~, Q~,
-//   C^, E and Gam_C in LDS;
+// - chain waves (dk/64, one lane per key dim; isotropic: each forms |k_t|^2
+//   over all key dims by a wave reduction and runs the scalar recursion in
+//   every lane): the precision recursion and the rows of K~, Q~, C^, E and
+//   Gam_C in LDS;
 // - prep waves (2): the Gram matrices on the matrix cores (wave 0 K~ C^T,
 //   wave 1 Q~ C^T), den = diag(K~ C^T) + r, and in wave 0 the inverse of the
 //   unit lower triangular I + N, N = diag(den)^-1 strictlower(K~ C^T), by
@@ -62,7 +62,7 @@ constexpr int kRcDVT = 64;              // value columns per workgroup
 
 template <int D, bool ISO>
 struct RcRoles {
-    static constexpr int NCW = ISO ? 1 : D / 64;  // chain waves (isotropic: one, a scalar precision)
+    static constexpr int NCW = D / 64;  // chain waves
     static constexpr int NSW = 2;       // state waves
     static constexpr int NPW = 2;       // prep waves
     static constexpr int NW = NCW + NSW + NPW;
@@ -77,7 +77,7 @@ struct RcRoles {
 template <typename S, int D, bool ISO>
 struct RcSm {
     static constexpr int NCW = RcRoles<D, ISO>::NCW;
-    static constexpr int DW = ISO ? D : 64;       // key dims per chain wave
+    static constexpr int DW = ISO ? D : 64;       // key dims staged per chain wave (isotropic: all, for |k|^2)
     static constexpr int PAD = 16 / (int)sizeof(S);
     static constexpr int KP = D + PAD;
     alignas(16) S kt[3][kRC][KP];                 // K~ rows
@@ -162,15 +162,19 @@ __global__ __launch_bounds__((RcRoles<D, ISO>::NW * 64)) void kla_fwd_residual_c
 
     if (wave < R::NCW) {
       if constexpr (ISO) {
-        // ---------------- chain (isotropic): one wave, lane holds key dims lane + 64 m;
+        // ---------------- chain (isotropic): lane holds key dim 64 cw + lane;
         // the precision, decay and process noise are scalars per token, the
-        // same in every lane
+        // same in every lane of every chain wave (each forms |k_t|^2 over all
+        // key dims itself)
         constexpr int NDL = D / 64;
+        const int cw = R::NCW == 1 ? 0 : wave, i = 64 * cw + lane;
         float l = p.l0 ? p.l0[bh] : 1.f;
-        // a chunk's k, q rows as 16-byte pieces: PRW per row, NP per lane
+        // a chunk's k rows (all key dims) and q rows (the wave's) as 16-byte
+        // pieces: PRW / PRQ per row, NP / NQ per lane
         constexpr int PRW = D * ES / 16, NP = kRC * PRW / 64;
+        constexpr int PRQ = 64 * ES / 16, NQ = kRC * PRQ / 64;
         struct RawI {
-            i32x4 k[NP], q[NP];
+            i32x4 k[NP], q[NQ];
             float a, qn, r;  // of token lane % 16
         };
         auto load = [&](int c, RawI& x) {
@@ -182,7 +186,11 @@ __global__ __launch_bounds__((RcRoles<D, ISO>::NW * 64)) void kla_fwd_residual_c
             for (int m = 0; m < NP; ++m) {
                 const int pc = lane + 64 * m, t = pc / PRW, pe = pc % PRW;
                 x.k[m] = buf_load<i32x4>(rk, t * D * ES + 16 * pe);
-                x.q[m] = buf_load<i32x4>(rq, t * D * ES + 16 * pe);
+            }
+#pragma unroll
+            for (int m = 0; m < NQ; ++m) {
+                const int pc = lane + 64 * m, t = pc / PRQ, pe = pc % PRQ;
+                x.q[m] = buf_load<i32x4>(rq, (t * D + 64 * cw) * ES + 16 * pe);
             }
             x.a = buf_load<float>(make_rsrc(p.a + r0, nv * 4), (lane & 15) * 4);
             x.qn = buf_load<float>(make_rsrc(p.qn + r0, nv * 4), (lane & 15) * 4);
@@ -192,8 +200,12 @@ __global__ __launch_bounds__((RcRoles<D, ISO>::NW * 64)) void kla_fwd_residual_c
 #pragma unroll
             for (int m = 0; m < NP; ++m) {
                 const int pc = lane + 64 * m, t = pc / PRW, pe = pc % PRW;
-                *(i32x4*)&sm.rk[0][t][pe * (16 / ES)] = x.k[m];
-                *(i32x4*)&sm.rq[0][t][pe * (16 / ES)] = x.q[m];
+                *(i32x4*)&sm.rk[cw][t][pe * (16 / ES)] = x.k[m];
+            }
+#pragma unroll
+            for (int m = 0; m < NQ; ++m) {
+                const int pc = lane + 64 * m, t = pc / PRQ, pe = pc % PRQ;
+                *(i32x4*)&sm.rq[cw][t][pe * (16 / ES)] = x.q[m];
             }
         };
         auto uni = [&](float v, int u) {
@@ -202,31 +214,30 @@ __global__ __launch_bounds__((RcRoles<D, ISO>::NW * 64)) void kla_fwd_residual_c
         auto chain = [&](int c, float a_l, float qn_l, float r_l) {
             const int b3 = c % 3, b2 = c & 1;
             const int nv = nvalid(c);
-            float kf[NDL][kRC], qf[NDL][kRC];
+            float kf[kRC], qf[kRC], ks[kRC];
 #pragma unroll
-            for (int u = 0; u < kRC; ++u)
+            for (int u = 0; u < kRC; ++u) {
+                qf[u] = (float)sm.rq[cw][u][lane];
+                float kn = (float)sm.rk[cw][u][lane];
+                kf[u] = kn;  // the wave's own key dim 64 cw + lane
+                ks[u] = kn * kn;
 #pragma unroll
-                for (int m = 0; m < NDL; ++m) {
-                    kf[m][u] = (float)sm.rk[0][u][lane + 64 * m];
-                    qf[m][u] = (float)sm.rq[0][u][lane + 64 * m];
+                for (int m = 1; m < NDL; ++m) {
+                    kn = (float)sm.rk[cw][u][lane + 64 * m];
+                    kf[u] = cw == m ? kn : kf[u];
+                    ks[u] = __builtin_fmaf(kn, kn, ks[u]);
                 }
+            }
             // token scalars (rows past the sequence's end: a = 1, r = 1, qn = 0)
             const bool lv = (lane & 15) < nv;
             const float av = lv ? a_l : 1.f, qv = lv ? qn_l : 0.f, rv = lv ? r_l : 1.f;
-            if (lane < kRC) sm.rr[b2][lane] = rv;
+            if (cw == 0 && lane < kRC) sm.rr[b2][lane] = rv;
             const float irv = fast_rcp(rv) * (1.f / (float)D);
             // |k_t|^2 over the key dims: a reduce-scatter leaves token
             // 8 b5 + 4 b4 + 2 b3 + b2 in lanes with those lane bits
-            float ks[kRC];
-#pragma unroll
-            for (int u = 0; u < kRC; ++u) {
-                ks[u] = kf[0][u] * kf[0][u];
-#pragma unroll
-                for (int m = 1; m < NDL; ++m) ks[u] = __builtin_fmaf(kf[m][u], kf[m][u], ks[u]);
-            }
             int base = 0;
             reduce_scatter<kRC, 32>(ks, lane, base);
-            float cv[NDL][kRC], chv[NDL][kRC];
+            float cv[kRC], chv[kRC];
             float gam = 1.f;
             bool ok = true;
 #pragma unroll
@@ -234,49 +245,40 @@ __global__ __launch_bounds__((RcRoles<D, ISO>::NW * 64)) void kla_fwd_residual_c
                 const int ol = ((u >> 3) & 1) << 5 | ((u >> 2) & 1) << 4 | ((u >> 1) & 1) << 3 | (u & 1) << 2;
                 const float ksq = uni(ks[0], ol), au = uni(av, u);
                 const float lp = l * fast_rcp(__builtin_fmaf(uni(qv, u), l, au * au));
-                const float rlp = fast_rcp(lp);
                 l = u < nv ? __builtin_fmaf(ksq, uni(irv, u), lp) : l;
                 gam *= au;
                 ok = ok && gam >= kGamLo && gam <= kGamHi;
-                const float igam = fast_rcp(gam);
-#pragma unroll
-                for (int m = 0; m < NDL; ++m) {
-                    const int i = lane + 64 * m;
-                    cv[m][u] = kf[m][u] * rlp;
-                    chv[m][u] = cv[m][u] * igam;
-                    sm.kt[b3][u][i] = (S)(gam * kf[m][u]);
-                    sm.qt[b3][u][i] = (S)(gam * qf[m][u]);
-                    sm.ch[b2][u][i] = (S)chv[m][u];
-                }
+                cv[u] = kf[u] * fast_rcp(lp);
+                chv[u] = cv[u] * fast_rcp(gam);
+                sm.kt[b3][u][i] = (S)(gam * kf[u]);
+                sm.qt[b3][u][i] = (S)(gam * qf[u]);
+                sm.ch[b2][u][i] = (S)chv[u];
             }
-#pragma unroll
-            for (int m = 0; m < NDL; ++m) sm.gc[b3][lane + 64 * m] = gam;
+            sm.gc[b3][i] = gam;
             const bool fac = __all(ok);
-#pragma unroll
-            for (int m = 0; m < NDL; ++m) {
+            {
                 float ev[kRC];
                 if (fac) {
 #pragma unroll
-                    for (int u = 0; u < kRC; ++u) ev[u] = gam * chv[m][u];
+                    for (int u = 0; u < kRC; ++u) ev[u] = gam * chv[u];
                 } else {
                     float sfx = 1.f;
 #pragma unroll
                     for (int u = kRC - 1; u >= 0; --u) {
-                        ev[u] = sfx * cv[m][u];
+                        ev[u] = sfx * cv[u];
                         sfx *= uni(av, u);
                     }
                 }
 #pragma unroll
                 for (int u4 = 0; u4 < kRC; u4 += 4)
-                    *(typename Quad<S>::V*)&sm.e[b3][lane + 64 * m][u4] =
+                    *(typename Quad<S>::V*)&sm.e[b3][i][u4] =
                         Quad<S>::make(f32x4{ev[u4], ev[u4 + 1], ev[u4 + 2], ev[u4 + 3]});
             }
             if (!fac) {
-                // exactly: D(s,t) k_t.c_s and D(s,t) q_t.c_s (s <= t), D a scalar product
+                // the wave's key dims, exactly: D(s,t) k_t c_s and D(s,t) q_t c_s
+                // (s <= t), D a product of the scalar decays
 #pragma unroll
-                for (int u = 0; u < kRC; ++u)
-#pragma unroll
-                    for (int m = 0; m < NDL; ++m) sm.ch[b2][u][lane + 64 * m] = (S)0.f;
+                for (int u = 0; u < kRC; ++u) sm.ch[b2][u][i] = (S)0.f;
 #pragma unroll
                 for (int t = 0; t < kRC; ++t) {
                     float w[2 * kRC];
@@ -289,21 +291,15 @@ __global__ __launch_bounds__((RcRoles<D, ISO>::NW * 64)) void kla_fwd_residual_c
                             continue;
                         }
                         if (s2 < t) dst *= uni(av, s2 + 1);
-                        float sk = 0.f, sq = 0.f;
-#pragma unroll
-                        for (int m = 0; m < NDL; ++m) {
-                            sk = __builtin_fmaf(kf[m][t], cv[m][s2], sk);
-                            sq = __builtin_fmaf(qf[m][t], cv[m][s2], sq);
-                        }
-                        w[s2] = dst * sk;
-                        w[kRC + s2] = dst * sq;
+                        w[s2] = dst * kf[t] * cv[s2];
+                        w[kRC + s2] = dst * qf[t] * cv[s2];
                     }
                     int b = 0;
                     reduce_scatter<2 * kRC, 32>(w, lane, b);
-                    if ((lane & 1) == 0) sm.gx[b2][0][t][b] = w[0];
+                    if ((lane & 1) == 0) sm.gx[b2][cw][t][b] = w[0];
                 }
             }
-            if (lane == 0) sm.off[b2][0] = fac ? 0 : 1;
+            if (lane == 0) sm.off[b2][cw] = fac ? 0 : 1;
         };
 
         RawI xa, xb;
@@ -323,10 +319,10 @@ __global__ __launch_bounds__((RcRoles<D, ISO>::NW * 64)) void kla_fwd_residual_c
             step(j, xa);
             if (j + 1 < nch + 2) step(j + 1, xb);
         }
-        if (p.lT && vt == 0 && lane == 0) p.lT[bh] = l;
+        if (p.lT && vt == 0 && cw == 0 && lane == 0) p.lT[bh] = l;
       } else {
         // ---------------- chain: one lane per key dim
-        const int cw = wave, i = 64 * cw + lane;
+        const int cw = R::NCW == 1 ? 0 : wave, i = 64 * cw + lane;
         float l = p.l0 ? p.l0[(size_t)bh * D + i] : 1.f;
         const float qn = p.qn[(size_t)h * D + i];
         // a chunk's rows of the wave's 64 key dims, 16-byte pieces: lane l
@@ -649,12 +645,8 @@ void launch(const FwdArgs& a, hipStream_t s) {
 
 template <typename TIn, bool ISO>
 void launch_d(const FwdArgs& a, hipStream_t s) {
-    if constexpr (ISO && sizeof(TIn) == 4) {
-        launch<TIn, 64, ISO>(a, s);  // fp32 isotropic dk 128 stays on the block kernel
-    } else {
-        if (a.dk == 64) launch<TIn, 64, ISO>(a, s);
-        else launch<TIn, 128, ISO>(a, s);
-    }
+    if (a.dk == 64) launch<TIn, 64, ISO>(a, s);
+    else launch<TIn, 128, ISO>(a, s);
 }
 
 }  // namespace
@@ -662,8 +654,9 @@ void launch_d(const FwdArgs& a, hipStream_t s) {
 bool fwd_residual_chunk_supported(int dk, int dv, int cov, int dtype) {
     const char* env = getenv("KLA_RES_IMPL");
     if (env && env[0] == 'b') return false;  // KLA_RES_IMPL=block
-    // fp32 isotropic dk 128: the chain wave's two input register sets would spill
-    return dk == dv && (dk == 64 || (dk == 128 && !(cov && dtype != DT_BF16)));
+    (void)cov;
+    (void)dtype;
+    return dk == dv && (dk == 64 || dk == 128);
 }
 
 hipError_t launch_fwd_residual_chunk(const FwdArgs& a, int dtype, int cov, hipStream_t s) {

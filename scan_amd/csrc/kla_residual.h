@@ -14,8 +14,8 @@ int fwd_residual_vtiles(int B, int H, int dk);
 hipError_t launch_fwd_residual(const FwdArgs& a, int dtype, int cov, hipStream_t s);
 
 // The chunked matrix-core forward (diagonal or isotropic, dk == dv in
-// {64, 128}; fp32 isotropic at 64 only); its own value tiles of 64 columns
-// (FwdArgs::n_vtiles is ignored).  KLA_RES_IMPL=block sends these shapes to the block kernel instead.
+// {64, 128}); its own value tiles of 64 columns (FwdArgs::n_vtiles is
+// ignored).  KLA_RES_IMPL=block sends these shapes to the block kernel instead.
 bool fwd_residual_chunk_supported(int dk, int dv, int cov, int dtype);
 hipError_t launch_fwd_residual_chunk(const FwdArgs& a, int dtype, int cov, hipStream_t s);
 

@@ -4,8 +4,8 @@ scan_amd.inputs.  Small cases compare every element; the LM-layer shape
 compares sampled (b,h) sequences.  Parity metric and bars as the KLA
 forward (tests.gpu_util).  Diagonal dk 64 / 128 run the chunked matrix-core
 kernel (exact sums where the decay products leave its range), and so do
-isotropic dk 64 / 128 (fp32 at 64 only); the rest, and those shapes under
-KLA_RES_IMPL=block, the block kernel."""
+isotropic dk 64 / 128; the rest, and those shapes under KLA_RES_IMPL=block,
+the block kernel."""
 import numpy as np
 import pytest
 import torch
@@ -208,8 +208,7 @@ def test_residual_many_heads_d128(cov):
 @pytest.mark.parametrize("d", [64, 128])
 def test_residual_chunk_ragged_grid_every_sequence(cov, dtype, d):
     """19 (b,h), so the 8-apart value tiles leave padding workgroups; chunks of
-    16 with a ragged last one; every sequence against the oracle (fp32
-    isotropic d 128 runs the block kernel)."""
+    16 with a ragged last one; every sequence against the oracle."""
     _print_case("chunk grid", cov, dtype, d)
     base = "small_diag" if cov == "diag" else "iso"
     inp = gen.make_inputs(base, seed=150 + d, B=1, H=19, T=41, dk=d, dv=d, dtype=dtype)
