@@ -50,7 +50,7 @@ KERNEL_SOURCES = {
     "residual": ["scan_amd/csrc/kla_fwd_residual.hip", "scan_amd/csrc/kla_fwd_residual_chunk.hip",
                  "scan_amd/csrc/kla_residual.h"] + _COMMON_SOURCES,
     "step": ["scan_amd/csrc/kla_step.hip"] + _COMMON_SOURCES,
-    "bwd": ["scan_amd/csrc/kla_bwd.hip", "scan_amd/csrc/kla_bwd.h"] + _COMMON_SOURCES,
+    "bwd": ["scan_amd/csrc/kla_bwd.hip", "scan_amd/csrc/kla_bwd_chunk.hip", "scan_amd/csrc/kla_bwd.h"] + _COMMON_SOURCES,
 }
 
 

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkla.so")
-SOURCES = ["kla_api.cpp", "kla_bwd.hip", "kla_fwd_diag.hip", "kla_fwd_diag_pipe.hip", "kla_fwd_iso.hip",
+SOURCES = ["kla_api.cpp", "kla_bwd.hip", "kla_bwd_chunk.hip", "kla_fwd_diag.hip", "kla_fwd_diag_pipe.hip", "kla_fwd_iso.hip",
            "kla_fwd_iso_pipe.hip", "kla_fwd_residual.hip", "kla_fwd_residual_chunk.hip", "kla_fwd_seg.hip", "kla_fwd_short.hip", "kla_noalloc.hip",
            "kla_step.hip"]
 

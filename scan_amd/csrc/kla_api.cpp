@@ -459,7 +459,8 @@ klaStatus klaFwdResidual(const klaDims* d, const void* q, const void* k, const v
 
 size_t klaBwdWorkspaceBytes(const klaDims* d) {
     if (!d || !dims_ok(d) || !kinds_ok(d) || !kla::bwd_supported(d->dk, d->dv)) return 0;
-    return (size_t)d->B * d->H * kla::bwd_ws_stride(d->B, d->H, d->T, d->dk, d->cov == KLA_ISO ? 1 : 0) * sizeof(float);
+    return (size_t)d->B * d->H * kla::bwd_ws_stride(d->B, d->H, d->T, d->dk, d->cov == KLA_ISO ? 1 : 0,
+                                                            d->dtype == KLA_BF16 ? kla::DT_BF16 : kla::DT_F32) * sizeof(float);
 }
 
 klaStatus klaBwd(const klaDims* d, const void* q, const void* k, const void* v, const float* a,
@@ -511,7 +512,10 @@ klaStatus klaBwd(const klaDims* d, const void* q, const void* k, const void* v, 
     ba.gq = dq; ba.gk = dk; ba.gv = dv; ba.ga = da; ba.gqn = dqnoise; ba.gr = dr; ba.gl0 = dl0;
     ba.geta0 = deta0;
     ba.ws = (float*)workspace;
-    ba.ws_stride = kla::bwd_ws_stride(d->B, d->H, d->T, d->dk, iso ? 1 : 0);
+    ba.ws_stride = kla::bwd_ws_stride(d->B, d->H, d->T, d->dk, iso ? 1 : 0,
+                                     d->dtype == KLA_BF16 ? kla::DT_BF16 : kla::DT_F32);
+    ba.gate_nt = 0;
+    ba.flag_off = 0;
     ba.B = d->B; ba.H = d->H; ba.T = d->T; ba.dk = d->dk; ba.dv = d->dv;
     const hipError_t e = kla::launch_bwd(ba, d->dtype, iso ? 1 : 0, (hipStream_t)hipStream);
     if (e == hipErrorInvalidValue) return KLA_ERR_UNSUPPORTED;

@@ -47,6 +47,8 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "kla_bwd.h"
 #include "kla_common.h"
 
@@ -535,6 +537,20 @@ __global__ __launch_bounds__(kBwdThreads) void kla_bwd_diag_kernel(BwdArgs p) {
     } else {
         bh_ = blockIdx.x / NRG;
         rgp = blockIdx.x % NRG;
+    }
+    if constexpr (NRG == 1) {
+        // after the chunked kernels: only the (b,h) they handed back
+        if (p.gate_nt > 0) {
+            int any = 0;
+            for (int g2 = 0; g2 < NH; ++g2) {
+                const int b2 = NH == 1 ? (int)blockIdx.x : (int)blockIdx.x * NH + g2;
+                if (b2 < nbh) {
+                    const int* fl = (const int*)(p.ws + (size_t)b2 * p.ws_stride + p.flag_off);
+                    for (int t2 = 0; t2 < p.gate_nt; ++t2) any |= fl[t2];
+                }
+            }
+            if (!any) return;  // uniform over the workgroup
+        }
     }
     const bool valid = NH == 1 || bh_ < nbh;
     const int bh = valid ? bh_ : nbh - 1;  // a spare group stays in bounds and stores nothing
@@ -1345,6 +1361,18 @@ bool bwd_plain() {
 
 template <typename TIn, int D, bool ISO>
 void launch_d(const BwdArgs& a, dim3 grid, dim3 block, hipStream_t s) {
+    if constexpr (!ISO && (D == 64 || D == 128) && std::is_same<TIn, bf16>::value) {
+        if (bwd_chunk_supported(a.dk, a.dv, 0, DT_BF16, a.T)) {
+            // the chunked kernels, then the token-serial kernel for the (b,h)
+            // whose decay products left the range of the chunk quotients
+            if (launch_bwd_chunk(a, DT_BF16, s) != hipSuccess) return;
+            BwdArgs f = a;
+            f.gate_nt = D / 64;
+            f.flag_off = bc_layout(a.T, D).flags;
+            hipLaunchKernelGGL((kla_bwd_diag_kernel<TIn, D, 1>), grid, block, 0, s, f);
+            return;
+        }
+    }
     if (ISO || bwd_plain()) {
         hipLaunchKernelGGL((kla_bwd_kernel<TIn, D, ISO>), grid, block, 0, s, a);
         return;
@@ -1393,7 +1421,8 @@ hipError_t dispatch(const BwdArgs& a, hipStream_t s) {
 
 bool bwd_supported(int dk, int dv) { return dk == dv && (dk == 16 || dk == 32 || dk == 64 || dk == 128); }
 
-size_t bwd_ws_stride(int B, int H, int T, int dk, int cov) {
+size_t bwd_ws_stride(int B, int H, int T, int dk, int cov, int dtype) {
+    if (bwd_chunk_supported(dk, dk, cov, dtype, T)) return bc_layout(T, dk).total;
     const size_t nl = cov ? 1 : (size_t)dk;
     // l_t and q dq (fp64), the diagonal qn partial (fp32), and with a row
     // split the row groups' partials of dv [NRG][T][dv] and dr [NRG][T]

@@ -255,6 +255,16 @@ def test_backward_argument_errors():
     # per (b,h): l_t and q dq fp64 [T][dk], qn partial fp32 [dk]
     per = 16 * 32 * 4 + 32
     assert scan_amd.klaBwdWorkspaceBytes(d) == 2 * 3 * 4 * ((per + 63) // 64 * 64)
+    # the chunked path (diagonal bf16, dk 64 / 128): the token-serial block
+    # (handed-back sequences), the row tiles' flags, then q.dq [T][dk], the
+    # partials of dv [NT][T][dk] and dr [NT][T4], the chunk-start precisions
+    # [nch][dk] and <detaT, eta_T> [dk]
+    for T, dk in [(40, 64), (77, 128), (1, 128)]:
+        nt, nch, t4 = dk // 64, (T + 15) // 16, (T + 3) // 4 * 4
+        q0 = (4 * T * dk + dk + 4 + 63) // 64 * 64
+        end = q0 + T * dk + nt * T * dk + nt * t4 + nch * dk + dk
+        assert scan_amd.klaBwdWorkspaceBytes(KlaDims(2, 3, T, dk, dk, BF16, DIAG)) == \
+            2 * 3 * 4 * ((end + 63) // 64 * 64), (T, dk)
     for field in ("B", "H", "T", "dk", "dv"):
         bad = KlaDims(2, 3, 16, 32, 32, BF16, DIAG)
         setattr(bad, field, -1)

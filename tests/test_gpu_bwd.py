@@ -141,11 +141,12 @@ def test_bwd_deterministic():
 @pytest.mark.parametrize("nrg", ["1", "2", "4"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_bwd_row_groups(monkeypatch, nrg, dtype):
-    """dk = 128 with its key dims on 1, 2 or 4 workgroups per (b,h) (the
+    """Token-serial kernels: dk = 128 with its key dims on 1, 2 or 4 workgroups per (b,h) (the
     row-group partials of dv and dr summed by the combine pass), ragged token
     blocks, a state and final-state gradients; and the row split equals the
     whole-row kernel to the fp32 bar."""
     _print_case("bwd row groups", nrg, dtype)
+    monkeypatch.setenv("KLA_BWD_IMPL", "rows")  # the token-serial kernels, not the chunked ones
     monkeypatch.setenv("KLA_BWD_NRG", nrg)
     inp = gen.make_inputs("small_diag", seed=350, B=2, H=3, T=77, dk=128, dv=128, dtype=dtype)
     w = inp["workload"]
@@ -167,3 +168,49 @@ def test_bwd_full_lm_shape_every_sequence():
     w = inp["workload"]
     up = gen.make_upstream(w, seed=1)
     check(run_bwd(inp, up, "diag"), run_ref(inp, up, "diag"), "diag", "bf16", "bwd full lm shape")
+
+
+# ------------------------------------------------ chunked kernels (bf16, diag, d 64 / 128)
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("T", [1, 16, 45, 300])
+def test_bwd_chunk_with_state(d, T):
+    """The chunked backward: ragged last chunks, a state, final-state
+    gradients, B*H = 10 (a grid padded to the XCD pattern at d 128)."""
+    _print_case("bwd chunk", d, T)
+    inp = gen.make_inputs("lm_diag", seed=360 + T + d, B=2, H=5, T=T, dk=d, dv=d)
+    w = inp["workload"]
+    st = gen.make_state(w, seed=361)
+    up = gen.make_upstream(w, seed=362)
+    check(run_bwd(inp, up, "diag", st), run_ref(inp, up, "diag", st), "diag", "bf16", f"bwd chunk d={d} T={T}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_chunk_hands_back_out_of_range(d):
+    """a = 0.01 on one head: its decay products leave [2^-64, 2^64] within a
+    chunk, so the token-serial kernel redoes that (b,h) (and, at d 64, the
+    one sharing its workgroup); the rest stay on the chunked path."""
+    _print_case("bwd chunk hand-back", d)
+    inp = gen.make_inputs("lm_diag", seed=370, B=2, H=3, T=50, dk=d, dv=d)
+    a = inp["a"].clone()
+    a[0, 1] = 0.01
+    inp["a"] = a
+    w = inp["workload"]
+    st = gen.make_state(w, seed=371)
+    up = gen.make_upstream(w, seed=372)
+    check(run_bwd(inp, up, "diag", st), run_ref(inp, up, "diag", st), "diag", "bf16", f"bwd hand-back d={d}")
+
+
+def test_bwd_chunk_matches_token_serial(monkeypatch):
+    """Chunked and token-serial kernels on the same inputs (long-context
+    laws): every gradient within the bf16 bar of each other."""
+    _print_case("bwd chunk vs token-serial")
+    inp = gen.make_inputs("long_diag", seed=380, B=1, H=4, T=400)
+    w = inp["workload"]
+    up = gen.make_upstream(w, seed=381)
+    chunk = run_bwd(inp, up, "diag")
+    monkeypatch.setenv("KLA_BWD_IMPL", "rows")
+    serial = run_bwd(inp, up, "diag")
+    errs = bwd_errors(chunk, serial, "diag")
+    print("chunk vs serial", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    assert all(v <= TOL["bf16"] for v in errs.values()), errs
