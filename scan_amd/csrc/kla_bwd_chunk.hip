@@ -168,10 +168,9 @@ __device__ __forceinline__ void mma_load(const BwdArgs& p, size_t row0, int c, i
         m.x[u] = buf_load<i32x4>(mat == 0 ? rd : rv, t * D * 2 + 16 * pe);
     }
 }
-// Row-major dO and v, and one of them transposed ([D][kBC + 8]).
-template <int D, bool TRANS_V>
-__device__ __forceinline__ void mma_stage(const MmaRaw<D>& m, bf16 (*dO)[D + 8], bf16 (*vv)[D + 8],
-                                          bf16 (*tr)[kBC + 8]) {
+// Row-major dO and v.
+template <int D>
+__device__ __forceinline__ void mma_stage(const MmaRaw<D>& m, bf16 (*dO)[D + 8], bf16 (*vv)[D + 8]) {
     typedef MmaRaw<D> R;
 #pragma unroll
     for (int u = 0; u < R::NP; ++u) {
@@ -179,12 +178,15 @@ __device__ __forceinline__ void mma_stage(const MmaRaw<D>& m, bf16 (*dO)[D + 8],
         const int mat = pc / (kBC * R::PR);
         const int rem = pc % (kBC * R::PR), t = rem / R::PR, pe = rem % R::PR;
         *(i32x4*)(mat == 0 ? &dO[t][8 * pe] : &vv[t][8 * pe]) = m.x[u];
-        if (mat == (TRANS_V ? 1 : 0)) {
-            const bf16x8 e8 = __builtin_bit_cast(bf16x8, m.x[u]);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) tr[8 * pe + e][t] = e8[e];
-        }
     }
+}
+// A K16 operand along tokens from a row-major [token][column] tile: the
+// lane's column at rows 4g .. 4g + 3 (p = &tile[4g][column], S the row
+// stride).  A transposed copy of the tile would cost scalar stores that all
+// fall in one bank.
+__device__ __forceinline__ s16x4 ld_col4(const bf16* p, int S) {
+    return s16x4{__builtin_bit_cast(short, p[0]), __builtin_bit_cast(short, p[S]),
+                 __builtin_bit_cast(short, p[2 * S]), __builtin_bit_cast(short, p[3 * S])};
 }
 
 // ============================================================ forward sweep
@@ -197,7 +199,6 @@ struct Bc1Sm {
     ChainStage cs[2];                    // raw k, q (also read by the matrix-core waves), a
     alignas(16) bf16 dO[2][kBC][D + 8];
     alignas(16) bf16 vv[2][kBC][D + 8];
-    alignas(16) bf16 vt[2][D][kBC + 8];  // v transposed
     alignas(16) float ost[4][2][kBC][16 + 4];
 };
 
@@ -286,13 +287,15 @@ __global__ __launch_bounds__(320) void kla_bwd_chunk_fwd(BwdArgs p) {
         const int b = c & 1, nv = nvalid(c);
         // X = dO eta_in^T, the state tiles as the B operand (K16 over value columns)
         // (two accumulators, so that consecutive MFMAs do not wait on each other)
-        f32x4 X0 = zero4(), X1 = zero4();
+        f32x4 Xacc[4] = {zero4(), zero4(), zero4(), zero4()};
 #pragma unroll
-        for (int jt = 0; jt < NJT; jt += 2) {
-            X0 = mma_xs(MB::ld16(&sm.dO[b][c16][16 * jt + 4 * g]), split4(eta[jt]), X0);
-            X1 = mma_xs(MB::ld16(&sm.dO[b][c16][16 * jt + 16 + 4 * g]), split4(eta[jt + 1]), X1);
+        for (int jt = 0; jt < NJT; ++jt) {
+            const s16x4 df = MB::ld16(&sm.dO[b][c16][16 * jt + 4 * g]);
+            const SplitK16 es = split4(eta[jt]);
+            Xacc[2 * (jt & 1)] = mfma16(df, es.hi, Xacc[2 * (jt & 1)]);
+            Xacc[2 * (jt & 1) + 1] = mfma16(df, es.lo, Xacc[2 * (jt & 1) + 1]);
         }
-        const f32x4 X = X0 + X1;
+        const f32x4 X = (Xacc[0] + Xacc[2]) + (Xacc[1] + Xacc[3]);
         // M^T[s][t] = v_s . dO_t; lane holds M[t = c16][s = 4g + e]: the A
         // operand of lower(M) (W / G) as it stands
         f32x4 Mt = zero4();
@@ -337,11 +340,11 @@ __global__ __launch_bounds__(320) void kla_bwd_chunk_fwd(BwdArgs p) {
         // eta_out = G_C (.) (eta_in + (W / G)^T V)
         const float gev = sm.ge[b][il];
 #pragma unroll
-        for (int jt = 0; jt < NJT; ++jt) eta[jt] = mma_xs(MB::ld16(&sm.vt[b][16 * jt + c16][4 * g]), wgs, eta[jt]) * gev;
+        for (int jt = 0; jt < NJT; ++jt) eta[jt] = mma_xs(ld_col4(&sm.vv[b][4 * g][16 * jt + c16], D + 8), wgs, eta[jt]) * gev;
     };
     mma_load<D>(p, row0, 0, nvalid(0), mr);
     for (int it = 0; it <= nch; ++it) {
-        if (it < nch) mma_stage<D, true>(mr, sm.dO[it & 1], sm.vv[it & 1], sm.vt[it & 1]);
+        if (it < nch) mma_stage<D>(mr, sm.dO[it & 1], sm.vv[it & 1]);
         if (it + 1 < nch) mma_load<D>(p, row0, it + 1, nvalid(it + 1), mr);
         if (it >= 1) step(it - 1);
         lds_barrier();
@@ -384,8 +387,6 @@ struct Bc2Sm {
     ChainStage cs;
     alignas(16) bf16 dO[2][kBC][D + 8];
     alignas(16) bf16 vv[2][kBC][D + 8];
-    alignas(16) bf16 dOT[2][D][kBC + 8];  // dO transposed
-    alignas(16) float dvs[4][kBC][D / 4 + 4];
 };
 
 template <int D>
@@ -597,13 +598,17 @@ __global__ __launch_bounds__(384) void kla_bwd_chunk_rev(BwdArgs p) {
     auto step = [&](int c) {
         const int b = c & 1, nv = nvalid(c);
         // P1 = V eps^T over value columns (state tiles as the B operand)
-        f32x4 Pa = zero4(), Pb = zero4();
+        // (four accumulators, hi and lo products in separate ones, so that
+        // consecutive MFMAs do not wait on each other)
+        f32x4 Pacc[4] = {zero4(), zero4(), zero4(), zero4()};
 #pragma unroll
-        for (int jt = 0; jt < NJT; jt += 2) {
-            Pa = mma_xs(MB::ld16(&sm.vv[b][c16][16 * jt + 4 * g]), split4(eA[jt]), Pa);
-            Pb = mma_xs(MB::ld16(&sm.vv[b][c16][16 * jt + 16 + 4 * g]), split4(eA[jt + 1]), Pb);
+        for (int jt = 0; jt < NJT; ++jt) {
+            const s16x4 vf = MB::ld16(&sm.vv[b][c16][16 * jt + 4 * g]);
+            const SplitK16 es = split4(eA[jt]);
+            Pacc[2 * (jt & 1)] = mfma16(vf, es.hi, Pacc[2 * (jt & 1)]);
+            Pacc[2 * (jt & 1) + 1] = mfma16(vf, es.lo, Pacc[2 * (jt & 1) + 1]);
         }
-        const f32x4 P1 = Pa + Pb;
+        const f32x4 P1 = (Pacc[0] + Pacc[2]) + (Pacc[1] + Pacc[3]);
         // lane holds (V dO^T)[t = c16][s = 4g + e]; keep s >= t
         f32x4 Mt = zero4();
 #pragma unroll
@@ -643,48 +648,41 @@ __global__ __launch_bounds__(384) void kla_bwd_chunk_rev(BwdArgs p) {
         // dv = (W / G) (G_C (.) eps) + upper((W / G) A^T) dO for the wave's columns
 #pragma unroll
         for (int jb = 0; jb < NJB; ++jb) {
-            f32x4 da_ = zero4(), db_ = zero4();
+            // one accumulator per key-dim block (three MFMAs each), the upper
+            // triangle's two in a fifth
+            f32x4 dacc[4];
 #pragma unroll
-            for (int ib = 0; ib < 4; ib += 2) {
-                da_ = Mma<float>::mma16(SplitK16{MB::ld16(&sm.wth[b][c16][16 * ib + 4 * g]),
-                                                 MB::ld16(&sm.wtl[b][c16][16 * ib + 4 * g])},
-                                        split4(eB[ib][jb]), da_);
-                db_ = Mma<float>::mma16(SplitK16{MB::ld16(&sm.wth[b][c16][16 * ib + 16 + 4 * g]),
-                                                 MB::ld16(&sm.wtl[b][c16][16 * ib + 16 + 4 * g])},
-                                        split4(eB[ib + 1][jb]), db_);
-            }
-            const f32x4 dv = mma_sx(wd, MB::ld16(&sm.dOT[b][jw0 + 16 * jb + c16][4 * g]), da_) + db_;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sm.dvs[w][4 * g + e][16 * jb + c16] = dv[e];
-        }
-        wave_sync();
-        {
-            constexpr int PRD = JW / 4, NPD = kBC * PRD / 64;
+            for (int ib = 0; ib < 4; ++ib)
+                dacc[ib] = Mma<float>::mma16(SplitK16{MB::ld16(&sm.wth[b][c16][16 * ib + 4 * g]),
+                                                      MB::ld16(&sm.wtl[b][c16][16 * ib + 4 * g])},
+                                             split4(eB[ib][jb]), zero4());
+            const f32x4 du = mma_sx(wd, ld_col4(&sm.dO[b][4 * g][jw0 + 16 * jb + c16], D + 8), zero4());
+            const f32x4 dv = ((dacc[0] + dacc[1]) + (dacc[2] + dacc[3])) + du;
+            // the partial straight from the accumulator: rows 4g + e, 16
+            // consecutive columns per row (rows past the end are dropped)
             const auto rs = rows_of(ws + L.dvp + (size_t)tile * T * D, (size_t)c * kBC, nv, D);
 #pragma unroll
-            for (int m = 0; m < NPD; ++m) {
-                const int pc = lane + 64 * m, tt = pc / PRD, cq = pc % PRD;
-                buf_store(*(const f32x4*)&sm.dvs[w][tt][4 * cq], rs, (tt * D + jw0 + 4 * cq) * 4);
-            }
+            for (int e = 0; e < 4; ++e) buf_store(dv[e], rs, ((4 * g + e) * D + jw0 + 16 * jb + c16) * 4);
         }
         // eps_in = G_C (.) eps_out + A^T dO, both copies
         {
             const float gev = sm.ge[b][il];
 #pragma unroll
-            for (int jt = 0; jt < NJT; ++jt) eA[jt] = mma_xs(MB::ld16(&sm.dOT[b][16 * jt + c16][4 * g]), as, eA[jt] * gev);
+            for (int jt = 0; jt < NJT; ++jt) eA[jt] = mma_xs(ld_col4(&sm.dO[b][4 * g][16 * jt + c16], D + 8), as, eA[jt] * gev);
         }
 #pragma unroll
         for (int ib = 0; ib < 4; ++ib) {
             const SplitK16 ak = {MB::ld16(&sm.akh[b][16 * ib + c16][4 * g]), MB::ld16(&sm.akl[b][16 * ib + c16][4 * g])};
 #pragma unroll
-            for (int jb = 0; jb < NJB; ++jb) eB[ib][jb] = mma_sx(ak, MB::ld16(&sm.dOT[b][jw0 + 16 * jb + c16][4 * g]), eB[ib][jb]);
+            for (int jb = 0; jb < NJB; ++jb)
+                eB[ib][jb] = mma_sx(ak, ld_col4(&sm.dO[b][4 * g][jw0 + 16 * jb + c16], D + 8), eB[ib][jb]);
         }
     };
     mma_load<D>(p, row0, nch - 1, nvalid(nch - 1), mr);
     for (int it = 0; it < nch + 2; ++it) {
         if (it < nch) {
             const int c = nch - 1 - it;
-            mma_stage<D, false>(mr, sm.dO[c & 1], sm.vv[c & 1], sm.dOT[c & 1]);
+            mma_stage<D>(mr, sm.dO[c & 1], sm.vv[c & 1]);
             if (c >= 1) mma_load<D>(p, row0, c - 1, nvalid(c - 1), mr);
         }
         if (it >= 1 && it <= nch) step(nch - it);
