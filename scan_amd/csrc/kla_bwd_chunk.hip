@@ -378,9 +378,10 @@ struct Bc2Sm {
     alignas(16) bf16 wtl[2][kBC][64 + 8];
     alignas(16) float ge[2][64];          // G_C
     // for the precision adjoint, by chunk mod 3
-    alignas(16) float la[3][64][kBP];     // a (1 past the end), key-major
+    alignas(16) float lg[3][64][kBP];     // g = a / D (1 past the end), key-major
+    alignas(16) float lP[3][64][kBP];     // P = l_{t-1} / D
+    alignas(16) float lia[3][64][kBP];    // 1 / a (1 past the end)
     alignas(16) float lw[3][64][kBP];     // w = k / r
-    alignas(16) float lp[3][64][kBP];     // l_{t-1}
     alignas(16) float lk[3][64][kBP];     // k
     alignas(16) float ir[3][kBC];         // 1 / r
     alignas(16) float ub[2][64][kBP];     // U, key-major, by chunk parity
@@ -427,20 +428,26 @@ __global__ __launch_bounds__(384) void kla_bwd_chunk_rev(BwdArgs p) {
             }
             const float irl = fast_rcp(lane < nv ? rlane : 1.f);
             if (lane < kBC) sm.ir[b3][lane] = irl;
-            float gam = 1.f;
-            float vr[kBC], vl[kBC], va[kBC], vw[kBC];
+            // 1 / G as a running product of D / a (the reciprocal of a is
+            // needed by the precision adjoint anyway)
+            float gam = 1.f, rg = 1.f;
+            float vr[kBC], vg[kBC], vP[kBC], vi[kBC], vw[kBC];
             bf16 vah[kBC], val[kBC];
 #pragma unroll
             for (int u = 0; u < kBC; ++u) {
                 const bool in = u < nv;
                 const float ir = uni(irl, u);
-                const float rd = fast_rcp(__builtin_fmaf(qn, l, af[u] * af[u]));
-                vl[u] = l;
-                va[u] = in ? af[u] : 1.f;
+                const float Dn = __builtin_fmaf(qn, l, af[u] * af[u]);
+                const float rd = fast_rcp(Dn);
+                const float ia = fast_rcp(in ? af[u] : 1.f);
                 const float g = in ? af[u] * rd : 1.f;
-                l = in ? __builtin_fmaf(kf[u] * kf[u], ir, l * rd) : l;
+                const float P = l * rd;
+                vg[u] = g;
+                vP[u] = P;
+                vi[u] = ia;
+                l = in ? __builtin_fmaf(kf[u] * kf[u], ir, P) : l;
                 gam *= g;
-                const float rg = fast_rcp(gam);
+                rg *= in ? Dn * ia : 1.f;
                 const float wv = kf[u] * ir;
                 vw[u] = wv;
                 const float A = gam * (qf[u] * fast_rcp(l));
@@ -457,8 +464,9 @@ __global__ __launch_bounds__(384) void kla_bwd_chunk_rev(BwdArgs p) {
             }
 #pragma unroll
             for (int u = 0; u < kBC; u += 4) {
-                *(f32x4*)&sm.lp[b3][il][u] = f32x4{vl[u], vl[u + 1], vl[u + 2], vl[u + 3]};
-                *(f32x4*)&sm.la[b3][il][u] = f32x4{va[u], va[u + 1], va[u + 2], va[u + 3]};
+                *(f32x4*)&sm.lg[b3][il][u] = f32x4{vg[u], vg[u + 1], vg[u + 2], vg[u + 3]};
+                *(f32x4*)&sm.lP[b3][il][u] = f32x4{vP[u], vP[u + 1], vP[u + 2], vP[u + 3]};
+                *(f32x4*)&sm.lia[b3][il][u] = f32x4{vi[u], vi[u + 1], vi[u + 2], vi[u + 3]};
                 *(f32x4*)&sm.lk[b3][il][u] = f32x4{kf[u], kf[u + 1], kf[u + 2], kf[u + 3]};
                 *(f32x4*)&sm.lw[b3][il][u] = f32x4{vw[u], vw[u + 1], vw[u + 2], vw[u + 3]};
                 *(f32x4*)&sm.rgam[b2][il][u] = f32x4{vr[u], vr[u + 1], vr[u + 2], vr[u + 3]};
@@ -508,17 +516,19 @@ __global__ __launch_bounds__(384) void kla_bwd_chunk_rev(BwdArgs p) {
         // depend on the recursion is formed outside its loop.
         auto adj = [&](int c) {
             const int b2 = c & 1, b3 = c % 3, nv = nvalid(c);
-            float q2[kBC], av[kBC], wv[kBC], lpv[kBC], kv[kBC], Uv[kBC], irv[kBC];
+            float q2[kBC], gv[kBC], Pv[kBC], iav[kBC], wv[kBC], kv[kBC], Uv[kBC], irv[kBC];
 #pragma unroll
             for (int u = 0; u < kBC; u += 4) {
-                const f32x4 a4 = *(const f32x4*)&sm.la[b3][il][u], w4 = *(const f32x4*)&sm.lw[b3][il][u];
-                const f32x4 l4 = *(const f32x4*)&sm.lp[b3][il][u], k4 = *(const f32x4*)&sm.lk[b3][il][u];
+                const f32x4 g4 = *(const f32x4*)&sm.lg[b3][il][u], p4 = *(const f32x4*)&sm.lP[b3][il][u];
+                const f32x4 i4 = *(const f32x4*)&sm.lia[b3][il][u], w4 = *(const f32x4*)&sm.lw[b3][il][u];
+                const f32x4 k4 = *(const f32x4*)&sm.lk[b3][il][u];
                 const f32x4 u4 = *(const f32x4*)&sm.ub[b2][il][u], r4 = *(const f32x4*)&sm.ir[b3][u];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    av[u + e] = a4[e];
+                    gv[u + e] = g4[e];
+                    Pv[u + e] = p4[e];
+                    iav[u + e] = i4[e];
                     wv[u + e] = w4[e];
-                    lpv[u + e] = l4[e];
                     kv[u + e] = k4[e];
                     Uv[u + e] = u4[e];
                     irv[u + e] = r4[e];
@@ -526,12 +536,11 @@ __global__ __launch_bounds__(384) void kla_bwd_chunk_rev(BwdArgs p) {
             }
 #pragma unroll
             for (int u = 0; u < kBC; ++u) q2[u] = qv[u];
-            float rd[kBC], rl[kBC];
+            // with g = a / D and P = l_{t-1} / D: l_t = P + k w, a^2 / D^2 = g^2,
+            // qn / D = qn g / a, a l_{t-1} / D^2 = g P
+            float rl[kBC];
 #pragma unroll
-            for (int u = 0; u < kBC; ++u) {
-                rd[u] = fast_rcp(__builtin_fmaf(qn, lpv[u], av[u] * av[u]));
-                rl[u] = fast_rcp(__builtin_fmaf(kv[u], wv[u], lpv[u] * rd[u]));  // 1 / l_t
-            }
+            for (int u = 0; u < kBC; ++u) rl[u] = fast_rcp(__builtin_fmaf(kv[u], wv[u], Pv[u]));  // 1 / l_t
             // the recursion, last token first: dlog g_t (cum) and lbar
             float lb[kBC], cm[kBC];
 #pragma unroll
@@ -540,8 +549,7 @@ __global__ __launch_bounds__(384) void kla_bwd_chunk_rev(BwdArgs p) {
                 lbar = __builtin_fmaf(-q2[u], rl[u], lbar);
                 lb[u] = lbar;
                 cm[u] = cum;
-                const float ard = av[u] * rd[u];
-                const float lnext = __builtin_fmaf(lbar, ard * ard, -cum * (qn * rd[u]));
+                const float lnext = __builtin_fmaf(lbar, gv[u] * gv[u], -cum * (qn * gv[u] * iav[u]));
                 lbar = u < nv ? lnext : lbar;
             }
             const auto rgk = rows_of((bf16*)p.gk, row0 + (size_t)c * kBC, nv, D);
@@ -549,13 +557,12 @@ __global__ __launch_bounds__(384) void kla_bwd_chunk_rev(BwdArgs p) {
             float dr[kBC];
 #pragma unroll
             for (int u = 0; u < kBC; ++u) {
-                const float lbu = lb[u], cmu = cm[u], a = av[u], lpu = lpv[u], rdu = rd[u];
+                const float lbu = lb[u], cmu = cm[u], g = gv[u], P = Pv[u];
                 buf_store_b16((bf16)(__builtin_fmaf(2.f * lbu, kv[u], Uv[u]) * irv[u]), rgk, (u * D + i) * 2);
                 dr[u] = -wv[u] * __builtin_fmaf(lbu, kv[u], Uv[u]) * irv[u];
-                const float rd2 = rdu * rdu;
-                buf_store(-2.f * lbu * a * lpu * rd2 + cmu * __builtin_fmaf(qn, lpu, -a * a) * rdu * fast_rcp(a), rga,
-                          (u * D + i) * 4);
-                const float dqt = lbu * lpu * lpu * rd2 + cmu * lpu * rdu;
+                // da = -2 lbar a l_{t-1} / D^2 + dlog g (qn l_{t-1} - a^2) / (a D)
+                buf_store(__builtin_fmaf(-2.f * lbu, g * P, cmu * __builtin_fmaf(-2.f, g, iav[u])), rga, (u * D + i) * 4);
+                const float dqt = __builtin_fmaf(lbu * P, P, cmu * P);
                 dqn -= u < nv ? dqt : 0.f;
             }
             // dr of the tile's key dims: a reduce-scatter leaves token
