@@ -147,8 +147,8 @@ __device__ __forceinline__ void chain_stage(ChainStage& st, const ChainRaw& x, i
 }
 
 // A chunk's 16 rows of dO and v in 16-byte pieces over the 256 lanes of the
-// four matrix-core waves (dk 128: one piece of each per lane; dk 64: waves
-// 0-1 dO, 2-3 v).
+// four matrix-core waves, mt = 64 w + lane for matrix-core wave w (dk 128:
+// one piece of each per lane; dk 64: waves 0-1 dO, 2-3 v).
 template <int D>
 struct MmaRaw {
     static constexpr int PR = D * 2 / 16;         // pieces per row
@@ -156,13 +156,13 @@ struct MmaRaw {
     i32x4 x[NP];
 };
 template <int D>
-__device__ __forceinline__ void mma_load(const BwdArgs& p, size_t row0, int c, int nv, MmaRaw<D>& m) {
+__device__ __forceinline__ void mma_load(const BwdArgs& p, size_t row0, int c, int nv, int mt, MmaRaw<D>& m) {
     typedef MmaRaw<D> R;
     const auto rd = rows_of((const bf16*)p.dO, row0 + (size_t)c * kBC, nv, D);
     const auto rv = rows_of((const bf16*)p.v, row0 + (size_t)c * kBC, nv, D);
 #pragma unroll
     for (int u = 0; u < R::NP; ++u) {
-        const int pc = (int)threadIdx.x + 256 * u;
+        const int pc = mt + 256 * u;
         const int mat = __builtin_amdgcn_readfirstlane(pc / (kBC * R::PR));  // uniform per wave
         const int rem = pc % (kBC * R::PR), t = rem / R::PR, pe = rem % R::PR;
         m.x[u] = buf_load<i32x4>(mat == 0 ? rd : rv, t * D * 2 + 16 * pe);
@@ -170,11 +170,11 @@ __device__ __forceinline__ void mma_load(const BwdArgs& p, size_t row0, int c, i
 }
 // Row-major dO and v.
 template <int D>
-__device__ __forceinline__ void mma_stage(const MmaRaw<D>& m, bf16 (*dO)[D + 8], bf16 (*vv)[D + 8]) {
+__device__ __forceinline__ void mma_stage(const MmaRaw<D>& m, int mt, bf16 (*dO)[D + 8], bf16 (*vv)[D + 8]) {
     typedef MmaRaw<D> R;
 #pragma unroll
     for (int u = 0; u < R::NP; ++u) {
-        const int pc = (int)threadIdx.x + 256 * u;
+        const int pc = mt + 256 * u;
         const int mat = pc / (kBC * R::PR);
         const int rem = pc % (kBC * R::PR), t = rem / R::PR, pe = rem % R::PR;
         *(i32x4*)(mat == 0 ? &dO[t][8 * pe] : &vv[t][8 * pe]) = m.x[u];
@@ -276,7 +276,7 @@ __global__ __launch_bounds__(320) void kla_bwd_chunk_fwd(BwdArgs p) {
     }
 
     // ---------------- matrix-core waves: key dims 64 tile + 16 w + c16
-    const int w = wave, c16 = lane & 15, g = lane >> 4;
+    const int w = wave, c16 = lane & 15, g = lane >> 4, mt = 64 * w + lane;
     const int il = 16 * w + c16, ig = 64 * tile + il;
     f32x4 eta[NJT];  // eta[ig][16 jt + 4 g + e]
 #pragma unroll
@@ -342,10 +342,10 @@ __global__ __launch_bounds__(320) void kla_bwd_chunk_fwd(BwdArgs p) {
 #pragma unroll
         for (int jt = 0; jt < NJT; ++jt) eta[jt] = mma_xs(ld_col4(&sm.vv[b][4 * g][16 * jt + c16], D + 8), wgs, eta[jt]) * gev;
     };
-    mma_load<D>(p, row0, 0, nvalid(0), mr);
+    mma_load<D>(p, row0, 0, nvalid(0), mt, mr);
     for (int it = 0; it <= nch; ++it) {
-        if (it < nch) mma_stage<D>(mr, sm.dO[it & 1], sm.vv[it & 1]);
-        if (it + 1 < nch) mma_load<D>(p, row0, it + 1, nvalid(it + 1), mr);
+        if (it < nch) mma_stage<D>(mr, mt, sm.dO[it & 1], sm.vv[it & 1]);
+        if (it + 1 < nch) mma_load<D>(p, row0, it + 1, nvalid(it + 1), mt, mr);
         if (it >= 1) step(it - 1);
         lds_barrier();
     }
@@ -413,7 +413,10 @@ __global__ __launch_bounds__(384) void kla_bwd_chunk_rev(BwdArgs p) {
     }
     auto nvalid = [&](int c) { return T - c * kBC < kBC ? T - c * kBC : kBC; };
 
-    if (wave == 4) {
+    // waves go round-robin over the four SIMDs: the matrix-core waves are
+    // 0, 1, 4, 5 (two to a SIMD), the chain wave 2 and the adjoint wave 3
+    // each have a SIMD of their own
+    if (wave == 2) {
         // ---------------- chain: the chunk's precision again, from its start
         const int il = lane, i = 64 * tile + il;
         const float qn = p.qn[(size_t)h * D + i];
@@ -495,7 +498,7 @@ __global__ __launch_bounds__(384) void kla_bwd_chunk_rev(BwdArgs p) {
         return;
     }
 
-    if (wave == 5) {
+    if (wave == 3) {
         // ---------------- precision adjoint, two chunks behind the chain
         const int il = lane, i = 64 * tile + il;
         const float qn = p.qn[(size_t)h * D + i];
@@ -584,7 +587,7 @@ __global__ __launch_bounds__(384) void kla_bwd_chunk_rev(BwdArgs p) {
     }
 
     // ---------------- matrix-core waves
-    const int w = wave, c16 = lane & 15, g = lane >> 4;
+    const int w = wave < 2 ? wave : wave - 2, c16 = lane & 15, g = lane >> 4, mt = 64 * w + lane;
     const int il = 16 * w + c16, ig = 64 * tile + il;
     const int jw0 = JW * w;
     f32x4 eA[NJT];       // eps[ig][16 jt + 4 g + e]
@@ -685,12 +688,12 @@ __global__ __launch_bounds__(384) void kla_bwd_chunk_rev(BwdArgs p) {
                 eB[ib][jb] = mma_sx(ak, ld_col4(&sm.dO[b][4 * g][jw0 + 16 * jb + c16], D + 8), eB[ib][jb]);
         }
     };
-    mma_load<D>(p, row0, nch - 1, nvalid(nch - 1), mr);
+    mma_load<D>(p, row0, nch - 1, nvalid(nch - 1), mt, mr);
     for (int it = 0; it < nch + 2; ++it) {
         if (it < nch) {
             const int c = nch - 1 - it;
-            mma_stage<D>(mr, sm.dO[c & 1], sm.vv[c & 1]);
-            if (c >= 1) mma_load<D>(p, row0, c - 1, nvalid(c - 1), mr);
+            mma_stage<D>(mr, mt, sm.dO[c & 1], sm.vv[c & 1]);
+            if (c >= 1) mma_load<D>(p, row0, c - 1, nvalid(c - 1), mt, mr);
         }
         if (it >= 1 && it <= nch) step(nch - it);
         lds_barrier();
