@@ -385,6 +385,13 @@ struct Bc2Sm {
     alignas(16) float lk[3][64][kBP];     // k
     alignas(16) float ir[3][kBC];         // 1 / r
     alignas(16) float ub[2][64][kBP];     // U, key-major, by chunk parity
+    // the chunk's upper(V dO^T) and upper((W / G) A^T) as split K16 operands
+    // [t][s], formed once by the adjoint wave for the matrix-core waves
+    alignas(16) bf16 mvh[kBC][kBC + 4];
+    alignas(16) bf16 mvl[kBC][kBC + 4];
+    alignas(16) bf16 wdh[kBC][kBC + 4];
+    alignas(16) bf16 wdl[kBC][kBC + 4];
+    int hand;                             // chunk + 1 once they are written
     ChainStage cs;
     alignas(16) bf16 dO[2][kBC][D + 8];
     alignas(16) bf16 vv[2][kBC][D + 8];
@@ -411,6 +418,7 @@ __global__ __launch_bounds__(384) void kla_bwd_chunk_rev(BwdArgs p) {
         for (int t2 = 0; t2 < NT; ++t2) bad |= fl[t2];
         if (bad) return;  // uniform over the workgroup
     }
+    if (threadIdx.x == 0) sm.hand = 0;  // seen by the others after the first barrier
     auto nvalid = [&](int c) { return T - c * kBC < kBC ? T - c * kBC : kBC; };
 
     // waves go round-robin over the four SIMDs: the matrix-core waves are
@@ -576,8 +584,37 @@ __global__ __launch_bounds__(384) void kla_bwd_chunk_rev(BwdArgs p) {
             buf_store(dr[0], rows_of(ws + L.drp + (size_t)tile * L.t4, (size_t)c * kBC, nv, 1), base * 4);
             if (c >= 1) loadq(c - 1);  // lands during the next iteration
         };
+        // The chunk's two upper-triangular operands (the same for every
+        // matrix-core wave): lane (c16, g) holds rows t = c16, columns
+        // s = 4g + e of the accumulators, which is its K16 operand slot.
+        auto tri = [&](int c) {
+            const int b = c & 1, c16 = lane & 15, g = lane >> 4;
+            f32x4 Mt = zero4();
+#pragma unroll
+            for (int kb = 0; kb < D / 32; ++kb)
+                Mt = FB::mma(FB::ld(&sm.dO[b][c16][32 * kb], g), FB::ld(&sm.vv[b][c16][32 * kb], g), Mt);
+            f32x4 Wt = zero4();
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const SplitK32 xa = {FB::ld(&sm.ath[b][c16][32 * kb], g), FB::ld(&sm.atl[b][c16][32 * kb], g)};
+                const SplitK32 xw = {FB::ld(&sm.wth[b][c16][32 * kb], g), FB::ld(&sm.wtl[b][c16][32 * kb], g)};
+                Wt = Mma<float>::mma32(xa, xw, Wt);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                Mt[e] = 4 * g + e >= c16 ? Mt[e] : 0.f;
+                Wt[e] = 4 * g + e >= c16 ? Wt[e] : 0.f;
+            }
+            const SplitK16 ms = split4(Mt), wsp = split4(Wt);
+            *(s16x4*)&sm.mvh[c16][4 * g] = ms.hi;
+            *(s16x4*)&sm.mvl[c16][4 * g] = ms.lo;
+            *(s16x4*)&sm.wdh[c16][4 * g] = wsp.hi;
+            *(s16x4*)&sm.wdl[c16][4 * g] = wsp.lo;
+            __hip_atomic_store(&sm.hand, c + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        };
         loadq(nch - 1);
         for (int it = 0; it < nch + 2; ++it) {
+            if (it >= 1 && it <= nch) tri(nch - it);
             if (it >= 2) adj(nch + 1 - it);
             lds_barrier();
         }
@@ -619,15 +656,21 @@ __global__ __launch_bounds__(384) void kla_bwd_chunk_rev(BwdArgs p) {
             Pacc[2 * (jt & 1) + 1] = mfma16(vf, es.lo, Pacc[2 * (jt & 1) + 1]);
         }
         const f32x4 P1 = (Pacc[0] + Pacc[2]) + (Pacc[1] + Pacc[3]);
-        // lane holds (V dO^T)[t = c16][s = 4g + e]; keep s >= t
-        f32x4 Mt = zero4();
-#pragma unroll
-        for (int kb = 0; kb < D / 32; ++kb)
-            Mt = FB::mma(FB::ld(&sm.dO[b][c16][32 * kb], g), FB::ld(&sm.vv[b][c16][32 * kb], g), Mt);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) Mt[e] = 4 * g + e >= c16 ? Mt[e] : 0.f;
+        // the adjoint wave's upper(V dO^T) and upper((W / G) A^T) of this
+        // chunk: a bounded wait on its flag (within the workgroup, which it
+        // always reaches first thing in the iteration); should it ever run
+        // out, the (b,h) is handed to the token-serial kernel
+        {
+            int n = 0;
+            while (__hip_atomic_load(&sm.hand, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != c + 1 && n < (1 << 20)) {
+                __builtin_amdgcn_s_sleep(1);
+                ++n;
+            }
+            if (n == (1 << 20)) ((int*)(ws + L.flags))[tile] = 1;
+        }
         const SplitK16 as = {MB::ld16(&sm.akh[b][il][4 * g]), MB::ld16(&sm.akl[b][il][4 * g])};  // A[s][il]
-        const f32x4 P2 = Mma<float>::mma16(split4(Mt), as, zero4());
+        const f32x4 P2 = Mma<float>::mma16(SplitK16{MB::ld16(&sm.mvh[c16][4 * g]), MB::ld16(&sm.mvl[c16][4 * g])}, as,
+                                           zero4());
         // U = (1 / G) (.) (G_C P1 + P2), key-major for the adjoint wave
         {
             const f32x4 rg = *(const f32x4*)&sm.rgam[b][il][4 * g];
@@ -637,17 +680,7 @@ __global__ __launch_bounds__(384) void kla_bwd_chunk_rev(BwdArgs p) {
             for (int e = 0; e < 4; ++e) U[e] = rg[e] * __builtin_fmaf(gev, P1[e], P2[e]);
             *(f32x4*)&sm.ub[b][il][4 * g] = U;
         }
-        // lane holds ((W / G) A^T)[t = c16][s = 4g + e] over the tile's key dims; keep s >= t
-        f32x4 Wt = zero4();
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            const SplitK32 xa = {FB::ld(&sm.ath[b][c16][32 * kb], g), FB::ld(&sm.atl[b][c16][32 * kb], g)};
-            const SplitK32 xw = {FB::ld(&sm.wth[b][c16][32 * kb], g), FB::ld(&sm.wtl[b][c16][32 * kb], g)};
-            Wt = Mma<float>::mma32(xa, xw, Wt);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) Wt[e] = 4 * g + e >= c16 ? Wt[e] : 0.f;
-        const SplitK16 wd = split4(Wt);
+        const SplitK16 wd = {MB::ld16(&sm.wdh[c16][4 * g]), MB::ld16(&sm.wdl[c16][4 * g])};
         // G_C (.) eps on the rows of the value-column copy
 #pragma unroll
         for (int ib = 0; ib < 4; ++ib) {

@@ -63,29 +63,38 @@ struct Mma<bf16> {
 struct SplitK32 { bf16x8 hi, lo; };
 struct SplitK16 { s16x4 hi, lo; };
 
+// hi = bf16(x) (round to nearest even) for a pair, two per conversion
+// instruction; the hi values back as floats by a shift or a mask of the
+// packed word; lo = bf16(x - hi) likewise (x - hi is exact).
+__device__ __forceinline__ void split_pair(float x0, float x1, unsigned& hi, unsigned& lo) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    hi = __builtin_bit_cast(unsigned, __builtin_convertvector((f2){x0, x1}, b2));
+    const float h0 = __builtin_bit_cast(float, hi << 16), h1 = __builtin_bit_cast(float, hi & 0xffff0000u);
+    lo = __builtin_bit_cast(unsigned, __builtin_convertvector((f2){x0 - h0, x1 - h1}, b2));
+}
+
 __device__ __forceinline__ SplitK32 split8(f32x4 a, f32x4 b) {  // slots 0-3 from a, 4-7 from b
+    typedef unsigned u4 __attribute__((ext_vector_type(4)));
+    unsigned h0, h1, h2, h3, l0, l1, l2, l3;
+    split_pair(a[0], a[1], h0, l0);
+    split_pair(a[2], a[3], h1, l1);
+    split_pair(b[0], b[1], h2, l2);
+    split_pair(b[2], b[3], h3, l3);
     SplitK32 r;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const bf16 ha = (bf16)a[e], hb = (bf16)b[e];
-        r.hi[e] = ha;
-        r.hi[e + 4] = hb;
-        r.lo[e] = (bf16)(a[e] - (float)ha);
-        r.lo[e + 4] = (bf16)(b[e] - (float)hb);
-    }
+    r.hi = __builtin_bit_cast(bf16x8, (u4){h0, h1, h2, h3});
+    r.lo = __builtin_bit_cast(bf16x8, (u4){l0, l1, l2, l3});
     return r;
 }
 
 __device__ __forceinline__ SplitK16 split4(f32x4 a) {
-    bf16x4 h, l;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        h[e] = (bf16)a[e];
-        l[e] = (bf16)(a[e] - (float)h[e]);
-    }
+    typedef unsigned u2 __attribute__((ext_vector_type(2)));
+    unsigned h0, h1, l0, l1;
+    split_pair(a[0], a[1], h0, l0);
+    split_pair(a[2], a[3], h1, l1);
     SplitK16 r;
-    r.hi = __builtin_bit_cast(s16x4, h);
-    r.lo = __builtin_bit_cast(s16x4, l);
+    r.hi = __builtin_bit_cast(s16x4, (u2){h0, h1});
+    r.lo = __builtin_bit_cast(s16x4, (u2){l0, l1});
     return r;
 }
 
