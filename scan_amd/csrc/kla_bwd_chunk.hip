@@ -200,6 +200,7 @@ struct Bc1Sm {
     alignas(16) bf16 dO[2][kBC][D + 8];
     alignas(16) bf16 vv[2][kBC][D + 8];
     alignas(16) float ost[4][2][kBC][16 + 4];
+    int badw[4];                         // a matrix-core wave saw G out of range
 };
 
 template <int D>
@@ -222,9 +223,8 @@ __global__ __launch_bounds__(320) void kla_bwd_chunk_fwd(BwdArgs p) {
         const int il = lane, i = 64 * tile + il;
         float l = p.l0 ? p.l0[(size_t)bh * D + i] : 1.f;
         const float qn = p.qn[(size_t)h * D + i];
-        bool bad = false;
-        // the serial part only: the precision, G and the gate guard; the
-        // matrix-core waves form W / G, 1 / l and q / l for their own tokens
+        // the serial part only: the precision and G; the matrix-core waves
+        // form W / G, 1 / l and q / l for their own tokens and check G's range
         auto chain = [&](int c, float rlane) {
             const int b = c & 1, nv = nvalid(c);
             ws[L.lst + (size_t)c * D + i] = l;  // the precision before the chunk
@@ -237,7 +237,6 @@ __global__ __launch_bounds__(320) void kla_bwd_chunk_fwd(BwdArgs p) {
             const float irl = fast_rcp(lane < nv ? rlane : 1.f);
             if (lane < kBC) sm.ir[b][lane] = irl;
             float gam = 1.f;
-            bool ok = true;
             float vg[kBC], vl[kBC];
 #pragma unroll
             for (int u = 0; u < kBC; ++u) {
@@ -246,7 +245,6 @@ __global__ __launch_bounds__(320) void kla_bwd_chunk_fwd(BwdArgs p) {
                 const float g = in ? af[u] * rd : 1.f;
                 l = in ? __builtin_fmaf(kf[u] * kf[u], uni(irl, u), l * rd) : l;
                 gam *= g;
-                ok = ok && gam >= kGLo && gam <= kGHi;
                 vg[u] = gam;
                 vl[u] = l;
             }
@@ -256,7 +254,6 @@ __global__ __launch_bounds__(320) void kla_bwd_chunk_fwd(BwdArgs p) {
                 *(f32x4*)&sm.lt[b][il][u] = f32x4{vl[u], vl[u + 1], vl[u + 2], vl[u + 3]};
             }
             sm.ge[b][il] = gam;
-            bad = bad || !ok;
         };
         ChainRaw x;
         chain_load(p, row0, 0, nvalid(0), tile, lane, x);
@@ -270,8 +267,8 @@ __global__ __launch_bounds__(320) void kla_bwd_chunk_fwd(BwdArgs p) {
             }
             lds_barrier();
         }
-        const bool anybad = __any(bad ? 1 : 0);
-        if (lane == 0) ((int*)(ws + L.flags))[tile] = anybad ? 1 : 0;
+        lds_barrier();  // the matrix-core waves' range checks are in
+        if (lane == 0) ((int*)(ws + L.flags))[tile] = (sm.badw[0] | sm.badw[1] | sm.badw[2] | sm.badw[3]) ? 1 : 0;
         return;
     }
 
@@ -283,6 +280,7 @@ __global__ __launch_bounds__(320) void kla_bwd_chunk_fwd(BwdArgs p) {
     for (int jt = 0; jt < NJT; ++jt)
         eta[jt] = p.eta0 ? *(const f32x4*)&p.eta0[((size_t)bh * D + ig) * D + 16 * jt + 4 * g] : zero4();
     MmaRaw<D> mr;
+    bool bad = false;  // G of the lane's tokens and key dim left [2^-64, 2^64]
     auto step = [&](int c) {
         const int b = c & 1, nv = nvalid(c);
         // X = dO eta_in^T, the state tiles as the B operand (K16 over value columns)
@@ -308,6 +306,8 @@ __global__ __launch_bounds__(320) void kla_bwd_chunk_fwd(BwdArgs p) {
         // (rows past the end: k = q = 0)
         const f32x4 gm = *(const f32x4*)&sm.gam[b][il][4 * g];
         const f32x4 lv = *(const f32x4*)&sm.lt[b][il][4 * g];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bad = bad || !(gm[e] >= kGLo && gm[e] <= kGHi);
         const f32x4 irv = *(const f32x4*)&sm.ir[b][4 * g];
         f32x4 wgv, rlv, qhv;
 #pragma unroll
@@ -362,6 +362,9 @@ __global__ __launch_bounds__(320) void kla_bwd_chunk_fwd(BwdArgs p) {
     z += __shfl_xor(z, 16, 64);
     z += __shfl_xor(z, 32, 64);
     if (g == 0) ws[L.z + ig] = z;
+    const int wb = __any(bad ? 1 : 0);
+    if (lane == 0) sm.badw[w] = wb;
+    lds_barrier();  // the chain wave writes the flag
 }
 
 // ============================================================ reverse sweep
