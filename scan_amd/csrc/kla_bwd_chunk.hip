@@ -34,17 +34,20 @@
 // row tiles, 8 workgroups apart so that they share an XCD and its v, dO):
 // - kla_bwd_chunk_fwd: four matrix-core waves (16 key dims each, the state
 //   rows eta[i][:] in accumulator tiles; each forms W / G, 1 / l and q / l of
-//   its own tokens and key dims) and a chain wave one chunk ahead (the
-//   precision recursion, G, and l at chunk starts); writes dq, Q, the
-//   chunk-start precisions and <detaT, eta_T>.
-// - kla_bwd_chunk_rev: chunks last to first; a chain wave recomputes the
-//   chunk's precision from its start and splits A and W / G into bf16 pairs
-//   once for all four matrix-core waves, which hold the
-//   adjoint twice (eps[i][:] of 16 key dims for U and the update, and
-//   eps[:][j] of D/4 value columns over the tile's 64 key dims for dv: the
-//   two products contract it along different axes) and a precision-adjoint
-//   wave runs two chunks behind the chain.  dv and dr leave per-tile
-//   partials that a third kernel sums.
+//   its own tokens and key dims and checks the range of G) and a chain wave
+//   one chunk ahead (the precision recursion, G, and l at chunk starts);
+//   writes dq, Q, the chunk-start precisions, <detaT, eta_T> and the flag.
+// - kla_bwd_chunk_rev: chunks last to first.  A chain wave recomputes the
+//   chunk's precision from its start, splits A and W / G into bf16 pairs
+//   once for all matrix-core waves and hands the precision adjoint g,
+//   P = l_{t-1} / D and 1 / a.  Four matrix-core waves hold the adjoint
+//   twice: eps[i][:] of 16 key dims for U and the update, and eps[:][j] of
+//   D/4 value columns over the tile's 64 key dims for dv (the two products
+//   contract it along different axes).  The precision-adjoint wave runs two
+//   chunks behind the chain; at the start of each iteration it also forms
+//   the chunk's two upper-triangular operands, which the matrix-core waves
+//   take from LDS after a bounded wait on its flag.  dv and dr leave
+//   per-tile partials that a third kernel sums.
 // The quotients W / G and 1 / G need G in [2^-64, 2^64]: a (b,h) whose decay
 // products leave that range in some chunk is flagged by the forward sweep,
 // skipped by the reverse sweep and redone by the token-serial kernel.
