@@ -516,6 +516,7 @@ klaStatus klaBwd(const klaDims* d, const void* q, const void* k, const void* v, 
                                      d->dtype == KLA_BF16 ? kla::DT_BF16 : kla::DT_F32);
     ba.gate_nt = 0;
     ba.flag_off = 0;
+    ba.spin = 1 << 20;
     ba.B = d->B; ba.H = d->H; ba.T = d->T; ba.dk = d->dk; ba.dv = d->dv;
     const hipError_t e = kla::launch_bwd(ba, d->dtype, iso ? 1 : 0, (hipStream_t)hipStream);
     if (e == hipErrorInvalidValue) return KLA_ERR_UNSUPPORTED;

@@ -41,6 +41,9 @@ struct BwdArgs {
     // (b,h) is set (a sequence the chunked kernels handed back)
     int gate_nt;
     size_t flag_off;
+    // polls of the chunked reverse sweep's in-workgroup wait before it hands
+    // the (b,h) back (KLA_BWD_SPIN overrides; 0 forces the hand-back)
+    int spin;
 };
 
 // Workspace of the chunked backward (floats from the start of a (b,h)'s

@@ -668,11 +668,11 @@ __global__ __launch_bounds__(384) void kla_bwd_chunk_rev(BwdArgs p) {
         // out, the (b,h) is handed to the token-serial kernel
         {
             int n = 0;
-            while (__hip_atomic_load(&sm.hand, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != c + 1 && n < (1 << 20)) {
+            while (__hip_atomic_load(&sm.hand, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != c + 1 && n < p.spin) {
                 __builtin_amdgcn_s_sleep(1);
                 ++n;
             }
-            if (n == (1 << 20)) ((int*)(ws + L.flags))[tile] = 1;
+            if (n >= p.spin) ((int*)(ws + L.flags))[tile] = 1;
         }
         const SplitK16 as = {MB::ld16(&sm.akh[b][il][4 * g]), MB::ld16(&sm.akl[b][il][4 * g])};  // A[s][il]
         const f32x4 P2 = Mma<float>::mma16(SplitK16{MB::ld16(&sm.mvh[c16][4 * g]), MB::ld16(&sm.mvl[c16][4 * g])}, as,
@@ -790,8 +790,11 @@ bool bwd_chunk_supported(int dk, int dv, int cov, int dtype, int T) {
 
 hipError_t launch_bwd_chunk(const BwdArgs& a, int dtype, hipStream_t s) {
     if (!bwd_chunk_supported(a.dk, a.dv, 0, dtype, a.T) || a.B * a.H == 0) return hipErrorInvalidValue;
-    if (a.dk == 64) launch<64>(a, s);
-    else launch<128>(a, s);
+    BwdArgs b = a;
+    const char* e = getenv("KLA_BWD_SPIN");
+    if (e && *e) b.spin = atoi(e) < 0 ? 0 : atoi(e);
+    if (a.dk == 64) launch<64>(b, s);
+    else launch<128>(b, s);
     return hipGetLastError();
 }
 

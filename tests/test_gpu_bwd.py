@@ -214,3 +214,24 @@ def test_bwd_chunk_matches_token_serial(monkeypatch):
     errs = bwd_errors(chunk, serial, "diag")
     print("chunk vs serial", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
     assert all(v <= TOL["bf16"] for v in errs.values()), errs
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_chunk_wait_timeout_hands_back(monkeypatch, d):
+    """The reverse sweep's in-workgroup wait, forced to give up at once from
+    the host (KLA_BWD_SPIN=0): every (b,h) is flagged and redone by the
+    token-serial kernel, and the gradients still match the oracle."""
+    _print_case("bwd chunk forced hand-back", d)
+    monkeypatch.setenv("KLA_BWD_SPIN", "0")
+    inp = gen.make_inputs("lm_diag", seed=390, B=2, H=3, T=70, dk=d, dv=d)
+    w = inp["workload"]
+    st = gen.make_state(w, seed=391)
+    up = gen.make_upstream(w, seed=392)
+    got = run_bwd(inp, up, "diag", st)
+    check(got, run_ref(inp, up, "diag", st), "diag", "bf16", f"bwd forced hand-back d={d}")
+    # the same kernel run directly (one row group) gives the same bits
+    monkeypatch.setenv("KLA_BWD_IMPL", "rows")
+    monkeypatch.setenv("KLA_BWD_NRG", "1")
+    serial = run_bwd(inp, up, "diag", st)
+    for n in GRADS:
+        assert np.array_equal(got[n], serial[n]), n
