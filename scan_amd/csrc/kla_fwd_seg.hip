@@ -52,6 +52,21 @@ __device__ __forceinline__ bool seg_warm_ok(const FwdArgs& p, const int* ok, int
     return all != 0;
 }
 
+// Every (b,h) settled by the warm-up, checked by the whole workgroup at once
+// (one flag per thread, a workgroup vote) when the flags fit; the launches
+// that only handle unsettled ones then end at once.
+__device__ __forceinline__ bool seg_all_warm_ok(const FwdArgs& p, const int* ok) {
+    const int per = 2 * p.nseg, n = p.B * p.H * per;
+    if (n > (int)blockDim.x) return false;  // too many: checked per (b,h)
+    int good = 1;
+    const int x = (int)threadIdx.x;
+    if (x < n) {
+        const int bh = x / per, k = x % per;
+        if (k >= 2 && (k % 2 == 0 || p.dk == 128)) good = ok[seg_row(p, bh, 0) * 2 + k];
+    }
+    return __syncthreads_and(good) != 0;
+}
+
 // Scale a positive 2x2 map by a power of two (exact; the map is unchanged)
 // so that its entries sum to [1, 2).
 __device__ __forceinline__ void mob_renorm(double& p00, double& p01, double& p10, double& p11) {
@@ -320,8 +335,8 @@ __global__ __launch_bounds__(kMobThreads) void kla_seg_mobius(FwdArgs p, float* 
     __shared__ f32x4 sP[NSUB][DK];
     const int i = threadIdx.x % DK, sub = threadIdx.x / DK;
     const int nb = seg_blocks(p);
-    // at most kMobGrid workgroups stride over the blocks, so that the launch
-    // ends at once when the warm-up settled every (b,h)
+    if (seg_all_warm_ok(p, ok)) return;  // uniform over the workgroup
+    // at most kMobGrid workgroups stride over the blocks
     for (int blk = blockIdx.x; blk < p.B * p.H * nb; blk += gridDim.x) {
         const int bh = blk / nb, s = blk % nb;
         if (seg_warm_ok(p, ok, bh)) continue;  // uniform over the workgroup
@@ -333,6 +348,7 @@ __global__ __launch_bounds__(kMobThreads) void kla_seg_mobius(FwdArgs p, float* 
 // -------------------------------------------------- 2. precision carry
 __global__ void kla_seg_carry_l(FwdArgs p, const float* P, const int* ok) {
     const int n = p.B * p.H * p.dk;
+    if (seg_all_warm_ok(p, ok)) return;  // uniform over the workgroup
     const int x = blockIdx.x * blockDim.x + threadIdx.x;
     if (x >= n) return;
     const int bh = x / p.dk, i = x % p.dk;
