@@ -78,11 +78,12 @@ bool bwd_supported(int dk, int dv);
 size_t bwd_ws_stride(int B, int H, int T, int dk, int cov, int dtype);
 hipError_t launch_bwd(const BwdArgs& a, int dtype, int cov, hipStream_t s);
 
-// The chunked backward on the matrix cores (kla_bwd_chunk.hip): diagonal,
-// bf16, dk = dv in {64, 128}, T >= 1; KLA_BWD_IMPL=rows or plain turns it off.
+// The chunked backward on the matrix cores (kla_bwd_chunk.hip): bf16, T >= 1,
+// diagonal with dk = dv in {64, 128} or isotropic with dk = dv = 64;
+// KLA_BWD_IMPL=rows or plain turns it off.
 bool bwd_chunk_supported(int dk, int dv, int cov, int dtype, int T);
 // Its three launches (forward sweep, reverse sweep, dv/dr combine); the
 // caller then runs the token-serial kernel gated on the flags.
-hipError_t launch_bwd_chunk(const BwdArgs& a, int dtype, hipStream_t s);
+hipError_t launch_bwd_chunk(const BwdArgs& a, int dtype, int cov, hipStream_t s);
 
 }  // namespace kla

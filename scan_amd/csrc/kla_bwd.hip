@@ -132,6 +132,18 @@ __global__ __launch_bounds__(kBwdThreads) void kla_bwd_kernel(BwdArgs p) {
     const int tid = threadIdx.x;
     const int grp = NH == 1 ? 0 : tid / NTH, lt = NH == 1 ? tid : tid % NTH;
     const int nbh = p.B * p.H, bh_ = NH == 1 ? (int)blockIdx.x : (int)blockIdx.x * NH + grp;
+    // after the chunked kernels: only the (b,h) they handed back
+    if (p.gate_nt > 0) {
+        int any = 0;
+        for (int g2 = 0; g2 < NH; ++g2) {
+            const int b2 = NH == 1 ? (int)blockIdx.x : (int)blockIdx.x * NH + g2;
+            if (b2 < nbh) {
+                const int* fl = (const int*)(p.ws + (size_t)b2 * p.ws_stride + p.flag_off);
+                for (int t2 = 0; t2 < p.gate_nt; ++t2) any |= fl[t2];
+            }
+        }
+        if (!any) return;  // uniform over the workgroup
+    }
     const bool valid = NH == 1 || bh_ < nbh;
     const int bh = valid ? bh_ : nbh - 1;  // a spare group stays in bounds and stores nothing
     const int h = bh % p.H;
@@ -1361,15 +1373,18 @@ bool bwd_plain() {
 
 template <typename TIn, int D, bool ISO>
 void launch_d(const BwdArgs& a, dim3 grid, dim3 block, hipStream_t s) {
-    if constexpr (!ISO && (D == 64 || D == 128) && std::is_same<TIn, bf16>::value) {
-        if (bwd_chunk_supported(a.dk, a.dv, 0, DT_BF16, a.T)) {
+    if constexpr ((D == 64 || (D == 128 && !ISO)) && std::is_same<TIn, bf16>::value) {
+        if (bwd_chunk_supported(a.dk, a.dv, ISO ? 1 : 0, DT_BF16, a.T)) {
             // the chunked kernels, then the token-serial kernel for the (b,h)
             // whose decay products left the range of the chunk quotients
-            if (launch_bwd_chunk(a, DT_BF16, s) != hipSuccess) return;
+            if (launch_bwd_chunk(a, DT_BF16, ISO ? 1 : 0, s) != hipSuccess) return;
             BwdArgs f = a;
             f.gate_nt = D / 64;
             f.flag_off = bc_layout(a.T, D).flags;
-            hipLaunchKernelGGL((kla_bwd_diag_kernel<TIn, D, 1>), grid, block, 0, s, f);
+            if constexpr (ISO)
+                hipLaunchKernelGGL((kla_bwd_kernel<TIn, D, true>), grid, block, 0, s, f);
+            else
+                hipLaunchKernelGGL((kla_bwd_diag_kernel<TIn, D, 1>), grid, block, 0, s, f);
             return;
         }
     }

@@ -1,5 +1,5 @@
-// kla_bwd_chunk.hip -- gfx950 chunked backward of the diagonal forward on the
-// matrix cores (bf16 inputs, dk = dv in {64, 128}).
+// kla_bwd_chunk.hip -- gfx950 chunked backward of the forward on the matrix
+// cores (bf16 inputs; diagonal at dk = dv in {64, 128}, isotropic at 64).
 //
 // Sources: "Kalman Linear Attention: Parallel Bayesian Filtering For Efficient
 // Language Modelling and State Tracking" (fugumt abstract page: the filter is
@@ -48,6 +48,10 @@
 //   the chunk's two upper-triangular operands, which the matrix-core waves
 //   take from LDS after a bounded wait on its flag.  dv and dr leave
 //   per-tile partials that a third kernel sums.
+// Isotropic (one row tile): the precision, decay and process noise are
+// scalars per token, written into every lane's row, so the matrix-core code
+// is shared; the chain waves form |k_t|^2 over the key dims, the adjoint
+// wave sums Q and w U over them and runs the scalar recursion.
 // The quotients W / G and 1 / G need G in [2^-64, 2^64]: a (b,h) whose decay
 // products leave that range in some chunk is flagged by the forward sweep,
 // skipped by the reverse sweep and redone by the token-serial kernel.
@@ -115,29 +119,37 @@ __device__ __forceinline__ void bc_place(int& bh, int& tile) {
 struct ChainRaw {
     i32x4 k[2], q[2], a[4];
     float r, l;
+    float as, qs;  // isotropic: a and qn of token lane % 16
 };
 struct ChainStage {
     alignas(16) bf16 rk[kBC][64 + 8];
     alignas(16) bf16 rq[kBC][64 + 8];
     alignas(16) float ra[kBC][kTM];
 };
+template <bool ISO>
 __device__ __forceinline__ void chain_load(const BwdArgs& p, size_t row0, int c, int nv, int tile, int lane,
                                            ChainRaw& x) {
     const int D = p.dk, lt = lane >> 2, ld = 16 * (lane & 3);
     const size_t r0 = row0 + (size_t)c * kBC;
     const auto rk = rows_of((const bf16*)p.k, r0, nv, D);
     const auto rq = rows_of((const bf16*)p.q, r0, nv, D);
-    const auto ra = rows_of(p.a, r0, nv, D);
+    const auto ra = rows_of(p.a, r0, ISO ? 0 : nv, D);
     const int ko = (lt * D + 64 * tile + ld) * 2;
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
         x.k[m] = buf_load<i32x4>(rk, ko + 16 * m);
         x.q[m] = buf_load<i32x4>(rq, ko + 16 * m);
     }
+    if constexpr (ISO) {
+        x.as = buf_load<float>(make_rsrc(p.a + r0, nv * 4), (lane & 15) * 4);
+        x.qs = buf_load<float>(make_rsrc(p.qn + r0, nv * 4), (lane & 15) * 4);
+    } else {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) x.a[m] = buf_load<i32x4>(ra, (lt * D + 64 * tile + ld + 4 * m) * 4);
+        for (int m = 0; m < 4; ++m) x.a[m] = buf_load<i32x4>(ra, (lt * D + 64 * tile + ld + 4 * m) * 4);
+    }
     x.r = buf_load<float>(make_rsrc(p.r + r0, nv * 4), (lane & 15) * 4);
 }
+template <bool ISO>
 __device__ __forceinline__ void chain_stage(ChainStage& st, const ChainRaw& x, int lane) {
     const int lt = lane >> 2, ld = 16 * (lane & 3);
 #pragma unroll
@@ -145,8 +157,43 @@ __device__ __forceinline__ void chain_stage(ChainStage& st, const ChainRaw& x, i
         *(i32x4*)&st.rk[lt][ld + 8 * m] = x.k[m];
         *(i32x4*)&st.rq[lt][ld + 8 * m] = x.q[m];
     }
+    if constexpr (!ISO) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) *(i32x4*)&st.ra[lt][ld + 4 * m] = x.a[m];
+        for (int m = 0; m < 4; ++m) *(i32x4*)&st.ra[lt][ld + 4 * m] = x.a[m];
+    }
+}
+
+// The chain's per-token inputs: a, qn and k^2 (diagonal, per key dim) or the
+// head's scalars a_t, qn_t and |k_t|^2 / dk (isotropic; |k|^2 summed over the
+// wave's 64 key dims by a reduce-scatter, token u then held by lane
+// 32 b3 + 16 b2 + 8 b1 + 4 b0 of u).  Tokens past the end: a = qn = 1.
+template <bool ISO, int D>
+__device__ __forceinline__ void chain_inputs(const ChainStage& st, int il, int lane, int nv, float qn_dim, float as,
+                                             float qs, float (&kf)[kBC], float (&af)[kBC], float (&qv)[kBC],
+                                             float (&kk)[kBC]) {
+#pragma unroll
+    for (int u = 0; u < kBC; ++u) kf[u] = (float)st.rk[u][il];
+    if constexpr (ISO) {
+        float ks[kBC];
+#pragma unroll
+        for (int u = 0; u < kBC; ++u) ks[u] = kf[u] * kf[u];
+        int base = 0;
+        reduce_scatter<kBC, 32>(ks, lane, base);
+#pragma unroll
+        for (int u = 0; u < kBC; ++u) {
+            const int ol = ((u >> 3) & 1) << 5 | ((u >> 2) & 1) << 4 | ((u >> 1) & 1) << 3 | (u & 1) << 2;
+            kk[u] = uni(ks[0], ol) * (1.f / (float)D);
+            af[u] = u < nv ? uni(as, u) : 1.f;
+            qv[u] = u < nv ? uni(qs, u) : 1.f;
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < kBC; ++u) {
+            af[u] = st.ra[u][il];
+            qv[u] = qn_dim;
+            kk[u] = kf[u] * kf[u];
+        }
+    }
 }
 
 // A chunk's 16 rows of dO and v in 16-byte pieces over the 256 lanes of the
@@ -206,7 +253,7 @@ struct Bc1Sm {
     int badw[4];                         // a matrix-core wave saw G out of range
 };
 
-template <int D>
+template <int D, bool ISO>
 __global__ __launch_bounds__(320) void kla_bwd_chunk_fwd(BwdArgs p) {
     constexpr int NT = D / 64, NJT = D / 16;
     __shared__ Bc1Sm<D> sm;
@@ -224,19 +271,16 @@ __global__ __launch_bounds__(320) void kla_bwd_chunk_fwd(BwdArgs p) {
     if (wave == 4) {
         // ---------------- chain: one lane per key dim
         const int il = lane, i = 64 * tile + il;
-        float l = p.l0 ? p.l0[(size_t)bh * D + i] : 1.f;
-        const float qn = p.qn[(size_t)h * D + i];
+        // isotropic: one precision per head, the same in every lane
+        float l = p.l0 ? p.l0[ISO ? (size_t)bh : (size_t)bh * D + i] : 1.f;
+        const float qn = ISO ? 0.f : p.qn[(size_t)h * D + i];
         // the serial part only: the precision and G; the matrix-core waves
         // form W / G, 1 / l and q / l for their own tokens and check G's range
-        auto chain = [&](int c, float rlane) {
+        auto chain = [&](int c, float rlane, float as, float qs) {
             const int b = c & 1, nv = nvalid(c);
             ws[L.lst + (size_t)c * D + i] = l;  // the precision before the chunk
-            float kf[kBC], af[kBC];
-#pragma unroll
-            for (int u = 0; u < kBC; ++u) {
-                kf[u] = (float)sm.cs[b].rk[u][il];
-                af[u] = sm.cs[b].ra[u][il];
-            }
+            float kf[kBC], af[kBC], qv[kBC], kk[kBC];
+            chain_inputs<ISO, D>(sm.cs[b], il, lane, nv, qn, as, qs, kf, af, qv, kk);
             const float irl = fast_rcp(lane < nv ? rlane : 1.f);
             if (lane < kBC) sm.ir[b][lane] = irl;
             float gam = 1.f;
@@ -244,9 +288,9 @@ __global__ __launch_bounds__(320) void kla_bwd_chunk_fwd(BwdArgs p) {
 #pragma unroll
             for (int u = 0; u < kBC; ++u) {
                 const bool in = u < nv;
-                const float rd = fast_rcp(__builtin_fmaf(qn, l, af[u] * af[u]));
+                const float rd = fast_rcp(__builtin_fmaf(qv[u], l, af[u] * af[u]));
                 const float g = in ? af[u] * rd : 1.f;
-                l = in ? __builtin_fmaf(kf[u] * kf[u], uni(irl, u), l * rd) : l;
+                l = in ? __builtin_fmaf(kk[u], uni(irl, u), l * rd) : l;
                 gam *= g;
                 vg[u] = gam;
                 vl[u] = l;
@@ -259,14 +303,14 @@ __global__ __launch_bounds__(320) void kla_bwd_chunk_fwd(BwdArgs p) {
             sm.ge[b][il] = gam;
         };
         ChainRaw x;
-        chain_load(p, row0, 0, nvalid(0), tile, lane, x);
+        chain_load<ISO>(p, row0, 0, nvalid(0), tile, lane, x);
         for (int it = 0; it <= nch; ++it) {
             if (it < nch) {
-                chain_stage(sm.cs[it & 1], x, lane);
-                const float rl = x.r;
-                if (it + 1 < nch) chain_load(p, row0, it + 1, nvalid(it + 1), tile, lane, x);
+                chain_stage<ISO>(sm.cs[it & 1], x, lane);
+                const float rl = x.r, as = x.as, qs = x.qs;
+                if (it + 1 < nch) chain_load<ISO>(p, row0, it + 1, nvalid(it + 1), tile, lane, x);
                 wave_sync();
-                chain(it, rl);
+                chain(it, rl, as, qs);
             }
             lds_barrier();
         }
@@ -390,6 +434,8 @@ struct Bc2Sm {
     alignas(16) float lw[3][64][kBP];     // w = k / r
     alignas(16) float lk[3][64][kBP];     // k
     alignas(16) float ir[3][kBC];         // 1 / r
+    alignas(16) float lks[3][kBC];        // isotropic: |k|^2 / dk
+    alignas(16) float lqn[3][kBC];        // isotropic: qn
     alignas(16) float ub[2][64][kBP];     // U, key-major, by chunk parity
     // the chunk's upper(V dO^T) and upper((W / G) A^T) as split K16 operands
     // [t][s], formed once by the adjoint wave for the matrix-core waves
@@ -403,7 +449,7 @@ struct Bc2Sm {
     alignas(16) bf16 vv[2][kBC][D + 8];
 };
 
-template <int D>
+template <int D, bool ISO>
 __global__ __launch_bounds__(384) void kla_bwd_chunk_rev(BwdArgs p) {
     constexpr int NT = D / 64, NJT = D / 16, JW = D / 4, NJB = JW / 16;
     __shared__ Bc2Sm<D> sm;
@@ -433,18 +479,24 @@ __global__ __launch_bounds__(384) void kla_bwd_chunk_rev(BwdArgs p) {
     if (wave == 2) {
         // ---------------- chain: the chunk's precision again, from its start
         const int il = lane, i = 64 * tile + il;
-        const float qn = p.qn[(size_t)h * D + i];
-        auto chain = [&](int c, float rlane, float l) {
+        const float qn = ISO ? 0.f : p.qn[(size_t)h * D + i];
+        auto chain = [&](int c, float rlane, float l, float as, float qs) {
             const int b2 = c & 1, b3 = c % 3, nv = nvalid(c);
-            float kf[kBC], qf[kBC], af[kBC];
+            float kf[kBC], qf[kBC], af[kBC], qv[kBC], kk[kBC];
+            chain_inputs<ISO, D>(sm.cs, il, lane, nv, qn, as, qs, kf, af, qv, kk);
 #pragma unroll
-            for (int u = 0; u < kBC; ++u) {
-                kf[u] = (float)sm.cs.rk[u][il];
-                qf[u] = (float)sm.cs.rq[u][il];
-                af[u] = sm.cs.ra[u][il];
-            }
+            for (int u = 0; u < kBC; ++u) qf[u] = (float)sm.cs.rq[u][il];
             const float irl = fast_rcp(lane < nv ? rlane : 1.f);
             if (lane < kBC) sm.ir[b3][lane] = irl;
+            if constexpr (ISO) {
+                if (lane == 0) {
+#pragma unroll
+                    for (int u = 0; u < kBC; u += 4) {
+                        *(f32x4*)&sm.lks[b3][u] = f32x4{kk[u], kk[u + 1], kk[u + 2], kk[u + 3]};
+                        *(f32x4*)&sm.lqn[b3][u] = f32x4{qv[u], qv[u + 1], qv[u + 2], qv[u + 3]};
+                    }
+                }
+            }
             // 1 / G as a running product of D / a (the reciprocal of a is
             // needed by the precision adjoint anyway)
             float gam = 1.f, rg = 1.f;
@@ -454,7 +506,7 @@ __global__ __launch_bounds__(384) void kla_bwd_chunk_rev(BwdArgs p) {
             for (int u = 0; u < kBC; ++u) {
                 const bool in = u < nv;
                 const float ir = uni(irl, u);
-                const float Dn = __builtin_fmaf(qn, l, af[u] * af[u]);
+                const float Dn = __builtin_fmaf(qv[u], l, af[u] * af[u]);
                 const float rd = fast_rcp(Dn);
                 const float ia = fast_rcp(in ? af[u] : 1.f);
                 const float g = in ? af[u] * rd : 1.f;
@@ -462,7 +514,7 @@ __global__ __launch_bounds__(384) void kla_bwd_chunk_rev(BwdArgs p) {
                 vg[u] = g;
                 vP[u] = P;
                 vi[u] = ia;
-                l = in ? __builtin_fmaf(kf[u] * kf[u], ir, P) : l;
+                l = in ? __builtin_fmaf(kk[u], ir, P) : l;
                 gam *= g;
                 rg *= in ? Dn * ia : 1.f;
                 const float wv = kf[u] * ir;
@@ -494,18 +546,18 @@ __global__ __launch_bounds__(384) void kla_bwd_chunk_rev(BwdArgs p) {
         };
         ChainRaw x;
         auto load = [&](int c) {
-            chain_load(p, row0, c, nvalid(c), tile, lane, x);
+            chain_load<ISO>(p, row0, c, nvalid(c), tile, lane, x);
             x.l = ws[L.lst + (size_t)c * D + i];
         };
         load(nch - 1);
         for (int it = 0; it < nch + 2; ++it) {
             if (it < nch) {
                 const int c = nch - 1 - it;
-                chain_stage(sm.cs, x, lane);
-                const float rl = x.r, lc = x.l;
+                chain_stage<ISO>(sm.cs, x, lane);
+                const float rl = x.r, lc = x.l, as = x.as, qs = x.qs;
                 if (c >= 1) load(c - 1);
                 wave_sync();
-                chain(c, rl, lc);
+                chain(c, rl, lc, as, qs);
             }
             lds_barrier();
         }
@@ -515,9 +567,15 @@ __global__ __launch_bounds__(384) void kla_bwd_chunk_rev(BwdArgs p) {
     if (wave == 3) {
         // ---------------- precision adjoint, two chunks behind the chain
         const int il = lane, i = 64 * tile + il;
-        const float qn = p.qn[(size_t)h * D + i];
-        float lbar = p.dlT ? p.dlT[(size_t)bh * D + i] : 0.f;
+        const float qn = ISO ? 0.f : p.qn[(size_t)h * D + i];
+        // isotropic: lbar and dlog g are the head's scalars (the same in every
+        // lane), dlog g summing <detaT, eta_T> over the key dims
+        float lbar = p.dlT ? p.dlT[ISO ? (size_t)bh : (size_t)bh * D + i] : 0.f;
         float cum = ws[L.z + i];
+        if constexpr (ISO) {
+#pragma unroll
+            for (int m = 1; m < 64; m <<= 1) cum += __shfl_xor(cum, m, 64);
+        }
         float dqn = 0.f;
         float qv[kBC];
         auto loadq = [&](int c) {
@@ -553,41 +611,100 @@ __global__ __launch_bounds__(384) void kla_bwd_chunk_rev(BwdArgs p) {
             }
 #pragma unroll
             for (int u = 0; u < kBC; ++u) q2[u] = qv[u];
-            // with g = a / D and P = l_{t-1} / D: l_t = P + k w, a^2 / D^2 = g^2,
-            // qn / D = qn g / a, a l_{t-1} / D^2 = g P
-            float rl[kBC];
+            if constexpr (ISO) {
+                // the per-token sums over the key dims of Q and w U: a
+                // reduce-scatter leaves entry v (v < 16: Q of token v, else
+                // w U of token v - 16) in lane 32 b4 + 16 b3 + 8 b2 + 4 b1 + 2 b0
+                float sv[2 * kBC];
 #pragma unroll
-            for (int u = 0; u < kBC; ++u) rl[u] = fast_rcp(__builtin_fmaf(kv[u], wv[u], Pv[u]));  // 1 / l_t
-            // the recursion, last token first: dlog g_t (cum) and lbar
-            float lb[kBC], cm[kBC];
+                for (int u = 0; u < kBC; ++u) {
+                    sv[u] = q2[u];
+                    sv[kBC + u] = wv[u] * Uv[u];
+                }
+                int base = 0;
+                reduce_scatter<2 * kBC, 32>(sv, lane, base);
+                auto lane_of = [](int v) {
+                    return ((v >> 4) & 1) << 5 | ((v >> 3) & 1) << 4 | ((v >> 2) & 1) << 3 | ((v >> 1) & 1) << 2 |
+                           (v & 1) << 1;
+                };
+                float sQ[kBC], sR[kBC], ks[kBC], qt[kBC], rl[kBC];
 #pragma unroll
-            for (int u = kBC - 1; u >= 0; --u) {
-                cum = __builtin_fmaf(-wv[u], Uv[u], cum + q2[u]);
-                lbar = __builtin_fmaf(-q2[u], rl[u], lbar);
-                lb[u] = lbar;
-                cm[u] = cum;
-                const float lnext = __builtin_fmaf(lbar, gv[u] * gv[u], -cum * (qn * gv[u] * iav[u]));
-                lbar = u < nv ? lnext : lbar;
+                for (int u = 0; u < kBC; u += 4) {
+                    const f32x4 k4 = *(const f32x4*)&sm.lks[b3][u], q4 = *(const f32x4*)&sm.lqn[b3][u];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        ks[u + e] = k4[e];
+                        qt[u + e] = q4[e];
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < kBC; ++u) {
+                    sQ[u] = uni(sv[0], lane_of(u));
+                    sR[u] = uni(sv[0], lane_of(kBC + u));
+                    rl[u] = fast_rcp(__builtin_fmaf(ks[u], irv[u], Pv[u]));  // 1 / l_t
+                }
+                float lb[kBC], cm[kBC];
+#pragma unroll
+                for (int u = kBC - 1; u >= 0; --u) {
+                    cum += sQ[u] - sR[u];
+                    lbar = __builtin_fmaf(-sQ[u], rl[u], lbar);
+                    lb[u] = lbar;
+                    cm[u] = cum;
+                    const float lnext = __builtin_fmaf(lbar, gv[u] * gv[u], -cum * (qt[u] * gv[u] * iav[u]));
+                    lbar = u < nv ? lnext : lbar;
+                }
+                const auto rgk = rows_of((bf16*)p.gk, row0 + (size_t)c * kBC, nv, D);
+                // per-token outputs (a, qn and r of the head): every lane stores
+                // the same value
+                const auto rga = rows_of(p.ga, row0 + (size_t)c * kBC, nv, 1);
+                const auto rgq = rows_of(p.gqn, row0 + (size_t)c * kBC, nv, 1);
+                const auto rdr = rows_of(ws + L.drp, (size_t)c * kBC, nv, 1);
+#pragma unroll
+                for (int u = 0; u < kBC; ++u) {
+                    const float lbu = lb[u], cmu = cm[u], g = gv[u], P = Pv[u];
+                    buf_store_b16((bf16)(__builtin_fmaf(2.f * lbu * (1.f / (float)D), kv[u], Uv[u]) * irv[u]), rgk,
+                                  (u * D + i) * 2);
+                    buf_store(-irv[u] * __builtin_fmaf(lbu * ks[u], irv[u], sR[u]), rdr, u * 4);
+                    buf_store(__builtin_fmaf(-2.f * lbu, g * P, cmu * __builtin_fmaf(-2.f, g, iav[u])), rga, u * 4);
+                    buf_store(-__builtin_fmaf(lbu * P, P, cmu * P), rgq, u * 4);
+                }
+            } else {
+                // with g = a / D and P = l_{t-1} / D: l_t = P + k w, a^2 / D^2 = g^2,
+                // qn / D = qn g / a, a l_{t-1} / D^2 = g P
+                float rl[kBC];
+    #pragma unroll
+                for (int u = 0; u < kBC; ++u) rl[u] = fast_rcp(__builtin_fmaf(kv[u], wv[u], Pv[u]));  // 1 / l_t
+                // the recursion, last token first: dlog g_t (cum) and lbar
+                float lb[kBC], cm[kBC];
+    #pragma unroll
+                for (int u = kBC - 1; u >= 0; --u) {
+                    cum = __builtin_fmaf(-wv[u], Uv[u], cum + q2[u]);
+                    lbar = __builtin_fmaf(-q2[u], rl[u], lbar);
+                    lb[u] = lbar;
+                    cm[u] = cum;
+                    const float lnext = __builtin_fmaf(lbar, gv[u] * gv[u], -cum * (qn * gv[u] * iav[u]));
+                    lbar = u < nv ? lnext : lbar;
+                }
+                const auto rgk = rows_of((bf16*)p.gk, row0 + (size_t)c * kBC, nv, D);
+                const auto rga = rows_of(p.ga, row0 + (size_t)c * kBC, nv, D);
+                float dr[kBC];
+    #pragma unroll
+                for (int u = 0; u < kBC; ++u) {
+                    const float lbu = lb[u], cmu = cm[u], g = gv[u], P = Pv[u];
+                    buf_store_b16((bf16)(__builtin_fmaf(2.f * lbu, kv[u], Uv[u]) * irv[u]), rgk, (u * D + i) * 2);
+                    dr[u] = -wv[u] * __builtin_fmaf(lbu, kv[u], Uv[u]) * irv[u];
+                    // da = -2 lbar a l_{t-1} / D^2 + dlog g (qn l_{t-1} - a^2) / (a D)
+                    buf_store(__builtin_fmaf(-2.f * lbu, g * P, cmu * __builtin_fmaf(-2.f, g, iav[u])), rga, (u * D + i) * 4);
+                    const float dqt = __builtin_fmaf(lbu * P, P, cmu * P);
+                    dqn -= u < nv ? dqt : 0.f;
+                }
+                // dr of the tile's key dims: a reduce-scatter leaves token
+                // 8 b5 + 4 b4 + 2 b3 + b2 (lane bits) summed over the 64 lanes,
+                // the same in the four lanes of a quad
+                int base = 0;
+                reduce_scatter<kBC, 32>(dr, lane, base);
+                buf_store(dr[0], rows_of(ws + L.drp + (size_t)tile * L.t4, (size_t)c * kBC, nv, 1), base * 4);
             }
-            const auto rgk = rows_of((bf16*)p.gk, row0 + (size_t)c * kBC, nv, D);
-            const auto rga = rows_of(p.ga, row0 + (size_t)c * kBC, nv, D);
-            float dr[kBC];
-#pragma unroll
-            for (int u = 0; u < kBC; ++u) {
-                const float lbu = lb[u], cmu = cm[u], g = gv[u], P = Pv[u];
-                buf_store_b16((bf16)(__builtin_fmaf(2.f * lbu, kv[u], Uv[u]) * irv[u]), rgk, (u * D + i) * 2);
-                dr[u] = -wv[u] * __builtin_fmaf(lbu, kv[u], Uv[u]) * irv[u];
-                // da = -2 lbar a l_{t-1} / D^2 + dlog g (qn l_{t-1} - a^2) / (a D)
-                buf_store(__builtin_fmaf(-2.f * lbu, g * P, cmu * __builtin_fmaf(-2.f, g, iav[u])), rga, (u * D + i) * 4);
-                const float dqt = __builtin_fmaf(lbu * P, P, cmu * P);
-                dqn -= u < nv ? dqt : 0.f;
-            }
-            // dr of the tile's key dims: a reduce-scatter leaves token
-            // 8 b5 + 4 b4 + 2 b3 + b2 (lane bits) summed over the 64 lanes,
-            // the same in the four lanes of a quad
-            int base = 0;
-            reduce_scatter<kBC, 32>(dr, lane, base);
-            buf_store(dr[0], rows_of(ws + L.drp + (size_t)tile * L.t4, (size_t)c * kBC, nv, 1), base * 4);
             if (c >= 1) loadq(c - 1);  // lands during the next iteration
         };
         // The chunk's two upper-triangular operands (the same for every
@@ -624,8 +741,13 @@ __global__ __launch_bounds__(384) void kla_bwd_chunk_rev(BwdArgs p) {
             if (it >= 2) adj(nch + 1 - it);
             lds_barrier();
         }
-        if (p.gl0) p.gl0[(size_t)bh * D + i] = lbar;
-        ws[(size_t)4 * T * D + i] = dqn;  // this (b,h)'s qn partial
+        if constexpr (ISO) {
+            if (p.gl0 && lane == 0) p.gl0[bh] = lbar;
+        } else {
+            if (p.gl0) p.gl0[(size_t)bh * D + i] = lbar;
+            ws[(size_t)4 * T * D + i] = dqn;  // this (b,h)'s qn partial
+        }
+        (void)dqn;
         return;
     }
 
@@ -769,13 +891,13 @@ __global__ void kla_bwd_chunk_combine(BwdArgs p) {
     }
 }
 
-template <int D>
+template <int D, bool ISO>
 void launch(const BwdArgs& a, hipStream_t s) {
     constexpr int NT = D / 64;
     const int nbh = a.B * a.H;
     const dim3 grid((unsigned)(NT == 1 ? nbh : (nbh + 7) / 8 * 8 * NT));
-    hipLaunchKernelGGL((kla_bwd_chunk_fwd<D>), grid, dim3(320), 0, s, a);
-    hipLaunchKernelGGL((kla_bwd_chunk_rev<D>), grid, dim3(384), 0, s, a);
+    hipLaunchKernelGGL((kla_bwd_chunk_fwd<D, ISO>), grid, dim3(320), 0, s, a);
+    hipLaunchKernelGGL((kla_bwd_chunk_rev<D, ISO>), grid, dim3(384), 0, s, a);
     const size_t n = (size_t)nbh * a.T * (D / 4);
     hipLaunchKernelGGL((kla_bwd_chunk_combine<NT>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
 }
@@ -785,16 +907,19 @@ void launch(const BwdArgs& a, hipStream_t s) {
 bool bwd_chunk_supported(int dk, int dv, int cov, int dtype, int T) {
     const char* e = getenv("KLA_BWD_IMPL");
     if (e && (e[0] == 'r' || e[0] == 'p')) return false;  // KLA_BWD_IMPL=rows / plain
-    return cov == 0 && dtype == DT_BF16 && dk == dv && (dk == 64 || dk == 128) && T >= 1;
+    if (dtype != DT_BF16 || dk != dv || T < 1) return false;
+    // isotropic: the head's sums over key dims stay in one workgroup
+    return cov ? dk == 64 : (dk == 64 || dk == 128);
 }
 
-hipError_t launch_bwd_chunk(const BwdArgs& a, int dtype, hipStream_t s) {
-    if (!bwd_chunk_supported(a.dk, a.dv, 0, dtype, a.T) || a.B * a.H == 0) return hipErrorInvalidValue;
+hipError_t launch_bwd_chunk(const BwdArgs& a, int dtype, int cov, hipStream_t s) {
+    if (!bwd_chunk_supported(a.dk, a.dv, cov, dtype, a.T) || a.B * a.H == 0) return hipErrorInvalidValue;
     BwdArgs b = a;
     const char* e = getenv("KLA_BWD_SPIN");
     if (e && *e) b.spin = atoi(e) < 0 ? 0 : atoi(e);
-    if (a.dk == 64) launch<64>(b, s);
-    else launch<128>(b, s);
+    if (cov) launch<64, true>(b, s);
+    else if (a.dk == 64) launch<64, false>(b, s);
+    else launch<128, false>(b, s);
     return hipGetLastError();
 }
 

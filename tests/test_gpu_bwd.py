@@ -172,66 +172,67 @@ def test_bwd_full_lm_shape_every_sequence():
 
 # ------------------------------------------------ chunked kernels (bf16, diag, d 64 / 128)
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("cov,d", [("diag", 64), ("diag", 128), ("iso", 64)])
 @pytest.mark.parametrize("T", [1, 16, 45, 300])
-def test_bwd_chunk_with_state(d, T):
+def test_bwd_chunk_with_state(cov, d, T):
     """The chunked backward: ragged last chunks, a state, final-state
     gradients, B*H = 10 (a grid padded to the XCD pattern at d 128)."""
-    _print_case("bwd chunk", d, T)
-    inp = gen.make_inputs("lm_diag", seed=360 + T + d, B=2, H=5, T=T, dk=d, dv=d)
+    _print_case("bwd chunk", cov, d, T)
+    inp = gen.make_inputs("lm_diag" if cov == "diag" else "iso", seed=360 + T + d, B=2, H=5, T=T, dk=d, dv=d)
     w = inp["workload"]
     st = gen.make_state(w, seed=361)
     up = gen.make_upstream(w, seed=362)
-    check(run_bwd(inp, up, "diag", st), run_ref(inp, up, "diag", st), "diag", "bf16", f"bwd chunk d={d} T={T}")
+    check(run_bwd(inp, up, cov, st), run_ref(inp, up, cov, st), cov, "bf16", f"bwd chunk {cov} d={d} T={T}")
 
 
-@pytest.mark.parametrize("d", [64, 128])
-def test_bwd_chunk_hands_back_out_of_range(d):
+@pytest.mark.parametrize("cov,d", [("diag", 64), ("diag", 128), ("iso", 64)])
+def test_bwd_chunk_hands_back_out_of_range(cov, d):
     """a = 0.01 on one head: its decay products leave [2^-64, 2^64] within a
     chunk, so the token-serial kernel redoes that (b,h) (and, at d 64, the
     one sharing its workgroup); the rest stay on the chunked path."""
-    _print_case("bwd chunk hand-back", d)
-    inp = gen.make_inputs("lm_diag", seed=370, B=2, H=3, T=50, dk=d, dv=d)
+    _print_case("bwd chunk hand-back", cov, d)
+    inp = gen.make_inputs("lm_diag" if cov == "diag" else "iso", seed=370, B=2, H=3, T=50, dk=d, dv=d)
     a = inp["a"].clone()
     a[0, 1] = 0.01
     inp["a"] = a
     w = inp["workload"]
     st = gen.make_state(w, seed=371)
     up = gen.make_upstream(w, seed=372)
-    check(run_bwd(inp, up, "diag", st), run_ref(inp, up, "diag", st), "diag", "bf16", f"bwd hand-back d={d}")
+    check(run_bwd(inp, up, cov, st), run_ref(inp, up, cov, st), cov, "bf16", f"bwd hand-back {cov} d={d}")
 
 
-def test_bwd_chunk_matches_token_serial(monkeypatch):
-    """Chunked and token-serial kernels on the same inputs (long-context
-    laws): every gradient within the bf16 bar of each other."""
-    _print_case("bwd chunk vs token-serial")
-    inp = gen.make_inputs("long_diag", seed=380, B=1, H=4, T=400)
+@pytest.mark.parametrize("name", ["long_diag", "iso"])
+def test_bwd_chunk_matches_token_serial(monkeypatch, name):
+    """Chunked and token-serial kernels on the same inputs (long-context and
+    isotropic laws): every gradient within the bf16 bar of each other."""
+    _print_case("bwd chunk vs token-serial", name)
+    inp = gen.make_inputs(name, seed=380, B=1, H=4, T=400)
     w = inp["workload"]
     up = gen.make_upstream(w, seed=381)
-    chunk = run_bwd(inp, up, "diag")
+    chunk = run_bwd(inp, up, w.cov)
     monkeypatch.setenv("KLA_BWD_IMPL", "rows")
-    serial = run_bwd(inp, up, "diag")
-    errs = bwd_errors(chunk, serial, "diag")
+    serial = run_bwd(inp, up, w.cov)
+    errs = bwd_errors(chunk, serial, w.cov)
     print("chunk vs serial", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
     assert all(v <= TOL["bf16"] for v in errs.values()), errs
 
 
-@pytest.mark.parametrize("d", [64, 128])
-def test_bwd_chunk_wait_timeout_hands_back(monkeypatch, d):
+@pytest.mark.parametrize("cov,d", [("diag", 64), ("diag", 128), ("iso", 64)])
+def test_bwd_chunk_wait_timeout_hands_back(monkeypatch, cov, d):
     """The reverse sweep's in-workgroup wait, forced to give up at once from
     the host (KLA_BWD_SPIN=0): every (b,h) is flagged and redone by the
     token-serial kernel, and the gradients still match the oracle."""
-    _print_case("bwd chunk forced hand-back", d)
+    _print_case("bwd chunk forced hand-back", cov, d)
     monkeypatch.setenv("KLA_BWD_SPIN", "0")
-    inp = gen.make_inputs("lm_diag", seed=390, B=2, H=3, T=70, dk=d, dv=d)
+    inp = gen.make_inputs("lm_diag" if cov == "diag" else "iso", seed=390, B=2, H=3, T=70, dk=d, dv=d)
     w = inp["workload"]
     st = gen.make_state(w, seed=391)
     up = gen.make_upstream(w, seed=392)
-    got = run_bwd(inp, up, "diag", st)
-    check(got, run_ref(inp, up, "diag", st), "diag", "bf16", f"bwd forced hand-back d={d}")
+    got = run_bwd(inp, up, cov, st)
+    check(got, run_ref(inp, up, cov, st), cov, "bf16", f"bwd forced hand-back {cov} d={d}")
     # the same kernel run directly (one row group) gives the same bits
     monkeypatch.setenv("KLA_BWD_IMPL", "rows")
     monkeypatch.setenv("KLA_BWD_NRG", "1")
-    serial = run_bwd(inp, up, "diag", st)
+    serial = run_bwd(inp, up, cov, st)
     for n in GRADS:
         assert np.array_equal(got[n], serial[n]), n
