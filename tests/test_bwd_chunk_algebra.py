@@ -91,6 +91,63 @@ def _chunked_bwd(q, k, v, a, qn, r, l0, eta0, dO, dlT, detaT, mutant=None):
     return dict(dq=dq, dk=dk, dv=dv, da=da, dr=dr, dqn=dqn, dl0=lbar, deta0=eps)
 
 
+def _chunked_bwd_iso(q, k, v, a, qn, r, l0, eta0, dO, dlT, detaT):
+    """Isotropic: the precision, decay and process noise are scalars per
+    token (l_t = l_{t-1} / D_t + |k_t|^2 / (dk r_t)), so G is one scalar per
+    token and key dim alike; dlog g and lbar are the head's scalars, the
+    per-token terms summed over the key dims."""
+    T, D = q.shape
+    nch = (T + C - 1) // C
+
+    def chain(c, l):
+        c0, n = c * C, min(C, T - c * C)
+        lprev, lt, g, Dn = (np.zeros(n) for _ in range(4))
+        for u in range(n):
+            lprev[u] = l
+            Dn[u] = a[c0 + u] ** 2 + qn[c0 + u] * l
+            g[u] = a[c0 + u] / Dn[u]
+            l = l / Dn[u] + np.sum(k[c0 + u] ** 2) / (D * r[c0 + u])
+            lt[u] = l
+        return c0, n, lprev, lt, g, Dn, np.cumprod(g)[:, None] * np.ones((1, D))
+
+    l, eta = float(l0), eta0.copy()
+    lstart, Qs, dq = np.zeros(nch), np.zeros((T, D)), np.zeros((T, D))
+    for c in range(nch):
+        lstart[c] = l
+        c0, n, _, lt, g, _, G = chain(c, l)
+        l = lt[-1]
+        qh, W = q[c0:c0 + n] / lt[:, None], k[c0:c0 + n] / r[c0:c0 + n, None]
+        V, dOc = v[c0:c0 + n], dO[c0:c0 + n]
+        S = G * (dOc @ eta.T) + G * (np.tril(dOc @ V.T) @ (W / G))
+        dq[c0:c0 + n] = S / lt[:, None]
+        Qs[c0:c0 + n] = qh * S
+        eta = G[-1][:, None] * (eta + (W / G).T @ V)
+    cum = float((detaT * eta).sum())
+    eps, lbar = detaT.copy(), float(dlT)
+    dk, dv = np.zeros((T, D)), np.zeros((T, D))
+    da, dr, dqn = np.zeros(T), np.zeros(T), np.zeros(T)
+    for c in range(nch - 1, -1, -1):
+        c0, n, lprev, lt, g, Dn, G = chain(c, lstart[c])
+        gC = G[-1]
+        qh, W = q[c0:c0 + n] / lt[:, None], k[c0:c0 + n] / r[c0:c0 + n, None]
+        V, dOc = v[c0:c0 + n], dO[c0:c0 + n]
+        A = G * qh
+        U = (gC * (V @ eps.T) + np.triu(V @ dOc.T) @ A) / G
+        dv[c0:c0 + n] = (W / G) @ (gC[:, None] * eps) + np.triu((W / G) @ A.T) @ dOc
+        eps = gC[:, None] * eps + A.T @ dOc
+        for u in range(n - 1, -1, -1):
+            t = c0 + u
+            cum = cum + np.sum(Qs[t] - W[u] * U[u])
+            lbar = lbar - np.sum(Qs[t]) / lt[u]
+            rd = 1.0 / Dn[u]
+            dk[t] = U[u] / r[t] + 2 * lbar * k[t] / (D * r[t])
+            dr[t] = -(np.sum(k[t] * U[u]) + lbar * np.sum(k[t] ** 2) / D) / r[t] ** 2
+            da[t] = -2 * lbar * a[t] * lprev[u] * rd ** 2 + cum * (qn[t] * lprev[u] - a[t] ** 2) * rd / a[t]
+            dqn[t] = -lbar * lprev[u] ** 2 * rd ** 2 - cum * lprev[u] * rd
+            lbar = lbar * a[t] ** 2 * rd ** 2 - cum * qn[t] * rd
+    return dict(dq=dq, dk=dk, dv=dv, da=da, dr=dr, dqn=dqn, dl0=lbar, deta0=eps)
+
+
 def _check(inp, up, st=None, tol=1e-11, mutant=None):
     f = lambda x: x.double().numpy()  # noqa: E731
     q, k, v, a, qn, r = (f(inp[n]) for n in ("q", "k", "v", "a", "qn", "r"))
@@ -133,3 +190,25 @@ def test_bwd_chunk_algebra_catches_planted_mistakes(mutant):
     w = inp["workload"]
     with pytest.raises(AssertionError):
         _check(inp, gen.make_upstream(w, seed=66), gen.make_state(w, seed=67), mutant=mutant)
+
+
+@pytest.mark.parametrize("T", [1, 17, 45])
+def test_bwd_chunk_algebra_isotropic(T):
+    """The isotropic chunk algebra (scalar precision and decay per token, the
+    gate adjoint and lbar summed over the key dims) against the oracle."""
+    inp = gen.make_inputs("iso", seed=70 + T, B=1, H=2, T=T, dk=16, dv=16, dtype="f32")
+    w = inp["workload"]
+    up = gen.make_upstream(w, seed=71)
+    st = gen.make_state(w, seed=72)
+    f = lambda x: x.double().numpy()  # noqa: E731
+    q, k, v, a, qn, r = (f(inp[n]) for n in ("q", "k", "v", "a", "qn", "r"))
+    dO, dlT, detaT = f(up["do"]), f(up["dlT"]), f(up["detaT"])
+    l0, e0 = f(st["l0"]), f(st["eta0"])
+    ref = oracle.bwd(inp["q"], inp["k"], inp["v"], inp["a"], inp["qn"], inp["r"], st["l0"], st["eta0"],
+                     do=up["do"], dlT=up["dlT"], detaT=up["detaT"], cov=oracle.ISO)
+    for h in range(2):
+        got = _chunked_bwd_iso(q[0, h], k[0, h], v[0, h], a[0, h], qn[0, h], r[0, h], l0[0, h], e0[0, h],
+                               dO[0, h], dlT[0, h], detaT[0, h])
+        for n in ("dq", "dk", "dv", "da", "dr", "dqn", "dl0", "deta0"):
+            x, y = np.asarray(got[n]), np.asarray(ref[n][0, h])
+            assert np.abs(x - y).max() <= 1e-11 * np.abs(y).max(), (n, h)
