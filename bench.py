@@ -14,7 +14,7 @@ the host cores over a bounded sample of the same workload.
 
   python bench.py [--steps K] [--warmup W] [--workload long_diag] [--no-cpu]
   (workloads: the names in scan_amd.inputs, iso_decode, iso_prefill16,
-   residual_lm_diag, block_lm_diag, block_long_diag, bwd_lm_diag)
+   residual_lm_diag, block_lm_diag, block_long_diag, bwd_lm_diag, bwd_iso)
 """
 from __future__ import annotations
 
@@ -228,23 +228,34 @@ def run_decode(args, torch, np, scan_amd, gen) -> dict:
     }
 
 
+# backward workloads: the forward workload whose shape and value laws they use
+BWD_WORKLOADS = {"bwd_lm_diag": "lm_diag", "bwd_iso": "iso"}
+
+
 def bwd_alg_bytes(w) -> float:
     """Algorithmic HBM bytes of one backward pass (klaBwd) with upstream
     gradients for o, lT and etaT: the forward's inputs and do read once, the
-    input gradients written once (per head qn read, dqn written; per (b,h) dlT,
-    detaT read and dl0, deta0 written).  The fp64 trajectory the kernel keeps
-    in its workspace between its two sweeps is not counted."""
+    input gradients written once (per (b,h) dlT, detaT read and dl0, deta0
+    written; the diagonal qn per head read and dqn written, the isotropic
+    a, qn per token).  Workspace traffic is not counted."""
     es = 2 if w.dtype == "bf16" else 4
+    if w.cov == "iso":
+        per_tok = 2 * ((2 * w.dk + w.dv) * es + 12) + w.dv * es
+        per_seq = 2 * (4 + 4 * w.dk * w.dv)
+        return float(w.B * w.H * w.T * per_tok + w.B * w.H * per_seq)
     per_tok = 2 * ((2 * w.dk + w.dv) * es + 4 * w.dk + 4) + w.dv * es
     per_seq = 2 * (4 * w.dk + 4 * w.dk * w.dv)
     return float(w.B * w.H * w.T * per_tok + w.B * w.H * per_seq + w.H * 8 * w.dk)
 
 
 def run_bwd(args, torch, np, scan_amd, gen) -> dict:
-    """One step = one klaBwd over the whole LM-layer batch (gradients of
-    <do, o> + <dlT, lT> + <detaT, etaT> for every input), inputs and upstream
-    gradients resident in HBM, rotated like the forward's."""
-    w = gen.WORKLOADS["lm_diag"]
+    """One step = one klaBwd over the whole batch of the LM layer (bwd_lm_diag)
+    or of the isotropic workload (bwd_iso): gradients of <do, o> + <dlT, lT> +
+    <detaT, etaT> for every input, inputs and upstream gradients resident in
+    HBM, rotated like the forward's."""
+    name = args.workload
+    w = gen.WORKLOADS[BWD_WORKLOADS[name]]
+    iso = w.cov == "iso"
     print(f"bench: backward of {w}", file=sys.stderr, flush=True)
     host = gen.make_inputs(w, seed=0)
     up = gen.make_upstream(w, seed=1)
@@ -253,7 +264,7 @@ def run_bwd(args, torch, np, scan_amd, gen) -> dict:
     ncopies = max(2, -(-3 * MALL_BYTES // int(nbytes)))
     B, H, T, dk, dv = w.B, w.H, w.T, w.dk, w.dv
     dims = scan_amd.KlaDims(B, H, T, dk, dv, scan_amd.KLA_BF16 if w.dtype == "bf16" else scan_amd.KLA_F32,
-                            scan_amd.KLA_DIAG)
+                            scan_amd.KLA_ISO if iso else scan_amd.KLA_DIAG)
     ws_bytes = scan_amd.klaBwdWorkspaceBytes(dims)
     sets = []
     for _ in range(ncopies):
@@ -262,7 +273,8 @@ def run_bwd(args, torch, np, scan_amd, gen) -> dict:
         outs = {"dq": torch.empty_like(ins["q"]), "dk": torch.empty_like(ins["k"]),
                 "dv": torch.empty_like(ins["v"]), "da": torch.empty_like(ins["a"]),
                 "dqn": torch.empty_like(ins["qn"]), "dr": torch.empty_like(ins["r"]),
-                "dl0": torch.empty(B, H, dk, device="cuda"), "deta0": torch.empty(B, H, dk, dv, device="cuda")}
+                "dl0": torch.empty((B, H) if iso else (B, H, dk), device="cuda"),
+                "deta0": torch.empty(B, H, dk, dv, device="cuda")}
         ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
         sets.append((ins, outs, ws))
     stream = torch.cuda.current_stream()
@@ -296,22 +308,25 @@ def run_bwd(args, torch, np, scan_amd, gen) -> dict:
     if not args.no_cpu:
         import oracle
         threads = oracle.default_threads()
+        cov = oracle.ISO if iso else oracle.DIAG
         one = {n: host[n][:1, :1] for n in names}
-        one["qn"] = host["qn"][:1]
+        if not iso:
+            one["qn"] = host["qn"][:1]
         uo = {n: up[n][:1, :1] for n in ("do", "dlT", "detaT")}
         t0 = time.perf_counter()
-        oracle.bwd(*(one[n] for n in names), do=uo["do"], dlT=uo["dlT"], detaT=uo["detaT"], nthreads=1)
+        oracle.bwd(*(one[n] for n in names), do=uo["do"], dlT=uo["dlT"], detaT=uo["detaT"], cov=cov, nthreads=1)
         t_one = time.perf_counter() - t0
         nseq = int(max(threads, min(B * H, args.cpu_seconds * threads / max(t_one, 1e-6))))
         nh = H if nseq >= H else max(1, nseq)
         nb = max(1, min(B, nseq // H)) if nseq >= H else 1
         sub = {n: host[n][:nb, :nh] for n in names}
-        sub["qn"] = host["qn"][:nh]
+        if not iso:
+            sub["qn"] = host["qn"][:nh]
         us = {n: up[n][:nb, :nh] for n in ("do", "dlT", "detaT")}
         reps, t_cpu = 0, 0.0
         while reps == 0 or (t_cpu < 0.5 * args.cpu_seconds and reps < 100):
             t0 = time.perf_counter()
-            oracle.bwd(*(sub[n] for n in names), do=us["do"], dlT=us["dlT"], detaT=us["detaT"],
+            oracle.bwd(*(sub[n] for n in names), do=us["do"], dlT=us["dlT"], detaT=us["detaT"], cov=cov,
                        nthreads=threads)
             t_cpu += time.perf_counter() - t0
             reps += 1
@@ -319,7 +334,7 @@ def run_bwd(args, torch, np, scan_amd, gen) -> dict:
         cpu = {"value": seqs * T * reps / H / t_cpu, "unit": "tokens/s", "cores": threads, "kind": "oracle",
                "sample": f"{seqs} of {B * H} (b,h) sequences at full T={T} ({nb}x{nh}), fp64 reverse-mode "
                          f"adjoint, {reps} pass(es) in {t_cpu:.1f}s"}
-    traffic = stored_traffic("bwd_lm_diag", "bwd")
+    traffic = stored_traffic(name, "bwd")
     return {
         "metric": "KLA layer bwd tokens/s at B·T, H×d; % of HBM roofline",
         "value": B * T / (ms_per_step / 1e3),
@@ -333,12 +348,13 @@ def run_bwd(args, torch, np, scan_amd, gen) -> dict:
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": "bwd_lm_diag", "B": B, "H": H, "T": T, "dk": dk, "dv": dv, "cov": w.cov,
+        "config": {"workload": name, "B": B, "H": H, "T": T, "dk": dk, "dv": dv, "cov": w.cov,
                    "global_batch": B, "seq_len": T, "parallelism": "none"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic["bytes_per_launch"] if traffic else None,
-                     "kernel": "kla_bwd_kernel", "alg_bytes": nbytes, "kernel_ms": ms_per_step,
+                     "kernel": "kla_bwd_chunk_fwd + kla_bwd_chunk_rev (chunked sweeps)", "alg_bytes": nbytes,
+                     "kernel_ms": ms_per_step,
                      "copy_gbs": copy_gbs, "frac_of_copy": achieved / copy_gbs},
         "cpu_baseline": cpu,
     }
@@ -513,7 +529,7 @@ def main() -> int:
     if args.workload == gen.DECODE.name:
         print(json.dumps(run_decode(args, torch, np, scan_amd, gen)), flush=True)
         return 0
-    if args.workload == "bwd_lm_diag":
+    if args.workload in BWD_WORKLOADS:
         print(json.dumps(run_bwd(args, torch, np, scan_amd, gen)), flush=True)
         return 0
     if args.workload == gen.PREFILL.name:
