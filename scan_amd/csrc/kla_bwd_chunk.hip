@@ -59,6 +59,8 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "kla_bwd.h"
 #include "kla_common.h"
 
@@ -285,16 +287,22 @@ __global__ __launch_bounds__(320) void kla_bwd_chunk_fwd(BwdArgs p) {
             if (lane < kBC) sm.ir[b][lane] = irl;
             float gam = 1.f;
             float vg[kBC], vl[kBC];
+            // full chunks (all but perhaps the last) without the selects
+            // for tokens past the end
+            auto run = [&](auto full) {
 #pragma unroll
-            for (int u = 0; u < kBC; ++u) {
-                const bool in = u < nv;
-                const float rd = fast_rcp(__builtin_fmaf(qv[u], l, af[u] * af[u]));
-                const float g = in ? af[u] * rd : 1.f;
-                l = in ? __builtin_fmaf(kk[u], uni(irl, u), l * rd) : l;
-                gam *= g;
-                vg[u] = gam;
-                vl[u] = l;
-            }
+                for (int u = 0; u < kBC; ++u) {
+                    const bool in = decltype(full)::value || u < nv;
+                    const float rd = fast_rcp(__builtin_fmaf(qv[u], l, af[u] * af[u]));
+                    const float g = in ? af[u] * rd : 1.f;
+                    l = in ? __builtin_fmaf(kk[u], uni(irl, u), l * rd) : l;
+                    gam *= g;
+                    vg[u] = gam;
+                    vl[u] = l;
+                }
+            };
+            if (nv == kBC) run(std::true_type{});
+            else run(std::false_type{});
 #pragma unroll
             for (int u = 0; u < kBC; u += 4) {
                 *(f32x4*)&sm.gam[b][il][u] = f32x4{vg[u], vg[u + 1], vg[u + 2], vg[u + 3]};
@@ -502,35 +510,39 @@ __global__ __launch_bounds__(384) void kla_bwd_chunk_rev(BwdArgs p) {
             float gam = 1.f, rg = 1.f;
             float vr[kBC], vg[kBC], vP[kBC], vi[kBC], vw[kBC];
             bf16 vah[kBC], val[kBC];
+            auto run = [&](auto full) {
 #pragma unroll
-            for (int u = 0; u < kBC; ++u) {
-                const bool in = u < nv;
-                const float ir = uni(irl, u);
-                const float Dn = __builtin_fmaf(qv[u], l, af[u] * af[u]);
-                const float rd = fast_rcp(Dn);
-                const float ia = fast_rcp(in ? af[u] : 1.f);
-                const float g = in ? af[u] * rd : 1.f;
-                const float P = l * rd;
-                vg[u] = g;
-                vP[u] = P;
-                vi[u] = ia;
-                l = in ? __builtin_fmaf(kk[u], ir, P) : l;
-                gam *= g;
-                rg *= in ? Dn * ia : 1.f;
-                const float wv = kf[u] * ir;
-                vw[u] = wv;
-                const float A = gam * (qf[u] * fast_rcp(l));
-                const float W = wv * rg;
-                const bf16 ah = (bf16)A, wh = (bf16)W;
-                const bf16 al = (bf16)(A - (float)ah), wl = (bf16)(W - (float)wh);
-                vr[u] = rg;
-                vah[u] = ah;
-                val[u] = al;
-                sm.ath[b2][u][il] = ah;
-                sm.atl[b2][u][il] = al;
-                sm.wth[b2][u][il] = wh;
-                sm.wtl[b2][u][il] = wl;
-            }
+                for (int u = 0; u < kBC; ++u) {
+                    const bool in = decltype(full)::value || u < nv;
+                    const float ir = uni(irl, u);
+                    const float Dn = __builtin_fmaf(qv[u], l, af[u] * af[u]);
+                    const float rd = fast_rcp(Dn);
+                    const float ia = fast_rcp(in ? af[u] : 1.f);
+                    const float g = in ? af[u] * rd : 1.f;
+                    const float P = l * rd;
+                    vg[u] = g;
+                    vP[u] = P;
+                    vi[u] = ia;
+                    l = in ? __builtin_fmaf(kk[u], ir, P) : l;
+                    gam *= g;
+                    rg *= in ? Dn * ia : 1.f;
+                    const float wv = kf[u] * ir;
+                    vw[u] = wv;
+                    const float A = gam * (qf[u] * fast_rcp(l));
+                    const float W = wv * rg;
+                    const bf16 ah = (bf16)A, wh = (bf16)W;
+                    const bf16 al = (bf16)(A - (float)ah), wl = (bf16)(W - (float)wh);
+                    vr[u] = rg;
+                    vah[u] = ah;
+                    val[u] = al;
+                    sm.ath[b2][u][il] = ah;
+                    sm.atl[b2][u][il] = al;
+                    sm.wth[b2][u][il] = wh;
+                    sm.wtl[b2][u][il] = wl;
+                }
+            };
+            if (nv == kBC) run(std::true_type{});
+            else run(std::false_type{});
 #pragma unroll
             for (int u = 0; u < kBC; u += 4) {
                 *(f32x4*)&sm.lg[b3][il][u] = f32x4{vg[u], vg[u + 1], vg[u + 2], vg[u + 3]};
@@ -672,11 +684,11 @@ __global__ __launch_bounds__(384) void kla_bwd_chunk_rev(BwdArgs p) {
                 // with g = a / D and P = l_{t-1} / D: l_t = P + k w, a^2 / D^2 = g^2,
                 // qn / D = qn g / a, a l_{t-1} / D^2 = g P
                 float rl[kBC];
-    #pragma unroll
+#pragma unroll
                 for (int u = 0; u < kBC; ++u) rl[u] = fast_rcp(__builtin_fmaf(kv[u], wv[u], Pv[u]));  // 1 / l_t
                 // the recursion, last token first: dlog g_t (cum) and lbar
                 float lb[kBC], cm[kBC];
-    #pragma unroll
+#pragma unroll
                 for (int u = kBC - 1; u >= 0; --u) {
                     cum = __builtin_fmaf(-wv[u], Uv[u], cum + q2[u]);
                     lbar = __builtin_fmaf(-q2[u], rl[u], lbar);
@@ -688,7 +700,7 @@ __global__ __launch_bounds__(384) void kla_bwd_chunk_rev(BwdArgs p) {
                 const auto rgk = rows_of((bf16*)p.gk, row0 + (size_t)c * kBC, nv, D);
                 const auto rga = rows_of(p.ga, row0 + (size_t)c * kBC, nv, D);
                 float dr[kBC];
-    #pragma unroll
+#pragma unroll
                 for (int u = 0; u < kBC; ++u) {
                     const float lbu = lb[u], cmu = cm[u], g = gv[u], P = Pv[u];
                     buf_store_b16((bf16)(__builtin_fmaf(2.f * lbu, kv[u], Uv[u]) * irv[u]), rgk, (u * D + i) * 2);
