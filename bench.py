@@ -97,9 +97,16 @@ def alg_flops(w) -> float:
     return float(w.B * w.H * w.T * 5 * w.dk * w.dv)
 
 
-def measure_copy(torch, nbytes: float, reps: int = 10) -> float:
+def measure_copy(torch, nbytes: float, reps: int = 10, settle_s: float = 0.0) -> float:
     """GB/s of a plain device-to-device copy that moves nbytes in total (half
-    read, half written), timed with HIP events on the current stream."""
+    read, half written), timed with HIP events on the current stream.
+
+    With settle_s > 0 the copy first runs for about that many seconds of GPU
+    time, untimed: an idle GPU starts below its sustained clock and takes a
+    few tens of milliseconds of load to reach it (measured: the long-context
+    forward ran 0.45 ms per step after 5 warm-up steps, 0.37 ms after 100).
+    Called before a workload's warm-up, this brings the GPU to the clock the
+    timed steps then run at, and the copy rate is taken at that same clock."""
     half = int(nbytes // 2) // 16 * 16
     src = torch.empty(half, dtype=torch.uint8, device="cuda").fill_(1)
     dst = torch.empty_like(src)
@@ -108,6 +115,12 @@ def measure_copy(torch, nbytes: float, reps: int = 10) -> float:
     stream = torch.cuda.current_stream()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
+    if settle_s > 0:
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < settle_s:
+            for _ in range(8):
+                dst.copy_(src)
+            torch.cuda.synchronize()
     e0.record(stream)
     for _ in range(reps):
         dst.copy_(src)
@@ -170,6 +183,7 @@ def run_decode(args, torch, np, scan_amd, gen) -> dict:
     for t in range(n):
         toks.append([host[x][:, :, t].contiguous().to("cuda") for x in names])
     o = torch.empty(w.B, w.H, w.dv, dtype=toks[0][2].dtype, device="cuda")
+    measure_copy(torch, decode_alg_bytes(w), settle_s=args.settle_s)  # sustained clock
     for i in range(args.warmup):
         scan_amd.step(*toks[i % n], l, eta, cov=w.cov, o=o)
     torch.cuda.synchronize()
@@ -288,6 +302,8 @@ def run_bwd(args, torch, np, scan_amd, gen) -> dict:
         if rc != 0:
             raise scan_amd.KlaError(rc, "klaBwd")
 
+    # the copy reference, taken after it has brought the GPU to its sustained clock
+    copy_gbs = measure_copy(torch, nbytes, settle_s=args.settle_s)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -300,7 +316,6 @@ def run_bwd(args, torch, np, scan_amd, gen) -> dict:
     torch.cuda.synchronize()
     ms_per_step = ev0.elapsed_time(ev1) / args.steps
     achieved = nbytes / (ms_per_step / 1e3) / 1e9
-    copy_gbs = measure_copy(torch, nbytes)
     print(f"bench: backward {ms_per_step:.4f} ms/step, {achieved:.1f} GB/s algorithmic, "
           f"copy {copy_gbs:.1f} GB/s", file=sys.stderr, flush=True)
     calibration_copy(args, torch)
@@ -403,6 +418,7 @@ def run_prefill(args, torch, np, scan_amd, gen) -> dict:
 
     def step(i):
         scan_amd.fwd(*sets[i % 2], l0, eta0, cov=w.cov, o=o, lT=lT, etaT=etaT)
+    measure_copy(torch, prefill_alg_bytes(w), settle_s=args.settle_s)  # sustained clock
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -506,6 +522,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long_diag")
+    ap.add_argument("--settle-s", type=float, default=0.5,
+                    help="seconds of untimed device copies before the warm-up, so that the "
+                         "timed steps run at the sustained clock (0: none)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="target wall time of the oracle sample")
@@ -577,6 +596,9 @@ def main() -> int:
         else:
             scan_amd.fwd(*s, cov=w.cov, o=o, lT=lT, etaT=etaT)
 
+    # a plain device copy of the same byte count, measured now on this machine,
+    # after it has brought the GPU to its sustained clock
+    copy_gbs = measure_copy(torch, nbytes, settle_s=args.settle_s)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -606,8 +628,6 @@ def main() -> int:
     print(f"bench: {ms_per_step:.4f} ms/step (kernel {kern_ms:.4f} ms), {achieved:.1f} GB/s "
           f"algorithmic, {ncopies} rotating input copies, wall {wall:.3f}s",
           file=sys.stderr, flush=True)
-    # a plain device copy of the same byte count, measured now on this machine
-    copy_gbs = measure_copy(torch, nbytes)
     print(f"bench: device copy of {nbytes / 1e6:.1f} MB: {copy_gbs:.1f} GB/s",
           file=sys.stderr, flush=True)
 
