@@ -84,6 +84,20 @@ int env_nseg() {
     return atoi(s);
 }
 
+// Value tiles of the wave-specialised diagonal kernel: 64-column tiles, or,
+// for few long sequences that take the sequence split either way, whole
+// 128-column rows, so that the chain and gate work is done once per (b,h)
+// and segment instead of once per tile (measured 11% faster on the
+// B1 H16 T32768 d128 forward).
+int diag_pipe_vtiles(const klaDims* d) {
+    const int nvt = kla::fwd_diag_pipe_vtiles(d->dk, d->dv, d->dtype);
+    if (nvt == 2 && kla::fwd_diag_pipe_supported(d->dk, d->dv, 1, d->dtype) &&
+        kla::fwd_diag_nseg(d->B, d->H, d->T, d->dk, d->dv, 2) > 1 &&
+        kla::fwd_diag_nseg(d->B, d->H, d->T, d->dk, d->dv, 1) > 1)
+        return 1;
+    return nvt;
+}
+
 // Kernel that klaFwd launches for these (supported) dims; n_vtiles receives
 // the number of value-column tiles each (b,h) is split into.
 enum FwdKernel { FK_EMPTY, FK_SHORT, FK_ISO, FK_ISO_PIPE, FK_DIAG_PIPE, FK_DIAG_CHUNK };
@@ -109,7 +123,7 @@ FwdKernel pick_kernel(const klaDims* d, int* n_vtiles) {
         return FK_ISO;
     }
     if (use_pipe()) {
-        const int nvt_pipe = nvt_env > 0 ? nvt_env : kla::fwd_diag_pipe_vtiles(d->dk, d->dv, d->dtype);
+        const int nvt_pipe = nvt_env > 0 ? nvt_env : diag_pipe_vtiles(d);
         if (nvt_pipe > 0 && kla::fwd_diag_pipe_supported(d->dk, d->dv, nvt_pipe, d->dtype)) {
             *n_vtiles = nvt_pipe;
             return FK_DIAG_PIPE;

@@ -54,7 +54,12 @@ struct P3 {
     static constexpr int NCW = DK / 64;          // chain waves
     static constexpr int NMW = DV / 32;          // MMA waves
     static constexpr int JT = 2;                 // 16-column value tiles per MMA wave
-    static constexpr int NGW = 4;                // gate waves
+    // The gates of a chunk are cut into four groups of key-dim pairs (virtual
+    // gate waves).  With 64 value columns four gate waves take one group
+    // each; with 128 the four MMA waves leave room for two, which take two
+    // groups each, one after the other.
+    static constexpr int NGW = DV == 128 ? 2 : 4;  // gate waves
+    static constexpr int NVG = 4 / NGW;            // groups per gate wave
     static constexpr int NW = NCW + NMW + NGW;
     static constexpr int NT = 64 * NW;
     static constexpr int IT = DK / 16;           // 16-row tiles of the state
@@ -62,7 +67,7 @@ struct P3 {
     static constexpr int NIP = DK / 2;           // key-dim pairs
     static constexpr int NGRP = 256 / NIP;       // token groups
     static constexpr int TPG = C / NGRP;         // tokens per group
-    static constexpr int IPW = 64 / NGRP;        // key-dim pairs per gate wave
+    static constexpr int IPW = 64 / NGRP;        // key-dim pairs per group
     static constexpr int PE = 16 / (int)sizeof(TIn);
     static constexpr int QS = DK + PE;           // row stride of Q^, W^
     static constexpr int CS = C + PE;            // row stride of W^T, V^T
@@ -217,6 +222,10 @@ __device__ void chain_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int
     const int nchunks = (sp.TL + C - 1) / C;
     const int nsteps = pipe_steps<K>(nchunks);
     const TIn* kp = (const TIn*)p.k;
+    // The chain waves form the gates f, w themselves (instead of the gate
+    // waves) with the block prologue, whose gate waves have no k, and with
+    // 128-column tiles, whose two gate waves would otherwise bound the step.
+    constexpr bool CG = PRO || K::DV == 128;
 
     float l = SEG ? p.seg_l0[((size_t)bh * p.nseg + sp.seg) * DK + i]
                   : (p.l0 ? p.l0[(size_t)bh * DK + i] : 1.f);
@@ -329,7 +338,7 @@ __device__ void chain_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int
                         const float lp = l * fast_rcp(__builtin_fmaf(qn, l, a * a));
                         l = __builtin_fmaf(kv * kv, rt, lp);
                         const float alp = a * lp;
-                        if constexpr (PRO) {
+                        if constexpr (CG) {
                             // the gates themselves: the gate waves have no k
                             const float rl = fast_rcp(l);
                             sm.LP[par][t][i ^ lp_swz(t)] = f32x2{alp * rl, kv * rt * rl};
@@ -649,8 +658,17 @@ __device__ void gate_role(S3<TIn, K>& sm, TAPS& taps, const FwdArgs& p, const Sp
     const bool wq = SEG && sp.seg > 0 && vt == 0;
     const int nsteps = pipe_steps<K>(nchunks);
     const int grp = lane % K::NGRP, ipl = lane / K::NGRP;
-    const int ip = gw * K::IPW + ipl;
-    const int gtid = gw * 64 + lane;
+    // group h of this wave is virtual gate wave gw + h * NGW
+    constexpr int NV = K::NVG;
+    static_assert(NV == 1 || !PRO, "the block prologue runs with four gate waves");
+    int ipv[NV], gtv[NV];
+#pragma unroll
+    for (int h = 0; h < NV; ++h) {
+        ipv[h] = (gw + h * K::NGW) * K::IPW + ipl;
+        gtv[h] = (gw + h * K::NGW) * 64 + lane;
+    }
+    const int ip = ipv[0];
+    const int gtid = gtv[0];
     const TIn* qp = (const TIn*)p.q;
     const TIn* kp = (const TIn*)p.k;
     const TIn* vp = (const TIn*)p.v;
@@ -661,8 +679,15 @@ __device__ void gate_role(S3<TIn, K>& sm, TAPS& taps, const FwdArgs& p, const Sp
         QV vh[K::VPT][3];  // block prologue: the three v rows before the unit's tokens
     };
     constexpr int NB = K::NBG, D = NB - 1;
-    Buf b[NB];
-    constexpr int NLD = (PRO ? TPG + 5 * K::VPT : 2 * TPG + 2 * K::VPT);  // loads per chunk
+    // With two groups per wave each group keeps one buffer, refilled with
+    // the next chunk's rows once the step has used it (two in-flight chunks
+    // for both groups would not fit in the registers).
+    constexpr int NBUF = NV == 1 ? NB : 1;
+    Buf b[NBUF][NV];
+    // with the block prologue or 128-column tiles the chain waves form f
+    // and w, and the gate waves read no k
+    constexpr bool CG = PRO || K::DV == 128;
+    constexpr int NLD = (PRO ? TPG + 5 * K::VPT : CG ? TPG + 2 * K::VPT : 2 * TPG + 2 * K::VPT);  // loads per chunk
     // The next chunk's rows are requested after the step's work: at the step
     // start they queue with the chain waves' requests, which are on the
     // critical path (measured 8% faster on the LM-layer shape, 4% on the
@@ -674,14 +699,17 @@ __device__ void gate_role(S3<TIn, K>& sm, TAPS& taps, const FwdArgs& p, const Sp
     const char* qbase = (const char*)(qp + rowbase * DK);
     const char* kbase = (const char*)(kp + rowbase * DK);
     const char* vbase = (const char*)(vp + rowbase * p.dv);
-    const int qoff = grp * TPG * QRB + 2 * ip * ES;
-    int voff[K::VPT][2];
+    int qoffv[NV], voffv[NV][K::VPT][2];
 #pragma unroll
-    for (int x = 0; x < K::VPT; ++x) {
-        const int unit = gtid + x * 256;
-        const int tp = unit / K::VQ, jq = unit % K::VQ;
-        voff[x][0] = 2 * tp * VRB + (vt * DV + 4 * jq) * ES;
-        voff[x][1] = voff[x][0] + VRB;
+    for (int h = 0; h < NV; ++h) {
+        qoffv[h] = grp * TPG * QRB + 2 * ipv[h] * ES;
+#pragma unroll
+        for (int x = 0; x < K::VPT; ++x) {
+            const int unit = gtv[h] + x * 256;
+            const int tp = unit / K::VQ, jq = unit % K::VQ;
+            voffv[h][x][0] = 2 * tp * VRB + (vt * DV + 4 * jq) * ES;
+            voffv[h][x][1] = voffv[h][x][0] + VRB;
+        }
     }
     // Block prologue: the chain waves form k and the gates f, w; the gate
     // waves form q and v.  They stage the taps and biases in LDS (read from
@@ -712,7 +740,9 @@ __device__ void gate_role(S3<TIn, K>& sm, TAPS& taps, const FwdArgs& p, const Sp
             pq[j] = PR::make(pro_x(qp, p.conv_s[0], bh, p.T, W, DK, sp.T0 + j - 3, 2 * ip),
                              pro_x(qp, p.conv_s[0], bh, p.T, W, DK, sp.T0 + j - 3, 2 * ip + 1));
     }
-    auto load = [&](int c, Buf& bf) {
+    auto load = [&](int c, Buf& bf, int h) {
+        const int qoff = qoffv[h];
+        const auto& voff = voffv[h];
         const int t0 = c * C, n = sp.TL - t0;
         const int rows = n < 0 ? 0 : (n < C ? n : C);
         const auto rq = make_rsrc(qbase + (size_t)t0 * QRB, rows * QRB);
@@ -721,7 +751,7 @@ __device__ void gate_role(S3<TIn, K>& sm, TAPS& taps, const FwdArgs& p, const Sp
 #pragma unroll
         for (int u = 0; u < TPG; ++u) {
             bf.q[u] = buf_load<typename PR::V>(rq, qoff + u * QRB);
-            if constexpr (!PRO) bf.k[u] = buf_load<typename PR::V>(rk, qoff + u * QRB);
+            if constexpr (!CG) bf.k[u] = buf_load<typename PR::V>(rk, qoff + u * QRB);
         }
 #pragma unroll
         for (int x = 0; x < K::VPT; ++x)
@@ -741,9 +771,13 @@ __device__ void gate_role(S3<TIn, K>& sm, TAPS& taps, const FwdArgs& p, const Sp
         }
     };
 
-    auto step = [&](int c, Buf& cur, Buf& nxt) {
+    auto step = [&](int c, Buf (&curs)[NV], Buf (&nxts)[NV]) {
         const int cg = c + 1;  // chunk gated in this iteration
-        wait_loads<(D - 1) * NLD>();
+        wait_loads<(D - 1) * NLD * NV>();
+#pragma unroll
+        for (int h = 0; h < NV; ++h) {
+        const int ip = ipv[h], gtid = gtv[h], gwv = gw + h * K::NGW;
+        Buf& cur = curs[h];
         if (cg >= 0 && cg < nchunks) {
             const int L = chunk_len(sp.TL, cg, C), par = cg & 1;
             // V^T of the chunk
@@ -816,9 +850,9 @@ __device__ void gate_role(S3<TIn, K>& sm, TAPS& taps, const FwdArgs& p, const Sp
 #pragma unroll
             for (int u = 0; u < TPG; ++u) {
                 const int t = grp * TPG + u;
-                // a*lp, l (two key dims); with the block prologue f, w
+                // a*lp, l (two key dims); or f, w from the chain waves
                 const f32x4 lq = *(const f32x4*)&sm.LP[par][t][(2 * ip) ^ lp_swz(t)];
-                if constexpr (PRO) {
+                if constexpr (CG) {
                     f[u][0] = lq[0];
                     w[u][0] = lq[1];
                     f[u][1] = lq[2];
@@ -917,7 +951,7 @@ __device__ void gate_role(S3<TIn, K>& sm, TAPS& taps, const FwdArgs& p, const Sp
 #pragma unroll
                         for (int x = 0; x < K::IPW / 8; ++x) {
                             const int pid = x * 64 + lane, t = pid % C;
-                            const int i0 = gw * 2 * K::IPW + 8 * (pid / C);
+                            const int i0 = gwv * 2 * K::IPW + 8 * (pid / C);
                             const f32x4 c0 = *(const f32x4*)&sm.Wc[par][i0];
                             const f32x4 c1 = *(const f32x4*)&sm.Wc[par][i0 + 4];
                             store_qhat8(&sm.op[par].fac.Q[qw_row<K>(t)][i0], c0, c1,
@@ -969,20 +1003,32 @@ __device__ void gate_role(S3<TIn, K>& sm, TAPS& taps, const FwdArgs& p, const Sp
                 }
             }
         }
-        if (nchunks > 0) load(cg + D, nxt);
+        }
+        if (nchunks > 0) {
+#pragma unroll
+            for (int h = 0; h < NV; ++h) load(cg + D, nxts[h], h);
+        }
         lds_barrier();
     };
 
-    if (gtid < DK) sm.E[1][gtid] = 1.f;
+#pragma unroll
+    for (int h = 0; h < NV; ++h)
+        if (gtv[h] < DK) sm.E[1][gtv[h]] = 1.f;
     // step c gates chunk c+1 from buffer (c+1) mod NB and loads chunk c+1+D;
     // the first step only loads
     if (nchunks > 0) {
 #pragma unroll
-        for (int j = 0; j < D - 1; ++j) load(j, b[j]);
-    }
-    for (int c = -2; c < nsteps - 2; c += NB) {
+        for (int j = 0; j < D - 1; ++j)
 #pragma unroll
-        for (int s = 0; s < NB; ++s) step(c + s, b[(s + NB - 1) % NB], b[(s + NB - 2) % NB]);
+            for (int h = 0; h < NV; ++h) load(j, b[j % NBUF][h], h);
+    }
+    if constexpr (NBUF == 1) {
+        for (int c = -2; c < nsteps - 2; ++c) step(c, b[0], b[0]);
+    } else {
+        for (int c = -2; c < nsteps - 2; c += NB) {
+#pragma unroll
+            for (int s = 0; s < NB; ++s) step(c + s, b[(s + NB - 1) % NB], b[(s + NB - 2) % NB]);
+        }
     }
     lds_barrier();
 }
@@ -1206,23 +1252,29 @@ hipError_t launch_chain(const FwdArgs& a, hipStream_t s) {
 // (unsplit, serial chain) when conv_w is set
 template <typename TIn, int DK, int DV>
 hipError_t launch(const FwdArgs& a, hipStream_t s) {
-    if (a.conv_w > 0) {
-        typedef P3<TIn, DK, DV> K;
-        if (a.nseg > 1) {
-            const int nblk = a.B * a.H * a.n_vtiles * a.nseg;
-            hipLaunchKernelGGL((kla_fwd_diag_pipe_kernel<TIn, DK, DV, true, false, true>), dim3(nblk), dim3(K::NT),
-                               0, s, a);
-        } else {
-            const int nblk = a.B * a.H * a.n_vtiles;
-            hipLaunchKernelGGL((kla_fwd_diag_pipe_kernel<TIn, DK, DV, false, false, true>), dim3(nblk),
-                               dim3(K::NT), 0, s, a);
+    if constexpr (DV == 128) {
+        // 128-column tiles: the plain forward only (serial chain)
+        if (a.conv_w > 0 || a.chain_scan) return hipErrorInvalidValue;
+        return launch_chain<TIn, DK, DV, false>(a, s);
+    } else {
+        if (a.conv_w > 0) {
+            typedef P3<TIn, DK, DV> K;
+            if (a.nseg > 1) {
+                const int nblk = a.B * a.H * a.n_vtiles * a.nseg;
+                hipLaunchKernelGGL((kla_fwd_diag_pipe_kernel<TIn, DK, DV, true, false, true>), dim3(nblk),
+                                   dim3(K::NT), 0, s, a);
+            } else {
+                const int nblk = a.B * a.H * a.n_vtiles;
+                hipLaunchKernelGGL((kla_fwd_diag_pipe_kernel<TIn, DK, DV, false, false, true>), dim3(nblk),
+                                   dim3(K::NT), 0, s, a);
+            }
+            return hipGetLastError();
         }
-        return hipGetLastError();
+        if constexpr (std::is_same<TIn, bf16>::value) {
+            if (a.chain_scan) return launch_chain<TIn, DK, DV, true>(a, s);
+        }
+        return launch_chain<TIn, DK, DV, false>(a, s);
     }
-    if constexpr (std::is_same<TIn, bf16>::value) {
-        if (a.chain_scan) return launch_chain<TIn, DK, DV, true>(a, s);
-    }
-    return launch_chain<TIn, DK, DV, false>(a, s);
 }
 
 }  // namespace
@@ -1230,6 +1282,7 @@ hipError_t launch(const FwdArgs& a, hipStream_t s) {
 bool fwd_diag_pipe_supported(int dk, int dv, int nvt, int dtype) {
     if (dk != dv || nvt < 1 || dv % nvt) return false;
     const int dvt = dv / nvt;
+    if (dvt == 128) return dk == 128 && dtype == DT_BF16;
     return dvt == 64 && (dk == 64 || (dk == 128 && dtype == DT_BF16));
 }
 
@@ -1242,7 +1295,7 @@ int fwd_diag_pipe_vtiles(int dk, int dv, int dtype) {
 hipError_t launch_fwd_diag_pipe(const FwdArgs& a, int dtype, hipStream_t s) {
     if (!fwd_diag_pipe_supported(a.dk, a.dv, a.n_vtiles, dtype)) return hipErrorInvalidValue;
     const int dvt = a.dv / a.n_vtiles;
-    (void)dvt;
+    if (dtype == DT_BF16 && dvt == 128) return launch<bf16, 128, 128>(a, s);
     if (dtype == DT_BF16) return a.dk == 128 ? launch<bf16, 128, 64>(a, s) : launch<bf16, 64, 64>(a, s);
     return launch<float, 64, 64>(a, s);
 }

@@ -159,6 +159,8 @@ def test_kernel_name_reports_the_dispatch():
     assert scan_amd.klaFwdKernelName(KlaDims(64, 16, 2048, 128, 128, BF16, DIAG)) == \
         "kla_fwd_diag_pipe_kernel (value tiles)"
     assert scan_amd.klaFwdKernelName(KlaDims(8, 16, 2048, 64, 64, BF16, DIAG)) == "kla_fwd_diag_pipe_kernel"
+    # few long sequences: the sequence split on whole 128-column rows
+    assert scan_amd.klaFwdKernelName(KlaDims(1, 16, 32768, 128, 128, BF16, DIAG)) == "kla_fwd_diag_pipe_kernel"
     assert scan_amd.klaFwdKernelName(KlaDims(8, 16, 2048, 64, 64, F32, DIAG)) == "kla_fwd_diag_pipe_kernel"
     assert scan_amd.klaFwdKernelName(KlaDims(2, 3, 100, 32, 32, F32, DIAG)) == "kla_fwd_diag_kernel"
     assert scan_amd.klaFwdKernelName(KlaDims(2, 3, 100, 64, 64, F32, ISO)) == \

@@ -287,19 +287,23 @@ def test_parity_rescale_and_exact_mix(d, dtype):
     assert_parity(compare(hip, ref), dtype, "rescale-mix")
 
 
-@pytest.mark.parametrize("name,over,nseg,state", [
-    ("long_diag", dict(B=1, H=2, T=3000), "3", True),       # bf16 d128, ragged last segment
-    ("small_diag", dict(B=1, H=2, T=700, dk=64, dv=64), "4", True),  # fp32 d64
-    ("long_diag", dict(B=1, H=2, T=4096), "", False),       # split chosen by the library
+@pytest.mark.parametrize("name,over,nseg,state,vtiles", [
+    ("long_diag", dict(B=1, H=2, T=3000), "3", True, "1"),   # bf16 d128, 128-column tiles, ragged last segment
+    ("long_diag", dict(B=1, H=2, T=3000), "3", True, "2"),   # the same with 64-column tiles
+    ("small_diag", dict(B=1, H=2, T=700, dk=64, dv=64), "4", True, "1"),  # fp32 d64 (64-column tiles)
+    ("long_diag", dict(B=1, H=2, T=4096), "", False, ""),    # split and tiles chosen by the library
+    ("long_diag", dict(B=1, H=2, T=4096), "", False, "2"),   # library split, 64-column tiles
 ])
-def test_parity_sequence_split(monkeypatch, name, over, nseg, state):
+def test_parity_sequence_split(monkeypatch, name, over, nseg, state, vtiles):
     """Sequence split: segment precision products, carries and the output
-    correction reproduce the unsplit recurrence, with and without a state."""
-    _print_case("split", name, over, nseg)
+    correction reproduce the unsplit recurrence, with and without a state,
+    on 128-column tiles (the chain waves form the gates, two gate waves)
+    and on 64-column tiles."""
+    _print_case("split", name, over, nseg, vtiles)
     if nseg:
         monkeypatch.setenv("KLA_FWD_NSEG", nseg)
-    if over.get("dk") == 64:
-        monkeypatch.setenv("KLA_FWD_VTILES", "1")  # the 64-column wave-specialised kernel
+    if vtiles:
+        monkeypatch.setenv("KLA_FWD_VTILES", vtiles)
     inp = gen.make_inputs(name, seed=21, **over)
     w = inp["workload"]
     dims = scan_amd.KlaDims(w.B, w.H, w.T, w.dk, w.dv, 1 if w.dtype == "bf16" else 0, 0)
