@@ -135,9 +135,12 @@ FwdKernel pick_kernel(const klaDims* d, int* n_vtiles) {
 
 // Sequence segments klaFwd uses for these dims (1 = no split) and their
 // length: segments of seg_len tokens, the last one ragged and non-empty.
-int pick_nseg(const klaDims* d, int* seg_len = nullptr) {
+// nvt_run: the value tiles the caller launches with, if it picks them itself
+// (the block prologue keeps 64-column tiles); 0 = those of pick_kernel.
+int pick_nseg(const klaDims* d, int* seg_len = nullptr, int nvt_run = 0) {
     int nvt = 1;
     if (d->T <= 0 || pick_kernel(d, &nvt) != FK_DIAG_PIPE) return 1;
+    if (nvt_run > 0) nvt = nvt_run;
     const int e = env_nseg();
     int n = e > 0 ? e : kla::fwd_diag_nseg(d->B, d->H, d->T, d->dk, d->dv, nvt);
     if (n <= 1) return 1;
@@ -191,7 +194,7 @@ namespace {
 // correction.  workspace holds klaFwdWorkspaceBytes(d) bytes when split.
 hipError_t launch_diag_pipe(kla::FwdArgs& fa, const klaDims* d, void* workspace, hipStream_t st) {
     int seg_len = 0;
-    const int nseg = pick_nseg(d, &seg_len);
+    const int nseg = pick_nseg(d, &seg_len, fa.n_vtiles);
     if (nseg <= 1) return kla::launch_fwd_diag_pipe(fa, d->dtype, st);
     const size_t es = d->dtype == KLA_BF16 ? 2 : 4;
     const kla::SegWorkspace w = kla::seg_workspace(d->B, d->H, d->T, d->dk, d->dv, (int)es, nseg);
