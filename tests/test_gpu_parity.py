@@ -252,6 +252,39 @@ def test_adversarial_gates_finite_and_exact(dtype):
     assert_parity(compare(hip, ref), dtype, "adversarial")
 
 
+@pytest.mark.parametrize("vtiles", ["", "2"])
+def test_split_adversarial_gates(monkeypatch, vtiles):
+    """Gate products that underflow inside chunks in the middle of a split
+    sequence (a -> 0.01 on most tokens, r = 1e-3, |k| up to 5 there): those
+    chunks take the exact token-by-token path, the others the factorised
+    one, across segment boundaries; on the library's 128-column tiles (the
+    chain waves form the gates) and on 64-column tiles."""
+    _print_case("split adversarial", vtiles)
+    if vtiles:
+        monkeypatch.setenv("KLA_FWD_VTILES", vtiles)
+    inp = gen.make_inputs("long_diag", seed=31, B=1, H=2, T=4096)
+    w = inp["workload"]
+    dims = scan_amd.KlaDims(w.B, w.H, w.T, w.dk, w.dv, 1, 0)
+    assert scan_amd.klaFwdWorkspaceBytes(dims) > 0
+    g = torch.Generator().manual_seed(12)
+    lo, hi = 1000, 2600
+    a = inp["a"].clone()
+    a[:, :, lo:hi] = 0.01
+    a[:, :, lo:hi:7] = 0.9
+    inp["a"] = a
+    r = inp["r"].clone()
+    r[:, :, lo:hi] = 1e-3
+    inp["r"] = r
+    k = inp["k"].float().clone()
+    k[:, :, lo:hi] = 5 * (2 * torch.rand(1, 2, hi - lo, w.dk, generator=g) - 1)
+    inp["k"] = k.to(inp["k"].dtype)
+    hip = run_hip(inp, "diag")
+    for x in hip:
+        assert np.all(np.isfinite(hip[x])), x
+    ref = run_oracle(inp, "diag")
+    assert_parity(compare(hip, ref), w.dtype, f"split adversarial {vtiles}")
+
+
 def test_vtile_split_invariance(monkeypatch):
     """Splitting the value columns over workgroups changes no bit (the
     single-role kernel, which builds both one and two tiles at dk = 128)."""
