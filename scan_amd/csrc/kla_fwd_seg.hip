@@ -393,14 +393,30 @@ __global__ void kla_seg_carry_m(FwdArgs p) {
     const int j = (int)(x % p.dv);
     const int i = (int)((x / p.dv) % p.dk);
     const int bh = (int)(x / ((size_t)p.dv * p.dk));
+    // Eight segments at a time: their local states and decays are all read
+    // before any slot is rewritten (slot s-1 is rewritten only after segment
+    // s-1 has been read), so the reads of a batch are in flight together
+    // instead of one round trip per segment.
+    constexpr int NB = 8;
+    const size_t slot0 = (size_t)bh * p.nseg * p.dk * p.dv + (size_t)i * p.dv + j;
+    const size_t sstride = (size_t)p.dk * p.dv;
     float m = 0.f;
-    for (int s = 0; s < p.nseg; ++s) {
-        const size_t row = seg_row(p, bh, s);
-        float* slot = p.seg_m + (row * p.dk + i) * p.dv + j;
-        const float ml = *slot;
-        const float d = p.seg_d[row * p.dk + i];
-        if (s >= 1) *(slot - (size_t)p.dk * p.dv) = m;  // M entering segment s
-        m = __builtin_fmaf(d, m, ml);
+    for (int s0 = 0; s0 < p.nseg; s0 += NB) {
+        float ml[NB], d[NB];
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+            const int s = s0 + u;
+            ml[u] = s < p.nseg ? p.seg_m[slot0 + (size_t)s * sstride] : 0.f;
+            d[u] = s < p.nseg ? p.seg_d[seg_row(p, bh, s) * p.dk + i] : 1.f;
+        }
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+            const int s = s0 + u;
+            if (s < p.nseg) {
+                if (s >= 1) p.seg_m[slot0 + (size_t)(s - 1) * sstride] = m;  // M entering segment s
+                m = __builtin_fmaf(d[u], m, ml[u]);
+            }
+        }
     }
     if (p.etaT) p.etaT[x] = m * p.seg_lend[(size_t)bh * p.dk + i];
 }
