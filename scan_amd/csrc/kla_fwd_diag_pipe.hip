@@ -111,6 +111,9 @@ struct S3 {
     float lT[K::DK];
     alignas(16) float Wc[2][K::DK];  // sequence split: gate product from the segment
                                      // start through token 0 of the chunk
+    alignas(16) float WcM[2][K::DK];  // the same, handed by the gate waves to the
+                                      // MMA waves (with the block prologue, bf16:
+                                      // they store q-hat)
     int bad[4];                   // chunk needs the exact token-by-token path
 };
 
@@ -687,6 +690,12 @@ __device__ void gate_role(S3<TIn, K>& sm, TAPS& taps, const FwdArgs& p, const Sp
     // with the block prologue or 128-column tiles the chain waves form f
     // and w, and the gate waves read no k
     constexpr bool CG = PRO || K::DV == 128;
+    // sequence split with the block prologue, bf16: the MMA waves store
+    // q-hat, which leaves the gate waves (the convolution of q and v is theirs)
+    // more of the step (measured 7% faster on the B1 H16 T32768 block; without
+    // the prologue 3-4% slower, and with 128-column tiles it spilled the chain
+    // waves' registers)
+    constexpr bool QM = SEG && PRO && std::is_same<TIn, bf16>::value && K::DV == 64;
     constexpr int NLD = (PRO ? TPG + 5 * K::VPT : CG ? TPG + 2 * K::VPT : 2 * TPG + 2 * K::VPT);  // loads per chunk
     // The next chunk's rows are requested after the step's work: at the step
     // start they queue with the chain waves' requests, which are on the
@@ -938,7 +947,10 @@ __device__ void gate_role(S3<TIn, K>& sm, TAPS& taps, const FwdArgs& p, const Sp
             if (!__builtin_amdgcn_readfirstlane(sm.bad[cg & 3])) {
                 if (L == C) fac(std::true_type{});
                 else fac(std::false_type{});
-                if constexpr (SEG) {
+                if constexpr (QM) {
+                    // the MMA waves store q-hat from their Q^ fragments
+                    if (grp == 0) *(f32x2*)&sm.WcM[par][2 * ip] = f32x2{wc0, wc1};
+                } else if constexpr (SEG) {
                     if (wq) {
                         // q-hat = Q^ (.) Wc, read back from this wave's own
                         // block of Q^ (all tokens, its 2 IPW key dims) as 8
@@ -1034,12 +1046,14 @@ __device__ void gate_role(S3<TIn, K>& sm, TAPS& taps, const FwdArgs& p, const Sp
 }
 
 // ------------------------------------------------------------------ MMA role
-template <typename TIn, class K, bool SEG>
+template <typename TIn, class K, bool SEG, bool PRO>
 __device__ void mma_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int bh, int vt, int mw,
                          int lane) {
     typedef Frag<TIn> F;
     typedef typename F::V FV;
     constexpr int C = K::C, DK = K::DK, DV = K::DV, IT = K::IT, JT = K::JT, KB = K::KB;
+    // sequence split with the block prologue, bf16: these waves store q-hat
+    constexpr bool QM = SEG && PRO && std::is_same<TIn, bf16>::value && K::DV == 64;
     const size_t rowbase = (size_t)bh * p.T + sp.T0;
     const int nchunks = (sp.TL + C - 1) / C;
     const int nsteps = pipe_steps<K>(nchunks);
@@ -1128,6 +1142,47 @@ __device__ void mma_role(S3<TIn, K>& sm, const FwdArgs& p, const Span& sp, int b
                     const FV wt = F::ld(&o.WT[it * 16 + c16][0], g);
 #pragma unroll
                     for (int jj = 0; jj < JT; ++jj) acc[it][jj] = F::mma(wt, Vf[jj], acc[it][jj]);
+                }
+                // Sequence split, bf16: q-hat = Q^ (.) Wc for the correction pass,
+                // from the Q^ fragments (the MMA waves that share the chain
+                // waves' SIMDs, which have issue slots to spare).  Lanes g and
+                // g^1 swap a half so that each holds 8 consecutive key dims,
+                // the tiled layout's 16-byte piece: the same values the gate
+                // waves would store (bf16 Q^ times Wc, rounded once more).
+                if constexpr (QM) {
+                    if (sp.seg > 0 && vt == 0 && mw < 2) {
+                        const auto rqh = make_rsrc((const TIn*)p.seg_qhat +
+                                                       qhat_tile_offset(bh, p.T, DK, sp.T0 + t0, 0),
+                                                   (L + 15) / 16 * 16 * DK * (int)sizeof(TIn));
+                        const int odd = g & 1, gn = odd ? 2 + (g >> 1) : (g >> 1);
+#pragma unroll
+                        for (int b = 0; b < 2; ++b)
+#pragma unroll
+                            for (int kk = 0; kk < KB; ++kk) {
+                                if (kk % 2 != mw) continue;
+                                typedef unsigned u32x4 __attribute__((__vector_size__(16)));
+                                const u32x4 u = __builtin_bit_cast(u32x4, Qf[b][kk]);
+                                // slots 0-3: dims 4g.., 4-7: dims 16+4g..
+                                const unsigned x0 = odd ? u[0] : u[2], x1 = odd ? u[1] : u[3];
+                                const unsigned y0 = (unsigned)__shfl_xor((int)x0, 16, 64);
+                                const unsigned y1 = (unsigned)__shfl_xor((int)x1, 16, 64);
+                                const u32x4 nat = odd ? u32x4{y0, y1, u[2], u[3]} : u32x4{u[0], u[1], y0, y1};
+                                const int i0 = kk * 32 + 8 * gn;
+                                const f32x4 w0 = *(const f32x4*)&sm.WcM[par][i0];
+                                const f32x4 w1 = *(const f32x4*)&sm.WcM[par][i0 + 4];
+                                const f32x4 lo = f32x4{__builtin_bit_cast(float, nat[0] << 16),
+                                                       __builtin_bit_cast(float, nat[0] & 0xffff0000u),
+                                                       __builtin_bit_cast(float, nat[1] << 16),
+                                                       __builtin_bit_cast(float, nat[1] & 0xffff0000u)} * w0;
+                                const f32x4 hi = f32x4{__builtin_bit_cast(float, nat[2] << 16),
+                                                       __builtin_bit_cast(float, nat[2] & 0xffff0000u),
+                                                       __builtin_bit_cast(float, nat[3] << 16),
+                                                       __builtin_bit_cast(float, nat[3] & 0xffff0000u)} * w1;
+                                struct alignas(16) Two { typename Quad<TIn>::V x, y; };
+                                buf_store(__builtin_bit_cast(f32x4, Two{Quad<TIn>::make(lo), Quad<TIn>::make(hi)}),
+                                          rqh, ((b * KB + kk) * 512 + (gn * 16 + c16) * 8) * (int)sizeof(TIn));
+                            }
+                    }
                 }
             } else {
                 // exact path: m <- f_t (.) m + w_t v_t^T, o_t = q_t^T m, token by token
@@ -1226,7 +1281,7 @@ __global__ __launch_bounds__((P3<TIn, DK, DV>::NT)) void kla_fwd_diag_pipe_kerne
     } else if (wave < 4) {
         gate_role<TIn, K, SEG, PRO>(sm, taps, p, sp, bh, vt, wave - K::NCW, lane);
     } else if (wave < 4 + K::NMW) {
-        mma_role<TIn, K, SEG>(sm, p, sp, bh, vt, wave - 4, lane);
+        mma_role<TIn, K, SEG, PRO>(sm, p, sp, bh, vt, wave - 4, lane);
     } else {
         gate_role<TIn, K, SEG, PRO>(sm, taps, p, sp, bh, vt, 4 - K::NCW + (wave - 4 - K::NMW), lane);
     }
