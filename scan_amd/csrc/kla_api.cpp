@@ -210,7 +210,6 @@ hipError_t launch_diag_pipe(kla::FwdArgs& fa, const klaDims* d, void* workspace,
     int* ok = (int*)(ws + w.off_ok);
     hipError_t e = kla::launch_seg_warm(fa, ok, d->dtype, st);
     if (e == hipSuccess) e = kla::launch_seg_mobius(fa, P, ok, d->dtype, st);
-    if (e == hipSuccess) e = kla::launch_seg_carry_l(fa, P, ok, st);
     if (e == hipSuccess) e = kla::launch_fwd_diag_pipe(fa, d->dtype, st);
     if (e == hipSuccess) e = kla::launch_seg_carry_m(fa, st);
     if (e == hipSuccess) e = kla::launch_seg_correct(fa, d->dtype, st);

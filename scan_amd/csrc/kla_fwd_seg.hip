@@ -18,8 +18,9 @@
 //   1. kla_seg_mobius:   the product of the precision matrices of every
 //                        block of kSegBlk tokens before the last segment, per
 //                        key dim;
-//   2. kla_seg_carry_l:  the precision entering each segment (a walk over
-//                        the block products), exact from the caller's l0;
+//   2. the precision entering each segment (a walk over the block
+//      products), exact from the caller's l0, run by the last workgroup of
+//      pass 1 to finish;
 //   3. the wave-specialised forward on every segment (local outputs, local
 //      final mean state, the segment's total gate, and q (.) gate product);
 //   4. kla_seg_carry_m:  the mean state entering each segment, and etaT;
@@ -107,6 +108,8 @@ __global__ __launch_bounds__(64 * kWarmRuns) void kla_seg_warm(FwdArgs p, int* o
     const int i = g * 64 + lane;
     const int h = bh % p.H;
     const int bnd = s * p.seg_len;
+    // the counter of the exact passes' workgroups (launched next) starts at 0
+    if (blockIdx.x == 0 && threadIdx.x == 0) ok[(size_t)p.B * p.H * p.nseg * 2] = 0;
     const int n = bnd < kWarm ? bnd : kWarm;  // a multiple of kSegBlk
     const int t0 = bnd - n;
     const double qn = PRO ? act_softplus(p.qn[(size_t)h * DK + i]) : p.qn[(size_t)h * DK + i];
@@ -329,8 +332,10 @@ __device__ __forceinline__ void mobius_block(const FwdArgs& p, float* P, f32x4 (
     }
 }
 
+__device__ void seg_carry_l_one(const FwdArgs& p, const float* P, const int* ok, int x);
+
 template <typename TIn, int DK, bool PRO>
-__global__ __launch_bounds__(kMobThreads) void kla_seg_mobius(FwdArgs p, float* P, const int* ok) {
+__global__ __launch_bounds__(kMobThreads) void kla_seg_mobius(FwdArgs p, float* P, int* ok) {
     constexpr int NSUB = kMobThreads / DK;
     __shared__ f32x4 sP[NSUB][DK];
     const int i = threadIdx.x % DK, sub = threadIdx.x / DK;
@@ -343,14 +348,27 @@ __global__ __launch_bounds__(kMobThreads) void kla_seg_mobius(FwdArgs p, float* 
         mobius_block<TIn, DK, PRO>(p, P, sP, i, sub, nb, bh, s);
         __syncthreads();  // sP is reused by the next block
     }
+    // The last workgroup to finish (counted after its block matrices are
+    // released) runs pass 2, the precision carry, which needs all of them:
+    // one launch instead of two, and no workgroup waits for another.
+    __shared__ int last;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        __threadfence();
+        last = atomicAdd(ok + (size_t)p.B * p.H * p.nseg * 2, 1) == (int)gridDim.x - 1;
+    }
+    __syncthreads();
+    if (!last) return;
+    __threadfence();
+    for (int x = threadIdx.x; x < p.B * p.H * p.dk; x += blockDim.x) seg_carry_l_one(p, P, ok, x);
 }
 
 // -------------------------------------------------- 2. precision carry
-__global__ void kla_seg_carry_l(FwdArgs p, const float* P, const int* ok) {
-    const int n = p.B * p.H * p.dk;
-    if (seg_all_warm_ok(p, ok)) return;  // uniform over the workgroup
-    const int x = blockIdx.x * blockDim.x + threadIdx.x;
-    if (x >= n) return;
+// Entry x = (b,h, key dim) of a (b,h) the warm-up left unsettled: the
+// precision entering each segment from the caller's l0, composing the block
+// matrices of each segment eight loads at a time.  Run by the last workgroup
+// of pass 1 (below), once every block matrix is written.
+__device__ void seg_carry_l_one(const FwdArgs& p, const float* P, const int* ok, int x) {
     const int bh = x / p.dk, i = x % p.dk;
     if (seg_warm_ok(p, ok, bh)) return;
     float l = p.l0 ? p.l0[x] : 1.f;
@@ -556,7 +574,7 @@ hipError_t launch_warm_t(const FwdArgs& a, int* ok, hipStream_t s) {
 }
 
 template <typename TIn>
-hipError_t launch_mobius_t(const FwdArgs& a, float* P, const int* ok, hipStream_t s) {
+hipError_t launch_mobius_t(const FwdArgs& a, float* P, int* ok, hipStream_t s) {
     int nblk = a.B * a.H * (a.nseg - 1) * (a.seg_len / kSegBlk);
     if (nblk > kMobGrid) nblk = kMobGrid;
     const bool pro = a.conv_w > 0;
@@ -601,7 +619,7 @@ SegWorkspace seg_workspace(int B, int H, int T, int dk, int dv, int es, int nseg
     w.off_lend = o; o += align256(bh * dk * sizeof(float));
     w.off_m = o;    o += align256(bh * nseg * dk * dv * sizeof(float));
     w.off_qhat = o; o += align256(bh * (size_t)((T + 15) / 16 * 16) * dk * es);
-    w.off_ok = o;   o += align256(bh * nseg * 2 * sizeof(int));
+    w.off_ok = o;   o += align256((bh * nseg * 2 + 1) * sizeof(int));  // flags, then the pass-1 counter
     w.bytes = o;
     return w;
 }
@@ -628,15 +646,10 @@ hipError_t launch_seg_warm(const FwdArgs& a, int* ok, int dtype, hipStream_t s) 
     return dtype == DT_BF16 ? launch_warm_t<bf16>(a, ok, s) : launch_warm_t<float>(a, ok, s);
 }
 
-hipError_t launch_seg_mobius(const FwdArgs& a, float* P, const int* ok, int dtype, hipStream_t s) {
+hipError_t launch_seg_mobius(const FwdArgs& a, float* P, int* ok, int dtype, hipStream_t s) {
     return dtype == DT_BF16 ? launch_mobius_t<bf16>(a, P, ok, s) : launch_mobius_t<float>(a, P, ok, s);
 }
 
-hipError_t launch_seg_carry_l(const FwdArgs& a, const float* P, const int* ok, hipStream_t s) {
-    const int n = a.B * a.H * a.dk;
-    hipLaunchKernelGGL(kla_seg_carry_l, dim3((n + 255) / 256), dim3(256), 0, s, a, P, ok);
-    return hipGetLastError();
-}
 
 hipError_t launch_seg_carry_m(const FwdArgs& a, hipStream_t s) {
     const size_t n = (size_t)a.B * a.H * a.dk * a.dv;

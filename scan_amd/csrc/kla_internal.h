@@ -90,8 +90,10 @@ int fwd_diag_seg_len(int T, int nseg);
 // ok: [BH, nseg, 2] flags (per 64 key dims), written by the warm-up and
 // read by the exact passes.
 hipError_t launch_seg_warm(const FwdArgs& a, int* ok, int dtype, hipStream_t s);
-hipError_t launch_seg_mobius(const FwdArgs& a, float* P, const int* ok, int dtype, hipStream_t s);
-hipError_t launch_seg_carry_l(const FwdArgs& a, const float* P, const int* ok, hipStream_t s);
+// The exact passes 1 and 2 (block products, then the precision carry by the
+// last workgroup to finish); ok also holds their completion counter, after
+// the flags, which the warm-up zeroes.
+hipError_t launch_seg_mobius(const FwdArgs& a, float* P, int* ok, int dtype, hipStream_t s);
 hipError_t launch_seg_carry_m(const FwdArgs& a, hipStream_t s);
 hipError_t launch_seg_correct(const FwdArgs& a, int dtype, hipStream_t s);
 
