@@ -46,8 +46,9 @@
 //   contract it along different axes).  The precision-adjoint wave runs two
 //   chunks behind the chain; at the start of each iteration it also forms
 //   the chunk's two upper-triangular operands, which the matrix-core waves
-//   take from LDS after a bounded wait on its flag.  dv and dr leave
-//   per-tile partials that a third kernel sums.
+//   take from LDS after a bounded wait on its flag.  With two row tiles dv
+//   and dr leave per-tile partials that a third kernel sums; with one the
+//   sweep writes them itself.
 // Isotropic (one row tile): the precision, decay and process noise are
 // scalars per token, written into every lane's row, so the matrix-core code
 // is shared; the chain waves form |k_t|^2 over the key dims, the adjoint
@@ -670,7 +671,7 @@ __global__ __launch_bounds__(384) void kla_bwd_chunk_rev(BwdArgs p) {
                 // the same value
                 const auto rga = rows_of(p.ga, row0 + (size_t)c * kBC, nv, 1);
                 const auto rgq = rows_of(p.gqn, row0 + (size_t)c * kBC, nv, 1);
-                const auto rdr = rows_of(ws + L.drp, (size_t)c * kBC, nv, 1);
+                const auto rdr = rows_of(p.gr, row0 + (size_t)c * kBC, nv, 1);  // one row tile: dr itself
 #pragma unroll
                 for (int u = 0; u < kBC; ++u) {
                     const float lbu = lb[u], cmu = cm[u], g = gv[u], P = Pv[u];
@@ -715,7 +716,10 @@ __global__ __launch_bounds__(384) void kla_bwd_chunk_rev(BwdArgs p) {
                 // the same in the four lanes of a quad
                 int base = 0;
                 reduce_scatter<kBC, 32>(dr, lane, base);
-                buf_store(dr[0], rows_of(ws + L.drp + (size_t)tile * L.t4, (size_t)c * kBC, nv, 1), base * 4);
+                if constexpr (NT == 1)
+                    buf_store(dr[0], rows_of(p.gr, row0 + (size_t)c * kBC, nv, 1), base * 4);
+                else
+                    buf_store(dr[0], rows_of(ws + L.drp + (size_t)tile * L.t4, (size_t)c * kBC, nv, 1), base * 4);
             }
             if (c >= 1) loadq(c - 1);  // lands during the next iteration
         };
@@ -841,11 +845,18 @@ __global__ __launch_bounds__(384) void kla_bwd_chunk_rev(BwdArgs p) {
                                              split4(eB[ib][jb]), zero4());
             const f32x4 du = mma_sx(wd, ld_col4(&sm.dO[b][4 * g][jw0 + 16 * jb + c16], D + 8), zero4());
             const f32x4 dv = ((dacc[0] + dacc[1]) + (dacc[2] + dacc[3])) + du;
-            // the partial straight from the accumulator: rows 4g + e, 16
-            // consecutive columns per row (rows past the end are dropped)
-            const auto rs = rows_of(ws + L.dvp + (size_t)tile * T * D, (size_t)c * kBC, nv, D);
+            // straight from the accumulator: rows 4g + e, 16 consecutive
+            // columns per row (rows past the end are dropped); with one row
+            // tile dv itself, with two the tile's partial for the combine pass
+            if constexpr (NT == 1) {
+                const auto rg = rows_of((bf16*)p.gv, row0 + (size_t)c * kBC, nv, D);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) buf_store(dv[e], rs, ((4 * g + e) * D + jw0 + 16 * jb + c16) * 4);
+                for (int e = 0; e < 4; ++e) buf_store_b16((bf16)dv[e], rg, ((4 * g + e) * D + jw0 + 16 * jb + c16) * 2);
+            } else {
+                const auto rs = rows_of(ws + L.dvp + (size_t)tile * T * D, (size_t)c * kBC, nv, D);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) buf_store(dv[e], rs, ((4 * g + e) * D + jw0 + 16 * jb + c16) * 4);
+            }
         }
         // eps_in = G_C (.) eps_out + A^T dO, both copies
         {
@@ -877,8 +888,8 @@ __global__ __launch_bounds__(384) void kla_bwd_chunk_rev(BwdArgs p) {
     }
 }
 
-// dv and dr: the sums of the row tiles' partials (in tile order).  One
-// thread per (b,h, token, value quad).
+// dv and dr with two or more row tiles: the sums of the tiles' partials (in
+// tile order).  One thread per (b,h, token, value quad).
 template <int NT>
 __global__ void kla_bwd_chunk_combine(BwdArgs p) {
     const int D = p.dv, VQ = D / 4;
@@ -910,8 +921,10 @@ void launch(const BwdArgs& a, hipStream_t s) {
     const dim3 grid((unsigned)(NT == 1 ? nbh : (nbh + 7) / 8 * 8 * NT));
     hipLaunchKernelGGL((kla_bwd_chunk_fwd<D, ISO>), grid, dim3(320), 0, s, a);
     hipLaunchKernelGGL((kla_bwd_chunk_rev<D, ISO>), grid, dim3(384), 0, s, a);
-    const size_t n = (size_t)nbh * a.T * (D / 4);
-    hipLaunchKernelGGL((kla_bwd_chunk_combine<NT>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+    if constexpr (NT > 1) {  // one row tile writes dv and dr itself
+        const size_t n = (size_t)nbh * a.T * (D / 4);
+        hipLaunchKernelGGL((kla_bwd_chunk_combine<NT>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+    }
 }
 
 }  // namespace
